@@ -1,0 +1,167 @@
+/*
+ * sige.h -- C ABI of the tile-sparse incremental convolution library (libsige.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are cited per call below):
+ *   mer.dev notes, "Efficient Spatially Sparse Inference for Conditional GANs
+ *   and Diffusion Models", sections 3, 3.1, 3.2; the SIGE project README
+ *   (dongaigc.com mirror), section "Overview"; the nubint.ai review of the same
+ *   paper, "Proposed method".  The activations of the original image are
+ *   computed once and cached.  For an edited image: (1) diff the original and
+ *   edited activations into a change mask; (2) reduce the mask, pooled to each
+ *   layer's scale and dilated, to a list of active output blocks; (3) gather
+ *   the active blocks' input windows (with halo) from the edited activation,
+ *   stacked along a block dimension; (4) run the convolution on the stacked
+ *   blocks; (5) scatter the output blocks into (a copy of) the cached output of
+ *   the original image.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and never synchronises.
+ *   - Activations, caches and outputs are NHWC and contiguous.  Weights are
+ *     KRSC: [c_out][k][k][c_in], contiguous.  Bias is fp32 [c_out] or NULL.
+ *   - `dtype` is one of SIGE_F32, SIGE_BF16, SIGE_F16.  Convolutions multiply
+ *     in the storage type on the matrix cores, accumulate in fp32 and round
+ *     once (to nearest, ties to even) into the storage type.
+ *   - Tensors read or written in 16-byte vectors must be 16-byte aligned and
+ *     their channel rows a multiple of 16 bytes (c % 8 == 0 for 16-bit types,
+ *     c % 4 == 0 for fp32); otherwise SIGE_EALIGN.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it; results are ready when the stream reaches them.
+ *   - The number of active blocks stays on the device: `count` points to one
+ *     int32 in device memory written by sige_reduce_mask and read by the later
+ *     steps, so no step waits for the host.  Block buffers are sized for the
+ *     capacity sige_max_blocks(); only slots [0, *count) are read or written.
+ *   - Every call returns SIGE_OK (0) or a negative code.  Arguments are checked
+ *     on the host before anything is enqueued; a rejected call enqueues
+ *     nothing.  sige_strerror() names a code; sige_last_error() returns the
+ *     calling thread's last message.  Device faults surface at the caller's
+ *     next synchronisation (or inside the call when the environment variable
+ *     SIGE_DEBUG_SYNC=1 is set, which synchronises after every launch).
+ */
+#ifndef SIGE_H
+#define SIGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SIGE_OK 0
+#define SIGE_EINVAL (-1)  /* null pointer, bad shape/geometry, aliasing, unsupported parameter */
+#define SIGE_EDTYPE (-2)  /* dtype is not SIGE_F32 / SIGE_BF16 / SIGE_F16 */
+#define SIGE_EALIGN (-3)  /* pointer or channel row not 16-byte aligned */
+#define SIGE_EHIP (-4)    /* the HIP runtime reported an error (message in sige_last_error) */
+#define SIGE_ENODEV (-5)  /* no usable GPU */
+#define SIGE_ERANGE (-6)  /* a size exceeds a documented limit of a kernel */
+
+enum { SIGE_F32 = 0, SIGE_BF16 = 1, SIGE_F16 = 2 };
+
+/* Geometry of one convolution and its block grid.
+ *   input  [n, h, w, c_in];  k x k kernel, stride, zero padding pad;
+ *   output [n, ho, wo, c_out] with ho = (h + 2*pad - k)/stride + 1 (wo alike);
+ *   output blocks of block x block pixels: nby = ceil(ho/block), nbx = ceil(wo/block)
+ *   (the last row/column of blocks may be partial);
+ *   input window of block (by, bx): rows [by*block*stride - pad, ... + ib),
+ *   columns alike, ib = (block-1)*stride + k (neighbouring windows of a 3x3
+ *   stride-1 conv overlap by 2, SIGE README, "Overview").
+ * Supported: n, h, w, c_in, c_out >= 1; 1 <= k <= 7; 1 <= stride <= 4;
+ * 0 <= pad < k; 1 <= block <= 64; ib <= 64; h + 2*pad >= k (w alike). */
+typedef struct {
+    int32_t n, h, w;
+    int32_t c_in, c_out;
+    int32_t k, stride, pad;
+    int32_t block;
+} sige_geom;
+
+typedef struct {
+    int32_t ho, wo;   /* output size */
+    int32_t nby, nbx; /* block grid per image */
+    int32_t ib;       /* input window edge */
+    int64_t cap;      /* n * nby * nbx: capacity of idx and of block buffers */
+} sige_derived;
+
+/* Validate a geometry and fill its derived sizes.  Host only; no GPU needed. */
+int sige_geom_derive(const sige_geom *g, sige_derived *out);
+
+/* Capacity n*nby*nbx of a geometry, or a negative code. Host only. */
+int64_t sige_max_blocks(const sige_geom *g);
+
+/* Step 1 -- change mask (mer.dev notes, section 3; SIGE README, "Overview").
+ *   mask[p] = 1 if some channel of pixel p has |float(a_edit) - float(a_orig)| > thresh,
+ *   the difference taken in IEEE fp32; else 0.  p runs over the n*h*w pixels.
+ *   a_orig, a_edit: [n, h, w, c] in `dtype`, 16-byte aligned.
+ *   mask: uint8 [n, h, w], 4-byte aligned; written completely.
+ *   thresh: finite, >= 0.  NaN differences do not flag a pixel. */
+int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
+                   uint8_t *mask, void *stream);
+
+/* Step 2 -- active block list (mer.dev notes, 3.2: downsample the mask to each
+ * scale and dilate it; SIGE README, "Overview": reduce it to active block indices).
+ *   mask: uint8 [g->n, mask_h, mask_w], nonzero = changed.  mask_h = fy * g->h and
+ *     mask_w = fx * g->w for integers fy, fx >= 1; the mask is OR-pooled by (fy, fx).
+ *   A block is active when a changed pooled pixel lies in its input window
+ *     (clipped to the image); the block grid is then dilated by `dilate_blocks`
+ *     (square element, clipped at the grid edge).  0 <= dilate_blocks <= 16.
+ *   idx: int32 [cap] -- receives the linear indices (n*nby + by)*nbx + bx of the
+ *     active blocks in ascending order; entries at and after *count are not written.
+ *   count: one int32 in device memory; receives the number of active blocks.
+ *   Limits (else SIGE_ERANGE): g->h * ceil(g->w/32) <= 8192, nby*nbx <= 12288.
+ *   c_in/c_out of g are not used. */
+int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
+                     int32_t *idx, int32_t *count, void *stream);
+
+/* Step 3 -- gather (SIGE README, "Overview": collect the active blocks from the
+ * edited activation and stack them along the batch dimension).
+ *   blocks[slot, yy, xx, c] = a_edit[n, by*block*stride - pad + yy, bx*block*stride - pad + xx, c]
+ *   (zero outside the image) for slot < *count, where idx[slot] = (n*nby + by)*nbx + bx.
+ *   a_edit: [n, h, w, c_in];  blocks: [cap, ib, ib, c_in];  both in `dtype`. */
+int sige_gather(const void *a_edit, int dtype, const sige_geom *g, const int32_t *idx, const int32_t *count,
+                void *blocks, void *stream);
+
+/* Step 4 -- convolution of the stacked blocks (SIGE README, "Overview": feed
+ * the stacked blocks to F_l).  A valid k x k conv with the layer's stride on
+ * each block, as an implicit GEMM on the matrix cores:
+ *   out_blocks[slot, py, px, co] = bias[co] + sum_{ky,kx,ci} w[co,ky,kx,ci] * blocks[slot, py*stride+ky, px*stride+kx, ci]
+ *   for slot < *count.  blocks: [cap, ib, ib, c_in]; w_krsc: [c_out, k, k, c_in];
+ *   out_blocks: [cap, block, block, c_out]; bias: fp32 [c_out] or NULL. */
+int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, int dtype, const sige_geom *g,
+                     const int32_t *count, void *out_blocks, void *stream);
+
+/* Step 5 -- scatter (SIGE README, "Overview": scatter the output blocks back
+ * into the cached output of the original image).
+ *   copy_cached = 1: out = cached outside the listed blocks (a copy), and the
+ *     valid pixels of each listed block come from out_blocks.  `out` must not
+ *     overlap `cached`.  idx must be ascending (as sige_reduce_mask writes it).
+ *   copy_cached = 0: only the listed blocks' pixels of `out` are written; the
+ *     caller keeps `out` equal to the cache elsewhere (a persistent buffer).
+ *   Pixels of partial edge blocks beyond (ho, wo) are dropped.
+ *   out_blocks: [cap, block, block, c_out]; cached, out: [n, ho, wo, c_out]. */
+int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *count, const sige_geom *g, int dtype,
+                 const void *cached, void *out, int copy_cached, void *stream);
+
+/* Steps 3-5 fused into one kernel: the input windows of the listed blocks are
+ * staged from a_edit into LDS, convolved on the matrix cores and written
+ * straight into `out`; with copy_cached = 1 the same launch copies `cached`
+ * into `out` outside the listed blocks.  Result as sige_gather ->
+ * sige_conv_blocks -> sige_scatter, without the intermediate block tensors.
+ *   a_edit: [n, h, w, c_in]; w_krsc: [c_out, k, k, c_in]; bias fp32 [c_out] or NULL;
+ *   cached, out: [n, ho, wo, c_out]; idx ascending, count in device memory.
+ *   `out` must overlap neither `a_edit` nor (when copy_cached = 1) `cached`. */
+int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                           const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
+                           int copy_cached, void *stream);
+
+/* Name of a status code (static string). */
+const char *sige_strerror(int code);
+
+/* Message of the calling thread's most recent call: "" when it succeeded. */
+const char *sige_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGE_H */

@@ -1,0 +1,23 @@
+"""Tile-sparse incremental convolution (SIGE hot path) for AMD MI355X (gfx950).
+
+The compute lives in libsige.so (HIP kernels behind the C ABI of
+include/sige.h); this package is the ctypes binding over it.
+"""
+from ._lib import (  # noqa: F401
+    DTYPE_CODE,
+    EXPORTS,
+    Derived,
+    Geom,
+    SigeError,
+    geom,
+    lib,
+    sige_conv_blocks,
+    sige_diff_mask,
+    sige_gather,
+    sige_geom_derive,
+    sige_max_blocks,
+    sige_reduce_mask,
+    sige_scatter,
+    sige_sparse_conv_layer,
+    weight_to_krsc,
+)

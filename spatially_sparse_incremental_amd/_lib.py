@@ -1,0 +1,213 @@
+"""ctypes binding of libsige.so -- argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/sige.h) and
+passes torch tensors' device pointers plus the current HIP stream.  Every step
+of the computation runs in the HIP kernels; there is no other code path, and a
+missing library raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsige.so")
+
+SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERANGE = 0, -1, -2, -3, -4, -5, -6
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_gather",
+           "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_strerror", "sige_last_error")
+
+
+class SigeError(RuntimeError):
+    def __init__(self, code: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {msg} (code {code})")
+        self.code = code
+
+
+class Geom(ctypes.Structure):
+    """sige_geom: input [n, h, w, c_in], k x k kernel, stride, pad, output block edge."""
+    _fields_ = [(f, ctypes.c_int32) for f in ("n", "h", "w", "c_in", "c_out", "k", "stride", "pad", "block")]
+
+
+class Derived(ctypes.Structure):
+    _fields_ = [("ho", ctypes.c_int32), ("wo", ctypes.c_int32), ("nby", ctypes.c_int32), ("nbx", ctypes.c_int32),
+                ("ib", ctypes.c_int32), ("cap", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libsige.so (built in-tree by `python -m spatially_sparse_incremental_amd.build`)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m spatially_sparse_incremental_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        V, I, P = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(Geom)
+        L.sige_geom_derive.argtypes = [P, ctypes.POINTER(Derived)]
+        L.sige_max_blocks.argtypes = [P]
+        L.sige_max_blocks.restype = ctypes.c_int64
+        L.sige_diff_mask.argtypes = [V, V, I, I, I, I, I, ctypes.c_float, V, V]
+        L.sige_reduce_mask.argtypes = [V, I, I, P, I, V, V, V]
+        L.sige_gather.argtypes = [V, I, P, V, V, V, V]
+        L.sige_conv_blocks.argtypes = [V, V, V, I, P, V, V, V]
+        L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
+        L.sige_sparse_conv_layer.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
+        L.sige_strerror.restype = ctypes.c_char_p
+        L.sige_strerror.argtypes = [I]
+        L.sige_last_error.restype = ctypes.c_char_p
+        for f in EXPORTS:
+            if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks"):
+                getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, fn: str):
+    if rc != SIGE_OK:
+        msg = lib().sige_last_error().decode() or lib().sige_strerror(rc).decode()
+        raise SigeError(rc, fn, msg)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _dt(t):
+    try:
+        return DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise SigeError(SIGE_EDTYPE, "dtype", f"unsupported dtype {t.dtype}") from None
+
+
+# ---------------------------------------------------------------------------
+def geom(n, h, w, c_in, c_out, k=3, stride=1, pad=1, block=6) -> Geom:
+    return Geom(n, h, w, c_in, c_out, k, stride, pad, block)
+
+
+def sige_geom_derive(g: Geom) -> Derived:
+    d = Derived()
+    _check(lib().sige_geom_derive(ctypes.byref(g), ctypes.byref(d)), "sige_geom_derive")
+    return d
+
+
+def sige_max_blocks(g: Geom) -> int:
+    v = lib().sige_max_blocks(ctypes.byref(g))
+    if v < 0:
+        _check(int(v), "sige_max_blocks")
+    return int(v)
+
+
+def sige_diff_mask(a_orig, a_edit, thresh=1e-6, mask=None, stream=None):
+    """uint8 [n, h, w] change mask of two NHWC activations."""
+    _dev(a_orig, a_edit, mask)
+    if a_orig.shape != a_edit.shape or a_orig.dtype != a_edit.dtype or a_orig.dim() != 4:
+        raise ValueError("a_orig and a_edit must be NHWC tensors of one shape and dtype")
+    n, h, w, c = a_orig.shape
+    if mask is None:
+        mask = torch.empty((n, h, w), dtype=torch.uint8, device=a_orig.device)
+    rc = lib().sige_diff_mask(_p(a_orig), _p(a_edit), _dt(a_orig), n, h, w, c, ctypes.c_float(thresh), _p(mask),
+                              _stream(stream))
+    _check(rc, "sige_diff_mask")
+    return mask
+
+
+def sige_reduce_mask(mask, g: Geom, dilate_blocks=1, idx=None, count=None, stream=None):
+    """(idx int32 [cap], count int32 [1]) on the device; idx[:count] are the active blocks, ascending."""
+    if mask.dim() == 2:
+        mask = mask.unsqueeze(0)
+    _dev(mask, idx, count)
+    cap = sige_max_blocks(g)
+    dev = mask.device
+    if idx is None:
+        idx = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((1,), dtype=torch.int32, device=dev)
+    rc = lib().sige_reduce_mask(_p(mask), mask.shape[-2], mask.shape[-1], ctypes.byref(g), dilate_blocks, _p(idx),
+                                _p(count), _stream(stream))
+    _check(rc, "sige_reduce_mask")
+    return idx, count
+
+
+def sige_gather(a_edit, g: Geom, idx, count, blocks=None, stream=None):
+    """[cap, ib, ib, c_in]: input windows of the listed blocks (slots < count)."""
+    _dev(a_edit, idx, count, blocks)
+    d = sige_geom_derive(g)
+    if blocks is None:
+        blocks = torch.empty((max(d.cap, 1), d.ib, d.ib, g.c_in), dtype=a_edit.dtype, device=a_edit.device)
+    rc = lib().sige_gather(_p(a_edit), _dt(a_edit), ctypes.byref(g), _p(idx), _p(count), _p(blocks),
+                           _stream(stream))
+    _check(rc, "sige_gather")
+    return blocks
+
+
+def sige_conv_blocks(blocks, w_krsc, bias, g: Geom, count, out_blocks=None, stream=None):
+    """[cap, b, b, c_out]: conv of each stacked block (slots < count)."""
+    _dev(blocks, w_krsc, bias, count, out_blocks)
+    if w_krsc.dtype != blocks.dtype or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("weights must match the activation dtype; bias must be fp32")
+    d = sige_geom_derive(g)
+    if out_blocks is None:
+        out_blocks = torch.empty((max(d.cap, 1), g.block, g.block, g.c_out), dtype=blocks.dtype,
+                                 device=blocks.device)
+    rc = lib().sige_conv_blocks(_p(blocks), _p(w_krsc), _p(bias), _dt(blocks), ctypes.byref(g), _p(count),
+                                _p(out_blocks), _stream(stream))
+    _check(rc, "sige_conv_blocks")
+    return out_blocks
+
+
+def sige_scatter(out_blocks, idx, count, g: Geom, cached, out=None, copy_cached=True, stream=None):
+    """[n, ho, wo, c_out]: cached output with the listed blocks overwritten."""
+    _dev(out_blocks, idx, count, cached, out)
+    d = sige_geom_derive(g)
+    if out is None:
+        if not copy_cached:
+            raise ValueError("copy_cached=False needs a persistent `out`")
+        out = torch.empty((g.n, d.ho, d.wo, g.c_out), dtype=out_blocks.dtype, device=out_blocks.device)
+    rc = lib().sige_scatter(_p(out_blocks), _p(idx), _p(count), ctypes.byref(g), _dt(out_blocks),
+                            _p(cached if copy_cached else None), _p(out), int(bool(copy_cached)), _stream(stream))
+    _check(rc, "sige_scatter")
+    return out
+
+
+def sige_sparse_conv_layer(a_edit, w_krsc, bias, cached, idx, count, g: Geom, out=None, copy_cached=True,
+                           stream=None):
+    """Fused gather + conv + scatter into `out` (NHWC [n, ho, wo, c_out])."""
+    _dev(a_edit, w_krsc, bias, cached, idx, count, out)
+    if w_krsc.dtype != a_edit.dtype or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("weights must match the activation dtype; bias must be fp32")
+    d = sige_geom_derive(g)
+    if out is None:
+        if not copy_cached:
+            raise ValueError("copy_cached=False needs a persistent `out`")
+        out = torch.empty((g.n, d.ho, d.wo, g.c_out), dtype=a_edit.dtype, device=a_edit.device)
+    rc = lib().sige_sparse_conv_layer(_p(a_edit), _p(w_krsc), _p(bias), _p(cached if copy_cached else None),
+                                      _p(idx), _p(count), _dt(a_edit), ctypes.byref(g), _p(out),
+                                      int(bool(copy_cached)), _stream(stream))
+    _check(rc, "sige_sparse_conv_layer")
+    return out
+
+
+def weight_to_krsc(w_oihw: torch.Tensor) -> torch.Tensor:
+    """Repack PyTorch OIHW weights to the library's KRSC layout (once, at load time)."""
+    return w_oihw.permute(0, 2, 3, 1).contiguous()

@@ -1,0 +1,355 @@
+// sige_api.hip -- the C ABI of libsige.so: argument checks, status codes,
+// launch configuration.  Every check runs on the host before anything is
+// enqueued; the kernels live in kernels_mask.hip and kernels_conv.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "sige.h"
+#include "sige_internal.h"
+
+using sige::ConvCfg;
+using sige::Geo;
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dtype_ok(int dt) { return dt == SIGE_F32 || dt == SIGE_BF16 || dt == SIGE_F16; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+int derive(const sige_geom *gp, Geo *g) {
+    if (!gp) return fail(SIGE_EINVAL, "geometry pointer is NULL");
+    const sige_geom &q = *gp;
+    if (q.n < 1 || q.h < 1 || q.w < 1 || q.c_in < 1 || q.c_out < 1)
+        return fail(SIGE_EINVAL, "n, h, w, c_in, c_out must be >= 1 (got %d, %d, %d, %d, %d)", q.n, q.h, q.w,
+                    q.c_in, q.c_out);
+    if (q.k < 1 || q.k > 7) return fail(SIGE_EINVAL, "kernel size k=%d outside [1, 7]", q.k);
+    if (q.stride < 1 || q.stride > 4) return fail(SIGE_EINVAL, "stride=%d outside [1, 4]", q.stride);
+    if (q.pad < 0 || q.pad >= q.k) return fail(SIGE_EINVAL, "pad=%d outside [0, k-1]", q.pad);
+    if (q.block < 1 || q.block > 64) return fail(SIGE_EINVAL, "block=%d outside [1, 64]", q.block);
+    if (q.h + 2 * q.pad < q.k || q.w + 2 * q.pad < q.k)
+        return fail(SIGE_EINVAL, "padded input %dx%d smaller than the kernel", q.h + 2 * q.pad, q.w + 2 * q.pad);
+    Geo r;
+    r.n = q.n, r.h = q.h, r.w = q.w, r.cin = q.c_in, r.cout = q.c_out;
+    r.k = q.k, r.s = q.stride, r.p = q.pad, r.b = q.block;
+    r.ho = (q.h + 2 * q.pad - q.k) / q.stride + 1;
+    r.wo = (q.w + 2 * q.pad - q.k) / q.stride + 1;
+    r.nby = (r.ho + q.block - 1) / q.block;
+    r.nbx = (r.wo + q.block - 1) / q.block;
+    r.ib = (q.block - 1) * q.stride + q.k;
+    if (r.ib > 64) return fail(SIGE_EINVAL, "input window %d exceeds 64", r.ib);
+    const int64_t cap = (int64_t)q.n * r.nby * r.nbx;
+    if (cap > 0x7FFFFFFFLL) return fail(SIGE_ERANGE, "block capacity %lld exceeds int32", (long long)cap);
+    const int64_t in_elems = (int64_t)q.n * q.h * q.w * q.c_in, out_elems = (int64_t)q.n * r.ho * r.wo * q.c_out;
+    if (in_elems > (1LL << 40) || out_elems > (1LL << 40)) return fail(SIGE_ERANGE, "tensor too large");
+    r.cap = (int)cap;
+    *g = r;
+    return SIGE_OK;
+}
+
+int channel_rows_ok(int dt, int c, const char *what) {
+    const int es = sige::elem_bytes(dt);
+    if ((c * es) % 16)
+        return fail(SIGE_EALIGN, "%s=%d: a channel row of %d bytes is not a multiple of 16", what, c, c * es);
+    return SIGE_OK;
+}
+
+int device_ready() {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+        (void)hipGetLastError();
+        return fail(SIGE_ENODEV, "no HIP device available");
+    }
+    return SIGE_OK;
+}
+
+int finish(hipError_t e, const char *what, hipStream_t st) {
+    if (e != hipSuccess) return fail(SIGE_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    static int debug_sync = -1;
+    if (debug_sync < 0) {
+        const char *v = getenv("SIGE_DEBUG_SYNC");
+        debug_sync = (v && v[0] == '1') ? 1 : 0;
+    }
+    if (debug_sync) {
+        e = hipStreamSynchronize(st);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return fail(SIGE_EHIP, "%s failed on the device: %s", what, hipGetErrorString(e));
+    }
+    g_msg[0] = 0;
+    return SIGE_OK;
+}
+
+constexpr int kStaticLds = 1024;  // the conv kernel's static LDS (block list, copy flags), rounded up
+
+// LDS per workgroup the current device allows (160 KiB on gfx950).
+int lds_limit() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) {
+        (void)hipGetLastError();
+        return 64 * 1024;
+    }
+    return v;
+}
+
+// Copy units: segments of one output row, about 32 KiB each (at most 254
+// blocks wide, which bounds the per-unit block flags in LDS).
+void copy_plan(const Geo &g, int es, int *xw_out, int *units_out) {
+    int xw = (32 * 1024) / (g.cout * es);
+    if (xw < 1) xw = 1;
+    if (xw > 254 * g.b) xw = 254 * g.b;
+    if (xw > g.wo) xw = g.wo;
+    *xw_out = xw;
+    *units_out = g.n * g.ho * ((g.wo + xw - 1) / xw);
+}
+
+// Tile configuration of the implicit GEMM (see kernels_conv.hip).
+int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
+    ConvCfg c{};
+    c.mt = 4;
+    c.nt = 2;
+    const int BM = 16 * c.mt, BN = 16 * c.nt;
+    const int es = sige::elem_bytes(dt);
+    const int ks = dt == SIGE_F32 ? 16 : 32;
+    const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
+    int ns = (BM - 1) / b2 + 2;
+    if (ns > BM) ns = BM;
+    if (ns > g.cap) ns = g.cap;
+    c.ns_max = ns;
+    const int part = 4 * BM * (BN + 4) * 4;
+    const int cin_r = (g.cin + ks - 1) / ks * ks;
+    // Largest channel chunk within 64 KiB (two workgroups per CU); failing that,
+    // the largest within the device's per-workgroup LDS.
+    int best = 0;
+    for (int pass = 0; pass < 2 && !best; ++pass) {
+        const long budget = (pass == 0 ? 64 * 1024 : (long)lds_limit()) - kStaticLds;
+        for (int ck = (cin_r < 512 ? cin_r : 512); ck >= ks; ck -= ks) {
+            const int apix = ck * es + 16, brow = k2 * ck * es + 16;
+            const long a_bytes = (long)ns * ib2 * apix, lds = a_bytes + (long)BN * brow;
+            const long need = lds > part ? lds : part;
+            if (need <= budget) {
+                best = ck;
+                break;
+            }
+        }
+    }
+    if (!best)
+        return fail(SIGE_ERANGE, "staged windows (%d slots of %dx%d) and weights (k=%d) do not fit in LDS", ns, g.ib,
+                    g.ib, g.k);
+    c.ck = best;
+    c.a_pix_stride = best * es + 16;
+    c.b_row_stride = k2 * best * es + 16;
+    c.a_bytes = ns * ib2 * c.a_pix_stride;
+    {
+        const int lds = c.a_bytes + BN * c.b_row_stride;
+        c.lds_bytes = lds > part ? lds : part;
+    }
+    const long mt_cap = ((long)g.cap * b2 + BM - 1) / BM;
+    const long tiles_cap = mt_cap * ((g.cout + BN - 1) / BN);
+    long grid = tiles_cap < 512 ? tiles_cap : 512;
+    if (grid > 8) grid = grid / 8 * 8;  // keep tile t on XCD t % 8 across persistent passes
+    c.compute_grid = (int)(grid > 0 ? grid : 1);
+    c.copy_xw = 0;
+    c.copy_units = 0;
+    if (fused && copy) copy_plan(g, es, &c.copy_xw, &c.copy_units);
+    *out = c;
+    return SIGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sige_strerror(int code) {
+    switch (code) {
+    case SIGE_OK: return "SIGE_OK";
+    case SIGE_EINVAL: return "SIGE_EINVAL: invalid argument";
+    case SIGE_EDTYPE: return "SIGE_EDTYPE: unsupported dtype";
+    case SIGE_EALIGN: return "SIGE_EALIGN: misaligned pointer or channel row";
+    case SIGE_EHIP: return "SIGE_EHIP: HIP runtime error";
+    case SIGE_ENODEV: return "SIGE_ENODEV: no GPU";
+    case SIGE_ERANGE: return "SIGE_ERANGE: size beyond a kernel limit";
+    default: return "unknown status code";
+    }
+}
+
+const char *sige_last_error(void) { return g_msg; }
+
+int sige_geom_derive(const sige_geom *g, sige_derived *out) {
+    Geo d;
+    const int rc = derive(g, &d);
+    if (rc) return rc;
+    if (!out) return fail(SIGE_EINVAL, "output pointer is NULL");
+    out->ho = d.ho;
+    out->wo = d.wo;
+    out->nby = d.nby;
+    out->nbx = d.nbx;
+    out->ib = d.ib;
+    out->cap = d.cap;
+    g_msg[0] = 0;
+    return SIGE_OK;
+}
+
+int64_t sige_max_blocks(const sige_geom *g) {
+    Geo d;
+    const int rc = derive(g, &d);
+    if (rc) return rc;
+    g_msg[0] = 0;
+    return (int64_t)d.cap;
+}
+
+int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
+                   uint8_t *mask, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    if (n < 0 || h < 0 || w < 0 || c < 1) return fail(SIGE_EINVAL, "bad shape n=%d h=%d w=%d c=%d", n, h, w, c);
+    if (!(thresh >= 0.0f) || thresh > 3.0e38f) return fail(SIGE_EINVAL, "threshold must be finite and >= 0");
+    const long npix = (long)n * h * w;
+    if (npix == 0) {
+        g_msg[0] = 0;
+        return SIGE_OK;
+    }
+    if (!a_orig || !a_edit || !mask) return fail(SIGE_EINVAL, "NULL tensor pointer");
+    int rc = channel_rows_ok(dtype, c, "c");
+    if (rc) return rc;
+    if (!aligned(a_orig, 16) || !aligned(a_edit, 16)) return fail(SIGE_EALIGN, "activations must be 16-byte aligned");
+    if (!aligned(mask, 4)) return fail(SIGE_EALIGN, "mask must be 4-byte aligned");
+    const size_t bytes = (size_t)npix * c * sige::elem_bytes(dtype);
+    if (overlap(mask, (size_t)npix, a_orig, bytes) || overlap(mask, (size_t)npix, a_edit, bytes))
+        return fail(SIGE_EINVAL, "mask overlaps an input");
+    if ((rc = device_ready())) return rc;
+    const int vpp = c * sige::elem_bytes(dtype) / 16;
+    return finish(sige::launch_diff(dtype, a_orig, a_edit, npix, vpp, thresh, mask, (hipStream_t)stream),
+                  "sige_diff_mask", (hipStream_t)stream);
+}
+
+int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,
+                     int32_t *idx, int32_t *count, void *stream) {
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!mask || !idx || !count) return fail(SIGE_EINVAL, "NULL pointer");
+    if (mask_h < g.h || mask_w < g.w || mask_h % g.h || mask_w % g.w)
+        return fail(SIGE_EINVAL, "mask %dx%d is not an integer multiple of the conv input %dx%d", mask_h, mask_w,
+                    g.h, g.w);
+    if (dilate_blocks < 0 || dilate_blocks > 16) return fail(SIGE_EINVAL, "dilate_blocks=%d outside [0, 16]", dilate_blocks);
+    if ((long)g.h * ((g.w + 31) / 32) > sige::kReduceBitsWords)
+        return fail(SIGE_ERANGE, "conv input %dx%d exceeds the reduce limit", g.h, g.w);
+    if ((long)g.nby * g.nbx > sige::kReduceMaxBlocks)
+        return fail(SIGE_ERANGE, "block grid %dx%d exceeds the reduce limit", g.nby, g.nbx);
+    if (!aligned(idx, 4) || !aligned(count, 4)) return fail(SIGE_EALIGN, "idx/count must be 4-byte aligned");
+    const size_t mbytes = (size_t)g.n * mask_h * mask_w;
+    if (overlap(idx, (size_t)g.cap * 4, mask, mbytes) || overlap(count, 4, mask, mbytes) ||
+        overlap(count, 4, idx, (size_t)g.cap * 4))
+        return fail(SIGE_EINVAL, "idx, count and mask must not overlap");
+    if ((rc = device_ready())) return rc;
+    const int vec16 = (mask_w % 16 == 0) && aligned(mask, 16);
+    return finish(sige::launch_reduce(mask, mask_h, mask_w, g, dilate_blocks, vec16, idx, count, (hipStream_t)stream),
+                  "sige_reduce_mask", (hipStream_t)stream);
+}
+
+int sige_gather(const void *a_edit, int dtype, const sige_geom *gp, const int32_t *idx, const int32_t *count,
+                void *blocks, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!a_edit || !idx || !count || !blocks) return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in"))) return rc;
+    if (!aligned(a_edit, 16) || !aligned(blocks, 16)) return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    if (overlap(blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
+        return fail(SIGE_EINVAL, "blocks overlap the input");
+    if ((rc = device_ready())) return rc;
+    return finish(sige::launch_gather(a_edit, dtype, g, idx, count, blocks, (hipStream_t)stream), "sige_gather",
+                  (hipStream_t)stream);
+}
+
+int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, int dtype, const sige_geom *gp,
+                     const int32_t *count, void *out_blocks, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!blocks || !w_krsc || !count || !out_blocks) return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(blocks, 16) || !aligned(w_krsc, 16) || !aligned(out_blocks, 16))
+        return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    if (overlap(out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es, blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es))
+        return fail(SIGE_EINVAL, "out_blocks overlaps blocks");
+    ConvCfg cfg;
+    if ((rc = choose_conv(g, dtype, 0, 0, &cfg))) return rc;
+    if ((rc = device_ready())) return rc;
+    return finish(sige::launch_conv(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, g, cfg,
+                                    (hipStream_t)stream),
+                  "sige_conv_blocks", (hipStream_t)stream);
+}
+
+int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *count, const sige_geom *gp, int dtype,
+                 const void *cached, void *out, int copy_cached, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!out_blocks || !idx || !count || !out || (copy_cached && !cached)) return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(out_blocks, 16) || !aligned(out, 16) || (copy_cached && !aligned(cached, 16)))
+        return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
+    if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    if (overlap(out, obytes, out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es))
+        return fail(SIGE_EINVAL, "out overlaps out_blocks");
+    if ((rc = device_ready())) return rc;
+    int xw = 0, units = 0;
+    copy_plan(g, es, &xw, &units);
+    const int sgrid = g.cap < 1024 ? g.cap : 1024;
+    return finish(sige::launch_scatter(dtype, out_blocks, idx, count, g, cached, out, copy_cached ? 1 : 0, sgrid, xw,
+                                       units, (hipStream_t)stream),
+                  "sige_scatter", (hipStream_t)stream);
+}
+
+int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                           const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                           int copy_cached, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!a_edit || !w_krsc || !idx || !count || !out || (copy_cached && !cached))
+        return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || (copy_cached && !aligned(cached, 16)))
+        return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
+    if (overlap(out, obytes, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
+        return fail(SIGE_EINVAL, "out overlaps a_edit");
+    if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    ConvCfg cfg;
+    if ((rc = choose_conv(g, dtype, 1, copy_cached, &cfg))) return rc;
+    if ((rc = device_ready())) return rc;
+    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
+                                    g, cfg, (hipStream_t)stream),
+                  "sige_sparse_conv_layer", (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+"""Shared helpers of the GPU parity tests: inputs from `synth`, expected values
+from `oracle` (CPU), results from the HIP library through its binding."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import spatially_sparse_incremental_amd as ssi
+import synth
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+# max |gpu - oracle| <= TOL * max |oracle| over the recomputed pixels
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 2e-2}
+
+
+def rand(shape, dtype, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(dtype)
+
+
+def bits(t):
+    """Raw storage of a tensor, for bit-exact comparison."""
+    return t.contiguous().view(torch.uint8)
+
+
+def layer_inputs(n, h, w, cin, cout, k, dt, seed, mask, std=None):
+    """A_o, A_e (differs exactly on `mask`), weight OIHW, bias, on the CPU."""
+    a_o = rand((n, h, w, cin), dt, seed)
+    a_e = synth.make_edit(a_o, mask, "replace", seed + 1)
+    std = std if std is not None else (2.0 / (cin * k * k)) ** 0.5
+    wt = rand((cout, cin, k, k), dt, seed + 2, std)
+    bias = rand((cout,), torch.float32, seed + 3, 0.01)
+    return a_o, a_e, wt, bias
+
+
+def random_mask(n, h, w, frac, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.random((n, h, w)) < frac).astype(np.uint8)
+
+
+def gpu(t):
+    return t.to("cuda") if t is not None else None
+
+
+def active_pixels(act, b, ho, wo):
+    """bool [n, ho, wo, 1]: output pixel lies in an active block."""
+    up = act.bool().repeat_interleave(b, 1).repeat_interleave(b, 2)[:, :ho, :wo]
+    return up[..., None]
+
+
+def assert_close(got, ref64, dt, sel=None, what=""):
+    """max |got - ref| <= TOL[dt] * max |ref| over the selected elements."""
+    g = got.double()
+    if sel is not None:
+        sel = sel.expand_as(g)
+        g, ref64 = g[sel], ref64[sel]
+    if g.numel() == 0:
+        return 0.0
+    scale = ref64.abs().max().item()
+    err = (g - ref64).abs().max().item()
+    assert err <= TOL[dt] * max(scale, 1e-30), f"{what}: max err {err:.3e} vs scale {scale:.3e} (tol {TOL[dt]})"
+    return err / max(scale, 1e-30)
+
+
+def run_layer_gpu(a_o, a_e, wt, bias, cache, g, dilate, tau=1e-6, fused=True, copy=True):
+    """diff -> reduce -> (fused | gather+conv+scatter) on the GPU; returns CPU tensors."""
+    ao, ae = gpu(a_o), gpu(a_e)
+    wk = gpu(ssi.weight_to_krsc(wt))
+    bs = gpu(bias)
+    cg = gpu(cache)
+    mask = ssi.sige_diff_mask(ao, ae, tau)
+    idx, count = ssi.sige_reduce_mask(mask, g, dilate)
+    if fused:
+        out = ssi.sige_sparse_conv_layer(ae, wk, bs, cg, idx, count, g, copy_cached=True) if copy else None
+        if not copy:
+            out = cg.clone()
+            ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx, count, g, out=out, copy_cached=False)
+        blocks = ob = None
+    else:
+        blocks = ssi.sige_gather(ae, g, idx, count)
+        ob = ssi.sige_conv_blocks(blocks, wk, bs, g, count)
+        if copy:
+            out = ssi.sige_scatter(ob, idx, count, g, cg)
+        else:
+            out = cg.clone()
+            ssi.sige_scatter(ob, idx, count, g, None, out=out, copy_cached=False)
+    torch.cuda.synchronize()
+    cnt = int(count.item())
+    res = dict(mask=mask.cpu(), idx=idx[:cnt].cpu(), count=cnt, out=out.cpu())
+    if blocks is not None:
+        res["blocks"] = blocks[:cnt].cpu()
+        res["out_blocks"] = ob[:cnt].cpu()
+    return res
+
+
+def run_layer_oracle(a_o, a_e, wt, bias, cache, k, s, p, b, dilate, tau=1e-6):
+    mask = oracle.diff_mask(a_o, a_e, tau)
+    n, h, w, _ = a_o.shape
+    act = oracle.block_activity(mask, h, w, k, s, p, b, dilate)
+    idx = oracle.index_list(act)
+    out64 = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, act, cache, out_f64=True)
+    return dict(mask=mask, act=act, idx=idx, out64=out64)

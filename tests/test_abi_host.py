@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (no GPU work): exports, geometry, argument validation.
+
+Pointer arguments here are fake addresses; every call is rejected on the host
+before anything is enqueued, so nothing dereferences them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+import spatially_sparse_incremental_amd as ssi
+from spatially_sparse_incremental_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sige.h")
+
+EINVAL, EDTYPE, EALIGN, ENODEV, ERANGE = L.SIGE_EINVAL, L.SIGE_EDTYPE, L.SIGE_EALIGN, L.SIGE_ENODEV, L.SIGE_ERANGE
+A = 0x7F0000000000  # fake, 256-byte aligned device addresses, far apart
+B = A + (1 << 36)
+C = A + (2 << 36)
+D = A + (3 << 36)
+E = A + (4 << 36)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libsige.so not built")
+    return L.lib()
+
+
+def _g(n=1, h=256, w=256, ci=128, co=128, k=3, s=1, p=1, b=6):
+    return L.Geom(n, h, w, ci, co, k, s, p, b)
+
+
+def _v(x):
+    return ctypes.c_void_p(x)
+
+
+def test_every_declared_function_is_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(sige_\w+)\s*\(", text, re.M))
+    assert declared == set(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("geom", [(256, 256, 3, 1, 1, 6), (13, 17, 3, 2, 1, 3), (64, 64, 3, 1, 1, 8),
+                                  (16, 16, 1, 1, 0, 2), (11, 14, 5, 1, 2, 3), (32, 64, 3, 1, 1, 4)])
+def test_geometry_matches_oracle(lib, geom):
+    h, w, k, s, p, b = geom
+    d = ssi.sige_geom_derive(_g(2, h, w, 8, 8, k, s, p, b))
+    assert (d.ho, d.wo, d.nby, d.nbx, d.ib) == oracle.geometry(h, w, k, s, p, b)
+    assert d.cap == 2 * d.nby * d.nbx == ssi.sige_max_blocks(_g(2, h, w, 8, 8, k, s, p, b))
+
+
+@pytest.mark.parametrize("bad", [dict(n=0), dict(k=0), dict(k=8), dict(s=0), dict(p=3), dict(b=0), dict(b=65),
+                                 dict(h=1, p=0), dict(b=40, s=2)])
+def test_bad_geometry_is_einval(lib, bad):
+    kw = dict(n=1, h=64, w=64, ci=8, co=8, k=3, s=1, p=1, b=6)
+    kw.update(bad)
+    with pytest.raises(ssi.SigeError) as e:
+        ssi.sige_geom_derive(_g(**kw))
+    assert e.value.code == EINVAL
+    assert ssi.sige_max_blocks.__name__  # message path exercised above
+
+
+def test_diff_validation(lib):
+    f = lib.sige_diff_mask
+    s = _v(0)
+    assert f(_v(A), _v(B), 7, 1, 4, 4, 8, ctypes.c_float(1e-6), _v(C), s) == EDTYPE
+    assert f(None, _v(B), 1, 1, 4, 4, 8, ctypes.c_float(1e-6), _v(C), s) == EINVAL
+    assert f(_v(A), _v(B), 1, 1, 4, 4, 8, ctypes.c_float(float("nan")), _v(C), s) == EINVAL
+    assert f(_v(A), _v(B), 1, 1, 4, 4, 8, ctypes.c_float(-1.0), _v(C), s) == EINVAL
+    assert f(_v(A), _v(B), 1, 1, 4, 4, 12, ctypes.c_float(1e-6), _v(C), s) == EALIGN  # 24-byte rows
+    assert f(_v(A), _v(B), 0, 1, 4, 4, 6, ctypes.c_float(1e-6), _v(C), s) == EALIGN  # fp32 c % 4
+    assert f(_v(A + 8), _v(B), 1, 1, 4, 4, 8, ctypes.c_float(1e-6), _v(C), s) == EALIGN
+    assert f(_v(A), _v(B), 1, 1, 4, 4, 8, ctypes.c_float(1e-6), _v(C + 2), s) == EALIGN
+    assert f(_v(A), _v(B), 1, 1, 4, 4, 8, ctypes.c_float(1e-6), _v(A + 64), s) == EINVAL  # mask inside a_orig
+    assert f(_v(A), _v(B), 1, 1, 4, 4, 12, ctypes.c_float(1e-6), _v(C), s) == EALIGN
+    assert b"multiple of 16" in lib.sige_last_error()
+    assert f(None, None, 1, 0, 4, 4, 8, ctypes.c_float(1e-6), None, s) == 0  # empty: nothing to do
+    assert lib.sige_last_error() == b""
+
+
+def test_reduce_validation(lib):
+    f = lib.sige_reduce_mask
+    s = _v(0)
+    g = _g()
+    assert f(None, 256, 256, ctypes.byref(g), 1, _v(B), _v(C), s) == EINVAL
+    assert f(_v(A), 300, 256, ctypes.byref(g), 1, _v(B), _v(C), s) == EINVAL  # not an integer multiple
+    assert f(_v(A), 128, 128, ctypes.byref(g), 1, _v(B), _v(C), s) == EINVAL  # coarser than the input
+    assert f(_v(A), 256, 256, ctypes.byref(g), -1, _v(B), _v(C), s) == EINVAL
+    assert f(_v(A), 256, 256, ctypes.byref(g), 17, _v(B), _v(C), s) == EINVAL
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B + 2), _v(C), s) == EALIGN
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(A + 128), _v(C), s) == EINVAL  # idx inside mask
+    big = _g(h=1024, w=1024, b=8)  # 1024 * 32 words > 8192
+    assert f(_v(A), 1024, 1024, ctypes.byref(big), 1, _v(B), _v(C), s) == ERANGE
+    grid = _g(h=512, w=512, b=4)  # 128 x 128 blocks > 12288
+    assert f(_v(A), 512, 512, ctypes.byref(grid), 1, _v(B), _v(C), s) == ERANGE
+
+
+def test_conv_step_validation(lib):
+    s = _v(0)
+    g = _g()
+    assert lib.sige_gather(_v(A), 3, ctypes.byref(g), _v(B), _v(C), _v(D), s) == EDTYPE
+    assert lib.sige_gather(_v(A), 1, ctypes.byref(g), None, _v(C), _v(D), s) == EINVAL
+    assert lib.sige_gather(_v(A + 4), 1, ctypes.byref(g), _v(B), _v(C), _v(D), s) == EALIGN
+    assert lib.sige_conv_blocks(_v(A), _v(B), None, 1, ctypes.byref(g), _v(C), _v(A + 32), s) == EINVAL  # overlap
+    assert lib.sige_conv_blocks(_v(A), _v(B), _v(E + 2), 1, ctypes.byref(g), _v(C), _v(D), s) == EALIGN
+    odd = _g(ci=12)
+    assert lib.sige_conv_blocks(_v(A), _v(B), None, 1, ctypes.byref(odd), _v(C), _v(D), s) == EALIGN
+    assert lib.sige_scatter(_v(A), _v(B), _v(C), ctypes.byref(g), 1, _v(D), _v(D), 1, s) == EINVAL  # out == cached
+    assert lib.sige_scatter(_v(A), _v(B), _v(C), ctypes.byref(g), 1, None, _v(D), 1, s) == EINVAL
+    assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g), _v(A + 64), 1,
+                                      s) == EINVAL  # out overlaps a_edit
+    assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, None, _v(D), _v(E), 1, ctypes.byref(g), _v(C), 1,
+                                      s) == EINVAL  # copy without a cache
+    huge = _g(h=64, w=64, ci=4096, co=64, k=7, p=3, b=8)  # windows + weights cannot fit in LDS
+    assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(huge), _v(B + (1 << 35)),
+                                      1, s) == ERANGE
+
+
+def test_strerror_names_every_code(lib):
+    for code, name in [(0, b"SIGE_OK"), (EINVAL, b"SIGE_EINVAL"), (EDTYPE, b"SIGE_EDTYPE"), (EALIGN, b"SIGE_EALIGN"),
+                       (L.SIGE_EHIP, b"SIGE_EHIP"), (ENODEV, b"SIGE_ENODEV"), (ERANGE, b"SIGE_ERANGE")]:
+        assert lib.sige_strerror(code).startswith(name)
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(ssi.SigeError) as e:
+        ssi.sige_geom_derive(_g(k=9))
+    assert "k=9" in str(e.value)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-GPU path")
+def test_valid_call_without_gpu_is_enodev(lib):
+    g = _g()
+    assert lib.sige_diff_mask(_v(A), _v(B), 1, 1, 4, 4, 8, ctypes.c_float(1e-6), _v(C), _v(0)) == ENODEV
+    assert lib.sige_reduce_mask(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), _v(0)) == ENODEV
+    assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g),
+                                      _v(E + (1 << 35)), 1, _v(0)) == ENODEV
