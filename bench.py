@@ -1,0 +1,357 @@
+"""Benchmark of the tile-sparse incremental conv hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S] [--no-cpu]
+
+One step is one incremental update of one layer for one edit, on the
+U-Net-shaped workload (3x3 stride-1 conv, bf16 NHWC 1x256x256x128 -> 128,
+6x6 output blocks, block-grid dilation 1, seeded 3-ellipse blob edit covering
+1.2% of the pixels):
+    sige_diff_mask -> sige_reduce_mask -> sige_sparse_conv_layer (copy_cached=1)
+with every input already resident in device memory.  K steps run back to back
+as replays of a HIP graph of 10 captured steps, between two HIP events;
+`value` is the mean time per step in microseconds (lower is better).  The
+latency of one step launched alone (one graph replay, and eager launches from
+Python) is reported beside it.
+
+Prints ONE JSON line on stdout.  Also reported: each kernel's mean duration
+(HIP events around replays of a graph of 20 back-to-back launches of that call
+alone), its algorithmic bytes / flops and its fraction of the MI355X peak; the
+same step launched eagerly from Python; the three-call path; the copy-free
+path; the dense conv on the same GPU (MIOpen through torch, and this library
+with every block active); and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+METRIC = "sparse-conv layer latency & speedup vs dense at 1.2% edit; MFMA util, HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline sample length")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU split of the block list is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import spatially_sparse_incremental_amd as ssi
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = synth.workload("cfg2_unet_bf16")
+    L = wl.layers[0]
+    dt = synth.DTYPES[L.dtype]
+    es = torch.tensor([], dtype=dt).element_size()
+    seed = args.seed
+    shape = synth.edit_shape(wl, seed)
+    mask_np = shape.raster(L.h, L.w)
+    a_o_cpu = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
+    a_e_cpu = synth.make_edit(a_o_cpu, mask_np, wl.edit_kind, seed)
+    w_cpu, b_cpu = synth.make_layer_tensors(L, seed)
+
+    a_o, a_e = a_o_cpu.to(dev), a_e_cpu.to(dev)
+    w_krsc = ssi.weight_to_krsc(w_cpu).to(dev)
+    bias = b_cpu.to(dev)
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    d = ssi.sige_geom_derive(g)
+    cap = d.cap
+
+    # cache = conv(A_o), computed once (untimed) by the library with every block active
+    idx_all = torch.arange(cap, dtype=torch.int32, device=dev)
+    cnt_all = torch.tensor([cap], dtype=torch.int32, device=dev)
+    cache = torch.empty((1, d.ho, d.wo, L.c_out), dtype=dt, device=dev)
+    ssi.sige_sparse_conv_layer(a_o, w_krsc, bias, None, idx_all, cnt_all, g, out=cache, copy_cached=False)
+
+    mask = torch.empty((1, L.h, L.w), dtype=torch.uint8, device=dev)
+    idx = torch.empty((cap,), dtype=torch.int32, device=dev)
+    count = torch.empty((1,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(cache)
+
+    def step(st=None):
+        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask, stream=st)
+        ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count, stream=st)
+        ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g, out=out, copy_cached=True, stream=st)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    active = int(count.item())
+    edit_frac = float(mask_np.mean())
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def capture(fn, n_in):
+        """A HIP graph of n_in back-to-back calls of fn (launches only; no memsets inside)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(n_in):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        return gr
+
+    def graph_time(fn, n_in=20, replays=25):
+        """Mean duration of one fn call: events around `replays` replays of a graph of n_in calls."""
+        gr = capture(fn, n_in)
+        cur = torch.cuda.current_stream()
+        e0, e1 = ev(), ev()
+        e0.record(cur)
+        for _ in range(replays):
+            gr.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n_in * replays) * 1e3  # us
+
+    # ---- timed region: K steps back to back, as replays of a graph of S steps
+    S = 10
+    K = max(S, K // S * S)
+    gsteps = capture(step, S)
+    cur = torch.cuda.current_stream()
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(cur)
+    for _ in range(K // S):
+        gsteps.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / K
+    assert int(count.item()) == active
+    print(f"[bench] step {step_ms * 1e3:.2f} us (graphs of {S} steps), {wall / K * 1e6:.2f} us wall, "
+          f"active blocks {active}", file=sys.stderr, flush=True)
+
+    # one step per graph replay (includes the graph launch)
+    gstep = capture(step, 1)
+    e0, e1 = ev(), ev()
+    e0.record(cur)
+    for _ in range(K):
+        gstep.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    t_single = e0.elapsed_time(e1) / K * 1e3
+
+    # the same step launched eagerly from Python
+    t_eager = None
+    e0, e1 = ev(), ev()
+    e0.record(cur)
+    for _ in range(K):
+        step()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    t_eager = e0.elapsed_time(e1) / K * 1e3
+
+    # ---- per-kernel durations: graphs of 20 back-to-back launches of one call
+    kt = {
+        "diff": graph_time(lambda: ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)),
+        "reduce": graph_time(lambda: ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)),
+        "fused_layer": graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g,
+                                                                     out=out, copy_cached=True)),
+    }
+    print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
+
+    # the step without the cache copy (persistent output buffer)
+    out_persist = cache.clone()
+
+    def step_nocopy():
+        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+        ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+        ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False)
+
+    # the three-call path
+    blocks = torch.empty((cap, d.ib, d.ib, L.c_in), dtype=dt, device=dev)
+    oblocks = torch.empty((cap, L.block, L.block, L.c_out), dtype=dt, device=dev)
+    out3 = torch.empty_like(cache)
+
+    def step_three():
+        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+        ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+        ssi.sige_gather(a_e, g, idx, count, blocks=blocks)
+        ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks)
+        ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)
+
+    t_nocopy = graph_time(step_nocopy, 5, 40)
+    t_three = graph_time(step_three, 5, 40)
+    t_gather = graph_time(lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks))
+    t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks))
+    t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
+    t_fused_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g,
+                                                                   out=out_persist, copy_cached=False))
+    # dense comparators on the same GPU
+    dense_all = torch.empty_like(cache)
+    t_dense_ours = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx_all, cnt_all, g,
+                                                                 out=dense_all, copy_cached=False), 5, 10)
+
+    def timed_eager(fn, reps):
+        for _ in range(min(10, reps)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(cur)
+        for _ in range(reps):
+            fn()
+        b.record(cur)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3  # us
+
+    t_dense_miopen = None
+    try:
+        x_cl = a_e.permute(0, 3, 1, 2)  # NCHW view with channels_last strides
+        w_cl = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
+        with torch.no_grad():
+            t_dense_miopen = timed_eager(lambda: F.conv2d(x_cl, w_cl, bias.to(dt), padding=L.pad), max(20, K // 5))
+    except Exception as exc:  # noqa: BLE001 - report, do not hide
+        print(f"[bench] MIOpen dense conv failed: {exc}", file=sys.stderr)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- algorithmic work (the design doc states these formulas)
+    npix_in, npix_out = L.h * L.w, d.ho * d.wo
+    b2 = L.block * L.block
+    act_pix = int(_active_pixels(idx[:active].cpu().numpy(), d, L.block))
+    w_bytes = L.c_out * L.k * L.k * L.c_in * es
+    diff_bytes = 2 * npix_in * L.c_in * es + npix_in
+    reduce_bytes = npix_in + 4 * active + 4
+    blk_bytes = active * (d.ib * d.ib * L.c_in * es + b2 * L.c_out * es)
+    copy_bytes = 2 * (npix_out - act_pix) * L.c_out * es
+    fused_bytes = blk_bytes + w_bytes + 4 * L.c_out + copy_bytes
+    conv_flops = 2.0 * active * b2 * L.c_in * L.c_out * L.k * L.k
+    dense_flops = 2.0 * npix_out * L.c_in * L.c_out * L.k * L.k
+    peak_tf = PEAK_MFMA_TFLOPS[L.dtype]
+
+    def hbm(nbytes, us):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return dict(us=round(us, 3), bytes=int(nbytes), gbps=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
+
+    kernels = {
+        "diff": hbm(diff_bytes, kt["diff"]),
+        "reduce": dict(us=round(kt["reduce"], 3), bytes=int(reduce_bytes), bound="latency"),
+        "fused_layer": dict(hbm(fused_bytes, kt["fused_layer"]), flops=int(conv_flops),
+                            tflops=round(conv_flops / (kt["fused_layer"] * 1e-6) / 1e12, 2),
+                            frac_mfma=round(conv_flops / (kt["fused_layer"] * 1e-6) / 1e12 / peak_tf, 5)),
+        "fused_layer_nocopy": dict(hbm(blk_bytes + w_bytes + 4 * L.c_out, t_fused_nocopy), flops=int(conv_flops),
+                                   frac_mfma=round(conv_flops / (t_fused_nocopy * 1e-6) / 1e12 / peak_tf, 5)),
+        "gather": hbm(active * d.ib * d.ib * L.c_in * es * 2, t_gather),
+        "conv_blocks": dict(hbm(blk_bytes + w_bytes, t_convb), flops=int(conv_flops),
+                            frac_mfma=round(conv_flops / (t_convb * 1e-6) / 1e12 / peak_tf, 5)),
+        "scatter": hbm(active * b2 * L.c_out * es + act_pix * L.c_out * es + copy_bytes, t_scatter),
+    }
+    dom = max(("diff", "fused_layer"), key=lambda k: kt[k])
+    droof = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": droof["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(droof["gbps"] / PEAK_HBM_GBPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = _cpu_baseline(a_o_cpu, a_e_cpu, w_cpu, b_cpu, cache.cpu(), L, wl.tau, args.cpu_seconds)
+
+    step_us = step_ms * 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(step_us, 3),
+        "unit": "us per incremental layer update (diff + reduce + fused sparse conv)",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(step_ms, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": L.dtype,
+        "data": "synthetic: seeded 3-ellipse blob edit, N(0,1) activations, He-normal weights",
+        "config": {"workload": "unet_256x256x128_bf16_3x3s1_b6_d1_blob1.2pct", "n": 1, "h": L.h, "w": L.w,
+                   "c_in": L.c_in, "c_out": L.c_out, "k": L.k, "stride": L.stride, "block": L.block,
+                   "dilate": L.dilate, "seed": seed, "edit_fraction": round(edit_frac, 5),
+                   "active_blocks": active, "block_capacity": cap},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "comparators": {
+            "dense_conv_miopen_us": None if t_dense_miopen is None else round(t_dense_miopen, 3),
+            "dense_conv_ours_all_blocks_us": round(t_dense_ours, 3),
+            "speedup_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / step_us, 3),
+            "speedup_vs_dense_ours": round(t_dense_ours / step_us, 3),
+            "dense_ours_tflops": round(dense_flops / (t_dense_ours * 1e-6) / 1e12, 1),
+            "step_eager_launch_us": round(t_eager, 3),
+            "step_single_graph_replay_us": round(t_single, 3),
+            "step_no_copy_us": round(t_nocopy, 3),
+            "step_three_call_us": round(t_three, 3),
+            "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
+            "mac_reduction": round(dense_flops / conv_flops, 2) if conv_flops else None,
+            "step_wall_us": round(wall / K * 1e6, 3),
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _active_pixels(idx, d, b):
+    """Output pixels covered by the listed blocks (edge blocks clipped)."""
+    tot = 0
+    for lin in idx.tolist():
+        r = lin % (d.nby * d.nbx)
+        by, bx = r // d.nbx, r % d.nbx
+        tot += min(b, d.ho - by * b) * min(b, d.wo - bx * b)
+    return tot
+
+
+def _cpu_baseline(a_o, a_e, w, bias, cache, L, tau, seconds):
+    """The oracle, as it is, on the host cores: diff + reduce + edited layer output."""
+    import oracle
+
+    def once():
+        m = oracle.diff_mask(a_o, a_e, tau)
+        act = oracle.block_activity(m, L.h, L.w, L.k, L.stride, L.pad, L.block, L.dilate)
+        oracle.index_list(act)
+        oracle.sparse_layer(a_e, w, bias, L.k, L.stride, L.pad, L.block, act, cache)
+
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < seconds and len(times) < 50):
+        t0 = time.perf_counter()
+        once()
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": round(med * 1e6, 1), "unit": "us per incremental layer update", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the full workload (diff + reduce + edited layer incl. cache copy), median of {len(times)} "
+                      f"runs, {len(os.sched_getaffinity(0))} host CPUs visible"}
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,8 @@
  *     once (to nearest, ties to even) into the storage type.
  *   - Tensors read or written in 16-byte vectors must be 16-byte aligned and
  *     their channel rows a multiple of 16 bytes (c % 8 == 0 for 16-bit types,
- *     c % 4 == 0 for fp32); otherwise SIGE_EALIGN.
+ *     c % 4 == 0 for fp32); otherwise SIGE_EALIGN.  Channel rows are at most
+ *     8192 bytes (c <= 4096 for 16-bit types, 2048 for fp32); else SIGE_ERANGE.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it; results are ready when the stream reaches them.
  *   - The number of active blocks stays on the device: `count` points to one
@@ -108,7 +109,9 @@ int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int
  *   idx: int32 [cap] -- receives the linear indices (n*nby + by)*nbx + bx of the
  *     active blocks in ascending order; entries at and after *count are not written.
  *   count: one int32 in device memory; receives the number of active blocks.
- *   Limits (else SIGE_ERANGE): g->h * ceil(g->w/32) <= 8192, nby*nbx <= 12288.
+ *   The idx buffer doubles as scratch: a first launch writes one activity byte per
+ *     block into it, a second launch reads them all before writing the list.
+ *   Limits (else SIGE_ERANGE): g->w <= 8192, n*nby*nbx <= 16384.
  *   c_in/c_out of g are not used. */
 int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
                      int32_t *idx, int32_t *count, void *stream);

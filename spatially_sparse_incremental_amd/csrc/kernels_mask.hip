@@ -95,121 +95,336 @@ hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix
 }
 
 // ---------------------------------------------------------------------------
-// step 2: reduce.  Latency-bound and tiny, so one 1024-thread workgroup does all
-// of it in LDS, which also makes the ascending order free:
-//   a) OR-pool the mask by (fy, fx) into bit rows (32 pooled pixels per word),
-//      reading the mask in 16-byte vectors and merging bits with LDS atomics;
-//   b) window test per block: any set bit in its input window (clipped);
-//   c) dilation, separable: along x into a second array, then along y;
-//   d) compaction 1024 blocks at a time: wave64 __ballot gives each wave's
-//      flags, mbcnt the lane's rank inside the wave, a 16-entry LDS table the
-//      wave offsets; indices are written in ascending order.
+// step 2 for large inputs, in two launches.
+//  k_activity: one workgroup per (image, block row).  It ORs the full-resolution
+//    mask rows under the row's input windows into pooled column bits in LDS
+//    (16-byte mask loads, 8 in flight, bits merged with LDS atomics), then tests
+//    each block's window columns.  The raw activity flags (one byte per block)
+//    go into the caller's idx buffer, which is 4x larger than needed for them.
+//  k_compact: one 1024-thread workgroup.  It reads every flag into LDS first,
+//    then dilates (along x into a second array, then along y) and compacts
+//    1024 blocks at a time: wave64 __ballot gives each wave's flags, mbcnt the
+//    lane's rank, a 16-entry LDS table the wave offsets.  Indices are written
+//    in ascending order over the idx buffer, after all flags were read.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_reduce(const uint8_t *__restrict__ mask, int hm, int wm, int fy, int fx,
-                                                 Geo g, int dil, int vec16, int32_t *__restrict__ idx,
-                                                 int32_t *__restrict__ count) {
-    __shared__ uint32_t bits[kReduceBitsWords];
-    __shared__ uint8_t act[kReduceMaxBlocks];
-    __shared__ uint8_t tmp[kReduceMaxBlocks];
-    __shared__ int wcnt[16];
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+__global__ __launch_bounds__(256) void k_activity(const uint8_t *__restrict__ mask, int hm, int wm, int fy, int fx,
+                                                  Geo g, int vec16, uint8_t *__restrict__ flags) {
+    __shared__ uint32_t colbits[kReduceMaxWidth / 32];
+    constexpr int U = 8;
+    const int tid = threadIdx.x;
+    const int i = blockIdx.x, n = blockIdx.y;
     const int H = g.h, W = g.w, WW = (W + 31) >> 5;
-    const int nblk = g.nby * g.nbx;
     const int bs = g.b * g.s;
-    int running = 0;
-    for (int n = 0; n < g.n; ++n) {
-        for (int i = tid; i < H * WW; i += 1024) bits[i] = 0u;
-        __syncthreads();
-        const uint8_t *m = mask + (size_t)n * hm * wm;
-        if (vec16) {
-            const int vpr = wm >> 4;
-            for (int v = tid; v < hm * vpr; v += 1024) {
-                const int Y = v / vpr, q = v - Y * vpr;
-                const u32x4 d = *(const u32x4 *)(m + (size_t)Y * wm + q * 16);
-                if ((d.x | d.y | d.z | d.w) == 0u) continue;
-                const int yp = Y / fy;
+    for (int q = tid; q < WW; q += 256) colbits[q] = 0u;
+    __syncthreads();
+    const int pr0 = max(0, i * bs - g.p), pr1 = min(H, i * bs - g.p + g.ib);
+    const uint8_t *m = mask + ((size_t)n * hm + (size_t)pr0 * fy) * wm;
+    const int rows = (pr1 - pr0) * fy;
+    if (vec16) {
+        const int vpr = wm >> 4;
+        const int nv = rows * vpr;
+        for (int v0 = tid; v0 < nv; v0 += U * 256) {
+            u32x4 d[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * 256;
+                d[u] = u32x4{0u, 0u, 0u, 0u};
+                if (v < nv) d[u] = *(const u32x4 *)(m + (size_t)(v / vpr) * wm + (v % vpr) * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if ((d[u].x | d[u].y | d[u].z | d[u].w) == 0u) continue;
+                const int q = (v0 + u * 256) % vpr;
                 const int wlo = ((q * 16) / fx) >> 5;
                 uint32_t m0 = 0u, m1 = 0u;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if ((d[i >> 2] >> ((i & 3) * 8)) & 0xFFu) {
-                        const int xp = (q * 16 + i) / fx;
+                for (int b = 0; b < 16; ++b) {
+                    if ((d[u][b >> 2] >> ((b & 3) * 8)) & 0xFFu) {
+                        const int xp = (q * 16 + b) / fx;
                         const uint32_t bit = 1u << (xp & 31);
                         if ((xp >> 5) == wlo) m0 |= bit;
                         else m1 |= bit;
                     }
                 }
-                if (m0) atomicOr(&bits[yp * WW + wlo], m0);
-                if (m1) atomicOr(&bits[yp * WW + wlo + 1], m1);
-            }
-        } else {
-            for (int v = tid; v < hm * wm; v += 1024) {
-                if (!m[v]) continue;
-                const int Y = v / wm, X = v - Y * wm;
-                const int xp = X / fx, yp = Y / fy;
-                atomicOr(&bits[yp * WW + (xp >> 5)], 1u << (xp & 31));
+                if (m0) atomicOr(&colbits[wlo], m0);
+                if (m1) atomicOr(&colbits[wlo + 1], m1);
             }
         }
+    } else {
+        const int nv = rows * wm;
+        for (int v = tid; v < nv; v += 256) {
+            if (!m[v]) continue;
+            const int xp = (v % wm) / fx;
+            atomicOr(&colbits[xp >> 5], 1u << (xp & 31));
+        }
+    }
+    __syncthreads();
+    for (int j = tid; j < g.nbx; j += 256) {
+        const int c0 = max(0, j * bs - g.p), c1 = min(W, j * bs - g.p + g.ib);
+        bool hit = false;
+        if (pr0 < pr1 && c0 < c1) {
+            const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5;
+            for (int wd = w0; wd <= w1 && !hit; ++wd) {
+                const int lo = (wd == w0) ? (c0 & 31) : 0;
+                const int hi = (wd == w1) ? ((c1 - 1) & 31) : 31;
+                const uint32_t sel = (hi == 31 ? 0xFFFFFFFFu : ((1u << (hi + 1)) - 1u)) & ~((1u << lo) - 1u);
+                hit = (colbits[wd] & sel) != 0u;
+            }
+        }
+        flags[((size_t)n * g.nby + i) * g.nbx + j] = hit ? 1 : 0;
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_compact(Geo g, int dil, int32_t *__restrict__ idx,
+                                                  int32_t *__restrict__ count) {
+    __shared__ uint8_t act[kReduceMaxBlocks];
+    __shared__ uint8_t tmp[kReduceMaxBlocks];
+    __shared__ int wcnt[16];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int nblk = g.nby * g.nbx, cap = g.cap;
+    const uint32_t *fw = (const uint32_t *)idx;  // the flags k_activity left in idx
+    for (int q = tid; q < (cap + 3) / 4; q += 1024) {
+        const uint32_t v = fw[q];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (4 * q + b < cap) act[4 * q + b] = (v >> (8 * b)) & 0xFFu;
+    }
+    __syncthreads();
+    for (int q = tid; q < cap; q += 1024) {
+        const int r = q % nblk, i = r / g.nbx, j = r - i * g.nbx;
+        const int rowbase = q - j;
+        uint8_t on = 0;
+        for (int jj = max(0, j - dil); jj <= min(g.nbx - 1, j + dil); ++jj) on |= act[rowbase + jj];
+        tmp[q] = on;
+    }
+    __syncthreads();
+    int running = 0;
+    for (int base = 0; base < cap; base += 1024) {
+        const int q = base + tid;
+        bool on = false;
+        if (q < cap) {
+            const int r = q % nblk, i = r / g.nbx, j = r - i * g.nbx;
+            const int img = q - r;
+            for (int ii = max(0, i - dil); ii <= min(g.nby - 1, i + dil); ++ii) on |= tmp[img + ii * g.nbx + j] != 0;
+        }
+        const unsigned long long bal = __ballot(on);
+        const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+        if (lane == 0) wcnt[wid] = __popcll(bal);
         __syncthreads();
-        for (int q = tid; q < nblk; q += 1024) {
-            const int i = q / g.nbx, j = q - i * g.nbx;
-            const int r0 = max(0, i * bs - g.p), r1 = min(H, i * bs - g.p + g.ib);
-            const int c0 = max(0, j * bs - g.p), c1 = min(W, j * bs - g.p + g.ib);
-            bool hit = false;
-            if (r0 < r1 && c0 < c1) {
-                const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5;
-                for (int r = r0; r < r1 && !hit; ++r) {
-                    for (int wd = w0; wd <= w1; ++wd) {
-                        const int lo = (wd == w0) ? (c0 & 31) : 0;
-                        const int hi = (wd == w1) ? ((c1 - 1) & 31) : 31;
-                        const uint32_t sel = (hi == 31 ? 0xFFFFFFFFu : ((1u << (hi + 1)) - 1u)) & ~((1u << lo) - 1u);
-                        if (bits[r * WW + wd] & sel) {
-                            hit = true;
-                            break;
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int c = wcnt[w];
+            off += (w < wid) ? c : 0;
+            tot += c;
+        }
+        if (on) idx[running + off + rank] = q;
+        running += tot;
+        __syncthreads();
+    }
+    if (tid == 0) *count = running;
+}
+
+// ---------------------------------------------------------------------------
+// step 2 in one launch, for inputs whose pooled mask fits in LDS as bits
+// (h * ceil(w/32) <= kReduceBitsWords): one 1024-thread workgroup.
+//   a) OR-pool the mask into bit rows (32 pooled pixels per word): every
+//      16-byte mask load of a round is in flight before any is used, bits
+//      merged with LDS atomics;
+//   b) when consecutive input windows touch (k >= stride), the dilated
+//      activity of a block is one rectangle test: each block row's rows are
+//      ORed into one bit row, and every block tests its column range while
+//      being compacted (wave64 __ballot + mbcnt ranks, 16-entry LDS table of
+//      wave offsets); otherwise window test, dilation along x, then along y
+//      fused with the compaction.
+// All divisions by launch constants use host-computed multipliers.
+// ---------------------------------------------------------------------------
+struct RedCfg {
+    uint32_t m_vpr;  // fast_div_magic(mask_w / 16)
+    uint32_t m_wm;   // fast_div_magic(mask_w)
+    uint32_t m_fy, m_fx, m_nbx;
+};
+
+__device__ __forceinline__ int fdiv31(int x, uint32_t m) { return (int)(((uint64_t)(uint32_t)x * m) >> 31); }
+
+// Any set bit of bit row `br` in columns [c0, c1)?
+__device__ __forceinline__ bool any_bits(const uint32_t *br, int c0, int c1) {
+    if (c0 >= c1) return false;
+    const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5;
+    const uint32_t lo = ~((1u << (c0 & 31)) - 1u);
+    const uint32_t hi = ((c1 - 1) & 31) == 31 ? 0xFFFFFFFFu : ((1u << (((c1 - 1) & 31) + 1)) - 1u);
+    if (w0 == w1) return (br[w0] & lo & hi) != 0u;
+    uint32_t acc = (br[w0] & lo) | (br[w1] & hi);
+    for (int wd = w0 + 1; wd < w1; ++wd) acc |= br[wd];
+    return acc != 0u;
+}
+
+// Compact one round of 1024 candidate blocks [base, base+1024) in ascending
+// order: wave64 ballot, mbcnt rank, wave offsets through LDS.
+__device__ __forceinline__ int compact_round(bool on, int q_out, int running, int *wcnt, int32_t *idx) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const unsigned long long bal = __ballot(on);
+    const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+    if (lane == 0) wcnt[wid] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int c = wcnt[w];
+        off += (w < wid) ? c : 0;
+        tot += c;
+    }
+    if (on) idx[running + off + rank] = q_out;
+    __syncthreads();
+    return running + tot;
+}
+
+__global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__ mask, int hm, int wm, int fy, int fx,
+                                                     Geo g, int dil, int vec16, RedCfg rc,
+                                                     int32_t *__restrict__ idx, int32_t *__restrict__ count) {
+    __shared__ uint32_t bits[kReduceBitsWords];
+    // per block row: OR of the bit rows under its (dilated) windows; or, when
+    // windows do not touch, the raw and x-dilated block flags
+    __shared__ __attribute__((aligned(16))) uint8_t scratch[2 * kReduceMaxBlocks];
+    __shared__ int wcnt[16];
+    constexpr int U = 8;
+    const int tid = threadIdx.x;
+    const int H = g.h, W = g.w, WW = (W + 31) >> 5;
+    const int nblk = g.nby * g.nbx;
+    const int bs = g.b * g.s;
+    const bool touching = g.ib >= bs;  // consecutive windows overlap or touch
+    int running = 0;
+    for (int n = 0; n < g.n; ++n) {
+        for (int q = tid; q < H * WW; q += 1024) bits[q] = 0u;
+        __syncthreads();
+        const uint8_t *m = mask + (size_t)n * hm * wm;
+        if (vec16) {
+            const int vpr = wm >> 4, nv = hm * vpr;
+            for (int v0 = tid; v0 < nv; v0 += U * 1024) {
+                u32x4 d[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int v = v0 + u * 1024;
+                    d[u] = v < nv ? *(const u32x4 *)(m + (size_t)v * 16) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if ((d[u].x | d[u].y | d[u].z | d[u].w) == 0u) continue;
+                    const int v = v0 + u * 1024;
+                    const int Y = fdiv31(v, rc.m_vpr), q = v - Y * vpr;
+                    const int row = fdiv31(Y, rc.m_fy) * WW;
+                    const int wlo = fdiv31(q * 16, rc.m_fx) >> 5;
+                    uint32_t m0 = 0u, m1 = 0u;
+#pragma unroll
+                    for (int b = 0; b < 16; ++b) {
+                        if ((d[u][b >> 2] >> ((b & 3) * 8)) & 0xFFu) {
+                            const int xp = fx == 1 ? q * 16 + b : fdiv31(q * 16 + b, rc.m_fx);
+                            const uint32_t bit = 1u << (xp & 31);
+                            if ((xp >> 5) == wlo) m0 |= bit;
+                            else m1 |= bit;
                         }
                     }
+                    if (m0) atomicOr(&bits[row + wlo], m0);
+                    if (m1) atomicOr(&bits[row + wlo + 1], m1);
                 }
             }
-            act[q] = hit ? 1 : 0;
-        }
-        __syncthreads();
-        for (int q = tid; q < nblk; q += 1024) {
-            const int i = q / g.nbx, j = q - i * g.nbx;
-            uint8_t on = 0;
-            for (int jj = max(0, j - dil); jj <= min(g.nbx - 1, j + dil); ++jj) on |= act[i * g.nbx + jj];
-            tmp[q] = on;
-        }
-        __syncthreads();
-        for (int base = 0; base < nblk; base += 1024) {
-            const int q = base + tid;
-            bool on = false;
-            if (q < nblk) {
-                const int i = q / g.nbx, j = q - i * g.nbx;
-                for (int ii = max(0, i - dil); ii <= min(g.nby - 1, i + dil); ++ii) on |= tmp[ii * g.nbx + j] != 0;
-            }
-            const unsigned long long bal = __ballot(on);
-            const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-            if (lane == 0) wcnt[wid] = __popcll(bal);
-            __syncthreads();
-            int off = 0, tot = 0;
+        } else {
+            const int nv = hm * wm;
+            for (int v0 = tid; v0 < nv; v0 += U * 1024) {
+                uint8_t d[U];
 #pragma unroll
-            for (int w = 0; w < 16; ++w) {
-                const int c = wcnt[w];
-                off += (w < wid) ? c : 0;
-                tot += c;
+                for (int u = 0; u < U; ++u) d[u] = (v0 + u * 1024 < nv) ? m[v0 + u * 1024] : 0;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (!d[u]) continue;
+                    const int v = v0 + u * 1024;
+                    const int Y = fdiv31(v, rc.m_wm), X = v - Y * wm;
+                    const int xp = fdiv31(X, rc.m_fx), yp = fdiv31(Y, rc.m_fy);
+                    atomicOr(&bits[yp * WW + (xp >> 5)], 1u << (xp & 31));
+                }
             }
-            if (on) idx[running + off + rank] = n * nblk + q;
-            running += tot;
-            __syncthreads();
         }
+        __syncthreads();
+        if (touching) {
+            // The dilated activity of block (i, j) is "some set bit in the union of
+            // the windows of blocks (i', j'), |i'-i|, |j'-j| <= d", a rectangle when
+            // consecutive windows touch: rows [max(0,(i-d)bs-p), min(H,(i+d)bs-p+ib)),
+            // columns likewise.  First OR each block row's rows into one bit row.
+            uint32_t *rowbits = (uint32_t *)scratch;
+            for (int q = tid; q < g.nby * WW; q += 1024) {
+                const int i = q / WW, wd = q - i * WW;
+                const int r0 = max(0, max(0, i - dil) * bs - g.p);
+                const int r1 = min(H, min(g.nby - 1, i + dil) * bs - g.p + g.ib);
+                uint32_t acc = 0u;
+                for (int r = r0; r < r1; ++r) acc |= bits[r * WW + wd];
+                rowbits[q] = acc;
+            }
+            __syncthreads();
+            for (int base = 0; base < nblk; base += 1024) {
+                const int q = base + tid;
+                bool on = false;
+                if (q < nblk) {
+                    const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
+                    const int c0 = max(0, max(0, j - dil) * bs - g.p);
+                    const int c1 = min(W, min(g.nbx - 1, j + dil) * bs - g.p + g.ib);
+                    on = any_bits(rowbits + i * WW, c0, c1);
+                }
+                running = compact_round(on, n * nblk + q, running, wcnt, idx);
+            }
+        } else {
+            uint8_t *act = scratch, *tmp = scratch + kReduceMaxBlocks;
+            for (int q = tid; q < nblk; q += 1024) {
+                const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
+                const int r0 = max(0, i * bs - g.p), r1 = min(H, i * bs - g.p + g.ib);
+                const int c0 = max(0, j * bs - g.p), c1 = min(W, j * bs - g.p + g.ib);
+                bool hit = false;
+                for (int r = r0; r < r1 && !hit; ++r) hit = any_bits(bits + r * WW, c0, c1);
+                act[q] = hit ? 1 : 0;
+            }
+            __syncthreads();
+            for (int q = tid; q < nblk; q += 1024) {
+                const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
+                uint8_t on = 0;
+                for (int jj = max(0, j - dil); jj <= min(g.nbx - 1, j + dil); ++jj) on |= act[i * g.nbx + jj];
+                tmp[q] = on;
+            }
+            __syncthreads();
+            for (int base = 0; base < nblk; base += 1024) {
+                const int q = base + tid;
+                bool on = false;
+                if (q < nblk) {
+                    const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
+                    for (int ii = max(0, i - dil); ii <= min(g.nby - 1, i + dil); ++ii)
+                        on |= tmp[ii * g.nbx + j] != 0;
+                }
+                running = compact_round(on, n * nblk + q, running, wcnt, idx);
+            }
+        }
+        __syncthreads();  // scratch and bits are reused by the next image
     }
     if (tid == 0) *count = running;
 }
 
 hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
                          int32_t *count, hipStream_t st) {
-    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(1024), 0, st, mask, hm, wm, hm / g.h, wm / g.w, g, dilate, vec16,
-                       idx, count);
+    const int fy = hm / g.h, fx = wm / g.w;
+    const int WW = (g.w + 31) / 32;
+    // the one-launch path divides with 31-bit multipliers: every dividend * divisor < 2^31
+    const long lim = 1L << 31;
+    const bool exact = (vec16 ? (long)hm * (wm / 16) * (wm / 16) : (long)hm * wm * wm) < lim &&
+                       (long)hm * fy < lim && (long)wm * fx < lim;
+    if (exact && (long)g.h * WW <= kReduceBitsWords && g.nby * g.nbx <= kReduceMaxBlocks) {
+        RedCfg rc{vec16 ? fast_div_magic(wm / 16) : 1u, fast_div_magic(wm), fast_div_magic(fy), fast_div_magic(fx),
+                  fast_div_magic(g.nbx)};
+        hipLaunchKernelGGL(k_reduce_one, dim3(1), dim3(1024), 0, st, mask, hm, wm, fy, fx, g, dilate, vec16, rc, idx,
+                           count);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_activity, dim3(g.nby, g.n), dim3(256), 0, st, mask, hm, wm, fy, fx, g, vec16,
+                       (uint8_t *)idx);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, g, dilate, idx, count);
     return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ int channel_rows_ok(int dt, int c, const char *what) {
     const int es = sige::elem_bytes(dt);
     if ((c * es) % 16)
         return fail(SIGE_EALIGN, "%s=%d: a channel row of %d bytes is not a multiple of 16", what, c, c * es);
+    if (c * es > sige::kMaxRowBytes)
+        return fail(SIGE_ERANGE, "%s=%d: channel rows above %d bytes are not supported", what, c, sige::kMaxRowBytes);
     return SIGE_OK;
 }
 
@@ -95,79 +97,122 @@ int finish(hipError_t e, const char *what, hipStream_t st) {
     return SIGE_OK;
 }
 
-constexpr int kStaticLds = 1024;  // the conv kernel's static LDS (block list, copy flags), rounded up
+constexpr int kStaticLds = 2048;  // the conv kernel's static LDS (slot table, copy flags), rounded up
 
-// LDS per workgroup the current device allows (160 KiB on gfx950).
-int lds_limit() {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) {
+struct DevInfo {
+    int lds = 64 * 1024;  // LDS per workgroup
+    int cus = 256;        // compute units
+};
+
+// Per-device limits, queried once per device (160 KiB LDS and 256 CUs on MI355X).
+DevInfo dev_info() {
+    static DevInfo cache[64];
+    static bool have[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
-        return 64 * 1024;
+        return DevInfo{};
     }
-    return v;
+    if (!have[dev]) {
+        DevInfo d;
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+            d.lds = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            d.cus = v;
+        (void)hipGetLastError();
+        cache[dev] = d;
+        have[dev] = true;
+    }
+    return cache[dev];
 }
 
-// Copy units: segments of one output row, about 32 KiB each (at most 254
-// blocks wide, which bounds the per-unit block flags in LDS).
-void copy_plan(const Geo &g, int es, int *xw_out, int *units_out) {
-    int xw = (32 * 1024) / (g.cout * es);
+// Copy units: segments of output rows of about 64 KiB, at most 254 blocks
+// wide (the per-unit block flags).
+sige::CopyCfg copy_plan(const Geo &g, int es, bool copy) {
+    sige::CopyCfg c{};
+    c.row_bytes = g.cout * es;
+    c.m_vpp = sige::fast_div_magic(c.row_bytes / 16);
+    int xw = (64 * 1024) / c.row_bytes;
     if (xw < 1) xw = 1;
     if (xw > 254 * g.b) xw = 254 * g.b;
     if (xw > g.wo) xw = g.wo;
-    *xw_out = xw;
-    *units_out = g.n * g.ho * ((g.wo + xw - 1) / xw);
+    c.xw = xw;
+    c.units_per_row = (g.wo + xw - 1) / xw;
+    c.units = copy ? g.n * g.ho * c.units_per_row : 0;
+    return c;
 }
 
-// Tile configuration of the implicit GEMM (see kernels_conv.hip).
+// Tile shape override for tuning: SIGE_CONV_TILE="MT,NT" (one of 4,2 4,1 2,2 4,4).
+void tile_shape(int *mt, int *nt) {
+    *mt = 4;
+    *nt = 2;
+    const char *v = getenv("SIGE_CONV_TILE");
+    int a = 0, b = 0;
+    if (v && sscanf(v, "%d,%d", &a, &b) == 2) {
+        const int key = a * 10 + b;
+        if (key == 42 || key == 41 || key == 22 || key == 44) {
+            *mt = a;
+            *nt = b;
+        }
+    }
+}
+
+// Tile configuration of the implicit GEMM (see kernels_conv.hip).  Each of the
+// 8 waves holds the weight fragments of at most 10/NT K steps of a chunk in
+// registers, so a chunk has at most 8*10/NT steps: ck <= floor(80/(NT*k*k)) K
+// slices.
+// Among those, the fewest chunks whose input windows fit in the device's LDS.
+// The persistent grid fills every CU with up to two workgroups.
 int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
     ConvCfg c{};
-    c.mt = 4;
-    c.nt = 2;
-    const int BM = 16 * c.mt, BN = 16 * c.nt;
+    tile_shape(&c.mt, &c.nt);
     const int es = sige::elem_bytes(dt);
     const int ks = dt == SIGE_F32 ? 16 : 32;
     const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
+    while (c.nt > 1 && (8 * (10 / c.nt)) / k2 < 1) c.nt /= 2;  // large kernels: fewer channels per tile
+    const int max_kpc = (8 * (10 / c.nt)) / k2;                 // K slices per tap and chunk
+    if (max_kpc < 1) return fail(SIGE_ERANGE, "kernel size %d too large for the register-resident weights", g.k);
+    const int BM = 16 * c.mt, BN = 16 * c.nt;
     int ns = (BM - 1) / b2 + 2;
     if (ns > BM) ns = BM;
     if (ns > g.cap) ns = g.cap;
     c.ns_max = ns;
-    const int part = 4 * BM * (BN + 4) * 4;
-    const int cin_r = (g.cin + ks - 1) / ks * ks;
-    // Largest channel chunk within 64 KiB (two workgroups per CU); failing that,
-    // the largest within the device's per-workgroup LDS.
+    // output rows r (< cap*b*b + BM) are split with fast divisions by b*b: r * b*b < 2^31
+    if (((long)g.cap * b2 + BM) * b2 > 0x7FFFFFFFL) return fail(SIGE_ERANGE, "too many output rows for one launch");
+    const DevInfo dv = dev_info();
+    const long limit = (long)dv.lds - kStaticLds;
+    const long part = 4L * BM * (BN + 4) * 4;
+    const int kslices = (g.cin + ks - 1) / ks;
     int best = 0;
-    for (int pass = 0; pass < 2 && !best; ++pass) {
-        const long budget = (pass == 0 ? 64 * 1024 : (long)lds_limit()) - kStaticLds;
-        for (int ck = (cin_r < 512 ? cin_r : 512); ck >= ks; ck -= ks) {
-            const int apix = ck * es + 16, brow = k2 * ck * es + 16;
-            const long a_bytes = (long)ns * ib2 * apix, lds = a_bytes + (long)BN * brow;
-            const long need = lds > part ? lds : part;
-            if (need <= budget) {
-                best = ck;
-                break;
-            }
+    long best_lds = 0;
+    for (int nch = (kslices + max_kpc - 1) / max_kpc; nch <= kslices && !best; ++nch) {
+        const int ck = (kslices + nch - 1) / nch * ks;  // ceil(cin / nch), rounded up to a K slice
+        if (ck * es / 16 > 256) continue;               // one 16-byte vector per thread and pixel
+        const long apix = ck * es + 16;
+        const long lds = (long)ns * ib2 * apix;
+        const long need = lds > part ? lds : part;
+        if (need <= limit) {
+            best = ck;
+            best_lds = need;
         }
     }
     if (!best)
-        return fail(SIGE_ERANGE, "staged windows (%d slots of %dx%d) and weights (k=%d) do not fit in LDS", ns, g.ib,
-                    g.ib, g.k);
+        return fail(SIGE_ERANGE, "staged windows (%d slots of %dx%d) do not fit in LDS", ns, g.ib, g.ib);
     c.ck = best;
     c.a_pix_stride = best * es + 16;
-    c.b_row_stride = k2 * best * es + 16;
+    c.b_row_stride = 0;
     c.a_bytes = ns * ib2 * c.a_pix_stride;
-    {
-        const int lds = c.a_bytes + BN * c.b_row_stride;
-        c.lds_bytes = lds > part ? lds : part;
-    }
-    const long mt_cap = ((long)g.cap * b2 + BM - 1) / BM;
-    const long tiles_cap = mt_cap * ((g.cout + BN - 1) / BN);
-    long grid = tiles_cap < 512 ? tiles_cap : 512;
-    if (grid > 8) grid = grid / 8 * 8;  // keep tile t on XCD t % 8 across persistent passes
-    c.compute_grid = (int)(grid > 0 ? grid : 1);
-    c.copy_xw = 0;
-    c.copy_units = 0;
-    if (fused && copy) copy_plan(g, es, &c.copy_xw, &c.copy_units);
+    c.lds_bytes = (int)best_lds;
+    c.m_ib2 = sige::fast_div_magic(ib2);
+    c.m_ib = sige::fast_div_magic(g.ib);
+    c.m_vpc1 = sige::fast_div_magic(best * es / 16 + 1);
+    c.m_b2 = sige::fast_div_magic(b2);
+    c.m_b = sige::fast_div_magic(g.b);
+    long grid = 1L << 30;  // the launch trims this to the CUs' resident capacity
+    if (!(fused && copy)) grid = ((long)g.cap * b2 + BM - 1) / BM * ((g.cout + BN - 1) / BN);
+    c.cus = dv.cus;
+    c.grid = (int)(grid > 0 ? grid : 1);
     *out = c;
     return SIGE_OK;
 }
@@ -248,10 +293,10 @@ int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geo
         return fail(SIGE_EINVAL, "mask %dx%d is not an integer multiple of the conv input %dx%d", mask_h, mask_w,
                     g.h, g.w);
     if (dilate_blocks < 0 || dilate_blocks > 16) return fail(SIGE_EINVAL, "dilate_blocks=%d outside [0, 16]", dilate_blocks);
-    if ((long)g.h * ((g.w + 31) / 32) > sige::kReduceBitsWords)
-        return fail(SIGE_ERANGE, "conv input %dx%d exceeds the reduce limit", g.h, g.w);
-    if ((long)g.nby * g.nbx > sige::kReduceMaxBlocks)
-        return fail(SIGE_ERANGE, "block grid %dx%d exceeds the reduce limit", g.nby, g.nbx);
+    if (g.w > sige::kReduceMaxWidth)
+        return fail(SIGE_ERANGE, "conv input width %d exceeds the reduce limit %d", g.w, sige::kReduceMaxWidth);
+    if (g.cap > sige::kReduceMaxBlocks)
+        return fail(SIGE_ERANGE, "%d blocks (n*nby*nbx) exceed the reduce limit %d", g.cap, sige::kReduceMaxBlocks);
     if (!aligned(idx, 4) || !aligned(count, 4)) return fail(SIGE_EALIGN, "idx/count must be 4-byte aligned");
     const size_t mbytes = (size_t)g.n * mask_h * mask_w;
     if (overlap(idx, (size_t)g.cap * 4, mask, mbytes) || overlap(count, 4, mask, mbytes) ||
@@ -297,7 +342,8 @@ int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, 
     ConvCfg cfg;
     if ((rc = choose_conv(g, dtype, 0, 0, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
-    return finish(sige::launch_conv(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, g, cfg,
+    const sige::CopyCfg cc = copy_plan(g, es, false);
+    return finish(sige::launch_conv(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, g, cfg, cc,
                                     (hipStream_t)stream),
                   "sige_conv_blocks", (hipStream_t)stream);
 }
@@ -318,11 +364,11 @@ int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *coun
     if (overlap(out, obytes, out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es))
         return fail(SIGE_EINVAL, "out overlaps out_blocks");
     if ((rc = device_ready())) return rc;
-    int xw = 0, units = 0;
-    copy_plan(g, es, &xw, &units);
-    const int sgrid = g.cap < 1024 ? g.cap : 1024;
-    return finish(sige::launch_scatter(dtype, out_blocks, idx, count, g, cached, out, copy_cached ? 1 : 0, sgrid, xw,
-                                       units, (hipStream_t)stream),
+    const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
+    const DevInfo dv = dev_info();
+    const int grid = dv.cus * 4;
+    return finish(sige::launch_scatter(dtype, out_blocks, idx, count, g, copy_cached ? cached : nullptr, out, grid, cc,
+                                       (hipStream_t)stream),
                   "sige_scatter", (hipStream_t)stream);
 }
 
@@ -347,8 +393,9 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
     ConvCfg cfg;
     if ((rc = choose_conv(g, dtype, 1, copy_cached, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
+    const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
     return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
-                                    g, cfg, (hipStream_t)stream),
+                                    g, cfg, cc, (hipStream_t)stream),
                   "sige_sparse_conv_layer", (hipStream_t)stream);
 }
 

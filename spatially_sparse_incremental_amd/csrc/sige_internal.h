@@ -20,18 +20,34 @@ struct Geo {
     int cap;  // n * nby * nbx
 };
 
+// Multiplier for exact division x / d when x * d < 2^31: x / d = (x * m) >> 31.
+__host__ __device__ inline uint32_t fast_div_magic(uint32_t d) {
+    return (uint32_t)(((1ull << 31) + d - 1) / d);
+}
+
 // Launch parameters of the implicit-GEMM convolution.
 struct ConvCfg {
     int mt, nt;          // 16x16 tiles per workgroup along M (rows) and N (output channels)
     int ck;              // input channels staged per chunk
     int a_pix_stride;    // LDS bytes per staged input pixel (ck*es + 16)
-    int b_row_stride;    // LDS bytes per staged weight row (k*k*ck*es + 16)
+    int b_row_stride;    // unused (weights are read into registers)
     int a_bytes;         // LDS bytes of the staged input windows
     int lds_bytes;       // dynamic LDS per workgroup
     int ns_max;          // most block slots one M tile can touch
-    int compute_grid;    // persistent workgroups doing the GEMM
-    int copy_xw;         // output pixels per copy unit (one image row segment)
-    int copy_units;      // workgroups copying the cache (0 without copy)
+    int grid;            // most persistent workgroups worth launching (tiles at capacity; copy: no cap)
+    int cus;             // compute units of the device
+    uint32_t m_ib2, m_ib;  // fast_div_magic(ib*ib), fast_div_magic(ib)
+    uint32_t m_vpc1;       // fast_div_magic(ck*es/16 + 1): 16-byte LDS slots per staged pixel
+    uint32_t m_b2, m_b;    // fast_div_magic(b*b), fast_div_magic(b): output rows -> block slot, pixel
+};
+
+// Copy of the cache outside the listed blocks: units of `xw` pixels of one row.
+struct CopyCfg {
+    int units;           // total units (0: no copy)
+    int xw;              // pixels per unit
+    int units_per_row;   // ceil(wo / xw)
+    int row_bytes;       // c_out * element size
+    uint32_t m_vpp;      // fast_div_magic(row_bytes / 16)
 };
 
 hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix, int vpp, float tau,
@@ -43,13 +59,15 @@ hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t
 // fused = 0: src = stacked blocks, dst = output blocks.  fused = 1: src = a_edit, dst = out.
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                        const int32_t *count, void *dst, const void *cache, const Geo &g, const ConvCfg &cfg,
-                       hipStream_t st);
+                       const CopyCfg &cc, hipStream_t st);
 hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, const int32_t *count, const Geo &g,
-                          const void *cached, void *out, int copy_cached, int scatter_grid, int copy_xw,
-                          int copy_units, hipStream_t st);
+                          const void *cached, void *out, int grid, const CopyCfg &cc, hipStream_t st);
 
-// reduce limits (LDS of its single workgroup)
-constexpr int kReduceBitsWords = 8192;   // pooled mask rows, 32 pixels per word
-constexpr int kReduceMaxBlocks = 12288;  // block grid of one image
+// reduce limits (LDS of its workgroups)
+constexpr int kReduceMaxWidth = 8192;    // conv input width (pooled column bits of one block row)
+constexpr int kReduceBitsWords = 8192;   // pooled mask as bits, for the one-launch reduce (32 KiB)
+constexpr int kReduceMaxBlocks = 16384;  // n * nby * nbx (flags of all blocks in one workgroup)
+// channel rows of at most this many bytes (keeps the fast divisions exact)
+constexpr int kMaxRowBytes = 8192;
 
 }  // namespace sige

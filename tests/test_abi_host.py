@@ -97,10 +97,12 @@ def test_reduce_validation(lib):
     assert f(_v(A), 256, 256, ctypes.byref(g), 17, _v(B), _v(C), s) == EINVAL
     assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B + 2), _v(C), s) == EALIGN
     assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(A + 128), _v(C), s) == EINVAL  # idx inside mask
-    big = _g(h=1024, w=1024, b=8)  # 1024 * 32 words > 8192
-    assert f(_v(A), 1024, 1024, ctypes.byref(big), 1, _v(B), _v(C), s) == ERANGE
-    grid = _g(h=512, w=512, b=4)  # 128 x 128 blocks > 12288
-    assert f(_v(A), 512, 512, ctypes.byref(grid), 1, _v(B), _v(C), s) == ERANGE
+    wide = _g(h=16, w=8200, b=32)  # conv input wider than 8192
+    assert f(_v(A), 16, 8200, ctypes.byref(wide), 1, _v(B), _v(C), s) == ERANGE
+    grid = _g(h=516, w=516, b=4)  # 129 x 129 blocks > 16384
+    assert f(_v(A), 516, 516, ctypes.byref(grid), 1, _v(B), _v(C), s) == ERANGE
+    grid2 = _g(n=2, h=512, w=256, b=4)  # 2 x 128 x 64 = 16384: the limit itself is accepted up to the device
+    assert f(_v(A), 512, 256, ctypes.byref(grid2), 1, _v(B), _v(C), s) in (0, ENODEV)
 
 
 def test_conv_step_validation(lib):
@@ -113,13 +115,15 @@ def test_conv_step_validation(lib):
     assert lib.sige_conv_blocks(_v(A), _v(B), _v(E + 2), 1, ctypes.byref(g), _v(C), _v(D), s) == EALIGN
     odd = _g(ci=12)
     assert lib.sige_conv_blocks(_v(A), _v(B), None, 1, ctypes.byref(odd), _v(C), _v(D), s) == EALIGN
+    wide = _g(ci=8192)  # 16 KiB channel rows
+    assert lib.sige_conv_blocks(_v(A), _v(B), None, 1, ctypes.byref(wide), _v(C), _v(D), s) == ERANGE
     assert lib.sige_scatter(_v(A), _v(B), _v(C), ctypes.byref(g), 1, _v(D), _v(D), 1, s) == EINVAL  # out == cached
     assert lib.sige_scatter(_v(A), _v(B), _v(C), ctypes.byref(g), 1, None, _v(D), 1, s) == EINVAL
     assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g), _v(A + 64), 1,
                                       s) == EINVAL  # out overlaps a_edit
     assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, None, _v(D), _v(E), 1, ctypes.byref(g), _v(C), 1,
                                       s) == EINVAL  # copy without a cache
-    huge = _g(h=64, w=64, ci=4096, co=64, k=7, p=3, b=8)  # windows + weights cannot fit in LDS
+    huge = _g(h=128, w=128, ci=64, co=64, k=1, p=0, b=64)  # two 64x64 windows cannot fit in LDS
     assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(huge), _v(B + (1 << 35)),
                                       1, s) == ERANGE
 

@@ -1,0 +1,71 @@
+"""The hot path captured in a HIP graph: every replay equals the eager result.
+
+Replays are interleaved with eager work, synchronisations and input changes,
+and each one is compared bit for bit with an eager run on the same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import spatially_sparse_incremental_amd as ssi
+import synth
+from _parity import bits, layer_inputs, rand
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("copy", [True, False])
+def test_graph_replays_match_eager(copy):
+    n, h, w, c, b = 1, 64, 72, 64, 6
+    dt = torch.bfloat16
+    blob = synth.Blob.draw(5, h, w).fit_area(0.02)
+    mask0 = blob.raster()
+    a_o, a_e, wt, bias = [t.cuda() for t in layer_inputs(n, h, w, c, c, 3, dt, 201, mask0)]
+    wk = ssi.weight_to_krsc(wt)
+    cache = rand((n, h, w, c), dt, 202).cuda()
+    g = ssi.geom(n, h, w, c, c, 3, 1, 1, b)
+    cap = ssi.sige_max_blocks(g)
+    m = torch.empty((n, h, w), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((cap,), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((1,), dtype=torch.int32, device="cuda")
+    out = cache.clone()
+
+    def step():
+        ssi.sige_diff_mask(a_o, a_e, 1e-6, mask=m)
+        ssi.sige_reduce_mask(m, g, 1, idx=idx, count=cnt)
+        if copy:
+            ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out, copy_cached=True)
+        else:
+            ssi.sige_sparse_conv_layer(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    rng = np.random.default_rng(203)
+    for rep in range(5):
+        # a new edit, written in place into the captured input buffer
+        mk = torch.from_numpy((rng.random((n, h, w)) < 0.01).astype(np.uint8))
+        a_e.copy_(synth.make_edit(a_o.cpu(), mk.numpy(), "replace", 210 + rep).cuda())
+        out.copy_(cache)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        got_idx = idx[:int(cnt.item())].clone()
+        out.copy_(cache)
+        step()  # eager, same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, idx[:int(cnt.item())]), rep
+        assert torch.equal(bits(got), bits(out)), rep
+        assert int(cnt.item()) > 0

@@ -212,6 +212,10 @@ REDUCE = [  # (n, h, w, f, k, s, p, b, dilate, frac)
     (1, 256, 512, 1, 3, 1, 1, 6, 1, 0.001),
     (1, 64, 64, 1, 5, 1, 2, 3, 3, 0.001),
     (1, 9, 9, 1, 3, 1, 1, 1, 0, 0.05),
+    (1, 24, 20, 1, 1, 2, 0, 3, 1, 0.02),       # 1x1 stride 2: neighbouring windows do not touch
+    (2, 30, 22, 2, 1, 3, 0, 2, 2, 0.01),       # windows with gaps, two images, pooled
+    (1, 512, 1024, 1, 3, 1, 1, 6, 1, 0.0005),  # pooled bits exceed one workgroup's LDS: two-launch path
+    (2, 96, 640, 2, 3, 2, 1, 4, 2, 0.001),    # two-launch path, two images, stride 2, pooled
 ]
 
 
@@ -237,8 +241,8 @@ def test_reduce_parity(case):
 
 
 def test_reduce_at_its_limits():
-    # largest conv input (8192 bit words) and largest block grid (12288) accepted
-    for (h, w, b) in [(256, 1024, 16), (96, 128, 1)]:
+    # widest conv input (8192) and largest block grid (16384) accepted, on both reduce paths
+    for (h, w, b) in [(256, 1024, 16), (128, 128, 1), (16, 8192, 32), (1024, 8192, 32), (2048, 512, 8)]:
         g = _geom(1, h, w, 8, 8, 3, 1, 1, b)
         m = torch.from_numpy(random_mask(1, h, w, 0.0005, 111))
         idx, count = ssi.sige_reduce_mask(gpu(m), g, 1)
