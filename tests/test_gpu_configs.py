@@ -1,0 +1,186 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench uses.
+
+For every layer of every workload: the change mask and the block list are
+compared with the oracle in full (bit-exact), every output pixel outside the
+listed blocks must equal the cache bit for bit, and the recomputed values are
+checked against the oracle's fp64 result on a seeded sample of listed blocks
+(the oracle computes just those blocks; the rest of its output is the GPU's).
+The chain is checked layer by layer, each layer's oracle taking the GPU's
+output of the layer before as its edited input.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spatially_sparse_incremental_amd as ssi
+import synth
+from _parity import TOL, bits
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 6  # listed blocks recomputed by the oracle per layer
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_layer(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed):
+    """a_e, cache, out: CPU NHWC; idx: the GPU's list; mask_full: [n, hm, wm] diff mask."""
+    n, h, w, _ = a_e.shape
+    act = oracle.block_activity(mask_full, h, w, L.k, L.stride, L.pad, L.block, L.dilate)
+    ref_idx = oracle.index_list(act)
+    assert torch.equal(idx, ref_idx), f"{name}: block list differs"
+    ho, wo, nby, nbx, _ = oracle.geometry(h, w, L.k, L.stride, L.pad, L.block)
+    pm = act.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :ho, :wo, None]
+    keep = ~pm.expand_as(cache)
+    assert torch.equal(out[keep].view(torch.uint8), cache[keep].view(torch.uint8)), f"{name}: untouched pixels"
+    if ref_idx.numel() == 0:
+        return 0.0
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(ref_idx.numpy(), size=min(SAMPLE, ref_idx.numel()), replace=False)
+    sub = torch.zeros_like(act)
+    sub.view(-1)[torch.from_numpy(pick).long()] = 1
+    ref = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, sub, out, out_f64=True)
+    sel = sub.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :ho, :wo, None].expand_as(out)
+    g64, r64 = out.double()[sel], ref[sel]
+    scale = r64.abs().max().item()
+    err = (g64 - r64).abs().max().item()
+    assert err <= TOL[out.dtype] * scale, f"{name}: max err {err:.3e} vs scale {scale:.3e}"
+    return err / scale
+
+
+def _run_layer(a_e_gpu, wt, bias, cache_gpu, L, mask_gpu):
+    g = ssi.geom(a_e_gpu.shape[0], L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    idx, count = ssi.sige_reduce_mask(mask_gpu, g, L.dilate)
+    out = ssi.sige_sparse_conv_layer(a_e_gpu, ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache_gpu, idx, count, g)
+    torch.cuda.synchronize()
+    return out, idx[:int(count.item())].cpu()
+
+
+def test_cfg1_rectangle_fp32_nchw():
+    wl = synth.workload("cfg1_rect_f32")
+    L = wl.layers[0]
+    for seed in range(4):
+        m, _ = synth.rectangle_mask(seed, L.h, L.w)
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed, "NCHW")
+        a_e = synth.make_edit(a_o, m, wl.edit_kind, seed, "NCHW")
+        wt, bias = synth.make_layer_tensors(L, seed)
+        cache = oracle.dense_conv(a_o, wt, bias, L.k, L.stride, L.pad, "NCHW")
+        # the GPU path is NHWC: permute (untimed); the oracle reads NCHW directly
+        nhwc = lambda t: t.permute(0, 2, 3, 1).contiguous()  # noqa: E731
+        mask = ssi.sige_diff_mask(nhwc(a_o).cuda(), nhwc(a_e).cuda(), wl.tau)
+        out, idx = _run_layer(nhwc(a_e).cuda(), wt, bias, nhwc(cache).cuda(), L, mask)
+        assert torch.equal(mask.cpu()[0], torch.from_numpy(m))
+        act = oracle.block_activity(oracle.diff_mask(a_o, a_e, wl.tau, "NCHW"), L.h, L.w, L.k, L.stride, L.pad,
+                                    L.block, L.dilate)
+        assert torch.equal(idx, oracle.index_list(act))
+        ref = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, act, cache, "NCHW", out_f64=True)
+        got = out.cpu().permute(0, 3, 1, 2)
+        err = (got.double() - ref).abs().max().item()
+        assert err <= TOL[torch.float32] * ref.abs().max().item()
+        # V4: the sparse result is the dense conv of A_e at every pixel
+        dense = oracle.dense_conv(a_e, wt, bias, L.k, L.stride, L.pad, "NCHW", out_f64=True)
+        assert (got.double() - dense).abs().max().item() <= TOL[torch.float32] * dense.abs().max().item()
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_cfg2_unet_layer_full(seed):
+    wl = synth.workload("cfg2_unet_bf16")
+    L = wl.layers[0]
+    m = synth.edit_shape(wl, seed).raster(L.h, L.w)
+    a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
+    a_e = synth.make_edit(a_o, m, wl.edit_kind, seed)
+    wt, bias = synth.make_layer_tensors(L, seed)
+    cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + 100)  # the cache is an input
+    mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+    assert torch.equal(mask.cpu()[0], torch.from_numpy(m))
+    out, idx = _run_layer(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+    # every listed block, not a sample: the oracle finishes this layer in about a second
+    act = oracle.block_activity(mask.cpu(), L.h, L.w, L.k, L.stride, L.pad, L.block, L.dilate)
+    assert torch.equal(idx, oracle.index_list(act))
+    ref = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, act, cache, out_f64=True)
+    o = out.cpu()
+    pm = act.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :L.h, :L.w, None].expand_as(o)
+    assert torch.equal(o[~pm].view(torch.uint8), cache[~pm].view(torch.uint8))
+    err = (o.double()[pm] - ref[pm]).abs().max().item()
+    assert err <= TOL[torch.bfloat16] * ref[pm].abs().max().item()
+    assert 40 <= idx.numel() <= 130  # 1.2% blob, 6x6 blocks, dilation 1
+
+
+def test_cfg3_chain_layerwise():
+    wl = synth.workload("cfg3_chain_bf16")
+    seed = 3
+    first = wl.layers[0]
+    m = synth.edit_shape(wl, seed).raster(first.h, first.w)
+    a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed)
+    a_e = synth.make_edit(a_o, m, wl.edit_kind, seed)
+    mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)  # one diff at 256x256, pooled per layer
+    assert torch.equal(mask.cpu()[0], torch.from_numpy(m))
+    x = a_e.cuda()
+    for li, L in enumerate(wl.layers):
+        wt, bias = synth.make_layer_tensors(L, seed * 100 + li)
+        ho, wo, _, _, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
+        cache = synth.make_activation(1, ho, wo, L.c_out, L.dtype, seed * 100 + li + 50)
+        out, idx = _run_layer(x, wt, bias, cache.cuda(), L, mask)
+        _check_layer(f"chain {L.name}", x.cpu(), wt, bias, cache, out.cpu(), idx, L, mask.cpu(), seed + li)
+        x = out  # layer l+1 takes layer l's edited output
+
+
+@pytest.mark.parametrize("area", [0.005, 0.012, 0.05, 0.15, 0.30])
+def test_cfg4_gaugan_layers(area):
+    wl = synth.workload("cfg4_gaugan_bf16")
+    seed = 4
+    shape = synth.edit_shape(wl, seed, area)
+    for li, L in enumerate(wl.layers):
+        m = shape.raster(L.h, L.w)  # the polygon rasterised at the layer's resolution
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li)
+        a_e = synth.make_edit(a_o, m, wl.edit_kind, seed + li)
+        wt, bias = synth.make_layer_tensors(L, seed + li)
+        cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
+        mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+        out, idx = _run_layer(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+        _check_layer(f"gaugan {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
+
+
+@pytest.mark.parametrize("area", [0.012, 0.10])
+def test_cfg5_latent_diffusion_layers(area):
+    wl = synth.workload("cfg5_ldm_f16")
+    seed = 5
+    shape = synth.edit_shape(wl, seed, area)
+    for li, L in enumerate(wl.layers):
+        m = shape.raster(L.h, L.w)
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li)
+        a_e = synth.make_edit(a_o, m, wl.edit_kind, seed + li)
+        wt, bias = synth.make_layer_tensors(L, seed + li)
+        cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
+        mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+        out, idx = _run_layer(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+        _check_layer(f"ldm {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
+
+
+def test_cfg2_three_call_path_matches_fused_at_full_size():
+    wl = synth.workload("cfg2_unet_bf16")
+    L = wl.layers[0]
+    seed = 7
+    m = synth.edit_shape(wl, seed).raster(L.h, L.w)
+    a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed).cuda()
+    a_e = synth.make_edit(a_o.cpu(), m, wl.edit_kind, seed).cuda()
+    wt, bias = synth.make_layer_tensors(L, seed)
+    wk, b = ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + 1).cuda()
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    mask = ssi.sige_diff_mask(a_o, a_e, wl.tau)
+    idx, count = ssi.sige_reduce_mask(mask, g, L.dilate)
+    fused = ssi.sige_sparse_conv_layer(a_e, wk, b, cache, idx, count, g)
+    blocks = ssi.sige_gather(a_e, g, idx, count)
+    ob = ssi.sige_conv_blocks(blocks, wk, b, g, count)
+    three = ssi.sige_scatter(ob, idx, count, g, cache)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(fused), bits(three))
+    cnt = int(count.item())
+    assert torch.equal(bits(blocks[:cnt].cpu()), bits(oracle.gather(a_e.cpu(), L.k, L.stride, L.pad, L.block,
+                                                                    idx[:cnt].cpu())))
