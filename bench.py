@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline sample length")
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="time the step and its kernels only (for profiler runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     return ap.parse_args()
@@ -187,58 +189,60 @@ def main():
     }
     print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
 
-    # the step without the cache copy (persistent output buffer)
-    out_persist = cache.clone()
+    t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_nocopy = t_dense_ours = t_dense_miopen = None
+    if not args.no_comparators:
+        # the step without the cache copy (persistent output buffer)
+        out_persist = cache.clone()
 
-    def step_nocopy():
-        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
-        ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
-        ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False)
+        def step_nocopy():
+            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False)
 
-    # the three-call path
-    blocks = torch.empty((cap, d.ib, d.ib, L.c_in), dtype=dt, device=dev)
-    oblocks = torch.empty((cap, L.block, L.block, L.c_out), dtype=dt, device=dev)
-    out3 = torch.empty_like(cache)
+        # the three-call path
+        blocks = torch.empty((cap, d.ib, d.ib, L.c_in), dtype=dt, device=dev)
+        oblocks = torch.empty((cap, L.block, L.block, L.c_out), dtype=dt, device=dev)
+        out3 = torch.empty_like(cache)
 
-    def step_three():
-        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
-        ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
-        ssi.sige_gather(a_e, g, idx, count, blocks=blocks)
-        ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks)
-        ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)
+        def step_three():
+            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+            ssi.sige_gather(a_e, g, idx, count, blocks=blocks)
+            ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks)
+            ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)
 
-    t_nocopy = graph_time(step_nocopy, 5, 40)
-    t_three = graph_time(step_three, 5, 40)
-    t_gather = graph_time(lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks))
-    t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks))
-    t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
-    t_fused_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g,
-                                                                   out=out_persist, copy_cached=False))
-    # dense comparators on the same GPU
-    dense_all = torch.empty_like(cache)
-    t_dense_ours = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx_all, cnt_all, g,
-                                                                 out=dense_all, copy_cached=False), 5, 10)
+        t_nocopy = graph_time(step_nocopy, 5, 40)
+        t_three = graph_time(step_three, 5, 40)
+        t_gather = graph_time(lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks))
+        t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks))
+        t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
+        t_fused_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g,
+                                                                       out=out_persist, copy_cached=False))
+        # dense comparators on the same GPU
+        dense_all = torch.empty_like(cache)
+        t_dense_ours = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx_all, cnt_all, g,
+                                                                     out=dense_all, copy_cached=False), 5, 10)
 
-    def timed_eager(fn, reps):
-        for _ in range(min(10, reps)):
-            fn()
-        torch.cuda.synchronize()
-        a, b = ev(), ev()
-        a.record(cur)
-        for _ in range(reps):
-            fn()
-        b.record(cur)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3  # us
+        def timed_eager(fn, reps):
+            for _ in range(min(10, reps)):
+                fn()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record(cur)
+            for _ in range(reps):
+                fn()
+            b.record(cur)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps * 1e3  # us
 
-    t_dense_miopen = None
-    try:
-        x_cl = a_e.permute(0, 3, 1, 2)  # NCHW view with channels_last strides
-        w_cl = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
-        with torch.no_grad():
-            t_dense_miopen = timed_eager(lambda: F.conv2d(x_cl, w_cl, bias.to(dt), padding=L.pad), max(20, K // 5))
-    except Exception as exc:  # noqa: BLE001 - report, do not hide
-        print(f"[bench] MIOpen dense conv failed: {exc}", file=sys.stderr)
+        t_dense_miopen = None
+        try:
+            x_cl = a_e.permute(0, 3, 1, 2)  # NCHW view with channels_last strides
+            w_cl = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
+            with torch.no_grad():
+                t_dense_miopen = timed_eager(lambda: F.conv2d(x_cl, w_cl, bias.to(dt), padding=L.pad), max(20, K // 5))
+        except Exception as exc:  # noqa: BLE001 - report, do not hide
+            print(f"[bench] MIOpen dense conv failed: {exc}", file=sys.stderr)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -270,17 +274,21 @@ def main():
         "fused_layer": dict(hbm(fused_bytes, kt["fused_layer"]), flops=int(conv_flops),
                             tflops=round(conv_flops / (kt["fused_layer"] * 1e-6) / 1e12, 2),
                             frac_mfma=round(conv_flops / (kt["fused_layer"] * 1e-6) / 1e12 / peak_tf, 5)),
-        "fused_layer_nocopy": dict(hbm(blk_bytes + w_bytes + 4 * L.c_out, t_fused_nocopy), flops=int(conv_flops),
-                                   frac_mfma=round(conv_flops / (t_fused_nocopy * 1e-6) / 1e12 / peak_tf, 5)),
-        "gather": hbm(active * d.ib * d.ib * L.c_in * es * 2, t_gather),
-        "conv_blocks": dict(hbm(blk_bytes + w_bytes, t_convb), flops=int(conv_flops),
-                            frac_mfma=round(conv_flops / (t_convb * 1e-6) / 1e12 / peak_tf, 5)),
-        "scatter": hbm(active * b2 * L.c_out * es + act_pix * L.c_out * es + copy_bytes, t_scatter),
     }
+    if not args.no_comparators:
+        kernels.update({
+            "fused_layer_nocopy": dict(hbm(blk_bytes + w_bytes + 4 * L.c_out, t_fused_nocopy), flops=int(conv_flops),
+                                       frac_mfma=round(conv_flops / (t_fused_nocopy * 1e-6) / 1e12 / peak_tf, 5)),
+            "gather": hbm(active * d.ib * d.ib * L.c_in * es * 2, t_gather),
+            "conv_blocks": dict(hbm(blk_bytes + w_bytes, t_convb), flops=int(conv_flops),
+                                frac_mfma=round(conv_flops / (t_convb * 1e-6) / 1e12 / peak_tf, 5)),
+            "scatter": hbm(active * b2 * L.c_out * es + act_pix * L.c_out * es + copy_bytes, t_scatter),
+        })
     dom = max(("diff", "fused_layer"), key=lambda k: kt[k])
     droof = kernels[dom]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": droof["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(droof["gbps"] / PEAK_HBM_GBPS, 4), "traffic": None}
+                "frac": round(droof["gbps"] / PEAK_HBM_GBPS, 4),
+                "traffic": _measured_traffic() if dom == "fused_layer" else None}
 
     cpu = None
     if not args.no_cpu:
@@ -301,22 +309,42 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "comparators": {
+        "comparators": None if args.no_comparators else {
             "dense_conv_miopen_us": None if t_dense_miopen is None else round(t_dense_miopen, 3),
             "dense_conv_ours_all_blocks_us": round(t_dense_ours, 3),
             "speedup_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / step_us, 3),
             "speedup_vs_dense_ours": round(t_dense_ours / step_us, 3),
             "dense_ours_tflops": round(dense_flops / (t_dense_ours * 1e-6) / 1e12, 1),
-            "step_eager_launch_us": round(t_eager, 3),
-            "step_single_graph_replay_us": round(t_single, 3),
             "step_no_copy_us": round(t_nocopy, 3),
             "step_three_call_us": round(t_three, 3),
             "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
-            "mac_reduction": round(dense_flops / conv_flops, 2) if conv_flops else None,
+        },
+        "latency": {
+            "step_eager_launch_us": round(t_eager, 3),
+            "step_single_graph_replay_us": round(t_single, 3),
             "step_wall_us": round(wall / K * 1e6, 3),
         },
+        "mac_reduction": round(dense_flops / conv_flops, 2) if conv_flops else None,
     }
     print(json.dumps(res), flush=True)
+
+
+def _measured_traffic():
+    """HBM bytes per fused-layer launch from the committed counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    summary = os.path.join(here, "profiles", "fused_layer_unet256_pmc_traffic.md")
+    src = os.path.join(here, "spatially_sparse_incremental_amd", "csrc", "kernels_conv.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(summary).read().splitlines() if ": " in line)
+        current = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() == current:
+            return int(fields["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def _active_pixels(idx, d, b):
