@@ -18,10 +18,34 @@
 namespace sige {
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4 *)p; }
+
 __device__ __forceinline__ void st16(uint8_t *p, u32x4 v) { *(u32x4 *)p = v; }
 
 // x / d for x * d < 2^31, with m = ceil(2^31 / d) from the host (fast_div_magic)
 __device__ __forceinline__ int fdiv(int x, uint32_t m) { return (int)(((uint64_t)(uint32_t)x * m) >> 31); }
+
+// a / b and a % b for 0 <= a < 2^50, 0 < b < 2^31: a quotient from fp64 (off by
+// at most one there), then one correction step.  Much cheaper than the
+// 64-bit integer division routine.
+__device__ __forceinline__ long long div_ll(long long a, long long b, long long &r) {
+    long long q = (long long)((double)a / (double)b);
+    r = a - q * b;
+    if (r < 0) {
+        --q;
+        r += b;
+    } else if (r >= b) {
+        ++q;
+        r -= b;
+    }
+    return q;
+}
+
+// Split point i of [0, total) into n parts: floor(total * i / n), computed in
+// fp64 (exact operands for total * n < 2^53; the rounded quotient is monotone
+// in i and exact at i = 0 and i = n, so the parts tile the range).
+__device__ __forceinline__ long long split_point(long long total, int i, int n) {
+    return (long long)floor((double)total * (double)i / (double)n);
+}
 
 __device__ __forceinline__ bool decode_block(const Geo &g, int lin, int &n, int &by, int &bx) {
     if (lin < 0 || lin >= g.cap) return false;
@@ -53,11 +77,10 @@ __device__ __forceinline__ bool listed(const int32_t *__restrict__ idx, int cnt,
 
 // ---------------------------------------------------------------------------
 // Copying the cache outside the listed blocks.  A workgroup first marks every
-// listed block in an LDS bitmap (one batched read of idx[0, count)), then copies
-// its units.  Unit u = `xw` consecutive pixels of one output row; pixels of
-// listed blocks are skipped (the convolution writes them).  CB loads in
-// flight per thread.  Without room for the bitmap, a binary search over the ascending
-// list decides per block.
+// listed block in an LDS bitmap (one batched read of idx[0, count)), then
+// copies a contiguous span of the output's 16-byte vectors, skipping the
+// pixels of listed blocks (the convolution writes them).  Without room for
+// the bitmap, a binary search over the ascending list decides per vector.
 // ---------------------------------------------------------------------------
 
 template <int NTHR>
@@ -78,41 +101,126 @@ __device__ void build_bitmap(const int32_t *__restrict__ idx, int cnt, int cap, 
     __syncthreads();
 }
 
-template <int CB, int NTHR>  // CB loads in flight per thread, NTHR threads per workgroup
-__device__ void copy_unit(const Geo &g, const int32_t *__restrict__ idx, int cnt, const uint32_t *bm,
-                          const uint8_t *__restrict__ cache, uint8_t *__restrict__ out, const CopyCfg &cc, int u,
-                          uint8_t *on) {
-    const int upr = cc.units_per_row;
-    const int row = u / upr;  // n*ho + y
-    const int x0 = (u - row * upr) * cc.xw;
-    const int x1 = min(g.wo, x0 + cc.xw);
-    const int n = row / g.ho, y = row - n * g.ho;
-    const int by = y / g.b, j0 = x0 / g.b, j1 = (x1 - 1) / g.b;
-    __syncthreads();  // `on` may still be read by the previous unit
-    for (int j = threadIdx.x; j <= j1 - j0; j += NTHR) {
-        const int lin = (n * g.nby + by) * g.nbx + j0 + j;
-        on[j] = bm ? (bm[lin >> 5] >> (lin & 31)) & 1u : (listed(idx, cnt, lin) ? 1 : 0);
+// Vectors [v0, v1) of the output, flattened over (n, y, x, vector).  Thread t
+// takes v0 + t, v0 + t + NTHR, ...; its pixel coordinates are divided out once
+// and then advanced by addition.
+template <int CB, int NTHR>
+struct CopyWalk {
+    long long v, v1;
+    int cv, x, y, n, dp, dcv;
+
+    __device__ void init(const Geo &g, const CopyCfg &cc, long long v0, long long v1_) {
+        v = v0 + threadIdx.x;
+        v1 = v1_;
+        long long r;
+        const long long pix = div_ll(v, cc.vpp, r);
+        cv = (int)r;
+        const long long row = div_ll(pix, g.wo, r);
+        x = (int)r;
+        n = (int)div_ll(row, g.ho, r);
+        y = (int)r;
+        dp = NTHR / cc.vpp;  // pixels and vectors per stride
+        dcv = NTHR - dp * cc.vpp;
     }
-    __syncthreads();
-    const int row_bytes = cc.row_bytes, vpp = row_bytes >> 4;  // 16-byte vectors per pixel
-    const size_t base = ((size_t)row * g.wo + x0) * row_bytes;
-    const int nv = (x1 - x0) * vpp;
-    for (int v0 = threadIdx.x; v0 < nv; v0 += CB * NTHR) {
-        u32x4 r[CB];
-        bool go[CB];
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int v = v0 + i * NTHR;
-            go[i] = false;
-            if (v < nv) {
-                const int xl = fdiv(v, cc.m_vpp);
-                go[i] = !on[(x0 + xl) / g.b - j0];
-                if (go[i]) r[i] = ld16(cache + base + (size_t)v * 16);
+    // block index of the current vector
+    __device__ __forceinline__ int lin(const Geo &g, const CopyCfg &cc) const {
+        return (n * g.nby + fdiv(y, cc.m_b)) * g.nbx + fdiv(x, cc.m_b);
+    }
+    // on to this thread's next vector
+    __device__ __forceinline__ void step(const Geo &g, const CopyCfg &cc) {
+        v += NTHR;
+        cv += dcv;
+        x += dp;
+        if (cv >= cc.vpp) {
+            cv -= cc.vpp;
+            ++x;
+        }
+        while (x >= g.wo) {
+            x -= g.wo;
+            if (++y == g.ho) {
+                y = 0;
+                ++n;
             }
         }
+    }
+    // Loads of this thread's next CB vectors and their block indices.  The
+    // loads are unconditional (past the span they re-read its last vector,
+    // flagged -1), so a later wait can cover just the batch it needs.
+    __device__ long long fill(const Geo &g, const CopyCfg &cc, const uint8_t *__restrict__ cache, u32x4 (&r)[CB],
+                              int (&lin_)[CB]) {
+        const long long vb = v;
 #pragma unroll
-        for (int i = 0; i < CB; ++i)
-            if (go[i]) st16(out + base + (size_t)(v0 + i * NTHR) * 16, r[i]);
+        for (int i = 0; i < CB; ++i) {
+            const bool ok = v < v1;
+            lin_[i] = ok ? lin(g, cc) : -1;
+            r[i] = ld16(cache + (ok ? v : v1 - 1) * 16);
+            if (ok) step(g, cc);
+        }
+        return vb;
+    }
+};
+
+__device__ __forceinline__ bool block_listed(const uint32_t *bm, const int32_t *__restrict__ idx, int cnt, int lin) {
+    return bm ? ((bm[lin >> 5] >> (lin & 31)) & 1u) : listed(idx, cnt, lin);
+}
+
+// Stores of one batch, skipping vectors of listed blocks.
+template <int CB, int NTHR>
+__device__ __forceinline__ void copy_drain(uint8_t *__restrict__ out, long long vb, const u32x4 (&r)[CB],
+                                           const int (&lin)[CB], const uint32_t *bm, const int32_t *__restrict__ idx,
+                                           int cnt) {
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+        if (lin[i] >= 0 && !block_listed(bm, idx, cnt, lin[i])) st16(out + (vb + (long long)i * NTHR) * 16, r[i]);
+    }
+}
+
+// The copy of [v0, v1), software pipelined: the next batch's loads are in
+// flight while the current batch is stored, so reads and writes overlap.
+template <int CB, int NTHR>
+__device__ void copy_span(const Geo &g, const CopyCfg &cc, const uint32_t *bm, const int32_t *__restrict__ idx,
+                          int cnt, const uint8_t *__restrict__ cache, uint8_t *__restrict__ out, long long v0,
+                          long long v1) {
+    if (v0 + threadIdx.x >= v1) return;
+    CopyWalk<CB, NTHR> w;
+    w.init(g, cc, v0, v1);
+    u32x4 ra[CB], rb[CB];
+    int la[CB], lb[CB];
+    long long va = w.fill(g, cc, cache, ra, la);
+    for (;;) {
+        if (w.v >= v1) {
+            copy_drain<CB, NTHR>(out, va, ra, la, bm, idx, cnt);
+            return;
+        }
+        const long long vb = w.fill(g, cc, cache, rb, lb);
+        copy_drain<CB, NTHR>(out, va, ra, la, bm, idx, cnt);
+        if (w.v >= v1) {
+            copy_drain<CB, NTHR>(out, vb, rb, lb, bm, idx, cnt);
+            return;
+        }
+        va = w.fill(g, cc, cache, ra, la);
+        copy_drain<CB, NTHR>(out, vb, rb, lb, bm, idx, cnt);
+    }
+}
+
+// The part [lo, hi) of the copy that workgroup `bid` takes.  The workgroups
+// without a tile come first (they start at once): up to free_vec vectors each
+// per tile of the busiest workgroup.  What remains is split evenly over the
+// others, after their tiles.
+__device__ __forceinline__ void copy_split(const CopyCfg &cc, int ntiles, int grid, int bid, long long &lo,
+                                           long long &hi) {
+    const long long nvec = cc.nvec;
+    const int busy = min(ntiles, grid), nfree = grid - busy;
+    const int rounds = (ntiles + grid - 1) / grid;
+    long long to_free = (long long)nfree * cc.free_vec * max(rounds, 1);
+    if (busy == 0 || to_free > nvec) to_free = nvec;
+    if (bid >= busy) {
+        lo = split_point(to_free, bid - busy, nfree);
+        hi = split_point(to_free, bid - busy + 1, nfree);
+    } else {
+        const long long rest = nvec - to_free;
+        lo = to_free + split_point(rest, bid, busy);
+        hi = to_free + split_point(rest, bid + 1, busy);
     }
 }
 
@@ -260,7 +368,31 @@ struct ConvArgs {
 };
 
 constexpr int kConvWaves = 8;  // waves per workgroup of the implicit GEMM
+constexpr int kCopyBitmapWords = 1024;  // static LDS bitmap of listed blocks for the copy (32768 blocks)
 constexpr int kConvThreads = 64 * kConvWaves;
+
+// This wave's weight fragments for the chunk at input channel c0: K steps
+// wave, wave + 8, ... (tap, KS-channel slice), 16 output channels per N
+// subtile.  Unconditional loads at clamped addresses (the convolution zeroes
+// fragments outside the weight tensor where it uses them).
+template <int DT, int NT, int SMAX>
+__device__ __forceinline__ void load_weights(const ConvArgs &a, u32x4 (&bfr)[SMAX][NT], int c0, int n0, int wave,
+                                             int lane, int steps, int kpc) {
+    constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
+    const Geo &g = a.g;
+    const int k2 = g.k * g.k, kl = (lane >> 4) * EPV;
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int stp = min(wave + kConvWaves * j, steps - 1);
+        const int tap = stp / kpc, kk = stp - tap * kpc;
+        const int cb = min(c0 + kk * KS + kl, g.cin - EPV);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = min(n0 + nt * 16 + (lane & 15), g.cout - 1);
+            bfr[j][nt] = ld16(a.w + (((size_t)col * k2 + tap) * g.cin + cb) * ES);
+        }
+    }
+}
 
 // K steps per wave and chunk whose weight fragments a wave holds in registers
 template <int NT>
@@ -281,12 +413,16 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     constexpr int OPT = (BM * VPR + NTHR - 1) / NTHR;  // output vectors per thread
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // per staged slot: image, input-window origin, output-block origin
-    __shared__ int s_n[BM + 1], s_iy[BM + 1], s_ix[BM + 1], s_oy[BM + 1], s_ox[BM + 1];
-    __shared__ uint8_t s_on[256];
+    __shared__ int s_n[BM + 1], s_iy[BM + 1], s_ix[BM + 1], s_oy[BM + 1], s_ox[BM + 1], s_cnt;
+    __shared__ uint32_t s_bm[FUSED ? kCopyBitmapWords : 1];
+    __shared__ float s_bias[BN];
+    static_assert((BN & (BN - 1)) == 0 && BN <= 64, "wave 0 reads the tile's bias");
+    static_assert(BM <= 64, "wave 0 fills the slot table: at most 64 slots per tile");
 
     const Geo &g = a.g;
     const ConvCfg &c = a.c;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
     const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
     const int mcap = g.cap * b2;            // rows at full capacity (checked on the host)
     const int ntn = (g.cout + BN - 1) / BN;
@@ -296,12 +432,20 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     const int kpc = c.ck / KS;              // K steps per tap in a chunk
     const int steps = k2 * kpc;             // K steps per chunk
     const int kl = (lane >> 4) * EPV;       // this lane group's element offset inside a step
-    const int cnt_raw = *a.count;           // needed only to drop tiles beyond the list
-    int ntiles = -1;
+    int ntiles = -1, cnt_seen = 0;
+    // With the copy, the bitmap of listed blocks is built from a read of the
+    // list's first NTHR entries that rides along with the first tile's reads.
+    const int bm_words = (g.cap + 31) >> 5;
+    const bool spec_bm = FUSED && a.cc.nvec > 0 && bm_words <= kCopyBitmapWords;
+    bool spec_done = false;
+    if (spec_bm)
+        for (int q = tid; q < bm_words; q += NTHR) s_bm[q] = 0u;
     uint8_t *As = smem;
     float *part = (float *)smem;
+    const float *bsrc = a.bias ? a.bias : (const float *)a.w;  // any readable floats when there is no bias
 
     for (int t = blockIdx.x;; t += grid) {
+        if (ntiles >= 0 && t >= ntiles) break;  // known after the first tile
         const int tm = t / ntn, tn = t - tm * ntn;
         const int m0 = tm * BM;
         if (m0 >= mcap) break;
@@ -310,50 +454,50 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         const int s_hi = min(g.cap - 1, fdiv(m0 + BM - 1, c.m_b2));
         const int ns = s_hi - s_lo + 1;
         __syncthreads();  // the previous tile is done with LDS and the slot table
-        // Reads that do not depend on the block list go out together: the tile's
-        // block indices (before `count` is known), this wave's weight fragments
-        // for the first chunk, and the bias.
-        int lin = -1;
-        if (FUSED && tid < ns) lin = a.idx[s_lo + tid];
+        // First round trip: the list length and the tile's block indices (read
+        // before the length is known), this wave's weight fragments for the
+        // first chunk, and the bias.  Every read is unconditional (at a clamped
+        // address; what lies outside the tensors is zeroed where it is used), so
+        // each wait covers only the reads it needs.  Only wave 0 waits for the
+        // list: it fills the slot table while the other waves' reads land.
+        // (cap >> 31 is 0: the per-lane address keeps the length in a vector
+        // register, so the compiler does not move its wait up to the load.)
+        const int cnt_raw =
+            __hip_atomic_load(a.count + (lane & (g.cap >> 31)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int lin = FUSED ? a.idx[s_lo + min(lane, ns - 1)] : 0;
+        const int spec = FUSED ? a.idx[min(tid, g.cap - 1)] : 0;
+        const float bv = bsrc[min(n0 + (lane & (BN - 1)), g.cout - 1)];
         u32x4 bfr[SMAX][NT];
-#pragma unroll
-        for (int j = 0; j < SMAX; ++j) {
-            const int stp = wave + NW * j;
-            const int tap = stp / kpc, kk = stp - tap * kpc;
-            const int cb = kk * KS + kl;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int col = n0 + nt * 16 + (lane & 15);
-                bfr[j][nt] = u32x4{0u, 0u, 0u, 0u};
-                if (stp < steps && col < g.cout && cb < g.cin)
-                    bfr[j][nt] = ld16(a.w + (((size_t)col * k2 + tap) * g.cin + cb) * ES);
+        load_weights<DT, NT, SMAX>(a, bfr, 0, n0, wave, lane, steps, kpc);
+        __builtin_amdgcn_sched_barrier(0);  // every read above is issued before wave 0 waits for the list
+        if (wave == 0) {
+            if (lane == 0) s_cnt = min(max(cnt_raw, 0), g.cap);
+            if (lane < BN) s_bias[lane] = (a.bias && n0 + lane < g.cout) ? bv : 0.f;
+            if (lane < ns) {
+                int n = -1, by = 0, bx = 0;
+                if (FUSED) {
+                    if (!decode_block(g, lin, n, by, bx)) n = -1;
+                } else {
+                    n = 0;  // stacked blocks: positions inside the block tensor only
+                }
+                s_n[lane] = n;
+                s_iy[lane] = by * g.b * g.s - g.p;
+                s_ix[lane] = bx * g.b * g.s - g.p;
+                s_oy[lane] = by * g.b;
+                s_ox[lane] = bx * g.b;
             }
         }
-        float bias_r[OPT][8];
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-            const int co = n0 + ((tid + o * NTHR) % VPR) * 8;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bias_r[o][j] = (a.bias && co + j < g.cout) ? a.bias[co + j] : 0.f;
-        }
+        __syncthreads();  // the list length and the slot table are visible
         // the list length decides whether this tile exists
-        const int cnt = min(max(cnt_raw, 0), g.cap);
+        const int cnt = s_cnt;
+        cnt_seen = cnt;
+        if (spec_bm && !spec_done) {
+            if (tid < cnt && spec >= 0 && spec < g.cap) atomicOr(&s_bm[spec >> 5], 1u << (spec & 31));
+            spec_done = true;
+        }
         if (ntiles < 0) ntiles = ((cnt * b2 + BM - 1) / BM) * ntn;
         if (t >= ntiles) break;
         const int mrows = cnt * b2;
-        if (tid < ns) {
-            int n = -1, by = 0, bx = 0;
-            if (FUSED) {
-                if (!decode_block(g, lin, n, by, bx)) n = -1;
-            } else {
-                n = 0;  // stacked blocks: positions inside the block tensor only
-            }
-            s_n[tid] = n;
-            s_iy[tid] = by * g.b * g.s - g.p;
-            s_ix[tid] = bx * g.b * g.s - g.p;
-            s_oy[tid] = by * g.b;
-            s_ox[tid] = bx * g.b;
-        }
         // LDS byte offset of this lane's row in each M subtile (tap (0,0), channel 0)
         int rb[MT];
 #pragma unroll
@@ -376,27 +520,49 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         const int nslot = ns * ib2 * (vpc + 1);  // 16-byte LDS slots of the staged windows
         const int nq = (nslot + 63) / 64;        // 64-slot groups, one wave instruction each
         for (int c0 = 0; c0 < g.cin; c0 += c.ck) {
-            __syncthreads();  // slot table visible; every wave is done with the previous chunk
+            if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
             // Input windows straight from global memory into LDS: each wave fills
             // 64 consecutive 16-byte slots per instruction (lane i -> slot base + i;
             // a pixel occupies vpc slots plus one pad slot, left unwritten).
             // Slots outside the image or beyond c_in get zeros from their own lane.
-#pragma unroll 2
-            for (int q = wave; q < nq; q += NW) {
-                const int slot = q * 64 + lane;
-                const int P = fdiv(slot, c.m_vpc1), cvv = slot - P * (vpc + 1);
-                if (slot < nslot && cvv < vpc) {
-                    const int ch = c0 + cvv * EPV;
+            // Batches of QB slot groups per wave: decode, then every slot-table
+            // read of the batch, then every load.
+            constexpr int QB = 4;
+            for (int qb = wave; qb < nq; qb += NW * QB) {
+                int ls[QB], pix[QB], chv[QB];
+#pragma unroll
+                for (int i = 0; i < QB; ++i) {
+                    const int slot = (qb + NW * i) * 64 + lane;
+                    const int P = fdiv(slot, c.m_vpc1), cvv = slot - P * (vpc + 1);
+                    const bool act = slot < nslot && cvv < vpc;
+                    const int l = FUSED ? fdiv(P, c.m_ib2) : 0;
+                    ls[i] = act ? l : -1;
+                    pix[i] = FUSED ? P - l * ib2 : P;
+                    chv[i] = c0 + cvv * EPV;
+                }
+                int tn_[QB], ty[QB], tx[QB];
+                if (FUSED) {
+#pragma unroll
+                    for (int i = 0; i < QB; ++i) {
+                        const int l = max(ls[i], 0);
+                        tn_[i] = s_n[l];
+                        ty[i] = s_iy[l];
+                        tx[i] = s_ix[l];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < QB; ++i) {
+                    if (ls[i] < 0) continue;
+                    const int q = qb + NW * i;
                     const uint8_t *src = nullptr;
-                    if (ch < g.cin) {
+                    if (chv[i] < g.cin) {
                         if (FUSED) {
-                            const int ls = fdiv(P, c.m_ib2), pix = P - ls * ib2;
-                            const int yy = fdiv(pix, c.m_ib), xx = pix - yy * g.ib;
-                            const int n = s_n[ls], iy = s_iy[ls] + yy, ix = s_ix[ls] + xx;
-                            if (n >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w)
-                                src = a.src + ((((size_t)n * g.h + iy) * g.w + ix) * g.cin + ch) * ES;
+                            const int yy = fdiv(pix[i], c.m_ib), xx = pix[i] - yy * g.ib;
+                            const int iy = ty[i] + yy, ix = tx[i] + xx;
+                            if (tn_[i] >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w)
+                                src = a.src + ((((size_t)tn_[i] * g.h + iy) * g.w + ix) * g.cin + chv[i]) * ES;
                         } else {
-                            src = a.src + (((size_t)s_lo * ib2 + P) * g.cin + ch) * ES;
+                            src = a.src + (((size_t)s_lo * ib2 + pix[i]) * g.cin + chv[i]) * ES;
                         }
                     }
                     if (src)
@@ -404,71 +570,51 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
                                                          (__attribute__((address_space(3))) void *)(As + q * 1024),
                                                          16, 0, 0);
                     else
-                        st16(As + slot * 16, u32x4{0u, 0u, 0u, 0u});
+                        st16(As + (q * 64 + lane) * 16, u32x4{0u, 0u, 0u, 0u});
                 }
             }
-            if (c0 > 0) {  // the next chunk's weight fragments (the first chunk's are in flight)
-#pragma unroll
-                for (int j = 0; j < SMAX; ++j) {
-                    const int stp = wave + NW * j;
-                    const int tap = stp / kpc, kk = stp - tap * kpc;
-                    const int cb = c0 + kk * KS + kl;
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const int col = n0 + nt * 16 + (lane & 15);
-                        bfr[j][nt] = u32x4{0u, 0u, 0u, 0u};
-                        if (stp < steps && col < g.cout && cb < g.cin)
-                            bfr[j][nt] = ld16(a.w + (((size_t)col * k2 + tap) * g.cin + cb) * ES);
-                    }
-                }
-            }
+            if (c0 > 0)  // the next chunk's weight fragments (the first chunk's are in flight)
+                load_weights<DT, NT, SMAX>(a, bfr, c0, n0, wave, lane, steps, kpc);
             __builtin_amdgcn_s_waitcnt(0);  // the LDS loads and the weight fragments have landed
             __syncthreads();
+            // A fragments of step j + 1 are read from LDS while step j's MFMAs run.
+            u32x4 av[2][MT];
+            auto read_a = [&](int j, u32x4 (&dst)[MT]) {
+                const int stp = min(wave + NW * j, steps - 1);
+                const int tap = stp / kpc, kk = stp - tap * kpc;
+                const int ky = tap / g.k, kx = tap - ky * g.k;
+                const int aoff = (ky * g.ib + kx) * apix + (kk * KS + kl) * ES;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) dst[mt] = *(const u32x4 *)(As + rb[mt] + aoff);
+            };
+            if (wave < steps) read_a(0, av[0]);
 #pragma unroll
             for (int j = 0; j < SMAX; ++j) {
                 const int stp = wave + NW * j;
-                if (stp < steps) {
-                    const int tap = stp / kpc, kk = stp - tap * kpc;
-                    const int ky = tap / g.k, kx = tap - ky * g.k;
-                    const int aoff = (ky * g.ib + kx) * apix + (kk * KS + kl) * ES;
-                    u32x4 av[MT];
+                if (stp >= steps) break;
+                if (j + 1 < SMAX && stp + NW < steps) read_a(j + 1, av[(j + 1) & 1]);
+                const int kk = stp - (stp / kpc) * kpc;
+                const bool kin = c0 + kk * KS + kl < g.cin;
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) av[mt] = *(const u32x4 *)(As + rb[mt] + aoff);
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            acc[mt][nt] = MfmaStep<DT>::run(av[mt], bfr[j][nt], acc[mt][nt]);
-                }
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[mt][nt] = MfmaStep<DT>::run(
+                            av[j & 1][mt], (kin && n0 + nt * 16 + (lane & 15) < g.cout) ? bfr[j][nt] : u32x4{0u, 0u, 0u, 0u},
+                            acc[mt][nt]);
             }
         }
-        // Sum the 8 waves' partial tiles: waves 4..7 park theirs in LDS, waves 0..3
-        // add them in, park the sums, and every thread adds the four.
+        // Sum the 8 waves' partial tiles: every wave parks its tile in LDS, then
+        // each thread adds the eight copies of its output vector.
         // 16x16 accumulator layout: lane l holds rows 4*(l/16)+i, column l%16.
         __syncthreads();  // all waves done reading the staged windows
-        const int pw = wave & 3;
-        if (wave >= 4) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        part[(pw * BM + mt * 16 + (lane >> 4) * 4 + i) * PSTR + nt * 16 + (lane & 15)] =
-                            acc[mt][nt][i];
-        }
-        __syncthreads();
-        if (wave < 4) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float *q = &part[(pw * BM + mt * 16 + (lane >> 4) * 4 + i) * PSTR + nt * 16 + (lane & 15)];
-                        *q += acc[mt][nt][i];
-                    }
-        }
+                for (int i = 0; i < 4; ++i)
+                    part[(wave * BM + mt * 16 + (lane >> 4) * 4 + i) * PSTR + nt * 16 + (lane & 15)] = acc[mt][nt][i];
         __syncthreads();
 #pragma unroll
         for (int o = 0; o < OPT; ++o) {
@@ -482,9 +628,9 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             float sum[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float x = bias_r[o][j];
+                float x = s_bias[col + j];
 #pragma unroll
-                for (int w = 0; w < 4; ++w) x += part[(w * BM + row) * PSTR + col + j];
+                for (int w = 0; w < NW; ++w) x += part[(w * BM + row) * PSTR + col + j];
                 sum[j] = x;
             }
             const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
@@ -500,34 +646,29 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             }
         }
     }
-    if (FUSED && a.cc.units > 0) {
-        const int cnt = min(max(cnt_raw, 0), g.cap);
-        if (ntiles < 0) ntiles = ((cnt * b2 + BM - 1) / BM) * ntn;
-        // Copy units: the workgroups without a tile take up to twice the even
-        // share each (they start at once); the rest go round robin to the
-        // workgroups with a tile, after it.
-        const int units = a.cc.units;
-        const int busy = min(ntiles, grid), nfree = grid - busy;
-        const int share = (units + grid - 1) / grid;
-        const int to_free = nfree > 0 ? min(units, nfree * 2 * share) : 0;
-        int first, stride, last;
-        if ((int)blockIdx.x >= busy) {
-            first = blockIdx.x - busy;
-            stride = nfree;
-            last = to_free;
-        } else {
-            first = to_free + blockIdx.x;
-            stride = busy;
-            last = units;
+    if (FUSED && a.cc.nvec > 0) {
+        int cnt = cnt_seen;
+        if (ntiles < 0) {  // this workgroup had no tile position at all
+            cnt = min(max(__hip_atomic_load(a.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0), g.cap);
+            ntiles = ((cnt * b2 + BM - 1) / BM) * ntn;
         }
-        if (first < last) {
+        long long cp_lo, cp_hi;
+        copy_split(a.cc, ntiles, grid, blockIdx.x, cp_lo, cp_hi);
+        if (cp_lo < cp_hi) {
             uint32_t *bm = nullptr;
-            if (((g.cap + 31) >> 5) * 4 <= c.lds_bytes) {  // the GEMM's LDS is free now
-                bm = (uint32_t *)smem;
+            if (spec_done) {  // the first NTHR entries are in; add the rest
+                bm = s_bm;
+                __syncthreads();
+                for (int e = NTHR + tid; e < cnt; e += NTHR) {
+                    const int v = a.idx[e];
+                    if (v >= 0 && v < g.cap) atomicOr(&s_bm[v >> 5], 1u << (v & 31));
+                }
+                __syncthreads();
+            } else if (spec_bm || bm_words * 4 <= c.lds_bytes) {
+                bm = spec_bm ? s_bm : (uint32_t *)smem;  // the GEMM's LDS is free now
                 build_bitmap<NTHR>(a.idx, cnt, g.cap, bm);
             }
-            for (int u = first; u < last; u += stride)
-                copy_unit<16, NTHR>(g, a.idx, cnt, bm, a.cache, a.dst, a.cc, u, s_on);
+            copy_span<4, NTHR>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, cp_lo, cp_hi);
         }
     }
 }
@@ -601,19 +742,18 @@ hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const 
 
 // ---------------------------------------------------------------------------
 // step 5: scatter.  A persistent grid: each workgroup first writes listed
-// blocks' valid pixels (slot = workgroup, + grid, ...), then copy units
-// (unit u to workgroup (count + u) % grid) when copy_cached.
+// blocks' valid pixels (slot = workgroup, + grid, ...), then, when
+// copy_cached, an even share of the copy.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ob, const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ count, Geo g, uint32_t m_b,
                                                  const uint8_t *__restrict__ cache, uint8_t *__restrict__ out,
                                                  CopyCfg cc, int bm_bytes) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ uint8_t s_on[256];
     constexpr int U = 8;
     const int cnt = clamp_count(count, g.cap);
     const int grid = gridDim.x;
-    const int row_bytes = cc.row_bytes, vpp = row_bytes >> 4, b2 = g.b * g.b;
+    const int vpp = cc.vpp, row_bytes = vpp * 16, b2 = g.b * g.b;
     const int nv = b2 * vpp;
     for (int slot = blockIdx.x; slot < cnt; slot += grid) {
         int n, by, bx;
@@ -640,16 +780,15 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ob,
                 if (dst[i] != ~(size_t)0) st16(out + dst[i], r[i]);
         }
     }
-    if (cc.units > 0) {
-        int u0 = ((int)blockIdx.x - cnt) % grid;
-        if (u0 < 0) u0 += grid;
-        if (u0 < cc.units) {
+    if (cc.nvec > 0) {
+        const long long lo = split_point(cc.nvec, blockIdx.x, grid), hi = split_point(cc.nvec, blockIdx.x + 1, grid);
+        if (lo < hi) {
             uint32_t *bm = nullptr;
             if (bm_bytes > 0) {
                 bm = (uint32_t *)smem;
                 build_bitmap<256>(idx, cnt, g.cap, bm);
             }
-            for (int u = u0; u < cc.units; u += grid) copy_unit<16, 256>(g, idx, cnt, bm, cache, out, cc, u, s_on);
+            copy_span<4, 256>(g, cc, bm, idx, cnt, cache, out, lo, hi);
         }
     }
 }
@@ -658,10 +797,10 @@ hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, co
                           const void *cached, void *out, int grid, const CopyCfg &cc, hipStream_t st) {
     (void)dt;
     // bitmap of listed blocks for the copy, when it fits in 64 KiB of LDS
-    const long bm = cc.units > 0 ? ((long)(g.cap + 31) / 32) * 4 : 0;
+    const long bm = cc.nvec > 0 ? ((long)(g.cap + 31) / 32) * 4 : 0;
     const int bm_bytes = bm <= 64 * 1024 ? (int)bm : 0;
     hipLaunchKernelGGL(k_scatter, dim3(grid), dim3(256), bm_bytes, st, (const uint8_t *)out_blocks, idx, count, g,
-                       fast_div_magic(g.b), (const uint8_t *)cached, (uint8_t *)out, cc, bm_bytes);
+                       cc.m_b, (const uint8_t *)cached, (uint8_t *)out, cc, bm_bytes);
     return hipGetLastError();
 }
 

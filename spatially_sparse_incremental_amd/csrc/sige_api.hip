@@ -58,6 +58,8 @@ int derive(const sige_geom *gp, Geo *g) {
     if (cap > 0x7FFFFFFFLL) return fail(SIGE_ERANGE, "block capacity %lld exceeds int32", (long long)cap);
     const int64_t in_elems = (int64_t)q.n * q.h * q.w * q.c_in, out_elems = (int64_t)q.n * r.ho * r.wo * q.c_out;
     if (in_elems > (1LL << 40) || out_elems > (1LL << 40)) return fail(SIGE_ERANGE, "tensor too large");
+    if ((int64_t)r.ho * q.block > 0x7FFFFFFFLL || (int64_t)r.wo * q.block > 0x7FFFFFFFLL)
+        return fail(SIGE_ERANGE, "output %dx%d too large for block size %d", r.ho, r.wo, q.block);
     r.cap = (int)cap;
     *g = r;
     return SIGE_OK;
@@ -97,11 +99,11 @@ int finish(hipError_t e, const char *what, hipStream_t st) {
     return SIGE_OK;
 }
 
-constexpr int kStaticLds = 2048;  // the conv kernel's static LDS (slot table, copy flags), rounded up
+constexpr int kStaticLds = 6144;  // the conv kernel's static LDS (slot table, copy bitmap), rounded up
 
-struct DevInfo {
-    int lds = 64 * 1024;  // LDS per workgroup
-    int cus = 256;        // compute units
+struct DevInfo {  // defaults: gfx950
+    int lds = 160 * 1024;  // LDS per workgroup
+    int cus = 256;         // compute units
 };
 
 // Per-device limits, queried once per device (160 KiB LDS and 256 CUs on MI355X).
@@ -127,19 +129,23 @@ DevInfo dev_info() {
     return cache[dev];
 }
 
-// Copy units: segments of output rows of about 64 KiB, at most 254 blocks
-// wide (the per-unit block flags).
+// The copy of the cache outside the listed blocks, in 16-byte vectors.
+// free_vec: what a workgroup without a tile copies per tile of a busy one
+// (default 8192 vectors = 128 KiB, tuned on MI355X for the 256x256x128 layer;
+// SIGE_COPY_FREE_VEC overrides it for tuning).
 sige::CopyCfg copy_plan(const Geo &g, int es, bool copy) {
+    static int free_vec = -1;
+    if (free_vec < 0) {
+        const char *v = getenv("SIGE_COPY_FREE_VEC");
+        const long x = v ? strtol(v, nullptr, 10) : 0;
+        free_vec = (x > 0 && x < (1L << 30)) ? (int)x : 8192;
+    }
     sige::CopyCfg c{};
-    c.row_bytes = g.cout * es;
-    c.m_vpp = sige::fast_div_magic(c.row_bytes / 16);
-    int xw = (64 * 1024) / c.row_bytes;
-    if (xw < 1) xw = 1;
-    if (xw > 254 * g.b) xw = 254 * g.b;
-    if (xw > g.wo) xw = g.wo;
-    c.xw = xw;
-    c.units_per_row = (g.wo + xw - 1) / xw;
-    c.units = copy ? g.n * g.ho * c.units_per_row : 0;
+    c.vpp = g.cout * es / 16;
+    c.m_vpp = sige::fast_div_magic(c.vpp);
+    c.m_b = sige::fast_div_magic(g.b);
+    c.nvec = copy ? (long long)g.n * g.ho * g.wo * c.vpp : 0;
+    c.free_vec = free_vec;
     return c;
 }
 
@@ -182,7 +188,7 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
     if (((long)g.cap * b2 + BM) * b2 > 0x7FFFFFFFL) return fail(SIGE_ERANGE, "too many output rows for one launch");
     const DevInfo dv = dev_info();
     const long limit = (long)dv.lds - kStaticLds;
-    const long part = 4L * BM * (BN + 4) * 4;
+    const long part = 8L * BM * (BN + 4) * 4;  // the 8 waves' partial tiles
     const int kslices = (g.cin + ks - 1) / ks;
     int best = 0;
     long best_lds = 0;
@@ -201,7 +207,6 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
         return fail(SIGE_ERANGE, "staged windows (%d slots of %dx%d) do not fit in LDS", ns, g.ib, g.ib);
     c.ck = best;
     c.a_pix_stride = best * es + 16;
-    c.b_row_stride = 0;
     c.a_bytes = ns * ib2 * c.a_pix_stride;
     c.lds_bytes = (int)best_lds;
     c.m_ib2 = sige::fast_div_magic(ib2);

@@ -30,7 +30,6 @@ struct ConvCfg {
     int mt, nt;          // 16x16 tiles per workgroup along M (rows) and N (output channels)
     int ck;              // input channels staged per chunk
     int a_pix_stride;    // LDS bytes per staged input pixel (ck*es + 16)
-    int b_row_stride;    // unused (weights are read into registers)
     int a_bytes;         // LDS bytes of the staged input windows
     int lds_bytes;       // dynamic LDS per workgroup
     int ns_max;          // most block slots one M tile can touch
@@ -41,13 +40,14 @@ struct ConvCfg {
     uint32_t m_b2, m_b;    // fast_div_magic(b*b), fast_div_magic(b): output rows -> block slot, pixel
 };
 
-// Copy of the cache outside the listed blocks: units of `xw` pixels of one row.
+// Copy of the cache outside the listed blocks, in 16-byte vectors of the
+// output flattened over (n, y, x, vector of the channel row).
 struct CopyCfg {
-    int units;           // total units (0: no copy)
-    int xw;              // pixels per unit
-    int units_per_row;   // ceil(wo / xw)
-    int row_bytes;       // c_out * element size
-    uint32_t m_vpp;      // fast_div_magic(row_bytes / 16)
+    long long nvec;      // n * ho * wo * vpp (0: no copy)
+    int vpp;             // 16-byte vectors per output pixel
+    uint32_t m_vpp;      // fast_div_magic(vpp)
+    uint32_t m_b;        // fast_div_magic(b)
+    int free_vec;        // vectors a workgroup without a tile takes per tile of a busy one
 };
 
 hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix, int vpp, float tau,

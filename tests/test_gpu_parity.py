@@ -33,6 +33,8 @@ CASES = [
     ("tiny_blocks_f16", 1, 16, 16, 128, 128, 3, 1, 1, 2, "f16", 1, 0.03),
     ("one_px_blocks_bf16", 1, 9, 9, 32, 32, 3, 1, 1, 1, "bf16", 0, 0.05),
     ("wide_bf16", 1, 24, 40, 256, 160, 3, 1, 1, 6, "bf16", 1, 0.01),
+    # more listed blocks than one workgroup's threads (the copy's block bitmap is completed in a second pass)
+    ("many_blocks_f16", 1, 96, 96, 32, 32, 3, 1, 1, 2, "f16", 1, 0.10),
 ]
 
 
@@ -56,6 +58,7 @@ def test_layer_parity(case, fused):
     assert torch.equal(got["mask"], ref["mask"])
     assert got["count"] == ref["idx"].numel() > 0
     assert torch.equal(got["idx"], ref["idx"])
+    print(f"[case] {name}: {got['count']} listed blocks", flush=True)
     sel = active_pixels(ref["act"], b, ho, wo)
     keep = ~sel.expand_as(cache)
     assert torch.equal(got["out"][keep].view(torch.uint8), cache[keep].view(torch.uint8))
@@ -159,6 +162,38 @@ def test_single_layer_sparse_equals_dense_edited():
     got = run_layer_gpu(a_o, a_e, wt, bias, cache, g, 0)
     dense64 = oracle.dense_conv(a_e, wt, bias, k, 1, 1, out_f64=True)
     assert_close(got["out"], dense64, dt, None, "sparse vs dense edited")
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "three_step"])
+def test_block_grid_beyond_the_reduce_limit(fused):
+    # 200x200 one-pixel blocks: 40000 blocks, more than sige_reduce_mask takes, so
+    # the list comes from the oracle; the copy marks listed blocks without the
+    # static LDS bitmap
+    n, h, w, c, k, s, p, b = 1, 200, 200, 16, 3, 1, 1, 1
+    dt = torch.bfloat16
+    mask = random_mask(n, h, w, 0.03, 17)
+    a_o, a_e, wt, bias = layer_inputs(n, h, w, c, c, k, dt, 18, mask)
+    cache = rand((n, h, w, c), dt, 19)
+    act = oracle.block_activity(torch.from_numpy(mask), h, w, k, s, p, b, 0)
+    ref_idx = oracle.index_list(act)
+    cap = h * w
+    idx = torch.zeros(cap, dtype=torch.int32)
+    idx[:ref_idx.numel()] = ref_idx
+    idx, count = idx.cuda(), torch.tensor([ref_idx.numel()], dtype=torch.int32).cuda()
+    g = _geom(n, h, w, c, c, k, s, p, b)
+    wk, bs, ae, cg = ssi.weight_to_krsc(wt).cuda(), bias.cuda(), a_e.cuda(), cache.cuda()
+    if fused:
+        out = ssi.sige_sparse_conv_layer(ae, wk, bs, cg, idx, count, g)
+    else:
+        blocks = ssi.sige_gather(ae, g, idx, count)
+        out = ssi.sige_scatter(ssi.sige_conv_blocks(blocks, wk, bs, g, count), idx, count, g, cg)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, act, cache, out_f64=True)
+    sel = active_pixels(act, b, h, w)
+    o = out.cpu()
+    keep = ~sel.expand_as(cache)
+    assert torch.equal(o[keep].view(torch.uint8), cache[keep].view(torch.uint8))
+    assert_close(o, ref, dt, sel, "40000-block grid")
 
 
 def test_all_active_is_dense_conv():
