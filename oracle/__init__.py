@@ -66,6 +66,8 @@ def lib():
         L.oracle_scatter.argtypes = [c_void, c_int, c_long, c_void, c_int, c_int, c_int, c_int,
                                      c_int, c_void, c_void, c_int]
         L.oracle_num_threads.restype = c_int
+        L.oracle_restore_blocks.argtypes = [c_void, c_long, c_void, c_long, c_int, c_int, c_int, c_int, c_int,
+                                            c_int, c_void, c_void]
         L.oracle_set_threads.argtypes = [c_int]
         _lib = L
     return _lib
@@ -229,6 +231,20 @@ def scatter(out_blocks, idx, cache, b, copy_cached=True, out=None) -> torch.Tens
     rc = lib().oracle_scatter(_ptr(out_blocks), DT[cache.dtype], idx.numel(), _ptr(idx), n, ho, wo, cout, b,
                               _ptr(cache), _ptr(out), int(copy_cached))
     _check(rc, "scatter")
+    return out
+
+
+def restore_blocks(prev_idx, idx, cache, out, b) -> torch.Tensor:
+    """In place on `out` (NHWC, the previous edit's result): blocks listed in
+    prev_idx and not in idx get their cached pixels back.  idx may be None."""
+    cache = cache.contiguous()
+    assert out.is_contiguous() and out.shape == cache.shape and out.dtype == cache.dtype
+    n, ho, wo, cout = cache.shape
+    prev_idx = prev_idx.to(torch.int32).contiguous()
+    new = (idx if idx is not None else torch.zeros(0)).to(torch.int32).contiguous()
+    rc = lib().oracle_restore_blocks(_ptr(prev_idx), prev_idx.numel(), _ptr(new) if new.numel() else None,
+                                     new.numel(), n, ho, wo, cout, b, DT[cache.dtype], _ptr(cache), _ptr(out))
+    _check(rc, "restore_blocks")
     return out
 
 

@@ -432,3 +432,37 @@ int oracle_scatter(const void *out_blocks, int dt, long count, const int32_t *id
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* sequential edits ([REVIEW] ABSTRACT: results with sequential edits;          */
+/* Proposed method: the engine keeps its state between edits)                   */
+/* ------------------------------------------------------------------------ */
+/* `out` holds the previous edit's result: the cache outside the blocks of
+ * prev_idx[0, prev_count) and recomputed values inside them.  Every valid
+ * pixel of a block that prev_idx lists and idx[0, count) does not gets its
+ * cached value back (bit copy); blocks of both lists are left alone, since the
+ * new edit recomputes them.  idx may be NULL with count 0 (restore every
+ * previous block).  NHWC [n, ho, wo, cout]. */
+int oracle_restore_blocks(const int32_t *prev_idx, long prev_count, const int32_t *idx, long count, int n, int ho,
+                          int wo, int cout, int b, int dt, const void *cache, void *out) {
+    int es = elem_size(dt);
+    int nby = (ho + b - 1) / b, nbx = (wo + b - 1) / b;
+    for (long slot = 0; slot < prev_count; slot++) {
+        int32_t lin = prev_idx[slot];
+        int in_new = 0;
+        for (long e = 0; e < count; e++)
+            if (idx[e] == lin) in_new = 1;
+        if (in_new) continue;
+        int nn, i, j;
+        block_coords(lin, nby, nbx, &nn, &i, &j);
+        if (lin < 0 || nn >= n) return -1;
+        for (int py = 0; py < b; py++)
+            for (int px = 0; px < b; px++) {
+                int y = i * b + py, x = j * b + px;
+                if (y >= ho || x >= wo) continue;
+                long off = ((((long)nn * ho + y) * wo + x) * cout) * es;
+                memcpy((char *)out + off, (const char *)cache + off, (size_t)cout * es);
+            }
+    }
+    return 0;
+}

@@ -417,6 +417,76 @@ def test_three_steps_compose_to_the_layer(dt, k, s, p, b):
 
 
 # ---------------------------------------------------------------------------
+# sequential edits: restore the previous edit's blocks, then write the new ones
+# ---------------------------------------------------------------------------
+def _seq_case(dt, seed, h=29, w=23, k=3, s=1, p=1, b=4, cin=16, cout=8):
+    a_o = _rand((1, h, w, cin), dt, seed)
+    wt = _rand((cout, cin, k, k), dt, seed + 1, 0.2)
+    bias = _rand((cout,), torch.float32, seed + 2)
+    cache = oracle.dense_conv(a_o, wt, bias, k, s, p)
+    return a_o, wt, bias, cache
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_sequential_edits_through_restore_equal_fresh_layers(dt):
+    # out_k by restore(prev -> cache) + writing list k's blocks into a persistent
+    # buffer == the layer computed from scratch with the cache copy, bit for bit,
+    # over three edits with overlapping and disjoint block lists (partial edge blocks)
+    k, s, p, b = 3, 1, 1, 4
+    a_o, wt, bias, cache = _seq_case(dt, 111)
+    ho, wo = cache.shape[1:3]
+    rects = [(3, 9, 2, 8), (5, 14, 6, 12), (20, 29, 15, 23)]  # rows [y0, y1), cols [x0, x1)
+    out = cache.clone()
+    prev = torch.zeros(0, dtype=torch.int32)
+    for r, (y0, y1, x0, x1) in enumerate(rects):
+        m = np.zeros((29, 23), np.uint8)
+        m[y0:y1, x0:x1] = 1
+        a_e = synth.make_edit(a_o, m, "replace", 120 + r)
+        act = oracle.block_activity(oracle.diff_mask(a_o, a_e), 29, 23, k, s, p, b, 1)
+        idx = oracle.index_list(act)
+        fresh = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, act, cache)
+        oracle.restore_blocks(prev, idx, cache, out, b)
+        blocks = oracle.conv_blocks(oracle.gather(a_e, k, s, p, b, idx), wt, bias, k, s, b)
+        oracle.scatter(blocks, idx, cache, b, copy_cached=False, out=out)
+        assert torch.equal(out.view(torch.uint8), fresh.view(torch.uint8)), f"edit {r}"
+        prev = idx
+
+
+def test_restore_touches_exactly_the_blocks_left_behind():
+    # brute force on the block grid: pixels of blocks in prev and not in new take
+    # the cache; every other pixel keeps its value
+    dt = torch.bfloat16
+    n, ho, wo, c, b = 2, 13, 18, 8, 4
+    nby, nbx = -(-ho // b), -(-wo // b)
+    cache = _rand((n, ho, wo, c), dt, 131)
+    rng = np.random.default_rng(132)
+    for trial in range(20):
+        prev_act = rng.random((n, nby, nbx)) < 0.4
+        new_act = rng.random((n, nby, nbx)) < 0.4
+        before = _rand((n, ho, wo, c), dt, 140 + trial)
+        out = before.clone()
+        prev_idx = oracle.index_list(torch.from_numpy(prev_act.astype(np.uint8)))
+        new_idx = oracle.index_list(torch.from_numpy(new_act.astype(np.uint8)))
+        oracle.restore_blocks(prev_idx, new_idx, cache, out, b)
+        gone = torch.from_numpy(prev_act & ~new_act)
+        pix = _pixel_block_mask(gone, b, ho, wo)[..., None].expand_as(out)
+        expect = torch.where(pix, cache, before)
+        assert torch.equal(out.view(torch.int16), expect.view(torch.int16)), f"trial {trial}"
+
+
+def test_restore_special_cases():
+    dt = torch.float16
+    cache = _rand((1, 16, 16, 8), dt, 151)
+    out = _rand((1, 16, 16, 8), dt, 152)
+    idx = torch.tensor([0, 5, 6, 15], dtype=torch.int32)
+    same = oracle.restore_blocks(idx, idx, cache, out.clone(), 4)
+    assert torch.equal(same.view(torch.int16), out.view(torch.int16))  # prev == new: nothing to do
+    act = torch.ones((1, 4, 4), dtype=torch.uint8)
+    allb = oracle.restore_blocks(oracle.index_list(act), None, cache, out.clone(), 4)
+    assert torch.equal(allb.view(torch.int16), cache.view(torch.int16))  # no new list: all back to the cache
+
+
+# ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
 def _small_chain(dt=torch.bfloat16):
