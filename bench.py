@@ -190,6 +190,7 @@ def main():
     print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
 
     t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_nocopy = t_dense_ours = t_dense_miopen = None
+    t_seq = t_restore = None
     if not args.no_comparators:
         # the step without the cache copy (persistent output buffer)
         out_persist = cache.clone()
@@ -243,6 +244,29 @@ def main():
                 t_dense_miopen = timed_eager(lambda: F.conv2d(x_cl, w_cl, bias.to(dt), padding=L.pad), max(20, K // 5))
         except Exception as exc:  # noqa: BLE001 - report, do not hide
             print(f"[bench] MIOpen dense conv failed: {exc}", file=sys.stderr)
+
+        # sequential edits: two blob edits alternate through one persistent
+        # buffer; each step restores the previous edit's blocks that the new
+        # edit does not list, instead of copying the whole cache
+        a_e2 = synth.make_edit(a_o_cpu, synth.edit_shape(wl, seed + 1).raster(L.h, L.w), wl.edit_kind,
+                               seed + 1).to(dev)
+        seq_edits = [a_e, a_e2]
+        seq_idx = [torch.empty((cap,), dtype=torch.int32, device=dev) for _ in range(2)]
+        seq_cnt = [torch.zeros((1,), dtype=torch.int32, device=dev) for _ in range(2)]
+        seq_out = cache.clone()
+        seq_mask = torch.empty_like(mask)
+
+        def seq_step(k):
+            cur, prv = k % 2, (k + 1) % 2
+            ssi.sige_diff_mask(a_o, seq_edits[cur], wl.tau, mask=seq_mask)
+            ssi.sige_reduce_mask(seq_mask, g, L.dilate, idx=seq_idx[cur], count=seq_cnt[cur])
+            ssi.sige_restore_blocks(seq_idx[prv], seq_cnt[prv], seq_idx[cur], seq_cnt[cur], g, cache, seq_out)
+            ssi.sige_sparse_conv_layer(seq_edits[cur], w_krsc, bias, None, seq_idx[cur], seq_cnt[cur], g,
+                                       out=seq_out, copy_cached=False)
+
+        t_seq = graph_time(lambda: (seq_step(0), seq_step(1)), 5, 40) / 2  # both edits per call
+        t_restore = graph_time(lambda: ssi.sige_restore_blocks(seq_idx[1], seq_cnt[1], seq_idx[0], seq_cnt[0], g,
+                                                               cache, seq_out))
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -317,6 +341,8 @@ def main():
             "dense_ours_tflops": round(dense_flops / (t_dense_ours * 1e-6) / 1e12, 1),
             "step_no_copy_us": round(t_nocopy, 3),
             "step_three_call_us": round(t_three, 3),
+            "step_sequential_edits_us": round(t_seq, 3),
+            "restore_blocks_us": round(t_restore, 3),
             "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
         },
         "latency": {

@@ -157,6 +157,23 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
                            const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                            int copy_cached, void *stream);
 
+/* Sequential edits (nubint.ai review, "ABSTRACT": results with sequential
+ * edits; "Proposed method": the engine keeps its state between edits).  `out`
+ * is a persistent buffer that holds the previous edit's result: `cached`
+ * outside the blocks of prev_idx[0, *prev_count) and recomputed values inside
+ * them.  Every valid pixel of a block that prev_idx lists and idx[0, *count)
+ * does not gets its cached value back (a copy); blocks of both lists are left
+ * alone.  Then sige_sparse_conv_layer(..., copy_cached = 0) (or sige_scatter
+ * with copy_cached = 0) with idx on the same `out` gives the copy_cached = 1
+ * result without copying the whole tensor.  idx and count may both be NULL
+ * (restore every previous block).  Both lists ascending, as sige_reduce_mask
+ * writes them; entries outside [0, cap) are skipped.
+ *   cached, out: [n, ho, wo, c_out] in `dtype`, not overlapping.  c_in, k,
+ *   stride and pad of g only fix ho and wo. */
+int sige_restore_blocks(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
+                        const int32_t *count, const sige_geom *g, int dtype, const void *cached, void *out,
+                        void *stream);
+
 /* Name of a status code (static string). */
 const char *sige_strerror(int code);
 

@@ -19,7 +19,8 @@ SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERA
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_gather",
-           "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_strerror", "sige_last_error")
+           "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_strerror",
+           "sige_last_error")
 
 
 class SigeError(RuntimeError):
@@ -58,6 +59,7 @@ def lib():
         L.sige_conv_blocks.argtypes = [V, V, V, I, P, V, V, V]
         L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
         L.sige_sparse_conv_layer.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
+        L.sige_restore_blocks.argtypes = [V, V, V, V, P, I, V, V, V]
         L.sige_strerror.restype = ctypes.c_char_p
         L.sige_strerror.argtypes = [I]
         L.sige_last_error.restype = ctypes.c_char_p
@@ -211,3 +213,16 @@ def sige_sparse_conv_layer(a_edit, w_krsc, bias, cached, idx, count, g: Geom, ou
 def weight_to_krsc(w_oihw: torch.Tensor) -> torch.Tensor:
     """Repack PyTorch OIHW weights to the library's KRSC layout (once, at load time)."""
     return w_oihw.permute(0, 2, 3, 1).contiguous()
+
+
+def sige_restore_blocks(prev_idx, prev_count, idx, count, g: Geom, cached, out, stream=None):
+    """Sequential edits: in the persistent buffer `out`, the blocks of the
+    previous list that the new list (idx, count; both None: empty) does not
+    hold get the cache back.  Returns `out`."""
+    _dev(prev_idx, prev_count, idx, count, cached, out)
+    if (idx is None) != (count is None):
+        raise ValueError("idx and count must both be given or both be None")
+    rc = lib().sige_restore_blocks(_p(prev_idx), _p(prev_count), _p(idx), _p(count), ctypes.byref(g), _dt(cached),
+                                   _p(cached), _p(out), _stream(stream))
+    _check(rc, "sige_restore_blocks")
+    return out

@@ -804,4 +804,67 @@ hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, co
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Sequential edits: the previous edit's blocks that the new list does not hold
+// get the cache back.  A persistent grid: each workgroup marks the new list in
+// an LDS bitmap (when it fits), then takes previous blocks slot = workgroup,
+// + grid, ...; a block's valid pixels go as batches of 16-byte vectors.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_restore(const int32_t *__restrict__ prev_idx,
+                                                 const int32_t *__restrict__ prev_count,
+                                                 const int32_t *__restrict__ idx, const int32_t *__restrict__ count,
+                                                 Geo g, CopyCfg cc, const uint8_t *__restrict__ cache,
+                                                 uint8_t *__restrict__ out, int bm_bytes) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int U = 8;
+    const int np = clamp_count(prev_count, g.cap);
+    if ((int)blockIdx.x >= np) return;  // no previous block for this workgroup
+    const int nn = idx ? clamp_count(count, g.cap) : 0;
+    uint32_t *bm = nullptr;
+    if (idx && bm_bytes > 0) {
+        bm = (uint32_t *)smem;
+        build_bitmap<256>(idx, nn, g.cap, bm);
+    }
+    const int vpp = cc.vpp, row_bytes = vpp * 16, b2 = g.b * g.b;
+    const int nv = b2 * vpp;
+    for (int slot = blockIdx.x; slot < np; slot += gridDim.x) {
+        const int lin = prev_idx[slot];
+        int n, by, bx;
+        if (!decode_block(g, lin, n, by, bx)) continue;
+        if (idx && block_listed(bm, idx, nn, lin)) continue;
+        for (int v0 = threadIdx.x; v0 < nv; v0 += U * 256) {
+            u32x4 r[U];
+            size_t at[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int v = v0 + i * 256;
+                at[i] = ~(size_t)0;
+                if (v < nv) {
+                    const int pix = fdiv(v, cc.m_vpp), cvv = v - pix * vpp;
+                    const int py = fdiv(pix, cc.m_b), px = pix - py * g.b;
+                    const int y = by * g.b + py, x = bx * g.b + px;
+                    if (y < g.ho && x < g.wo) {
+                        at[i] = (((size_t)n * g.ho + y) * g.wo + x) * row_bytes + cvv * 16;
+                        r[i] = ld16(cache + at[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                if (at[i] != ~(size_t)0) st16(out + at[i], r[i]);
+        }
+    }
+}
+
+hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
+                          const int32_t *count, const Geo &g, const CopyCfg &cc, const void *cached, void *out,
+                          int grid, hipStream_t st) {
+    // bitmap of the new list, when it fits in 64 KiB of LDS (else a binary search per block)
+    const long bm = idx ? ((long)(g.cap + 31) / 32) * 4 : 0;
+    const int bm_bytes = bm <= 64 * 1024 ? (int)bm : 0;
+    hipLaunchKernelGGL(k_restore, dim3(grid), dim3(256), bm_bytes, st, prev_idx, prev_count, idx, count, g, cc,
+                       (const uint8_t *)cached, (uint8_t *)out, bm_bytes);
+    return hipGetLastError();
+}
+
 }  // namespace sige

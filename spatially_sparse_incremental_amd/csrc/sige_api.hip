@@ -404,4 +404,25 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
                   "sige_sparse_conv_layer", (hipStream_t)stream);
 }
 
+int sige_restore_blocks(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
+                        const int32_t *count, const sige_geom *gp, int dtype, const void *cached, void *out,
+                        void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!prev_idx || !prev_count || !cached || !out) return fail(SIGE_EINVAL, "NULL pointer");
+    if ((idx == nullptr) != (count == nullptr)) return fail(SIGE_EINVAL, "idx and count must both be given or both NULL");
+    if ((rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(cached, 16) || !aligned(out, 16)) return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * sige::elem_bytes(dtype);
+    if (overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    if ((rc = device_ready())) return rc;
+    const sige::CopyCfg cc = copy_plan(g, sige::elem_bytes(dtype), true);
+    const DevInfo dv = dev_info();
+    const int grid = g.cap < dv.cus ? g.cap : dv.cus;
+    return finish(sige::launch_restore(prev_idx, prev_count, idx, count, g, cc, cached, out, grid, (hipStream_t)stream),
+                  "sige_restore_blocks", (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -60,6 +60,9 @@ hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                        const int32_t *count, void *dst, const void *cache, const Geo &g, const ConvCfg &cfg,
                        const CopyCfg &cc, hipStream_t st);
+hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
+                          const int32_t *count, const Geo &g, const CopyCfg &cc, const void *cached, void *out,
+                          int grid, hipStream_t st);
 hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, const int32_t *count, const Geo &g,
                           const void *cached, void *out, int grid, const CopyCfg &cc, hipStream_t st);
 

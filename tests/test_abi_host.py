@@ -128,6 +128,19 @@ def test_conv_step_validation(lib):
                                       1, s) == ERANGE
 
 
+def test_restore_validation(lib):
+    s = _v(0)
+    g = _g()
+    f = lib.sige_restore_blocks
+    assert f(_v(A), _v(B), _v(C), _v(D), ctypes.byref(g), 3, _v(E), _v(E + (1 << 35)), s) == EDTYPE
+    assert f(None, _v(B), _v(C), _v(D), ctypes.byref(g), 1, _v(E), _v(E + (1 << 35)), s) == EINVAL
+    assert f(_v(A), _v(B), _v(C), None, ctypes.byref(g), 1, _v(E), _v(E + (1 << 35)), s) == EINVAL  # idx, no count
+    assert f(_v(A), _v(B), _v(C), _v(D), ctypes.byref(g), 1, _v(E), _v(E + 64), s) == EINVAL  # out overlaps cached
+    assert f(_v(A), _v(B), _v(C), _v(D), ctypes.byref(g), 1, _v(E + 8), _v(E + (1 << 35)), s) == EALIGN
+    assert f(_v(A), _v(B), _v(C), _v(D), ctypes.byref(_g(co=12)), 1, _v(E), _v(E + (1 << 35)), s) == EALIGN
+    assert f(_v(A), _v(B), None, None, ctypes.byref(_g(k=9)), 1, _v(E), _v(E + (1 << 35)), s) == EINVAL
+
+
 def test_strerror_names_every_code(lib):
     for code, name in [(0, b"SIGE_OK"), (EINVAL, b"SIGE_EINVAL"), (EDTYPE, b"SIGE_EDTYPE"), (EALIGN, b"SIGE_EALIGN"),
                        (L.SIGE_EHIP, b"SIGE_EHIP"), (ENODEV, b"SIGE_ENODEV"), (ERANGE, b"SIGE_ERANGE")]:
@@ -147,3 +160,5 @@ def test_valid_call_without_gpu_is_enodev(lib):
     assert lib.sige_reduce_mask(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), _v(0)) == ENODEV
     assert lib.sige_sparse_conv_layer(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g),
                                       _v(E + (1 << 35)), 1, _v(0)) == ENODEV
+    assert lib.sige_restore_blocks(_v(A), _v(B), None, None, ctypes.byref(g), 1, _v(E), _v(E + (1 << 35)),
+                                   _v(0)) == ENODEV
