@@ -174,6 +174,15 @@ int sige_restore_blocks(const int32_t *prev_idx, const int32_t *prev_count, cons
                         const int32_t *count, const sige_geom *g, int dtype, const void *cached, void *out,
                         void *stream);
 
+/* Sequential edits in one launch: sige_restore_blocks(prev_idx, prev_count,
+ * idx, count, ...) followed by sige_sparse_conv_layer(..., copy_cached = 0) on
+ * the persistent buffer `out`, with the restore done by the workgroups that
+ * have no tile of the convolution.  Same arguments and conventions as those two
+ * calls; every pointer except bias is required. */
+int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                   const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
+                                   const int32_t *count, int dtype, const sige_geom *g, void *out, void *stream);
+
 /* Name of a status code (static string). */
 const char *sige_strerror(int code);
 

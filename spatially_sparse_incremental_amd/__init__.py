@@ -20,5 +20,6 @@ from ._lib import (  # noqa: F401
     sige_restore_blocks,
     sige_scatter,
     sige_sparse_conv_layer,
+    sige_sparse_conv_layer_restore,
     weight_to_krsc,
 )

@@ -19,7 +19,8 @@ SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERA
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_gather",
-           "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_strerror",
+           "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
+           "sige_strerror",
            "sige_last_error")
 
 
@@ -60,6 +61,7 @@ def lib():
         L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
         L.sige_sparse_conv_layer.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
         L.sige_restore_blocks.argtypes = [V, V, V, V, P, I, V, V, V]
+        L.sige_sparse_conv_layer_restore.argtypes = [V, V, V, V, V, V, V, V, I, P, V, V]
         L.sige_strerror.restype = ctypes.c_char_p
         L.sige_strerror.argtypes = [I]
         L.sige_last_error.restype = ctypes.c_char_p
@@ -225,4 +227,18 @@ def sige_restore_blocks(prev_idx, prev_count, idx, count, g: Geom, cached, out, 
     rc = lib().sige_restore_blocks(_p(prev_idx), _p(prev_count), _p(idx), _p(count), ctypes.byref(g), _dt(cached),
                                    _p(cached), _p(out), _stream(stream))
     _check(rc, "sige_restore_blocks")
+    return out
+
+
+def sige_sparse_conv_layer_restore(a_edit, w_krsc, bias, cached, prev_idx, prev_count, idx, count, g: Geom, out,
+                                   stream=None):
+    """Sequential edits in one launch: restore the previous list's blocks that
+    the new list does not hold, and write the new blocks, into `out`."""
+    _dev(a_edit, w_krsc, bias, cached, prev_idx, prev_count, idx, count, out)
+    if w_krsc.dtype != a_edit.dtype or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("weights must match the activation dtype; bias must be fp32")
+    rc = lib().sige_sparse_conv_layer_restore(_p(a_edit), _p(w_krsc), _p(bias), _p(cached), _p(prev_idx),
+                                              _p(prev_count), _p(idx), _p(count), _dt(a_edit), ctypes.byref(g),
+                                              _p(out), _stream(stream))
+    _check(rc, "sige_sparse_conv_layer_restore")
     return out

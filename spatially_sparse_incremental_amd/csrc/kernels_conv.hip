@@ -225,6 +225,60 @@ __device__ __forceinline__ void copy_split(const CopyCfg &cc, int ntiles, int gr
 }
 
 // ---------------------------------------------------------------------------
+// Sequential edits: the previous edit's blocks that the new list does not hold
+// get the cache back.  restore_slots takes previous-list slots first, first +
+// step, ... below end; a block's valid pixels go as batches of 16-byte vectors.
+// ---------------------------------------------------------------------------
+template <int NTHR>
+__device__ void restore_slots(const Geo &g, const CopyCfg &cc, const int32_t *__restrict__ prev_idx, int first,
+                              int step, int end, const uint32_t *bm, const int32_t *__restrict__ idx, int cnt,
+                              const uint8_t *__restrict__ cache, uint8_t *__restrict__ out) {
+    constexpr int U = 8;
+    const int vpp = cc.vpp, row_bytes = vpp * 16, nv = g.b * g.b * vpp;
+    for (int slot = first; slot < end; slot += step) {
+        const int lin = prev_idx[slot];
+        int n, by, bx;
+        if (!decode_block(g, lin, n, by, bx)) continue;
+        if (idx && block_listed(bm, idx, cnt, lin)) continue;
+        for (int v0 = threadIdx.x; v0 < nv; v0 += U * NTHR) {
+            u32x4 r[U];
+            size_t at[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int v = v0 + i * NTHR;
+                at[i] = ~(size_t)0;
+                if (v < nv) {
+                    const int pix = fdiv(v, cc.m_vpp), cvv = v - pix * vpp;
+                    const int py = fdiv(pix, cc.m_b), px = pix - py * g.b;
+                    const int y = by * g.b + py, x = bx * g.b + px;
+                    if (y < g.ho && x < g.wo) {
+                        at[i] = (((size_t)n * g.ho + y) * g.wo + x) * row_bytes + cvv * 16;
+                        r[i] = ld16(cache + at[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                if (at[i] != ~(size_t)0) st16(out + at[i], r[i]);
+        }
+    }
+}
+
+// The slots [lo, hi) of the previous list that workgroup `bid` restores: the
+// workgroups without a tile share them evenly; without such workgroups, all
+// share them after their tiles.
+__device__ __forceinline__ void restore_split(int np, int ntiles, int grid, int bid, long long &lo, long long &hi) {
+    const int busy = min(ntiles, grid), nfree = grid - busy;
+    if (nfree > 0) {
+        lo = bid >= busy ? split_point(np, bid - busy, nfree) : 0;
+        hi = bid >= busy ? split_point(np, bid - busy + 1, nfree) : 0;
+    } else {
+        lo = split_point(np, bid, grid);
+        hi = split_point(np, bid + 1, grid);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // step 3: gather.  One workgroup per listed block (grid-stride over slots).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ a, Geo g, int row_bytes, uint32_t m_vpp,
@@ -362,6 +416,8 @@ struct ConvArgs {
     const int32_t *count;
     uint8_t *dst;
     const uint8_t *cache;
+    const int32_t *prev_idx;    // restore mode: the previous edit's list (NULL: none)
+    const int32_t *prev_count;
     Geo g;
     ConvCfg c;
     CopyCfg cc;
@@ -433,10 +489,10 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     const int steps = k2 * kpc;             // K steps per chunk
     const int kl = (lane >> 4) * EPV;       // this lane group's element offset inside a step
     int ntiles = -1, cnt_seen = 0;
-    // With the copy, the bitmap of listed blocks is built from a read of the
+    // With the copy (or the restore), the bitmap of listed blocks is built from a read of the
     // list's first NTHR entries that rides along with the first tile's reads.
     const int bm_words = (g.cap + 31) >> 5;
-    const bool spec_bm = FUSED && a.cc.nvec > 0 && bm_words <= kCopyBitmapWords;
+    const bool spec_bm = FUSED && (a.cc.nvec > 0 || a.prev_idx) && bm_words <= kCopyBitmapWords;
     bool spec_done = false;
     if (spec_bm)
         for (int q = tid; q < bm_words; q += NTHR) s_bm[q] = 0u;
@@ -646,15 +702,21 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             }
         }
     }
-    if (FUSED && a.cc.nvec > 0) {
+    if (FUSED && (a.cc.nvec > 0 || a.prev_idx)) {
         int cnt = cnt_seen;
         if (ntiles < 0) {  // this workgroup had no tile position at all
             cnt = min(max(__hip_atomic_load(a.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0), g.cap);
             ntiles = ((cnt * b2 + BM - 1) / BM) * ntn;
         }
-        long long cp_lo, cp_hi;
-        copy_split(a.cc, ntiles, grid, blockIdx.x, cp_lo, cp_hi);
-        if (cp_lo < cp_hi) {
+        // this workgroup's part: vectors of the copy, or slots of the previous list
+        long long lo, hi;
+        if (a.prev_idx) {
+            const int np = clamp_count(a.prev_count, g.cap);
+            restore_split(np, ntiles, grid, blockIdx.x, lo, hi);
+        } else {
+            copy_split(a.cc, ntiles, grid, blockIdx.x, lo, hi);
+        }
+        if (lo < hi) {
             uint32_t *bm = nullptr;
             if (spec_done) {  // the first NTHR entries are in; add the rest
                 bm = s_bm;
@@ -668,7 +730,10 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
                 bm = spec_bm ? s_bm : (uint32_t *)smem;  // the GEMM's LDS is free now
                 build_bitmap<NTHR>(a.idx, cnt, g.cap, bm);
             }
-            copy_span<4, NTHR>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, cp_lo, cp_hi);
+            if (a.prev_idx)
+                restore_slots<NTHR>(g, a.cc, a.prev_idx, (int)lo, 1, (int)hi, bm, a.idx, cnt, a.cache, a.dst);
+            else
+                copy_span<4, NTHR>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, lo, hi);
         }
     }
 }
@@ -729,10 +794,11 @@ static hipError_t launch_conv_dt(int fused, const ConvArgs &args, hipStream_t st
 }
 
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
-                       const int32_t *count, void *dst, const void *cache, const Geo &g, const ConvCfg &cfg,
-                       const CopyCfg &cc, hipStream_t st) {
+                       const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
+                       const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
+                       hipStream_t st) {
     ConvArgs args{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
-                  (const uint8_t *)cache, g, cfg, cc};
+                  (const uint8_t *)cache, prev_idx, prev_count, g, cfg, cc};
     switch (dt) {
     case 0: return launch_conv_dt<0>(fused, args, st);
     case 1: return launch_conv_dt<1>(fused, args, st);
@@ -805,18 +871,14 @@ hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, co
 }
 
 // ---------------------------------------------------------------------------
-// Sequential edits: the previous edit's blocks that the new list does not hold
-// get the cache back.  A persistent grid: each workgroup marks the new list in
-// an LDS bitmap (when it fits), then takes previous blocks slot = workgroup,
-// + grid, ...; a block's valid pixels go as batches of 16-byte vectors.
-// ---------------------------------------------------------------------------
+// The standalone restore: a persistent grid, each workgroup marks the new list
+// in an LDS bitmap (when it fits), then takes slots workgroup, + grid, ...
 __global__ __launch_bounds__(256) void k_restore(const int32_t *__restrict__ prev_idx,
                                                  const int32_t *__restrict__ prev_count,
                                                  const int32_t *__restrict__ idx, const int32_t *__restrict__ count,
                                                  Geo g, CopyCfg cc, const uint8_t *__restrict__ cache,
                                                  uint8_t *__restrict__ out, int bm_bytes) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int U = 8;
     const int np = clamp_count(prev_count, g.cap);
     if ((int)blockIdx.x >= np) return;  // no previous block for this workgroup
     const int nn = idx ? clamp_count(count, g.cap) : 0;
@@ -825,35 +887,7 @@ __global__ __launch_bounds__(256) void k_restore(const int32_t *__restrict__ pre
         bm = (uint32_t *)smem;
         build_bitmap<256>(idx, nn, g.cap, bm);
     }
-    const int vpp = cc.vpp, row_bytes = vpp * 16, b2 = g.b * g.b;
-    const int nv = b2 * vpp;
-    for (int slot = blockIdx.x; slot < np; slot += gridDim.x) {
-        const int lin = prev_idx[slot];
-        int n, by, bx;
-        if (!decode_block(g, lin, n, by, bx)) continue;
-        if (idx && block_listed(bm, idx, nn, lin)) continue;
-        for (int v0 = threadIdx.x; v0 < nv; v0 += U * 256) {
-            u32x4 r[U];
-            size_t at[U];
-#pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int v = v0 + i * 256;
-                at[i] = ~(size_t)0;
-                if (v < nv) {
-                    const int pix = fdiv(v, cc.m_vpp), cvv = v - pix * vpp;
-                    const int py = fdiv(pix, cc.m_b), px = pix - py * g.b;
-                    const int y = by * g.b + py, x = bx * g.b + px;
-                    if (y < g.ho && x < g.wo) {
-                        at[i] = (((size_t)n * g.ho + y) * g.wo + x) * row_bytes + cvv * 16;
-                        r[i] = ld16(cache + at[i]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < U; ++i)
-                if (at[i] != ~(size_t)0) st16(out + at[i], r[i]);
-        }
-    }
+    restore_slots<256>(g, cc, prev_idx, blockIdx.x, gridDim.x, np, bm, idx, nn, cache, out);
 }
 
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,

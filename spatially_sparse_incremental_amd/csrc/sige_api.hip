@@ -348,7 +348,8 @@ int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, 
     if ((rc = choose_conv(g, dtype, 0, 0, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, false);
-    return finish(sige::launch_conv(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, g, cfg, cc,
+    return finish(sige::launch_conv(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, nullptr,
+                                    nullptr, g, cfg, cc,
                                     (hipStream_t)stream),
                   "sige_conv_blocks", (hipStream_t)stream);
 }
@@ -400,8 +401,35 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
     return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
-                                    g, cfg, cc, (hipStream_t)stream),
+                                    nullptr, nullptr, g, cfg, cc, (hipStream_t)stream),
                   "sige_sparse_conv_layer", (hipStream_t)stream);
+}
+
+int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                   const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
+                                   const int32_t *count, int dtype, const sige_geom *gp, void *out, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!a_edit || !w_krsc || !cached || !prev_idx || !prev_count || !idx || !count || !out)
+        return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || !aligned(cached, 16))
+        return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
+    if (overlap(out, obytes, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
+        return fail(SIGE_EINVAL, "out overlaps a_edit");
+    if (overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    ConvCfg cfg;
+    if ((rc = choose_conv(g, dtype, 1, 1, &cfg))) return rc;  // the full persistent grid: free workgroups restore
+    if ((rc = device_ready())) return rc;
+    const sige::CopyCfg cc = copy_plan(g, es, false);
+    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, cached, prev_idx, prev_count, g,
+                                    cfg, cc, (hipStream_t)stream),
+                  "sige_sparse_conv_layer_restore", (hipStream_t)stream);
 }
 
 int sige_restore_blocks(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,

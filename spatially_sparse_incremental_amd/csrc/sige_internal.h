@@ -56,10 +56,12 @@ hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int 
                          int32_t *count, hipStream_t st);
 hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t *idx, const int32_t *count,
                          void *blocks, hipStream_t st);
-// fused = 0: src = stacked blocks, dst = output blocks.  fused = 1: src = a_edit, dst = out.
+// fused = 0: src = stacked blocks, dst = output blocks.  fused = 1: src = a_edit, dst = out;
+// with prev_idx (fused only), the previous list's blocks not in idx are restored from cache.
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
-                       const int32_t *count, void *dst, const void *cache, const Geo &g, const ConvCfg &cfg,
-                       const CopyCfg &cc, hipStream_t st);
+                       const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
+                       const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
+                       hipStream_t st);
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
                           const int32_t *count, const Geo &g, const CopyCfg &cc, const void *cached, void *out,
                           int grid, hipStream_t st);

@@ -139,6 +139,14 @@ def test_restore_validation(lib):
     assert f(_v(A), _v(B), _v(C), _v(D), ctypes.byref(g), 1, _v(E + 8), _v(E + (1 << 35)), s) == EALIGN
     assert f(_v(A), _v(B), _v(C), _v(D), ctypes.byref(_g(co=12)), 1, _v(E), _v(E + (1 << 35)), s) == EALIGN
     assert f(_v(A), _v(B), None, None, ctypes.byref(_g(k=9)), 1, _v(E), _v(E + (1 << 35)), s) == EINVAL
+    h = lib.sige_sparse_conv_layer_restore
+    far = _v(E + (1 << 35))
+    assert h(_v(A), _v(B), None, _v(C), _v(D), _v(D + 64), None, _v(E), 1, ctypes.byref(g), far, s) == EINVAL
+    assert h(_v(A), _v(B), None, _v(C), _v(D), _v(D + 64), _v(E), _v(E + 64), 1, ctypes.byref(g), _v(A + 64),
+             s) == EINVAL  # out overlaps a_edit
+    assert h(_v(A), _v(B), None, _v(C), _v(D), _v(D + 64), _v(E), _v(E + 64), 1, ctypes.byref(g), _v(C), s) == EINVAL
+    assert h(_v(A), _v(B + 4), None, _v(C), _v(D), _v(D + 64), _v(E), _v(E + 64), 1, ctypes.byref(g), far,
+             s) == EALIGN
 
 
 def test_strerror_names_every_code(lib):
@@ -162,3 +170,5 @@ def test_valid_call_without_gpu_is_enodev(lib):
                                       _v(E + (1 << 35)), 1, _v(0)) == ENODEV
     assert lib.sige_restore_blocks(_v(A), _v(B), None, None, ctypes.byref(g), 1, _v(E), _v(E + (1 << 35)),
                                    _v(0)) == ENODEV
+    assert lib.sige_sparse_conv_layer_restore(_v(A), _v(B), None, _v(C), _v(D), _v(D + 64), _v(E), _v(E + 64), 1,
+                                              ctypes.byref(g), _v(E + (1 << 35)), _v(0)) == ENODEV

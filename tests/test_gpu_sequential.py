@@ -54,8 +54,8 @@ def test_restore_matches_oracle_bitwise(with_new):
         assert torch.equal(bits(out.cpu()), bits(ref)), f"trial {trial}"
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "three_step"])
-def test_sequence_of_edits_through_a_persistent_buffer(fused):
+@pytest.mark.parametrize("mode", ["one_call", "restore_then_fused", "three_step"])
+def test_sequence_of_edits_through_a_persistent_buffer(mode):
     # four edits (overlapping, disjoint, empty, then a new one): after each, the
     # persistent buffer equals the copy_cached = 1 result bit for bit and the
     # oracle's layer computed from scratch
@@ -70,8 +70,8 @@ def test_sequence_of_edits_through_a_persistent_buffer(fused):
     wk, bs, cg, ao = ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache.cuda(), a_o.cuda()
     rects = [(4, 12, 3, 15), (8, 20, 10, 25), None, (25, 37, 30, 45)]
     persist = cg.clone()
-    idx_buf = [torch.empty(d.cap, dtype=torch.int32, device="cuda") for _ in range(2)]
-    cnt_buf = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    idx_buf = [torch.zeros(d.cap, dtype=torch.int32, device="cuda") for _ in range(2)]
+    cnt_buf = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]  # no previous edit at first
     for e, r in enumerate(rects):
         m = np.zeros((n, h, w), np.uint8)
         if r is not None:
@@ -81,12 +81,15 @@ def test_sequence_of_edits_through_a_persistent_buffer(fused):
         cur, prv = e % 2, (e + 1) % 2
         mask = ssi.sige_diff_mask(ao, ae, 1e-6)
         ssi.sige_reduce_mask(mask, g, dil, idx=idx_buf[cur], count=cnt_buf[cur])
-        if e > 0:
+        if mode == "one_call":
+            ssi.sige_sparse_conv_layer_restore(ae, wk, bs, cg, idx_buf[prv], cnt_buf[prv], idx_buf[cur],
+                                               cnt_buf[cur], g, persist)
+        elif mode == "restore_then_fused":
             ssi.sige_restore_blocks(idx_buf[prv], cnt_buf[prv], idx_buf[cur], cnt_buf[cur], g, cg, persist)
-        if fused:
             ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx_buf[cur], cnt_buf[cur], g, out=persist,
                                        copy_cached=False)
         else:
+            ssi.sige_restore_blocks(idx_buf[prv], cnt_buf[prv], idx_buf[cur], cnt_buf[cur], g, cg, persist)
             blocks = ssi.sige_gather(ae, g, idx_buf[cur], cnt_buf[cur])
             ob = ssi.sige_conv_blocks(blocks, wk, bs, g, cnt_buf[cur])
             ssi.sige_scatter(ob, idx_buf[cur], cnt_buf[cur], g, None, out=persist, copy_cached=False)
@@ -101,7 +104,8 @@ def test_sequence_of_edits_through_a_persistent_buffer(fused):
         assert_close(persist.cpu(), ref, dt, None, f"edit {e}")
 
 
-def test_unet_layer_alternating_edits_full_size():
+@pytest.mark.parametrize("one_call", [True, False], ids=["one_call", "two_calls"])
+def test_unet_layer_alternating_edits_full_size(one_call):
     # the 256x256x128 bf16 layer: two blob edits alternate through one persistent
     # buffer; each step must equal the copy_cached = 1 result bit for bit
     wl = synth.workload("cfg2_unet_bf16")
@@ -116,16 +120,20 @@ def test_unet_layer_alternating_edits_full_size():
     ao = a_o.cuda()
     cg = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, 5).cuda()
     persist = cg.clone()
-    idx_buf = [torch.empty(d.cap, dtype=torch.int32, device="cuda") for _ in range(2)]
-    cnt_buf = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    idx_buf = [torch.zeros(d.cap, dtype=torch.int32, device="cuda") for _ in range(2)]
+    cnt_buf = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]  # no previous edit at first
     for step in range(5):
         cur, prv = step % 2, (step + 1) % 2
         ae = edits[cur]
         mask = ssi.sige_diff_mask(ao, ae, wl.tau)
         ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx_buf[cur], count=cnt_buf[cur])
-        if step > 0:
+        if one_call:
+            ssi.sige_sparse_conv_layer_restore(ae, wk, bs, cg, idx_buf[prv], cnt_buf[prv], idx_buf[cur],
+                                               cnt_buf[cur], g, persist)
+        else:
             ssi.sige_restore_blocks(idx_buf[prv], cnt_buf[prv], idx_buf[cur], cnt_buf[cur], g, cg, persist)
-        ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx_buf[cur], cnt_buf[cur], g, out=persist, copy_cached=False)
+            ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx_buf[cur], cnt_buf[cur], g, out=persist,
+                                       copy_cached=False)
         literal = ssi.sige_sparse_conv_layer(ae, wk, bs, cg, idx_buf[cur], cnt_buf[cur], g)
         torch.cuda.synchronize()
         print(f"\n[case] step {step}: {int(cnt_buf[cur].item())} blocks", flush=True)
