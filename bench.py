@@ -62,6 +62,7 @@ def main():
 
     import spatially_sparse_incremental_amd as ssi
     import synth
+    from spatially_sparse_incremental_amd import comparators as cmp
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -190,7 +191,8 @@ def main():
     print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
 
     t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_nocopy = t_dense_ours = t_dense_miopen = None
-    t_seq = t_seq2 = t_restore = None
+    t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = None
+    bbox_flops = bbox_blocks = rect = None
     if not args.no_comparators:
         # the step without the cache copy (persistent output buffer)
         out_persist = cache.clone()
@@ -274,6 +276,36 @@ def main():
         t_restore = graph_time(lambda: ssi.sige_restore_blocks(seq_idx[1], seq_cnt[1], seq_idx[0], seq_cnt[0], g,
                                                                cache, seq_out))
 
+        # the bounding-box crop that the pages set aside: a dense conv (torch,
+        # i.e. MIOpen) of the output rectangle the edit's bounding box reaches,
+        # written into a copy of the cache; and the same rectangle as a block
+        # list through this library.  The box is found once, outside the timing.
+        rect = cmp.bbox_out_rect(cmp.edit_bbox(mask), L.h, L.w, L.k, L.stride, L.pad)
+        bbox_rows, bbox_cols = rect[1] - rect[0] + 1, rect[3] - rect[2] + 1
+        bbox_flops = 2 * bbox_rows * bbox_cols * L.c_out * L.c_in * L.k * L.k
+        bbox_out = torch.empty_like(cache)
+        w_cl2 = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
+
+        def step_bbox():
+            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            bbox_out.copy_(cache)
+            cmp.bbox_crop_conv(a_e, w_cl2, bias, cache, rect, L.k, L.stride, L.pad, out=bbox_out)
+
+        try:
+            with torch.no_grad():
+                t_bbox = timed_eager(step_bbox, max(20, K // 5))
+        except Exception as exc:  # noqa: BLE001 - report, do not hide
+            print(f"[bench] bounding-box comparator failed: {exc}", file=sys.stderr)
+        bbox_idx, bbox_cnt = cmp.bbox_block_list(rect, L.block, d.nby, d.nbx, device=dev)
+        bbox_blocks = int(bbox_cnt.item())
+
+        def step_bbox_tiles():
+            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, bbox_idx, bbox_cnt, g, out=bbox_out,
+                                       copy_cached=True)
+
+        t_bbox_tiles = graph_time(step_bbox_tiles, 5, 40)
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -350,6 +382,11 @@ def main():
             "step_sequential_edits_us": round(t_seq, 3),
             "step_sequential_edits_two_calls_us": round(t_seq2, 3),
             "restore_blocks_us": round(t_restore, 3),
+            "bbox_crop_dense_step_us": None if t_bbox is None else round(t_bbox, 3),
+            "bbox_tiles_step_us": round(t_bbox_tiles, 3),
+            "bbox_output_rect": list(rect),
+            "bbox_blocks": bbox_blocks,
+            "bbox_mac_reduction": round(dense_flops / bbox_flops, 2),
             "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
         },
         "latency": {
