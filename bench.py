@@ -45,6 +45,8 @@ def parse():
                     help="time the step and its kernels only (for profiler runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: the block size and dilation sweep (a line per point, then a table)")
     return ap.parse_args()
 
 
@@ -55,6 +57,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the multi-GPU split of the block list is a design note, not built.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        run_sweep(args)
+        return
 
     import numpy as np
     import torch
@@ -111,36 +117,7 @@ def main():
     active = int(count.item())
     edit_frac = float(mask_np.mean())
 
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    def capture(fn, n_in):
-        """A HIP graph of n_in back-to-back calls of fn (launches only; no memsets inside)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for _ in range(n_in):
-                fn()
-        gr.replay()
-        torch.cuda.synchronize()
-        return gr
-
-    def graph_time(fn, n_in=20, replays=25):
-        """Mean duration of one fn call: events around `replays` replays of a graph of n_in calls."""
-        gr = capture(fn, n_in)
-        cur = torch.cuda.current_stream()
-        e0, e1 = ev(), ev()
-        e0.record(cur)
-        for _ in range(replays):
-            gr.replay()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (n_in * replays) * 1e3  # us
+    ev, capture, graph_time = _timers(torch)
 
     # ---- timed region: K steps back to back, as replays of a graph of S steps
     S = 10
@@ -397,6 +374,110 @@ def main():
         "mac_reduction": round(dense_flops / conv_flops, 2) if conv_flops else None,
     }
     print(json.dumps(res), flush=True)
+
+
+def _timers(torch):
+    """HIP-event timing helpers: ev(), capture(fn, n_in) -> graph, graph_time(fn, n_in, replays) -> us."""
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def capture(fn, n_in):
+        """A HIP graph of n_in back-to-back calls of fn (launches only; no memsets inside)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(n_in):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        return gr
+
+    def graph_time(fn, n_in=20, replays=25):
+        """Mean duration of one fn call: events around `replays` replays of a graph of n_in calls."""
+        gr = capture(fn, n_in)
+        cur = torch.cuda.current_stream()
+        e0, e1 = ev(), ev()
+        e0.record(cur)
+        for _ in range(replays):
+            gr.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n_in * replays) * 1e3  # us
+
+    return ev, capture, graph_time
+
+
+def run_sweep(args):
+    """Block size and dilation sweep (one JSON line per point, then a markdown
+    table): blocks listed, MAC reduction, reduce and fused-layer times with and
+    without the cache copy, and the dense conv (torch/MIOpen) of the layer."""
+    import torch
+    import torch.nn.functional as F
+
+    import spatially_sparse_incremental_amd as ssi
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ev, capture, graph_time = _timers(torch)
+    rows, dense_t = [], {}
+    for wname, L in synth.SWEEP:
+        wl = synth.workload(wname)
+        seed = args.seed
+        m = synth.edit_shape(wl, seed).raster(L.h, L.w)
+        a_o_cpu = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
+        a_o = a_o_cpu.to(dev)
+        a_e = synth.make_edit(a_o_cpu, m, wl.edit_kind, seed).to(dev)
+        w_cpu, b_cpu = synth.make_layer_tensors(L, seed)
+        wk, bias = ssi.weight_to_krsc(w_cpu).to(dev), b_cpu.to(dev)
+        g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+        d = ssi.sige_geom_derive(g)
+        cache = synth.make_activation(1, d.ho, d.wo, L.c_out, L.dtype, seed + 50).to(dev)
+        out, persist = torch.empty_like(cache), cache.clone()
+        mask = ssi.sige_diff_mask(a_o, a_e, wl.tau)
+        idx, cnt = ssi.sige_reduce_mask(mask, g, L.dilate)
+        torch.cuda.synchronize()
+        blocks = int(cnt.item())
+        t_red = graph_time(lambda: ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=cnt))
+        t_copy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out))
+        t_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, None, idx, cnt, g, out=persist,
+                                                                 copy_cached=False))
+        key = (wname, L.h, L.c_in)
+        if key not in dense_t:
+            x_cl = a_e.permute(0, 3, 1, 2)
+            w_cl = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
+            with torch.no_grad():
+                for _ in range(10):
+                    F.conv2d(x_cl, w_cl, bias.to(a_e.dtype), padding=L.pad)
+                torch.cuda.synchronize()
+                e0, e1 = ev(), ev()
+                e0.record()
+                for _ in range(50):
+                    F.conv2d(x_cl, w_cl, bias.to(a_e.dtype), padding=L.pad)
+                e1.record()
+                torch.cuda.synchronize()
+            dense_t[key] = e0.elapsed_time(e1) / 50 * 1e3
+        act_pix = _active_pixels(idx[:blocks].cpu().numpy(), d, L.block)
+        row = {"layer": L.name, "h": L.h, "w": L.w, "c_in": L.c_in, "c_out": L.c_out, "dtype": L.dtype,
+               "block": L.block, "dilate": L.dilate, "blocks": blocks, "capacity": d.cap,
+               "edit_fraction": round(float(m.mean()), 5),
+               "mac_reduction": round(d.ho * d.wo / act_pix, 2) if act_pix else None,
+               "reduce_us": round(t_red, 3), "fused_copy_us": round(t_copy, 3),
+               "fused_nocopy_us": round(t_nocopy, 3), "dense_miopen_us": round(dense_t[key], 3),
+               "speedup_nocopy_vs_dense": round(dense_t[key] / t_nocopy, 2)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    cols = ["layer", "block", "dilate", "blocks", "capacity", "mac_reduction", "reduce_us", "fused_copy_us",
+            "fused_nocopy_us", "dense_miopen_us", "speedup_nocopy_vs_dense"]
+    print("| " + " | ".join(cols) + " |")
+    print("|" + "---|" * len(cols))
+    for r in rows:
+        print("| " + " | ".join(str(r[c]) for c in cols) + " |")
 
 
 def _measured_traffic():

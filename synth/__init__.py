@@ -8,6 +8,7 @@ from .gen import (  # noqa: F401
     DTYPES,
     Blob,
     LayerSpec,
+    SWEEP,
     StarPolygon,
     Workload,
     WORKLOADS,

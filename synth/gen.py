@@ -22,6 +22,7 @@ convolution.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass, field
 
@@ -296,6 +297,27 @@ WORKLOADS = {
 
 def workload(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def _sweep_points():
+    """Block size and dilation sweep: (workload name, layer with the swept
+    block size and dilation).  The U-Net layer at 256x256, and the latent-
+    diffusion 3x3 layers at the low resolutions (32x32, 16x16) where only
+    1-2 pixel blocks keep the update sparse."""
+    pts = []
+    base = WORKLOADS["cfg2_unet_bf16"].layers[0]
+    for b in (2, 4, 6, 8, 12, 16):
+        for d in (0, 1, 2):
+            pts.append(("cfg2_unet_bf16", dataclasses.replace(base, name=f"unet_b{b}_d{d}", block=b, dilate=d)))
+    for lname, blocks in (("l32_3x3", (1, 2, 4, 8)), ("l16_3x3", (1, 2, 4))):
+        lay = next(x for x in WORKLOADS["cfg5_ldm_f16"].layers if x.name == lname)
+        for b in blocks:
+            for d in (0, 1):
+                pts.append(("cfg5_ldm_f16", dataclasses.replace(lay, name=f"{lname}_b{b}_d{d}", block=b, dilate=d)))
+    return tuple(pts)
+
+
+SWEEP = _sweep_points()
 
 
 def edit_shape(wl: Workload, seed: int, area: float | None = None):

@@ -101,3 +101,40 @@ def run_layer_oracle(a_o, a_e, wt, bias, cache, k, s, p, b, dilate, tau=1e-6):
     idx = oracle.index_list(act)
     out64 = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, act, cache, out_f64=True)
     return dict(mask=mask, act=act, idx=idx, out64=out64)
+
+
+def check_layer_sampled(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed, sample=6):
+    """Full-size check of one layer: the block list bit for bit, every pixel outside
+    the listed blocks equal to the cache bit for bit, and `sample` listed blocks
+    recomputed by the oracle (fp64) within tolerance.  a_e, cache, out: CPU NHWC;
+    idx: the GPU's list; mask_full: [n, hm, wm] diff mask.  Returns the relative error."""
+    n, h, w, _ = a_e.shape
+    act = oracle.block_activity(mask_full, h, w, L.k, L.stride, L.pad, L.block, L.dilate)
+    ref_idx = oracle.index_list(act)
+    assert torch.equal(idx, ref_idx), f"{name}: block list differs"
+    ho, wo, nby, nbx, _ = oracle.geometry(h, w, L.k, L.stride, L.pad, L.block)
+    pm = act.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :ho, :wo, None]
+    keep = ~pm.expand_as(cache)
+    assert torch.equal(out[keep].view(torch.uint8), cache[keep].view(torch.uint8)), f"{name}: untouched pixels"
+    if ref_idx.numel() == 0:
+        return 0.0
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(ref_idx.numpy(), size=min(sample, ref_idx.numel()), replace=False)
+    sub = torch.zeros_like(act)
+    sub.view(-1)[torch.from_numpy(pick).long()] = 1
+    ref = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, sub, out, out_f64=True)
+    sel = sub.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :ho, :wo, None].expand_as(out)
+    g64, r64 = out.double()[sel], ref[sel]
+    scale = r64.abs().max().item()
+    err = (g64 - r64).abs().max().item()
+    assert err <= TOL[out.dtype] * scale, f"{name}: max err {err:.3e} vs scale {scale:.3e}"
+    return err / scale
+
+
+def run_layer_full(a_e_gpu, wt, bias, cache_gpu, L, mask_gpu):
+    """reduce + fused layer (copy_cached = 1) on the GPU for layer spec L; returns (out, CPU list)."""
+    g = ssi.geom(a_e_gpu.shape[0], L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    idx, count = ssi.sige_reduce_mask(mask_gpu, g, L.dilate)
+    out = ssi.sige_sparse_conv_layer(a_e_gpu, ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache_gpu, idx, count, g)
+    torch.cuda.synchronize()
+    return out, idx[:int(count.item())].cpu()

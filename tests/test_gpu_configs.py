@@ -15,50 +15,14 @@ import torch
 import oracle
 import spatially_sparse_incremental_amd as ssi
 import synth
-from _parity import TOL, bits
+from _parity import TOL, bits, check_layer_sampled, run_layer_full
 
 pytestmark = pytest.mark.gpu
-
-SAMPLE = 6  # listed blocks recomputed by the oracle per layer
-
 
 @pytest.fixture(autouse=True)
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def _check_layer(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed):
-    """a_e, cache, out: CPU NHWC; idx: the GPU's list; mask_full: [n, hm, wm] diff mask."""
-    n, h, w, _ = a_e.shape
-    act = oracle.block_activity(mask_full, h, w, L.k, L.stride, L.pad, L.block, L.dilate)
-    ref_idx = oracle.index_list(act)
-    assert torch.equal(idx, ref_idx), f"{name}: block list differs"
-    ho, wo, nby, nbx, _ = oracle.geometry(h, w, L.k, L.stride, L.pad, L.block)
-    pm = act.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :ho, :wo, None]
-    keep = ~pm.expand_as(cache)
-    assert torch.equal(out[keep].view(torch.uint8), cache[keep].view(torch.uint8)), f"{name}: untouched pixels"
-    if ref_idx.numel() == 0:
-        return 0.0
-    rng = np.random.default_rng(seed)
-    pick = rng.choice(ref_idx.numpy(), size=min(SAMPLE, ref_idx.numel()), replace=False)
-    sub = torch.zeros_like(act)
-    sub.view(-1)[torch.from_numpy(pick).long()] = 1
-    ref = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, sub, out, out_f64=True)
-    sel = sub.bool().repeat_interleave(L.block, 1).repeat_interleave(L.block, 2)[:, :ho, :wo, None].expand_as(out)
-    g64, r64 = out.double()[sel], ref[sel]
-    scale = r64.abs().max().item()
-    err = (g64 - r64).abs().max().item()
-    assert err <= TOL[out.dtype] * scale, f"{name}: max err {err:.3e} vs scale {scale:.3e}"
-    return err / scale
-
-
-def _run_layer(a_e_gpu, wt, bias, cache_gpu, L, mask_gpu):
-    g = ssi.geom(a_e_gpu.shape[0], L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
-    idx, count = ssi.sige_reduce_mask(mask_gpu, g, L.dilate)
-    out = ssi.sige_sparse_conv_layer(a_e_gpu, ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache_gpu, idx, count, g)
-    torch.cuda.synchronize()
-    return out, idx[:int(count.item())].cpu()
 
 
 def test_cfg1_rectangle_fp32_nchw():
@@ -73,7 +37,7 @@ def test_cfg1_rectangle_fp32_nchw():
         # the GPU path is NHWC: permute (untimed); the oracle reads NCHW directly
         nhwc = lambda t: t.permute(0, 2, 3, 1).contiguous()  # noqa: E731
         mask = ssi.sige_diff_mask(nhwc(a_o).cuda(), nhwc(a_e).cuda(), wl.tau)
-        out, idx = _run_layer(nhwc(a_e).cuda(), wt, bias, nhwc(cache).cuda(), L, mask)
+        out, idx = run_layer_full(nhwc(a_e).cuda(), wt, bias, nhwc(cache).cuda(), L, mask)
         assert torch.equal(mask.cpu()[0], torch.from_numpy(m))
         act = oracle.block_activity(oracle.diff_mask(a_o, a_e, wl.tau, "NCHW"), L.h, L.w, L.k, L.stride, L.pad,
                                     L.block, L.dilate)
@@ -98,7 +62,7 @@ def test_cfg2_unet_layer_full(seed):
     cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + 100)  # the cache is an input
     mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
     assert torch.equal(mask.cpu()[0], torch.from_numpy(m))
-    out, idx = _run_layer(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+    out, idx = run_layer_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
     # every listed block, not a sample: the oracle finishes this layer in about a second
     act = oracle.block_activity(mask.cpu(), L.h, L.w, L.k, L.stride, L.pad, L.block, L.dilate)
     assert torch.equal(idx, oracle.index_list(act))
@@ -125,8 +89,8 @@ def test_cfg3_chain_layerwise():
         wt, bias = synth.make_layer_tensors(L, seed * 100 + li)
         ho, wo, _, _, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
         cache = synth.make_activation(1, ho, wo, L.c_out, L.dtype, seed * 100 + li + 50)
-        out, idx = _run_layer(x, wt, bias, cache.cuda(), L, mask)
-        _check_layer(f"chain {L.name}", x.cpu(), wt, bias, cache, out.cpu(), idx, L, mask.cpu(), seed + li)
+        out, idx = run_layer_full(x, wt, bias, cache.cuda(), L, mask)
+        check_layer_sampled(f"chain {L.name}", x.cpu(), wt, bias, cache, out.cpu(), idx, L, mask.cpu(), seed + li)
         x = out  # layer l+1 takes layer l's edited output
 
 
@@ -142,8 +106,8 @@ def test_cfg4_gaugan_layers(area):
         wt, bias = synth.make_layer_tensors(L, seed + li)
         cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
         mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
-        out, idx = _run_layer(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
-        _check_layer(f"gaugan {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
+        out, idx = run_layer_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+        check_layer_sampled(f"gaugan {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
 
 
 @pytest.mark.parametrize("area", [0.012, 0.10])
@@ -158,8 +122,8 @@ def test_cfg5_latent_diffusion_layers(area):
         wt, bias = synth.make_layer_tensors(L, seed + li)
         cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
         mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
-        out, idx = _run_layer(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
-        _check_layer(f"ldm {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
+        out, idx = run_layer_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+        check_layer_sampled(f"ldm {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
 
 
 def test_cfg2_three_call_path_matches_fused_at_full_size():
