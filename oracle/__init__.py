@@ -68,6 +68,8 @@ def lib():
         L.oracle_num_threads.restype = c_int
         L.oracle_restore_blocks.argtypes = [c_void, c_long, c_void, c_long, c_int, c_int, c_int, c_int, c_int,
                                             c_int, c_void, c_void]
+        L.oracle_sparse_attention.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int,
+                                              ctypes.c_double, c_int, c_void, c_void, c_void, c_int]
         L.oracle_set_threads.argtypes = [c_int]
         _lib = L
     return _lib
@@ -245,6 +247,30 @@ def restore_blocks(prev_idx, idx, cache, out, b) -> torch.Tensor:
     rc = lib().oracle_restore_blocks(_ptr(prev_idx), prev_idx.numel(), _ptr(new) if new.numel() else None,
                                      new.numel(), n, ho, wo, cout, b, DT[cache.dtype], _ptr(cache), _ptr(out))
     _check(rc, "restore_blocks")
+    return out
+
+
+def sparse_attention(q, k, v, heads, b, active, cache, scale=None, out_f64=False) -> torch.Tensor:
+    """Query-pruned self-attention over a token grid.
+
+    q, k, v, cache: [n, h, w, heads*d] (tokens row-major), storage dtype.
+    active: uint8 [n, ceil(h/b), ceil(w/b)] blocks of query tokens, or None (all).
+    scale defaults to 1/sqrt(d).  Tokens outside active blocks keep the cache.
+    """
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    n, h, w, C = q.shape
+    assert k.shape == q.shape == v.shape and k.dtype == q.dtype == v.dtype and C % heads == 0
+    d = C // heads
+    scale = d ** -0.5 if scale is None else scale
+    out = torch.empty(q.shape, dtype=torch.float64 if out_f64 else q.dtype)
+    if active is not None:
+        active = active.to(torch.uint8).contiguous()
+        assert active.shape == (n, -(-h // b), -(-w // b))
+        cache = cache.contiguous()
+        assert cache.shape == q.shape and cache.dtype == q.dtype
+    rc = lib().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), DT[q.dtype], n, h, w, heads, d, float(scale), b,
+                                       _ptr(active), _ptr(cache), _ptr(out), DT[out.dtype])
+    _check(rc, "sparse_attention")
     return out
 
 

@@ -466,3 +466,70 @@ int oracle_restore_blocks(const int32_t *prev_idx, long prev_count, const int32_
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* query-pruned self-attention ([REVIEW] Proposed method: attention layers are */
+/* handled by pruning the queries of unedited tokens, so that the attention    */
+/* work scales with the edited area)                                            */
+/* ------------------------------------------------------------------------ */
+/* Tokens are the pixels of an h x w grid in row-major order; q, k, v, cache
+ * and out are [n, h*w, heads*d] (head hd owns channels [hd*d, hd*d + d)).  For
+ * every token of an active block (b x b tokens, clipped at the grid edge;
+ * active NULL: every token) and every head:
+ *   out[t] = sum over the tokens j of the same image of
+ *            softmax_j(scale * q[t] . k[j]) * v[j],
+ * the scores, the softmax (its maximum subtracted) and the weighted sum in
+ * fp64 from the exactly widened stored values, then one rounding to out_dt
+ * (the storage dtype, or OR_F64).  Every other token: the cached value. */
+int oracle_sparse_attention(const void *q, const void *kt, const void *v, int dt, int n, int h, int w, int heads,
+                            int d, double scale, int b, const uint8_t *active, const void *cache, void *out,
+                            int out_dt) {
+    if (!elem_size(dt) || n < 1 || h < 1 || w < 1 || heads < 1 || d < 1 || b < 1) return -1;
+    if (out_dt != dt && out_dt != OR_F64) return -1;
+    if (active && !cache) return -1;
+    const long L = (long)h * w, C = (long)heads * d;
+    const int nby = (h + b - 1) / b, nbx = (w + b - 1) / b;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * L);
+        double *acc = (double *)malloc(sizeof(double) * d);
+        if (!sc || !acc) {
+#pragma omp critical
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 4) collapse(2)
+        for (int nn = 0; nn < n; nn++)
+            for (long t = 0; t < L; t++) {
+                if (!sc || !acc) continue;
+                const int y = (int)(t / w), x = (int)(t % w);
+                const long base = ((long)nn * L + t) * C;
+                if (active && !active[((long)nn * nby + y / b) * nbx + x / b]) {
+                    for (long c = 0; c < C; c++) store_elem(out, base + c, out_dt, load_elem(cache, base + c, dt));
+                    continue;
+                }
+                for (int hd = 0; hd < heads; hd++) {
+                    double mx = -INFINITY;
+                    for (long j = 0; j < L; j++) {
+                        const long kb = ((long)nn * L + j) * C + (long)hd * d;
+                        double s = 0.0;
+                        for (int c = 0; c < d; c++) s += load_elem(q, base + (long)hd * d + c, dt) * load_elem(kt, kb + c, dt);
+                        sc[j] = scale * s;
+                        if (sc[j] > mx) mx = sc[j];
+                    }
+                    double sum = 0.0;
+                    for (int c = 0; c < d; c++) acc[c] = 0.0;
+                    for (long j = 0; j < L; j++) {
+                        const double e = exp(sc[j] - mx);
+                        const long vb = ((long)nn * L + j) * C + (long)hd * d;
+                        sum += e;
+                        for (int c = 0; c < d; c++) acc[c] += e * load_elem(v, vb + c, dt);
+                    }
+                    for (int c = 0; c < d; c++) store_elem(out, base + (long)hd * d + c, out_dt, acc[c] / sum);
+                }
+            }
+        free(sc);
+        free(acc);
+    }
+    return err;
+}

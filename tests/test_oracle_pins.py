@@ -487,6 +487,83 @@ def test_restore_special_cases():
 
 
 # ---------------------------------------------------------------------------
+# query-pruned self-attention
+# ---------------------------------------------------------------------------
+def _attn_torch_f64(q, k, v, heads, scale):
+    """Library reference: torch softmax and matmul in fp64, per image and head."""
+    n, h, w, C = q.shape
+    d = C // heads
+    qd, kd, vd = (oracle.decode(t).reshape(n, h * w, heads, d).permute(0, 2, 1, 3) for t in (q, k, v))
+    p = torch.softmax(scale * qd @ kd.transpose(-1, -2), dim=-1)
+    return (p @ vd).permute(0, 2, 1, 3).reshape(n, h, w, C)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_attention_dense_matches_torch_fp64(dt):
+    n, h, w, heads, d = 2, 6, 7, 2, 8
+    q, k, v = (_rand((n, h, w, heads * d), dt, 501 + i) for i in range(3))
+    ref = _attn_torch_f64(q, k, v, heads, d ** -0.5)
+    got = oracle.sparse_attention(q, k, v, heads, 2, None, None, out_f64=True)
+    assert (got - ref).abs().max() <= 1e-12 * ref.abs().max()
+    rounded = oracle.sparse_attention(q, k, v, heads, 2, None, None)
+    assert torch.equal(rounded.view(torch.uint8), oracle.round_to(got, dt).view(torch.uint8))
+
+
+def test_attention_uniform_keys_average_the_values():
+    n, h, w, heads, d = 1, 5, 6, 3, 4
+    dt = torch.float32
+    q = _rand((n, h, w, heads * d), dt, 511)
+    k = _rand((1, 1, 1, heads * d), dt, 512).expand(n, h, w, heads * d).contiguous()  # every key the same
+    v = _rand((n, h, w, heads * d), dt, 513)
+    got = oracle.sparse_attention(q, k, v, heads, 2, None, None, out_f64=True)
+    mean = v.double().reshape(n, h * w, heads * d).mean(dim=1)
+    assert (got.reshape(n, h * w, -1) - mean[:, None, :]).abs().max() <= 1e-12
+
+
+def test_attention_dominant_key_selects_its_value():
+    n, h, w, heads, d = 1, 4, 4, 1, 16
+    dt = torch.float32
+    eye = torch.eye(16)
+    k = (eye * 40.0).reshape(1, 4, 4, 16)  # key j = 40 e_j: q = e_j scores 40 against 0 for every other key
+    q = eye.reshape(1, 4, 4, 16)
+    v = _rand((n, h, w, 16), dt, 521)
+    got = oracle.sparse_attention(q, k, v, heads, 4, None, None, out_f64=True, scale=1.0)
+    e = math.exp(-40.0)
+    vv = v.double().reshape(16, 16)
+    expect = (vv + e * (vv.sum(0, keepdim=True) - vv)) / (1 + 15 * e)  # closed form of the softmax mixture
+    assert (got.reshape(16, 16) - expect).abs().max() <= 1e-12
+
+
+def test_attention_is_invariant_to_a_joint_key_value_permutation_and_images_are_independent():
+    n, h, w, heads, d = 2, 5, 5, 2, 8
+    dt = torch.float64
+    q, k, v = (_rand((n, h, w, heads * d), dt, 531 + i) for i in range(3))
+    base = oracle.sparse_attention(q, k, v, heads, 2, None, None)
+    perm = torch.randperm(h * w, generator=torch.Generator().manual_seed(5))
+    kp = k.reshape(n, h * w, -1)[:, perm].reshape(k.shape)
+    vp = v.reshape(n, h * w, -1)[:, perm].reshape(v.shape)
+    assert (oracle.sparse_attention(q, kp, vp, heads, 2, None, None) - base).abs().max() <= 1e-12
+    one = oracle.sparse_attention(q[1:].clone(), k[1:].clone(), v[1:].clone(), heads, 2, None, None)
+    assert torch.equal(one, base[1:])
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_attention_pruned_queries_keep_the_cache(dt):
+    n, h, w, heads, d, b = 1, 9, 10, 2, 8, 4
+    q, k, v = (_rand((n, h, w, heads * d), dt, 541 + i) for i in range(3))
+    cache = _rand((n, h, w, heads * d), dt, 545)
+    act = torch.zeros((n, 3, 3), dtype=torch.uint8)
+    act[0, 0, 1] = act[0, 2, 2] = 1  # the second includes the clipped corner block
+    got = oracle.sparse_attention(q, k, v, heads, b, act, cache)
+    dense = oracle.sparse_attention(q, k, v, heads, b, None, None)
+    sel = _pixel_block_mask(act, b, h, w)[..., None].expand_as(got)
+    assert torch.equal(got[sel].view(torch.uint8), dense[sel].view(torch.uint8))
+    assert torch.equal(got[~sel].view(torch.uint8), cache[~sel].view(torch.uint8))
+    empty = oracle.sparse_attention(q, k, v, heads, b, torch.zeros_like(act), cache)
+    assert torch.equal(empty.view(torch.uint8), cache.view(torch.uint8))
+
+
+# ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
 def _small_chain(dt=torch.bfloat16):
