@@ -168,7 +168,7 @@ def main():
     print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
 
     t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_nocopy = t_dense_ours = t_dense_miopen = None
-    t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = None
+    t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = attention = None
     bbox_flops = bbox_blocks = rect = None
     if not args.no_comparators:
         # the step without the cache copy (persistent output buffer)
@@ -283,6 +283,8 @@ def main():
 
         t_bbox_tiles = graph_time(step_bbox_tiles, 5, 40)
 
+        attention = _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed)
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -364,6 +366,7 @@ def main():
             "bbox_output_rect": list(rect),
             "bbox_blocks": bbox_blocks,
             "bbox_mac_reduction": round(dense_flops / bbox_flops, 2),
+            "attention_ldm_64x64x5x64_f16": attention,
             "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
         },
         "latency": {
@@ -478,6 +481,49 @@ def run_sweep(args):
     print("|" + "---|" * len(cols))
     for r in rows:
         print("| " + " | ".join(str(r[c]) for c in cols) + " |")
+
+
+def _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
+    """Query-pruned self-attention at the latent-diffusion shape (64x64 tokens,
+    5 heads of 64, fp16): query blocks of 4x4 tokens from a blob edit's diff
+    (k = 1 geometry, dilation 1) at 1.2% and 10% of the frame, against dense
+    attention over all 4096 queries (torch scaled_dot_product_attention)."""
+    dev = torch.device("cuda:0")
+    wl = synth.workload("cfg5_ldm_f16")
+    h = w = 64
+    heads, d, b = 5, 64, 4
+    g = ssi.geom(1, h, w, heads * d, heads * d, 1, 1, 0, b)
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    q, k, v = ((torch.randn((1, h, w, heads * d), generator=gen) * 0.5).to(torch.float16).to(dev) for _ in range(3))
+    cache = torch.randn((1, h, w, heads * d), generator=gen).to(torch.float16).to(dev)
+    out = torch.empty_like(cache)
+    ws = torch.empty(ssi.sige_sparse_attention_workspace(1, h, w, heads, d, b), dtype=torch.uint8, device=dev)
+    x_o = synth.make_activation(1, h, w, 320, "f16", seed).to(dev)
+    res = {}
+    for area in (0.012, 0.10):
+        m = synth.edit_shape(wl, seed, area).raster(h, w)
+        x_e = synth.make_edit(x_o.cpu(), m, "replace", seed).to(dev)
+        mask = ssi.sige_diff_mask(x_o, x_e, wl.tau)
+        idx, cnt = ssi.sige_reduce_mask(mask, g, 1)
+        torch.cuda.synchronize()
+        blocks = int(cnt.item())
+        t = graph_time(lambda: ssi.sige_sparse_attention(q, k, v, idx, cnt, heads, b, cached=cache, out=out,
+                                                         workspace=ws))
+        t_nocopy = graph_time(lambda: ssi.sige_sparse_attention(q, k, v, idx, cnt, heads, b, out=out,
+                                                                copy_cached=False, workspace=ws))
+        flops = 4.0 * blocks * b * b * heads * d * h * w
+        key = f"area_{area:g}"
+        res[key] = {"query_blocks": blocks, "sparse_us": round(t, 3), "sparse_nocopy_us": round(t_nocopy, 3),
+                    "tflops_nocopy": round(flops / (t_nocopy * 1e-6) / 1e12, 2)}
+    qh, kh, vh = (x.reshape(1, h * w, heads, d).transpose(1, 2).contiguous() for x in (q, k, v))
+    try:
+        with torch.no_grad():
+            t_dense = timed_eager(lambda: F.scaled_dot_product_attention(qh, kh, vh), 50)
+        res["dense_sdpa_us"] = round(t_dense, 3)
+        res["dense_tflops"] = round(4.0 * h * w * heads * d * h * w / (t_dense * 1e-6) / 1e12, 2)
+    except Exception as exc:  # noqa: BLE001 - report, do not hide
+        print(f"[bench] dense attention failed: {exc}", file=sys.stderr)
+    return res
 
 
 def _measured_traffic():

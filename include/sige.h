@@ -183,6 +183,30 @@ int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const
                                    const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
                                    const int32_t *count, int dtype, const sige_geom *g, void *out, void *stream);
 
+/* Query-pruned self-attention (nubint.ai review, "Proposed method": attention
+ * layers are handled by pruning the queries of unedited tokens, so that the
+ * attention work scales with the edited area).
+ *   Tokens are the pixels of an h x w grid in row-major order; q, k, v, cached
+ *   and out are [n, h*w, heads*head_dim] in dtype (SIGE_F16 or SIGE_BF16), head
+ *   hd owning channels [hd*head_dim, (hd+1)*head_dim).  idx[0, *count) lists
+ *   blocks of block x block tokens, ascending (as sige_reduce_mask writes it
+ *   for the k = 1, stride 1, pad 0 geometry of the token grid).  For every token
+ *   t of a listed block (clipped at the grid edge) and every head:
+ *     out[t] = sum_j softmax_j(scale * q[t] . k[j]) v[j], j over the tokens of t's image,
+ *   with fp32 products and softmax on the matrix cores, the probabilities
+ *   rounded to dtype for the second product.
+ *   copy_cached = 1: out = cached for every other token (a copy; out must not
+ *   overlap cached); 0: those tokens of out are left alone.
+ *   workspace: caller-owned device scratch of at least
+ *   sige_sparse_attention_workspace() bytes, 16-byte aligned, needing no
+ *   initialisation; its contents afterwards are meaningless.
+ *   Limits: head_dim 64, n <= 8 (else SIGE_ERANGE).  Two kernel launches. */
+int64_t sige_sparse_attention_workspace(int n, int h, int w, int heads, int head_dim, int block);
+int sige_sparse_attention(const void *q, const void *k, const void *v, const int32_t *idx, const int32_t *count,
+                          int dtype, int n, int h, int w, int heads, int head_dim, int block, float scale,
+                          const void *cached, void *out, int copy_cached, void *workspace, int64_t workspace_bytes,
+                          void *stream);
+
 /* Name of a status code (static string). */
 const char *sige_strerror(int code);
 

@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     sige_reduce_mask,
     sige_restore_blocks,
     sige_scatter,
+    sige_sparse_attention,
+    sige_sparse_attention_workspace,
     sige_sparse_conv_layer,
     sige_sparse_conv_layer_restore,
     weight_to_krsc,

@@ -20,7 +20,7 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
-           "sige_strerror",
+           "sige_sparse_attention_workspace", "sige_sparse_attention", "sige_strerror",
            "sige_last_error")
 
 
@@ -62,11 +62,15 @@ def lib():
         L.sige_sparse_conv_layer.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
         L.sige_restore_blocks.argtypes = [V, V, V, V, P, I, V, V, V]
         L.sige_sparse_conv_layer_restore.argtypes = [V, V, V, V, V, V, V, V, I, P, V, V]
+        L.sige_sparse_attention_workspace.argtypes = [I] * 6
+        L.sige_sparse_attention_workspace.restype = ctypes.c_int64
+        L.sige_sparse_attention.argtypes = [V, V, V, V, V, I, I, I, I, I, I, I, ctypes.c_float, V, V, I, V,
+                                            ctypes.c_int64, V]
         L.sige_strerror.restype = ctypes.c_char_p
         L.sige_strerror.argtypes = [I]
         L.sige_last_error.restype = ctypes.c_char_p
         for f in EXPORTS:
-            if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks"):
+            if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks", "sige_sparse_attention_workspace"):
                 getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -241,4 +245,36 @@ def sige_sparse_conv_layer_restore(a_edit, w_krsc, bias, cached, prev_idx, prev_
                                               _p(prev_count), _p(idx), _p(count), _dt(a_edit), ctypes.byref(g),
                                               _p(out), _stream(stream))
     _check(rc, "sige_sparse_conv_layer_restore")
+    return out
+
+
+def sige_sparse_attention_workspace(n, h, w, heads, head_dim, block) -> int:
+    nbytes = lib().sige_sparse_attention_workspace(n, h, w, heads, head_dim, block)
+    if nbytes < 0:
+        _check(int(nbytes), "sige_sparse_attention_workspace")
+    return int(nbytes)
+
+
+def sige_sparse_attention(q, k, v, idx, count, heads, block, scale=None, cached=None, out=None, copy_cached=True,
+                          workspace=None, stream=None):
+    """Query-pruned self-attention over a token grid: q, k, v, cached, out are
+    [n, h, w, heads*head_dim] (NHWC = tokens row-major).  The workspace is
+    allocated here when not given."""
+    _dev(q, k, v, idx, count, cached, out, workspace)
+    n, h, w, c = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype or c % heads:
+        raise ValueError("q, k and v must match, with heads dividing the channels")
+    d = c // heads
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        if not copy_cached:
+            raise ValueError("copy_cached=False needs a persistent `out`")
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = sige_sparse_attention_workspace(n, h, w, heads, d, block)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    rc = lib().sige_sparse_attention(_p(q), _p(k), _p(v), _p(idx), _p(count), _dt(q), n, h, w, heads, d, block,
+                                     ctypes.c_float(scale), _p(cached if copy_cached else None), _p(out),
+                                     int(bool(copy_cached)), _p(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "sige_sparse_attention")
     return out

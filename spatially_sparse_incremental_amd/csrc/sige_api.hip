@@ -222,6 +222,33 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
     return SIGE_OK;
 }
 
+// Attention: the token grid as a k = 1 geometry, and the workspace the two kernels need.
+int attn_geom(int n, int h, int w, int heads, int head_dim, int block, Geo *g) {
+    if (head_dim != sige::kAttnHeadDim) return fail(SIGE_ERANGE, "head_dim %d: only 64 is supported", head_dim);
+    if (heads < 1) return fail(SIGE_EINVAL, "heads=%d", heads);
+    if (n < 1 || n > sige::kAttnImages) return fail(SIGE_ERANGE, "n=%d: 1 to %d images", n, sige::kAttnImages);
+    const sige_geom q{n, h, w, heads * head_dim, heads * head_dim, 1, 1, 0, block};
+    return derive(&q, g);
+}
+
+int attn_grid1() {
+    static int grid[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return sige::attn_partial_grid(dev_info().cus);
+    }
+    if (!grid[dev]) grid[dev] = sige::attn_partial_grid(dev_info().cus);
+    return grid[dev];
+}
+
+int64_t attn_ws_bytes(const Geo &g, int heads, int grid1) {
+    const long per = (long)g.nby * g.nbx, b2 = (long)g.b * g.b;
+    const long max_items = (long)g.n * ((per * b2 + 63) / 64) * heads;
+    const long items = max_items > 2L * grid1 ? max_items : 2L * grid1;
+    return (int64_t)items * sige::kAttnWsBytesPerItem;
+}
+
 }  // namespace
 
 extern "C" {
@@ -430,6 +457,45 @@ int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const
     return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, cached, prev_idx, prev_count, g,
                                     cfg, cc, (hipStream_t)stream),
                   "sige_sparse_conv_layer_restore", (hipStream_t)stream);
+}
+
+int64_t sige_sparse_attention_workspace(int n, int h, int w, int heads, int head_dim, int block) {
+    Geo g;
+    const int rc = attn_geom(n, h, w, heads, head_dim, block, &g);
+    if (rc) return rc;
+    g_msg[0] = 0;
+    return attn_ws_bytes(g, heads, attn_grid1());
+}
+
+int sige_sparse_attention(const void *q, const void *k, const void *v, const int32_t *idx, const int32_t *count,
+                          int dtype, int n, int h, int w, int heads, int head_dim, int block, float scale,
+                          const void *cached, void *out, int copy_cached, void *workspace, int64_t workspace_bytes,
+                          void *stream) {
+    if (dtype != SIGE_BF16 && dtype != SIGE_F16) return fail(SIGE_EDTYPE, "dtype %d: bf16 or fp16 only", dtype);
+    Geo g;
+    int rc = attn_geom(n, h, w, heads, head_dim, block, &g);
+    if (rc) return rc;
+    if (!q || !k || !v || !idx || !count || !out || !workspace || (copy_cached && !cached))
+        return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cout, "heads*head_dim"))) return rc;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+        (copy_cached && !aligned(cached, 16)))
+        return fail(SIGE_EALIGN, "tensors and workspace must be 16-byte aligned");
+    if (!(scale > 0.f) || scale > 1e6f) return fail(SIGE_EINVAL, "scale must be positive and finite");
+    const size_t tbytes = (size_t)n * h * w * g.cout * 2;
+    if (overlap(out, tbytes, q, tbytes) || overlap(out, tbytes, k, tbytes) || overlap(out, tbytes, v, tbytes))
+        return fail(SIGE_EINVAL, "out overlaps q, k or v");
+    if (copy_cached && overlap(out, tbytes, cached, tbytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    if ((rc = device_ready())) return rc;
+    const int grid1 = attn_grid1();
+    const int64_t need = attn_ws_bytes(g, heads, grid1);
+    if (workspace_bytes < need)
+        return fail(SIGE_ERANGE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+    if (overlap(out, tbytes, workspace, (size_t)need)) return fail(SIGE_EINVAL, "out overlaps the workspace");
+    const sige::CopyCfg cc = copy_plan(g, 2, copy_cached != 0);
+    return finish(sige::launch_attention(dtype, q, k, v, idx, count, g, heads, scale, copy_cached ? cached : nullptr,
+                                         out, cc, workspace, grid1, dev_info().cus * 4, (hipStream_t)stream),
+                  "sige_sparse_attention", (hipStream_t)stream);
 }
 
 int sige_restore_blocks(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,

@@ -68,6 +68,15 @@ hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, co
 hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, const int32_t *count, const Geo &g,
                           const void *cached, void *out, int grid, const CopyCfg &cc, hipStream_t st);
 
+// Query-pruned attention (kernels_attn.hip): head dim 64, at most 8 images.
+constexpr int kAttnHeadDim = 64;
+constexpr int kAttnImages = 8;
+constexpr long kAttnWsBytesPerItem = 64L * (64 + 4) * 4;  // partial of one (64-query tile, head, key split)
+int attn_partial_grid(int cus);
+hipError_t launch_attention(int dt, const void *q, const void *k, const void *v, const int32_t *idx,
+                            const int32_t *count, const Geo &g, int heads, float scale, const void *cached, void *out,
+                            const CopyCfg &cc, void *ws, int grid1, int grid2, hipStream_t st);
+
 // reduce limits (LDS of its workgroups)
 constexpr int kReduceMaxWidth = 8192;    // conv input width (pooled column bits of one block row)
 constexpr int kReduceBitsWords = 8192;   // pooled mask as bits, for the one-launch reduce (32 KiB)

@@ -149,6 +149,27 @@ def test_restore_validation(lib):
              s) == EALIGN
 
 
+def test_attention_validation(lib):
+    s = _v(0)
+    f = lib.sige_sparse_attention
+    far = _v(E + (1 << 35))
+
+    def call(dtype=2, n=1, h=64, w=64, heads=5, hd=64, b=4, q=A, out=far, ws=C, wsb=1 << 30, scale=0.125):
+        return f(_v(q), _v(B), _v(D), _v(A + (1 << 37)), _v(A + (1 << 38)), dtype, n, h, w, heads, hd, b,
+                 ctypes.c_float(scale), _v(E), out, 1, _v(ws), wsb, s)
+
+    assert call(dtype=0) == EDTYPE
+    assert call(hd=32) == ERANGE
+    assert call(n=9) == ERANGE
+    assert call(heads=0) == EINVAL
+    assert call(b=0) == EINVAL
+    assert call(q=A + 8) == EALIGN
+    assert call(out=_v(A + 64)) == EINVAL  # overlaps q
+    assert call(scale=0.0) == EINVAL
+    assert lib.sige_sparse_attention_workspace(1, 64, 64, 5, 32, 4) == ERANGE
+    assert lib.sige_sparse_attention_workspace(1, 64, 64, 5, 64, 4) >= 64 * 68 * 4
+
+
 def test_strerror_names_every_code(lib):
     for code, name in [(0, b"SIGE_OK"), (EINVAL, b"SIGE_EINVAL"), (EDTYPE, b"SIGE_EDTYPE"), (EALIGN, b"SIGE_EALIGN"),
                        (L.SIGE_EHIP, b"SIGE_EHIP"), (ENODEV, b"SIGE_ENODEV"), (ERANGE, b"SIGE_ERANGE")]:
