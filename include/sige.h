@@ -116,6 +116,18 @@ int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int
 int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
                      int32_t *idx, int32_t *count, void *stream);
 
+/* Step 2 with the cache copy of step 5 in the same launch: sige_reduce_mask,
+ * while the other workgroups copy `cached` into `out` (all of it:
+ * out = cached).  sige_sparse_conv_layer(..., copy_cached = 0) or
+ * sige_scatter(..., copy_cached = 0) on that `out` then gives the
+ * copy_cached = 1 result; the copy runs beside the single-workgroup reduce
+ * instead of on the convolution's critical path.
+ *   cached, out: [n, ho, wo, c_out] in `dtype` for the conv geometry g; out
+ *   must not overlap cached, mask, idx or count.  Other arguments and limits
+ *   as sige_reduce_mask. */
+int sige_reduce_mask_copy(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
+                          int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream);
+
 /* Step 3 -- gather (SIGE README, "Overview": collect the active blocks from the
  * edited activation and stack them along the batch dimension).
  *   blocks[slot, yy, xx, c] = a_edit[n, by*block*stride - pad + yy, bx*block*stride - pad + xx, c]

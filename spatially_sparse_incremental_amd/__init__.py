@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     sige_geom_derive,
     sige_max_blocks,
     sige_reduce_mask,
+    sige_reduce_mask_copy,
     sige_restore_blocks,
     sige_scatter,
     sige_sparse_attention,

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libsige.so")
 SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERANGE = 0, -1, -2, -3, -4, -5, -6
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
-EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_gather",
+EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_reduce_mask_copy",
+           "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
            "sige_sparse_attention_workspace", "sige_sparse_attention", "sige_strerror",
            "sige_last_error")
@@ -56,6 +57,7 @@ def lib():
         L.sige_max_blocks.restype = ctypes.c_int64
         L.sige_diff_mask.argtypes = [V, V, I, I, I, I, I, ctypes.c_float, V, V]
         L.sige_reduce_mask.argtypes = [V, I, I, P, I, V, V, V]
+        L.sige_reduce_mask_copy.argtypes = [V, I, I, P, I, V, V, I, V, V, V]
         L.sige_gather.argtypes = [V, I, P, V, V, V, V]
         L.sige_conv_blocks.argtypes = [V, V, V, I, P, V, V, V]
         L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
@@ -155,6 +157,26 @@ def sige_reduce_mask(mask, g: Geom, dilate_blocks=1, idx=None, count=None, strea
                                 _p(count), _stream(stream))
     _check(rc, "sige_reduce_mask")
     return idx, count
+
+
+def sige_reduce_mask_copy(mask, g: Geom, dilate_blocks, cached, out=None, idx=None, count=None, stream=None):
+    """sige_reduce_mask, with `cached` copied into `out` (all of it) by the same
+    launch; returns (idx, count, out)."""
+    if mask.dim() == 2:
+        mask = mask.unsqueeze(0)
+    _dev(mask, idx, count, cached, out)
+    cap = sige_max_blocks(g)
+    dev = mask.device
+    if idx is None:
+        idx = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((1,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(cached)
+    rc = lib().sige_reduce_mask_copy(_p(mask), mask.shape[-2], mask.shape[-1], ctypes.byref(g), dilate_blocks,
+                                     _p(idx), _p(count), _dt(cached), _p(cached), _p(out), _stream(stream))
+    _check(rc, "sige_reduce_mask_copy")
+    return idx, count, out
 
 
 def sige_gather(a_edit, g: Geom, idx, count, blocks=None, stream=None):

@@ -192,4 +192,39 @@ __device__ void copy_span(const Geo &g, const CopyCfg &cc, const uint32_t *bm, c
     }
 }
 
+// Unconditional copy of the 16-byte vectors [v0, v1) from src to dst: thread t
+// takes v0 + t, v0 + t + NTHR, ...; CB loads of the next batch are in flight
+// while the current one is stored.
+template <int CB, int NTHR>
+__device__ void copy_all_span(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, long long v0, long long v1) {
+    long long v = v0 + threadIdx.x;
+    if (v >= v1) return;
+    u32x4 ra[CB], rb[CB];
+    auto fill = [&](u32x4 (&r)[CB], long long base) {
+#pragma unroll
+        for (int i = 0; i < CB; ++i) r[i] = ld16(src + min(base + (long long)i * NTHR, v1 - 1) * 16);
+    };
+    auto drain = [&](const u32x4 (&r)[CB], long long base) {
+#pragma unroll
+        for (int i = 0; i < CB; ++i)
+            if (base + (long long)i * NTHR < v1) st16(dst + (base + (long long)i * NTHR) * 16, r[i]);
+    };
+    constexpr long long step = (long long)CB * NTHR;
+    fill(ra, v);
+    for (;; v += 2 * step) {
+        if (v + step >= v1) {
+            drain(ra, v);
+            return;
+        }
+        fill(rb, v + step);
+        drain(ra, v);
+        if (v + 2 * step >= v1) {
+            drain(rb, v + step);
+            return;
+        }
+        fill(ra, v + 2 * step);
+        drain(rb, v + step);
+    }
+}
+
 }  // namespace sige

@@ -314,11 +314,18 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     float *part = (float *)smem;
     const float *bsrc = a.bias ? a.bias : (const float *)a.w;  // any readable floats when there is no bias
 
+    // Tile t runs on XCD t % 8 (the grid is a multiple of 8), and the N tiles of
+    // one M tile share t % 8: t = 8 * (ntn * q + tn) + x holds M tile 8 * q + x,
+    // so an M tile's input windows are fetched into one XCD's L2 only.  M tiles
+    // are padded to a multiple of 8; the padding tiles are empty.
+    const int tiles_cap = ((mcap + BM - 1) / BM + 7) / 8 * 8 * ntn;
+    auto tiles_of = [&](int cnt) { return ((cnt * b2 + BM - 1) / BM + 7) / 8 * 8 * ntn; };
     for (int t = blockIdx.x;; t += grid) {
         if (ntiles >= 0 && t >= ntiles) break;  // known after the first tile
-        const int tm = t / ntn, tn = t - tm * ntn;
-        const int m0 = tm * BM;
-        if (m0 >= mcap) break;
+        if (t >= tiles_cap) break;
+        const int r8 = t >> 3, tn = r8 % ntn;
+        const int tm = (r8 / ntn) * 8 + (t & 7);
+        const int m0 = min(tm * BM, mcap - 1);  // padding tiles past capacity read the last slot
         const int n0 = tn * BN;
         const int s_lo = fdiv(m0, c.m_b2);
         const int s_hi = min(g.cap - 1, fdiv(m0 + BM - 1, c.m_b2));
@@ -365,9 +372,10 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             if (tid < cnt && spec >= 0 && spec < g.cap) atomicOr(&s_bm[spec >> 5], 1u << (spec & 31));
             spec_done = true;
         }
-        if (ntiles < 0) ntiles = ((cnt * b2 + BM - 1) / BM) * ntn;
+        if (ntiles < 0) ntiles = tiles_of(cnt);
         if (t >= ntiles) break;
         const int mrows = cnt * b2;
+        if (tm * BM >= mrows) continue;  // a padding tile
         // LDS byte offset of this lane's row in each M subtile (tap (0,0), channel 0)
         int rb[MT];
 #pragma unroll
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         int cnt = cnt_seen;
         if (ntiles < 0) {  // this workgroup had no tile position at all
             cnt = min(max(__hip_atomic_load(a.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0), g.cap);
-            ntiles = ((cnt * b2 + BM - 1) / BM) * ntn;
+            ntiles = tiles_of(cnt);
         }
         // this workgroup's part: vectors of the copy, or slots of the previous list
         long long lo, hi;

@@ -6,7 +6,7 @@
 // "Overview" (compute the difference mask).  Step 2 follows the same notes,
 // section 3.2 (downsample the mask to several scales, dilate it, use it to pick
 // tiles) and the README "Overview" (reduce the mask to active block indices).
-#include "sige_internal.h"
+#include "device_common.h"
 
 namespace sige {
 
@@ -108,7 +108,15 @@ hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix
 //    in ascending order over the idx buffer, after all flags were read.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_activity(const uint8_t *__restrict__ mask, int hm, int wm, int fy, int fx,
-                                                  Geo g, int vec16, uint8_t *__restrict__ flags) {
+                                                  Geo g, int vec16, uint8_t *__restrict__ flags, ReduceCopy cp,
+                                                  int ncopy) {
+    if ((int)blockIdx.x >= g.nby) {  // workgroups past the block rows copy the cache (image row 0 only)
+        if (blockIdx.y == 0) {
+            const int i = blockIdx.x - g.nby;
+            copy_all_span<4, 256>(cp.src, cp.dst, split_point(cp.nvec, i, ncopy), split_point(cp.nvec, i + 1, ncopy));
+        }
+        return;
+    }
     __shared__ uint32_t colbits[kReduceMaxWidth / 32];
     constexpr int U = 8;
     const int tid = threadIdx.x;
@@ -281,7 +289,13 @@ __device__ __forceinline__ int compact_round(bool on, int q_out, int running, in
 
 __global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__ mask, int hm, int wm, int fy, int fx,
                                                      Geo g, int dil, int vec16, RedCfg rc,
-                                                     int32_t *__restrict__ idx, int32_t *__restrict__ count) {
+                                                     int32_t *__restrict__ idx, int32_t *__restrict__ count,
+                                                     ReduceCopy cp) {
+    if (blockIdx.x > 0) {  // the other workgroups copy the cache meanwhile
+        const int i = blockIdx.x - 1, nw = gridDim.x - 1;
+        copy_all_span<2, 1024>(cp.src, cp.dst, split_point(cp.nvec, i, nw), split_point(cp.nvec, i + 1, nw));
+        return;
+    }
     __shared__ uint32_t bits[kReduceBitsWords];
     // per block row: OR of the bit rows under its (dilated) windows; or, when
     // windows do not touch, the raw and x-dilated block flags
@@ -406,7 +420,8 @@ __global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__
 }
 
 hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
-                         int32_t *count, hipStream_t st) {
+                         int32_t *count, const ReduceCopy &cp, int copy_wgs, hipStream_t st) {
+    const int ncopy = cp.nvec > 0 ? copy_wgs : 0;
     const int fy = hm / g.h, fx = wm / g.w;
     const int WW = (g.w + 31) / 32;
     // the one-launch path divides with 31-bit multipliers: every dividend * divisor < 2^31
@@ -416,12 +431,13 @@ hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int 
     if (exact && (long)g.h * WW <= kReduceBitsWords && g.nby * g.nbx <= kReduceMaxBlocks) {
         RedCfg rc{vec16 ? fast_div_magic(wm / 16) : 1u, fast_div_magic(wm), fast_div_magic(fy), fast_div_magic(fx),
                   fast_div_magic(g.nbx)};
-        hipLaunchKernelGGL(k_reduce_one, dim3(1), dim3(1024), 0, st, mask, hm, wm, fy, fx, g, dilate, vec16, rc, idx,
-                           count);
+        hipLaunchKernelGGL(k_reduce_one, dim3(1 + ncopy), dim3(1024), 0, st, mask, hm, wm, fy, fx, g, dilate, vec16,
+                           rc, idx, count, cp);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_activity, dim3(g.nby, g.n), dim3(256), 0, st, mask, hm, wm, fy, fx, g, vec16,
-                       (uint8_t *)idx);
+    const int ncopy4 = ncopy * 4;  // 256-thread workgroups
+    hipLaunchKernelGGL(k_activity, dim3(g.nby + ncopy4, g.n), dim3(256), 0, st, mask, hm, wm, fy, fx, g, vec16,
+                       (uint8_t *)idx, cp, ncopy4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, g, dilate, idx, count);

@@ -215,7 +215,8 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
     c.m_b2 = sige::fast_div_magic(b2);
     c.m_b = sige::fast_div_magic(g.b);
     long grid = 1L << 30;  // the launch trims this to the CUs' resident capacity
-    if (!(fused && copy)) grid = ((long)g.cap * b2 + BM - 1) / BM * ((g.cout + BN - 1) / BN);
+    if (!(fused && copy))  // tiles at capacity, M tiles padded to a multiple of 8 (see the kernel's tile order)
+        grid = (((long)g.cap * b2 + BM - 1) / BM + 7) / 8 * 8 * ((g.cout + BN - 1) / BN);
     c.cus = dv.cus;
     c.grid = (int)(grid > 0 ? grid : 1);
     *out = c;
@@ -247,6 +248,50 @@ int64_t attn_ws_bytes(const Geo &g, int heads, int grid1) {
     const long max_items = (long)g.n * ((per * b2 + 63) / 64) * heads;
     const long items = max_items > 2L * grid1 ? max_items : 2L * grid1;
     return (int64_t)items * sige::kAttnWsBytesPerItem;
+}
+
+int reduce_common(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks, int32_t *idx,
+                  int32_t *count, int dtype, const void *cached, void *out, void *stream, const char *what) {
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!mask || !idx || !count) return fail(SIGE_EINVAL, "NULL pointer");
+    if (mask_h < g.h || mask_w < g.w || mask_h % g.h || mask_w % g.w)
+        return fail(SIGE_EINVAL, "mask %dx%d is not an integer multiple of the conv input %dx%d", mask_h, mask_w,
+                    g.h, g.w);
+    if (dilate_blocks < 0 || dilate_blocks > 16) return fail(SIGE_EINVAL, "dilate_blocks=%d outside [0, 16]", dilate_blocks);
+    if (g.w > sige::kReduceMaxWidth)
+        return fail(SIGE_ERANGE, "conv input width %d exceeds the reduce limit %d", g.w, sige::kReduceMaxWidth);
+    if (g.cap > sige::kReduceMaxBlocks)
+        return fail(SIGE_ERANGE, "%d blocks (n*nby*nbx) exceed the reduce limit %d", g.cap, sige::kReduceMaxBlocks);
+    if (!aligned(idx, 4) || !aligned(count, 4)) return fail(SIGE_EALIGN, "idx/count must be 4-byte aligned");
+    const size_t mbytes = (size_t)g.n * mask_h * mask_w;
+    if (overlap(idx, (size_t)g.cap * 4, mask, mbytes) || overlap(count, 4, mask, mbytes) ||
+        overlap(count, 4, idx, (size_t)g.cap * 4))
+        return fail(SIGE_EINVAL, "idx, count and mask must not overlap");
+    sige::ReduceCopy cp{nullptr, nullptr, 0};
+    if (out) {  // the reduce with the cache copy
+        if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+        if (!cached) return fail(SIGE_EINVAL, "NULL pointer");
+        if ((rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+        if (!aligned(cached, 16) || !aligned(out, 16)) return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
+        const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * sige::elem_bytes(dtype);
+        if (overlap(out, obytes, cached, obytes) || overlap(out, obytes, mask, mbytes) ||
+            overlap(out, obytes, idx, (size_t)g.cap * 4) || overlap(out, obytes, count, 4))
+            return fail(SIGE_EINVAL, "out overlaps cached, mask, idx or count");
+        cp = sige::ReduceCopy{(const uint8_t *)cached, (uint8_t *)out, (long long)(obytes / 16)};
+    }
+    if ((rc = device_ready())) return rc;
+    const int vec16 = (mask_w % 16 == 0) && aligned(mask, 16);
+    static int copy_wgs = -1;  // SIGE_REDUCE_COPY_WGS overrides the copy's workgroups (tuning)
+    if (copy_wgs < 0) {
+        const char *v = getenv("SIGE_REDUCE_COPY_WGS");
+        const long x = v ? strtol(v, nullptr, 10) : 0;
+        copy_wgs = (x > 0 && x < 65536) ? (int)x : 0;
+    }
+    return finish(sige::launch_reduce(mask, mask_h, mask_w, g, dilate_blocks, vec16, idx, count, cp,
+                                      copy_wgs ? copy_wgs : dev_info().cus / 2, (hipStream_t)stream),
+                  what, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -315,29 +360,18 @@ int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int
                   "sige_diff_mask", (hipStream_t)stream);
 }
 
+
 int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,
                      int32_t *idx, int32_t *count, void *stream) {
-    Geo g;
-    int rc = derive(gp, &g);
-    if (rc) return rc;
-    if (!mask || !idx || !count) return fail(SIGE_EINVAL, "NULL pointer");
-    if (mask_h < g.h || mask_w < g.w || mask_h % g.h || mask_w % g.w)
-        return fail(SIGE_EINVAL, "mask %dx%d is not an integer multiple of the conv input %dx%d", mask_h, mask_w,
-                    g.h, g.w);
-    if (dilate_blocks < 0 || dilate_blocks > 16) return fail(SIGE_EINVAL, "dilate_blocks=%d outside [0, 16]", dilate_blocks);
-    if (g.w > sige::kReduceMaxWidth)
-        return fail(SIGE_ERANGE, "conv input width %d exceeds the reduce limit %d", g.w, sige::kReduceMaxWidth);
-    if (g.cap > sige::kReduceMaxBlocks)
-        return fail(SIGE_ERANGE, "%d blocks (n*nby*nbx) exceed the reduce limit %d", g.cap, sige::kReduceMaxBlocks);
-    if (!aligned(idx, 4) || !aligned(count, 4)) return fail(SIGE_EALIGN, "idx/count must be 4-byte aligned");
-    const size_t mbytes = (size_t)g.n * mask_h * mask_w;
-    if (overlap(idx, (size_t)g.cap * 4, mask, mbytes) || overlap(count, 4, mask, mbytes) ||
-        overlap(count, 4, idx, (size_t)g.cap * 4))
-        return fail(SIGE_EINVAL, "idx, count and mask must not overlap");
-    if ((rc = device_ready())) return rc;
-    const int vec16 = (mask_w % 16 == 0) && aligned(mask, 16);
-    return finish(sige::launch_reduce(mask, mask_h, mask_w, g, dilate_blocks, vec16, idx, count, (hipStream_t)stream),
-                  "sige_reduce_mask", (hipStream_t)stream);
+    return reduce_common(mask, mask_h, mask_w, gp, dilate_blocks, idx, count, 0, nullptr, nullptr, stream,
+                         "sige_reduce_mask");
+}
+
+int sige_reduce_mask_copy(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,
+                          int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream) {
+    if (!out) return fail(SIGE_EINVAL, "NULL pointer");
+    return reduce_common(mask, mask_h, mask_w, gp, dilate_blocks, idx, count, dtype, cached, out, stream,
+                         "sige_reduce_mask_copy");
 }
 
 int sige_gather(const void *a_edit, int dtype, const sige_geom *gp, const int32_t *idx, const int32_t *count,

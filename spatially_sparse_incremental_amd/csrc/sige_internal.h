@@ -52,8 +52,15 @@ struct CopyCfg {
 
 hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix, int vpp, float tau,
                        uint8_t *mask, hipStream_t st);
+// An unconditional copy of nvec 16-byte vectors from src to dst, done by extra
+// workgroups of the reduce launch (nvec 0: none).
+struct ReduceCopy {
+    const uint8_t *src;
+    uint8_t *dst;
+    long long nvec;
+};
 hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
-                         int32_t *count, hipStream_t st);
+                         int32_t *count, const ReduceCopy &cp, int copy_wgs, hipStream_t st);
 hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t *idx, const int32_t *count,
                          void *blocks, hipStream_t st);
 // fused = 0: src = stacked blocks, dst = output blocks.  fused = 1: src = a_edit, dst = out;

@@ -128,6 +128,19 @@ def test_conv_step_validation(lib):
                                       1, s) == ERANGE
 
 
+def test_reduce_copy_validation(lib):
+    s = _v(0)
+    g = _g()
+    f = lib.sige_reduce_mask_copy
+    far = _v(E + (1 << 35))
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, None, far, s) == EINVAL
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, _v(D), None, s) == EINVAL
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), 5, _v(D), far, s) == EDTYPE
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, _v(D + 8), far, s) == EALIGN
+    assert f(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, _v(D), _v(D + 256), s) == EINVAL  # overlap
+    assert f(_v(A), 255, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, _v(D), far, s) == EINVAL  # not a multiple
+
+
 def test_restore_validation(lib):
     s = _v(0)
     g = _g()

@@ -20,7 +20,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("copy", [True, False])
+@pytest.mark.parametrize("copy", ["conv", "reduce", "none"])
 def test_graph_replays_match_eager(copy):
     n, h, w, c, b = 1, 64, 72, 64, 6
     dt = torch.bfloat16
@@ -38,8 +38,11 @@ def test_graph_replays_match_eager(copy):
 
     def step():
         ssi.sige_diff_mask(a_o, a_e, 1e-6, mask=m)
-        ssi.sige_reduce_mask(m, g, 1, idx=idx, count=cnt)
-        if copy:
+        if copy == "reduce":  # the copy of the cache rides with the reduce
+            ssi.sige_reduce_mask_copy(m, g, 1, cache, out=out, idx=idx, count=cnt)
+        else:
+            ssi.sige_reduce_mask(m, g, 1, idx=idx, count=cnt)
+        if copy == "conv":
             ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out, copy_cached=True)
         else:
             ssi.sige_sparse_conv_layer(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False)
@@ -55,15 +58,16 @@ def test_graph_replays_match_eager(copy):
         step()
     rng = np.random.default_rng(203)
     for rep in range(5):
-        # a new edit, written in place into the captured input buffer
+        # a new edit, written in place into the captured input buffer; `out` holds
+        # stale values where the graph must overwrite them
         mk = torch.from_numpy((rng.random((n, h, w)) < 0.01).astype(np.uint8))
         a_e.copy_(synth.make_edit(a_o.cpu(), mk.numpy(), "replace", 210 + rep).cuda())
-        out.copy_(cache)
+        out.copy_(cache if copy == "none" else torch.zeros_like(cache))
         graph.replay()
         torch.cuda.synchronize()
         got = out.clone()
         got_idx = idx[:int(cnt.item())].clone()
-        out.copy_(cache)
+        out.copy_(cache if copy == "none" else torch.zeros_like(cache))
         step()  # eager, same inputs
         torch.cuda.synchronize()
         assert torch.equal(got_idx, idx[:int(cnt.item())]), rep

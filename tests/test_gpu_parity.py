@@ -275,6 +275,45 @@ def test_reduce_parity(case):
     assert torch.equal(idx[:cap].cpu(), torch.arange(cap, dtype=torch.int32))
 
 
+@pytest.mark.parametrize("case", [REDUCE[0], REDUCE[1], REDUCE[5], REDUCE[10], REDUCE[11]])
+def test_reduce_with_copy(case):
+    # the same list as sige_reduce_mask, and out == cached bit for bit (one- and two-launch paths)
+    n, h, w, f, k, s, p, b, d, frac = case
+    print(f"\n[reduce+copy] {case}", flush=True)
+    m = gpu(torch.from_numpy(random_mask(n, h * f, w * f, frac, 101 + h + w)))
+    cout = 24
+    g = _geom(n, h, w, 8, cout, k, s, p, b)
+    ho, wo, _, _, _ = oracle.geometry(h, w, k, s, p, b)
+    cache = rand((n, ho, wo, cout), torch.bfloat16, 77).cuda()
+    ref_idx, ref_cnt = ssi.sige_reduce_mask(m, g, d)
+    idx, cnt, out = ssi.sige_reduce_mask_copy(m, g, d, cache)
+    torch.cuda.synchronize()
+    c = int(cnt.item())
+    assert c == int(ref_cnt.item())
+    assert torch.equal(idx[:c], ref_idx[:c])
+    assert torch.equal(bits(out), bits(cache))
+
+
+@pytest.mark.parametrize("case", CASES[:4] + CASES[5:6], ids=[c[0] for c in CASES[:4] + CASES[5:6]])
+def test_step_with_copy_in_the_reduce(case):
+    # diff -> reduce+copy -> fused conv (copy_cached = 0) == diff -> reduce -> fused conv (copy_cached = 1)
+    name, n, h, w, cin, cout, k, s, p, b, dts, d, frac = case
+    dt = DT[dts]
+    mask = random_mask(n, h, w, frac, 7)
+    a_o, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 11, mask)
+    ho, wo, _, _, _ = oracle.geometry(h, w, k, s, p, b)
+    cache = rand((n, ho, wo, cout), dt, 13).cuda()
+    g = _geom(n, h, w, cin, cout, k, s, p, b)
+    ae, wk, bs = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    mk = ssi.sige_diff_mask(a_o.cuda(), ae, 1e-6)
+    idx, cnt = ssi.sige_reduce_mask(mk, g, d)
+    lit = ssi.sige_sparse_conv_layer(ae, wk, bs, cache, idx, cnt, g)
+    idx2, cnt2, out = ssi.sige_reduce_mask_copy(mk, g, d, cache)
+    ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx2, cnt2, g, out=out, copy_cached=False)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(lit)), name
+
+
 def test_reduce_at_its_limits():
     # widest conv input (8192) and largest block grid (16384) accepted, on both reduce paths
     for (h, w, b) in [(256, 1024, 16), (128, 128, 1), (16, 8192, 32), (1024, 8192, 32), (2048, 512, 8)]:
