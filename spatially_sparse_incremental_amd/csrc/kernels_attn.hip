@@ -5,10 +5,14 @@
 // the edited area.  Queries: the tokens of the listed blocks (block x block
 // tokens of the h x w grid); keys and values: every token of the same image.
 //
-// Split over keys (as in flash decoding): a work item is (64-query tile of one
-// image, head, key split).  Its 4 waves own 16 queries each and run an online
-// softmax over the split's keys, 64 at a time, with both products on the
-// matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
+// Split over keys (as in flash decoding): a work item is (128-query tile of one
+// image, head, key split).  Its 4 waves own 32 queries each (two groups of 16
+// that share every K and V fragment) and run an online softmax over the
+// split's keys, 64 at a time, with both products on the matrix cores
+// (v_mfma_f32_16x16x32_{f16,bf16}).  The key tiles of a split
+// are staged kAttnChunk at a time (K straight into LDS, V through registers
+// and written transposed), all loads of a chunk in flight together, so a
+// split of up to kAttnChunk tiles costs one memory round trip:
 //   S^T  = K Q^T      A = key rows from LDS, B = this wave's Q^T fragments (registers)
 //   O^T += V^T P^T    A = rows of a transposed V tile in LDS, B = P^T taken from S^T
 // In S^T's accumulator layout a lane holds one query and 4 keys of each
@@ -16,12 +20,13 @@
 // (the order of k inside one MFMA is free, as long as A uses the same order),
 // and every softmax statistic of a query lives in the lanes l, l^16, l^32,
 // l^48.  O^T's accumulators hold the same query per lane, so the rescale by
-// exp(m_old - m_new) needs no lane exchange.  Each item leaves (max, sum,
+// exp(m_old - m_new) needs no lane exchange; the max and sum over the four
+// k groups are two lane swaps (v_permlane16_swap, v_permlane32_swap).  Each item leaves (max, sum,
 // unnormalised O) in the caller's workspace; a second kernel combines the
 // splits, writes the queries' outputs and copies the cache elsewhere.
 //
 // Query tiles never straddle two images: each image's listed blocks are
-// padded to whole 64-row tiles (per-image block counts come from one pass
+// padded to whole 128-row tiles (per-image block counts come from one pass
 // over the list in every workgroup).
 #include "device_common.h"
 
@@ -29,12 +34,18 @@ namespace sige {
 
 constexpr int kAttnD = 64;          // head dim
 constexpr int kAttnKT = 64;         // keys per LDS tile
-constexpr int kAttnQT = 64;         // queries per work item (4 waves x 16)
+constexpr int kAttnQW = 32;         // queries per wave (two groups of 16)
+constexpr int kAttnQT = 4 * kAttnQW;  // queries per work item
+static_assert(kAttnQT == kAttnQueryTile, "query tile");
 constexpr int kAttnThreads = 256;
 constexpr int kAttnMaxImages = 8;
 constexpr int kAttnWsRow = kAttnD + 4;  // floats per query in the workspace: O^T column, max, sum, pad
 constexpr int kAttnKPitch = kAttnD + 8;   // halves per key row of the K tile in LDS
 constexpr int kAttnVPitch = kAttnKT + 8;  // halves per d row of the transposed V tile
+constexpr int kAttnChunk = 4;             // key tiles staged in LDS per round trip
+constexpr int kAttnKTile = kAttnKT * kAttnKPitch;
+constexpr int kAttnVTile = kAttnD * kAttnVPitch;
+constexpr int kAttnPartialLds = kAttnChunk * (kAttnKTile + kAttnVTile) * 2;  // bytes of dynamic LDS
 
 struct AttnArgs {
     const uint8_t *q, *k, *v;
@@ -61,17 +72,34 @@ struct AttnMfma {  // one 16x16x32 MFMA
     }
 };
 
+// Two floats rounded to nearest even and packed (one v_cvt_pk_{bf16,f16}_f32).
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    uint16_t a, b;
-    if constexpr (DT == 1) {
-        a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-        b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    } else {
-        a = __builtin_bit_cast(uint16_t, (_Float16)lo);
-        b = __builtin_bit_cast(uint16_t, (_Float16)hi);
-    }
-    return (uint32_t)a | ((uint32_t)b << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    if constexpr (DT == 1)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+
+
+// Max and sum over the lanes l, l^16, l^32, l^48 (the four k groups that hold
+// one query's statistics): each lane swap leaves a lane's own value and its
+// partner's in the two outputs, in either order.
+__device__ __forceinline__ float qmax(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float qsum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Per-image bookkeeping of the listed blocks, in LDS: first slot and first
@@ -83,6 +111,15 @@ struct AttnTiles {
 
 __device__ void attn_tiles(const Geo &g, const int32_t *__restrict__ idx, int cnt, AttnTiles *t, int *cnt_img) {
     const int per = g.nby * g.nbx, b2 = g.b * g.b;
+    if (g.n == 1) {  // one image: every slot is its own, no pass over the list
+        if (threadIdx.x == 0) {
+            t->first_slot[0] = t->first_tile[0] = 0;
+            t->first_slot[1] = cnt;
+            t->first_tile[1] = (cnt * b2 + kAttnQT - 1) / kAttnQT;
+        }
+        __syncthreads();
+        return;
+    }
     if (threadIdx.x < kAttnMaxImages) cnt_img[threadIdx.x] = 0;
     __syncthreads();
     constexpr int U = 4;
@@ -109,33 +146,43 @@ __device__ void attn_tiles(const Geo &g, const int32_t *__restrict__ idx, int cn
     __syncthreads();
 }
 
-// Keys per split: the split count gives the grid about two items per workgroup.
+// Keys per split: enough splits for every co-resident workgroup to hold a work
+// item, at most 16, and none shorter than one staged chunk of key tiles.
 __device__ __forceinline__ void attn_split(int items, int nkt, int grid, int &S, int &ktp) {
-    S = items > 0 ? (2 * grid) / items : 1;
-    S = max(1, min(S, min(16, nkt)));
+    const int one_chunk = (nkt + kAttnChunk - 1) / kAttnChunk;
+    S = items > 0 ? grid / items : 1;
+    S = max(1, min(S, min(16, one_chunk)));
     ktp = (nkt + S - 1) / S;
 }
 
-// The token of query row `row` of a tile of image n (or -1 past the image's rows
-// or outside the grid).
-__device__ __forceinline__ int attn_token(const Geo &g, const int32_t *__restrict__ idx, const AttnTiles &t, int n,
-                                          int row) {
+// The list entry behind query row `row` of a tile of image n is idx[slot]; the
+// token it names (or -1: a row past the image's rows, an invalid entry, a
+// pixel outside the grid).
+__device__ __forceinline__ int attn_slot(const Geo &g, const AttnTiles &t, int n, int row) {
+    const int b2 = g.b * g.b;
+    const int nrows = (t.first_slot[n + 1] - t.first_slot[n]) * b2;
+    const int slot = t.first_slot[n] + min(row, max(nrows - 1, 0)) / b2;
+    return min(max(slot, 0), g.cap - 1);
+}
+
+__device__ __forceinline__ int attn_token_of(const Geo &g, const AttnTiles &t, int n, int row, int ent) {
     const int b2 = g.b * g.b;
     const int nrows = (t.first_slot[n + 1] - t.first_slot[n]) * b2;
     if (row >= nrows) return -1;
-    const int slot = t.first_slot[n] + row / b2, pix = row - (row / b2) * b2;
+    const int pix = row - (row / b2) * b2;
     int nn, by, bx;
-    if (!decode_block(g, idx[slot], nn, by, bx) || nn != n) return -1;
+    if (!decode_block(g, ent, nn, by, bx) || nn != n) return -1;
     const int y = by * g.b + pix / g.b, x = bx * g.b + pix % g.b;
     if (y >= g.h || x >= g.w) return -1;
     return y * g.w + x;
 }
 
 template <int DT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(AttnArgs a) {
     constexpr int D = kAttnD, KT = kAttnKT;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * kAttnKPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kAttnVPitch];
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    uint16_t *const Ks = lds;                            // kAttnChunk K tiles, key rows
+    uint16_t *const Vt = lds + kAttnChunk * kAttnKTile;  // kAttnChunk V tiles, transposed
     __shared__ AttnTiles tiles;
     __shared__ int cnt_img[kAttnMaxImages];
     const Geo &g = a.g;
@@ -148,124 +195,196 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     const int ntiles = tiles.first_tile[g.n];
     const int items = ntiles * a.heads;
     int S, ktp;
-    attn_split(items, nkt, gridDim.x, S, ktp);
+    attn_split(items, nkt, a.grid1, S, ktp);
     const int ql = lane & 15, kg = lane >> 4;  // this lane's query (B/C column) and k group
+    constexpr int G = kAttnQW / 16;             // 16-query groups per wave
     for (int p = blockIdx.x; p < items * S; p += gridDim.x) {
         const int split = p % S, item = p / S;
         const int head = item % a.heads, tile = item / a.heads;
         int n = 0;
         while (n + 1 < g.n && tiles.first_tile[n + 1] <= tile) ++n;
-        const int row = (tile - tiles.first_tile[n]) * kAttnQT + wave * 16 + ql;
-        const int tok = attn_token(g, a.idx, tiles, n, row);
-        // this wave's Q^T fragments: query ql, d = 32 * ks + 8 * kg + (0..7)
-        u32x4 qf[2];
         const size_t img = (size_t)n * L;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            qf[ks] = ld16(a.q + ((img + (tok < 0 ? 0 : tok)) * C + head * D + ks * 32 + kg * 8) * 2);
-        f32x4 oT[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) oT[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run = -INFINITY, l_run = 0.f;
+        const int row0 = (tile - tiles.first_tile[n]) * kAttnQT + wave * kAttnQW + ql;  // group q: row0 + 16 q
         const int kt0 = split * ktp, kt1 = min(nkt, kt0 + ktp);
-        for (int kt = kt0; kt < kt1; ++kt) {
-            const int j0 = kt * KT;
-            __syncthreads();  // every wave is done with the previous tile
-            // K tile: key rows of 8 16-byte slots and a pad slot, straight into LDS
-            for (int qg = wave; qg < (KT * 9 + 63) / 64; qg += 4) {
-                const int slot = qg * 64 + lane, key = slot / 9, c = slot - key * 9;
-                if (key < KT && c < 8) {
-                    const int j = min(j0 + key, L - 1);
+        __syncthreads();  // every wave is done with the staged tiles of the previous item
+        // One round trip per chunk: the list entries of this lane's queries
+        // first, then every K and V load of the chunk (keys past the end are
+        // clamped and their values never used).
+        int ent[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) ent[q] = a.idx[attn_slot(g, tiles, n, row0 + 16 * q)];
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 vv[kAttnChunk][2];
+        auto issue = [&](int c0, int nt) {
+            // K: up to kAttnChunk tiles x 64 keys x 9 slots (8 of 16 bytes, then
+            // a pad slot that takes a duplicate) = 9 wave loads per wave and 4 tiles
+#pragma unroll
+            for (int i = 0; i < kAttnChunk * KT * 9 / 64 / 4; ++i) {
+                const int qg = wave + 4 * i;
+                const int s = qg * 64 + lane;
+                const int t = s / (KT * 9), r = s - t * (KT * 9), key = r / 9, c = (r - key * 9) & 7;
+                if (qg * 64 < nt * KT * 9) {  // wave-uniform
+                    const int j = min(min(c0 + t, nkt - 1) * KT + key, L - 1);
                     __builtin_amdgcn_global_load_lds(
                         (const void *)(a.k + ((img + j) * C + head * D + c * 8) * 2),
                         (__attribute__((address_space(3))) void *)((uint8_t *)Ks + qg * 1024), 16, 0, 0);
                 }
             }
-            // V tile, transposed: 16 bytes of one key row per thread and step
+            // V: 16 bytes of one key row per thread, two per tile (into registers);
+            // a wave takes one 8-channel slice of 64 keys, so that the transposed
+            // writes below go to 64 consecutive halves
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int c = tid + i * kAttnThreads, key = c >> 3, dc = c & 7;
-                const int j = min(j0 + key, L - 1);
-                const u32x4 vv = ld16(a.v + ((img + j) * C + head * D + dc * 8) * 2);
+            for (int t = 0; t < kAttnChunk; ++t)
+                if (t < nt) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Vt[(dc * 8 + 2 * e) * kAttnVPitch + key] = (uint16_t)(vv[e] & 0xFFFFu);
-                    Vt[(dc * 8 + 2 * e + 1) * kAttnVPitch + key] = (uint16_t)(vv[e] >> 16);
+                    for (int i = 0; i < 2; ++i) {
+                        const int cx = tid + i * kAttnThreads, key = cx & 63, dc = cx >> 6;
+                        const int j = min((c0 + t) * KT + key, L - 1);
+                        vv[t][i] = ld16(a.v + ((img + j) * C + head * D + dc * 8) * 2);
+                    }
                 }
+        };
+        issue(kt0, min(kAttnChunk, kt1 - kt0));
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's Q^T fragments: query ql of group q, d = 32 * ks + 8 * kg + (0..7)
+        u32x4 qf[G][2];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int tok = attn_token_of(g, tiles, n, row0 + 16 * q, ent[q]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                qf[q][ks] = ld16(a.q + ((img + (tok < 0 ? 0 : tok)) * C + head * D + ks * 32 + kg * 8) * 2);
+        }
+        f32x4 oT[G][4];
+        float m_run[G], l_run[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) oT[q][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run[q] = -INFINITY;
+            l_run[q] = 0.f;
+        }
+        for (int c0 = kt0; c0 < kt1; c0 += kAttnChunk) {
+            const int nt = min(kAttnChunk, kt1 - c0);
+            if (c0 > kt0) {
+                __syncthreads();  // every wave is done with the previous chunk
+                issue(c0, nt);
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(0);  // the chunk (LDS and registers) has landed
+            // V tiles, transposed: 8 values of one key row per thread and load
+#pragma unroll
+            for (int t = 0; t < kAttnChunk; ++t)
+                if (t < nt) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int cx = tid + i * kAttnThreads, key = cx & 63, dc = cx >> 6;
+                        uint16_t *vt = Vt + t * kAttnVTile + key;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            vt[(dc * 8 + 2 * e) * kAttnVPitch] = (uint16_t)(vv[t][i][e] & 0xFFFFu);
+                            vt[(dc * 8 + 2 * e + 1) * kAttnVPitch] = (uint16_t)(vv[t][i][e] >> 16);
+                        }
+                    }
+                }
             __syncthreads();
-            // S^T = K Q^T for the 4 subtiles of 16 keys
-            f32x4 sT[4];
+            for (int t = 0; t < nt; ++t) {
+                const int j0 = (c0 + t) * KT;
+                const uint16_t *kb = Ks + t * kAttnKTile, *vb = Vt + t * kAttnVTile;
+                // every fragment of the tile requested at once: K rows for S^T,
+                // rows of V^T for O^T (keys 32*pr + 4*kg + (0..3) and 32*pr + 16 + 4*kg + (0..3));
+                // both query groups share them
+                u32x4 kf[4][2], vf[2][4];
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) {
-                sT[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const u32x4 kf = *(const u32x4 *)(Ks + (sub * 16 + ql) * kAttnKPitch + ks * 32 + kg * 8);
-                    sT[sub] = AttnMfma<DT>::run(kf, qf[ks], sT[sub]);
+                    for (int ks = 0; ks < 2; ++ks)
+                        kf[sub][ks] = *(const u32x4 *)(kb + (sub * 16 + ql) * kAttnKPitch + ks * 32 + kg * 8);
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint16_t *vr = vb + (m * 16 + ql) * kAttnVPitch + pr * 32 + kg * 4;
+                        const uint2 lo = *(const uint2 *)vr, hi = *(const uint2 *)(vr + 16);
+                        vf[pr][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    }
+                // S^T = K Q^T for the 4 subtiles of 16 keys
+                f32x4 sT[G][4];
+#pragma unroll
+                for (int q = 0; q < G; ++q)
+#pragma unroll
+                    for (int sub = 0; sub < 4; ++sub) {
+                        sT[q][sub] = AttnMfma<DT>::run(kf[sub][0], qf[q][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                        sT[q][sub] = AttnMfma<DT>::run(kf[sub][1], qf[q][1], sT[q][sub]);
+                    }
+                // online softmax for query ql of each group: keys 16 * sub + 4 * kg + i
+                // of this tile.  Scores stay unscaled (the scale is positive, so the
+                // max commutes with it); only a tile past the last key masks.
+                if (j0 + KT > L) {
+#pragma unroll
+                    for (int q = 0; q < G; ++q)
+#pragma unroll
+                        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (j0 + sub * 16 + kg * 4 + i >= L) sT[q][sub][i] = -INFINITY;
                 }
-            }
-            // online softmax for query ql: keys 16 * sub + 4 * kg + i of this tile
-            float mt = -INFINITY;
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
+                for (int q = 0; q < G; ++q) {
+                    float mt = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool valid = j0 + sub * 16 + kg * 4 + i < L;
-                    const float x = valid ? sT[sub][i] * a.scale_log2 : -INFINITY;
-                    sT[sub][i] = x;
-                    mt = fmaxf(mt, x);
+                    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sT[q][sub][i]);
+                    const float m_new = fmaxf(m_run[q], a.scale_log2 * qmax(mt));
+                    if (__ballot(m_new != m_run[q])) {  // some query's max moved: rescale the wave's sums
+                        const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
+                        l_run[q] *= alpha;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) oT[q][m] *= alpha;
+                        m_run[q] = m_new;
+                    }
+                    float ps = 0.f;
+#pragma unroll
+                    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = __builtin_amdgcn_exp2f(fmaf(sT[q][sub][i], a.scale_log2, -m_new));
+                            sT[q][sub][i] = e;
+                            ps += e;
+                        }
+                    l_run[q] += qsum(ps);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = exp2f(m_run - m_new);
-            float ps = 0.f;
+                // O^T += V^T P^T, 32 keys per MFMA; P^T straight from S^T's accumulators
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
+                for (int q = 0; q < G; ++q)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = exp2f(sT[sub][i] - m_new);
-                    sT[sub][i] = e;
-                    ps += e;
-                }
-            ps += __shfl_xor(ps, 16);
-            ps += __shfl_xor(ps, 32);
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const u32x4 pb = u32x4{pack2<DT>(sT[q][2 * pr][0], sT[q][2 * pr][1]),
+                                               pack2<DT>(sT[q][2 * pr][2], sT[q][2 * pr][3]),
+                                               pack2<DT>(sT[q][2 * pr + 1][0], sT[q][2 * pr + 1][1]),
+                                               pack2<DT>(sT[q][2 * pr + 1][2], sT[q][2 * pr + 1][3])};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) oT[m] *= alpha;
-            // O^T += V^T P^T, 32 keys per MFMA: keys 32*pr + 4*kg + (0..3) and 32*pr + 16 + 4*kg + (0..3)
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const u32x4 pb = u32x4{pack2<DT>(sT[2 * pr][0], sT[2 * pr][1]), pack2<DT>(sT[2 * pr][2], sT[2 * pr][3]),
-                                       pack2<DT>(sT[2 * pr + 1][0], sT[2 * pr + 1][1]),
-                                       pack2<DT>(sT[2 * pr + 1][2], sT[2 * pr + 1][3])};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint16_t *vr = Vt + (m * 16 + ql) * kAttnVPitch + pr * 32 + kg * 4;
-                    const uint2 lo = *(const uint2 *)vr, hi = *(const uint2 *)(vr + 16);
-                    oT[m] = AttnMfma<DT>::run(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, oT[m]);
-                }
+                        for (int m = 0; m < 4; ++m) oT[q][m] = AttnMfma<DT>::run(vf[pr][m], pb, oT[q][m]);
+                    }
             }
         }
-        // this item's partial: unnormalised O^T column of query ql, then max and sum
-        float *wp = a.ws + ((size_t)p * kAttnQT + wave * 16 + ql) * kAttnWsRow;
+        // this item's partial: unnormalised O^T column of each query, then max and sum
 #pragma unroll
-        for (int m = 0; m < 4; ++m) *(f32x4 *)(wp + m * 16 + kg * 4) = oT[m];
-        if (kg == 0) {
-            wp[D] = m_run;
-            wp[D + 1] = l_run;
+        for (int q = 0; q < G; ++q) {
+            float *wp = a.ws + ((size_t)p * kAttnQT + wave * kAttnQW + 16 * q + ql) * kAttnWsRow;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) *(f32x4 *)(wp + m * 16 + kg * 4) = oT[q][m];
+            if (kg == 0) *(float2 *)(wp + D) = float2{m_run[q], l_run[q]};
         }
     }
 }
 
-// Combine the key splits of every query and head, write the outputs, then copy
-// the cache elsewhere (copy_cached).
+// Combine the key splits of every query and head and write the outputs; the
+// workgroups past the ones with combine work copy the cache elsewhere
+// (copy_cached).  Every split's partial of a thread is requested at once.
 template <int DT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
-    constexpr int D = kAttnD;
+    constexpr int D = kAttnD, SMAX = 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ AttnTiles tiles;
     __shared__ int cnt_img[kAttnMaxImages];
@@ -287,21 +406,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
         const int head = item % a.heads, tile = item / a.heads;
         int n = 0;
         while (n + 1 < g.n && tiles.first_tile[n + 1] <= tile) ++n;
-        const int tok = attn_token(g, a.idx, tiles, n, (tile - tiles.first_tile[n]) * kAttnQT + qi);
+        const int row = (tile - tiles.first_tile[n]) * kAttnQT + qi;
+        const int ent = a.idx[attn_slot(g, tiles, n, row)];
+        float2 ml[SMAX];
+        f32x4 x0[SMAX], x1[SMAX];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            if (s < S) {
+                const float *wp = a.ws + ((size_t)(item * S + s) * kAttnQT + qi) * kAttnWsRow;
+                ml[s] = *(const float2 *)(wp + D);
+                x0[s] = *(const f32x4 *)(wp + dc * 8);
+                x1[s] = *(const f32x4 *)(wp + dc * 8 + 4);
+            }
+        }
+        const int tok = attn_token_of(g, tiles, n, row, ent);
         if (tok < 0) continue;
         float mx = -INFINITY;
-        for (int s = 0; s < S; ++s)
-            mx = fmaxf(mx, a.ws[((size_t)(item * S + s) * kAttnQT + qi) * kAttnWsRow + D]);
-        float sum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-            const float *wp = a.ws + ((size_t)(item * S + s) * kAttnQT + qi) * kAttnWsRow;
-            const float f = wp[D] == -INFINITY ? 0.f : exp2f(wp[D] - mx);
-            sum += f * wp[D + 1];
-            const f32x4 x0 = *(const f32x4 *)(wp + dc * 8), x1 = *(const f32x4 *)(wp + dc * 8 + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[e] += f * x0[e];
-                o[4 + e] += f * x1[e];
+        for (int s = 0; s < SMAX; ++s)
+            if (s < S) mx = fmaxf(mx, ml[s].x);
+        float sum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            if (s < S) {
+                const float f = ml[s].x == -INFINITY ? 0.f : exp2f(ml[s].x - mx);
+                sum += f * ml[s].y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[e] += f * x0[s][e];
+                    o[4 + e] += f * x1[s][e];
+                }
             }
         }
         const float inv = 1.f / sum;
@@ -311,8 +445,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
         st16(a.out + (((size_t)n * L + tok) * C + head * D + dc * 8) * 2, r);
     }
     if (a.cc.nvec > 0) {
-        const long long lo = split_point(a.cc.nvec, blockIdx.x, gridDim.x);
-        const long long hi = split_point(a.cc.nvec, blockIdx.x + 1, gridDim.x);
+        const int busy = (int)((total + kAttnThreads - 1) / kAttnThreads);
+        const int c0 = busy < (int)gridDim.x / 2 ? busy : 0;  // the copy goes to the idle workgroups
+        if ((int)blockIdx.x < c0) return;
+        const int i = blockIdx.x - c0, nw = gridDim.x - c0;
+        const long long lo = split_point(a.cc.nvec, i, nw), hi = split_point(a.cc.nvec, i + 1, nw);
         if (lo < hi) {
             uint32_t *bm = nullptr;
             if (((g.cap + 31) >> 5) * 4 <= 64 * 1024) {
@@ -326,7 +463,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
 
 int attn_partial_grid(int cus) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_partial<2>, kAttnThreads, 0) != hipSuccess || n < 1) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_partial<2>, kAttnThreads, kAttnPartialLds) !=
+            hipSuccess ||
+        n < 1) {
         (void)hipGetLastError();
         n = 1;
     }
@@ -340,10 +479,10 @@ hipError_t launch_attention(int dt, const void *q, const void *k, const void *v,
                (const uint8_t *)cached, (uint8_t *)out, g, cc, heads, scale * 1.4426950408889634f, grid1};
     const int bm = cc.nvec > 0 && ((g.cap + 31) / 32) * 4 <= 64 * 1024 ? ((g.cap + 31) / 32) * 4 : 0;
     if (dt == 1) {
-        hipLaunchKernelGGL(k_attn_partial<1>, dim3(grid1), dim3(kAttnThreads), 0, st, a);
+        hipLaunchKernelGGL(k_attn_partial<1>, dim3(grid1), dim3(kAttnThreads), kAttnPartialLds, st, a);
         hipLaunchKernelGGL(k_attn_combine<1>, dim3(grid2), dim3(kAttnThreads), bm, st, a);
     } else {
-        hipLaunchKernelGGL(k_attn_partial<2>, dim3(grid1), dim3(kAttnThreads), 0, st, a);
+        hipLaunchKernelGGL(k_attn_partial<2>, dim3(grid1), dim3(kAttnThreads), kAttnPartialLds, st, a);
         hipLaunchKernelGGL(k_attn_combine<2>, dim3(grid2), dim3(kAttnThreads), bm, st, a);
     }
     return hipGetLastError();

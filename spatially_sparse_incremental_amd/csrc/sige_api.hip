@@ -245,7 +245,7 @@ int attn_grid1() {
 
 int64_t attn_ws_bytes(const Geo &g, int heads, int grid1) {
     const long per = (long)g.nby * g.nbx, b2 = (long)g.b * g.b;
-    const long max_items = (long)g.n * ((per * b2 + 63) / 64) * heads;
+    const long max_items = (long)g.n * ((per * b2 + sige::kAttnQueryTile - 1) / sige::kAttnQueryTile) * heads;
     const long items = max_items > 2L * grid1 ? max_items : 2L * grid1;
     return (int64_t)items * sige::kAttnWsBytesPerItem;
 }

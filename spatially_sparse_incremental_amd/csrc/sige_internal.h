@@ -78,7 +78,8 @@ hipError_t launch_scatter(int dt, const void *out_blocks, const int32_t *idx, co
 // Query-pruned attention (kernels_attn.hip): head dim 64, at most 8 images.
 constexpr int kAttnHeadDim = 64;
 constexpr int kAttnImages = 8;
-constexpr long kAttnWsBytesPerItem = 64L * (64 + 4) * 4;  // partial of one (64-query tile, head, key split)
+constexpr long kAttnQueryTile = 128;  // queries per work item
+constexpr long kAttnWsBytesPerItem = kAttnQueryTile * (64 + 4) * 4;  // partial of one (query tile, head, key split)
 int attn_partial_grid(int cus);
 hipError_t launch_attention(int dt, const void *q, const void *k, const void *v, const int32_t *idx,
                             const int32_t *count, const Geo &g, int heads, float scale, const void *cached, void *out,
