@@ -6,7 +6,7 @@
 // "Overview" (compute the difference mask).  Step 2 follows the same notes,
 // section 3.2 (downsample the mask to several scales, dilate it, use it to pick
 // tiles) and the README "Overview" (reduce the mask to active block indices).
-#include "device_common.h"
+#include "mask_core.h"
 
 namespace sige {
 
@@ -18,67 +18,9 @@ namespace sige {
 // lanes of a group is one __ballot; the group leader writes 4 mask bytes at once.
 // ---------------------------------------------------------------------------
 template <int DT>
-__device__ __forceinline__ bool vec_differs(u32x4 x, u32x4 y, float tau) {
-    bool f = false;
-    if constexpr (DT == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f |= fabsf(__uint_as_float(y[i]) - __uint_as_float(x[i])) > tau;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int hw = 0; hw < 2; ++hw) {
-                const uint32_t xo = (x[i] >> (16 * hw)) & 0xFFFFu, ye = (y[i] >> (16 * hw)) & 0xFFFFu;
-                float fo, fe;
-                if constexpr (DT == 1) {  // bf16 widens exactly by a 16-bit shift
-                    fo = __uint_as_float(xo << 16);
-                    fe = __uint_as_float(ye << 16);
-                } else {  // fp16 -> fp32 is exact
-                    fo = (float)__builtin_bit_cast(_Float16, (uint16_t)xo);
-                    fe = (float)__builtin_bit_cast(_Float16, (uint16_t)ye);
-                }
-                f |= fabsf(fe - fo) > tau;
-            }
-        }
-    }
-    return f;
-}
-
-template <int DT>
 __global__ __launch_bounds__(256) void k_diff(const uint8_t *__restrict__ ao, const uint8_t *__restrict__ ae,
                                               long npix, int vpp, float tau, uint8_t *__restrict__ mask) {
-    const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
-    const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const long p0 = wave * 16 + sub * 4;  // this group's 4 consecutive pixels
-    bool flag[4] = {false, false, false, false};
-    for (int v0 = 0; v0 < vpp; v0 += 16) {
-        const int v = v0 + li;
-        u32x4 x[4], y[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            x[u] = y[u] = u32x4{0, 0, 0, 0};
-            if (p0 + u < npix && v < vpp) {
-                const size_t off = ((size_t)(p0 + u) * vpp + v) * 16;
-                x[u] = *(const u32x4 *)(ao + off);
-                y[u] = *(const u32x4 *)(ae + off);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) flag[u] |= vec_differs<DT>(x[u], y[u], tau);
-    }
-    uint32_t word = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const unsigned long long bal = __ballot(flag[u]);
-        if ((bal >> (sub * 16)) & 0xFFFFull) word |= 1u << (8 * u);
-    }
-    if (li == 0 && p0 < npix) {
-        if (p0 + 3 < npix) {
-            *(uint32_t *)(mask + p0) = word;
-        } else {
-            for (int u = 0; p0 + u < npix; ++u) mask[p0 + u] = (word >> (8 * u)) & 1u;
-        }
-    }
+    diff16<DT>(ao, ae, npix, vpp, tau, mask, (long)blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
 hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix, int vpp, float tau,
@@ -247,46 +189,6 @@ __global__ __launch_bounds__(1024) void k_compact(Geo g, int dil, int32_t *__res
 //      fused with the compaction.
 // All divisions by launch constants use host-computed multipliers.
 // ---------------------------------------------------------------------------
-struct RedCfg {
-    uint32_t m_vpr;  // fast_div_magic(mask_w / 16)
-    uint32_t m_wm;   // fast_div_magic(mask_w)
-    uint32_t m_fy, m_fx, m_nbx;
-};
-
-__device__ __forceinline__ int fdiv31(int x, uint32_t m) { return (int)(((uint64_t)(uint32_t)x * m) >> 31); }
-
-// Any set bit of bit row `br` in columns [c0, c1)?
-__device__ __forceinline__ bool any_bits(const uint32_t *br, int c0, int c1) {
-    if (c0 >= c1) return false;
-    const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5;
-    const uint32_t lo = ~((1u << (c0 & 31)) - 1u);
-    const uint32_t hi = ((c1 - 1) & 31) == 31 ? 0xFFFFFFFFu : ((1u << (((c1 - 1) & 31) + 1)) - 1u);
-    if (w0 == w1) return (br[w0] & lo & hi) != 0u;
-    uint32_t acc = (br[w0] & lo) | (br[w1] & hi);
-    for (int wd = w0 + 1; wd < w1; ++wd) acc |= br[wd];
-    return acc != 0u;
-}
-
-// Compact one round of 1024 candidate blocks [base, base+1024) in ascending
-// order: wave64 ballot, mbcnt rank, wave offsets through LDS.
-__device__ __forceinline__ int compact_round(bool on, int q_out, int running, int *wcnt, int32_t *idx) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const unsigned long long bal = __ballot(on);
-    const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-    if (lane == 0) wcnt[wid] = __popcll(bal);
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        const int c = wcnt[w];
-        off += (w < wid) ? c : 0;
-        tot += c;
-    }
-    if (on) idx[running + off + rank] = q_out;
-    __syncthreads();
-    return running + tot;
-}
-
 __global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__ mask, int hm, int wm, int fy, int fx,
                                                      Geo g, int dil, int vec16, RedCfg rc,
                                                      int32_t *__restrict__ idx, int32_t *__restrict__ count,
@@ -301,122 +203,8 @@ __global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__
     // windows do not touch, the raw and x-dilated block flags
     __shared__ __attribute__((aligned(16))) uint8_t scratch[2 * kReduceMaxBlocks];
     __shared__ int wcnt[16];
-    constexpr int U = 8;
-    const int tid = threadIdx.x;
-    const int H = g.h, W = g.w, WW = (W + 31) >> 5;
-    const int nblk = g.nby * g.nbx;
-    const int bs = g.b * g.s;
-    const bool touching = g.ib >= bs;  // consecutive windows overlap or touch
-    int running = 0;
-    for (int n = 0; n < g.n; ++n) {
-        for (int q = tid; q < H * WW; q += 1024) bits[q] = 0u;
-        __syncthreads();
-        const uint8_t *m = mask + (size_t)n * hm * wm;
-        if (vec16) {
-            const int vpr = wm >> 4, nv = hm * vpr;
-            for (int v0 = tid; v0 < nv; v0 += U * 1024) {
-                u32x4 d[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int v = v0 + u * 1024;
-                    d[u] = v < nv ? *(const u32x4 *)(m + (size_t)v * 16) : u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if ((d[u].x | d[u].y | d[u].z | d[u].w) == 0u) continue;
-                    const int v = v0 + u * 1024;
-                    const int Y = fdiv31(v, rc.m_vpr), q = v - Y * vpr;
-                    const int row = fdiv31(Y, rc.m_fy) * WW;
-                    const int wlo = fdiv31(q * 16, rc.m_fx) >> 5;
-                    uint32_t m0 = 0u, m1 = 0u;
-#pragma unroll
-                    for (int b = 0; b < 16; ++b) {
-                        if ((d[u][b >> 2] >> ((b & 3) * 8)) & 0xFFu) {
-                            const int xp = fx == 1 ? q * 16 + b : fdiv31(q * 16 + b, rc.m_fx);
-                            const uint32_t bit = 1u << (xp & 31);
-                            if ((xp >> 5) == wlo) m0 |= bit;
-                            else m1 |= bit;
-                        }
-                    }
-                    if (m0) atomicOr(&bits[row + wlo], m0);
-                    if (m1) atomicOr(&bits[row + wlo + 1], m1);
-                }
-            }
-        } else {
-            const int nv = hm * wm;
-            for (int v0 = tid; v0 < nv; v0 += U * 1024) {
-                uint8_t d[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) d[u] = (v0 + u * 1024 < nv) ? m[v0 + u * 1024] : 0;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (!d[u]) continue;
-                    const int v = v0 + u * 1024;
-                    const int Y = fdiv31(v, rc.m_wm), X = v - Y * wm;
-                    const int xp = fdiv31(X, rc.m_fx), yp = fdiv31(Y, rc.m_fy);
-                    atomicOr(&bits[yp * WW + (xp >> 5)], 1u << (xp & 31));
-                }
-            }
-        }
-        __syncthreads();
-        if (touching) {
-            // The dilated activity of block (i, j) is "some set bit in the union of
-            // the windows of blocks (i', j'), |i'-i|, |j'-j| <= d", a rectangle when
-            // consecutive windows touch: rows [max(0,(i-d)bs-p), min(H,(i+d)bs-p+ib)),
-            // columns likewise.  First OR each block row's rows into one bit row.
-            uint32_t *rowbits = (uint32_t *)scratch;
-            for (int q = tid; q < g.nby * WW; q += 1024) {
-                const int i = q / WW, wd = q - i * WW;
-                const int r0 = max(0, max(0, i - dil) * bs - g.p);
-                const int r1 = min(H, min(g.nby - 1, i + dil) * bs - g.p + g.ib);
-                uint32_t acc = 0u;
-                for (int r = r0; r < r1; ++r) acc |= bits[r * WW + wd];
-                rowbits[q] = acc;
-            }
-            __syncthreads();
-            for (int base = 0; base < nblk; base += 1024) {
-                const int q = base + tid;
-                bool on = false;
-                if (q < nblk) {
-                    const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
-                    const int c0 = max(0, max(0, j - dil) * bs - g.p);
-                    const int c1 = min(W, min(g.nbx - 1, j + dil) * bs - g.p + g.ib);
-                    on = any_bits(rowbits + i * WW, c0, c1);
-                }
-                running = compact_round(on, n * nblk + q, running, wcnt, idx);
-            }
-        } else {
-            uint8_t *act = scratch, *tmp = scratch + kReduceMaxBlocks;
-            for (int q = tid; q < nblk; q += 1024) {
-                const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
-                const int r0 = max(0, i * bs - g.p), r1 = min(H, i * bs - g.p + g.ib);
-                const int c0 = max(0, j * bs - g.p), c1 = min(W, j * bs - g.p + g.ib);
-                bool hit = false;
-                for (int r = r0; r < r1 && !hit; ++r) hit = any_bits(bits + r * WW, c0, c1);
-                act[q] = hit ? 1 : 0;
-            }
-            __syncthreads();
-            for (int q = tid; q < nblk; q += 1024) {
-                const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
-                uint8_t on = 0;
-                for (int jj = max(0, j - dil); jj <= min(g.nbx - 1, j + dil); ++jj) on |= act[i * g.nbx + jj];
-                tmp[q] = on;
-            }
-            __syncthreads();
-            for (int base = 0; base < nblk; base += 1024) {
-                const int q = base + tid;
-                bool on = false;
-                if (q < nblk) {
-                    const int i = fdiv31(q, rc.m_nbx), j = q - i * g.nbx;
-                    for (int ii = max(0, i - dil); ii <= min(g.nby - 1, i + dil); ++ii)
-                        on |= tmp[ii * g.nbx + j] != 0;
-                }
-                running = compact_round(on, n * nblk + q, running, wcnt, idx);
-            }
-        }
-        __syncthreads();  // scratch and bits are reused by the next image
-    }
-    if (tid == 0) *count = running;
+    const int running = reduce_list<1024>(mask, hm, wm, fy, fx, g, dil, vec16, rc, bits, scratch, wcnt, idx);
+    if (threadIdx.x == 0) *count = running;
 }
 
 hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
