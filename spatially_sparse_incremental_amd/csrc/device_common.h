@@ -194,8 +194,9 @@ __device__ void copy_span(const Geo &g, const CopyCfg &cc, const uint32_t *bm, c
 
 // Unconditional copy of the 16-byte vectors [v0, v1) from src to dst: thread t
 // takes v0 + t, v0 + t + NTHR, ...; CB loads of the next batch are in flight
-// while the current one is stored.
-template <int CB, int NTHR>
+// while the current one is stored.  NTS: non-temporal stores (no dirty L2
+// lines left for the end of the kernel to write back).
+template <int CB, int NTHR, bool NTS = false>
 __device__ void copy_all_span(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, long long v0, long long v1) {
     long long v = v0 + threadIdx.x;
     if (v >= v1) return;
@@ -207,7 +208,12 @@ __device__ void copy_all_span(const uint8_t *__restrict__ src, uint8_t *__restri
     auto drain = [&](const u32x4 (&r)[CB], long long base) {
 #pragma unroll
         for (int i = 0; i < CB; ++i)
-            if (base + (long long)i * NTHR < v1) st16(dst + (base + (long long)i * NTHR) * 16, r[i]);
+            if (base + (long long)i * NTHR < v1) {
+                if (NTS)
+                    __builtin_nontemporal_store(r[i], (u32x4 *)(dst + (base + (long long)i * NTHR) * 16));
+                else
+                    st16(dst + (base + (long long)i * NTHR) * 16, r[i]);
+            }
     };
     constexpr long long step = (long long)CB * NTHR;
     fill(ra, v);

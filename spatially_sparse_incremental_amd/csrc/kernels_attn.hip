@@ -373,8 +373,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(AttnArgs a) {
         for (int q = 0; q < G; ++q) {
             float *wp = a.ws + ((size_t)p * kAttnQT + wave * kAttnQW + 16 * q + ql) * kAttnWsRow;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) *(f32x4 *)(wp + m * 16 + kg * 4) = oT[q][m];
-            if (kg == 0) *(float2 *)(wp + D) = float2{m_run[q], l_run[q]};
+            for (int m = 0; m < 4; ++m) __builtin_nontemporal_store(oT[q][m], (f32x4 *)(wp + m * 16 + kg * 4));
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            if (kg == 0) __builtin_nontemporal_store(f32x2{m_run[q], l_run[q]}, (f32x2 *)(wp + D));
         }
     }
 }

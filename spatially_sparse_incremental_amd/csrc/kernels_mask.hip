@@ -195,7 +195,7 @@ __global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__
                                                      ReduceCopy cp) {
     if (blockIdx.x > 0) {  // the other workgroups copy the cache meanwhile
         const int i = blockIdx.x - 1, nw = gridDim.x - 1;
-        copy_all_span<2, 1024>(cp.src, cp.dst, split_point(cp.nvec, i, nw), split_point(cp.nvec, i + 1, nw));
+        copy_all_span<2, 1024, true>(cp.src, cp.dst, split_point(cp.nvec, i, nw), split_point(cp.nvec, i + 1, nw));
         return;
     }
     __shared__ uint32_t bits[kReduceBitsWords];
