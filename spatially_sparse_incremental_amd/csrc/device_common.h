@@ -153,14 +153,17 @@ __device__ __forceinline__ bool block_listed(const uint32_t *bm, const int32_t *
     return bm ? ((bm[lin >> 5] >> (lin & 31)) & 1u) : listed(idx, cnt, lin);
 }
 
-// Stores of one batch, skipping vectors of listed blocks.
+// Stores of one batch, skipping vectors of listed blocks; non-temporal (the
+// copy is not read again in its kernel, so it leaves no dirty L2 lines for
+// the end of the kernel to write back).
 template <int CB, int NTHR>
 __device__ __forceinline__ void copy_drain(uint8_t *__restrict__ out, long long vb, const u32x4 (&r)[CB],
                                            const int (&lin)[CB], const uint32_t *bm, const int32_t *__restrict__ idx,
                                            int cnt) {
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-        if (lin[i] >= 0 && !block_listed(bm, idx, cnt, lin[i])) st16(out + (vb + (long long)i * NTHR) * 16, r[i]);
+        if (lin[i] >= 0 && !block_listed(bm, idx, cnt, lin[i]))
+            __builtin_nontemporal_store(r[i], (u32x4 *)(out + (vb + (long long)i * NTHR) * 16));
     }
 }
 
