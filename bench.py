@@ -50,6 +50,8 @@ def parse():
                     help="also run one plain device copy of this size (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: the block size and dilation sweep (a line per point, then a table)")
+    ap.add_argument("--attention", action="store_true",
+                    help="instead of the step: only the query-pruned attention comparator (one JSON line)")
     return ap.parse_args()
 
 
@@ -63,6 +65,9 @@ def main():
 
     if args.sweep:
         run_sweep(args)
+        return
+    if args.attention:
+        run_attention(args)
         return
 
     import numpy as np
@@ -445,6 +450,37 @@ def _timers(torch):
     return ev, capture, graph_time
 
 
+def run_attention(args):
+    """Only the query-pruned attention comparator, as one JSON line (for profiler runs)."""
+    import torch
+    import torch.nn.functional as F
+
+    import spatially_sparse_incremental_amd as ssi
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    ev, _, graph_time = _timers(torch)
+
+    def timed_eager(fn, reps):
+        for _ in range(min(10, reps)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        cur = torch.cuda.current_stream()
+        a.record(cur)
+        for _ in range(reps):
+            fn()
+        b.record(cur)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3  # us
+
+    res = _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, args.seed)
+    print(json.dumps({"attention_ldm_64x64x5x64_f16": res}), flush=True)
+
+
 def run_sweep(args):
     """Block size and dilation sweep (one JSON line per point, then a markdown
     table): blocks listed, MAC reduction, reduce and fused-layer times with and
@@ -556,6 +592,9 @@ def _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     return res
 
 
+KERNEL_SOURCES = ("kernels_conv.hip", "device_common.h", "sige_internal.h")
+
+
 def _measured_traffic():
     """HBM bytes per fused-layer launch from the committed counter summary, or None
     when the kernel source has changed since the counters were taken."""
@@ -563,10 +602,13 @@ def _measured_traffic():
 
     here = os.path.dirname(os.path.abspath(__file__))
     summary = os.path.join(here, "profiles", "fused_layer_unet256_pmc_traffic.md")
-    src = os.path.join(here, "spatially_sparse_incremental_amd", "csrc", "kernels_conv.hip")
+    csrc = os.path.join(here, "spatially_sparse_incremental_amd", "csrc")
     try:
         fields = dict(line.split(": ", 1) for line in open(summary).read().splitlines() if ": " in line)
-        current = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for name in KERNEL_SOURCES:  # the conv kernel and the headers it includes
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        current = h.hexdigest()
         if fields.get("kernel_source_sha256", "").strip() == current:
             return int(fields["traffic_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
