@@ -169,6 +169,24 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
                            const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                            int copy_cached, void *stream);
 
+/* The fused layer split over input channels, for weight-bound layers (few
+ * listed blocks, many input channels: the low-resolution latent-diffusion
+ * levels, where the mer.dev notes, 5 "Conclusion & Discussion", find tiles
+ * least effective).  Same arguments and result as sige_sparse_conv_layer up to
+ * the fp32 summation order, in two launches: work items (tile, range of input
+ * channels) fill the GPU's resident slots and leave fp32 partial tiles in
+ * `workspace`; a second kernel adds them in range order with the bias and
+ * writes the listed blocks.  The split is chosen on the device from *count:
+ * when the tiles fill at most half of the slots; otherwise one range per tile.
+ *   workspace: caller-owned device memory of at least
+ *   sige_sparse_conv_layer_split_workspace() bytes, 16-byte aligned, needing no
+ *   initialisation; its contents afterwards are meaningless.  Calls that share
+ *   a workspace must not overlap in time. */
+int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *g, int dtype);
+int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                 const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
+                                 int copy_cached, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Sequential edits (nubint.ai review, "ABSTRACT": results with sequential
  * edits; "Proposed method": the engine keeps its state between edits).  `out`
  * is a persistent buffer that holds the previous edit's result: `cached`

@@ -24,5 +24,7 @@ from ._lib import (  # noqa: F401
     sige_sparse_attention_workspace,
     sige_sparse_conv_layer,
     sige_sparse_conv_layer_restore,
+    sige_sparse_conv_layer_split,
+    sige_sparse_conv_layer_split_workspace,
     weight_to_krsc,
 )

@@ -19,6 +19,7 @@ SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERA
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_reduce_mask_copy",
+           "sige_sparse_conv_layer_split", "sige_sparse_conv_layer_split_workspace",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
            "sige_sparse_attention_workspace", "sige_sparse_attention", "sige_strerror",
@@ -62,6 +63,9 @@ def lib():
         L.sige_conv_blocks.argtypes = [V, V, V, I, P, V, V, V]
         L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
         L.sige_sparse_conv_layer.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
+        L.sige_sparse_conv_layer_split_workspace.argtypes = [P, I]
+        L.sige_sparse_conv_layer_split_workspace.restype = ctypes.c_int64
+        L.sige_sparse_conv_layer_split.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
         L.sige_restore_blocks.argtypes = [V, V, V, V, P, I, V, V, V]
         L.sige_sparse_conv_layer_restore.argtypes = [V, V, V, V, V, V, V, V, I, P, V, V]
         L.sige_sparse_attention_workspace.argtypes = [I] * 6
@@ -235,6 +239,37 @@ def sige_sparse_conv_layer(a_edit, w_krsc, bias, cached, idx, count, g: Geom, ou
                                       _p(idx), _p(count), _dt(a_edit), ctypes.byref(g), _p(out),
                                       int(bool(copy_cached)), _stream(stream))
     _check(rc, "sige_sparse_conv_layer")
+    return out
+
+
+def sige_sparse_conv_layer_split_workspace(g: Geom, dtype) -> int:
+    """Bytes of the workspace of sige_sparse_conv_layer_split for g and a torch dtype."""
+    nbytes = lib().sige_sparse_conv_layer_split_workspace(ctypes.byref(g), DTYPE_CODE[dtype])
+    if nbytes < 0:
+        _check(int(nbytes), "sige_sparse_conv_layer_split_workspace")
+    return int(nbytes)
+
+
+def sige_sparse_conv_layer_split(a_edit, w_krsc, bias, cached, idx, count, g: Geom, out=None, copy_cached=True,
+                                 workspace=None, stream=None):
+    """The fused layer split over input channels (weight-bound layers); the
+    workspace is allocated here when not given."""
+    _dev(a_edit, w_krsc, bias, cached, idx, count, out, workspace)
+    if w_krsc.dtype != a_edit.dtype or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("weights must match the activation dtype; bias must be fp32")
+    d = sige_geom_derive(g)
+    if out is None:
+        if not copy_cached:
+            raise ValueError("copy_cached=False needs a persistent `out`")
+        out = torch.empty((g.n, d.ho, d.wo, g.c_out), dtype=a_edit.dtype, device=a_edit.device)
+    if workspace is None:
+        workspace = torch.empty(sige_sparse_conv_layer_split_workspace(g, a_edit.dtype), dtype=torch.uint8,
+                                device=a_edit.device)
+    rc = lib().sige_sparse_conv_layer_split(_p(a_edit), _p(w_krsc), _p(bias), _p(cached if copy_cached else None),
+                                            _p(idx), _p(count), _dt(a_edit), ctypes.byref(g), _p(out),
+                                            int(bool(copy_cached)), _p(workspace), workspace.numel(),
+                                            _stream(stream))
+    _check(rc, "sige_sparse_conv_layer_split")
     return out
 
 

@@ -232,10 +232,30 @@ struct ConvArgs {
     const uint8_t *cache;
     const int32_t *prev_idx;    // restore mode: the previous edit's list (NULL: none)
     const int32_t *prev_count;
+    float *ws;                  // split mode: fp32 partial tiles (NULL otherwise)
     Geo g;
     ConvCfg c;
     CopyCfg cc;
 };
+
+// Split over input channels (fused layer, weight-bound shapes): with few tiles
+// the grid's resident slots are shared out as (tile, channel range) work items,
+// so the weights stream through many CUs instead of one per tile.  Both the
+// convolution and the combine derive the same split from the list length:
+// S = min(slots / tiles, chunks) when the tiles fill at most half the slots,
+// then evened out so that no range is empty.
+struct Split {
+    int tiles, S, cpk, items;  // tiles, ranges per tile, chunks per range, work items
+};
+__device__ __forceinline__ Split split_of(int cnt, int b2, int bm, int ntn, int nch, int slots) {
+    Split p;
+    p.tiles = (cnt * b2 + bm - 1) / bm * ntn;
+    int S = (p.tiles > 0 && 2 * p.tiles <= slots) ? min(slots / p.tiles, nch) : 1;
+    p.cpk = (nch + S - 1) / S;
+    p.S = (nch + p.cpk - 1) / p.cpk;
+    p.items = p.tiles * p.S;
+    return p;
+}
 
 constexpr int kConvWaves = 8;  // waves per workgroup of the implicit GEMM
 constexpr int kCopyBitmapWords = 1024;  // static LDS bitmap of listed blocks for the copy (32768 blocks)
@@ -270,8 +290,11 @@ struct Smax {
     static constexpr int v = 10 / NT;
 };
 
-template <int DT, int MT, int NT, bool FUSED>
+// SPL (fused only): the split over input channels; each work item leaves the
+// fp32 sum of its channel range in a.ws and k_split_combine finishes the tile.
+template <int DT, int MT, int NT, bool FUSED, bool SPL>
 __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
+    static_assert(FUSED || !SPL, "the split is for the fused layer");
     constexpr int NW = kConvWaves, NTHR = kConvThreads;
     constexpr int ES = elem_bytes(DT);
     constexpr int EPV = 16 / ES;  // elements per 16-byte vector
@@ -317,14 +340,42 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     // Tile t runs on XCD t % 8 (the grid is a multiple of 8), and the N tiles of
     // one M tile share t % 8: t = 8 * (ntn * q + tn) + x holds M tile 8 * q + x,
     // so an M tile's input windows are fetched into one XCD's L2 only.  M tiles
-    // are padded to a multiple of 8; the padding tiles are empty.
-    const int tiles_cap = ((mcap + BM - 1) / BM + 7) / 8 * 8 * ntn;
-    auto tiles_of = [&](int cnt) { return ((cnt * b2 + BM - 1) / BM + 7) / 8 * 8 * ntn; };
+    // are padded to a multiple of 8; the padding tiles are empty.  Layers with
+    // fewer than 8 M tiles at capacity (a few blocks, many output channels) take
+    // the tiles in plain order instead: padding would be most of their tiles.
+    const bool xcd = (mcap + BM - 1) / BM >= 8;
+    auto tiles_of = [&](int cnt) {
+        const int mtn = (cnt * b2 + BM - 1) / BM;
+        return (xcd ? (mtn + 7) / 8 * 8 : mtn) * ntn;
+    };
+    const int tiles_cap = tiles_of(g.cap);
+    // split mode: the list length first (the work items depend on it), then
+    // items (tile, channel range), ranges of one tile adjacent
+    const int nch = (g.cin + c.ck - 1) / c.ck;
+    Split sp{};
+    if (SPL) {
+        sp = split_of(clamp_count(a.count, g.cap), b2, BM, ntn, nch, grid);
+        ntiles = sp.items;
+    }
     for (int t = blockIdx.x;; t += grid) {
         if (ntiles >= 0 && t >= ntiles) break;  // known after the first tile
-        if (t >= tiles_cap) break;
-        const int r8 = t >> 3, tn = r8 % ntn;
-        const int tm = (r8 / ntn) * 8 + (t & 7);
+        if (!SPL && t >= tiles_cap) break;
+        int tn, tm, ks = 0;
+        if (SPL) {
+            const int tile = t / sp.S;
+            ks = t - tile * sp.S;
+            tn = tile % ntn;
+            tm = tile / ntn;
+        } else if (xcd) {
+            const int r8 = t >> 3;
+            tn = r8 % ntn;
+            tm = (r8 / ntn) * 8 + (t & 7);
+        } else {
+            tn = t % ntn;
+            tm = t / ntn;
+        }
+        const int c_first = ks * sp.cpk * c.ck;                                // this item's channels
+        const int c_last = SPL ? min(g.cin, (ks + 1) * sp.cpk * c.ck) : g.cin;  // [c_first, c_last)
         const int m0 = min(tm * BM, mcap - 1);  // padding tiles past capacity read the last slot
         const int n0 = tn * BN;
         const int s_lo = fdiv(m0, c.m_b2);
@@ -345,7 +396,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         const int spec = FUSED ? a.idx[min(tid, g.cap - 1)] : 0;
         const float bv = bsrc[min(n0 + (lane & (BN - 1)), g.cout - 1)];
         u32x4 bfr[SMAX][NT];
-        load_weights<DT, NT, SMAX>(a, bfr, 0, n0, wave, lane, steps, kpc);
+        load_weights<DT, NT, SMAX>(a, bfr, c_first, n0, wave, lane, steps, kpc);
         __builtin_amdgcn_sched_barrier(0);  // every read above is issued before wave 0 waits for the list
         if (wave == 0) {
             if (lane == 0) s_cnt = min(max(cnt_raw, 0), g.cap);
@@ -375,7 +426,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         if (ntiles < 0) ntiles = tiles_of(cnt);
         if (t >= ntiles) break;
         const int mrows = cnt * b2;
-        if (tm * BM >= mrows) continue;  // a padding tile
+        if (!SPL && tm * BM >= mrows) continue;  // a padding tile
         // LDS byte offset of this lane's row in each M subtile (tap (0,0), channel 0)
         int rb[MT];
 #pragma unroll
@@ -397,8 +448,8 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
 
         const int nslot = ns * ib2 * (vpc + 1);  // 16-byte LDS slots of the staged windows
         const int nq = (nslot + 63) / 64;        // 64-slot groups, one wave instruction each
-        for (int c0 = 0; c0 < g.cin; c0 += c.ck) {
-            if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+        for (int c0 = c_first; c0 < c_last; c0 += c.ck) {
+            if (c0 > c_first) __syncthreads();  // every wave is done with the previous chunk
             // Input windows straight from global memory into LDS: each wave fills
             // 64 consecutive 16-byte slots per instruction (lane i -> slot base + i;
             // a pixel occupies vpc slots plus one pad slot, left unwritten).
@@ -451,7 +502,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
                         st16(As + (q * 64 + lane) * 16, u32x4{0u, 0u, 0u, 0u});
                 }
             }
-            if (c0 > 0)  // the next chunk's weight fragments (the first chunk's are in flight)
+            if (c0 > c_first)  // the next chunk's weight fragments (the first chunk's are in flight)
                 load_weights<DT, NT, SMAX>(a, bfr, c0, n0, wave, lane, steps, kpc);
             __builtin_amdgcn_s_waitcnt(0);  // the LDS loads and the weight fragments have landed
             __syncthreads();
@@ -506,10 +557,16 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             float sum[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float x = s_bias[col + j];
+                float x = SPL ? 0.f : s_bias[col + j];
 #pragma unroll
                 for (int w = 0; w < NW; ++w) x += part[(w * BM + row) * PSTR + col + j];
                 sum[j] = x;
+            }
+            if (SPL) {  // this channel range's sum of the tile, for k_split_combine
+                float *wp = a.ws + ((size_t)t * BM + row) * BN + col;
+                __builtin_nontemporal_store(f32x4{sum[0], sum[1], sum[2], sum[3]}, (f32x4 *)wp);
+                __builtin_nontemporal_store(f32x4{sum[4], sum[5], sum[6], sum[7]}, (f32x4 *)(wp + 4));
+                continue;
             }
             const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
             const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
@@ -560,6 +617,48 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     }
 }
 
+// The end of the split: for each tile of the split, the ranges' fp32 sums added
+// in range order, the bias, one rounding, 16-byte stores into the output image
+// (grid-stride over (tile, row, 8 output channels)).  `slots` is the
+// convolution's grid, from which it took the split.
+template <int DT, int MT, int NT>
+__global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
+    constexpr int ES = elem_bytes(DT), BM = 16 * MT, BN = 16 * NT, VPR = BN / 8;
+    const Geo &g = a.g;
+    const ConvCfg &c = a.c;
+    const int b2 = g.b * g.b, ntn = (g.cout + BN - 1) / BN;
+    const int cnt = clamp_count(a.count, g.cap);
+    const Split sp = split_of(cnt, b2, BM, ntn, (g.cin + c.ck - 1) / c.ck, slots);
+    const int mrows = cnt * b2;
+    const long total = (long)sp.tiles * BM * VPR;
+    for (long u = (long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long)gridDim.x * 256) {
+        const int tile = (int)(u / (BM * VPR)), rem = (int)(u - (long)tile * BM * VPR);
+        const int row = rem / VPR, col = (rem - row * VPR) * 8;
+        const int tn = tile % ntn, tm = tile / ntn;
+        const int r = tm * BM + row, co = tn * BN + col;
+        if (r >= mrows || co >= g.cout) continue;
+        const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
+        const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+        int n, by, bx;
+        if (!decode_block(g, a.idx[slot], n, by, bx)) continue;
+        const int y = by * g.b + py, x = bx * g.b + px;
+        if (y >= g.ho || x >= g.wo) continue;
+        float sum[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] = a.bias ? a.bias[min(co + j, g.cout - 1)] : 0.f;
+        for (int ks = 0; ks < sp.S; ++ks) {
+            const float *wp = a.ws + ((size_t)(tile * sp.S + ks) * BM + row) * BN + col;
+            const f32x4 lo = *(const f32x4 *)wp, hi = *(const f32x4 *)(wp + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sum[j] += lo[j];
+                sum[4 + j] += hi[j];
+            }
+        }
+        store_row8<DT>(a.dst + ((((size_t)n * g.ho + y) * g.wo + x) * g.cout + co) * ES, sum, g.cout - co >= 8);
+    }
+}
+
 // Workgroups of `kernel` that fit on one CU with `lds` bytes of dynamic LDS
 // (register and LDS limits), from the runtime; cached per kernel and LDS size.
 template <typename K>
@@ -593,14 +692,56 @@ static unsigned conv_grid(K kernel, const ConvArgs &args) {
 
 template <int DT, int MT, int NT>
 static hipError_t launch_conv_t(int fused, const ConvArgs &args, hipStream_t st) {
-    if (fused) {
-        auto k = k_conv<DT, MT, NT, true>;
+    if (fused && args.ws) {  // the split over input channels, then the combine
+        auto k = k_conv<DT, MT, NT, true, true>;
+        const int slots = args.c.cus * resident_per_cu(k, args.c.lds_bytes);
+        hipLaunchKernelGGL(k, dim3(slots), dim3(kConvThreads), args.c.lds_bytes, st, args);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        constexpr int BM = 16 * MT, BN = 16 * NT;
+        const long work = (long)(args.g.cap * args.g.b * args.g.b + BM - 1) / BM *
+                          ((args.g.cout + BN - 1) / BN) * BM * (BN / 8);  // tiles at capacity
+        const long grid = (work + 255) / 256 < 4L * args.c.cus ? (work + 255) / 256 : 4L * args.c.cus;
+        auto kc = k_split_combine<DT, MT, NT>;
+        hipLaunchKernelGGL(kc, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, st, args, slots);
+    } else if (fused) {
+        auto k = k_conv<DT, MT, NT, true, false>;
         hipLaunchKernelGGL(k, dim3(conv_grid(k, args)), dim3(kConvThreads), args.c.lds_bytes, st, args);
     } else {
-        auto k = k_conv<DT, MT, NT, false>;
+        auto k = k_conv<DT, MT, NT, false, false>;
         hipLaunchKernelGGL(k, dim3(conv_grid(k, args)), dim3(kConvThreads), args.c.lds_bytes, st, args);
     }
     return hipGetLastError();
+}
+
+// Work items the split's workspace must hold: every resident slot (a split),
+// or every tile at capacity (no split).
+template <int DT, int MT, int NT>
+static long split_items_t(const Geo &g, const ConvCfg &c) {
+    constexpr int BM = 16 * MT, BN = 16 * NT;
+    const long slots = (long)c.cus * resident_per_cu(k_conv<DT, MT, NT, true, true>, c.lds_bytes);
+    const long tiles = ((long)g.cap * g.b * g.b + BM - 1) / BM * ((g.cout + BN - 1) / BN);
+    return slots > tiles ? slots : tiles;
+}
+
+long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c) {
+    const int key = c.mt * 10 + c.nt;
+    long items = 0;
+#define SIGE_SPLIT_ITEMS(D)                                         \
+    switch (key) {                                                  \
+    case 42: items = split_items_t<D, 4, 2>(g, c); break;           \
+    case 41: items = split_items_t<D, 4, 1>(g, c); break;           \
+    case 22: items = split_items_t<D, 2, 2>(g, c); break;           \
+    case 44: items = split_items_t<D, 4, 4>(g, c); break;           \
+    default: return -1;                                             \
+    }
+    switch (dt) {
+    case 0: SIGE_SPLIT_ITEMS(0) break;
+    case 1: SIGE_SPLIT_ITEMS(1) break;
+    default: SIGE_SPLIT_ITEMS(2) break;
+    }
+#undef SIGE_SPLIT_ITEMS
+    return items * (16L * c.mt) * (16L * c.nt) * 4;
 }
 
 template <int DT>
@@ -618,9 +759,9 @@ static hipError_t launch_conv_dt(int fused, const ConvArgs &args, hipStream_t st
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                        const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
-                       hipStream_t st) {
+                       hipStream_t st, float *ws) {
     ConvArgs args{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
-                  (const uint8_t *)cache, prev_idx, prev_count, g, cfg, cc};
+                  (const uint8_t *)cache, prev_idx, prev_count, ws, g, cfg, cc};
     switch (dt) {
     case 0: return launch_conv_dt<0>(fused, args, st);
     case 1: return launch_conv_dt<1>(fused, args, st);

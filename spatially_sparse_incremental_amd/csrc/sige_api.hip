@@ -466,6 +466,56 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
                   "sige_sparse_conv_layer", (hipStream_t)stream);
 }
 
+int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *gp, int dtype) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    ConvCfg cfg;
+    if ((rc = choose_conv(g, dtype, 1, 1, &cfg))) return rc;
+    const long bytes = sige::split_workspace_bytes(dtype, g, cfg);
+    if (bytes < 0) return fail(SIGE_EINVAL, "unknown tile shape");
+    g_msg[0] = 0;
+    return (int64_t)bytes;
+}
+
+int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                 const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                                 int copy_cached, void *workspace, int64_t workspace_bytes, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!a_edit || !w_krsc || !idx || !count || !out || !workspace || (copy_cached && !cached))
+        return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+        (copy_cached && !aligned(cached, 16)))
+        return fail(SIGE_EALIGN, "tensors and workspace must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
+    const size_t ibytes = (size_t)g.n * g.h * g.w * g.cin * es;
+    if (overlap(out, obytes, a_edit, ibytes)) return fail(SIGE_EINVAL, "out overlaps a_edit");
+    if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    ConvCfg cfg;
+    if ((rc = choose_conv(g, dtype, 1, 1, &cfg))) return rc;  // the full resident grid
+    if ((rc = device_ready())) return rc;
+    const long need = sige::split_workspace_bytes(dtype, g, cfg);
+    if (need < 0) return fail(SIGE_EINVAL, "unknown tile shape");
+    if (workspace_bytes < need)
+        return fail(SIGE_ERANGE, "workspace of %lld bytes, %ld needed", (long long)workspace_bytes, need);
+    if (overlap(workspace, (size_t)need, out, obytes) || overlap(workspace, (size_t)need, a_edit, ibytes) ||
+        overlap(workspace, (size_t)need, idx, (size_t)g.cap * 4) || overlap(workspace, (size_t)need, count, 4) ||
+        (copy_cached && overlap(workspace, (size_t)need, cached, obytes)))
+        return fail(SIGE_EINVAL, "the workspace overlaps another argument");
+    const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
+    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
+                                    nullptr, nullptr, g, cfg, cc, (hipStream_t)stream, (float *)workspace),
+                  "sige_sparse_conv_layer_split", (hipStream_t)stream);
+}
+
 int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                                    const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
                                    const int32_t *count, int dtype, const sige_geom *gp, void *out, void *stream) {

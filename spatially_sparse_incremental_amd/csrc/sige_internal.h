@@ -65,10 +65,13 @@ hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t
                          void *blocks, hipStream_t st);
 // fused = 0: src = stacked blocks, dst = output blocks.  fused = 1: src = a_edit, dst = out;
 // with prev_idx (fused only), the previous list's blocks not in idx are restored from cache.
+// ws (fused only): the fp32 workspace of the split over input channels (NULL: no split).
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                        const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
-                       hipStream_t st);
+                       hipStream_t st, float *ws = nullptr);
+// Bytes of that workspace for g and the launch configuration c (< 0: unknown tile shape).
+long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c);
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
                           const int32_t *count, const Geo &g, const CopyCfg &cc, const void *cached, void *out,
                           int grid, hipStream_t st);

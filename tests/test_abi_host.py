@@ -141,6 +141,23 @@ def test_reduce_copy_validation(lib):
     assert f(_v(A), 255, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, _v(D), far, s) == EINVAL  # not a multiple
 
 
+def test_split_layer_validation(lib):
+    s = _v(0)
+    g = _g(h=16, w=16, ci=1280, co=1280, b=2)
+    f = lib.sige_sparse_conv_layer_split
+    far = _v(E + (1 << 35))
+    ws = 0x7F9000000000
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), far, 1, None, 1 << 30, s) == EINVAL
+    assert f(_v(A), _v(B), None, None, _v(D), _v(E), 2, ctypes.byref(g), far, 1, _v(ws), 1 << 30, s) == EINVAL
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 7, ctypes.byref(g), far, 1, _v(ws), 1 << 30, s) == EDTYPE
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), far, 1, _v(ws + 8), 1 << 30, s) == EALIGN
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), _v(A + 64), 1, _v(ws), 1 << 30,
+             s) == EINVAL  # out overlaps a_edit
+    assert lib.sige_sparse_conv_layer_split_workspace(ctypes.byref(g), 2) > 0
+    assert lib.sige_sparse_conv_layer_split_workspace(ctypes.byref(g), 9) == EDTYPE
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), far, 1, _v(ws), 1 << 30, s) == ENODEV
+
+
 def test_restore_validation(lib):
     s = _v(0)
     g = _g()
