@@ -484,7 +484,8 @@ def run_attention(args):
 def run_sweep(args):
     """Block size and dilation sweep (one JSON line per point, then a markdown
     table): blocks listed, MAC reduction, reduce and fused-layer times with and
-    without the cache copy, and the dense conv (torch/MIOpen) of the layer."""
+    without the cache copy, the same for the layer split over input channels,
+    and the dense conv (torch/MIOpen) of the layer."""
     import torch
     import torch.nn.functional as F
 
@@ -516,6 +517,12 @@ def run_sweep(args):
         t_copy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out))
         t_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, None, idx, cnt, g, out=persist,
                                                                  copy_cached=False))
+        ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8, device=dev)
+        t_split_copy = graph_time(lambda: ssi.sige_sparse_conv_layer_split(a_e, wk, bias, cache, idx, cnt, g, out=out,
+                                                                           workspace=ws))
+        t_split_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer_split(a_e, wk, bias, None, idx, cnt, g,
+                                                                             out=persist, copy_cached=False,
+                                                                             workspace=ws))
         key = (wname, L.h, L.c_in)
         if key not in dense_t:
             x_cl = a_e.permute(0, 3, 1, 2)
@@ -537,12 +544,13 @@ def run_sweep(args):
                "edit_fraction": round(float(m.mean()), 5),
                "mac_reduction": round(d.ho * d.wo / act_pix, 2) if act_pix else None,
                "reduce_us": round(t_red, 3), "fused_copy_us": round(t_copy, 3),
-               "fused_nocopy_us": round(t_nocopy, 3), "dense_miopen_us": round(dense_t[key], 3),
-               "speedup_nocopy_vs_dense": round(dense_t[key] / t_nocopy, 2)}
+               "fused_nocopy_us": round(t_nocopy, 3), "split_copy_us": round(t_split_copy, 3),
+               "split_nocopy_us": round(t_split_nocopy, 3), "dense_miopen_us": round(dense_t[key], 3),
+               "speedup_nocopy_vs_dense": round(dense_t[key] / min(t_nocopy, t_split_nocopy), 2)}
         rows.append(row)
         print(json.dumps(row), flush=True)
     cols = ["layer", "block", "dilate", "blocks", "capacity", "mac_reduction", "reduce_us", "fused_copy_us",
-            "fused_nocopy_us", "dense_miopen_us", "speedup_nocopy_vs_dense"]
+            "fused_nocopy_us", "split_copy_us", "split_nocopy_us", "dense_miopen_us", "speedup_nocopy_vs_dense"]
     print("| " + " | ".join(cols) + " |")
     print("|" + "---|" * len(cols))
     for r in rows:
