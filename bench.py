@@ -307,6 +307,7 @@ def main():
         t_bbox_tiles = graph_time(step_bbox_tiles, 5, 40)
 
         attention = _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed)
+        ldm_split = _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -402,6 +403,7 @@ def main():
             "bbox_blocks": bbox_blocks,
             "bbox_mac_reduction": round(dense_flops / bbox_flops, 2),
             "attention_ldm_64x64x5x64_f16": attention,
+            "ldm_16x16x1280_f16_split": ldm_split,
             "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
         },
         "latency": {
@@ -597,6 +599,39 @@ def _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
         res["dense_tflops"] = round(4.0 * h * w * heads * d * h * w / (t_dense * 1e-6) / 1e12, 2)
     except Exception as exc:  # noqa: BLE001 - report, do not hide
         print(f"[bench] dense attention failed: {exc}", file=sys.stderr)
+    return res
+
+
+def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
+    """The latent-diffusion 16x16x1280 fp16 3x3 layer (b = 2, dilation 1) with the
+    blob edit: the single-range fused layer, the layer split over input channels
+    and the dense conv (torch/MIOpen), each with the cache copy."""
+    dev = torch.device("cuda:0")
+    wl = synth.workload("cfg5_ldm_f16")
+    L = [x for x in wl.layers if x.name == "l16_3x3"][0]
+    a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
+    a_e = synth.make_edit(a_o, synth.edit_shape(wl, seed).raster(L.h, L.w), wl.edit_kind, seed).to(dev)
+    a_o = a_o.to(dev)
+    w_cpu, b_cpu = synth.make_layer_tensors(L, seed)
+    wk, bias = ssi.weight_to_krsc(w_cpu).to(dev), b_cpu.to(dev)
+    cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + 50).to(dev)
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    idx, cnt = ssi.sige_reduce_mask(ssi.sige_diff_mask(a_o, a_e, wl.tau), g, L.dilate)
+    out = torch.empty_like(cache)
+    ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8, device=dev)
+    t_plain = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out))
+    t_split = graph_time(lambda: ssi.sige_sparse_conv_layer_split(a_e, wk, bias, cache, idx, cnt, g, out=out,
+                                                                  workspace=ws))
+    res = {"blocks": int(cnt.item()), "single_range_us": round(t_plain, 3), "split_us": round(t_split, 3)}
+    try:
+        x_cl = a_e.permute(0, 3, 1, 2)
+        w_cl = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
+        with torch.no_grad():
+            t_dense = timed_eager(lambda: F.conv2d(x_cl, w_cl, bias.to(a_e.dtype), padding=L.pad), 50)
+        res["dense_miopen_us"] = round(t_dense, 3)
+        res["speedup_split_vs_dense"] = round(t_dense / t_split, 2)
+    except Exception as exc:  # noqa: BLE001 - report, do not hide
+        print(f"[bench] dense 16x16x1280 conv failed: {exc}", file=sys.stderr)
     return res
 
 
