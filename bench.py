@@ -158,6 +158,40 @@ def main():
     torch.cuda.synchronize()
     t_single = e0.elapsed_time(e1) / K * 1e3
 
+    # spread: each replay of the 10-step graph timed alone (per-step mean of each)
+    spread = []
+    for _ in range(60):
+        a, b = ev(), ev()
+        a.record(cur)
+        gsteps.replay()
+        b.record(cur)
+        b.synchronize()
+        spread.append(a.elapsed_time(b) / S * 1e3)
+    # cold: the 256 MB MALL (and the L2s) evicted by writing 512 MiB before every
+    # step (outside the events); one step per replay, events around it
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(40):
+        evict.fill_(i & 0xFF)
+        a, b = ev(), ev()
+        a.record(cur)
+        gstep.replay()
+        b.record(cur)
+        b.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    del evict
+
+    def pct(v, q):
+        v = sorted(v)
+        return round(v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))], 3)
+
+    distribution = {"warm_per_step_us": {"p10": pct(spread, 0.1), "p50": pct(spread, 0.5), "p90": pct(spread, 0.9),
+                                         "replays": len(spread), "note": "each replay of a 10-step graph"},
+                    "cold_step_us": {"p10": pct(cold, 0.1), "p50": pct(cold, 0.5), "p90": pct(cold, 0.9),
+                                     "runs": len(cold),
+                                     "note": "512 MiB written before each step to evict the MALL; one step "
+                                             "per graph replay, HIP events around it (includes the graph launch)"}}
+
     # the same step launched eagerly from Python
     t_eager = None
     e0, e1 = ev(), ev()
@@ -180,7 +214,8 @@ def main():
 
     t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_copy = t_dense_ours = t_dense_miopen = None
     t_reduce = t_step_conv_copy = None
-    t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = attention = None
+    t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = attention = ldm_split = t_layer = None
+    chain = gaugan = None
     bbox_flops = bbox_blocks = rect = None
     if not args.no_comparators:
         # the step with the copy inside the conv launch instead of the reduce launch
@@ -192,6 +227,12 @@ def main():
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g, out=out_c, copy_cached=True)
 
         t_step_conv_copy = graph_time(step_conv_copy, 5, 40)
+
+        def layer_only():  # the per-layer part of the step: reduce (with the copy) and the fused layer
+            ssi.sige_reduce_mask_copy(mask, g, L.dilate, cache, out=out, idx=idx, count=count)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False)
+
+        t_layer = graph_time(layer_only, 5, 40)
         t_reduce = graph_time(lambda: ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count))
         t_fused_copy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g,
                                                                      out=out_c, copy_cached=True))
@@ -308,6 +349,14 @@ def main():
 
         attention = _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed)
         ldm_split = _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed)
+        try:
+            chain = _chain_comparator(torch, F, ssi, synth, graph_time, seed)
+        except Exception as exc:  # noqa: BLE001 - report, do not hide
+            print(f"[bench] chain comparator failed: {exc}", file=sys.stderr)
+        try:
+            gaugan = _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed)
+        except Exception as exc:  # noqa: BLE001 - report, do not hide
+            print(f"[bench] GauGAN comparator failed: {exc}", file=sys.stderr)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -384,6 +433,7 @@ def main():
                    "active_blocks": active, "block_capacity": cap},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "distribution": distribution,
         "kernels": kernels,
         "comparators": None if args.no_comparators else {
             "dense_conv_miopen_us": None if t_dense_miopen is None else round(t_dense_miopen, 3),
@@ -404,6 +454,10 @@ def main():
             "bbox_mac_reduction": round(dense_flops / bbox_flops, 2),
             "attention_ldm_64x64x5x64_f16": attention,
             "ldm_16x16x1280_f16_split": ldm_split,
+            "layer_reduce_and_fused_us": round(t_layer, 3),
+            "speedup_layer_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_layer, 3),
+            "chain_unet_12conv_bf16": chain,
+            "gaugan_convs_bf16": gaugan,
             "speedup_no_copy_vs_dense_miopen": None if t_dense_miopen is None else round(t_dense_miopen / t_nocopy, 3),
         },
         "latency": {
@@ -635,6 +689,104 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     return res
 
 
+def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
+    """The 12-conv U-Net chain (cfg3) at the 1.2% blob edit, as HIP graphs: one
+    diff at 256x256, then per layer the reduce (the mask pooled to the layer's
+    input) and the fused layer with the cache copy, layer l+1 reading layer l's
+    output; against the same 12 convs dense through torch/MIOpen."""
+    dev = torch.device("cuda:0")
+    wl = synth.workload("cfg3_chain_bf16")
+    first = wl.layers[0]
+    m = synth.edit_shape(wl, seed).raster(first.h, first.w)
+    a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed).to(dev)
+    a_e = synth.make_edit(a_o.cpu(), m, wl.edit_kind, seed).to(dev)
+    mask = torch.empty((1, first.h, first.w), dtype=torch.uint8, device=dev)
+    layers = []
+    x_dense = [a_e.permute(0, 3, 1, 2)]
+    for li, L in enumerate(wl.layers):
+        w_cpu, b_cpu = synth.make_layer_tensors(L, seed * 100 + li)
+        g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+        d = ssi.sige_geom_derive(g)
+        cache = synth.make_activation(1, d.ho, d.wo, L.c_out, L.dtype, seed * 100 + li + 50).to(dev)
+        layers.append(dict(L=L, g=g, wk=ssi.weight_to_krsc(w_cpu).to(dev), bias=b_cpu.to(dev), cache=cache,
+                           out=torch.empty_like(cache), idx=torch.empty((d.cap,), dtype=torch.int32, device=dev),
+                           cnt=torch.empty((1,), dtype=torch.int32, device=dev),
+                           w_cl=w_cpu.to(dev).contiguous(memory_format=torch.channels_last),
+                           b16=b_cpu.to(dev).to(a_e.dtype)))
+    blocks = []
+
+    def sparse_chain():
+        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+        x = a_e
+        for ly in layers:
+            ssi.sige_reduce_mask(mask, ly["g"], ly["L"].dilate, idx=ly["idx"], count=ly["cnt"])
+            ssi.sige_sparse_conv_layer(x, ly["wk"], ly["bias"], ly["cache"], ly["idx"], ly["cnt"], ly["g"],
+                                       out=ly["out"])
+            x = ly["out"]
+
+    def dense_chain():
+        x = x_dense[0]
+        for ly in layers:
+            x = F.conv2d(x, ly["w_cl"], ly["b16"], stride=ly["L"].stride, padding=ly["L"].pad)
+
+    sparse_chain()
+    torch.cuda.synchronize()
+    blocks = [int(ly["cnt"].item()) for ly in layers]
+    t_sparse = graph_time(sparse_chain, 2, 25)
+    with torch.no_grad():
+        t_dense = graph_time(dense_chain, 1, 10)
+    return {"sparse_us": round(t_sparse, 3), "dense_miopen_us": round(t_dense, 3),
+            "speedup": round(t_dense / t_sparse, 2), "blocks_per_layer": blocks,
+            "note": "one diff + 12 x (reduce + fused layer with the cache copy); dense: 12 x F.conv2d; HIP graphs"}
+
+
+def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
+    """The four GauGAN-shaped bf16 convs (cfg4) under the seeded star polygon at
+    0.5 / 1.2 / 5 / 15 / 30% of the frame: reduce + the faster of the fused
+    layer and its split (both with the cache copy) per layer, against the dense
+    conv through torch/MIOpen."""
+    dev = torch.device("cuda:0")
+    wl = synth.workload("cfg4_gaugan_bf16")
+    res, dense = {}, {}
+    prep = []
+    for li, L in enumerate(wl.layers):
+        w_cpu, b_cpu = synth.make_layer_tensors(L, seed + li)
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li).to(dev)
+        g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+        cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50).to(dev)
+        prep.append((L, g, a_o, ssi.weight_to_krsc(w_cpu).to(dev), b_cpu.to(dev), cache,
+                     w_cpu.to(dev).contiguous(memory_format=torch.channels_last)))
+        with torch.no_grad():
+            x = a_o.permute(0, 3, 1, 2)
+            dense[L.name] = round(timed_eager(lambda: F.conv2d(x, prep[-1][6], prep[-1][4].to(a_o.dtype),
+                                                               padding=L.pad), 20), 3)
+    for area in (0.005, 0.012, 0.05, 0.15, 0.30):
+        shape = synth.edit_shape(wl, seed, area)
+        row = {}
+        for li, (L, g, a_o, wk, bias, cache, _) in enumerate(prep):
+            a_e = synth.make_edit(a_o.cpu(), shape.raster(L.h, L.w), wl.edit_kind, seed + li).to(dev)
+            mask = ssi.sige_diff_mask(a_o, a_e, wl.tau)
+            idx, cnt = ssi.sige_reduce_mask(mask, g, L.dilate)
+            out = torch.empty_like(cache)
+            ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def one():
+                ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=cnt)
+                ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out)
+
+            def split():
+                ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=cnt)
+                ssi.sige_sparse_conv_layer_split(a_e, wk, bias, cache, idx, cnt, g, out=out, workspace=ws)
+
+            t1, t2 = graph_time(one, 5, 20), graph_time(split, 5, 20)
+            row[L.name] = {"blocks": int(cnt.item()), "sparse_us": round(min(t1, t2), 3),
+                           "path": "split" if t2 < t1 else "single", "dense_miopen_us": dense[L.name],
+                           "speedup": round(dense[L.name] / min(t1, t2), 2)}
+        res[f"area_{area:g}"] = row
+    return res
+
+
 KERNEL_SOURCES = ("kernels_conv.hip", "device_common.h", "sige_internal.h")
 
 
@@ -687,10 +839,32 @@ def _cpu_baseline(a_o, a_e, w, bias, cache, L, tau, seconds):
         times.append(time.perf_counter() - t0)
     times.sort()
     med = times[len(times) // 2]
-    return {"value": round(med * 1e6, 1), "unit": "us per incremental layer update", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    # one thread, and the dense CPU conv of the same layer (every block), each timed once
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        once()
+        single = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    t0 = time.perf_counter()
+    oracle.dense_conv(a_e, w, bias, L.k, L.stride, L.pad)
+    dense = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(med * 1e6, 1), "unit": "us per incremental layer update", "cores": threads,
             "kind": "oracle",
             "sample": f"the full workload (diff + reduce + edited layer incl. cache copy), median of {len(times)} "
-                      f"runs, {len(os.sched_getaffinity(0))} host CPUs visible"}
+                      f"runs, {len(os.sched_getaffinity(0))} host CPUs visible",
+            "single_thread_us": round(single * 1e6, 1), "dense_conv_us": round(dense * 1e6, 1),
+            "cpu_model": model}
 
 
 if __name__ == "__main__":
