@@ -175,3 +175,23 @@ def test_split_graph_replays_match_eager():
         step()
         torch.cuda.synchronize()
         assert torch.equal(bits(got), bits(out)), rep
+
+
+@pytest.mark.parametrize("area", [0.005, 0.012, 0.05])
+def test_split_gaugan_layers(area):
+    # the four GauGAN-shaped bf16 convs (18.9 MB of weights at 32x64x1024): list and
+    # untouched pixels bit for bit, sampled blocks against the oracle
+    wl = synth.workload("cfg4_gaugan_bf16")
+    seed = 6
+    shape = synth.edit_shape(wl, seed, area)
+    for li, L in enumerate(wl.layers):
+        m = shape.raster(L.h, L.w)
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li)
+        a_e = synth.make_edit(a_o, m, wl.edit_kind, seed + li)
+        wt, bias = synth.make_layer_tensors(L, seed + li)
+        cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
+        mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+        out, idx = _split_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
+        print(f"\n[case] gaugan split {L.name} area {area}: {idx.numel()} blocks", flush=True)
+        check_layer_sampled(f"gaugan split {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L,
+                            mask.cpu(), li)
