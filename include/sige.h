@@ -169,19 +169,23 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
                            const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                            int copy_cached, void *stream);
 
-/* The fused layer split over input channels, for weight-bound layers (few
- * listed blocks, many input channels: the low-resolution latent-diffusion
- * levels, where the mer.dev notes, 5 "Conclusion & Discussion", find tiles
- * least effective).  Same arguments and result as sige_sparse_conv_layer up to
- * the fp32 summation order, in two launches: work items (tile, range of input
- * channels) fill the GPU's resident slots and leave fp32 partial tiles in
- * `workspace`; a second kernel adds them in range order with the bias and
- * writes the listed blocks.  The split is chosen on the device from *count:
- * when the tiles fill at most half of the slots; otherwise one range per tile.
+/* The fused layer split over input channels, for weight-bound layers (many
+ * input channels: the low-resolution latent-diffusion levels, where the
+ * mer.dev notes, 5 "Conclusion & Discussion", find tiles least effective, and
+ * the GauGAN-sized convolutions).  Same arguments and result as
+ * sige_sparse_conv_layer up to the fp32 summation order, in two launches: a
+ * work item (group of output-row tiles, one chunk of input channels, one tile
+ * of output channels) reads its weights once and walks its row tiles, leaving
+ * one fp32 partial tile per (row tile, channel tile, chunk) in `workspace`;
+ * the second kernel adds a tile's chunks in chunk order with the bias, writes
+ * the listed blocks and, with copy_cached, copies the cache elsewhere.  The
+ * row groups are chosen on the device from *count, as many as fill the GPU's
+ * resident slots.
  *   workspace: caller-owned device memory of at least
- *   sige_sparse_conv_layer_split_workspace() bytes, 16-byte aligned, needing no
- *   initialisation; its contents afterwards are meaningless.  Calls that share
- *   a workspace must not overlap in time. */
+ *   sige_sparse_conv_layer_split_workspace() bytes (a partial tile per row
+ *   tile, channel tile and chunk at full capacity), 16-byte aligned, needing
+ *   no initialisation; its contents afterwards are meaningless.  Calls that
+ *   share a workspace must not overlap in time. */
 int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *g, int dtype);
 int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                                  const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,

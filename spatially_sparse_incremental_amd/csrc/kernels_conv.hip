@@ -238,22 +238,52 @@ struct ConvArgs {
     CopyCfg cc;
 };
 
-// Split over input channels (fused layer, weight-bound shapes): with few tiles
-// the grid's resident slots are shared out as (tile, channel range) work items,
-// so the weights stream through many CUs instead of one per tile.  Both the
-// convolution and the combine derive the same split from the list length:
-// S = min(slots / tiles, chunks) when the tiles fill at most half the slots,
-// then evened out so that no range is empty.
-struct Split {
-    int tiles, S, cpk, items;  // tiles, ranges per tile, chunks per range, work items
+// Split over input channels (the fused layer with a workspace): a work item
+// is (group of R consecutive M tiles, range of cpk chunks of input channels,
+// N tile).  For each chunk of its range it reads its weight fragments once and
+// walks every M tile of the group, so the weights cross the chip once per
+// group instead of once per M tile, and the chunks spread one layer's weights
+// over many CUs.  Each (M tile, N tile, chunk) leaves an fp32 partial tile;
+// the combine adds a tile's chunks in order.  When N tiles x chunks fit in the
+// resident slots, a range is one chunk and the groups take the rest of the
+// slots (G = slots / (N tiles x chunks), at most one per M tile, evened out);
+// otherwise there is one group and as many ranges as the slots allow.  A
+// group of one M tile with several chunks per range (acc_range) keeps its
+// accumulators over the range and leaves one partial tile per range, at the
+// range's first chunk.  Both kernels derive the same plan from the list
+// length.  Window group = (group,
+// range): the items that stage the same windows.  With at least 8 window
+// groups (and no extra round of positions from the padding), position
+// p = 8 * (tn + ntn * (wg / 8)) + wg % 8 puts every N tile of window group wg
+// on XCD wg % 8, so those windows are fetched into one L2.
+struct StreamPlan {
+    int mtn, ntn, nch;  // M tiles, N tiles, chunks
+    int R, G;           // M tiles per group, groups
+    int cpk, S;         // chunks per range, ranges
+    int nwg;            // window groups (G * S)
+    bool acc_range;     // one partial tile per range (R == 1, cpk > 1)
+    bool xcd;
+    int positions;      // work positions, padding included
 };
-__device__ __forceinline__ Split split_of(int cnt, int b2, int bm, int ntn, int nch, int slots) {
-    Split p;
-    p.tiles = (cnt * b2 + bm - 1) / bm * ntn;
-    int S = (p.tiles > 0 && 2 * p.tiles <= slots) ? min(slots / p.tiles, nch) : 1;
+__device__ __forceinline__ StreamPlan stream_plan(int cnt, int b2, int bm, int ntn, int nch, int slots) {
+    StreamPlan p;
+    p.mtn = (cnt * b2 + bm - 1) / bm;
+    p.ntn = ntn;
+    p.nch = nch;
+    int G = 1, S = nch;
+    if (ntn * nch <= slots)
+        G = min(slots / max(ntn * nch, 1), max(p.mtn, 1));
+    else
+        S = max(1, min(nch, slots / max(ntn, 1)));
     p.cpk = (nch + S - 1) / S;
-    p.S = (nch + p.cpk - 1) / p.cpk;
-    p.items = p.tiles * p.S;
+    p.S = (nch + p.cpk - 1) / p.cpk;  // evened: no empty range
+    p.R = max(1, (p.mtn + G - 1) / G);
+    p.G = (p.mtn + p.R - 1) / p.R;  // 0 for an empty list
+    p.nwg = p.G * p.S;
+    p.acc_range = p.R == 1 && p.cpk > 1;
+    const int padded = (p.nwg + 7) / 8 * 8 * ntn;
+    p.xcd = p.nwg >= 8 && (p.nwg % 8 == 0 || padded <= slots);
+    p.positions = p.xcd ? padded : p.nwg * ntn;
     return p;
 }
 
@@ -290,11 +320,143 @@ struct Smax {
     static constexpr int v = 10 / NT;
 };
 
-// SPL (fused only): the split over input channels; each work item leaves the
-// fp32 sum of its channel range in a.ws and k_split_combine finishes the tile.
-template <int DT, int MT, int NT, bool FUSED, bool SPL>
+// Stage the input windows of one M tile's block slots for the channels
+// [c0, c0 + ck) into LDS at As, straight from global memory
+// (global_load_lds_dwordx4: no registers, every load in flight at once).  Each
+// wave fills 64 consecutive 16-byte slots per instruction (lane i -> slot base
+// + i; a pixel occupies vpc slots plus one pad slot, left unwritten).  Slots
+// outside the image or beyond c_in get zeros from their own lane.  Batches of
+// QB slot groups per wave: decode, then every slot-table read of the batch,
+// then every load.  t_n, t_iy, t_ix: image and window origin per block slot
+// (fused); the stacked block tensor starts at slot s_lo otherwise.
+template <int DT, bool FUSED>
+__device__ __forceinline__ void stage_windows(const ConvArgs &a, uint8_t *As, const int *t_n, const int *t_iy,
+                                              const int *t_ix, int c0, int nslot, int s_lo, int wave, int lane) {
+    constexpr int NW = kConvWaves, ES = elem_bytes(DT), EPV = 16 / ES, QB = 4;
+    const Geo &g = a.g;
+    const ConvCfg &c = a.c;
+    const int vpc = c.ck / EPV, ib2 = g.ib * g.ib;
+    const int nq = (nslot + 63) / 64;  // 64-slot groups, one wave instruction each
+    for (int qb = wave; qb < nq; qb += NW * QB) {
+        int ls[QB], pix[QB], chv[QB];
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+            const int slot = (qb + NW * i) * 64 + lane;
+            const int P = fdiv(slot, c.m_vpc1), cvv = slot - P * (vpc + 1);
+            const bool act = slot < nslot && cvv < vpc;
+            const int l = FUSED ? fdiv(P, c.m_ib2) : 0;
+            ls[i] = act ? l : -1;
+            pix[i] = FUSED ? P - l * ib2 : P;
+            chv[i] = c0 + cvv * EPV;
+        }
+        int tn_[QB], ty[QB], tx[QB];
+        if (FUSED) {
+#pragma unroll
+            for (int i = 0; i < QB; ++i) {
+                const int l = max(ls[i], 0);
+                tn_[i] = t_n[l];
+                ty[i] = t_iy[l];
+                tx[i] = t_ix[l];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+            if (ls[i] < 0) continue;
+            const int q = qb + NW * i;
+            const uint8_t *src = nullptr;
+            if (chv[i] < g.cin) {
+                if (FUSED) {
+                    const int yy = fdiv(pix[i], c.m_ib), xx = pix[i] - yy * g.ib;
+                    const int iy = ty[i] + yy, ix = tx[i] + xx;
+                    if (tn_[i] >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w)
+                        src = a.src + ((((size_t)tn_[i] * g.h + iy) * g.w + ix) * g.cin + chv[i]) * ES;
+                } else {
+                    src = a.src + (((size_t)s_lo * ib2 + pix[i]) * g.cin + chv[i]) * ES;
+                }
+            }
+            if (src)
+                __builtin_amdgcn_global_load_lds((const void *)src,
+                                                 (__attribute__((address_space(3))) void *)(As + q * 1024), 16, 0, 0);
+            else
+                st16(As + (q * 64 + lane) * 16, u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+}
+
+// LDS byte offset of this lane's row in each M subtile of the tile at row m0
+// (tap (0,0), channel 0) inside the windows staged from slot s_lo; rows at or
+// past mrows read slot 0's first pixel (their results are never stored).
+template <int MT>
+__device__ __forceinline__ void row_offsets(const Geo &g, const ConvCfg &c, int m0, int mrows, int s_lo, int lane,
+                                            int (&rb)[MT]) {
+    const int b2 = g.b * g.b, ib2 = g.ib * g.ib;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int r = m0 + mt * 16 + (lane & 15);
+        int off = 0;
+        if (r < mrows) {
+            const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
+            const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+            off = ((slot - s_lo) * ib2 + py * g.s * g.ib + px * g.s) * c.a_pix_stride;
+        }
+        rb[mt] = off;
+    }
+}
+
+// This wave's K steps of one chunk (wave, wave + 8, ...) on the staged
+// windows: A fragments from LDS (rows at byte offsets rb), B fragments from
+// registers (zero outside c_in and c_out).  The A fragments of step j + 1 are
+// read from LDS while step j's MFMAs run.
+template <int DT, int MT, int NT, int SMAX>
+__device__ __forceinline__ void mfma_chunk(const ConvArgs &a, const uint8_t *As, const int (&rb)[MT],
+                                           const u32x4 (&bfr)[SMAX][NT], f32x4 (&acc)[MT][NT], int c0, int n0,
+                                           int wave, int lane, int steps, int kpc) {
+    constexpr int NW = kConvWaves, ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
+    const Geo &g = a.g;
+    const int apix = a.c.a_pix_stride, kl = (lane >> 4) * EPV;
+    u32x4 av[2][MT];
+    auto read_a = [&](int j, u32x4 (&dst)[MT]) {
+        const int stp = min(wave + NW * j, steps - 1);
+        const int tap = stp / kpc, kk = stp - tap * kpc;
+        const int ky = tap / g.k, kx = tap - ky * g.k;
+        const int aoff = (ky * g.ib + kx) * apix + (kk * KS + kl) * ES;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) dst[mt] = *(const u32x4 *)(As + rb[mt] + aoff);
+    };
+    if (wave < steps) read_a(0, av[0]);
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int stp = wave + NW * j;
+        if (stp >= steps) break;
+        if (j + 1 < SMAX && stp + NW < steps) read_a(j + 1, av[(j + 1) & 1]);
+        const int kk = stp - (stp / kpc) * kpc;
+        const bool kin = c0 + kk * KS + kl < g.cin;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = MfmaStep<DT>::run(
+                    av[j & 1][mt], (kin && n0 + nt * 16 + (lane & 15) < g.cout) ? bfr[j][nt] : u32x4{0u, 0u, 0u, 0u},
+                    acc[mt][nt]);
+    }
+}
+
+// Every wave parks its partial tile in LDS (16x16 accumulator layout: lane l
+// holds rows 4*(l/16)+i, column l%16), rows of PSTR floats, wave-major.
+template <int MT, int NT, int PSTR>
+__device__ __forceinline__ void park_partials(float *part, const f32x4 (&acc)[MT][NT], int wave, int lane) {
+    constexpr int BM = 16 * MT;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                part[(wave * BM + mt * 16 + (lane >> 4) * 4 + i) * PSTR + nt * 16 + (lane & 15)] = acc[mt][nt][i];
+}
+
+template <int DT, int MT, int NT, bool FUSED>
 __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
-    static_assert(FUSED || !SPL, "the split is for the fused layer");
     constexpr int NW = kConvWaves, NTHR = kConvThreads;
     constexpr int ES = elem_bytes(DT);
     constexpr int EPV = 16 / ES;  // elements per 16-byte vector
@@ -321,10 +483,8 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     const int ntn = (g.cout + BN - 1) / BN;
     const int grid = gridDim.x;
     const int vpc = c.ck / EPV;             // 16-byte vectors per staged pixel
-    const int apix = c.a_pix_stride;
     const int kpc = c.ck / KS;              // K steps per tap in a chunk
     const int steps = k2 * kpc;             // K steps per chunk
-    const int kl = (lane >> 4) * EPV;       // this lane group's element offset inside a step
     int ntiles = -1, cnt_seen = 0;
     // With the copy (or the restore), the bitmap of listed blocks is built from a read of the
     // list's first NTHR entries that rides along with the first tile's reads.
@@ -349,24 +509,11 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         return (xcd ? (mtn + 7) / 8 * 8 : mtn) * ntn;
     };
     const int tiles_cap = tiles_of(g.cap);
-    // split mode: the list length first (the work items depend on it), then
-    // items (tile, channel range), ranges of one tile adjacent
-    const int nch = (g.cin + c.ck - 1) / c.ck;
-    Split sp{};
-    if (SPL) {
-        sp = split_of(clamp_count(a.count, g.cap), b2, BM, ntn, nch, grid);
-        ntiles = sp.items;
-    }
     for (int t = blockIdx.x;; t += grid) {
         if (ntiles >= 0 && t >= ntiles) break;  // known after the first tile
-        if (!SPL && t >= tiles_cap) break;
-        int tn, tm, ks = 0;
-        if (SPL) {
-            const int tile = t / sp.S;
-            ks = t - tile * sp.S;
-            tn = tile % ntn;
-            tm = tile / ntn;
-        } else if (xcd) {
+        if (t >= tiles_cap) break;
+        int tn, tm;
+        if (xcd) {
             const int r8 = t >> 3;
             tn = r8 % ntn;
             tm = (r8 / ntn) * 8 + (t & 7);
@@ -374,8 +521,6 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             tn = t % ntn;
             tm = t / ntn;
         }
-        const int c_first = ks * sp.cpk * c.ck;                                // this item's channels
-        const int c_last = SPL ? min(g.cin, (ks + 1) * sp.cpk * c.ck) : g.cin;  // [c_first, c_last)
         const int m0 = min(tm * BM, mcap - 1);  // padding tiles past capacity read the last slot
         const int n0 = tn * BN;
         const int s_lo = fdiv(m0, c.m_b2);
@@ -396,7 +541,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         const int spec = FUSED ? a.idx[min(tid, g.cap - 1)] : 0;
         const float bv = bsrc[min(n0 + (lane & (BN - 1)), g.cout - 1)];
         u32x4 bfr[SMAX][NT];
-        load_weights<DT, NT, SMAX>(a, bfr, c_first, n0, wave, lane, steps, kpc);
+        load_weights<DT, NT, SMAX>(a, bfr, 0, n0, wave, lane, steps, kpc);
         __builtin_amdgcn_sched_barrier(0);  // every read above is issued before wave 0 waits for the list
         if (wave == 0) {
             if (lane == 0) s_cnt = min(max(cnt_raw, 0), g.cap);
@@ -426,20 +571,9 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
         if (ntiles < 0) ntiles = tiles_of(cnt);
         if (t >= ntiles) break;
         const int mrows = cnt * b2;
-        if (!SPL && tm * BM >= mrows) continue;  // a padding tile
-        // LDS byte offset of this lane's row in each M subtile (tap (0,0), channel 0)
+        if (tm * BM >= mrows) continue;  // a padding tile
         int rb[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = m0 + mt * 16 + (lane & 15);
-            int off = 0;
-            if (r < mrows) {
-                const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
-                const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
-                off = ((slot - s_lo) * ib2 + py * g.s * g.ib + px * g.s) * apix;
-            }
-            rb[mt] = off;
-        }
+        row_offsets<MT>(g, c, m0, mrows, s_lo, lane, rb);
         f32x4 acc[MT][NT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -447,103 +581,19 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         const int nslot = ns * ib2 * (vpc + 1);  // 16-byte LDS slots of the staged windows
-        const int nq = (nslot + 63) / 64;        // 64-slot groups, one wave instruction each
-        for (int c0 = c_first; c0 < c_last; c0 += c.ck) {
-            if (c0 > c_first) __syncthreads();  // every wave is done with the previous chunk
-            // Input windows straight from global memory into LDS: each wave fills
-            // 64 consecutive 16-byte slots per instruction (lane i -> slot base + i;
-            // a pixel occupies vpc slots plus one pad slot, left unwritten).
-            // Slots outside the image or beyond c_in get zeros from their own lane.
-            // Batches of QB slot groups per wave: decode, then every slot-table
-            // read of the batch, then every load.
-            constexpr int QB = 4;
-            for (int qb = wave; qb < nq; qb += NW * QB) {
-                int ls[QB], pix[QB], chv[QB];
-#pragma unroll
-                for (int i = 0; i < QB; ++i) {
-                    const int slot = (qb + NW * i) * 64 + lane;
-                    const int P = fdiv(slot, c.m_vpc1), cvv = slot - P * (vpc + 1);
-                    const bool act = slot < nslot && cvv < vpc;
-                    const int l = FUSED ? fdiv(P, c.m_ib2) : 0;
-                    ls[i] = act ? l : -1;
-                    pix[i] = FUSED ? P - l * ib2 : P;
-                    chv[i] = c0 + cvv * EPV;
-                }
-                int tn_[QB], ty[QB], tx[QB];
-                if (FUSED) {
-#pragma unroll
-                    for (int i = 0; i < QB; ++i) {
-                        const int l = max(ls[i], 0);
-                        tn_[i] = s_n[l];
-                        ty[i] = s_iy[l];
-                        tx[i] = s_ix[l];
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < QB; ++i) {
-                    if (ls[i] < 0) continue;
-                    const int q = qb + NW * i;
-                    const uint8_t *src = nullptr;
-                    if (chv[i] < g.cin) {
-                        if (FUSED) {
-                            const int yy = fdiv(pix[i], c.m_ib), xx = pix[i] - yy * g.ib;
-                            const int iy = ty[i] + yy, ix = tx[i] + xx;
-                            if (tn_[i] >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w)
-                                src = a.src + ((((size_t)tn_[i] * g.h + iy) * g.w + ix) * g.cin + chv[i]) * ES;
-                        } else {
-                            src = a.src + (((size_t)s_lo * ib2 + pix[i]) * g.cin + chv[i]) * ES;
-                        }
-                    }
-                    if (src)
-                        __builtin_amdgcn_global_load_lds((const void *)src,
-                                                         (__attribute__((address_space(3))) void *)(As + q * 1024),
-                                                         16, 0, 0);
-                    else
-                        st16(As + (q * 64 + lane) * 16, u32x4{0u, 0u, 0u, 0u});
-                }
-            }
-            if (c0 > c_first)  // the next chunk's weight fragments (the first chunk's are in flight)
+        for (int c0 = 0; c0 < g.cin; c0 += c.ck) {
+            if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+            stage_windows<DT, FUSED>(a, As, s_n, s_iy, s_ix, c0, nslot, s_lo, wave, lane);
+            if (c0 > 0)  // the next chunk's weight fragments (the first chunk's are in flight)
                 load_weights<DT, NT, SMAX>(a, bfr, c0, n0, wave, lane, steps, kpc);
             __builtin_amdgcn_s_waitcnt(0);  // the LDS loads and the weight fragments have landed
             __syncthreads();
-            // A fragments of step j + 1 are read from LDS while step j's MFMAs run.
-            u32x4 av[2][MT];
-            auto read_a = [&](int j, u32x4 (&dst)[MT]) {
-                const int stp = min(wave + NW * j, steps - 1);
-                const int tap = stp / kpc, kk = stp - tap * kpc;
-                const int ky = tap / g.k, kx = tap - ky * g.k;
-                const int aoff = (ky * g.ib + kx) * apix + (kk * KS + kl) * ES;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) dst[mt] = *(const u32x4 *)(As + rb[mt] + aoff);
-            };
-            if (wave < steps) read_a(0, av[0]);
-#pragma unroll
-            for (int j = 0; j < SMAX; ++j) {
-                const int stp = wave + NW * j;
-                if (stp >= steps) break;
-                if (j + 1 < SMAX && stp + NW < steps) read_a(j + 1, av[(j + 1) & 1]);
-                const int kk = stp - (stp / kpc) * kpc;
-                const bool kin = c0 + kk * KS + kl < g.cin;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        acc[mt][nt] = MfmaStep<DT>::run(
-                            av[j & 1][mt], (kin && n0 + nt * 16 + (lane & 15) < g.cout) ? bfr[j][nt] : u32x4{0u, 0u, 0u, 0u},
-                            acc[mt][nt]);
-            }
+            mfma_chunk<DT, MT, NT, SMAX>(a, As, rb, bfr, acc, c0, n0, wave, lane, steps, kpc);
         }
         // Sum the 8 waves' partial tiles: every wave parks its tile in LDS, then
         // each thread adds the eight copies of its output vector.
-        // 16x16 accumulator layout: lane l holds rows 4*(l/16)+i, column l%16.
         __syncthreads();  // all waves done reading the staged windows
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    part[(wave * BM + mt * 16 + (lane >> 4) * 4 + i) * PSTR + nt * 16 + (lane & 15)] = acc[mt][nt][i];
+        park_partials<MT, NT, PSTR>(part, acc, wave, lane);
         __syncthreads();
 #pragma unroll
         for (int o = 0; o < OPT; ++o) {
@@ -557,16 +607,10 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
             float sum[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float x = SPL ? 0.f : s_bias[col + j];
+                float x = s_bias[col + j];
 #pragma unroll
                 for (int w = 0; w < NW; ++w) x += part[(w * BM + row) * PSTR + col + j];
                 sum[j] = x;
-            }
-            if (SPL) {  // this channel range's sum of the tile, for k_split_combine
-                float *wp = a.ws + ((size_t)t * BM + row) * BN + col;
-                __builtin_nontemporal_store(f32x4{sum[0], sum[1], sum[2], sum[3]}, (f32x4 *)wp);
-                __builtin_nontemporal_store(f32x4{sum[4], sum[5], sum[6], sum[7]}, (f32x4 *)(wp + 4));
-                continue;
             }
             const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
             const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
@@ -617,20 +661,198 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
     }
 }
 
-// The end of the split: for each tile of the split, the ranges' fp32 sums added
-// in range order, the bias, one rounding, 16-byte stores into the output image
-// (grid-stride over (tile, row, 8 output channels)).  `slots` is the
-// convolution's grid, from which it took the split.
+// A workgroup barrier for LDS accesses only.  Each wave waits for its own LDS
+// accesses (s_waitcnt lgkmcnt(0)); the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.  Global loads in flight (the
+// next tile's windows, on their way into the other LDS buffer) and global
+// stores are not waited for, as the fences of __syncthreads would.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maximum
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The split over input channels (see StreamPlan).  A work item walks its
+// group's M tiles with the windows double-buffered in LDS: while tile i's MFMAs
+// run, tile i + 1's windows are in flight into the other buffer and tile
+// i + 2's block indices into registers.  Per M tile the eight waves' partial
+// tiles are summed through LDS and the chunk's fp32 sum goes to the workspace
+// (non-temporal stores, issued one tile later so that no wait covers them
+// early): partial (M tile tm, N tile tn, chunk ks) at
+// ((tm * ntn + tn) * nch + ks) * BM * BN.
+// LDS: buffer 0 at 0, buffer 1 at max(W, P), where W is one buffer of windows
+// and P the eight partial tiles; the partial tiles of the tile staged in buffer
+// b start at b * W, so they overlap only the buffer whose windows are consumed.
+// The slot table (image and window origin per block slot) has two copies: one
+// for the group's first tile, kept for every chunk of the range, and one for
+// the others (written for tile i + 1 after every wave has passed the barriers
+// that follow its last read, the staging of tile i).
+template <int DT, int MT, int NT>
+__global__ __launch_bounds__(kConvThreads, 2) void k_conv_stream(ConvArgs a) {
+    constexpr int NTHR = kConvThreads;
+    constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
+    constexpr int BM = 16 * MT, BN = 16 * NT;
+    constexpr int PSTR = BN + 4;
+    constexpr int SMAX = Smax<NT>::v;
+    constexpr int VPR = BN / 8;
+    static_assert(BM <= 64, "wave 0 fills the slot table: at most 64 slots per tile");
+    static_assert(BM * VPR <= NTHR, "one output vector per thread");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int s_n[2][BM + 1], s_iy[2][BM + 1], s_ix[2][BM + 1];
+
+    const Geo &g = a.g;
+    const ConvCfg &c = a.c;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
+    const int ntn = (g.cout + BN - 1) / BN;
+    const int vpc = c.ck / EPV, kpc = c.ck / KS, steps = k2 * kpc;
+    const int nch = (g.cin + c.ck - 1) / c.ck;
+    const int wbytes = c.a_bytes;                          // one buffer of windows
+    const int pbytes = kConvWaves * BM * PSTR * 4;         // the eight partial tiles
+    const int buf1 = wbytes > pbytes ? wbytes : pbytes;    // byte offset of buffer 1
+    const int cnt = clamp_count(a.count, g.cap);
+    const int mrows = cnt * b2;
+    const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, gridDim.x);
+
+    // the block slots of M tile tm: the first, and how many
+    auto slots_of = [&](int tm, int &s_lo, int &ns) {
+        const int m0 = tm * BM;
+        s_lo = fdiv(m0, c.m_b2);
+        ns = min(g.cap - 1, fdiv(m0 + BM - 1, c.m_b2)) - s_lo + 1;
+    };
+    // wave 0: lane l's block index of M tile tm (an unconditional read at a clamped slot)
+    auto read_lin = [&](int tm) {
+        int s_lo, ns;
+        slots_of(tm, s_lo, ns);
+        return a.idx[s_lo + min(lane, ns - 1)];
+    };
+    auto fill_table = [&](int tm, int lin, int tb) {
+        int s_lo, ns;
+        slots_of(tm, s_lo, ns);
+        if (lane < ns) {
+            int n, by, bx;
+            if (!decode_block(g, lin, n, by, bx)) n = -1;
+            s_n[tb][lane] = n;
+            s_iy[tb][lane] = by * g.b * g.s - g.p;
+            s_ix[tb][lane] = bx * g.b * g.s - g.p;
+        }
+    };
+    auto stage = [&](int tm, int tb, uint8_t *buf, int c0) {
+        int s_lo, ns;
+        slots_of(tm, s_lo, ns);
+        stage_windows<DT, true>(a, buf, s_n[tb], s_iy[tb], s_ix[tb], c0, ns * ib2 * (vpc + 1), s_lo, wave, lane);
+    };
+
+    for (int p = blockIdx.x; p < pl.positions; p += gridDim.x) {
+        int tn, wg;
+        if (pl.xcd) {
+            const int r8 = p >> 3;
+            tn = r8 % ntn;
+            wg = (r8 / ntn) * 8 + (p & 7);
+        } else {
+            tn = p % ntn;
+            wg = p / ntn;
+        }
+        if (wg >= pl.nwg) continue;  // padding
+        const int grp = wg / pl.S, rng = wg - grp * pl.S;
+        const int tm0 = grp * pl.R, tm1 = min(pl.mtn, tm0 + pl.R);
+        const int n0 = tn * BN;
+        __syncthreads();  // the previous item is done with LDS and the slot tables
+        if (wave == 0) {  // the first tile's slot table, for every chunk of the range
+            const int lin0 = read_lin(tm0);
+            fill_table(tm0, lin0, 0);
+        }
+        const int ks0 = rng * pl.cpk, ks1 = min(nch, ks0 + pl.cpk);
+        f32x4 acc[MT][NT];
+        for (int ks = ks0; ks < ks1; ++ks) {
+            const int c0 = ks * c.ck;
+            __syncthreads();  // the first slot table is visible; the previous chunk is done with LDS
+            // one round trip: this wave's weight fragments for the chunk (kept for
+            // every M tile of the group), the first tile's windows and wave 0's
+            // block indices of the second tile
+            u32x4 bfr[SMAX][NT];
+            load_weights<DT, NT, SMAX>(a, bfr, c0, n0, wave, lane, steps, kpc);
+            int lin = 0;
+            if (wave == 0 && tm0 + 1 < tm1) lin = read_lin(tm0 + 1);
+            stage(tm0, 0, smem, c0);
+            // this thread's output vector of the previous tile, stored one tile later
+            float *pend = nullptr;
+            f32x4 plo{0.f, 0.f, 0.f, 0.f}, phi{0.f, 0.f, 0.f, 0.f};
+            const int row = tid / VPR, col = (tid - row * VPR) * 8;
+            for (int tm = tm0, i = 0; tm < tm1; ++tm, ++i) {
+                const int cur = i & 1;
+                uint8_t *As = smem + cur * buf1;
+                __builtin_amdgcn_s_waitcnt(0);  // this tile's windows, the weights, the next block indices
+                if (pend) {
+                    __builtin_nontemporal_store(plo, (f32x4 *)pend);
+                    __builtin_nontemporal_store(phi, (f32x4 *)(pend + 4));
+                    pend = nullptr;
+                }
+                if (wave == 0 && tm + 1 < tm1) fill_table(tm + 1, lin, 1);
+                lds_barrier();  // windows and the next slot table visible; the other buffer is free
+                if (tm + 1 < tm1) stage(tm + 1, 1, smem + (cur ^ 1) * buf1, c0);
+                if (wave == 0 && tm + 2 < tm1) lin = read_lin(tm + 2);
+                int s_lo, ns;
+                slots_of(tm, s_lo, ns);
+                int rb[MT];
+                row_offsets<MT>(g, c, tm * BM, mrows, s_lo, lane, rb);
+                if (!pl.acc_range || ks == ks0) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                mfma_chunk<DT, MT, NT, SMAX>(a, As, rb, bfr, acc, c0, n0, wave, lane, steps, kpc);
+                if (pl.acc_range && ks + 1 < ks1) continue;  // the range goes on in the accumulators
+                lds_barrier();  // every wave is done reading this tile's windows
+                float *part = (float *)(smem + cur * wbytes);
+                park_partials<MT, NT, PSTR>(part, acc, wave, lane);
+                lds_barrier();
+                if (tid < BM * VPR && tm * BM + row < mrows && n0 + col < g.cout) {
+                    float sum[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int w = 0; w < kConvWaves; ++w) x += part[(w * BM + row) * PSTR + col + j];
+                        sum[j] = x;
+                    }
+                    const size_t tile = (size_t)tm * ntn + tn;
+                    const int kout = pl.acc_range ? ks0 : ks;
+                    pend = a.ws + (((tile * nch + kout) * BM + row) * BN + col);
+                    plo = f32x4{sum[0], sum[1], sum[2], sum[3]};
+                    phi = f32x4{sum[4], sum[5], sum[6], sum[7]};
+                }
+            }
+            if (pend) {
+                __builtin_nontemporal_store(plo, (f32x4 *)pend);
+                __builtin_nontemporal_store(phi, (f32x4 *)(pend + 4));
+            }
+        }
+    }
+}
+
+// The end of the split: for each listed output row and 8 output channels, the
+// partial tiles (per chunk, or per range) added in order, the bias, one
+// rounding, a 16-byte store into the output image.  With the copy
+// (cc.nvec > 0), the workgroups past the ones with combine work copy the cache
+// outside the listed blocks (when the combine work fills at least half of the
+// grid, every workgroup takes a share after its rows).  `slots` is the
+// convolution's grid, from which it took the plan.
 template <int DT, int MT, int NT>
 __global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
     constexpr int ES = elem_bytes(DT), BM = 16 * MT, BN = 16 * NT, VPR = BN / 8;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const Geo &g = a.g;
     const ConvCfg &c = a.c;
     const int b2 = g.b * g.b, ntn = (g.cout + BN - 1) / BN;
+    const int nch = (g.cin + c.ck - 1) / c.ck;
     const int cnt = clamp_count(a.count, g.cap);
-    const Split sp = split_of(cnt, b2, BM, ntn, (g.cin + c.ck - 1) / c.ck, slots);
+    const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, slots);
     const int mrows = cnt * b2;
-    const long total = (long)sp.tiles * BM * VPR;
+    const long total = (long)pl.mtn * ntn * BM * VPR;
     for (long u = (long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long)gridDim.x * 256) {
         const int tile = (int)(u / (BM * VPR)), rem = (int)(u - (long)tile * BM * VPR);
         const int row = rem / VPR, col = (rem - row * VPR) * 8;
@@ -646,8 +868,8 @@ __global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
         float sum[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) sum[j] = a.bias ? a.bias[min(co + j, g.cout - 1)] : 0.f;
-        for (int ks = 0; ks < sp.S; ++ks) {
-            const float *wp = a.ws + ((size_t)(tile * sp.S + ks) * BM + row) * BN + col;
+        for (int ks = 0; ks < nch; ks += pl.acc_range ? pl.cpk : 1) {
+            const float *wp = a.ws + (((size_t)tile * nch + ks) * BM + row) * BN + col;
             const f32x4 lo = *(const f32x4 *)wp, hi = *(const f32x4 *)(wp + 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -656,6 +878,21 @@ __global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
             }
         }
         store_row8<DT>(a.dst + ((((size_t)n * g.ho + y) * g.wo + x) * g.cout + co) * ES, sum, g.cout - co >= 8);
+    }
+    if (a.cc.nvec > 0) {
+        const int busy = (int)((total + 255) / 256);
+        const int c0 = busy < (int)gridDim.x / 2 ? busy : 0;
+        if ((int)blockIdx.x < c0) return;
+        const int i = blockIdx.x - c0, nw = gridDim.x - c0;
+        const long long lo = split_point(a.cc.nvec, i, nw), hi = split_point(a.cc.nvec, i + 1, nw);
+        if (lo < hi) {
+            uint32_t *bm = nullptr;
+            if (((g.cap + 31) >> 5) * 4 <= 64 * 1024) {
+                bm = (uint32_t *)smem;
+                build_bitmap<256>(a.idx, cnt, g.cap, bm);
+            }
+            copy_span<4, 256>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, lo, hi);
+        }
     }
 }
 
@@ -692,36 +929,40 @@ static unsigned conv_grid(K kernel, const ConvArgs &args) {
 
 template <int DT, int MT, int NT>
 static hipError_t launch_conv_t(int fused, const ConvArgs &args, hipStream_t st) {
-    if (fused && args.ws) {  // the split over input channels, then the combine
-        auto k = k_conv<DT, MT, NT, true, true>;
-        const int slots = args.c.cus * resident_per_cu(k, args.c.lds_bytes);
-        hipLaunchKernelGGL(k, dim3(slots), dim3(kConvThreads), args.c.lds_bytes, st, args);
+    if (fused && args.ws) {  // the split over input channels, then the combine (and the copy)
+        auto k = k_conv_stream<DT, MT, NT>;
+        int slots = args.c.cus * resident_per_cu(k, args.c.lds_bytes);
+        if (slots > 8) slots = slots / 8 * 8;  // keep position p on XCD p % 8 across passes
+        ConvArgs conv = args;
+        conv.cc.nvec = 0;  // the combine copies the cache
+        hipLaunchKernelGGL(k, dim3(slots), dim3(kConvThreads), args.c.lds_bytes, st, conv);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         constexpr int BM = 16 * MT, BN = 16 * NT;
-        const long work = (long)(args.g.cap * args.g.b * args.g.b + BM - 1) / BM *
-                          ((args.g.cout + BN - 1) / BN) * BM * (BN / 8);  // tiles at capacity
-        const long grid = (work + 255) / 256 < 4L * args.c.cus ? (work + 255) / 256 : 4L * args.c.cus;
+        const long work = ((long)args.g.cap * args.g.b * args.g.b + BM - 1) / BM *
+                          ((args.g.cout + BN - 1) / BN) * BM * (BN / 8);  // rows x vectors at capacity
+        long grid = (work + 255) / 256 < 4L * args.c.cus ? (work + 255) / 256 : 4L * args.c.cus;
+        if (args.cc.nvec > 0) grid = 4L * args.c.cus;  // room for the copy
+        const int bm = args.cc.nvec > 0 && ((args.g.cap + 31) / 32) * 4 <= 64 * 1024 ? ((args.g.cap + 31) / 32) * 4 : 0;
         auto kc = k_split_combine<DT, MT, NT>;
-        hipLaunchKernelGGL(kc, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, st, args, slots);
+        hipLaunchKernelGGL(kc, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), bm, st, args, slots);
     } else if (fused) {
-        auto k = k_conv<DT, MT, NT, true, false>;
+        auto k = k_conv<DT, MT, NT, true>;
         hipLaunchKernelGGL(k, dim3(conv_grid(k, args)), dim3(kConvThreads), args.c.lds_bytes, st, args);
     } else {
-        auto k = k_conv<DT, MT, NT, false, false>;
+        auto k = k_conv<DT, MT, NT, false>;
         hipLaunchKernelGGL(k, dim3(conv_grid(k, args)), dim3(kConvThreads), args.c.lds_bytes, st, args);
     }
     return hipGetLastError();
 }
 
-// Work items the split's workspace must hold: every resident slot (a split),
-// or every tile at capacity (no split).
+// Partial tiles the split's workspace must hold: one per (M tile, N tile,
+// chunk) at full capacity.
 template <int DT, int MT, int NT>
 static long split_items_t(const Geo &g, const ConvCfg &c) {
     constexpr int BM = 16 * MT, BN = 16 * NT;
-    const long slots = (long)c.cus * resident_per_cu(k_conv<DT, MT, NT, true, true>, c.lds_bytes);
     const long tiles = ((long)g.cap * g.b * g.b + BM - 1) / BM * ((g.cout + BN - 1) / BN);
-    return slots > tiles ? slots : tiles;
+    return tiles * ((g.cin + c.ck - 1) / c.ck);
 }
 
 long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c) {

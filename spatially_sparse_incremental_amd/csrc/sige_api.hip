@@ -168,9 +168,11 @@ void tile_shape(int *mt, int *nt) {
 // 8 waves holds the weight fragments of at most 10/NT K steps of a chunk in
 // registers, so a chunk has at most 8*10/NT steps: ck <= floor(80/(NT*k*k)) K
 // slices.
-// Among those, the fewest chunks whose input windows fit in the device's LDS.
+// Among those, the fewest chunks whose input windows fit in the device's LDS
+// (stream: the split over input channels, which holds two buffers of windows
+// and the partial tiles overlapping one of them).
 // The persistent grid fills every CU with up to two workgroups.
-int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
+int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int stream = 0) {
     ConvCfg c{};
     tile_shape(&c.mt, &c.nt);
     const int es = sige::elem_bytes(dt);
@@ -197,7 +199,7 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out) {
         if (ck * es / 16 > 256) continue;               // one 16-byte vector per thread and pixel
         const long apix = ck * es + 16;
         const long lds = (long)ns * ib2 * apix;
-        const long need = lds > part ? lds : part;
+        const long need = (lds > part ? lds : part) + (stream ? lds : 0);
         if (need <= limit) {
             best = ck;
             best_lds = need;
@@ -239,7 +241,11 @@ int attn_grid1() {
         (void)hipGetLastError();
         return sige::attn_partial_grid(dev_info().cus);
     }
-    if (!grid[dev]) grid[dev] = sige::attn_partial_grid(dev_info().cus);
+    if (!grid[dev]) {  // SIGE_ATTN_GRID overrides the partial kernel's grid (tuning)
+        const char *v = getenv("SIGE_ATTN_GRID");
+        const long x = v ? strtol(v, nullptr, 10) : 0;
+        grid[dev] = (x > 0 && x <= 65536) ? (int)x : sige::attn_partial_grid(dev_info().cus);
+    }
     return grid[dev];
 }
 
@@ -473,7 +479,7 @@ int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *gp, int dtype) {
     if (rc) return rc;
     if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
     ConvCfg cfg;
-    if ((rc = choose_conv(g, dtype, 1, 1, &cfg))) return rc;
+    if ((rc = choose_conv(g, dtype, 1, 1, &cfg, 1))) return rc;
     const long bytes = sige::split_workspace_bytes(dtype, g, cfg);
     if (bytes < 0) return fail(SIGE_EINVAL, "unknown tile shape");
     g_msg[0] = 0;
@@ -500,7 +506,7 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
     if (overlap(out, obytes, a_edit, ibytes)) return fail(SIGE_EINVAL, "out overlaps a_edit");
     if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
     ConvCfg cfg;
-    if ((rc = choose_conv(g, dtype, 1, 1, &cfg))) return rc;  // the full resident grid
+    if ((rc = choose_conv(g, dtype, 1, 1, &cfg, 1))) return rc;
     if ((rc = device_ready())) return rc;
     const long need = sige::split_workspace_bytes(dtype, g, cfg);
     if (need < 0) return fail(SIGE_EINVAL, "unknown tile shape");
