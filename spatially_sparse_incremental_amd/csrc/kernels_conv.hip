@@ -250,8 +250,12 @@ struct ConvArgs {
 // otherwise there is one group and as many ranges as the slots allow.  A
 // group of one M tile with several chunks per range (acc_range) keeps its
 // accumulators over the range and leaves one partial tile per range, at the
-// range's first chunk.  Both kernels derive the same plan from the list
-// length.  Window group = (group,
+// range's first chunk.  Without room for a second LDS buffer of windows
+// (dbuf), and when chunk ranges are needed for at most 4 M tiles (streaming
+// would reuse each chunk's weights at most 4 times but pay an epilogue per M
+// tile and chunk), every group is one M tile.  Both kernels derive the same
+// plan from the list length (its arithmetic runs at the start of both
+// launches, on the path to the first loads, so it is kept short).  Window group = (group,
 // range): the items that stage the same windows.  With at least 8 window
 // groups (and no extra round of positions from the padding), position
 // p = 8 * (tn + ntn * (wg / 8)) + wg % 8 puts every N tile of window group wg
@@ -265,20 +269,29 @@ struct StreamPlan {
     bool xcd;
     int positions;      // work positions, padding included
 };
-__device__ __forceinline__ StreamPlan stream_plan(int cnt, int b2, int bm, int ntn, int nch, int slots) {
+// Whether the launch's LDS holds two buffers of windows next to the partial
+// tiles of NW waves (see k_conv_stream).
+__device__ __forceinline__ bool stream_dbuf(const ConvCfg &c, int bm, int bn, int nw) {
+    const int pbytes = nw * bm * (bn + 4) * 4;
+    return c.lds_bytes >= (c.a_bytes > pbytes ? c.a_bytes : pbytes) + c.a_bytes;
+}
+
+__device__ __forceinline__ StreamPlan stream_plan(int cnt, int b2, int bm, int ntn, int nch, int slots, bool dbuf) {
     StreamPlan p;
     p.mtn = (cnt * b2 + bm - 1) / bm;
     p.ntn = ntn;
     p.nch = nch;
+    const int mt = max(p.mtn, 1);
     int G = 1, S = nch;
-    if (ntn * nch <= slots)
-        G = min(slots / max(ntn * nch, 1), max(p.mtn, 1));
-    else
-        S = max(1, min(nch, slots / max(ntn, 1)));
+    if (dbuf && ntn * nch <= slots)
+        G = min(slots / max(ntn * nch, 1), mt);
+    else if (!dbuf || mt <= 4)
+        G = mt;  // one M tile per group, chunk ranges in the accumulators
+    if (G * ntn * nch > slots) S = max(1, min(nch, slots / max(G * ntn, 1)));
     p.cpk = (nch + S - 1) / S;
     p.S = (nch + p.cpk - 1) / p.cpk;  // evened: no empty range
-    p.R = max(1, (p.mtn + G - 1) / G);
-    p.G = (p.mtn + p.R - 1) / p.R;  // 0 for an empty list
+    p.R = (mt + G - 1) / G;
+    p.G = p.mtn > 0 ? (p.mtn + p.R - 1) / p.R : 0;  // 0 for an empty list
     p.nwg = p.G * p.S;
     p.acc_range = p.R == 1 && p.cpk > 1;
     const int padded = (p.nwg + 7) / 8 * 8 * ntn;
@@ -684,6 +697,8 @@ __device__ __forceinline__ void lds_barrier() {
 // LDS: buffer 0 at 0, buffer 1 at max(W, P), where W is one buffer of windows
 // and P the eight partial tiles; the partial tiles of the tile staged in buffer
 // b start at b * W, so they overlap only the buffer whose windows are consumed.
+// When the launch has no room for buffer 1 (large halos), the plan gives every
+// group one M tile, so no tile is staged while another is computed.
 // The slot table (image and window origin per block slot) has two copies: one
 // for the group's first tile, kept for every chunk of the range, and one for
 // the others (written for tile i + 1 after every wave has passed the barriers
@@ -711,10 +726,11 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv_stream(ConvArgs a) {
     const int nch = (g.cin + c.ck - 1) / c.ck;
     const int wbytes = c.a_bytes;                          // one buffer of windows
     const int pbytes = kConvWaves * BM * PSTR * 4;         // the eight partial tiles
-    const int buf1 = wbytes > pbytes ? wbytes : pbytes;    // byte offset of buffer 1
+    const bool dbuf = stream_dbuf(c, BM, BN, kConvWaves);  // two buffers of windows
+    const int buf1 = dbuf ? (wbytes > pbytes ? wbytes : pbytes) : 0;  // byte offset of buffer 1
     const int cnt = clamp_count(a.count, g.cap);
     const int mrows = cnt * b2;
-    const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, gridDim.x);
+    const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, gridDim.x, dbuf);
 
     // the block slots of M tile tm: the first, and how many
     auto slots_of = [&](int tm, int &s_lo, int &ns) {
@@ -807,7 +823,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv_stream(ConvArgs a) {
                 mfma_chunk<DT, MT, NT, SMAX>(a, As, rb, bfr, acc, c0, n0, wave, lane, steps, kpc);
                 if (pl.acc_range && ks + 1 < ks1) continue;  // the range goes on in the accumulators
                 lds_barrier();  // every wave is done reading this tile's windows
-                float *part = (float *)(smem + cur * wbytes);
+                float *part = (float *)(smem + (dbuf ? cur * wbytes : 0));
                 park_partials<MT, NT, PSTR>(part, acc, wave, lane);
                 lds_barrier();
                 if (tid < BM * VPR && tm * BM + row < mrows && n0 + col < g.cout) {
@@ -850,7 +866,7 @@ __global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
     const int b2 = g.b * g.b, ntn = (g.cout + BN - 1) / BN;
     const int nch = (g.cin + c.ck - 1) / c.ck;
     const int cnt = clamp_count(a.count, g.cap);
-    const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, slots);
+    const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, slots, stream_dbuf(c, BM, BN, kConvWaves));
     const int mrows = cnt * b2;
     const long total = (long)pl.mtn * ntn * BM * VPR;
     for (long u = (long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long)gridDim.x * 256) {

@@ -169,8 +169,8 @@ void tile_shape(int *mt, int *nt) {
 // registers, so a chunk has at most 8*10/NT steps: ck <= floor(80/(NT*k*k)) K
 // slices.
 // Among those, the fewest chunks whose input windows fit in the device's LDS
-// (stream: the split over input channels, which holds two buffers of windows
-// and the partial tiles overlapping one of them).
+// (stream: the split over input channels, which also takes a second buffer of
+// windows when it fits, to stage the next M tile during the current one).
 // The persistent grid fills every CU with up to two workgroups.
 int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int stream = 0) {
     ConvCfg c{};
@@ -199,10 +199,10 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
         if (ck * es / 16 > 256) continue;               // one 16-byte vector per thread and pixel
         const long apix = ck * es + 16;
         const long lds = (long)ns * ib2 * apix;
-        const long need = (lds > part ? lds : part) + (stream ? lds : 0);
+        const long need = lds > part ? lds : part;
         if (need <= limit) {
             best = ck;
-            best_lds = need;
+            best_lds = stream && need + lds <= limit ? need + lds : need;
         }
     }
     if (!best)
