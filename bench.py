@@ -6,10 +6,11 @@ One step is one incremental update of one layer for one edit, on the
 U-Net-shaped workload (3x3 stride-1 conv, bf16 NHWC 1x256x256x128 -> 128,
 6x6 output blocks, block-grid dilation 1, seeded 3-ellipse blob edit covering
 1.2% of the pixels):
-    sige_diff_mask -> sige_reduce_mask_copy -> sige_sparse_conv_layer (copy_cached=0)
+    sige_diff_mask_bits -> sige_reduce_bits_copy -> sige_sparse_conv_layer (copy_cached=0)
 whose result is the spec-literal one (the cached output with the listed blocks
-recomputed): the full copy of the cache into the output runs on the idle
-workgroups of the single-workgroup reduce launch.  Every input is already
+recomputed): the change mask is written one bit per pixel (the reduce's single
+workgroup reads 8 KiB instead of 64 KiB), and the full copy of the cache into
+the output runs on the idle workgroups of the single-workgroup reduce launch.  Every input is already
 resident in device memory.  K steps run back to back
 as replays of a HIP graph of 10 captured steps, between two HIP events;
 `value` is the mean time per step in microseconds (lower is better).  The
@@ -109,6 +110,7 @@ def main():
     ssi.sige_sparse_conv_layer(a_o, w_krsc, bias, None, idx_all, cnt_all, g, out=cache, copy_cached=False)
 
     mask = torch.empty((1, L.h, L.w), dtype=torch.uint8, device=dev)
+    mbits = torch.empty((L.h * L.w // 32,), dtype=torch.int32, device=dev)  # the mask, one bit per pixel
     idx = torch.empty((cap,), dtype=torch.int32, device=dev)
     count = torch.empty((1,), dtype=torch.int32, device=dev)
     out = torch.empty_like(cache)
@@ -116,8 +118,8 @@ def main():
     def step(st=None):
         # out = cache outside the listed blocks (a full copy), conv inside: the copy
         # runs on the idle workgroups of the single-workgroup reduce
-        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask, stream=st)
-        ssi.sige_reduce_mask_copy(mask, g, L.dilate, cache, out=out, idx=idx, count=count, stream=st)
+        ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits, stream=st)
+        ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=count, stream=st)
         ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False, stream=st)
 
     K, W = args.steps, args.warmup
@@ -204,16 +206,16 @@ def main():
 
     # ---- per-kernel durations: graphs of 20 back-to-back launches of one call
     kt = {  # the three calls of the step
-        "diff": graph_time(lambda: ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)),
-        "reduce_copy": graph_time(lambda: ssi.sige_reduce_mask_copy(mask, g, L.dilate, cache, out=out, idx=idx,
-                                                                    count=count)),
+        "diff": graph_time(lambda: ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)),
+        "reduce_copy": graph_time(lambda: ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out,
+                                                                    idx=idx, count=count)),
         "fused_layer": graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g,
                                                                      out=out, copy_cached=False)),
     }
     print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
 
     t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_copy = t_dense_ours = t_dense_miopen = None
-    t_reduce = t_step_conv_copy = None
+    t_reduce = t_step_conv_copy = t_step_bytes = t_reduce_bytes = None
     t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = attention = ldm_split = t_layer = None
     chain = gaugan = None
     bbox_flops = bbox_blocks = rect = None
@@ -229,11 +231,19 @@ def main():
         t_step_conv_copy = graph_time(step_conv_copy, 5, 40)
 
         def layer_only():  # the per-layer part of the step: reduce (with the copy) and the fused layer
-            ssi.sige_reduce_mask_copy(mask, g, L.dilate, cache, out=out, idx=idx, count=count)
+            ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=count)
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False)
 
         t_layer = graph_time(layer_only, 5, 40)
-        t_reduce = graph_time(lambda: ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count))
+        t_reduce = graph_time(lambda: ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count))
+
+        def step_bytes():  # the step with the change mask as bytes
+            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            ssi.sige_reduce_mask_copy(mask, g, L.dilate, cache, out=out, idx=idx, count=count)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False)
+
+        t_step_bytes = graph_time(step_bytes, 5, 40)
+        t_reduce_bytes = graph_time(lambda: ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count))
         t_fused_copy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g,
                                                                      out=out_c, copy_cached=True))
 
@@ -369,8 +379,8 @@ def main():
     b2 = L.block * L.block
     act_pix = int(_active_pixels(idx[:active].cpu().numpy(), d, L.block))
     w_bytes = L.c_out * L.k * L.k * L.c_in * es
-    diff_bytes = 2 * npix_in * L.c_in * es + npix_in
-    reduce_bytes = npix_in + 4 * active + 4
+    diff_bytes = 2 * npix_in * L.c_in * es + npix_in // 8    # the mask written one bit per pixel
+    reduce_bytes = npix_in // 8 + 4 * active + 4
     blk_bytes = active * (d.ib * d.ib * L.c_in * es + b2 * L.c_out * es)
     copy_bytes = 2 * (npix_out - act_pix) * L.c_out * es
     conv_flops = 2.0 * active * b2 * L.c_in * L.c_out * L.k * L.k
@@ -442,6 +452,8 @@ def main():
             "speedup_vs_dense_ours": round(t_dense_ours / step_us, 3),
             "dense_ours_tflops": round(dense_flops / (t_dense_ours * 1e-6) / 1e12, 1),
             "step_no_copy_us": round(t_nocopy, 3),
+            "step_byte_mask_us": round(t_step_bytes, 3),
+            "reduce_byte_mask_us": round(t_reduce_bytes, 3),
             "step_copy_in_conv_us": round(t_step_conv_copy, 3),
             "step_three_call_us": round(t_three, 3),
             "step_sequential_edits_us": round(t_seq, 3),
@@ -691,16 +703,17 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
 
 def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
     """The 12-conv U-Net chain (cfg3) at the 1.2% blob edit, as HIP graphs: one
-    diff at 256x256, then per layer the reduce (the mask pooled to the layer's
-    input) and the fused layer with the cache copy, layer l+1 reading layer l's
-    output; against the same 12 convs dense through torch/MIOpen."""
+    diff at 256x256 (the mask one bit per pixel), then per layer the reduce of
+    the mask pooled to the layer's input with the cache copy on its idle
+    workgroups, and the fused layer, layer l+1 reading layer l's output;
+    against the same 12 convs dense through torch/MIOpen."""
     dev = torch.device("cuda:0")
     wl = synth.workload("cfg3_chain_bf16")
     first = wl.layers[0]
     m = synth.edit_shape(wl, seed).raster(first.h, first.w)
     a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed).to(dev)
     a_e = synth.make_edit(a_o.cpu(), m, wl.edit_kind, seed).to(dev)
-    mask = torch.empty((1, first.h, first.w), dtype=torch.uint8, device=dev)
+    mbits = torch.empty((first.h * first.w // 32,), dtype=torch.int32, device=dev)
     layers = []
     x_dense = [a_e.permute(0, 3, 1, 2)]
     for li, L in enumerate(wl.layers):
@@ -716,12 +729,13 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
     blocks = []
 
     def sparse_chain():
-        ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+        ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
         x = a_e
         for ly in layers:
-            ssi.sige_reduce_mask(mask, ly["g"], ly["L"].dilate, idx=ly["idx"], count=ly["cnt"])
-            ssi.sige_sparse_conv_layer(x, ly["wk"], ly["bias"], ly["cache"], ly["idx"], ly["cnt"], ly["g"],
-                                       out=ly["out"])
+            ssi.sige_reduce_bits_copy(mbits, first.h, first.w, ly["g"], ly["L"].dilate, ly["cache"], out=ly["out"],
+                                      idx=ly["idx"], count=ly["cnt"])
+            ssi.sige_sparse_conv_layer(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"], out=ly["out"],
+                                       copy_cached=False)
             x = ly["out"]
 
     def dense_chain():
@@ -737,14 +751,14 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
         t_dense = graph_time(dense_chain, 1, 10)
     return {"sparse_us": round(t_sparse, 3), "dense_miopen_us": round(t_dense, 3),
             "speedup": round(t_dense / t_sparse, 2), "blocks_per_layer": blocks,
-            "note": "one diff + 12 x (reduce + fused layer with the cache copy); dense: 12 x F.conv2d; HIP graphs"}
+            "note": "one diff + 12 x (reduce with the cache copy + fused layer); dense: 12 x F.conv2d; HIP graphs"}
 
 
 def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     """The four GauGAN-shaped bf16 convs (cfg4) under the seeded star polygon at
-    0.5 / 1.2 / 5 / 15 / 30% of the frame: reduce + the faster of the fused
-    layer and its split (both with the cache copy) per layer, against the dense
-    conv through torch/MIOpen."""
+    0.5 / 1.2 / 5 / 15 / 30% of the frame: the reduce (mask one bit per pixel,
+    the cache copy on its idle workgroups) + the faster of the fused layer and
+    its split per layer, against the dense conv through torch/MIOpen."""
     dev = torch.device("cuda:0")
     wl = synth.workload("cfg4_gaugan_bf16")
     res, dense = {}, {}
@@ -765,19 +779,20 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
         row = {}
         for li, (L, g, a_o, wk, bias, cache, _) in enumerate(prep):
             a_e = synth.make_edit(a_o.cpu(), shape.raster(L.h, L.w), wl.edit_kind, seed + li).to(dev)
-            mask = ssi.sige_diff_mask(a_o, a_e, wl.tau)
-            idx, cnt = ssi.sige_reduce_mask(mask, g, L.dilate)
+            mbits = ssi.sige_diff_mask_bits(a_o, a_e, wl.tau)
+            idx, cnt = ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate)
             out = torch.empty_like(cache)
             ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8,
                              device=dev)
 
             def one():
-                ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=cnt)
-                ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out)
+                ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)
+                ssi.sige_sparse_conv_layer(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False)
 
             def split():
-                ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=cnt)
-                ssi.sige_sparse_conv_layer_split(a_e, wk, bias, cache, idx, cnt, g, out=out, workspace=ws)
+                ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)
+                ssi.sige_sparse_conv_layer_split(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False,
+                                                 workspace=ws)
 
             t1, t2 = graph_time(one, 5, 20), graph_time(split, 5, 20)
             row[L.name] = {"blocks": int(cnt.item()), "sparse_us": round(min(t1, t2), 3),

@@ -99,6 +99,18 @@ int64_t sige_max_blocks(const sige_geom *g);
 int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
                    uint8_t *mask, void *stream);
 
+/* Step 1 with the mask also (or only) packed one bit per pixel: the same change
+ * mask as sige_diff_mask, written to `bits` as bit p % 32 of 32-bit word p / 32
+ * for pixel p (p = (n*h + y)*w + x).  The packed form is what
+ * sige_reduce_bits reads: one eighth of the mask bytes through the single
+ * workgroup that pools it.
+ *   w must be a multiple of 32 (whole words per row), else SIGE_EINVAL.
+ *   bits: uint32 [n*h*w/32], 4-byte aligned; written completely.
+ *   mask: as sige_diff_mask, or NULL to write the bits only (not both NULL).
+ *   Other arguments as sige_diff_mask. */
+int sige_diff_mask_bits(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
+                        uint8_t *mask, uint32_t *bits, void *stream);
+
 /* Step 2 -- active block list (mer.dev notes, 3.2: downsample the mask to each
  * scale and dilate it; SIGE README, "Overview": reduce it to active block indices).
  *   mask: uint8 [g->n, mask_h, mask_w], nonzero = changed.  mask_h = fy * g->h and
@@ -126,6 +138,18 @@ int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geo
  *   must not overlap cached, mask, idx or count.  Other arguments and limits
  *   as sige_reduce_mask. */
 int sige_reduce_mask_copy(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
+                          int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream);
+
+/* sige_reduce_mask and sige_reduce_mask_copy with the mask packed one bit per
+ * pixel, as sige_diff_mask_bits writes it: bit p % 32 of word p / 32 for pixel
+ * p = (n*mask_h + y)*mask_w + x.  Same results (bit for bit) as the byte-mask
+ * calls on the unpacked mask.
+ *   bits: uint32 [g->n*mask_h*mask_w/32], 4-byte aligned (else SIGE_EALIGN);
+ *   mask_w a multiple of 32 (else SIGE_EINVAL).  Other arguments and limits as
+ *   the byte-mask calls. */
+int sige_reduce_bits(const uint32_t *bits, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
+                     int32_t *idx, int32_t *count, void *stream);
+int sige_reduce_bits_copy(const uint32_t *bits, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
                           int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream);
 
 /* Step 3 -- gather (SIGE README, "Overview": collect the active blocks from the

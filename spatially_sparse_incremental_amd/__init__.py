@@ -13,9 +13,12 @@ from ._lib import (  # noqa: F401
     lib,
     sige_conv_blocks,
     sige_diff_mask,
+    sige_diff_mask_bits,
     sige_gather,
     sige_geom_derive,
     sige_max_blocks,
+    sige_reduce_bits,
+    sige_reduce_bits_copy,
     sige_reduce_mask,
     sige_reduce_mask_copy,
     sige_restore_blocks,

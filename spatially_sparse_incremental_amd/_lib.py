@@ -19,6 +19,7 @@ SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERA
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_reduce_mask_copy",
+           "sige_diff_mask_bits", "sige_reduce_bits", "sige_reduce_bits_copy",
            "sige_sparse_conv_layer_split", "sige_sparse_conv_layer_split_workspace",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
@@ -59,6 +60,9 @@ def lib():
         L.sige_diff_mask.argtypes = [V, V, I, I, I, I, I, ctypes.c_float, V, V]
         L.sige_reduce_mask.argtypes = [V, I, I, P, I, V, V, V]
         L.sige_reduce_mask_copy.argtypes = [V, I, I, P, I, V, V, I, V, V, V]
+        L.sige_diff_mask_bits.argtypes = [V, V, I, I, I, I, I, ctypes.c_float, V, V, V]
+        L.sige_reduce_bits.argtypes = [V, I, I, P, I, V, V, V]
+        L.sige_reduce_bits_copy.argtypes = [V, I, I, P, I, V, V, I, V, V, V]
         L.sige_gather.argtypes = [V, I, P, V, V, V, V]
         L.sige_conv_blocks.argtypes = [V, V, V, I, P, V, V, V]
         L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
@@ -144,6 +148,55 @@ def sige_diff_mask(a_orig, a_edit, thresh=1e-6, mask=None, stream=None):
                               _stream(stream))
     _check(rc, "sige_diff_mask")
     return mask
+
+
+def sige_diff_mask_bits(a_orig, a_edit, thresh=1e-6, bits=None, mask=None, stream=None):
+    """The change mask packed one bit per pixel: int32 [n*h*w/32] (bit p % 32 of
+    word p / 32 for pixel p); also the uint8 [n, h, w] mask when `mask` is given
+    (a tensor to fill).  w must be a multiple of 32."""
+    _dev(a_orig, a_edit, bits, mask)
+    if a_orig.shape != a_edit.shape or a_orig.dtype != a_edit.dtype or a_orig.dim() != 4:
+        raise ValueError("a_orig and a_edit must be NHWC tensors of one shape and dtype")
+    n, h, w, c = a_orig.shape
+    if bits is None:
+        bits = torch.empty((max(n * h * w // 32, 1),), dtype=torch.int32, device=a_orig.device)
+    rc = lib().sige_diff_mask_bits(_p(a_orig), _p(a_edit), _dt(a_orig), n, h, w, c, ctypes.c_float(thresh),
+                                   _p(mask), _p(bits), _stream(stream))
+    _check(rc, "sige_diff_mask_bits")
+    return bits
+
+
+def sige_reduce_bits(bits, mask_h, mask_w, g: Geom, dilate_blocks=1, idx=None, count=None, stream=None):
+    """sige_reduce_mask on a mask packed as sige_diff_mask_bits writes it (mask_h x mask_w per image)."""
+    _dev(bits, idx, count)
+    cap = sige_max_blocks(g)
+    dev = bits.device
+    if idx is None:
+        idx = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((1,), dtype=torch.int32, device=dev)
+    rc = lib().sige_reduce_bits(_p(bits), mask_h, mask_w, ctypes.byref(g), dilate_blocks, _p(idx), _p(count),
+                                _stream(stream))
+    _check(rc, "sige_reduce_bits")
+    return idx, count
+
+
+def sige_reduce_bits_copy(bits, mask_h, mask_w, g: Geom, dilate_blocks, cached, out=None, idx=None, count=None,
+                          stream=None):
+    """sige_reduce_bits with `cached` copied into `out` by the same launch; returns (idx, count, out)."""
+    _dev(bits, idx, count, cached, out)
+    cap = sige_max_blocks(g)
+    dev = bits.device
+    if idx is None:
+        idx = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((1,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(cached)
+    rc = lib().sige_reduce_bits_copy(_p(bits), mask_h, mask_w, ctypes.byref(g), dilate_blocks, _p(idx), _p(count),
+                                     _dt(cached), _p(cached), _p(out), _stream(stream))
+    _check(rc, "sige_reduce_bits_copy")
+    return idx, count, out
 
 
 def sige_reduce_mask(mask, g: Geom, dilate_blocks=1, idx=None, count=None, stream=None):

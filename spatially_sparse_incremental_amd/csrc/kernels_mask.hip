@@ -15,23 +15,26 @@ namespace sige {
 // A 64-lane wave handles 16 pixels: four 16-lane groups, each reading one pixel's
 // channel row in 16-byte vectors (1 KiB contiguous per wave and load), four
 // pixels per group issued before any compare.  The per-pixel OR over the 16
-// lanes of a group is one __ballot; the group leader writes 4 mask bytes at once.
+// lanes of a group is one __ballot; the group leader writes 4 mask bytes at
+// once, and lane 0 the wave's 16 bits of the packed mask when one is asked for.
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void k_diff(const uint8_t *__restrict__ ao, const uint8_t *__restrict__ ae,
-                                              long npix, int vpp, float tau, uint8_t *__restrict__ mask) {
-    diff16<DT>(ao, ae, npix, vpp, tau, mask, (long)blockIdx.x * 4 + (threadIdx.x >> 6));
+                                              long npix, int vpp, float tau, uint8_t *__restrict__ mask,
+                                              uint16_t *__restrict__ bits) {
+    diff16<DT>(ao, ae, npix, vpp, tau, mask, bits, (long)blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
 hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix, int vpp, float tau,
-                       uint8_t *mask, hipStream_t st) {
+                       uint8_t *mask, uint32_t *bits, hipStream_t st) {
     const long waves = (npix + 15) / 16;
     const unsigned grid = (unsigned)((waves + 3) / 4);
     const uint8_t *ao = (const uint8_t *)a_orig, *ae = (const uint8_t *)a_edit;
+    uint16_t *b16 = (uint16_t *)bits;
     switch (dt) {
-    case 0: hipLaunchKernelGGL(k_diff<0>, dim3(grid), dim3(256), 0, st, ao, ae, npix, vpp, tau, mask); break;
-    case 1: hipLaunchKernelGGL(k_diff<1>, dim3(grid), dim3(256), 0, st, ao, ae, npix, vpp, tau, mask); break;
-    default: hipLaunchKernelGGL(k_diff<2>, dim3(grid), dim3(256), 0, st, ao, ae, npix, vpp, tau, mask); break;
+    case 0: hipLaunchKernelGGL(k_diff<0>, dim3(grid), dim3(256), 0, st, ao, ae, npix, vpp, tau, mask, b16); break;
+    case 1: hipLaunchKernelGGL(k_diff<1>, dim3(grid), dim3(256), 0, st, ao, ae, npix, vpp, tau, mask, b16); break;
+    default: hipLaunchKernelGGL(k_diff<2>, dim3(grid), dim3(256), 0, st, ao, ae, npix, vpp, tau, mask, b16); break;
     }
     return hipGetLastError();
 }
@@ -68,9 +71,22 @@ __global__ __launch_bounds__(256) void k_activity(const uint8_t *__restrict__ ma
     for (int q = tid; q < WW; q += 256) colbits[q] = 0u;
     __syncthreads();
     const int pr0 = max(0, i * bs - g.p), pr1 = min(H, i * bs - g.p + g.ib);
-    const uint8_t *m = mask + ((size_t)n * hm + (size_t)pr0 * fy) * wm;
+    const size_t pix0 = ((size_t)n * hm + (size_t)pr0 * fy) * wm;  // first pixel of the band
+    const uint8_t *m = mask + (vec16 == 2 ? pix0 / 8 : pix0);
     const int rows = (pr1 - pr0) * fy;
-    if (vec16) {
+    if (vec16 == 2) {  // a bitset (wm a multiple of 32)
+        const uint32_t *mb = (const uint32_t *)m;
+        const int wpr = wm >> 5, nv = rows * wpr;
+        const uint32_t m_fx = fast_div_magic(fx);
+        for (int v0 = tid; v0 < nv; v0 += U * 256) {
+            uint32_t d[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) d[u] = (v0 + u * 256 < nv) ? mb[v0 + u * 256] : 0u;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (d[u]) pool_word(colbits, d[u], ((v0 + u * 256) % wpr) * 32, fx, m_fx);
+        }
+    } else if (vec16) {
         const int vpr = wm >> 4;
         const int nv = rows * vpr;
         for (int v0 = tid; v0 < nv; v0 += U * 256) {
@@ -214,10 +230,11 @@ hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int 
     const int WW = (g.w + 31) / 32;
     // the one-launch path divides with 31-bit multipliers: every dividend * divisor < 2^31
     const long lim = 1L << 31;
-    const bool exact = (vec16 ? (long)hm * (wm / 16) * (wm / 16) : (long)hm * wm * wm) < lim &&
-                       (long)hm * fy < lim && (long)wm * fx < lim;
+    const int vdiv = vec16 == 2 ? wm / 32 : vec16 ? wm / 16 : 1;  // bitset words or 16-byte vectors per row
+    const bool exact = (vec16 ? (long)hm * vdiv * vdiv : (long)hm * wm * wm) < lim && (long)hm * fy < lim &&
+                       (long)wm * fx < lim;
     if (exact && (long)g.h * WW <= kReduceBitsWords && g.nby * g.nbx <= kReduceMaxBlocks) {
-        RedCfg rc{vec16 ? fast_div_magic(wm / 16) : 1u, fast_div_magic(wm), fast_div_magic(fy), fast_div_magic(fx),
+        RedCfg rc{fast_div_magic(vdiv), fast_div_magic(wm), fast_div_magic(fy), fast_div_magic(fx),
                   fast_div_magic(g.nbx)};
         hipLaunchKernelGGL(k_reduce_one, dim3(1 + ncopy), dim3(1024), 0, st, mask, hm, wm, fy, fx, g, dilate, vec16,
                            rc, idx, count, cp);

@@ -37,10 +37,13 @@ __device__ __forceinline__ bool vec_differs(u32x4 x, u32x4 y, float tau) {
 // reading one pixel's channel row in 16-byte vectors (1 KiB contiguous per
 // wave and load), four pixels per group issued before any compare.  The
 // per-pixel OR over the 16 lanes of a group is one __ballot; the group leader
-// writes 4 mask bytes at once.
+// writes 4 mask bytes at once (mask not NULL), and lane 0 writes the wave's 16
+// pixels as one 16-bit half of a bitset word (bits not NULL; bit p % 32 of word
+// p / 32 for pixel p, npix a multiple of 16).
 template <int DT>
 __device__ __forceinline__ void diff16(const uint8_t *__restrict__ ao, const uint8_t *__restrict__ ae, long npix,
-                                           int vpp, float tau, uint8_t *__restrict__ mask, long wave) {
+                                       int vpp, float tau, uint8_t *__restrict__ mask, uint16_t *__restrict__ bits,
+                                       long wave) {
     const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
     const long p0 = wave * 16 + sub * 4;  // this group's 4 consecutive pixels
     bool flag[4] = {false, false, false, false};
@@ -59,13 +62,17 @@ __device__ __forceinline__ void diff16(const uint8_t *__restrict__ ao, const uin
 #pragma unroll
         for (int u = 0; u < 4; ++u) flag[u] |= vec_differs<DT>(x[u], y[u], tau);
     }
-    uint32_t word = 0;
+    uint32_t word = 0, half = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const unsigned long long bal = __ballot(flag[u]);
         if ((bal >> (sub * 16)) & 0xFFFFull) word |= 1u << (8 * u);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+            if ((bal >> (gq * 16)) & 0xFFFFull) half |= 1u << (gq * 4 + u);
     }
-    if (li == 0 && p0 < npix) {
+    if (bits && lane == 0 && wave * 16 < npix) bits[wave] = (uint16_t)half;
+    if (mask && li == 0 && p0 < npix) {
         if (p0 + 3 < npix) {
             *(uint32_t *)(mask + p0) = word;
         } else {
@@ -115,8 +122,32 @@ __device__ __forceinline__ int compact_round(bool on, int q_out, int running, in
     return running + tot;
 }
 
+// OR the 32 pixels of one bitset word (columns x0 .. x0 + 31 of a row, x0 a
+// multiple of 32) into the bit row `row`, pooled by fx along x (m_fx its
+// multiplier).
+__device__ __forceinline__ void pool_word(uint32_t *row, uint32_t v, int x0, int fx, uint32_t m_fx) {
+    if (fx == 1) {
+        atomicOr(&row[x0 >> 5], v);
+        return;
+    }
+    const int wlo = fdiv31(x0, m_fx) >> 5;
+    uint32_t m0 = 0u, m1 = 0u;
+    while (v) {
+        const int i = __builtin_ctz(v);
+        v &= v - 1u;
+        const int xp = fdiv31(x0 + i, m_fx);
+        if ((xp >> 5) == wlo) m0 |= 1u << (xp & 31);
+        else m1 |= 1u << (xp & 31);
+    }
+    if (m0) atomicOr(&row[wlo], m0);
+    if (m1) atomicOr(&row[wlo + 1], m1);
+}
+
 // One image's mask m [hm, wm], OR-pooled by (fy, fx), as bit rows in LDS:
 // bits[y * ceil(w / 32) + x / 32] bit x % 32 for the pooled pixel (y, x).
+// Input modes: bytes (vec16 0), bytes read as 16-byte vectors (1), or a bitset
+// (2: bit x % 32 of word (y * wm + x) / 32, wm a multiple of 32; rc.m_vpr is
+// then the multiplier of wm / 32).
 template <int NTHR>
 __device__ __forceinline__ void mask_to_bits(const uint8_t *__restrict__ m, int hm, int wm, int fy, int fx,
                                              const Geo &g, int vec16, const RedCfg &rc, uint32_t *bits) {
@@ -125,7 +156,22 @@ __device__ __forceinline__ void mask_to_bits(const uint8_t *__restrict__ m, int 
     const int H = g.h, WW = (g.w + 31) >> 5;
     for (int q = tid; q < H * WW; q += NTHR) bits[q] = 0u;
     __syncthreads();
-    if (vec16) {
+    if (vec16 == 2) {
+        const uint32_t *mb = (const uint32_t *)m;
+        const int wpr = wm >> 5, nv = hm * wpr;
+        for (int v0 = tid; v0 < nv; v0 += U * NTHR) {
+            uint32_t d[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) d[u] = (v0 + u * NTHR < nv) ? mb[v0 + u * NTHR] : 0u;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!d[u]) continue;
+                const int v = v0 + u * NTHR;
+                const int Y = fdiv31(v, rc.m_vpr), q = v - Y * wpr;
+                pool_word(bits + fdiv31(Y, rc.m_fy) * WW, d[u], q * 32, fx, rc.m_fx);
+            }
+        }
+    } else if (vec16) {
         const int vpr = wm >> 4, nv = hm * vpr;
         for (int v0 = tid; v0 < nv; v0 += U * NTHR) {
             u32x4 d[U];
@@ -252,8 +298,9 @@ __device__ int reduce_list(const uint8_t *__restrict__ mask, int hm, int wm, int
                            int vec16, const RedCfg &rc, uint32_t *bits, uint8_t *scratch, int *wcnt,
                            int32_t *out) {
     int running = 0;
+    const size_t istride = vec16 == 2 ? (size_t)hm * wm / 8 : (size_t)hm * wm;  // bytes per image
     for (int n = 0; n < g.n; ++n) {
-        mask_to_bits<NTHR>(mask + (size_t)n * hm * wm, hm, wm, fy, fx, g, vec16, rc, bits);
+        mask_to_bits<NTHR>(mask + (size_t)n * istride, hm, wm, fy, fx, g, vec16, rc, bits);
         running = bits_to_list<NTHR>(g, dil, rc, bits, scratch, wcnt, out, n, running);
     }
     return running;

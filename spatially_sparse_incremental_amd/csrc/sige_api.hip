@@ -256,12 +256,18 @@ int64_t attn_ws_bytes(const Geo &g, int heads, int grid1) {
     return (int64_t)items * sige::kAttnWsBytesPerItem;
 }
 
+// bitset: the mask as one bit per pixel (bit p % 32 of word p / 32), mask_w a
+// multiple of 32
 int reduce_common(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks, int32_t *idx,
-                  int32_t *count, int dtype, const void *cached, void *out, void *stream, const char *what) {
+                  int32_t *count, int dtype, const void *cached, void *out, void *stream, const char *what,
+                  int bitset = 0) {
     Geo g;
     int rc = derive(gp, &g);
     if (rc) return rc;
     if (!mask || !idx || !count) return fail(SIGE_EINVAL, "NULL pointer");
+    if (bitset && (mask_w % 32 || !aligned(mask, 4)))
+        return fail(mask_w % 32 ? SIGE_EINVAL : SIGE_EALIGN, "bitset mask: width %d must be a multiple of 32 and "
+                    "the words 4-byte aligned", mask_w);
     if (mask_h < g.h || mask_w < g.w || mask_h % g.h || mask_w % g.w)
         return fail(SIGE_EINVAL, "mask %dx%d is not an integer multiple of the conv input %dx%d", mask_h, mask_w,
                     g.h, g.w);
@@ -271,7 +277,7 @@ int reduce_common(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *
     if (g.cap > sige::kReduceMaxBlocks)
         return fail(SIGE_ERANGE, "%d blocks (n*nby*nbx) exceed the reduce limit %d", g.cap, sige::kReduceMaxBlocks);
     if (!aligned(idx, 4) || !aligned(count, 4)) return fail(SIGE_EALIGN, "idx/count must be 4-byte aligned");
-    const size_t mbytes = (size_t)g.n * mask_h * mask_w;
+    const size_t mbytes = (size_t)g.n * mask_h * mask_w / (bitset ? 8 : 1);
     if (overlap(idx, (size_t)g.cap * 4, mask, mbytes) || overlap(count, 4, mask, mbytes) ||
         overlap(count, 4, idx, (size_t)g.cap * 4))
         return fail(SIGE_EINVAL, "idx, count and mask must not overlap");
@@ -288,7 +294,7 @@ int reduce_common(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *
         cp = sige::ReduceCopy{(const uint8_t *)cached, (uint8_t *)out, (long long)(obytes / 16)};
     }
     if ((rc = device_ready())) return rc;
-    const int vec16 = (mask_w % 16 == 0) && aligned(mask, 16);
+    const int vec16 = bitset ? 2 : (mask_w % 16 == 0) && aligned(mask, 16);
     static int copy_wgs = -1;  // SIGE_REDUCE_COPY_WGS overrides the copy's workgroups (tuning)
     if (copy_wgs < 0) {
         const char *v = getenv("SIGE_REDUCE_COPY_WGS");
@@ -342,28 +348,38 @@ int64_t sige_max_blocks(const sige_geom *g) {
     return (int64_t)d.cap;
 }
 
-int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
-                   uint8_t *mask, void *stream) {
+int sige_diff_mask_bits(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
+                        uint8_t *mask, uint32_t *bits, void *stream) {
+    const char *what = bits ? "sige_diff_mask_bits" : "sige_diff_mask";
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
     if (n < 0 || h < 0 || w < 0 || c < 1) return fail(SIGE_EINVAL, "bad shape n=%d h=%d w=%d c=%d", n, h, w, c);
     if (!(thresh >= 0.0f) || thresh > 3.0e38f) return fail(SIGE_EINVAL, "threshold must be finite and >= 0");
+    if (bits && w % 32) return fail(SIGE_EINVAL, "bitset mask: width %d must be a multiple of 32", w);
     const long npix = (long)n * h * w;
     if (npix == 0) {
         g_msg[0] = 0;
         return SIGE_OK;
     }
-    if (!a_orig || !a_edit || !mask) return fail(SIGE_EINVAL, "NULL tensor pointer");
+    if (!a_orig || !a_edit || (!mask && !bits)) return fail(SIGE_EINVAL, "NULL tensor pointer");
     int rc = channel_rows_ok(dtype, c, "c");
     if (rc) return rc;
     if (!aligned(a_orig, 16) || !aligned(a_edit, 16)) return fail(SIGE_EALIGN, "activations must be 16-byte aligned");
-    if (!aligned(mask, 4)) return fail(SIGE_EALIGN, "mask must be 4-byte aligned");
+    if (!aligned(mask, 4) || !aligned(bits, 4)) return fail(SIGE_EALIGN, "mask and bits must be 4-byte aligned");
     const size_t bytes = (size_t)npix * c * sige::elem_bytes(dtype);
-    if (overlap(mask, (size_t)npix, a_orig, bytes) || overlap(mask, (size_t)npix, a_edit, bytes))
+    if (mask && (overlap(mask, (size_t)npix, a_orig, bytes) || overlap(mask, (size_t)npix, a_edit, bytes)))
         return fail(SIGE_EINVAL, "mask overlaps an input");
+    if (bits && (overlap(bits, (size_t)npix / 8, a_orig, bytes) || overlap(bits, (size_t)npix / 8, a_edit, bytes) ||
+                 (mask && overlap(bits, (size_t)npix / 8, mask, (size_t)npix))))
+        return fail(SIGE_EINVAL, "bits overlap an input or the mask");
     if ((rc = device_ready())) return rc;
     const int vpp = c * sige::elem_bytes(dtype) / 16;
-    return finish(sige::launch_diff(dtype, a_orig, a_edit, npix, vpp, thresh, mask, (hipStream_t)stream),
-                  "sige_diff_mask", (hipStream_t)stream);
+    return finish(sige::launch_diff(dtype, a_orig, a_edit, npix, vpp, thresh, mask, bits, (hipStream_t)stream), what,
+                  (hipStream_t)stream);
+}
+
+int sige_diff_mask(const void *a_orig, const void *a_edit, int dtype, int n, int h, int w, int c, float thresh,
+                   uint8_t *mask, void *stream) {
+    return sige_diff_mask_bits(a_orig, a_edit, dtype, n, h, w, c, thresh, mask, nullptr, stream);
 }
 
 
@@ -371,6 +387,19 @@ int sige_reduce_mask(const uint8_t *mask, int mask_h, int mask_w, const sige_geo
                      int32_t *idx, int32_t *count, void *stream) {
     return reduce_common(mask, mask_h, mask_w, gp, dilate_blocks, idx, count, 0, nullptr, nullptr, stream,
                          "sige_reduce_mask");
+}
+
+int sige_reduce_bits(const uint32_t *bits, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,
+                     int32_t *idx, int32_t *count, void *stream) {
+    return reduce_common((const uint8_t *)bits, mask_h, mask_w, gp, dilate_blocks, idx, count, 0, nullptr, nullptr,
+                         stream, "sige_reduce_bits", 1);
+}
+
+int sige_reduce_bits_copy(const uint32_t *bits, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,
+                          int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream) {
+    if (!out) return fail(SIGE_EINVAL, "NULL pointer");
+    return reduce_common((const uint8_t *)bits, mask_h, mask_w, gp, dilate_blocks, idx, count, dtype, cached, out,
+                         stream, "sige_reduce_bits_copy", 1);
 }
 
 int sige_reduce_mask_copy(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,

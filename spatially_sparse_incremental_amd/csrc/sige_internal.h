@@ -51,7 +51,7 @@ struct CopyCfg {
 };
 
 hipError_t launch_diff(int dt, const void *a_orig, const void *a_edit, long npix, int vpp, float tau,
-                       uint8_t *mask, hipStream_t st);
+                       uint8_t *mask, uint32_t *bits, hipStream_t st);
 // An unconditional copy of nvec 16-byte vectors from src to dst, done by extra
 // workgroups of the reduce launch (nvec 0: none).
 struct ReduceCopy {
@@ -59,6 +59,8 @@ struct ReduceCopy {
     uint8_t *dst;
     long long nvec;
 };
+// vec16: the mask as bytes (0), bytes read in 16-byte vectors (1), or a bitset
+// (2: bit p % 32 of 32-bit word p / 32 for pixel p, wm a multiple of 32)
 hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
                          int32_t *count, const ReduceCopy &cp, int copy_wgs, hipStream_t st);
 hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t *idx, const int32_t *count,

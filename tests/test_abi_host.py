@@ -86,6 +86,29 @@ def test_diff_validation(lib):
     assert lib.sige_last_error() == b""
 
 
+def test_bitset_validation(lib):
+    s = _v(0)
+    f = lib.sige_diff_mask_bits
+    assert f(_v(A), _v(B), 1, 1, 4, 48, 8, ctypes.c_float(1e-6), _v(C), _v(D), s) == EINVAL  # w % 32
+    assert b"multiple of 32" in lib.sige_last_error()
+    assert f(_v(A), _v(B), 1, 1, 4, 32, 8, ctypes.c_float(1e-6), None, None, s) == EINVAL  # no output
+    assert f(_v(A), _v(B), 1, 1, 4, 32, 8, ctypes.c_float(1e-6), None, _v(D + 2), s) == EALIGN
+    assert f(_v(A), _v(B), 1, 1, 4, 32, 8, ctypes.c_float(1e-6), None, _v(A + 64), s) == EINVAL  # bits in a_orig
+    assert f(_v(A), _v(B), 1, 1, 4, 32, 8, ctypes.c_float(1e-6), _v(C), _v(C + 64), s) == EINVAL  # bits in mask
+    assert f(_v(A), _v(B), 7, 1, 4, 32, 8, ctypes.c_float(1e-6), None, _v(D), s) == EDTYPE
+    assert f(_v(A), _v(B), 1, 1, 4, 32, 8, ctypes.c_float(1e-6), None, _v(D), s) == ENODEV
+    g = _g()
+    r = lib.sige_reduce_bits
+    assert r(None, 256, 256, ctypes.byref(g), 1, _v(B), _v(C), s) == EINVAL
+    assert r(_v(A + 2), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), s) == EALIGN
+    odd = _g(h=16, w=40, b=4)
+    assert r(_v(A), 16, 40, ctypes.byref(odd), 1, _v(B), _v(C), s) == EINVAL  # mask width % 32
+    assert r(_v(A), 256, 256, ctypes.byref(g), 1, _v(A + 64), _v(C), s) == EINVAL  # idx inside the bits
+    rc = lib.sige_reduce_bits_copy
+    assert rc(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), 1, _v(D), None, s) == EINVAL
+    assert r(_v(A), 256, 256, ctypes.byref(g), 1, _v(B), _v(C), s) == ENODEV
+
+
 def test_reduce_validation(lib):
     f = lib.sige_reduce_mask
     s = _v(0)
