@@ -85,7 +85,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wl = synth.workload("cfg2_unet_bf16")
+    wl = synth.workload("unet_256x256x128_bf16")
     L = wl.layers[0]
     dt = synth.DTYPES[L.dtype]
     es = torch.tensor([], dtype=dt).element_size()
@@ -374,7 +374,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    # ---- algorithmic work (the design doc states these formulas)
+    # ---- algorithmic work: flops and bytes per listed block, per layer and per edit
     npix_in, npix_out = L.h * L.w, d.ho * d.wo
     b2 = L.block * L.block
     act_pix = int(_active_pixels(idx[:active].cpu().numpy(), d, L.block))
@@ -631,7 +631,7 @@ def _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     (k = 1 geometry, dilation 1) at 1.2% and 10% of the frame, against dense
     attention over all 4096 queries (torch scaled_dot_product_attention)."""
     dev = torch.device("cuda:0")
-    wl = synth.workload("cfg5_ldm_f16")
+    wl = synth.workload("ldm_64x64x320_f16")
     h = w = 64
     heads, d, b = 5, 64, 4
     g = ssi.geom(1, h, w, heads * d, heads * d, 1, 1, 0, b)
@@ -673,7 +673,7 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     blob edit: the single-range fused layer, the layer split over input channels
     and the dense conv (torch/MIOpen), each with the cache copy."""
     dev = torch.device("cuda:0")
-    wl = synth.workload("cfg5_ldm_f16")
+    wl = synth.workload("ldm_64x64x320_f16")
     L = [x for x in wl.layers if x.name == "l16_3x3"][0]
     a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
     a_e = synth.make_edit(a_o, synth.edit_shape(wl, seed).raster(L.h, L.w), wl.edit_kind, seed).to(dev)
@@ -702,13 +702,13 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
 
 
 def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
-    """The 12-conv U-Net chain (cfg3) at the 1.2% blob edit, as HIP graphs: one
+    """The 12-conv U-Net chain (256 to 32 pixels, 128 to 512 channels) at the 1.2% blob edit, as HIP graphs: one
     diff at 256x256 (the mask one bit per pixel), then per layer the reduce of
     the mask pooled to the layer's input with the cache copy on its idle
     workgroups, and the fused layer, layer l+1 reading layer l's output;
     against the same 12 convs dense through torch/MIOpen."""
     dev = torch.device("cuda:0")
-    wl = synth.workload("cfg3_chain_bf16")
+    wl = synth.workload("unet_chain_12conv_bf16")
     first = wl.layers[0]
     m = synth.edit_shape(wl, seed).raster(first.h, first.w)
     a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed).to(dev)
@@ -755,12 +755,12 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
 
 
 def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
-    """The four GauGAN-shaped bf16 convs (cfg4) under the seeded star polygon at
+    """The four GauGAN-shaped bf16 convs (32x64x1024 to 256x512x256) under the seeded star polygon at
     0.5 / 1.2 / 5 / 15 / 30% of the frame: the reduce (mask one bit per pixel,
     the cache copy on its idle workgroups) + the faster of the fused layer and
     its split per layer, against the dense conv through torch/MIOpen."""
     dev = torch.device("cuda:0")
-    wl = synth.workload("cfg4_gaugan_bf16")
+    wl = synth.workload("gaugan_4conv_bf16")
     res, dense = {}, {}
     prep = []
     for li, L in enumerate(wl.layers):

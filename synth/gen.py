@@ -261,29 +261,29 @@ def _chain_layers():
 
 
 WORKLOADS = {
-    "cfg1_rect_f32": Workload(
-        "cfg1_rect_f32",
+    "rect_64x64x64_f32": Workload(
+        "rect_64x64x64_f32",
         "3x3 s1 p1 conv, fp32, NCHW 1x64x64x64 -> 64; 10x12 rectangle edit; 8x8 output blocks",
         (LayerSpec("conv", 64, 64, 64, 64, 3, 1, 1, 8, 0, "f32", 0.05),),
         edit="rect", area=120 / 4096, edit_kind="add", layout="NCHW", mask_hw=(64, 64)),
-    "cfg2_unet_bf16": Workload(
-        "cfg2_unet_bf16",
+    "unet_256x256x128_bf16": Workload(
+        "unet_256x256x128_bf16",
         "U-Net-shaped 3x3 s1 conv, bf16 NHWC 1x256x256x128 -> 128; 1.2% blob; 6x6 blocks, dilate 1",
         (LayerSpec("conv", 256, 256, 128, 128, 3, 1, 1, 6, 1, "bf16"),)),
-    "cfg3_chain_bf16": Workload(
-        "cfg3_chain_bf16",
+    "unet_chain_12conv_bf16": Workload(
+        "unet_chain_12conv_bf16",
         "U-Net conv chain 256/128/64/32 x 128/256/256/512, bf16; mask pooled per scale",
         _chain_layers(), chain=True),
-    "cfg4_gaugan_bf16": Workload(
-        "cfg4_gaugan_bf16",
+    "gaugan_4conv_bf16": Workload(
+        "gaugan_4conv_bf16",
         "GauGAN-like standalone 3x3 convs, bf16, 1.2% polygon (area sweep 0.5-30%)",
         (LayerSpec("g32x64", 32, 64, 1024, 1024, 3, 1, 1, 4, 1),
          LayerSpec("g64x128", 64, 128, 1024, 512, 3, 1, 1, 4, 1),
          LayerSpec("g128x256", 128, 256, 512, 256, 3, 1, 1, 6, 1),
          LayerSpec("g256x512", 256, 512, 256, 128, 3, 1, 1, 6, 1)),
         edit="polygon", mask_hw=(256, 512)),
-    "cfg5_ldm_f16": Workload(
-        "cfg5_ldm_f16",
+    "ldm_64x64x320_f16": Workload(
+        "ldm_64x64x320_f16",
         "latent-diffusion-shaped 3x3 and 1x1 convs, fp16, 64^2x320 / 32^2x640 / 16^2x1280",
         (LayerSpec("l64_3x3", 64, 64, 320, 320, 3, 1, 1, 4, 1, "f16"),
          LayerSpec("l64_1x1", 64, 64, 320, 320, 1, 1, 0, 4, 1, "f16"),
@@ -305,15 +305,15 @@ def _sweep_points():
     diffusion 3x3 layers at the low resolutions (32x32, 16x16) where only
     1-2 pixel blocks keep the update sparse."""
     pts = []
-    base = WORKLOADS["cfg2_unet_bf16"].layers[0]
+    base = WORKLOADS["unet_256x256x128_bf16"].layers[0]
     for b in (2, 4, 6, 8, 12, 16):
         for d in (0, 1, 2):
-            pts.append(("cfg2_unet_bf16", dataclasses.replace(base, name=f"unet_b{b}_d{d}", block=b, dilate=d)))
+            pts.append(("unet_256x256x128_bf16", dataclasses.replace(base, name=f"unet_b{b}_d{d}", block=b, dilate=d)))
     for lname, blocks in (("l32_3x3", (1, 2, 4, 8)), ("l16_3x3", (1, 2, 4))):
-        lay = next(x for x in WORKLOADS["cfg5_ldm_f16"].layers if x.name == lname)
+        lay = next(x for x in WORKLOADS["ldm_64x64x320_f16"].layers if x.name == lname)
         for b in blocks:
             for d in (0, 1):
-                pts.append(("cfg5_ldm_f16", dataclasses.replace(lay, name=f"{lname}_b{b}_d{d}", block=b, dilate=d)))
+                pts.append(("ldm_64x64x320_f16", dataclasses.replace(lay, name=f"{lname}_b{b}_d{d}", block=b, dilate=d)))
     return tuple(pts)
 
 

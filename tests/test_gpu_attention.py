@@ -97,7 +97,7 @@ def test_attention_latent_diffusion_shape_with_a_blob_edit():
     # 64x64 tokens, 5 heads of 64, fp16; query blocks of 4x4 tokens from the diff of
     # a 1.2% blob edit (k = 1 geometry, dilation 1), every listed token checked on a
     # sample of blocks against the oracle, the pruned tokens bit for bit
-    wl = synth.workload("cfg5_ldm_f16")
+    wl = synth.workload("ldm_64x64x320_f16")
     h = w = 64
     heads, b, dt = 5, 4, torch.float16
     m = synth.edit_shape(wl, 3).raster(h, w)

@@ -46,7 +46,7 @@ def test_crop_conv_equals_dense_edited_conv(dt, k, s, p, b):
 
 
 def test_bbox_rectangle_through_the_tile_path_on_the_unet_layer():
-    wl = synth.workload("cfg2_unet_bf16")
+    wl = synth.workload("unet_256x256x128_bf16")
     L = wl.layers[0]
     a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 1)
     a_e = synth.make_edit(a_o, synth.edit_shape(wl, 1).raster(L.h, L.w), wl.edit_kind, 1)

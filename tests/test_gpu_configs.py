@@ -25,8 +25,8 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def test_cfg1_rectangle_fp32_nchw():
-    wl = synth.workload("cfg1_rect_f32")
+def test_rectangle_64x64x64_fp32_nchw():
+    wl = synth.workload("rect_64x64x64_f32")
     L = wl.layers[0]
     for seed in range(4):
         m, _ = synth.rectangle_mask(seed, L.h, L.w)
@@ -52,8 +52,8 @@ def test_cfg1_rectangle_fp32_nchw():
 
 
 @pytest.mark.parametrize("seed", [1, 2])
-def test_cfg2_unet_layer_full(seed):
-    wl = synth.workload("cfg2_unet_bf16")
+def test_unet256_layer_full(seed):
+    wl = synth.workload("unet_256x256x128_bf16")
     L = wl.layers[0]
     m = synth.edit_shape(wl, seed).raster(L.h, L.w)
     a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
@@ -75,8 +75,8 @@ def test_cfg2_unet_layer_full(seed):
     assert 40 <= idx.numel() <= 130  # 1.2% blob, 6x6 blocks, dilation 1
 
 
-def test_cfg3_chain_layerwise():
-    wl = synth.workload("cfg3_chain_bf16")
+def test_unet_chain_12conv_layerwise():
+    wl = synth.workload("unet_chain_12conv_bf16")
     seed = 3
     first = wl.layers[0]
     m = synth.edit_shape(wl, seed).raster(first.h, first.w)
@@ -95,8 +95,8 @@ def test_cfg3_chain_layerwise():
 
 
 @pytest.mark.parametrize("area", [0.005, 0.012, 0.05, 0.15, 0.30])
-def test_cfg4_gaugan_layers(area):
-    wl = synth.workload("cfg4_gaugan_bf16")
+def test_gaugan_4conv_layers(area):
+    wl = synth.workload("gaugan_4conv_bf16")
     seed = 4
     shape = synth.edit_shape(wl, seed, area)
     for li, L in enumerate(wl.layers):
@@ -111,8 +111,8 @@ def test_cfg4_gaugan_layers(area):
 
 
 @pytest.mark.parametrize("area", [0.012, 0.10])
-def test_cfg5_latent_diffusion_layers(area):
-    wl = synth.workload("cfg5_ldm_f16")
+def test_latent_diffusion_layers(area):
+    wl = synth.workload("ldm_64x64x320_f16")
     seed = 5
     shape = synth.edit_shape(wl, seed, area)
     for li, L in enumerate(wl.layers):
@@ -126,8 +126,8 @@ def test_cfg5_latent_diffusion_layers(area):
         check_layer_sampled(f"ldm {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
 
 
-def test_cfg2_three_call_path_matches_fused_at_full_size():
-    wl = synth.workload("cfg2_unet_bf16")
+def test_unet256_three_call_path_matches_fused_at_full_size():
+    wl = synth.workload("unet_256x256x128_bf16")
     L = wl.layers[0]
     seed = 7
     m = synth.edit_shape(wl, seed).raster(L.h, L.w)

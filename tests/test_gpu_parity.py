@@ -25,7 +25,7 @@ def _need_gpu():
 
 # (name, n, h, w, cin, cout, k, s, p, b, dtype, dilate, edit fraction)
 CASES = [
-    ("cfg1_shape_f32", 1, 64, 64, 64, 64, 3, 1, 1, 8, "f32", 0, 0.01),
+    ("rect_64x64x64_shape_f32", 1, 64, 64, 64, 64, 3, 1, 1, 8, "f32", 0, 0.01),
     ("ragged_bf16", 2, 13, 17, 40, 24, 3, 1, 1, 4, "bf16", 1, 0.02),
     ("stride2_f16", 1, 30, 26, 32, 48, 3, 2, 1, 3, "f16", 1, 0.02),
     ("pointwise_f16", 1, 20, 20, 320, 64, 1, 1, 0, 4, "f16", 1, 0.02),

@@ -108,7 +108,7 @@ def test_sequence_of_edits_through_a_persistent_buffer(mode):
 def test_unet_layer_alternating_edits_full_size(one_call):
     # the 256x256x128 bf16 layer: two blob edits alternate through one persistent
     # buffer; each step must equal the copy_cached = 1 result bit for bit
-    wl = synth.workload("cfg2_unet_bf16")
+    wl = synth.workload("unet_256x256x128_bf16")
     L = wl.layers[0]
     a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 1)
     edits = [synth.make_edit(a_o, synth.edit_shape(wl, sd).raster(L.h, L.w), wl.edit_kind, sd).cuda()

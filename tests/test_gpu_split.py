@@ -36,14 +36,14 @@ def _split_full(a_e, wt, bias, cache, L, mask):
     return out, idx[:int(cnt.item())].cpu()
 
 
-LDM = [L for L in synth.workload("cfg5_ldm_f16").layers if L.h <= 32]
-LOWRES = [L for w, L in synth.SWEEP if w == "cfg5_ldm_f16"]
+LDM = [L for L in synth.workload("ldm_64x64x320_f16").layers if L.h <= 32]
+LOWRES = [L for w, L in synth.SWEEP if w == "ldm_64x64x320_f16"]
 
 
 @pytest.mark.parametrize("area", [0.012, 0.10])
 @pytest.mark.parametrize("L", LDM, ids=[L.name for L in LDM])
 def test_split_ldm_layers(L, area):
-    wl = synth.workload("cfg5_ldm_f16")
+    wl = synth.workload("ldm_64x64x320_f16")
     seed = 3
     m = synth.edit_shape(wl, seed, area).raster(L.h, L.w)
     a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
@@ -58,7 +58,7 @@ def test_split_ldm_layers(L, area):
 
 @pytest.mark.parametrize("L", LOWRES, ids=[L.name for L in LOWRES])
 def test_split_sweep_points(L):
-    wl = synth.workload("cfg5_ldm_f16")
+    wl = synth.workload("ldm_64x64x320_f16")
     seed = 9
     m = synth.edit_shape(wl, seed).raster(L.h, L.w)
     a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed)
@@ -181,7 +181,7 @@ def test_split_graph_replays_match_eager():
 def test_split_gaugan_layers(area):
     # the four GauGAN-shaped bf16 convs (18.9 MB of weights at 32x64x1024): list and
     # untouched pixels bit for bit, sampled blocks against the oracle
-    wl = synth.workload("cfg4_gaugan_bf16")
+    wl = synth.workload("gaugan_4conv_bf16")
     seed = 6
     shape = synth.edit_shape(wl, seed, area)
     for li, L in enumerate(wl.layers):

@@ -99,7 +99,7 @@ def test_diff_small_bf16_change_is_seen():
     assert oracle.diff_mask(a_o, a_e).tolist() == [[[0, 1]]]
 
 
-@pytest.mark.parametrize("name", ["cfg1_rect_f32", "cfg2_unet_bf16"])
+@pytest.mark.parametrize("name", ["rect_64x64x64_f32", "unet_256x256x128_bf16"])
 def test_diff_recovers_generated_edit_region(name):
     # the generator changes every channel of exactly the masked pixels
     wl = synth.workload(name)
