@@ -212,9 +212,17 @@ def main():
         "fused_layer": graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g,
                                                                      out=out, copy_cached=False)),
     }
-    print(f"[bench] kernels {kt}", file=sys.stderr, flush=True)
+    # the three-call path's kernels on the same list (separate launches, block tensors in HBM)
+    blocks = torch.empty((cap, d.ib, d.ib, L.c_in), dtype=dt, device=dev)
+    oblocks = torch.empty((cap, L.block, L.block, L.c_out), dtype=dt, device=dev)
+    out3 = torch.empty_like(cache)
+    t_gather = graph_time(lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks))
+    t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks))
+    t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
+    print(f"[bench] kernels {kt} gather {t_gather:.2f} conv_blocks {t_convb:.2f} scatter {t_scatter:.2f}",
+          file=sys.stderr, flush=True)
 
-    t_nocopy = t_three = t_gather = t_convb = t_scatter = t_fused_copy = t_dense_ours = t_dense_miopen = None
+    t_nocopy = t_three = t_fused_copy = t_dense_ours = t_dense_miopen = None
     t_reduce = t_step_conv_copy = t_step_bytes = t_reduce_bytes = None
     t_seq = t_seq2 = t_restore = t_bbox = t_bbox_tiles = attention = ldm_split = t_layer = None
     chain = gaugan = None
@@ -256,10 +264,6 @@ def main():
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False)
 
         # the three-call path
-        blocks = torch.empty((cap, d.ib, d.ib, L.c_in), dtype=dt, device=dev)
-        oblocks = torch.empty((cap, L.block, L.block, L.c_out), dtype=dt, device=dev)
-        out3 = torch.empty_like(cache)
-
         def step_three():
             ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
             ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
@@ -269,9 +273,6 @@ def main():
 
         t_nocopy = graph_time(step_nocopy, 5, 40)
         t_three = graph_time(step_three, 5, 40)
-        t_gather = graph_time(lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks))
-        t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks))
-        t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
         # dense comparators on the same GPU
         dense_all = torch.empty_like(cache)
         t_dense_ours = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx_all, cnt_all, g,
@@ -404,22 +405,30 @@ def main():
         "reduce_copy": dict(hbm(reduce_copy_bytes, kt["reduce_copy"]), note="reduce on one workgroup, the full "
                             "cache copy on the others"),
         "fused_layer": dict(hbm(conv_bytes, kt["fused_layer"]), **mfma(kt["fused_layer"])),
+        "gather": hbm(active * d.ib * d.ib * L.c_in * es * 2, t_gather),
+        "conv_blocks": dict(hbm(blk_bytes + w_bytes, t_convb), **mfma(t_convb)),
+        "scatter": hbm(active * b2 * L.c_out * es + act_pix * L.c_out * es + copy_bytes, t_scatter),
     }
     if not args.no_comparators:
         kernels.update({
             "reduce": dict(us=round(t_reduce, 3), bytes=int(reduce_bytes), bound="latency"),
             "fused_layer_with_copy": dict(hbm(conv_bytes + copy_bytes, t_fused_copy), **mfma(t_fused_copy)),
-            "gather": hbm(active * d.ib * d.ib * L.c_in * es * 2, t_gather),
-            "conv_blocks": dict(hbm(blk_bytes + w_bytes, t_convb), **mfma(t_convb)),
-            "scatter": hbm(active * b2 * L.c_out * es + act_pix * L.c_out * es + copy_bytes, t_scatter),
         })
+    # HBM bytes per launch read from the rocprofv3 counters (FETCH_SIZE and WRITE_SIZE,
+    # calibrated on a plain copy), while the sources they were taken on are unchanged
+    for name, tb in _measured_kernel_traffic().items():
+        if name in kernels:
+            us = kernels[name]["us"]
+            kernels[name]["traffic_bytes"] = tb
+            kernels[name]["traffic_gbps"] = round(tb / (us * 1e-6) / 1e9, 1)
+            kernels[name]["traffic_frac_hbm"] = round(tb / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
     # the roofline of the step's longest launch: the conv against the MFMA peak (it
     # is the contraction), the others against HBM
     dom = max(kt, key=lambda k: kt[k])
     if dom == "fused_layer":
         tf = conv_flops / (kt[dom] * 1e-6) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 2), "peak": peak_tf, "unit": "TFLOP/s",
-                    "frac": round(tf / peak_tf, 4), "traffic": _measured_traffic()}
+                    "frac": round(tf / peak_tf, 4), "traffic": _measured_kernel_traffic().get("fused_layer")}
     else:
         droof = kernels[dom]
         roofline = {"kernel": dom, "bound": "hbm", "achieved": droof["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -802,28 +811,31 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     return res
 
 
-KERNEL_SOURCES = ("kernels_conv.hip", "device_common.h", "sige_internal.h")
-
-
-def _measured_traffic():
-    """HBM bytes per fused-layer launch from the committed counter summary, or None
-    when the kernel source has changed since the counters were taken."""
+def _csrc_hash():
+    """sha256 over every file of the HIP sources, in name order."""
     import hashlib
 
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "spatially_sparse_incremental_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def _measured_kernel_traffic():
+    """HBM bytes per launch of each kernel of the step and of the three-call path,
+    from the committed counter summary; empty when any HIP source has changed
+    since the counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
-    summary = os.path.join(here, "profiles", "fused_layer_unet256_pmc_traffic.md")
-    csrc = os.path.join(here, "spatially_sparse_incremental_amd", "csrc")
+    summary = os.path.join(here, "profiles", "step_kernels_unet256_pmc_traffic.md")
     try:
         fields = dict(line.split(": ", 1) for line in open(summary).read().splitlines() if ": " in line)
-        h = hashlib.sha256()
-        for name in KERNEL_SOURCES:  # the conv kernel and the headers it includes
-            h.update(open(os.path.join(csrc, name), "rb").read())
-        current = h.hexdigest()
-        if fields.get("kernel_source_sha256", "").strip() == current:
-            return int(fields["traffic_bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
-        pass
-    return None
+        if fields.get("csrc_sha256", "").strip() != _csrc_hash():
+            return {}
+        return {k[len("traffic_bytes."):]: int(v) for k, v in fields.items() if k.startswith("traffic_bytes.")}
+    except (OSError, ValueError):
+        return {}
 
 
 def _active_pixels(idx, d, b):
