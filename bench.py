@@ -734,7 +734,7 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
                            out=torch.empty_like(cache), idx=torch.empty((d.cap,), dtype=torch.int32, device=dev),
                            cnt=torch.empty((1,), dtype=torch.int32, device=dev),
                            w_cl=w_cpu.to(dev).contiguous(memory_format=torch.channels_last),
-                           b16=b_cpu.to(dev).to(a_e.dtype)))
+                           b16=b_cpu.to(dev).to(a_e.dtype), mbits=mbits))
     blocks = []
 
     def sparse_chain():
@@ -755,12 +755,48 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
     sparse_chain()
     torch.cuda.synchronize()
     blocks = [int(ly["cnt"].item()) for ly in layers]
-    t_sparse = graph_time(sparse_chain, 2, 25)
+    t_single = graph_time(sparse_chain, 2, 25)
+    # per layer, the faster of the single-range layer and its split over input
+    # channels (each timed with its reduce, on the inputs and lists of the run above)
+    xs = [a_e] + [ly["out"] for ly in layers[:-1]]
+    for ly, x in zip(layers, xs):
+        ly["ws"] = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(ly["g"], a_e.dtype), dtype=torch.uint8,
+                               device=dev)
+        ly["split"] = False
+        t1 = graph_time(lambda: _chain_layer(ssi, ly, x, first), 5, 20)
+        ly["split"] = True
+        t2 = graph_time(lambda: _chain_layer(ssi, ly, x, first), 5, 20)
+        ly["split"] = t2 < t1
+
+    def chosen_chain():
+        ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+        x = a_e
+        for ly in layers:
+            _chain_layer(ssi, ly, x, first)
+            x = ly["out"]
+
+    t_sparse = graph_time(chosen_chain, 2, 25)
     with torch.no_grad():
         t_dense = graph_time(dense_chain, 1, 10)
     return {"sparse_us": round(t_sparse, 3), "dense_miopen_us": round(t_dense, 3),
             "speedup": round(t_dense / t_sparse, 2), "blocks_per_layer": blocks,
-            "note": "one diff + 12 x (reduce with the cache copy + fused layer); dense: 12 x F.conv2d; HIP graphs"}
+            "path_per_layer": ["split" if ly["split"] else "single" for ly in layers],
+            "sparse_single_range_only_us": round(t_single, 3),
+            "note": "one diff + 12 x (reduce with the cache copy + the faster of the fused layer and its split, "
+                    "chosen per layer); dense: 12 x F.conv2d; HIP graphs"}
+
+
+def _chain_layer(ssi, ly, x, first):
+    """One layer of the chain: the reduce with the cache copy, then the layer."""
+    mbits = ly["mbits"]
+    ssi.sige_reduce_bits_copy(mbits, first.h, first.w, ly["g"], ly["L"].dilate, ly["cache"], out=ly["out"],
+                              idx=ly["idx"], count=ly["cnt"])
+    if ly["split"]:
+        ssi.sige_sparse_conv_layer_split(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
+                                         out=ly["out"], copy_cached=False, workspace=ly["ws"])
+    else:
+        ssi.sige_sparse_conv_layer(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"], out=ly["out"],
+                                   copy_cached=False)
 
 
 def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):

@@ -195,3 +195,26 @@ def test_split_gaugan_layers(area):
         print(f"\n[case] gaugan split {L.name} area {area}: {idx.numel()} blocks", flush=True)
         check_layer_sampled(f"gaugan split {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L,
                             mask.cpu(), li)
+
+
+def test_split_unet_chain_12conv_layerwise():
+    """The split on every layer of the 12-conv U-Net chain (stride-1 and stride-2
+    layers, 128 to 512 channels), layer by layer as the chain runs: the bench
+    times the faster of the two layer kernels per layer of this chain."""
+    wl = synth.workload("unet_chain_12conv_bf16")
+    seed = 4
+    first = wl.layers[0]
+    m = synth.edit_shape(wl, seed).raster(first.h, first.w)
+    a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed)
+    a_e = synth.make_edit(a_o, m, wl.edit_kind, seed)
+    mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)  # one diff at 256x256, pooled per layer
+    x = a_e.cuda()
+    for li, L in enumerate(wl.layers):
+        wt, bias = synth.make_layer_tensors(L, seed * 100 + li)
+        ho, wo, _, _, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
+        cache = synth.make_activation(1, ho, wo, L.c_out, L.dtype, seed * 100 + li + 50)
+        out, idx = _split_full(x, wt, bias, cache.cuda(), L, mask)
+        print(f"\n[case] chain split {L.name}: {idx.numel()} blocks", flush=True)
+        check_layer_sampled(f"chain split {L.name}", x.cpu(), wt, bias, cache, out.cpu(), idx, L, mask.cpu(),
+                            seed + li)
+        x = out  # layer l+1 takes layer l's edited output
