@@ -232,8 +232,8 @@ def main():
         out_c = torch.empty_like(cache)
 
         def step_conv_copy():
-            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
-            ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+            ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count)
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g, out=out_c, copy_cached=True)
 
         t_step_conv_copy = graph_time(step_conv_copy, 5, 40)
@@ -259,14 +259,14 @@ def main():
         out_persist = cache.clone()
 
         def step_nocopy():
-            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
-            ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+            ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count)
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False)
 
         # the three-call path
         def step_three():
-            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
-            ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count)
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+            ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count)
             ssi.sige_gather(a_e, g, idx, count, blocks=blocks)
             ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks)
             ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)
@@ -308,12 +308,12 @@ def main():
         seq_idx = [torch.empty((cap,), dtype=torch.int32, device=dev) for _ in range(2)]
         seq_cnt = [torch.zeros((1,), dtype=torch.int32, device=dev) for _ in range(2)]
         seq_out = cache.clone()
-        seq_mask = torch.empty_like(mask)
+        seq_bits = torch.empty_like(mbits)
 
         def seq_step(k, one_call):
             cur, prv = k % 2, (k + 1) % 2
-            ssi.sige_diff_mask(a_o, seq_edits[cur], wl.tau, mask=seq_mask)
-            ssi.sige_reduce_mask(seq_mask, g, L.dilate, idx=seq_idx[cur], count=seq_cnt[cur])
+            ssi.sige_diff_mask_bits(a_o, seq_edits[cur], wl.tau, bits=seq_bits)
+            ssi.sige_reduce_bits(seq_bits, L.h, L.w, g, L.dilate, idx=seq_idx[cur], count=seq_cnt[cur])
             if one_call:  # restore and conv in one launch
                 ssi.sige_sparse_conv_layer_restore(seq_edits[cur], w_krsc, bias, cache, seq_idx[prv], seq_cnt[prv],
                                                    seq_idx[cur], seq_cnt[cur], g, seq_out)
@@ -339,7 +339,7 @@ def main():
         w_cl2 = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
 
         def step_bbox():
-            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
             bbox_out.copy_(cache)
             cmp.bbox_crop_conv(a_e, w_cl2, bias, cache, rect, L.k, L.stride, L.pad, out=bbox_out)
 
@@ -352,7 +352,7 @@ def main():
         bbox_blocks = int(bbox_cnt.item())
 
         def step_bbox_tiles():
-            ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, bbox_idx, bbox_cnt, g, out=bbox_out,
                                        copy_cached=True)
 
