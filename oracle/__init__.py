@@ -20,8 +20,24 @@ Functions and the passages they follow (page title, section):
 * ``gather``, ``conv_blocks``, ``scatter`` -- SIGE README Overview (gather with
   overlap 2 for 3x3 s1, stack on batch, F_l, scatter).  Pinned: zero-padded
   slicing, torch fp64 valid conv, slicing.
+* ``sparse_chain``     -- mer.dev notes section 3.2 (the mask downsampled to
+  each layer's scale); the layer-wise update of the README Overview applied
+  conv after conv.  Pinned: all-active chain equals the dense chain, an empty
+  edit returns the caches, a dilation wider than the chain's halo equals the
+  dense edited chain.
+* ``restore_blocks``   -- nubint.ai review, ABSTRACT (sequential edits) and
+  Proposed method (state kept between edits).  Pinned: a sequence of edits
+  through one buffer equals each edit computed from scratch; exactly the
+  blocks listed before and not now change.
+* ``sparse_attention`` -- nubint.ai review, Proposed method (attention prunes
+  the queries of unedited tokens).  Pinned: every query listed equals torch
+  fp64 softmax(QK^T/sqrt(d))V; identical keys give the mean value; one
+  dominant key returns its value; permuting keys with values changes nothing;
+  unlisted tokens keep the cache bit for bit.
 * ``round_to``         -- IEEE 754 binary16 / bfloat16 round-to-nearest-even.
   Pinned: hand-listed bit patterns, numpy float16 and torch bfloat16 casts.
+
+No function is unpinned.
 """
 from __future__ import annotations
 
