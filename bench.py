@@ -51,6 +51,10 @@ def parse():
                     help="also run one plain device copy of this size (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: the block size and dilation sweep (a line per point, then a table)")
+    ap.add_argument("--cold-kernels", type=int, default=0, metavar="R",
+                    help="R rounds of every kernel of the step and of the three-call path, each launched after "
+                         "512 MiB of writes, then R rounds each after 512 MiB of reads, that evict the MALL (for a "
+                         "profiler's kernel trace and counters)")
     ap.add_argument("--attention", action="store_true",
                     help="instead of the step: only the query-pruned attention comparator (one JSON line)")
     return ap.parse_args()
@@ -169,12 +173,13 @@ def main():
         b.record(cur)
         b.synchronize()
         spread.append(a.elapsed_time(b) / S * 1e3)
-    # cold: the 256 MB MALL (and the L2s) evicted by writing 512 MiB before every
-    # step (outside the events); one step per replay, events around it
-    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # cold: the 256 MB MALL (and the L2s) evicted by reading 512 MiB before every
+    # step (outside the events; reads leave clean lines, so no write-back of the
+    # eviction competes with the step); one step per replay, events around it
+    evict = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
     for i in range(40):
-        evict.fill_(i & 0xFF)
+        torch.amax(evict)
         a, b = ev(), ev()
         a.record(cur)
         gstep.replay()
@@ -191,7 +196,7 @@ def main():
                                          "replays": len(spread), "note": "each replay of a 10-step graph"},
                     "cold_step_us": {"p10": pct(cold, 0.1), "p50": pct(cold, 0.5), "p90": pct(cold, 0.9),
                                      "runs": len(cold),
-                                     "note": "512 MiB written before each step to evict the MALL; one step "
+                                     "note": "512 MiB read before each step to evict the MALL; one step "
                                              "per graph replay, HIP events around it (includes the graph launch)"}}
 
     # the same step launched eagerly from Python
@@ -221,6 +226,30 @@ def main():
     t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
     print(f"[bench] kernels {kt} gather {t_gather:.2f} conv_blocks {t_convb:.2f} scatter {t_scatter:.2f}",
           file=sys.stderr, flush=True)
+    if args.cold_kernels:
+        # each call alone on cold caches: 512 MiB written first, so its reads come from HBM
+        calls = [lambda: ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits),
+                 lambda: ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx,
+                                                   count=count),
+                 lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out,
+                                                    copy_cached=False),
+                 lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks),
+                 lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks),
+                 lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)]
+        evict = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+        for r in range(args.cold_kernels):  # evicted by writes: the MALL is left full of dirty lines
+            for f in calls:
+                evict.fill_(r & 0xFF)
+                f()
+        evict.zero_()
+        for r in range(args.cold_kernels):  # evicted by reads: the MALL is left full of clean lines
+            for f in calls:
+                torch.amax(evict)
+                f()
+        torch.cuda.synchronize()
+        del evict
+        print(f"[bench] cold kernels: {args.cold_kernels} rounds of {len(calls)} calls, after writes and after "
+              "reads of 512 MiB", file=sys.stderr, flush=True)
 
     t_nocopy = t_three = t_fused_copy = t_dense_ours = t_dense_miopen = None
     t_reduce = t_step_conv_copy = t_step_bytes = t_reduce_bytes = None
