@@ -804,15 +804,32 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
             _chain_layer(ssi, ly, x, first)
             x = ly["out"]
 
-    t_sparse = graph_time(chosen_chain, 2, 25)
+    t_per_layer = graph_time(chosen_chain, 2, 25)
+    # every layer's list depends on the one mask only: all twelve lists and cache
+    # copies in one launch, then the twelve layers
+    geoms, dils = [ly["g"] for ly in layers], [ly["L"].dilate for ly in layers]
+    idxs, cnts = [ly["idx"] for ly in layers], [ly["cnt"] for ly in layers]
+    caches, outs = [ly["cache"] for ly in layers], [ly["out"] for ly in layers]
+
+    def batched_chain():
+        ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+        ssi.sige_reduce_bits_layers(mbits, first.h, first.w, geoms, dils, idxs, cnts, caches, outs)
+        x = a_e
+        for ly in layers:
+            _chain_conv(ssi, ly, x)
+            x = ly["out"]
+
+    t_sparse = graph_time(batched_chain, 2, 25)
     with torch.no_grad():
         t_dense = graph_time(dense_chain, 1, 10)
     return {"sparse_us": round(t_sparse, 3), "dense_miopen_us": round(t_dense, 3),
             "speedup": round(t_dense / t_sparse, 2), "blocks_per_layer": blocks,
             "path_per_layer": ["split" if ly["split"] else "single" for ly in layers],
+            "sparse_per_layer_reduce_us": round(t_per_layer, 3),
             "sparse_single_range_only_us": round(t_single, 3),
-            "note": "one diff + 12 x (reduce with the cache copy + the faster of the fused layer and its split, "
-                    "chosen per layer); dense: 12 x F.conv2d; HIP graphs"}
+            "note": "one diff + one launch building all 12 lists with the 12 cache copies + 12 layers (the faster "
+                    "of the fused layer and its split, chosen per layer); per_layer_reduce: a reduce with its "
+                    "copy before each layer; dense: 12 x F.conv2d; HIP graphs"}
 
 
 def _chain_layer(ssi, ly, x, first):
@@ -820,6 +837,11 @@ def _chain_layer(ssi, ly, x, first):
     mbits = ly["mbits"]
     ssi.sige_reduce_bits_copy(mbits, first.h, first.w, ly["g"], ly["L"].dilate, ly["cache"], out=ly["out"],
                               idx=ly["idx"], count=ly["cnt"])
+    _chain_conv(ssi, ly, x)
+
+
+def _chain_conv(ssi, ly, x):
+    """The layer of the chain on its list, into its output (which holds the cache copy)."""
     if ly["split"]:
         ssi.sige_sparse_conv_layer_split(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
                                          out=ly["out"], copy_cached=False, workspace=ly["ws"])

@@ -152,6 +152,30 @@ int sige_reduce_bits(const uint32_t *bits, int mask_h, int mask_w, const sige_ge
 int sige_reduce_bits_copy(const uint32_t *bits, int mask_h, int mask_w, const sige_geom *g, int dilate_blocks,
                           int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream);
 
+/* Step 2 for the layers of a network at one edit, in one launch (mer.dev notes,
+ * 3.2: the one change mask downsampled to every layer's scale).  Layer l's list
+ * is what sige_reduce_bits(bits, mask_h, mask_w, &geoms[l], dilate_blocks[l],
+ * idx[l], count[l]) writes (bit for bit); one workgroup builds each list, and
+ * the launch's other workgroups meanwhile copy cached[l] into out[l] (all of
+ * it) for every layer that has a copy, as sige_reduce_bits_copy does.  All
+ * lists depend on the mask only, so they can be built before any layer runs;
+ * each layer then calls sige_sparse_conv_layer(..., copy_cached = 0) (or its
+ * split) on out[l] with idx[l] and count[l].
+ *   geoms, dilate_blocks, idx, count: host arrays of nlayers entries (idx[l],
+ *     count[l] device pointers as in sige_reduce_bits); 1 <= nlayers <= 16.
+ *     Every layer has the same n.
+ *   cached, out: host arrays of nlayers device pointers ([n, ho, wo, c_out] of
+ *     layer l in `dtype`), or NULL for no copies; cached[l] and out[l] both
+ *     NULL skips layer l's copy.  dtype is checked only when some layer copies.
+ *   Nothing a layer writes (idx, count, out) may overlap what any layer writes
+ *   or reads (bits, cached).
+ *   Limits: every layer's pooled mask and block grid must fit one workgroup
+ *   (conv input h * ceil(w/32) <= 8192 words, n*nby*nbx <= 16384), else
+ *   SIGE_ERANGE; other checks as sige_reduce_bits_copy. */
+int sige_reduce_bits_layers(const uint32_t *bits, int mask_h, int mask_w, int nlayers, const sige_geom *geoms,
+                            const int *dilate_blocks, int32_t *const *idx, int32_t *const *count, int dtype,
+                            const void *const *cached, void *const *out, void *stream);
+
 /* Step 3 -- gather (SIGE README, "Overview": collect the active blocks from the
  * edited activation and stack them along the batch dimension).
  *   blocks[slot, yy, xx, c] = a_edit[n, by*block*stride - pad + yy, bx*block*stride - pad + xx, c]

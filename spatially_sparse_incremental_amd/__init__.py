@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     sige_max_blocks,
     sige_reduce_bits,
     sige_reduce_bits_copy,
+    sige_reduce_bits_layers,
     sige_reduce_mask,
     sige_reduce_mask_copy,
     sige_restore_blocks,

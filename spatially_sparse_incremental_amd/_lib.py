@@ -19,7 +19,7 @@ SIGE_OK, SIGE_EINVAL, SIGE_EDTYPE, SIGE_EALIGN, SIGE_EHIP, SIGE_ENODEV, SIGE_ERA
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_reduce_mask_copy",
-           "sige_diff_mask_bits", "sige_reduce_bits", "sige_reduce_bits_copy",
+           "sige_diff_mask_bits", "sige_reduce_bits", "sige_reduce_bits_copy", "sige_reduce_bits_layers",
            "sige_sparse_conv_layer_split", "sige_sparse_conv_layer_split_workspace",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
@@ -63,6 +63,8 @@ def lib():
         L.sige_diff_mask_bits.argtypes = [V, V, I, I, I, I, I, ctypes.c_float, V, V, V]
         L.sige_reduce_bits.argtypes = [V, I, I, P, I, V, V, V]
         L.sige_reduce_bits_copy.argtypes = [V, I, I, P, I, V, V, I, V, V, V]
+        L.sige_reduce_bits_layers.argtypes = [V, I, I, I, P, ctypes.POINTER(I), ctypes.POINTER(V), ctypes.POINTER(V),
+                                              I, ctypes.POINTER(V), ctypes.POINTER(V), V]
         L.sige_gather.argtypes = [V, I, P, V, V, V, V]
         L.sige_conv_blocks.argtypes = [V, V, V, I, P, V, V, V]
         L.sige_scatter.argtypes = [V, V, V, P, I, V, V, I, V]
@@ -196,6 +198,28 @@ def sige_reduce_bits_copy(bits, mask_h, mask_w, g: Geom, dilate_blocks, cached, 
     rc = lib().sige_reduce_bits_copy(_p(bits), mask_h, mask_w, ctypes.byref(g), dilate_blocks, _p(idx), _p(count),
                                      _dt(cached), _p(cached), _p(out), _stream(stream))
     _check(rc, "sige_reduce_bits_copy")
+    return idx, count, out
+
+
+def sige_reduce_bits_layers(bits, mask_h, mask_w, geoms, dilate_blocks, idx, count, cached=None, out=None,
+                            stream=None):
+    """Every layer's block list from one packed mask in one launch, with the
+    layers' cache copies (cached[l] -> out[l]) on its other workgroups.
+    geoms, dilate_blocks, idx, count (and cached, out, or None) are lists with
+    one entry per layer; cached[l] and out[l] may both be None."""
+    n = len(geoms)
+    _dev(bits, *idx, *count, *(cached or []), *(out or []))
+    GA = Geom * n
+    IA = ctypes.c_int * n
+    VA = ctypes.c_void_p * n
+    cached = cached or [None] * n
+    out = out or [None] * n
+    dt = next((_dt(c) for c in cached if c is not None), 0)
+    rc = lib().sige_reduce_bits_layers(_p(bits), mask_h, mask_w, n, GA(*geoms), IA(*dilate_blocks),
+                                       VA(*[t.data_ptr() for t in idx]), VA(*[t.data_ptr() for t in count]), dt,
+                                       VA(*[t.data_ptr() if t is not None else 0 for t in cached]),
+                                       VA(*[t.data_ptr() if t is not None else 0 for t in out]), _stream(stream))
+    _check(rc, "sige_reduce_bits_layers")
     return idx, count, out
 
 

@@ -223,9 +223,7 @@ __global__ __launch_bounds__(1024) void k_reduce_one(const uint8_t *__restrict__
     if (threadIdx.x == 0) *count = running;
 }
 
-hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
-                         int32_t *count, const ReduceCopy &cp, int copy_wgs, hipStream_t st) {
-    const int ncopy = cp.nvec > 0 ? copy_wgs : 0;
+bool reduce_one_launch_ok(int hm, int wm, const Geo &g, int vec16) {
     const int fy = hm / g.h, fx = wm / g.w;
     const int WW = (g.w + 31) / 32;
     // the one-launch path divides with 31-bit multipliers: every dividend * divisor < 2^31
@@ -233,7 +231,15 @@ hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int 
     const int vdiv = vec16 == 2 ? wm / 32 : vec16 ? wm / 16 : 1;  // bitset words or 16-byte vectors per row
     const bool exact = (vec16 ? (long)hm * vdiv * vdiv : (long)hm * wm * wm) < lim && (long)hm * fy < lim &&
                        (long)wm * fx < lim;
-    if (exact && (long)g.h * WW <= kReduceBitsWords && g.nby * g.nbx <= kReduceMaxBlocks) {
+    return exact && (long)g.h * WW <= kReduceBitsWords && g.nby * g.nbx <= kReduceMaxBlocks;
+}
+
+hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
+                         int32_t *count, const ReduceCopy &cp, int copy_wgs, hipStream_t st) {
+    const int ncopy = cp.nvec > 0 ? copy_wgs : 0;
+    const int fy = hm / g.h, fx = wm / g.w;
+    const int vdiv = vec16 == 2 ? wm / 32 : vec16 ? wm / 16 : 1;
+    if (reduce_one_launch_ok(hm, wm, g, vec16)) {
         RedCfg rc{fast_div_magic(vdiv), fast_div_magic(wm), fast_div_magic(fy), fast_div_magic(fx),
                   fast_div_magic(g.nbx)};
         hipLaunchKernelGGL(k_reduce_one, dim3(1 + ncopy), dim3(1024), 0, st, mask, hm, wm, fy, fx, g, dilate, vec16,
@@ -246,6 +252,79 @@ hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, g, dilate, idx, count);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// step 2 for the layers of a network at one edit: every layer's list comes
+// from the same change mask, pooled to that layer's input (mer.dev notes, 3.2:
+// one mask downsampled to several scales), so all of them can be built before
+// any layer runs.  Workgroup i < n builds layer i's list as k_reduce_one does
+// (packed mask); the other workgroups copy the layers' caches into their
+// outputs, the copies taken as one range of 16-byte vectors split evenly.
+// ---------------------------------------------------------------------------
+struct ReduceLayer {
+    Geo g;
+    int fy, fx, dil;
+    RedCfg rc;
+    int32_t *idx, *count;
+    const uint8_t *src;
+    uint8_t *dst;
+    long long nvec;
+};
+struct ReduceLayers {
+    int n;
+    long long total_vec;
+    ReduceLayer l[kReduceMaxLayers];
+};
+
+__global__ __launch_bounds__(1024) void k_reduce_layers(const uint8_t *__restrict__ mask, int hm, int wm,
+                                                        ReduceLayers L) {
+    if ((int)blockIdx.x >= L.n) {
+        const int i = blockIdx.x - L.n, nw = gridDim.x - L.n;
+        const long long lo = split_point(L.total_vec, i, nw), hi = split_point(L.total_vec, i + 1, nw);
+        long long base = 0;
+        for (int l = 0; l < L.n; ++l) {
+            const long long nv = L.l[l].nvec;
+            const long long a = lo > base ? lo : base, b = hi < base + nv ? hi : base + nv;
+            if (a < b) copy_all_span<2, 1024, true>(L.l[l].src, L.l[l].dst, a - base, b - base);
+            base += nv;
+        }
+        return;
+    }
+    __shared__ uint32_t bits[kReduceBitsWords];
+    __shared__ __attribute__((aligned(16))) uint8_t scratch[2 * kReduceMaxBlocks];
+    __shared__ int wcnt[16];
+    const ReduceLayer &ly = L.l[blockIdx.x];
+    const int running =
+        reduce_list<1024>(mask, hm, wm, ly.fy, ly.fx, ly.g, ly.dil, 2, ly.rc, bits, scratch, wcnt, ly.idx);
+    if (threadIdx.x == 0) *ly.count = running;
+}
+
+hipError_t launch_reduce_layers(const uint32_t *bits, int hm, int wm, int n, const ReduceLayerArgs *layers,
+                                int copy_wgs, hipStream_t st) {
+    if (n < 1 || n > kReduceMaxLayers) return hipErrorInvalidValue;
+    ReduceLayers L{};
+    L.n = n;
+    for (int i = 0; i < n; ++i) {
+        const ReduceLayerArgs &a = layers[i];
+        if (!reduce_one_launch_ok(hm, wm, a.g, 2)) return hipErrorInvalidValue;  // checked by the caller
+        ReduceLayer &d = L.l[i];
+        d.g = a.g;
+        d.fy = hm / a.g.h;
+        d.fx = wm / a.g.w;
+        d.dil = a.dilate;
+        d.rc = RedCfg{fast_div_magic(wm / 32), fast_div_magic(wm), fast_div_magic(d.fy), fast_div_magic(d.fx),
+                      fast_div_magic(a.g.nbx)};
+        d.idx = a.idx;
+        d.count = a.count;
+        d.src = a.src;
+        d.dst = a.dst;
+        d.nvec = a.src ? a.nvec : 0;
+        L.total_vec += d.nvec;
+    }
+    const int ncopy = L.total_vec > 0 ? copy_wgs : 0;
+    hipLaunchKernelGGL(k_reduce_layers, dim3(n + ncopy), dim3(1024), 0, st, (const uint8_t *)bits, hm, wm, L);
     return hipGetLastError();
 }
 

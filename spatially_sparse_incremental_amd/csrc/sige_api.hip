@@ -402,6 +402,77 @@ int sige_reduce_bits_copy(const uint32_t *bits, int mask_h, int mask_w, const si
                          stream, "sige_reduce_bits_copy", 1);
 }
 
+int sige_reduce_bits_layers(const uint32_t *bits, int mask_h, int mask_w, int nlayers, const sige_geom *geoms,
+                            const int *dilate_blocks, int32_t *const *idx, int32_t *const *count, int dtype,
+                            const void *const *cached, void *const *out, void *stream) {
+    if (nlayers < 1 || nlayers > sige::kReduceMaxLayers)
+        return fail(SIGE_EINVAL, "nlayers=%d outside [1, %d]", nlayers, sige::kReduceMaxLayers);
+    if (!bits || !geoms || !dilate_blocks || !idx || !count) return fail(SIGE_EINVAL, "NULL pointer");
+    if (mask_w % 32 || !aligned(bits, 4))
+        return fail(mask_w % 32 ? SIGE_EINVAL : SIGE_EALIGN, "bitset mask: width %d must be a multiple of 32 and "
+                    "the words 4-byte aligned", mask_w);
+    sige::ReduceLayerArgs L[sige::kReduceMaxLayers];
+    struct Region {
+        const void *p;
+        size_t n;
+    } wr[3 * sige::kReduceMaxLayers], rd[1 + sige::kReduceMaxLayers];
+    int nw = 0, nr = 0, rc;
+    for (int l = 0; l < nlayers; ++l) {
+        Geo g;
+        if ((rc = derive(&geoms[l], &g))) return rc;
+        if (!idx[l] || !count[l]) return fail(SIGE_EINVAL, "layer %d: NULL idx or count", l);
+        if (l == 0) {
+            rd[nr++] = Region{bits, (size_t)g.n * mask_h * mask_w / 8};
+        } else if (g.n != geoms[0].n) {
+            return fail(SIGE_EINVAL, "layer %d: n=%d differs from layer 0 (one mask for every layer)", l, g.n);
+        }
+        if (mask_h < g.h || mask_w < g.w || mask_h % g.h || mask_w % g.w)
+            return fail(SIGE_EINVAL, "layer %d: mask %dx%d is not an integer multiple of the conv input %dx%d", l,
+                        mask_h, mask_w, g.h, g.w);
+        if (dilate_blocks[l] < 0 || dilate_blocks[l] > 16)
+            return fail(SIGE_EINVAL, "layer %d: dilate_blocks=%d outside [0, 16]", l, dilate_blocks[l]);
+        if (!sige::reduce_one_launch_ok(mask_h, mask_w, g, 2))
+            return fail(SIGE_ERANGE, "layer %d: its pooled mask or block grid exceeds one workgroup "
+                        "(build its list with sige_reduce_bits)", l);
+        if (!aligned(idx[l], 4) || !aligned(count[l], 4))
+            return fail(SIGE_EALIGN, "layer %d: idx/count must be 4-byte aligned", l);
+        wr[nw++] = Region{idx[l], (size_t)g.cap * 4};
+        wr[nw++] = Region{count[l], 4};
+        L[l] = sige::ReduceLayerArgs{g, dilate_blocks[l], idx[l], count[l], nullptr, nullptr, 0};
+        const void *c = cached ? cached[l] : nullptr;
+        void *o = out ? out[l] : nullptr;
+        if (!c != !o) return fail(SIGE_EINVAL, "layer %d: cached and out must both be given or both NULL", l);
+        if (o) {
+            if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+            if ((rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+            if (!aligned(c, 16) || !aligned(o, 16)) return fail(SIGE_EALIGN, "layer %d: tensors must be 16-byte aligned", l);
+            const size_t ob = (size_t)g.n * g.ho * g.wo * g.cout * sige::elem_bytes(dtype);
+            wr[nw++] = Region{o, ob};
+            rd[nr++] = Region{c, ob};
+            L[l].src = (const uint8_t *)c;
+            L[l].dst = (uint8_t *)o;
+            L[l].nvec = (long long)(ob / 16);
+        }
+    }
+    for (int i = 0; i < nw; ++i) {  // what the launch writes overlaps nothing else it touches
+        for (int j = i + 1; j < nw; ++j)
+            if (overlap(wr[i].p, wr[i].n, wr[j].p, wr[j].n)) return fail(SIGE_EINVAL, "outputs of the layers overlap");
+        for (int j = 0; j < nr; ++j)
+            if (overlap(wr[i].p, wr[i].n, rd[j].p, rd[j].n))
+                return fail(SIGE_EINVAL, "an output overlaps the mask or a cache");
+    }
+    if ((rc = device_ready())) return rc;
+    static int copy_wgs = -1;  // SIGE_REDUCE_COPY_WGS overrides the copy's workgroups (tuning)
+    if (copy_wgs < 0) {
+        const char *v = getenv("SIGE_REDUCE_COPY_WGS");
+        const long x = v ? strtol(v, nullptr, 10) : 0;
+        copy_wgs = (x > 0 && x < 65536) ? (int)x : 0;
+    }
+    return finish(sige::launch_reduce_layers(bits, mask_h, mask_w, nlayers, L, copy_wgs ? copy_wgs : dev_info().cus / 2,
+                                             (hipStream_t)stream),
+                  "sige_reduce_bits_layers", (hipStream_t)stream);
+}
+
 int sige_reduce_mask_copy(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *gp, int dilate_blocks,
                           int32_t *idx, int32_t *count, int dtype, const void *cached, void *out, void *stream) {
     if (!out) return fail(SIGE_EINVAL, "NULL pointer");

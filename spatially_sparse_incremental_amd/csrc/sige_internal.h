@@ -63,6 +63,21 @@ struct ReduceCopy {
 // (2: bit p % 32 of 32-bit word p / 32 for pixel p, wm a multiple of 32)
 hipError_t launch_reduce(const uint8_t *mask, int hm, int wm, const Geo &g, int dilate, int vec16, int32_t *idx,
                          int32_t *count, const ReduceCopy &cp, int copy_wgs, hipStream_t st);
+// Whether one workgroup can build the list of geometry g from an hm x wm mask
+// (vec16 as above): the pooled bits fit in LDS and the fast divisions are exact.
+bool reduce_one_launch_ok(int hm, int wm, const Geo &g, int vec16);
+// Several layers' lists from one packed mask in one launch, with their cache copies.
+constexpr int kReduceMaxLayers = 16;
+struct ReduceLayerArgs {
+    Geo g;
+    int dilate;
+    int32_t *idx, *count;
+    const uint8_t *src;  // cache to copy (NULL: none for this layer)
+    uint8_t *dst;
+    long long nvec;      // 16-byte vectors of the copy
+};
+hipError_t launch_reduce_layers(const uint32_t *bits, int hm, int wm, int n, const ReduceLayerArgs *layers,
+                                int copy_wgs, hipStream_t st);
 hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t *idx, const int32_t *count,
                          void *blocks, hipStream_t st);
 // fused = 0: src = stacked blocks, dst = output blocks.  fused = 1: src = a_edit, dst = out;

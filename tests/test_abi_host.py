@@ -246,3 +246,41 @@ def test_valid_call_without_gpu_is_enodev(lib):
                                    _v(0)) == ENODEV
     assert lib.sige_sparse_conv_layer_restore(_v(A), _v(B), None, _v(C), _v(D), _v(D + 64), _v(E), _v(E + 64), 1,
                                               ctypes.byref(g), _v(E + (1 << 35)), _v(0)) == ENODEV
+
+
+def test_reduce_layers_validation(lib):
+    """sige_reduce_bits_layers: host arrays of per-layer geometries, lists and copies."""
+    f = lib.sige_reduce_bits_layers
+    s = _v(0)
+    gs = [_g(), _g(h=128, w=128, ci=128, co=256), _g(h=64, w=64, ci=256, co=256, b=4)]
+    n = len(gs)
+    step = 1 << 30
+
+    def call(nl=n, geoms=gs, dil=(1, 1, 1), idx=None, cnt=None, dt=1, cached=None, out=None, mw=256, bits=A):
+        GA, IA, VA = L.Geom * len(geoms), ctypes.c_int * len(dil), ctypes.c_void_p * n
+        idx = idx or [B + i * step for i in range(n)]
+        cnt = cnt or [C + i * 256 for i in range(n)]
+        ca = VA(*cached) if cached is not None else None
+        oa = VA(*out) if out is not None else None
+        return f(_v(bits), 256, mw, nl, GA(*geoms), IA(*dil), VA(*idx), VA(*cnt), dt, ca, oa, s)
+
+    cached = [D + i * step for i in range(n)]
+    out = [E + i * step for i in range(n)]
+    assert call() == ENODEV                                   # valid, no GPU here
+    assert call(cached=cached, out=out) == ENODEV
+    assert call(nl=0) == EINVAL
+    assert call(nl=17) == EINVAL
+    assert call(mw=250) == EINVAL                             # packed rows need whole words
+    assert call(bits=A + 2) == EALIGN
+    assert call(dil=(1, 17, 1)) == EINVAL
+    assert call(geoms=[gs[0], _g(h=96, w=96), gs[2]]) == EINVAL  # 256 is not a multiple of 96
+    assert call(geoms=[gs[0], _g(n=2, h=128, w=128), gs[2]]) == EINVAL  # one mask: the same n everywhere
+    assert call(idx=[B, B + 64, B + 2 * step]) == EINVAL      # two layers' lists overlap
+    assert call(cnt=[C, C, C + 512]) == EINVAL                # shared count
+    assert call(cached=[cached[0], None, cached[2]], out=out) == EINVAL  # copy half given
+    assert call(cached=[cached[0], None, cached[2]], out=[out[0], None, out[2]]) == ENODEV  # layer 1 not copied
+    assert call(cached=cached, out=[out[0], out[0] + 256, out[2]]) == EINVAL  # outputs overlap
+    assert call(cached=cached, out=[out[0], cached[1], out[2]]) == EINVAL     # output is another layer's cache
+    assert call(cached=cached, out=out, dt=7) == EDTYPE
+    assert call(cached=[cached[0] + 8, cached[1], cached[2]], out=out) == EALIGN
+    assert call(geoms=[gs[0], _g(h=256, w=256, b=1), gs[2]]) == ERANGE  # 65536 blocks: beyond one workgroup

@@ -136,3 +136,96 @@ def test_step_through_the_bitset_equals_the_byte_mask_step(dts):
     torch.cuda.synchronize()
     assert int(cnt.item()) == int(rcnt.item()) > 0
     assert torch.equal(bits(out), bits(ref))
+
+
+
+def _layers_case(wl, layers, m, seed, copy_mask):
+    """One sige_reduce_bits_layers call over `layers` of the workload for the
+    change mask m (at the first layer's input): every list against the oracle's
+    (bit-exact, pooled from the one mask), nothing written past a count, and
+    every copy equal to its cache bit for bit."""
+    first = wl.layers[0]
+    mbits = pack(m).cuda()
+    geoms, dil, idx, cnt, cached, out = [], [], [], [], [], []
+    for li, L in enumerate(layers):
+        g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+        d = ssi.sige_geom_derive(g)
+        geoms.append(g)
+        dil.append(L.dilate)
+        idx.append(torch.full((d.cap,), -7, dtype=torch.int32, device="cuda"))
+        cnt.append(torch.full((1,), -7, dtype=torch.int32, device="cuda"))
+        dt = synth.DTYPES[L.dtype]
+        cached.append(rand((1, d.ho, d.wo, L.c_out), dt, seed * 10 + li).cuda() if copy_mask[li] else None)
+        out.append(rand((1, d.ho, d.wo, L.c_out), dt, seed * 10 + li + 5).cuda() if copy_mask[li] else None)
+    print(f"\n[case] reduce layers: {len(layers)} layers, {int(m.sum())} changed pixels, seed {seed}", flush=True)
+    ssi.sige_reduce_bits_layers(mbits, first.h, first.w, geoms, dil, idx, cnt, cached, out)
+    torch.cuda.synchronize()
+    for li, L in enumerate(layers):
+        act = oracle.block_activity(torch.from_numpy(m).unsqueeze(0), L.h, L.w, L.k, L.stride, L.pad, L.block,
+                                    L.dilate)
+        ref = oracle.index_list(act)
+        k = int(cnt[li].item())
+        assert k == ref.numel(), (L.name, k, ref.numel())
+        assert torch.equal(idx[li][:k].cpu(), ref.to(torch.int32)), L.name
+        assert bool((idx[li][k:] == -7).all()), L.name  # nothing written past the count
+        if copy_mask[li]:
+            assert torch.equal(bits(out[li].cpu()), bits(cached[li].cpu())), L.name
+
+
+def test_reduce_layers_builds_every_chain_list_and_copy():
+    """All 12 layers of the U-Net chain in one launch at the 1.2% blob; the
+    deeper layers at a 5% blob with one layer left without a copy; one layer at
+    an empty edit."""
+    wl = synth.workload("unet_chain_12conv_bf16")
+    first = wl.layers[0]
+    m = synth.edit_shape(wl, 5).raster(first.h, first.w)
+    _layers_case(wl, wl.layers, m, 5, [True] * 12)
+    m5 = synth.edit_shape(wl, 6, 0.05).raster(first.h, first.w)
+    _layers_case(wl, wl.layers[5:], m5, 6, [True, True, False, True, True, True, True])
+    _layers_case(wl, wl.layers[:1], np.zeros_like(m), 7, [True])
+
+
+def test_chain_with_all_lists_in_one_launch_equals_the_per_layer_chain():
+    """The 12-conv chain run as one diff, one sige_reduce_bits_layers launch and
+    12 fused layers equals, at every layer and bit for bit, the chain run with a
+    sige_reduce_bits_copy before each layer (itself checked against the oracle
+    layer by layer in the full-size workload tests)."""
+    wl = synth.workload("unet_chain_12conv_bf16")
+    seed = 8
+    first = wl.layers[0]
+    m = synth.edit_shape(wl, seed).raster(first.h, first.w)
+    a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed).cuda()
+    a_e = synth.make_edit(a_o.cpu(), m, wl.edit_kind, seed).cuda()
+    mbits = ssi.sige_diff_mask_bits(a_o, a_e, wl.tau)
+    lay = []
+    for li, L in enumerate(wl.layers):
+        wt, bias = synth.make_layer_tensors(L, seed * 100 + li)
+        g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+        d = ssi.sige_geom_derive(g)
+        cache = synth.make_activation(1, d.ho, d.wo, L.c_out, L.dtype, seed * 100 + li + 50).cuda()
+        lay.append(dict(L=L, g=g, wk=ssi.weight_to_krsc(wt).cuda(), bias=bias.cuda(), cache=cache, cap=d.cap))
+
+    def run(batched):
+        idx = [torch.empty((ly["cap"],), dtype=torch.int32, device="cuda") for ly in lay]
+        cnt = [torch.empty((1,), dtype=torch.int32, device="cuda") for ly in lay]
+        out = [torch.empty_like(ly["cache"]) for ly in lay]
+        if batched:
+            ssi.sige_reduce_bits_layers(mbits, first.h, first.w, [ly["g"] for ly in lay],
+                                        [ly["L"].dilate for ly in lay], idx, cnt, [ly["cache"] for ly in lay], out)
+        x = a_e
+        for i, ly in enumerate(lay):
+            if not batched:
+                ssi.sige_reduce_bits_copy(mbits, first.h, first.w, ly["g"], ly["L"].dilate, ly["cache"], out=out[i],
+                                          idx=idx[i], count=cnt[i])
+            ssi.sige_sparse_conv_layer(x, ly["wk"], ly["bias"], None, idx[i], cnt[i], ly["g"], out=out[i],
+                                       copy_cached=False)
+            x = out[i]
+        torch.cuda.synchronize()
+        return [o.cpu() for o in out], [int(c.item()) for c in cnt]
+
+    print(f"\n[case] chain, lists in one launch vs per layer, seed {seed}", flush=True)
+    ref, ref_cnt = run(False)
+    got, got_cnt = run(True)
+    assert got_cnt == ref_cnt
+    for li in range(len(lay)):
+        assert torch.equal(bits(got[li]), bits(ref[li])), wl.layers[li].name
