@@ -16,7 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["sige_api.hip", "kernels_mask.hip", "kernels_conv.hip", "kernels_attn.hip"]
+SOURCES = ["sige_api.hip", "kernels_mask.hip", "kernels_conv.hip", "kernels_layer.hip", "kernels_attn.hip"]
 LIB = os.path.join(PKG, "libsige.so")
 
 

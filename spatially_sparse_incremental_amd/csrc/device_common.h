@@ -236,4 +236,83 @@ __device__ void copy_all_span(const uint8_t *__restrict__ src, uint8_t *__restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// Work split of the copy and of the restore among the workgroups of a launch.
+// ---------------------------------------------------------------------------
+
+// The part [lo, hi) of the copy that workgroup `bid` takes.  The workgroups
+// without a tile come first (they start at once): up to free_vec vectors each
+// per tile of the busiest workgroup.  What remains is split evenly over the
+// others, after their tiles.
+__device__ __forceinline__ void copy_split(const CopyCfg &cc, int ntiles, int grid, int bid, long long &lo,
+                                           long long &hi) {
+    const long long nvec = cc.nvec;
+    const int busy = min(ntiles, grid), nfree = grid - busy;
+    const int rounds = (ntiles + grid - 1) / grid;
+    long long to_free = (long long)nfree * cc.free_vec * max(rounds, 1);
+    if (busy == 0 || to_free > nvec) to_free = nvec;
+    if (bid >= busy) {
+        lo = split_point(to_free, bid - busy, nfree);
+        hi = split_point(to_free, bid - busy + 1, nfree);
+    } else {
+        const long long rest = nvec - to_free;
+        lo = to_free + split_point(rest, bid, busy);
+        hi = to_free + split_point(rest, bid + 1, busy);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sequential edits: the previous edit's blocks that the new list does not hold
+// get the cache back.  restore_slots takes previous-list slots first, first +
+// step, ... below end; a block's valid pixels go as batches of 16-byte vectors.
+// ---------------------------------------------------------------------------
+template <int NTHR>
+__device__ void restore_slots(const Geo &g, const CopyCfg &cc, const int32_t *__restrict__ prev_idx, int first,
+                              int step, int end, const uint32_t *bm, const int32_t *__restrict__ idx, int cnt,
+                              const uint8_t *__restrict__ cache, uint8_t *__restrict__ out) {
+    constexpr int U = 8;
+    const int vpp = cc.vpp, row_bytes = vpp * 16, nv = g.b * g.b * vpp;
+    for (int slot = first; slot < end; slot += step) {
+        const int lin = prev_idx[slot];
+        int n, by, bx;
+        if (!decode_block(g, lin, n, by, bx)) continue;
+        if (idx && block_listed(bm, idx, cnt, lin)) continue;
+        for (int v0 = threadIdx.x; v0 < nv; v0 += U * NTHR) {
+            u32x4 r[U];
+            size_t at[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int v = v0 + i * NTHR;
+                at[i] = ~(size_t)0;
+                if (v < nv) {
+                    const int pix = fdiv(v, cc.m_vpp), cvv = v - pix * vpp;
+                    const int py = fdiv(pix, cc.m_b), px = pix - py * g.b;
+                    const int y = by * g.b + py, x = bx * g.b + px;
+                    if (y < g.ho && x < g.wo) {
+                        at[i] = (((size_t)n * g.ho + y) * g.wo + x) * row_bytes + cvv * 16;
+                        r[i] = ld16(cache + at[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                if (at[i] != ~(size_t)0) st16(out + at[i], r[i]);
+        }
+    }
+}
+
+// The slots [lo, hi) of the previous list that workgroup `bid` restores: the
+// workgroups without a tile share them evenly; without such workgroups, all
+// share them after their tiles.
+__device__ __forceinline__ void restore_split(int np, int ntiles, int grid, int bid, long long &lo, long long &hi) {
+    const int busy = min(ntiles, grid), nfree = grid - busy;
+    if (nfree > 0) {
+        lo = bid >= busy ? split_point(np, bid - busy, nfree) : 0;
+        hi = bid >= busy ? split_point(np, bid - busy + 1, nfree) : 0;
+    } else {
+        lo = split_point(np, bid, grid);
+        hi = split_point(np, bid + 1, grid);
+    }
+}
+
 }  // namespace sige

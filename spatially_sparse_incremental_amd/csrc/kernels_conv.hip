@@ -1,5 +1,5 @@
-// kernels_conv.hip -- steps 3-5 (gather, block convolution, scatter) and the
-// fused layer on gfx950.
+// kernels_conv.hip -- steps 3 and 5 (gather, scatter), the restore of
+// sequential edits, and the fused layer split over input channels, on gfx950.
 //
 // SIGE README mirror, "Overview": gather the active blocks (with their halo;
 // blocks of a 3x3 stride-1 conv overlap by 2) from the edited activation, stack
@@ -13,84 +13,9 @@
 // Every memory-bound loop issues a batch of independent 16-byte loads before
 // it stores any of them, so a thread waits for memory once per batch rather
 // than once per vector.
-#include "device_common.h"
+#include "conv_common.h"
 
 namespace sige {
-
-// The part [lo, hi) of the copy that workgroup `bid` takes.  The workgroups
-// without a tile come first (they start at once): up to free_vec vectors each
-// per tile of the busiest workgroup.  What remains is split evenly over the
-// others, after their tiles.
-__device__ __forceinline__ void copy_split(const CopyCfg &cc, int ntiles, int grid, int bid, long long &lo,
-                                           long long &hi) {
-    const long long nvec = cc.nvec;
-    const int busy = min(ntiles, grid), nfree = grid - busy;
-    const int rounds = (ntiles + grid - 1) / grid;
-    long long to_free = (long long)nfree * cc.free_vec * max(rounds, 1);
-    if (busy == 0 || to_free > nvec) to_free = nvec;
-    if (bid >= busy) {
-        lo = split_point(to_free, bid - busy, nfree);
-        hi = split_point(to_free, bid - busy + 1, nfree);
-    } else {
-        const long long rest = nvec - to_free;
-        lo = to_free + split_point(rest, bid, busy);
-        hi = to_free + split_point(rest, bid + 1, busy);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Sequential edits: the previous edit's blocks that the new list does not hold
-// get the cache back.  restore_slots takes previous-list slots first, first +
-// step, ... below end; a block's valid pixels go as batches of 16-byte vectors.
-// ---------------------------------------------------------------------------
-template <int NTHR>
-__device__ void restore_slots(const Geo &g, const CopyCfg &cc, const int32_t *__restrict__ prev_idx, int first,
-                              int step, int end, const uint32_t *bm, const int32_t *__restrict__ idx, int cnt,
-                              const uint8_t *__restrict__ cache, uint8_t *__restrict__ out) {
-    constexpr int U = 8;
-    const int vpp = cc.vpp, row_bytes = vpp * 16, nv = g.b * g.b * vpp;
-    for (int slot = first; slot < end; slot += step) {
-        const int lin = prev_idx[slot];
-        int n, by, bx;
-        if (!decode_block(g, lin, n, by, bx)) continue;
-        if (idx && block_listed(bm, idx, cnt, lin)) continue;
-        for (int v0 = threadIdx.x; v0 < nv; v0 += U * NTHR) {
-            u32x4 r[U];
-            size_t at[U];
-#pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int v = v0 + i * NTHR;
-                at[i] = ~(size_t)0;
-                if (v < nv) {
-                    const int pix = fdiv(v, cc.m_vpp), cvv = v - pix * vpp;
-                    const int py = fdiv(pix, cc.m_b), px = pix - py * g.b;
-                    const int y = by * g.b + py, x = bx * g.b + px;
-                    if (y < g.ho && x < g.wo) {
-                        at[i] = (((size_t)n * g.ho + y) * g.wo + x) * row_bytes + cvv * 16;
-                        r[i] = ld16(cache + at[i]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < U; ++i)
-                if (at[i] != ~(size_t)0) st16(out + at[i], r[i]);
-        }
-    }
-}
-
-// The slots [lo, hi) of the previous list that workgroup `bid` restores: the
-// workgroups without a tile share them evenly; without such workgroups, all
-// share them after their tiles.
-__device__ __forceinline__ void restore_split(int np, int ntiles, int grid, int bid, long long &lo, long long &hi) {
-    const int busy = min(ntiles, grid), nfree = grid - busy;
-    if (nfree > 0) {
-        lo = bid >= busy ? split_point(np, bid - busy, nfree) : 0;
-        hi = bid >= busy ? split_point(np, bid - busy + 1, nfree) : 0;
-    } else {
-        lo = split_point(np, bid, grid);
-        hi = split_point(np, bid + 1, grid);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // step 3: gather.  One workgroup per listed block (grid-stride over slots).
@@ -139,89 +64,24 @@ hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// step 4 (and the fused layer): implicit GEMM on the matrix cores.
+// The fused layer split over input channels (weight-bound layers), an
+// implicit GEMM on the matrix cores like k_layer (kernels_layer.hip, which
+// runs the unsplit layer and the block convolution):
 //   M = listed blocks x b*b output pixels (flattened over all blocks, so tiles
 //       are not padded per block), N = c_out, K = k*k*c_in.
-// A persistent grid of workgroups (8 waves each) walks tiles of 16*MT rows x
-// 16*NT output channels.  The 8 waves split each chunk's K steps (tap, one
-// 32-channel slice; 16 for fp32) round robin and each accumulates the whole
-// tile, so no wave idles on small tiles and every per-wave chain (staging,
-// MFMA) is short; the eight partial tiles are summed through LDS at the end.
+// Workgroups of 8 waves walk tiles of 16*MT rows x 16*NT output channels.  The
+// 8 waves split each chunk's K steps (tap, one 32-channel slice; 16 for fp32)
+// round robin and each accumulates the whole tile; the eight partial tiles
+// are summed through LDS at the end.
 //   - Weights: a wave's B fragments are used by that wave only, so they go
-//     straight from global memory (L2-resident: every tile with the same
-//     channel slice reads them) into registers, up to SMAX steps per chunk.
-//     They do not depend on the block list: the first chunk's are issued
-//     together with the block-index, count and bias reads, so one memory
-//     round trip covers all of them.
+//     straight from global memory (L2-resident) into registers, up to SMAX
+//     steps per chunk.
 //   - Input windows: every wave reads every row, so the halo windows of the
 //     block slots a tile touches are staged once in LDS, loaded from global
-//     memory straight into LDS (global_load_lds_dwordx4: no registers, every
-//     load of the stage in flight at once), zero outside the image.
-//   - The tile's slots follow from its index alone, so the block indices are
-//     read before `count` is known; a tile at or beyond count is dropped.
+//     memory straight into LDS (global_load_lds_dwordx4), zero outside the
+//     image.
 // MFMA: v_mfma_f32_16x16x32_{bf16,f16} (fp32: four v_mfma_f32_16x16x4_f32).
-// Epilogue: partial tiles summed through LDS, bias (prefetched) added, one
-// rounding to the storage type, 16-byte row stores into the output image
-// (fused) or the block tensor.  With copy_cached, the workgroups that own no
-// tile copy the cache outside the listed blocks meanwhile.
 // ---------------------------------------------------------------------------
-template <int DT>
-struct MfmaStep;
-
-template <>
-struct MfmaStep<1> {  // bf16: one 16x16x32 MFMA per (16 B of A, 16 B of B)
-    static constexpr int KS = 32;
-    __device__ static __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                       c, 0, 0, 0);
-    }
-};
-template <>
-struct MfmaStep<2> {  // fp16
-    static constexpr int KS = 32;
-    __device__ static __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
-                                                      0, 0, 0);
-    }
-};
-template <>
-struct MfmaStep<0> {  // fp32: four 16x16x4 MFMAs; lane group g holds k = 4g..4g+3
-    static constexpr int KS = 16;
-    __device__ static __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
-        return c;
-    }
-};
-
-// Store 8 consecutive channels (fp32: the second 16-byte half only when
-// `full`; c_out is a multiple of 4 there, of 8 for 16-bit types).
-template <int DT>
-__device__ __forceinline__ void store_row8(uint8_t *p, const float *v, bool full) {
-    if constexpr (DT == 0) {
-        st16(p, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
-        if (full)
-            st16(p + 16,
-                 u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
-    } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint16_t lo, hi;
-            if constexpr (DT == 1) {
-                lo = __builtin_bit_cast(uint16_t, (__bf16)v[2 * i]);
-                hi = __builtin_bit_cast(uint16_t, (__bf16)v[2 * i + 1]);
-            } else {
-                lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
-                hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
-            }
-            w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-        }
-        st16(p, u32x4{w[0], w[1], w[2], w[3]});
-    }
-}
-
 struct ConvArgs {
     const uint8_t *src;
     const uint8_t *w;
@@ -466,212 +326,6 @@ __device__ __forceinline__ void park_partials(float *part, const f32x4 (&acc)[MT
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 part[(wave * BM + mt * 16 + (lane >> 4) * 4 + i) * PSTR + nt * 16 + (lane & 15)] = acc[mt][nt][i];
-}
-
-template <int DT, int MT, int NT, bool FUSED>
-__global__ __launch_bounds__(kConvThreads, 2) void k_conv(ConvArgs a) {
-    constexpr int NW = kConvWaves, NTHR = kConvThreads;
-    constexpr int ES = elem_bytes(DT);
-    constexpr int EPV = 16 / ES;  // elements per 16-byte vector
-    constexpr int KS = MfmaStep<DT>::KS;
-    constexpr int BM = 16 * MT, BN = 16 * NT;
-    constexpr int PSTR = BN + 4;  // padded row of a partial tile (floats)
-    constexpr int SMAX = Smax<NT>::v;
-    constexpr int VPR = BN / 8;   // 8-channel output vectors per tile row
-    constexpr int OPT = (BM * VPR + NTHR - 1) / NTHR;  // output vectors per thread
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // per staged slot: image, input-window origin, output-block origin
-    __shared__ int s_n[BM + 1], s_iy[BM + 1], s_ix[BM + 1], s_oy[BM + 1], s_ox[BM + 1], s_cnt;
-    __shared__ uint32_t s_bm[FUSED ? kCopyBitmapWords : 1];
-    __shared__ float s_bias[BN];
-    static_assert((BN & (BN - 1)) == 0 && BN <= 64, "wave 0 reads the tile's bias");
-    static_assert(BM <= 64, "wave 0 fills the slot table: at most 64 slots per tile");
-
-    const Geo &g = a.g;
-    const ConvCfg &c = a.c;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
-    const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
-    const int mcap = g.cap * b2;            // rows at full capacity (checked on the host)
-    const int ntn = (g.cout + BN - 1) / BN;
-    const int grid = gridDim.x;
-    const int vpc = c.ck / EPV;             // 16-byte vectors per staged pixel
-    const int kpc = c.ck / KS;              // K steps per tap in a chunk
-    const int steps = k2 * kpc;             // K steps per chunk
-    int ntiles = -1, cnt_seen = 0;
-    // With the copy (or the restore), the bitmap of listed blocks is built from a read of the
-    // list's first NTHR entries that rides along with the first tile's reads.
-    const int bm_words = (g.cap + 31) >> 5;
-    const bool spec_bm = FUSED && (a.cc.nvec > 0 || a.prev_idx) && bm_words <= kCopyBitmapWords;
-    bool spec_done = false;
-    if (spec_bm)
-        for (int q = tid; q < bm_words; q += NTHR) s_bm[q] = 0u;
-    uint8_t *As = smem;
-    float *part = (float *)smem;
-    const float *bsrc = a.bias ? a.bias : (const float *)a.w;  // any readable floats when there is no bias
-
-    // Tile t runs on XCD t % 8 (the grid is a multiple of 8), and the N tiles of
-    // one M tile share t % 8: t = 8 * (ntn * q + tn) + x holds M tile 8 * q + x,
-    // so an M tile's input windows are fetched into one XCD's L2 only.  M tiles
-    // are padded to a multiple of 8; the padding tiles are empty.  Layers with
-    // fewer than 8 M tiles at capacity (a few blocks, many output channels) take
-    // the tiles in plain order instead: padding would be most of their tiles.
-    const bool xcd = (mcap + BM - 1) / BM >= 8;
-    auto tiles_of = [&](int cnt) {
-        const int mtn = (cnt * b2 + BM - 1) / BM;
-        return (xcd ? (mtn + 7) / 8 * 8 : mtn) * ntn;
-    };
-    const int tiles_cap = tiles_of(g.cap);
-    for (int t = blockIdx.x;; t += grid) {
-        if (ntiles >= 0 && t >= ntiles) break;  // known after the first tile
-        if (t >= tiles_cap) break;
-        int tn, tm;
-        if (xcd) {
-            const int r8 = t >> 3;
-            tn = r8 % ntn;
-            tm = (r8 / ntn) * 8 + (t & 7);
-        } else {
-            tn = t % ntn;
-            tm = t / ntn;
-        }
-        const int m0 = min(tm * BM, mcap - 1);  // padding tiles past capacity read the last slot
-        const int n0 = tn * BN;
-        const int s_lo = fdiv(m0, c.m_b2);
-        const int s_hi = min(g.cap - 1, fdiv(m0 + BM - 1, c.m_b2));
-        const int ns = s_hi - s_lo + 1;
-        __syncthreads();  // the previous tile is done with LDS and the slot table
-        // First round trip: the list length and the tile's block indices (read
-        // before the length is known), this wave's weight fragments for the
-        // first chunk, and the bias.  Every read is unconditional (at a clamped
-        // address; what lies outside the tensors is zeroed where it is used), so
-        // each wait covers only the reads it needs.  Only wave 0 waits for the
-        // list: it fills the slot table while the other waves' reads land.
-        // (cap >> 31 is 0: the per-lane address keeps the length in a vector
-        // register, so the compiler does not move its wait up to the load.)
-        const int cnt_raw =
-            __hip_atomic_load(a.count + (lane & (g.cap >> 31)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int lin = FUSED ? a.idx[s_lo + min(lane, ns - 1)] : 0;
-        const int spec = FUSED ? a.idx[min(tid, g.cap - 1)] : 0;
-        const float bv = bsrc[min(n0 + (lane & (BN - 1)), g.cout - 1)];
-        u32x4 bfr[SMAX][NT];
-        load_weights<DT, NT, SMAX>(a, bfr, 0, n0, wave, lane, steps, kpc);
-        __builtin_amdgcn_sched_barrier(0);  // every read above is issued before wave 0 waits for the list
-        if (wave == 0) {
-            if (lane == 0) s_cnt = min(max(cnt_raw, 0), g.cap);
-            if (lane < BN) s_bias[lane] = (a.bias && n0 + lane < g.cout) ? bv : 0.f;
-            if (lane < ns) {
-                int n = -1, by = 0, bx = 0;
-                if (FUSED) {
-                    if (!decode_block(g, lin, n, by, bx)) n = -1;
-                } else {
-                    n = 0;  // stacked blocks: positions inside the block tensor only
-                }
-                s_n[lane] = n;
-                s_iy[lane] = by * g.b * g.s - g.p;
-                s_ix[lane] = bx * g.b * g.s - g.p;
-                s_oy[lane] = by * g.b;
-                s_ox[lane] = bx * g.b;
-            }
-        }
-        __syncthreads();  // the list length and the slot table are visible
-        // the list length decides whether this tile exists
-        const int cnt = s_cnt;
-        cnt_seen = cnt;
-        if (spec_bm && !spec_done) {
-            if (tid < cnt && spec >= 0 && spec < g.cap) atomicOr(&s_bm[spec >> 5], 1u << (spec & 31));
-            spec_done = true;
-        }
-        if (ntiles < 0) ntiles = tiles_of(cnt);
-        if (t >= ntiles) break;
-        const int mrows = cnt * b2;
-        if (tm * BM >= mrows) continue;  // a padding tile
-        int rb[MT];
-        row_offsets<MT>(g, c, m0, mrows, s_lo, lane, rb);
-        f32x4 acc[MT][NT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        const int nslot = ns * ib2 * (vpc + 1);  // 16-byte LDS slots of the staged windows
-        for (int c0 = 0; c0 < g.cin; c0 += c.ck) {
-            if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
-            stage_windows<DT, FUSED>(a, As, s_n, s_iy, s_ix, c0, nslot, s_lo, wave, lane);
-            if (c0 > 0)  // the next chunk's weight fragments (the first chunk's are in flight)
-                load_weights<DT, NT, SMAX>(a, bfr, c0, n0, wave, lane, steps, kpc);
-            __builtin_amdgcn_s_waitcnt(0);  // the LDS loads and the weight fragments have landed
-            __syncthreads();
-            mfma_chunk<DT, MT, NT, SMAX>(a, As, rb, bfr, acc, c0, n0, wave, lane, steps, kpc);
-        }
-        // Sum the 8 waves' partial tiles: every wave parks its tile in LDS, then
-        // each thread adds the eight copies of its output vector.
-        __syncthreads();  // all waves done reading the staged windows
-        park_partials<MT, NT, PSTR>(part, acc, wave, lane);
-        __syncthreads();
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-            const int v = tid + o * NTHR;
-            if (v >= BM * VPR) break;
-            const int row = v / VPR, col = (v - row * VPR) * 8;
-            const int r = m0 + row;
-            const int co = n0 + col;
-            if (r >= mrows || co >= g.cout) continue;
-            const int nval = min(8, g.cout - co);  // 8, or 4 for an fp32 tail
-            float sum[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float x = s_bias[col + j];
-#pragma unroll
-                for (int w = 0; w < NW; ++w) x += part[(w * BM + row) * PSTR + col + j];
-                sum[j] = x;
-            }
-            const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
-            const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
-            if (FUSED) {
-                const int ls = slot - s_lo, n = s_n[ls];
-                if (n < 0) continue;
-                const int y = s_oy[ls] + py, x = s_ox[ls] + px;
-                if (y >= g.ho || x >= g.wo) continue;
-                store_row8<DT>(a.dst + ((((size_t)n * g.ho + y) * g.wo + x) * g.cout + co) * ES, sum, nval == 8);
-            } else {
-                store_row8<DT>(a.dst + ((((size_t)slot * g.b + py) * g.b + px) * g.cout + co) * ES, sum, nval == 8);
-            }
-        }
-    }
-    if (FUSED && (a.cc.nvec > 0 || a.prev_idx)) {
-        int cnt = cnt_seen;
-        if (ntiles < 0) {  // this workgroup had no tile position at all
-            cnt = min(max(__hip_atomic_load(a.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0), g.cap);
-            ntiles = tiles_of(cnt);
-        }
-        // this workgroup's part: vectors of the copy, or slots of the previous list
-        long long lo, hi;
-        if (a.prev_idx) {
-            const int np = clamp_count(a.prev_count, g.cap);
-            restore_split(np, ntiles, grid, blockIdx.x, lo, hi);
-        } else {
-            copy_split(a.cc, ntiles, grid, blockIdx.x, lo, hi);
-        }
-        if (lo < hi) {
-            uint32_t *bm = nullptr;
-            if (spec_done) {  // the first NTHR entries are in; add the rest
-                bm = s_bm;
-                __syncthreads();
-                for (int e = NTHR + tid; e < cnt; e += NTHR) {
-                    const int v = a.idx[e];
-                    if (v >= 0 && v < g.cap) atomicOr(&s_bm[v >> 5], 1u << (v & 31));
-                }
-                __syncthreads();
-            } else if (spec_bm || bm_words * 4 <= c.lds_bytes) {
-                bm = spec_bm ? s_bm : (uint32_t *)smem;  // the GEMM's LDS is free now
-                build_bitmap<NTHR>(a.idx, cnt, g.cap, bm);
-            }
-            if (a.prev_idx)
-                restore_slots<NTHR>(g, a.cc, a.prev_idx, (int)lo, 1, (int)hi, bm, a.idx, cnt, a.cache, a.dst);
-            else
-                copy_span<4, NTHR>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, lo, hi);
-        }
-    }
 }
 
 // A workgroup barrier for LDS accesses only.  Each wave waits for its own LDS
@@ -933,16 +587,6 @@ static int resident_per_cu(K kernel, int lds) {
     return n;
 }
 
-// The persistent grid: every resident slot of every CU, and no more (a
-// workgroup that cannot start until another ends only delays the kernel).
-template <typename K>
-static unsigned conv_grid(K kernel, const ConvArgs &args) {
-    long grid = (long)args.c.cus * resident_per_cu(kernel, args.c.lds_bytes);
-    if (args.c.grid < grid) grid = args.c.grid;  // the host's cap: tiles at full capacity
-    if (grid > 8) grid = grid / 8 * 8;           // keep tile t on XCD t % 8 across passes
-    return (unsigned)(grid > 0 ? grid : 1);
-}
-
 template <int DT, int MT, int NT>
 static hipError_t launch_conv_t(int fused, const ConvArgs &args, hipStream_t st) {
     if (fused && args.ws) {  // the split over input channels, then the combine (and the copy)
@@ -962,12 +606,8 @@ static hipError_t launch_conv_t(int fused, const ConvArgs &args, hipStream_t st)
         const int bm = args.cc.nvec > 0 && ((args.g.cap + 31) / 32) * 4 <= 64 * 1024 ? ((args.g.cap + 31) / 32) * 4 : 0;
         auto kc = k_split_combine<DT, MT, NT>;
         hipLaunchKernelGGL(kc, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), bm, st, args, slots);
-    } else if (fused) {
-        auto k = k_conv<DT, MT, NT, true>;
-        hipLaunchKernelGGL(k, dim3(conv_grid(k, args)), dim3(kConvThreads), args.c.lds_bytes, st, args);
     } else {
-        auto k = k_conv<DT, MT, NT, false>;
-        hipLaunchKernelGGL(k, dim3(conv_grid(k, args)), dim3(kConvThreads), args.c.lds_bytes, st, args);
+        return hipErrorInvalidValue;  // the unsplit layer and the block conv run on k_layer (kernels_layer.hip)
     }
     return hipGetLastError();
 }

@@ -1,0 +1,480 @@
+// kernels_layer.hip -- the fused sparse layer (steps 3-5 in one kernel) and
+// the block convolution of the three-call path (step 4), as an implicit GEMM
+// on the matrix cores of gfx950.
+//
+// SIGE README mirror, "Overview": the input window of every active block (its
+// halo of k-1 pixels included) is gathered from the edited activation, the
+// convolution runs on the stacked windows, and each output block is written
+// into the cached output of the original image.  Here the three happen in one
+// kernel and no block tensor is materialised: windows go from the activation
+// into LDS, results from the matrix cores into the output image.
+//
+// The GEMM: M = listed blocks x b*b output pixels, flattened over the list (so
+// 6x6 blocks waste nothing to 16-row MFMA tiles); N = c_out; K = k*k*c_in,
+// walked as (tap, slice of KS input channels) steps.  A workgroup of 4 waves
+// owns a tile of 16*MT rows x 16*NT output channels; the waves split the K
+// steps in contiguous runs and each accumulates the whole tile, so every
+// staged window element is read from LDS by one wave only.  Two workgroups
+// share a CU, so one's memory round trips overlap the other's MFMAs.
+//
+// The critical path of a tile, at small edits the whole launch:
+//   1. the list length and the block index of each of the tile's slots (one
+//      vector load per lane, issued first), and this wave's weight fragments
+//      (L2 into registers; a wave's fragments are its own);
+//   2. each wave decodes the slots' window origins in its own lanes and
+//      stages its share of the windows straight into LDS
+//      (global_load_lds_dwordx4), lane l taking slot l's origin by
+//      ds_bpermute -- no slot table, no barrier before the window loads;
+//   3. one barrier, the MFMAs (A from LDS, B from registers);
+//   4. the 4 partial tiles parked in LDS in accumulator layout (16-byte
+//      writes and reads, no bank conflicts), summed, bias added, rounded
+//      once, transposed through LDS and stored as 16-byte rows.
+// Tile t runs on XCD t % 8 and the N tiles of one M tile share it, so a
+// window is fetched into one XCD's L2.  With TAIL, the workgroups then copy
+// the cache outside the listed blocks (copy_cached), or restore the previous
+// edit's blocks (sequential edits), as split by copy_split / restore_split.
+#include <type_traits>
+
+#include "conv_common.h"
+
+namespace sige {
+
+// Source of the window vectors that are zero (outside the image, past c_in,
+// pad slots): every such lane of a staging load reads these 16 bytes.
+__device__ __attribute__((aligned(16))) const u32x4 k_zero16 = {0u, 0u, 0u, 0u};
+
+struct LayerArgs {
+    const uint8_t *src;   // edited activation (fused) or stacked input blocks
+    const uint8_t *w;     // KRSC weights
+    const float *bias;    // fp32 [c_out] or NULL
+    const int32_t *idx;   // block list (fused)
+    const int32_t *count;
+    uint8_t *dst;         // output image (fused) or output blocks
+    const uint8_t *cache;          // TAIL: the cached output
+    const int32_t *prev_idx;       // TAIL restore: the previous edit's list (NULL: copy)
+    const int32_t *prev_count;
+    Geo g;
+    LayerCfg c;
+    CopyCfg cc;
+};
+
+__device__ __forceinline__ void layer_tile(const LayerCfg &c, int t, int &tm, int &tn) {
+    if (c.xcd) {
+        const int r8 = t >> 3;
+        tn = r8 % c.ntn;
+        tm = (r8 / c.ntn) * 8 + (t & 7);
+    } else {
+        tn = t % c.ntn;
+        tm = t / c.ntn;
+    }
+}
+
+// Tiles (padding included) for a list of cnt blocks.
+template <int BM>
+__device__ __forceinline__ int layer_tiles(const LayerCfg &c, int cnt, int b2) {
+    const int mtn = (cnt * b2 + BM - 1) / BM;
+    return (c.xcd ? (mtn + 7) / 8 * 8 : mtn) * c.ntn;
+}
+
+// This wave's weight fragments of the K steps st0, st0 + 1, ... of the chunk
+// at input channel c0 (lane l: column l % 16 of each N subtile and the EPV
+// input channels at (l / 16) * EPV of the step's slice).  wcol[nt] is the
+// lane's column offset into the weights; the step's (tap, slice) offset is
+// uniform, so each load is a scalar base plus a 32-bit lane offset.  Channels
+// past c_in (a partial last chunk) read the last valid ones of the column:
+// their products meet zeros in the staged windows.  `dummy` points every
+// lane at the first fragment instead (one cache line), for a workgroup that
+// does not know yet whether it has a tile.
+template <int DT, int NT, int SMAX>
+__device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, const LayerCfg &c,
+                                              u32x4 (&bfr)[SMAX][NT], const int (&wcol)[NT], int c0, int st0,
+                                              int kl, bool dummy) {
+    constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
+    const uint32_t keep = dummy ? 0u : ~0u;  // masks instead of selects: no branches between the loads
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int stp = min(st0 + j, c.steps - 1);
+        const int tap = stp >> c.lkpc, cb = c0 + (stp & (c.kpc - 1)) * KS;
+        const uint8_t *base = w + ((uint32_t)((tap * g.cin + cb) * ES) & keep);
+        const int lch = min(kl, g.cin - EPV - cb) * ES;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bfr[j][nt] = ld16(base + ((uint32_t)(wcol[nt] + lch) & keep));
+    }
+}
+
+template <int DT, int MT, int NT, bool FUSED, bool TAIL>
+__global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
+    constexpr int NW = kLayerWaves, NTHR = kLayerThreads;
+    constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
+    constexpr int BM = 16 * MT, BN = 16 * NT, NF = MT * NT;
+    constexpr int SMAX = kLayerFrags / NT;  // K steps per wave and chunk (weights in registers)
+    constexpr int JMAX = kLayerGroups;      // staging groups per wave and block slot
+    constexpr int VPR = BN * ES / 16;       // 16-byte output vectors per tile row
+    static_assert(BM <= 64, "a tile touches at most 64 block slots: one per lane");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const Geo &g = a.g;
+    const LayerCfg &c = a.c;
+    // Every argument the tile path reads, in SGPRs at once: one batch of scalar
+    // loads instead of a round trip at each first use.
+    asm volatile("" ::"s"(a.src), "s"(a.w), "s"(a.bias), "s"(a.idx), "s"(a.count), "s"(a.dst), "s"(g.h), "s"(g.w),
+                 "s"(g.cin), "s"(g.cout), "s"(g.k), "s"(g.s), "s"(g.p), "s"(g.b), "s"(g.ho), "s"(g.wo));
+    asm volatile("" ::"s"(g.nby), "s"(g.nbx), "s"(g.ib), "s"(g.cap), "s"(c.ck), "s"(c.nch), "s"(c.kpc),
+                 "s"(c.lkpc), "s"(c.steps), "s"(c.spw), "s"(c.vpc), "s"(c.ps), "s"(c.rs), "s"(c.gps), "s"(c.sb), "s"(c.ntn),
+                 "s"(c.xcd));
+    asm volatile("" ::"s"(c.tiles_cap), "s"(c.spec), "s"(c.m_ps), "s"(c.m_rs), "s"(c.m_b2),
+                 "s"(c.m_b));
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
+    const int mcap = g.cap * b2;  // output rows at capacity
+    const int grid = gridDim.x;
+    const int st0 = wave * c.spw;                                                     // this wave's K steps
+    const int nst = __builtin_amdgcn_readfirstlane(max(0, min(c.steps - st0, c.spw)));  // [st0, st0 + nst)
+    const int kl = (lane >> 4) * EPV;  // this lane's channels within a K slice
+
+    // The list length, as a vector load issued before anything else (cap >> 31
+    // is 0: the per-lane address keeps the value in a vector register, so the
+    // compiler does not move its wait up to the load).
+    const int cnt_raw = a.count[lane & (g.cap >> 31)];
+    int cnt = -1, ntiles = -1, mrows = 0;
+    int tn_w = -1;  // N tile whose (single-chunk) weights are in the registers
+    u32x4 bfr[SMAX][NT];
+
+    // LDS layout of a staged window, in 16-byte units: pixel (yy, xx) holds its
+    // vpc vectors at yy*rs + xx*ps (ps = vpc + 1: one pad unit per pixel; rs
+    // = b mod 16: one pad run per window row), so the 16 rows of an MFMA
+    // fragment -- consecutive output pixels of a block, row after row -- fall on
+    // 16 different 16-byte bank groups at every tap.  Block slot l's window
+    // starts at unit l*sb/16 + (l*b*b mod 16), which continues that pattern
+    // across the blocks of a tile.
+    //
+    // Staging table: this wave stages the 64-unit groups gj = wave + 4 jj of
+    // every block slot's window.  Per lane and jj: the byte offset of its
+    // 16-byte vector from the window origin, and (row, column, vector) in the
+    // window (-1: a pad unit or past the window).  The same for every tile.
+    int loff[JMAX], pk[JMAX];
+#pragma unroll
+    for (int jj = 0; jj < JMAX; ++jj) {
+        const int gj = wave + NW * jj;
+        const int u = gj * 64 + lane;
+        const int yy = fdiv(u, c.m_rs), rem = u - yy * c.rs;
+        const int xx = fdiv(rem, c.m_ps), cv = rem - xx * c.ps;
+        const bool act = gj < c.gps && yy < g.ib && xx < g.ib && cv < c.vpc;
+        pk[jj] = act ? (yy | (xx << 8) | (cv << 16)) : -1;
+        loff[jj] = FUSED ? ((yy * g.w + xx) * g.cin + cv * EPV) * ES : ((yy * g.ib + xx) * g.cin + cv * EPV) * ES;
+    }
+    // this wave's first K step as (tap column kx, unit offset of the tap in the window, slice)
+    int kk0, kx0, toff0;
+    {
+        const int tap = st0 >> c.lkpc;
+        kk0 = st0 & (c.kpc - 1);
+        const int ky = tap / g.k;
+        kx0 = tap - ky * g.k;
+        toff0 = ky * c.rs + kx0 * c.ps;
+    }
+
+    // One tile.  The first tile of the workgroup is a separate instantiation
+    // (FIRST): its loads before the list length is known are unconditional, so
+    // the compiler's wait for the block indices does not cover the weights.
+    // Returns false when the workgroup has no more tiles.
+    auto tile = [&](int t, auto first_tag) __attribute__((always_inline)) -> bool {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        int tm, tn;
+        layer_tile(c, t, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int mc = min(m0, mcap - 1);  // padding tiles past capacity read the last slot
+        const int s_lo = fdiv(mc, c.m_b2);
+        const int ns = min(g.cap - 1, fdiv(min(m0 + BM - 1, mcap - 1), c.m_b2)) - s_lo + 1;
+        // the first round trip: slot s_lo + lane's block index and the bias of
+        // this lane's columns; on the first tile also this wave's weight
+        // fragments (the first workgroup of a CU fetches them before the list
+        // length is known; the others load one line instead, then the weights
+        // once the tile is known to exist)
+        const int lin = FUSED ? a.idx[s_lo + min(lane, ns - 1)] : 0;
+        float bcol[NT];
+        int wcol[NT];
+        const float *bsrc = a.bias ? a.bias : (const float *)a.w;  // any readable floats without a bias
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = min(n0 + nt * 16 + (lane & 15), g.cout - 1);
+            bcol[nt] = bsrc[col];
+            wcol[nt] = col * k2 * g.cin * ES;
+        }
+        const bool early_w = (int)blockIdx.x < c.spec;
+        if constexpr (FIRST) {
+            layer_weights<DT, NT, SMAX>(a.w, g, c, bfr, wcol, 0, st0, kl, !early_w);
+            __builtin_amdgcn_sched_barrier(0);
+            cnt = min(max(cnt_raw, 0), g.cap);
+            ntiles = layer_tiles<BM>(c, cnt, b2);
+            mrows = cnt * b2;
+            if (t >= ntiles) return false;
+        }
+        if (m0 >= mrows) return true;  // a padding tile
+        const bool need_w = FIRST ? !early_w : (c.nch > 1 || tn != tn_w);
+        tn_w = c.nch > 1 ? -1 : tn;
+
+        // slot l = lane l's image, window origin and output-block origin
+        int sn = -1, siy = 0, six = 0, soy = 0, sox = 0;
+        if (FUSED) {
+            int n, by, bx;
+            if (lane < ns && decode_block(g, lin, n, by, bx)) {
+                sn = n;
+                siy = by * g.b * g.s - g.p;
+                six = bx * g.b * g.s - g.p;
+                soy = by * g.b;
+                sox = bx * g.b;
+            }
+        }
+        // LDS byte offset of this lane's row in each M subtile (tap 0, this lane's channels)
+        int rb[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = m0 + mt * 16 + (lane & 15);
+            int off = 0;
+            if (r < mrows) {
+                const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
+                const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+                const int l = slot - s_lo;
+                off = l * c.sb + (((l * b2) & 15) + py * g.s * c.rs + px * g.s * c.ps) * 16;
+            }
+            rb[mt] = off + kl * ES;
+        }
+        f32x4 acc[MT][NT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int ch = 0; ch < c.nch; ++ch) {
+            const int c0 = ch * c.ck;
+            const bool full = c0 + c.ck <= g.cin;  // every channel of the chunk exists
+            if (ch > 0) __syncthreads();  // every wave is done with the previous chunk's windows
+            // Stage the windows (the layout above): this wave fills groups wave + 4 jj
+            // of every slot's window, lane i writing 16 bytes at the group's base + 16 i.
+            for (int l = 0; l < ns; ++l) {
+                const int n = FUSED ? __builtin_amdgcn_readlane(sn, l) : 0;
+                const int iy0 = FUSED ? __builtin_amdgcn_readlane(siy, l) : 0;
+                const int ix0 = FUSED ? __builtin_amdgcn_readlane(six, l) : 0;
+                const bool inner = !FUSED || (n >= 0 && iy0 >= 0 && iy0 + g.ib <= g.h && ix0 >= 0 &&
+                                              ix0 + g.ib <= g.w);
+                const uint8_t *base =
+                    FUSED ? a.src + ((((long)n * g.h + iy0) * g.w + ix0) * g.cin + c0) * (long)ES
+                          : a.src + (((size_t)(s_lo + l) * ib2) * g.cin + c0) * ES;
+                uint8_t *dst0 = smem + l * c.sb + ((l * b2) & 15) * 16;
+#pragma unroll
+                for (int jj = 0; jj < JMAX; ++jj) {
+                    const int gj = wave + NW * jj;
+                    if (gj >= c.gps) continue;
+                    const int q = pk[jj];
+                    bool ok = q >= 0;
+                    if (!(inner && full)) {
+                        const int yy = q & 255, xx = (q >> 8) & 255, cv = q >> 16;
+                        ok = ok && n >= 0 && c0 + cv * EPV < g.cin && iy0 + yy >= 0 && iy0 + yy < g.h &&
+                             ix0 + xx >= 0 && ix0 + xx < g.w;
+                    }
+                    // every lane loads: its vector, or the zero vector
+                    const void *src = ok ? (const void *)(base + (uint32_t)loff[jj]) : (const void *)&k_zero16;
+                    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst0 + gj * 1024),
+                                                     16, 0, 0);
+                }
+            }
+            // the weights, when the registers do not hold this chunk's yet
+            if (ch > 0 || need_w) layer_weights<DT, NT, SMAX>(a.w, g, c, bfr, wcol, c0, st0, kl, false);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's windows and weights have landed
+            __syncthreads();
+            // This wave's K steps: A fragments from LDS, B from registers.  Step
+            // j + 1's reads are issued (unconditionally, at the last step's
+            // address past the wave's run) while step j's MFMAs run, so every
+            // LDS wait is exact.
+            {
+                int kk = kk0, kx = kx0, toff = toff0;
+                u32x4 av[2][MT];
+                int ua = (toff + kk * 4) * 16;  // a K slice is 4 units (KS * ES = 64 bytes)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) av[0][mt] = *(const u32x4 *)(smem + rb[mt] + ua);
+#pragma unroll
+                for (int j = 0; j < SMAX; ++j) {
+                    if (j + 1 < SMAX) {
+                        if (j + 1 < nst) {
+                            if (++kk == c.kpc) {
+                                kk = 0;
+                                toff += c.ps;
+                                if (++kx == g.k) {
+                                    kx = 0;
+                                    toff += c.rs - g.k * c.ps;
+                                }
+                            }
+                            ua = (toff + kk * 4) * 16;
+                        }
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) av[(j + 1) & 1][mt] = *(const u32x4 *)(smem + rb[mt] + ua);
+                    }
+                    if (j < nst) {
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+                                acc[mt][nt] = MfmaStep<DT>::run(av[j & 1][mt], bfr[j][nt], acc[mt][nt]);
+                    }
+                }
+            }
+        }
+
+        // Epilogue: park the 4 partial tiles in accumulator layout, sum them per
+        // (fragment, lane), add the bias, round, transpose through LDS, store rows.
+        __syncthreads();  // every wave is done reading the windows (the partials take their LDS)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *(f32x4 *)(smem + (((wave * NF + mt * NT + nt) << 6) + lane) * 16) = acc[mt][nt];
+        __syncthreads();
+        uint8_t *otile = smem + NW * NF * 64 * 16;  // the rounded tile, [BM][BN] in the storage type
+#pragma unroll
+        for (int e0 = 0; e0 < NF * 64; e0 += NTHR) {
+            const int f = (e0 + tid) >> 6;  // fragment f, lane `lane` of it
+            f32x4 s = *(const f32x4 *)(smem + ((f << 6) + lane) * 16);
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                const f32x4 v = *(const f32x4 *)(smem + (((w * NF + f) << 6) + lane) * 16);
+                s += v;
+            }
+            const int mt = f / NT, nt = f - mt * NT;
+            float bv = bcol[0];
+#pragma unroll
+            for (int q = 1; q < NT; ++q) bv = nt == q ? bcol[q] : bv;
+            if (!a.bias) bv = 0.f;
+            const int col = nt * 16 + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = mt * 16 + (lane >> 4) * 4 + i;
+                const float v = s[i] + bv;
+                if constexpr (DT == 0) {
+                    *(float *)(otile + (row * BN + col) * 4) = v;
+                } else if constexpr (DT == 1) {
+                    *(__bf16 *)(otile + (row * BN + col) * 2) = (__bf16)v;
+                } else {
+                    *(_Float16 *)(otile + (row * BN + col) * 2) = (_Float16)v;
+                }
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < BM * VPR; e += NTHR) {
+            const int row = e / VPR, v = e - row * VPR;
+            const int r = m0 + row, co = n0 + v * EPV;
+            const int slot = fdiv(min(r, mcap - 1), c.m_b2), pix = min(r, mcap - 1) - slot * b2;
+            const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+            const u32x4 val = *(const u32x4 *)(otile + row * BN * ES + v * 16);
+            if (FUSED) {
+                const int l = min(max(slot - s_lo, 0), 63);
+                const int pn = __builtin_amdgcn_ds_bpermute(l << 2, sn);
+                const int y = __builtin_amdgcn_ds_bpermute(l << 2, soy) + py;
+                const int x = __builtin_amdgcn_ds_bpermute(l << 2, sox) + px;
+                if (r >= mrows || co >= g.cout || pn < 0 || y >= g.ho || x >= g.wo) continue;
+                __builtin_nontemporal_store(
+                    val, (u32x4 *)(a.dst + ((((size_t)pn * g.ho + y) * g.wo + x) * g.cout + co) * ES));
+            } else {
+                if (r >= mrows || co >= g.cout) continue;
+                __builtin_nontemporal_store(val, (u32x4 *)(a.dst + (((size_t)slot * b2 + pix) * g.cout + co) * ES));
+            }
+        }
+        __syncthreads();  // the next tile's windows reuse this LDS
+        return true;
+    };
+
+    if ((int)blockIdx.x < c.tiles_cap && tile(blockIdx.x, std::true_type{})) {
+        for (int t = blockIdx.x + grid; t < ntiles; t += grid)
+            if (!tile(t, std::false_type{})) break;
+    }
+
+    if (TAIL) {
+        if (cnt < 0) {  // this workgroup had no tile position at all
+            cnt = min(max(cnt_raw, 0), g.cap);
+            ntiles = layer_tiles<BM>(c, cnt, b2);
+        }
+        long long lo, hi;
+        if (a.prev_idx) {
+            const int np = clamp_count(a.prev_count, g.cap);
+            restore_split(np, ntiles, grid, blockIdx.x, lo, hi);
+        } else {
+            copy_split(a.cc, ntiles, grid, blockIdx.x, lo, hi);
+        }
+        if (lo < hi) {
+            uint32_t *bm = nullptr;
+            if (((g.cap + 31) >> 5) * 4 <= c.lds_bytes) {  // bitmap of listed blocks in LDS, else binary search
+                bm = (uint32_t *)smem;
+                build_bitmap<NTHR>(a.idx, cnt, g.cap, bm);
+            }
+            if (a.prev_idx)
+                restore_slots<NTHR>(g, a.cc, a.prev_idx, (int)lo, 1, (int)hi, bm, a.idx, cnt, a.cache, a.dst);
+            else
+                copy_span<4, NTHR>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, lo, hi);
+        }
+    }
+}
+
+// Workgroups of `kernel` resident on one CU with `lds` bytes of dynamic LDS
+// (register and LDS limits), from the runtime; cached per kernel and size.
+template <typename K>
+static int layer_resident(K kernel, int lds) {
+    struct Entry {
+        const void *k;
+        int lds, n;
+    };
+    static thread_local Entry cache[32];
+    static thread_local int used = 0;
+    for (int i = 0; i < used; ++i)
+        if (cache[i].k == (const void *)kernel && cache[i].lds == lds) return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kLayerThreads, lds) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = 1;
+    }
+    cache[used < 32 ? used++ : 31] = Entry{(const void *)kernel, lds, n};
+    return n;
+}
+
+template <int DT, int MT, int NT, bool FUSED, bool TAIL>
+static hipError_t launch_layer_k(const LayerArgs &args, hipStream_t st) {
+    auto k = k_layer<DT, MT, NT, FUSED, TAIL>;
+    const LayerCfg &c = args.c;
+    long grid = (long)c.cus * layer_resident(k, c.lds_bytes);
+    if (!TAIL && c.tiles_cap < grid) grid = c.tiles_cap;  // nothing past the tiles at capacity
+    if (grid > 8) grid = grid / 8 * 8;                     // keep tile t on XCD t % 8 across passes
+    LayerArgs a = args;
+    a.c.spec = (int)(grid < c.cus ? grid : c.cus);         // the first workgroup of each CU
+    hipLaunchKernelGGL(k, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kLayerThreads), c.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, int MT, int NT>
+static hipError_t launch_layer_t(int fused, bool tail, const LayerArgs &a, hipStream_t st) {
+    if (!fused) return launch_layer_k<DT, MT, NT, false, false>(a, st);
+    return tail ? launch_layer_k<DT, MT, NT, true, true>(a, st) : launch_layer_k<DT, MT, NT, true, false>(a, st);
+}
+
+template <int DT>
+static hipError_t launch_layer_dt(int fused, bool tail, const LayerArgs &a, hipStream_t st) {
+    switch (a.c.mt * 10 + a.c.nt) {
+    case 42: return launch_layer_t<DT, 4, 2>(fused, tail, a, st);
+    case 41: return launch_layer_t<DT, 4, 1>(fused, tail, a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
+                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
+                        const int32_t *prev_count, const Geo &g, const LayerCfg &cfg, const CopyCfg &cc,
+                        hipStream_t st) {
+    const LayerArgs a{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
+                      (const uint8_t *)cache, prev_idx, prev_count, g, cfg, cc};
+    const bool tail = fused && (cc.nvec > 0 || prev_idx);
+    switch (dt) {
+    case 0: return launch_layer_dt<0>(fused, tail, a, st);
+    case 1: return launch_layer_dt<1>(fused, tail, a, st);
+    default: return launch_layer_dt<2>(fused, tail, a, st);
+    }
+}
+
+}  // namespace sige

@@ -225,6 +225,93 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
     return SIGE_OK;
 }
 
+// Launch configuration of k_layer (kernels_layer.hip).  A wave holds the
+// weight fragments of at most kLayerFrags/NT K steps of a chunk, so a chunk
+// has at most 4*kLayerFrags/NT steps: kpc <= floor(4*kLayerFrags/(NT*k*k))
+// K slices per tap, a power of 2.  Among those, the fewest K slices in all
+// (then the fewest chunks) whose staged windows fit in half of the CU's LDS
+// (two workgroups per CU), else in all of it.  A block slot's staged window
+// takes gps groups of 64 16-byte units (at most 4*kLayerGroups) plus 16 units
+// for its bank rotation (see kernels_layer.hip); the LDS also holds the
+// epilogue's 4 partial tiles and the rounded tile.
+int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
+    sige::LayerCfg c{};
+    c.mt = 4;
+    c.nt = 2;
+    const int es = sige::elem_bytes(dt);
+    const int ks = dt == SIGE_F32 ? 16 : 32;
+    const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
+    const int nw = sige::kLayerWaves;
+    if ((nw * (sige::kLayerFrags / c.nt)) / k2 < 1) c.nt = 1;  // large kernels: 16 channels per tile
+    const int max_kpc = (nw * (sige::kLayerFrags / c.nt)) / k2;  // K slices per tap and chunk
+    if (max_kpc < 1) return fail(SIGE_ERANGE, "kernel size %d too large for the register-resident weights", g.k);
+    const int BM = 16 * c.mt, BN = 16 * c.nt;
+    int ns = (BM - 1) / b2 + 2;
+    if (ns > BM) ns = BM;
+    if (ns > g.cap) ns = g.cap;
+    if (((long)g.cap * b2 + BM) * b2 > 0x7FFFFFFFL) return fail(SIGE_ERANGE, "too many output rows for one launch");
+    // 32-bit offsets of a staged vector from its window origin, and of a weight column
+    if (((long)(g.ib - 1) * g.w + g.ib) * (long)g.cin * es > 0x7FFFFFFFL)
+        return fail(SIGE_ERANGE, "a %dx%d window of %d-wide rows of %d channels exceeds 32-bit offsets", g.ib, g.ib,
+                    g.w, g.cin);
+    const DevInfo dv = dev_info();
+    const long epi = (long)nw * c.mt * c.nt * 64 * 16 + (long)BM * BN * es;  // partial tiles + rounded tile
+    const int kslices = (g.cin + ks - 1) / ks;
+    int best_kpc = 0, best_gps = 0;
+    long best_lds = 0;
+    for (int pass = 0; pass < 2 && !best_kpc; ++pass) {
+        const long limit = (pass == 0 ? dv.lds / 2 : (long)dv.lds) - 1024;  // 1 KiB: static LDS, alignment
+        long best_cost = 0;
+        for (int kpc = 1; kpc <= max_kpc; kpc *= 2) {
+            const int nch = (kslices + kpc - 1) / kpc;
+            const int ck = kpc * ks;
+            if (ck * es / 16 > 255) break;
+            const int ps = ck * es / 16 + 1;
+            const int rs = g.ib * ps + (((g.b - g.ib * ps) % 16) + 16) % 16;
+            const int gps = (g.ib * rs + 63) / 64;
+            if (gps > nw * sige::kLayerGroups) break;
+            const long need_w = (long)ns * (64 * gps + 16) * 16;
+            const long need = need_w > epi ? need_w : epi;
+            if (need > limit) break;
+            const long cost = (long)nch * kpc * 1024 + nch;  // K slices in all, then chunks
+            if (!best_kpc || cost < best_cost) {
+                best_kpc = kpc;
+                best_gps = gps;
+                best_lds = need;
+                best_cost = cost;
+            }
+        }
+    }
+    if (!best_kpc) return fail(SIGE_ERANGE, "staged windows (%d slots of %dx%d) do not fit in LDS", ns, g.ib, g.ib);
+    c.kpc = best_kpc;
+    c.lkpc = 0;
+    while ((1 << c.lkpc) < best_kpc) ++c.lkpc;
+    c.ck = best_kpc * ks;
+    c.nch = (kslices + best_kpc - 1) / best_kpc;
+    c.steps = k2 * c.kpc;
+    c.spw = (c.steps + nw - 1) / nw;
+    c.vpc = c.ck * es / 16;
+    c.ps = c.vpc + 1;
+    c.rs = g.ib * c.ps + (((g.b - g.ib * c.ps) % 16) + 16) % 16;
+    c.gps = best_gps;
+    c.sb = (64 * best_gps + 16) * 16;
+    c.lds_bytes = (int)best_lds;
+    c.ntn = (g.cout + BN - 1) / BN;
+    const long mtn = ((long)g.cap * b2 + BM - 1) / BM;
+    c.xcd = mtn >= 8;
+    const long tiles = (c.xcd ? (mtn + 7) / 8 * 8 : mtn) * c.ntn;
+    if (tiles > 0x7FFFFFFFL) return fail(SIGE_ERANGE, "too many tiles for one launch");
+    c.tiles_cap = (int)tiles;
+    c.cus = dv.cus;
+    c.spec = 0;
+    c.m_ps = sige::fast_div_magic(c.ps);
+    c.m_rs = sige::fast_div_magic(c.rs);
+    c.m_b2 = sige::fast_div_magic(b2);
+    c.m_b = sige::fast_div_magic(g.b);
+    *out = c;
+    return SIGE_OK;
+}
+
 // Attention: the token grid as a k = 1 geometry, and the workspace the two kernels need.
 int attn_geom(int n, int h, int w, int heads, int head_dim, int block, Geo *g) {
     if (head_dim != sige::kAttnHeadDim) return fail(SIGE_ERANGE, "head_dim %d: only 64 is supported", head_dim);
@@ -511,13 +598,12 @@ int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, 
     const int es = sige::elem_bytes(dtype);
     if (overlap(out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es, blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es))
         return fail(SIGE_EINVAL, "out_blocks overlaps blocks");
-    ConvCfg cfg;
-    if ((rc = choose_conv(g, dtype, 0, 0, &cfg))) return rc;
+    sige::LayerCfg cfg;
+    if ((rc = choose_layer(g, dtype, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, false);
-    return finish(sige::launch_conv(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, nullptr,
-                                    nullptr, g, cfg, cc,
-                                    (hipStream_t)stream),
+    return finish(sige::launch_layer(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, nullptr,
+                                     nullptr, g, cfg, cc, (hipStream_t)stream),
                   "sige_conv_blocks", (hipStream_t)stream);
 }
 
@@ -563,12 +649,12 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
     if (overlap(out, obytes, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
         return fail(SIGE_EINVAL, "out overlaps a_edit");
     if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
-    ConvCfg cfg;
-    if ((rc = choose_conv(g, dtype, 1, copy_cached, &cfg))) return rc;
+    sige::LayerCfg cfg;
+    if ((rc = choose_layer(g, dtype, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
-    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
-                                    nullptr, nullptr, g, cfg, cc, (hipStream_t)stream),
+    return finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
+                                     nullptr, nullptr, g, cfg, cc, (hipStream_t)stream),
                   "sige_sparse_conv_layer", (hipStream_t)stream);
 }
 
@@ -607,9 +693,9 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
     if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
     ConvCfg cfg;
     if ((rc = choose_conv(g, dtype, 1, 1, &cfg, 1))) return rc;
-    if ((rc = device_ready())) return rc;
     const long need = sige::split_workspace_bytes(dtype, g, cfg);
     if (need < 0) return fail(SIGE_EINVAL, "unknown tile shape");
+    if ((rc = device_ready())) return rc;
     if (workspace_bytes < need)
         return fail(SIGE_ERANGE, "workspace of %lld bytes, %ld needed", (long long)workspace_bytes, need);
     if (overlap(workspace, (size_t)need, out, obytes) || overlap(workspace, (size_t)need, a_edit, ibytes) ||
@@ -640,12 +726,12 @@ int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const
     if (overlap(out, obytes, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
         return fail(SIGE_EINVAL, "out overlaps a_edit");
     if (overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
-    ConvCfg cfg;
-    if ((rc = choose_conv(g, dtype, 1, 1, &cfg))) return rc;  // the full persistent grid: free workgroups restore
+    sige::LayerCfg cfg;
+    if ((rc = choose_layer(g, dtype, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, false);
-    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, cached, prev_idx, prev_count, g,
-                                    cfg, cc, (hipStream_t)stream),
+    return finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out, cached, prev_idx, prev_count,
+                                     g, cfg, cc, (hipStream_t)stream),
                   "sige_sparse_conv_layer_restore", (hipStream_t)stream);
 }
 

@@ -40,6 +40,27 @@ struct ConvCfg {
     uint32_t m_b2, m_b;    // fast_div_magic(b*b), fast_div_magic(b): output rows -> block slot, pixel
 };
 
+// Launch configuration of the fused layer / block convolution (kernels_layer.hip).
+constexpr int kLayerWaves = 4;                  // waves per workgroup (they split the K steps)
+constexpr int kLayerThreads = 64 * kLayerWaves;
+constexpr int kLayerFrags = 18;                 // weight fragments per lane and chunk (SMAX * NT)
+constexpr int kLayerGroups = 8;                 // 64-slot staging groups per wave and block slot
+struct LayerCfg {
+    int mt, nt;          // 16x16 subtiles per tile along M (rows) and N (output channels)
+    int ck, nch;         // input channels per chunk (kpc K slices), chunks
+    int kpc, lkpc;       // K slices per tap and chunk (a power of 2), its log2
+    int steps, spw;      // K steps per chunk (k*k*kpc), steps per wave
+    int vpc, ps, rs;     // 16-byte vectors of a staged pixel (ck*es/16); LDS units (16 B) per pixel (vpc + 1)
+                         // and per window row (ib*ps + pad, = b mod 16)
+    int gps, sb;         // 64-unit groups of one block slot's staged window; LDS bytes per slot (64 gps + 16 units)
+    int lds_bytes;       // dynamic LDS per workgroup
+    int ntn, xcd;        // N tiles; tile order keeping an M tile's N tiles on one XCD
+    int tiles_cap;       // tiles (padding included) at full capacity
+    int cus;             // compute units of the device
+    int spec;            // workgroups below this fetch their first weights before the list length (set at launch)
+    uint32_t m_ps, m_rs, m_b2, m_b;  // fast_div_magic of ps, rs, b*b, b
+};
+
 // Copy of the cache outside the listed blocks, in 16-byte vectors of the
 // output flattened over (n, y, x, vector of the channel row).
 struct CopyCfg {
@@ -87,6 +108,14 @@ hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const 
                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                        const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
                        hipStream_t st, float *ws = nullptr);
+// The fused layer (fused = 1: src = a_edit, dst = out; with cc.nvec > 0 the
+// cache is copied outside the listed blocks, with prev_idx the previous
+// list's blocks are restored) or the block convolution (fused = 0: src =
+// stacked blocks, dst = output blocks), on kernels_layer.hip's k_layer.
+hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
+                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
+                        const int32_t *prev_count, const Geo &g, const LayerCfg &cfg, const CopyCfg &cc,
+                        hipStream_t st);
 // Bytes of that workspace for g and the launch configuration c (< 0: unknown tile shape).
 long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c);
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,
