@@ -31,8 +31,10 @@
  *     enqueues work on it; results are ready when the stream reaches them.
  *   - The number of active blocks stays on the device: `count` points to one
  *     int32 in device memory written by sige_reduce_mask and read by the later
- *     steps, so no step waits for the host.  Block buffers are sized for the
- *     capacity sige_max_blocks(); only slots [0, *count) are read or written.
+ *     steps, so no step waits for the host.  Lists (idx) and block buffers
+ *     hold sige_max_blocks() entries: a kernel may read idx entries past
+ *     *count (a tile's block indices are fetched before the count arrives)
+ *     and ignores their values; only slots [0, *count) are written or used.
  *   - Every call returns SIGE_OK (0) or a negative code.  Arguments are checked
  *     on the host before anything is enqueued; a rejected call enqueues
  *     nothing.  sige_strerror() names a code; sige_last_error() returns the

@@ -82,7 +82,8 @@ def lib():
         L.sige_strerror.argtypes = [I]
         L.sige_last_error.restype = ctypes.c_char_p
         for f in EXPORTS:
-            if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks", "sige_sparse_attention_workspace"):
+            if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks", "sige_sparse_attention_workspace",
+                         "sige_sparse_conv_layer_split_workspace"):
                 getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -118,6 +119,36 @@ def _dt(t):
         return DTYPE_CODE[t.dtype]
     except KeyError:
         raise SigeError(SIGE_EDTYPE, "dtype", f"unsupported dtype {t.dtype}") from None
+
+
+def _need(t, what, dtype=None, shape=None, numel=None):
+    """Checks a caller tensor's dtype, shape or size before its pointer goes to the library."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {numel} needed")
+
+
+def _need_list(g, idx, count):
+    """A block list holds sige_max_blocks(g) int32 entries (the kernels may read past *count) and
+    its count one int32."""
+    _need(idx, "idx", dtype=torch.int32, numel=sige_max_blocks(g))
+    _need(count, "count", dtype=torch.int32, numel=1)
+
+
+def _need_layer(g, a_edit, w_krsc, bias, cached, out):
+    """Shapes of a layer's tensors: NHWC activation and outputs, KRSC weights, fp32 bias."""
+    d = sige_geom_derive(g)
+    _need(a_edit, "a_edit", shape=(g.n, g.h, g.w, g.c_in))
+    _need(w_krsc, "w_krsc", dtype=a_edit.dtype, shape=(g.c_out, g.k, g.k, g.c_in))
+    _need(bias, "bias", dtype=torch.float32, shape=(g.c_out,))
+    _need(cached, "cached", dtype=a_edit.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
+    _need(out, "out", dtype=a_edit.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
+    return d
 
 
 # ---------------------------------------------------------------------------
@@ -171,6 +202,8 @@ def sige_diff_mask_bits(a_orig, a_edit, thresh=1e-6, bits=None, mask=None, strea
 def sige_reduce_bits(bits, mask_h, mask_w, g: Geom, dilate_blocks=1, idx=None, count=None, stream=None):
     """sige_reduce_mask on a mask packed as sige_diff_mask_bits writes it (mask_h x mask_w per image)."""
     _dev(bits, idx, count)
+    _need_list(g, idx, count)
+    _need(bits, "bits", dtype=torch.int32, numel=g.n * mask_h * mask_w // 32)
     cap = sige_max_blocks(g)
     dev = bits.device
     if idx is None:
@@ -187,6 +220,11 @@ def sige_reduce_bits_copy(bits, mask_h, mask_w, g: Geom, dilate_blocks, cached, 
                           stream=None):
     """sige_reduce_bits with `cached` copied into `out` by the same launch; returns (idx, count, out)."""
     _dev(bits, idx, count, cached, out)
+    _need_list(g, idx, count)
+    _need(bits, "bits", dtype=torch.int32, numel=g.n * mask_h * mask_w // 32)
+    d = sige_geom_derive(g)
+    _need(cached, "cached", shape=(g.n, d.ho, d.wo, g.c_out))
+    _need(out, "out", dtype=cached.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
     cap = sige_max_blocks(g)
     dev = bits.device
     if idx is None:
@@ -209,6 +247,15 @@ def sige_reduce_bits_layers(bits, mask_h, mask_w, geoms, dilate_blocks, idx, cou
     one entry per layer; cached[l] and out[l] may both be None."""
     n = len(geoms)
     _dev(bits, *idx, *count, *(cached or []), *(out or []))
+    if not (len(dilate_blocks) == len(idx) == len(count) == n) or (cached and len(cached) != n) or \
+            (out and len(out) != n):
+        raise ValueError("geoms, dilate_blocks, idx, count (and cached, out) need one entry per layer")
+    for l, gl in enumerate(geoms):
+        _need_list(gl, idx[l], count[l])
+        if cached and out and cached[l] is not None:
+            dl = sige_geom_derive(gl)
+            _need(cached[l], f"cached[{l}]", shape=(gl.n, dl.ho, dl.wo, gl.c_out))
+            _need(out[l], f"out[{l}]", dtype=cached[l].dtype, shape=(gl.n, dl.ho, dl.wo, gl.c_out))
     GA = Geom * n
     IA = ctypes.c_int * n
     VA = ctypes.c_void_p * n
@@ -228,6 +275,8 @@ def sige_reduce_mask(mask, g: Geom, dilate_blocks=1, idx=None, count=None, strea
     if mask.dim() == 2:
         mask = mask.unsqueeze(0)
     _dev(mask, idx, count)
+    _need_list(g, idx, count)
+    _need(mask, "mask", dtype=torch.uint8)
     cap = sige_max_blocks(g)
     dev = mask.device
     if idx is None:
@@ -246,6 +295,11 @@ def sige_reduce_mask_copy(mask, g: Geom, dilate_blocks, cached, out=None, idx=No
     if mask.dim() == 2:
         mask = mask.unsqueeze(0)
     _dev(mask, idx, count, cached, out)
+    _need_list(g, idx, count)
+    _need(mask, "mask", dtype=torch.uint8)
+    d = sige_geom_derive(g)
+    _need(cached, "cached", shape=(g.n, d.ho, d.wo, g.c_out))
+    _need(out, "out", dtype=cached.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
     cap = sige_max_blocks(g)
     dev = mask.device
     if idx is None:
@@ -263,7 +317,10 @@ def sige_reduce_mask_copy(mask, g: Geom, dilate_blocks, cached, out=None, idx=No
 def sige_gather(a_edit, g: Geom, idx, count, blocks=None, stream=None):
     """[cap, ib, ib, c_in]: input windows of the listed blocks (slots < count)."""
     _dev(a_edit, idx, count, blocks)
+    _need_list(g, idx, count)
     d = sige_geom_derive(g)
+    _need(a_edit, "a_edit", shape=(g.n, g.h, g.w, g.c_in))
+    _need(blocks, "blocks", dtype=a_edit.dtype, shape=(max(d.cap, 1), d.ib, d.ib, g.c_in))
     if blocks is None:
         blocks = torch.empty((max(d.cap, 1), d.ib, d.ib, g.c_in), dtype=a_edit.dtype, device=a_edit.device)
     rc = lib().sige_gather(_p(a_edit), _dt(a_edit), ctypes.byref(g), _p(idx), _p(count), _p(blocks),
@@ -278,6 +335,11 @@ def sige_conv_blocks(blocks, w_krsc, bias, g: Geom, count, out_blocks=None, stre
     if w_krsc.dtype != blocks.dtype or (bias is not None and bias.dtype != torch.float32):
         raise ValueError("weights must match the activation dtype; bias must be fp32")
     d = sige_geom_derive(g)
+    _need(count, "count", dtype=torch.int32, numel=1)
+    _need(blocks, "blocks", shape=(max(d.cap, 1), d.ib, d.ib, g.c_in))
+    _need(w_krsc, "w_krsc", shape=(g.c_out, g.k, g.k, g.c_in))
+    _need(bias, "bias", shape=(g.c_out,))
+    _need(out_blocks, "out_blocks", dtype=blocks.dtype, shape=(max(d.cap, 1), g.block, g.block, g.c_out))
     if out_blocks is None:
         out_blocks = torch.empty((max(d.cap, 1), g.block, g.block, g.c_out), dtype=blocks.dtype,
                                  device=blocks.device)
@@ -290,7 +352,11 @@ def sige_conv_blocks(blocks, w_krsc, bias, g: Geom, count, out_blocks=None, stre
 def sige_scatter(out_blocks, idx, count, g: Geom, cached, out=None, copy_cached=True, stream=None):
     """[n, ho, wo, c_out]: cached output with the listed blocks overwritten."""
     _dev(out_blocks, idx, count, cached, out)
+    _need_list(g, idx, count)
     d = sige_geom_derive(g)
+    _need(out_blocks, "out_blocks", shape=(max(d.cap, 1), g.block, g.block, g.c_out))
+    _need(cached, "cached", dtype=out_blocks.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
+    _need(out, "out", dtype=out_blocks.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
     if out is None:
         if not copy_cached:
             raise ValueError("copy_cached=False needs a persistent `out`")
@@ -305,9 +371,8 @@ def sige_sparse_conv_layer(a_edit, w_krsc, bias, cached, idx, count, g: Geom, ou
                            stream=None):
     """Fused gather + conv + scatter into `out` (NHWC [n, ho, wo, c_out])."""
     _dev(a_edit, w_krsc, bias, cached, idx, count, out)
-    if w_krsc.dtype != a_edit.dtype or (bias is not None and bias.dtype != torch.float32):
-        raise ValueError("weights must match the activation dtype; bias must be fp32")
-    d = sige_geom_derive(g)
+    _need_list(g, idx, count)
+    d = _need_layer(g, a_edit, w_krsc, bias, cached if copy_cached else None, out)
     if out is None:
         if not copy_cached:
             raise ValueError("copy_cached=False needs a persistent `out`")
@@ -332,9 +397,8 @@ def sige_sparse_conv_layer_split(a_edit, w_krsc, bias, cached, idx, count, g: Ge
     """The fused layer split over input channels (weight-bound layers); the
     workspace is allocated here when not given."""
     _dev(a_edit, w_krsc, bias, cached, idx, count, out, workspace)
-    if w_krsc.dtype != a_edit.dtype or (bias is not None and bias.dtype != torch.float32):
-        raise ValueError("weights must match the activation dtype; bias must be fp32")
-    d = sige_geom_derive(g)
+    _need_list(g, idx, count)
+    d = _need_layer(g, a_edit, w_krsc, bias, cached if copy_cached else None, out)
     if out is None:
         if not copy_cached:
             raise ValueError("copy_cached=False needs a persistent `out`")
@@ -362,6 +426,11 @@ def sige_restore_blocks(prev_idx, prev_count, idx, count, g: Geom, cached, out, 
     _dev(prev_idx, prev_count, idx, count, cached, out)
     if (idx is None) != (count is None):
         raise ValueError("idx and count must both be given or both be None")
+    _need_list(g, prev_idx, prev_count)
+    _need_list(g, idx, count)
+    d = sige_geom_derive(g)
+    _need(cached, "cached", shape=(g.n, d.ho, d.wo, g.c_out))
+    _need(out, "out", dtype=cached.dtype, shape=(g.n, d.ho, d.wo, g.c_out))
     rc = lib().sige_restore_blocks(_p(prev_idx), _p(prev_count), _p(idx), _p(count), ctypes.byref(g), _dt(cached),
                                    _p(cached), _p(out), _stream(stream))
     _check(rc, "sige_restore_blocks")
@@ -373,8 +442,9 @@ def sige_sparse_conv_layer_restore(a_edit, w_krsc, bias, cached, prev_idx, prev_
     """Sequential edits in one launch: restore the previous list's blocks that
     the new list does not hold, and write the new blocks, into `out`."""
     _dev(a_edit, w_krsc, bias, cached, prev_idx, prev_count, idx, count, out)
-    if w_krsc.dtype != a_edit.dtype or (bias is not None and bias.dtype != torch.float32):
-        raise ValueError("weights must match the activation dtype; bias must be fp32")
+    _need_list(g, prev_idx, prev_count)
+    _need_list(g, idx, count)
+    _need_layer(g, a_edit, w_krsc, bias, cached, out)
     rc = lib().sige_sparse_conv_layer_restore(_p(a_edit), _p(w_krsc), _p(bias), _p(cached), _p(prev_idx),
                                               _p(prev_count), _p(idx), _p(count), _dt(a_edit), ctypes.byref(g),
                                               _p(out), _stream(stream))
@@ -400,6 +470,9 @@ def sige_sparse_attention(q, k, v, idx, count, heads, block, scale=None, cached=
         raise ValueError("q, k and v must match, with heads dividing the channels")
     d = c // heads
     scale = d ** -0.5 if scale is None else scale
+    _need_list(geom(n, h, w, c, c, 1, 1, 0, block), idx, count)
+    _need(cached, "cached", dtype=q.dtype, shape=q.shape)
+    _need(out, "out", dtype=q.dtype, shape=q.shape)
     if out is None:
         if not copy_cached:
             raise ValueError("copy_cached=False needs a persistent `out`")

@@ -108,7 +108,6 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
     constexpr int BM = 16 * MT, BN = 16 * NT, NF = MT * NT;
     constexpr int SMAX = kLayerFrags / NT;  // K steps per wave and chunk (weights in registers)
-    constexpr int JMAX = kLayerGroups;      // staging groups per wave and block slot
     constexpr int VPR = BN * ES / 16;       // 16-byte output vectors per tile row
     static_assert(BM <= 64, "a tile touches at most 64 block slots: one per lane");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -147,23 +146,8 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     // fragment -- consecutive output pixels of a block, row after row -- fall on
     // 16 different 16-byte bank groups at every tap.  Block slot l's window
     // starts at unit l*sb/16 + (l*b*b mod 16), which continues that pattern
-    // across the blocks of a tile.
-    //
-    // Staging table: this wave stages the 64-unit groups gj = wave + 4 jj of
-    // every block slot's window.  Per lane and jj: the byte offset of its
-    // 16-byte vector from the window origin, and (row, column, vector) in the
-    // window (-1: a pad unit or past the window).  The same for every tile.
-    int loff[JMAX], pk[JMAX];
-#pragma unroll
-    for (int jj = 0; jj < JMAX; ++jj) {
-        const int gj = wave + NW * jj;
-        const int u = gj * 64 + lane;
-        const int yy = fdiv(u, c.m_rs), rem = u - yy * c.rs;
-        const int xx = fdiv(rem, c.m_ps), cv = rem - xx * c.ps;
-        const bool act = gj < c.gps && yy < g.ib && xx < g.ib && cv < c.vpc;
-        pk[jj] = act ? (yy | (xx << 8) | (cv << 16)) : -1;
-        loff[jj] = FUSED ? ((yy * g.w + xx) * g.cin + cv * EPV) * ES : ((yy * g.ib + xx) * g.cin + cv * EPV) * ES;
-    }
+    // across the blocks of a tile.  Wave w stages the 64-unit groups w, w + 4,
+    // ... of every block slot's window, one global_load_lds_dwordx4 each.
     // this wave's first K step as (tap column kx, unit offset of the tap in the window, slice)
     int kk0, kx0, toff0;
     {
@@ -262,19 +246,20 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                     FUSED ? a.src + ((((long)n * g.h + iy0) * g.w + ix0) * g.cin + c0) * (long)ES
                           : a.src + (((size_t)(s_lo + l) * ib2) * g.cin + c0) * ES;
                 uint8_t *dst0 = smem + l * c.sb + ((l * b2) & 15) * 16;
-#pragma unroll
-                for (int jj = 0; jj < JMAX; ++jj) {
-                    const int gj = wave + NW * jj;
-                    if (gj >= c.gps) continue;
-                    const int q = pk[jj];
-                    bool ok = q >= 0;
-                    if (!(inner && full)) {
-                        const int yy = q & 255, xx = (q >> 8) & 255, cv = q >> 16;
+                // a compact loop: the same few instruction-cache lines for every group
+#pragma unroll 1
+                for (int gj = wave; gj < c.gps; gj += NW) {
+                    const int u = gj * 64 + lane;  // this lane's unit of the window
+                    const int yy = fdiv(u, c.m_rs), rem = u - yy * c.rs;
+                    const int xx = fdiv(rem, c.m_ps), cv = rem - xx * c.ps;
+                    bool ok = yy < g.ib && xx < g.ib && cv < c.vpc;  // else a pad unit
+                    if (!(inner && full))
                         ok = ok && n >= 0 && c0 + cv * EPV < g.cin && iy0 + yy >= 0 && iy0 + yy < g.h &&
                              ix0 + xx >= 0 && ix0 + xx < g.w;
-                    }
+                    const uint32_t off = FUSED ? ((yy * g.w + xx) * g.cin + cv * EPV) * ES
+                                               : ((yy * g.ib + xx) * g.cin + cv * EPV) * ES;
                     // every lane loads: its vector, or the zero vector
-                    const void *src = ok ? (const void *)(base + (uint32_t)loff[jj]) : (const void *)&k_zero16;
+                    const void *src = ok ? (const void *)(base + off) : (const void *)&k_zero16;
                     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst0 + gj * 1024),
                                                      16, 0, 0);
                 }

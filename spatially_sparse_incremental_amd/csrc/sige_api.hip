@@ -33,6 +33,24 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     return na && nb && x < y + nb && y < x + na;
 }
 
+// A byte range a launch reads or writes (p NULL: none).
+struct Region {
+    const void *p;
+    size_t n;
+};
+
+// Whether any written range overlaps another written range or a read range.
+bool regions_overlap(const Region *wr, int nw, const Region *rd, int nr) {
+    for (int i = 0; i < nw; ++i) {
+        if (!wr[i].p) continue;
+        for (int j = i + 1; j < nw; ++j)
+            if (wr[j].p && overlap(wr[i].p, wr[i].n, wr[j].p, wr[j].n)) return true;
+        for (int j = 0; j < nr; ++j)
+            if (rd[j].p && overlap(wr[i].p, wr[i].n, rd[j].p, rd[j].n)) return true;
+    }
+    return false;
+}
+
 int derive(const sige_geom *gp, Geo *g) {
     if (!gp) return fail(SIGE_EINVAL, "geometry pointer is NULL");
     const sige_geom &q = *gp;
@@ -231,8 +249,8 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
 // K slices per tap, a power of 2.  Among those, the fewest K slices in all
 // (then the fewest chunks) whose staged windows fit in half of the CU's LDS
 // (two workgroups per CU), else in all of it.  A block slot's staged window
-// takes gps groups of 64 16-byte units (at most 4*kLayerGroups) plus 16 units
-// for its bank rotation (see kernels_layer.hip); the LDS also holds the
+// takes gps groups of 64 16-byte units plus 16 units for its bank rotation
+// (see kernels_layer.hip); the LDS also holds the
 // epilogue's 4 partial tiles and the rounded tile.
 int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
     sige::LayerCfg c{};
@@ -269,7 +287,6 @@ int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
             const int ps = ck * es / 16 + 1;
             const int rs = g.ib * ps + (((g.b - g.ib * ps) % 16) + 16) % 16;
             const int gps = (g.ib * rs + 63) / 64;
-            if (gps > nw * sige::kLayerGroups) break;
             const long need_w = (long)ns * (64 * gps + 16) * 16;
             const long need = need_w > epi ? need_w : epi;
             if (need > limit) break;
@@ -393,6 +410,48 @@ int reduce_common(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *
                   what, (hipStream_t)stream);
 }
 
+int split_common(const void *a_edit, const void *w_krsc, const float *bias, const void *cached, const int32_t *idx,
+                 const int32_t *count, int dtype, const sige_geom *gp, void *out, int copy_cached, void *workspace,
+                 int64_t workspace_bytes, void *stream, const char *what) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!a_edit || !w_krsc || !idx || !count || !out || !workspace || (copy_cached && !cached))
+        return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+        (copy_cached && !aligned(cached, 16)))
+        return fail(SIGE_EALIGN, "tensors and workspace must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
+    const int es = sige::elem_bytes(dtype);
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
+    const size_t ibytes = (size_t)g.n * g.h * g.w * g.cin * es;
+    const Region rd[] = {{a_edit, ibytes}, {copy_cached ? cached : nullptr, obytes},
+                         {w_krsc, (size_t)g.cout * g.k * g.k * g.cin * es}, {bias, (size_t)g.cout * 4},
+                         {idx, (size_t)g.cap * 4}, {count, 4}};
+    {
+        const Region wr[] = {{out, obytes}};
+        if (regions_overlap(wr, 1, rd, 6))
+            return fail(SIGE_EINVAL, "out overlaps a_edit, cached, the weights, bias, idx or count");
+    }
+    ConvCfg cfg;
+    if ((rc = choose_conv(g, dtype, 1, 1, &cfg, 1))) return rc;
+    const long need = sige::split_workspace_bytes(dtype, g, cfg);
+    if (need < 0) return fail(SIGE_EINVAL, "unknown tile shape");
+    if ((rc = device_ready())) return rc;
+    if (workspace_bytes < need)
+        return fail(SIGE_ERANGE, "workspace of %lld bytes, %ld needed", (long long)workspace_bytes, need);
+    {
+        const Region wr[] = {{out, obytes}, {workspace, (size_t)need}};
+        if (regions_overlap(wr, 2, rd, 6)) return fail(SIGE_EINVAL, "the workspace overlaps another argument");
+    }
+    const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
+    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
+                                    nullptr, nullptr, g, cfg, cc, (hipStream_t)stream, (float *)workspace),
+                  what, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -499,10 +558,7 @@ int sige_reduce_bits_layers(const uint32_t *bits, int mask_h, int mask_w, int nl
         return fail(mask_w % 32 ? SIGE_EINVAL : SIGE_EALIGN, "bitset mask: width %d must be a multiple of 32 and "
                     "the words 4-byte aligned", mask_w);
     sige::ReduceLayerArgs L[sige::kReduceMaxLayers];
-    struct Region {
-        const void *p;
-        size_t n;
-    } wr[3 * sige::kReduceMaxLayers], rd[1 + sige::kReduceMaxLayers];
+    Region wr[3 * sige::kReduceMaxLayers], rd[1 + sige::kReduceMaxLayers];
     int nw = 0, nr = 0, rc;
     for (int l = 0; l < nlayers; ++l) {
         Geo g;
@@ -518,6 +574,12 @@ int sige_reduce_bits_layers(const uint32_t *bits, int mask_h, int mask_w, int nl
                         mask_h, mask_w, g.h, g.w);
         if (dilate_blocks[l] < 0 || dilate_blocks[l] > 16)
             return fail(SIGE_EINVAL, "layer %d: dilate_blocks=%d outside [0, 16]", l, dilate_blocks[l]);
+        if (g.w > sige::kReduceMaxWidth)
+            return fail(SIGE_ERANGE, "layer %d: conv input width %d exceeds the reduce limit %d", l, g.w,
+                        sige::kReduceMaxWidth);
+        if (g.cap > sige::kReduceMaxBlocks)
+            return fail(SIGE_ERANGE, "layer %d: %d blocks (n*nby*nbx) exceed the reduce limit %d", l, g.cap,
+                        sige::kReduceMaxBlocks);
         if (!sige::reduce_one_launch_ok(mask_h, mask_w, g, 2))
             return fail(SIGE_ERANGE, "layer %d: its pooled mask or block grid exceeds one workgroup "
                         "(build its list with sige_reduce_bits)", l);
@@ -541,13 +603,8 @@ int sige_reduce_bits_layers(const uint32_t *bits, int mask_h, int mask_w, int nl
             L[l].nvec = (long long)(ob / 16);
         }
     }
-    for (int i = 0; i < nw; ++i) {  // what the launch writes overlaps nothing else it touches
-        for (int j = i + 1; j < nw; ++j)
-            if (overlap(wr[i].p, wr[i].n, wr[j].p, wr[j].n)) return fail(SIGE_EINVAL, "outputs of the layers overlap");
-        for (int j = 0; j < nr; ++j)
-            if (overlap(wr[i].p, wr[i].n, rd[j].p, rd[j].n))
-                return fail(SIGE_EINVAL, "an output overlaps the mask or a cache");
-    }
+    if (regions_overlap(wr, nw, rd, nr))  // what the launch writes overlaps nothing else it touches
+        return fail(SIGE_EINVAL, "an output of the layers overlaps another output, the mask or a cache");
     if ((rc = device_ready())) return rc;
     static int copy_wgs = -1;  // SIGE_REDUCE_COPY_WGS overrides the copy's workgroups (tuning)
     if (copy_wgs < 0) {
@@ -577,8 +634,11 @@ int sige_gather(const void *a_edit, int dtype, const sige_geom *gp, const int32_
     if ((rc = channel_rows_ok(dtype, g.cin, "c_in"))) return rc;
     if (!aligned(a_edit, 16) || !aligned(blocks, 16)) return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
     const int es = sige::elem_bytes(dtype);
-    if (overlap(blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
-        return fail(SIGE_EINVAL, "blocks overlap the input");
+    {
+        const Region wr[] = {{blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es}};
+        const Region rd[] = {{a_edit, (size_t)g.n * g.h * g.w * g.cin * es}, {idx, (size_t)g.cap * 4}, {count, 4}};
+        if (regions_overlap(wr, 1, rd, 3)) return fail(SIGE_EINVAL, "blocks overlap the input, idx or count");
+    }
     if ((rc = device_ready())) return rc;
     return finish(sige::launch_gather(a_edit, dtype, g, idx, count, blocks, (hipStream_t)stream), "sige_gather",
                   (hipStream_t)stream);
@@ -596,8 +656,12 @@ int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, 
         return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
     if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
     const int es = sige::elem_bytes(dtype);
-    if (overlap(out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es, blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es))
-        return fail(SIGE_EINVAL, "out_blocks overlaps blocks");
+    {
+        const Region wr[] = {{out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es}};
+        const Region rd[] = {{blocks, (size_t)g.cap * g.ib * g.ib * g.cin * es},
+                             {w_krsc, (size_t)g.cout * g.k * g.k * g.cin * es}, {bias, (size_t)g.cout * 4}, {count, 4}};
+        if (regions_overlap(wr, 1, rd, 4)) return fail(SIGE_EINVAL, "out_blocks overlaps blocks, weights, bias or count");
+    }
     sige::LayerCfg cfg;
     if ((rc = choose_layer(g, dtype, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
@@ -619,9 +683,12 @@ int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *coun
         return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
     const int es = sige::elem_bytes(dtype);
     const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
-    if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
-    if (overlap(out, obytes, out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es))
-        return fail(SIGE_EINVAL, "out overlaps out_blocks");
+    {
+        const Region wr[] = {{out, obytes}};
+        const Region rd[] = {{copy_cached ? cached : nullptr, obytes},
+                             {out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es}, {idx, (size_t)g.cap * 4}, {count, 4}};
+        if (regions_overlap(wr, 1, rd, 4)) return fail(SIGE_EINVAL, "out overlaps cached, out_blocks, idx or count");
+    }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
     const DevInfo dv = dev_info();
@@ -646,9 +713,14 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
     if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
     const int es = sige::elem_bytes(dtype);
     const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
-    if (overlap(out, obytes, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
-        return fail(SIGE_EINVAL, "out overlaps a_edit");
-    if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    {
+        const Region wr[] = {{out, obytes}};
+        const Region rd[] = {{a_edit, (size_t)g.n * g.h * g.w * g.cin * es}, {copy_cached ? cached : nullptr, obytes},
+                             {w_krsc, (size_t)g.cout * g.k * g.k * g.cin * es}, {bias, (size_t)g.cout * 4},
+                             {idx, (size_t)g.cap * 4}, {count, 4}};
+        if (regions_overlap(wr, 1, rd, 6))
+            return fail(SIGE_EINVAL, "out overlaps a_edit, cached, the weights, bias, idx or count");
+    }
     sige::LayerCfg cfg;
     if ((rc = choose_layer(g, dtype, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
@@ -675,37 +747,8 @@ int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *gp, int dtype) {
 int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                                  const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
                                  int copy_cached, void *workspace, int64_t workspace_bytes, void *stream) {
-    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
-    Geo g;
-    int rc = derive(gp, &g);
-    if (rc) return rc;
-    if (!a_edit || !w_krsc || !idx || !count || !out || !workspace || (copy_cached && !cached))
-        return fail(SIGE_EINVAL, "NULL pointer");
-    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
-    if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
-        (copy_cached && !aligned(cached, 16)))
-        return fail(SIGE_EALIGN, "tensors and workspace must be 16-byte aligned");
-    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
-    const int es = sige::elem_bytes(dtype);
-    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
-    const size_t ibytes = (size_t)g.n * g.h * g.w * g.cin * es;
-    if (overlap(out, obytes, a_edit, ibytes)) return fail(SIGE_EINVAL, "out overlaps a_edit");
-    if (copy_cached && overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
-    ConvCfg cfg;
-    if ((rc = choose_conv(g, dtype, 1, 1, &cfg, 1))) return rc;
-    const long need = sige::split_workspace_bytes(dtype, g, cfg);
-    if (need < 0) return fail(SIGE_EINVAL, "unknown tile shape");
-    if ((rc = device_ready())) return rc;
-    if (workspace_bytes < need)
-        return fail(SIGE_ERANGE, "workspace of %lld bytes, %ld needed", (long long)workspace_bytes, need);
-    if (overlap(workspace, (size_t)need, out, obytes) || overlap(workspace, (size_t)need, a_edit, ibytes) ||
-        overlap(workspace, (size_t)need, idx, (size_t)g.cap * 4) || overlap(workspace, (size_t)need, count, 4) ||
-        (copy_cached && overlap(workspace, (size_t)need, cached, obytes)))
-        return fail(SIGE_EINVAL, "the workspace overlaps another argument");
-    const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
-    return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
-                                    nullptr, nullptr, g, cfg, cc, (hipStream_t)stream, (float *)workspace),
-                  "sige_sparse_conv_layer_split", (hipStream_t)stream);
+    return split_common(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, workspace,
+                        workspace_bytes, stream, "sige_sparse_conv_layer_split");
 }
 
 int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
@@ -723,9 +766,14 @@ int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const
     if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
     const int es = sige::elem_bytes(dtype);
     const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
-    if (overlap(out, obytes, a_edit, (size_t)g.n * g.h * g.w * g.cin * es))
-        return fail(SIGE_EINVAL, "out overlaps a_edit");
-    if (overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    {
+        const Region wr[] = {{out, obytes}};
+        const Region rd[] = {{a_edit, (size_t)g.n * g.h * g.w * g.cin * es}, {cached, obytes},
+                             {w_krsc, (size_t)g.cout * g.k * g.k * g.cin * es}, {bias, (size_t)g.cout * 4},
+                             {idx, (size_t)g.cap * 4}, {count, 4}, {prev_idx, (size_t)g.cap * 4}, {prev_count, 4}};
+        if (regions_overlap(wr, 1, rd, 8))
+            return fail(SIGE_EINVAL, "out overlaps a_edit, cached, the weights, bias or a list");
+    }
     sige::LayerCfg cfg;
     if ((rc = choose_layer(g, dtype, &cfg))) return rc;
     if ((rc = device_ready())) return rc;
@@ -759,15 +807,21 @@ int sige_sparse_attention(const void *q, const void *k, const void *v, const int
         return fail(SIGE_EALIGN, "tensors and workspace must be 16-byte aligned");
     if (!(scale > 0.f) || scale > 1e6f) return fail(SIGE_EINVAL, "scale must be positive and finite");
     const size_t tbytes = (size_t)n * h * w * g.cout * 2;
-    if (overlap(out, tbytes, q, tbytes) || overlap(out, tbytes, k, tbytes) || overlap(out, tbytes, v, tbytes))
-        return fail(SIGE_EINVAL, "out overlaps q, k or v");
-    if (copy_cached && overlap(out, tbytes, cached, tbytes)) return fail(SIGE_EINVAL, "out overlaps cached");
-    if ((rc = device_ready())) return rc;
-    const int grid1 = attn_grid1();
+    const Region rd[] = {{q, tbytes}, {k, tbytes}, {v, tbytes}, {copy_cached ? cached : nullptr, tbytes},
+                         {idx, (size_t)g.cap * 4}, {count, 4}};
+    {
+        const Region wr[] = {{out, tbytes}};
+        if (regions_overlap(wr, 1, rd, 6)) return fail(SIGE_EINVAL, "out overlaps q, k, v, cached, idx or count");
+    }
+    const int grid1 = attn_grid1();  // from the device's CU count (gfx950's 256 when none is visible)
     const int64_t need = attn_ws_bytes(g, heads, grid1);
     if (workspace_bytes < need)
         return fail(SIGE_ERANGE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
-    if (overlap(out, tbytes, workspace, (size_t)need)) return fail(SIGE_EINVAL, "out overlaps the workspace");
+    {
+        const Region wr[] = {{out, tbytes}, {workspace, (size_t)need}};
+        if (regions_overlap(wr, 2, rd, 6)) return fail(SIGE_EINVAL, "the workspace overlaps another argument");
+    }
+    if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, 2, copy_cached != 0);
     return finish(sige::launch_attention(dtype, q, k, v, idx, count, g, heads, scale, copy_cached ? cached : nullptr,
                                          out, cc, workspace, grid1, dev_info().cus * 4, (hipStream_t)stream),
@@ -786,7 +840,12 @@ int sige_restore_blocks(const int32_t *prev_idx, const int32_t *prev_count, cons
     if ((rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
     if (!aligned(cached, 16) || !aligned(out, 16)) return fail(SIGE_EALIGN, "tensors must be 16-byte aligned");
     const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * sige::elem_bytes(dtype);
-    if (overlap(out, obytes, cached, obytes)) return fail(SIGE_EINVAL, "out overlaps cached");
+    {
+        const Region wr[] = {{out, obytes}};
+        const Region rd[] = {{cached, obytes}, {prev_idx, (size_t)g.cap * 4}, {prev_count, 4},
+                             {idx, (size_t)g.cap * 4}, {count, 4}};
+        if (regions_overlap(wr, 1, rd, 5)) return fail(SIGE_EINVAL, "out overlaps cached or a list");
+    }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, sige::elem_bytes(dtype), true);
     const DevInfo dv = dev_info();

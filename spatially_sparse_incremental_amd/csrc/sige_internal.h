@@ -44,7 +44,6 @@ struct ConvCfg {
 constexpr int kLayerWaves = 4;                  // waves per workgroup (they split the K steps)
 constexpr int kLayerThreads = 64 * kLayerWaves;
 constexpr int kLayerFrags = 18;                 // weight fragments per lane and chunk (SMAX * NT)
-constexpr int kLayerGroups = 8;                 // 64-slot staging groups per wave and block slot
 struct LayerCfg {
     int mt, nt;          // 16x16 subtiles per tile along M (rows) and N (output channels)
     int ck, nch;         // input channels per chunk (kpc K slices), chunks

@@ -151,6 +151,81 @@ def test_conv_step_validation(lib):
                                       1, s) == ERANGE
 
 
+def test_outputs_overlapping_lists_weights_or_workspace_are_rejected(lib):
+    """Every entry point checks what it writes against everything it reads: the
+    block list, the count, the weights and the bias too."""
+    s = _v(0)
+    g = _g()
+    far = _v(E + (1 << 35))
+    conv = lib.sige_sparse_conv_layer
+    assert conv(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g), far, 1, s) == ENODEV  # valid
+    assert conv(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g), _v(D), 1, s) == EINVAL  # out = idx
+    assert conv(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g), _v(E), 1, s) == EINVAL  # out = count
+    assert conv(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(g), _v(B + 256), 1, s) == EINVAL  # weights
+    assert conv(_v(A), _v(B), _v(far.value + 64), _v(C), _v(D), _v(E), 1, ctypes.byref(g), far, 1,
+                s) == EINVAL  # bias inside out
+    sc = lib.sige_scatter
+    assert sc(_v(A), _v(B), _v(C), ctypes.byref(g), 1, _v(D), far, 1, s) == ENODEV
+    assert sc(_v(A), _v(B), _v(C), ctypes.byref(g), 1, _v(D), _v(B), 1, s) == EINVAL  # out = idx
+    assert sc(_v(A), _v(B), _v(C), ctypes.byref(g), 1, _v(D), _v(C), 0, s) == EINVAL  # out = count
+    assert lib.sige_gather(_v(A), 1, ctypes.byref(g), _v(B), _v(C), _v(B), s) == EINVAL  # blocks = idx
+    assert lib.sige_conv_blocks(_v(A), _v(B), None, 1, ctypes.byref(g), _v(C), _v(B + 64), s) == EINVAL  # weights
+    att = lib.sige_sparse_attention
+    q, k, v, idx, cnt = A, B, D, A + (1 << 39), A + (1 << 40)
+
+    def call(out=far.value, ws=C):
+        return att(_v(q), _v(k), _v(v), _v(idx), _v(cnt), 2, 1, 64, 64, 5, 64, 4, ctypes.c_float(0.125), _v(E),
+                   _v(out), 1, _v(ws), 1 << 30, s)
+
+    assert call() == ENODEV
+    assert call(ws=k) == EINVAL          # workspace overlaps k
+    assert call(ws=idx) == EINVAL        # workspace overlaps idx
+    assert call(ws=E) == EINVAL          # workspace overlaps cached
+    assert call(out=idx) == EINVAL       # out overlaps idx
+    assert call(ws=far.value + 64) == EINVAL  # workspace overlaps out
+    rs = lib.sige_restore_blocks
+    assert rs(_v(A), _v(B), _v(C), _v(D), ctypes.byref(g), 1, _v(E), far, s) == ENODEV
+    assert rs(_v(A), _v(B), _v(C), _v(D), ctypes.byref(g), 1, _v(E), _v(A), s) == EINVAL  # out = prev_idx
+
+
+def test_reduce_limits_match_between_one_layer_and_many(lib):
+    """sige_reduce_bits_layers applies the single-layer reduce's limits per layer."""
+    s = _v(0)
+    many = _g(n=5, h=256, w=256)  # 5 * 1849 = 9245 blocks per launch: fine for both
+    over = _g(n=9, h=256, w=256)  # 9 * 1849 = 16641 > 16384
+    f1 = lib.sige_reduce_bits
+    assert f1(_v(A), 256, 256, ctypes.byref(many), 1, _v(B), _v(C), s) == ENODEV
+    assert f1(_v(A), 256, 256, ctypes.byref(over), 1, _v(B), _v(C), s) == ERANGE
+    fl = lib.sige_reduce_bits_layers
+    for geo, want in ((many, ENODEV), (over, ERANGE)):
+        GA, IA, VA = L.Geom * 1, ctypes.c_int * 1, ctypes.c_void_p * 1
+        rc = fl(_v(A), 256, 256, 1, GA(geo), IA(1), VA(B), VA(C), 1, None, None, s)
+        assert rc == want, (geo.n, rc)
+
+
+def test_binding_checks_list_capacity_and_shapes():
+    """The binding refuses a block list shorter than the capacity (the kernels may
+    read entries past *count) and tensors of the wrong shape or dtype."""
+    g = ssi.geom(1, 64, 64, 32, 32, 3, 1, 1, 8)  # 8 x 8 = 64 blocks
+    L._need_list(g, torch.zeros(64, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="idx"):
+        L._need_list(g, torch.zeros(10, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="idx"):
+        L._need_list(g, torch.zeros(64, dtype=torch.int64), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="count"):
+        L._need_list(g, torch.zeros(64, dtype=torch.int32), torch.zeros(0, dtype=torch.int32))
+    a = torch.zeros(1, 64, 64, 32, dtype=torch.bfloat16)
+    w = torch.zeros(32, 3, 3, 32, dtype=torch.bfloat16)
+    b = torch.zeros(32, dtype=torch.float32)
+    L._need_layer(g, a, w, b, a, a)
+    with pytest.raises(ValueError, match="w_krsc"):
+        L._need_layer(g, a, w.permute(0, 3, 1, 2), b, None, None)
+    with pytest.raises(ValueError, match="out"):
+        L._need_layer(g, a, w, b, None, a[:, :32])
+    with pytest.raises(ValueError, match="bias"):
+        L._need_layer(g, a, w, b.double(), None, None)
+
+
 def test_reduce_copy_validation(lib):
     s = _v(0)
     g = _g()
@@ -208,7 +283,7 @@ def test_attention_validation(lib):
     far = _v(E + (1 << 35))
 
     def call(dtype=2, n=1, h=64, w=64, heads=5, hd=64, b=4, q=A, out=far, ws=C, wsb=1 << 30, scale=0.125):
-        return f(_v(q), _v(B), _v(D), _v(A + (1 << 37)), _v(A + (1 << 38)), dtype, n, h, w, heads, hd, b,
+        return f(_v(q), _v(B), _v(D), _v(A + (1 << 39)), _v(A + (1 << 40)), dtype, n, h, w, heads, hd, b,
                  ctypes.c_float(scale), _v(E), out, 1, _v(ws), wsb, s)
 
     assert call(dtype=0) == EDTYPE
