@@ -241,6 +241,25 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
                                  const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                                  int copy_cached, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* sige_sparse_conv_layer_split without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The partial tiles go to a static
+ * device array of the library, sige_noalloc_scratch_bytes() = 64 MiB per GPU,
+ * held until the process ends; the call itself allocates nothing.  Same
+ * arguments (minus the workspace), checks and result as
+ * sige_sparse_conv_layer_split, whose kernels it runs.
+ *   SIGE_ERANGE when the layer's split needs more scratch than that
+ *   (sige_sparse_conv_layer_split_workspace(g, dtype) > 64 MiB); nothing is
+ *   enqueued then.
+ *   Every call on one GPU shares that GPU's array: calls whose executions
+ *   overlap on one GPU (two streams, two threads) race on it and give wrong
+ *   results; calls ordered on one stream are safe.  Nothing in it needs to
+ *   start at zero. */
+int64_t sige_noalloc_scratch_bytes(void);
+int sige_sparse_conv_layer_split_noalloc(const void *a_edit, const void *w_krsc, const float *bias,
+                                         const void *cached, const int32_t *idx, const int32_t *count, int dtype,
+                                         const sige_geom *g, void *out, int copy_cached, void *stream);
+
 /* Sequential edits (nubint.ai review, "ABSTRACT": results with sequential
  * edits; "Proposed method": the engine keeps its state between edits).  `out`
  * is a persistent buffer that holds the previous edit's result: `cached`

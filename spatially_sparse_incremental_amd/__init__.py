@@ -28,7 +28,9 @@ from ._lib import (  # noqa: F401
     sige_sparse_attention_workspace,
     sige_sparse_conv_layer,
     sige_sparse_conv_layer_restore,
+    sige_noalloc_scratch_bytes,
     sige_sparse_conv_layer_split,
+    sige_sparse_conv_layer_split_noalloc,
     sige_sparse_conv_layer_split_workspace,
     weight_to_krsc,
 )

@@ -21,6 +21,7 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce_mask", "sige_reduce_mask_copy",
            "sige_diff_mask_bits", "sige_reduce_bits", "sige_reduce_bits_copy", "sige_reduce_bits_layers",
            "sige_sparse_conv_layer_split", "sige_sparse_conv_layer_split_workspace",
+           "sige_sparse_conv_layer_split_noalloc", "sige_noalloc_scratch_bytes",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
            "sige_sparse_attention_workspace", "sige_sparse_attention", "sige_strerror",
@@ -72,6 +73,9 @@ def lib():
         L.sige_sparse_conv_layer_split_workspace.argtypes = [P, I]
         L.sige_sparse_conv_layer_split_workspace.restype = ctypes.c_int64
         L.sige_sparse_conv_layer_split.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
+        L.sige_sparse_conv_layer_split_noalloc.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
+        L.sige_noalloc_scratch_bytes.argtypes = []
+        L.sige_noalloc_scratch_bytes.restype = ctypes.c_int64
         L.sige_restore_blocks.argtypes = [V, V, V, V, P, I, V, V, V]
         L.sige_sparse_conv_layer_restore.argtypes = [V, V, V, V, V, V, V, V, I, P, V, V]
         L.sige_sparse_attention_workspace.argtypes = [I] * 6
@@ -83,7 +87,7 @@ def lib():
         L.sige_last_error.restype = ctypes.c_char_p
         for f in EXPORTS:
             if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks", "sige_sparse_attention_workspace",
-                         "sige_sparse_conv_layer_split_workspace"):
+                         "sige_sparse_conv_layer_split_workspace", "sige_noalloc_scratch_bytes"):
                 getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -411,6 +415,26 @@ def sige_sparse_conv_layer_split(a_edit, w_krsc, bias, cached, idx, count, g: Ge
                                             int(bool(copy_cached)), _p(workspace), workspace.numel(),
                                             _stream(stream))
     _check(rc, "sige_sparse_conv_layer_split")
+    return out
+
+
+def sige_noalloc_scratch_bytes() -> int:
+    """Bytes of the library's static scratch (per GPU) used by sige_sparse_conv_layer_split_noalloc."""
+    return int(lib().sige_noalloc_scratch_bytes())
+
+
+def sige_sparse_conv_layer_split_noalloc(a_edit, w_krsc, bias, cached, idx, count, g: Geom, out, copy_cached=True,
+                                         stream=None):
+    """sige_sparse_conv_layer_split on the library's static scratch: no workspace, and the
+    call allocates nothing (`out` is required)."""
+    _dev(a_edit, w_krsc, bias, cached, idx, count, out)
+    _need_list(g, idx, count)
+    _need_layer(g, a_edit, w_krsc, bias, cached if copy_cached else None, out)
+    rc = lib().sige_sparse_conv_layer_split_noalloc(_p(a_edit), _p(w_krsc), _p(bias),
+                                                    _p(cached if copy_cached else None), _p(idx), _p(count),
+                                                    _dt(a_edit), ctypes.byref(g), _p(out), int(bool(copy_cached)),
+                                                    _stream(stream))
+    _check(rc, "sige_sparse_conv_layer_split_noalloc")
     return out
 
 

@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sige.h"
 #include "sige_internal.h"
 
@@ -410,14 +412,44 @@ int reduce_common(const uint8_t *mask, int mask_h, int mask_w, const sige_geom *
                   what, (hipStream_t)stream);
 }
 
+// The static scratch of sige_sparse_conv_layer_split_noalloc: one array per
+// GPU in the library's code object, for callers that cannot allocate (under
+// graph capture, in serving loops).  Host code never passes `scratch` itself:
+// its device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device on the entry point's first call there and kept.
+constexpr size_t kScratchBytes = 64u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_address(void **out) {
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return fail(SIGE_ENODEV, "no current HIP device below 64");
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(SIGE_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        }
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return SIGE_OK;
+}
+
 int split_common(const void *a_edit, const void *w_krsc, const float *bias, const void *cached, const int32_t *idx,
                  const int32_t *count, int dtype, const sige_geom *gp, void *out, int copy_cached, void *workspace,
-                 int64_t workspace_bytes, void *stream, const char *what) {
+                 int64_t workspace_bytes, void *stream, const char *what, bool use_scratch = false) {
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
     Geo g;
     int rc = derive(gp, &g);
     if (rc) return rc;
-    if (!a_edit || !w_krsc || !idx || !count || !out || !workspace || (copy_cached && !cached))
+    if (!a_edit || !w_krsc || !idx || !count || !out || (!workspace && !use_scratch) || (copy_cached && !cached))
         return fail(SIGE_EINVAL, "NULL pointer");
     if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
     if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
@@ -439,7 +471,15 @@ int split_common(const void *a_edit, const void *w_krsc, const float *bias, cons
     if ((rc = choose_conv(g, dtype, 1, 1, &cfg, 1))) return rc;
     const long need = sige::split_workspace_bytes(dtype, g, cfg);
     if (need < 0) return fail(SIGE_EINVAL, "unknown tile shape");
+    if (use_scratch && (size_t)need > kScratchBytes)
+        return fail(SIGE_ERANGE, "this layer's split needs %ld bytes of scratch, above the static %zu bytes of "
+                    "sige_sparse_conv_layer_split_noalloc (use sige_sparse_conv_layer_split with a workspace)",
+                    need, kScratchBytes);
     if ((rc = device_ready())) return rc;
+    if (use_scratch) {
+        if ((rc = scratch_address(&workspace))) return rc;
+        workspace_bytes = (int64_t)kScratchBytes;
+    }
     if (workspace_bytes < need)
         return fail(SIGE_ERANGE, "workspace of %lld bytes, %ld needed", (long long)workspace_bytes, need);
     {
@@ -749,6 +789,15 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
                                  int copy_cached, void *workspace, int64_t workspace_bytes, void *stream) {
     return split_common(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, workspace,
                         workspace_bytes, stream, "sige_sparse_conv_layer_split");
+}
+
+int64_t sige_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
+
+int sige_sparse_conv_layer_split_noalloc(const void *a_edit, const void *w_krsc, const float *bias,
+                                         const void *cached, const int32_t *idx, const int32_t *count, int dtype,
+                                         const sige_geom *gp, void *out, int copy_cached, void *stream) {
+    return split_common(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, nullptr, 0, stream,
+                        "sige_sparse_conv_layer_split_noalloc", true);
 }
 
 int sige_sparse_conv_layer_restore(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,

@@ -256,6 +256,24 @@ def test_split_layer_validation(lib):
     assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), far, 1, _v(ws), 1 << 30, s) == ENODEV
 
 
+def test_split_noalloc_limit_and_validation(lib):
+    s = _v(0)
+    f = lib.sige_sparse_conv_layer_split_noalloc
+    far = _v(E + (1 << 35))
+    assert lib.sige_noalloc_scratch_bytes() == 64 << 20
+    # the 64x128x1024 -> 512 GauGAN-shaped layer needs 128 MiB of partial tiles: past the static scratch
+    big = _g(h=64, w=128, ci=1024, co=512, b=4)
+    assert lib.sige_sparse_conv_layer_split_workspace(ctypes.byref(big), 1) > lib.sige_noalloc_scratch_bytes()
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 1, ctypes.byref(big), far, 1, s) == ERANGE
+    assert b"scratch" in lib.sige_last_error()
+    g = _g(h=16, w=16, ci=1280, co=1280, b=2)
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 7, ctypes.byref(g), far, 1, s) == EDTYPE
+    assert f(_v(A), _v(B), None, None, _v(D), _v(E), 2, ctypes.byref(g), far, 1, s) == EINVAL
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), _v(A + 64), 1, s) == EINVAL
+    # within the limit, a valid call reaches the device check (no GPU here)
+    assert f(_v(A), _v(B), None, _v(C), _v(D), _v(E), 2, ctypes.byref(g), far, 1, s) == ENODEV
+
+
 def test_restore_validation(lib):
     s = _v(0)
     g = _g()
