@@ -10,8 +10,25 @@ import spatially_sparse_incremental_amd as ssi
 import synth
 
 DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-# max |gpu - oracle| <= TOL * max |oracle| over the recomputed pixels
-TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 2e-2}
+# max |gpu - oracle| <= TOL * max |oracle| over the recomputed pixels.
+# fp32 1e-4 and bf16 2e-2 are the bounds the method's statement gives.  fp16
+# has none there; it is derived from the arithmetic: products of fp16 values
+# are exact in fp32, so a recomputed value carries the one final rounding (at
+# most 2^-11 = 4.9e-4 of |out|) plus the fp32 accumulation over K <= 11520
+# terms (a few 2^-24 * sqrt(K) * sum|a w|), and the attention's probabilities
+# are rounded to fp16 (2^-11 each) before their product with V.  3e-3 is six
+# fp16 roundoff units: errors measured on every fp16 case stay below 1.5e-3.
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 3e-3}
+# largest observed max|gpu - oracle| / max|oracle| per dtype in this session
+# (reported at the end of the run by conftest.py)
+WORST = {}
+
+
+def note_error(dt, rel, what=""):
+    """Records one case's relative error, for the end-of-session report."""
+    cur = WORST.get(dt)
+    if cur is None or rel > cur[0]:
+        WORST[dt] = (rel, what)
 
 
 def rand(shape, dtype, seed, std=1.0):
@@ -59,6 +76,7 @@ def assert_close(got, ref64, dt, sel=None, what=""):
         return 0.0
     scale = ref64.abs().max().item()
     err = (g - ref64).abs().max().item()
+    note_error(dt, err / max(scale, 1e-30), what)
     assert err <= TOL[dt] * max(scale, 1e-30), f"{what}: max err {err:.3e} vs scale {scale:.3e} (tol {TOL[dt]})"
     return err / max(scale, 1e-30)
 
@@ -106,8 +124,9 @@ def run_layer_oracle(a_o, a_e, wt, bias, cache, k, s, p, b, dilate, tau=1e-6):
 def check_layer_sampled(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed, sample=6):
     """Full-size check of one layer: the block list bit for bit, every pixel outside
     the listed blocks equal to the cache bit for bit, and `sample` listed blocks
-    recomputed by the oracle (fp64) within tolerance.  a_e, cache, out: CPU NHWC;
-    idx: the GPU's list; mask_full: [n, hm, wm] diff mask.  Returns the relative error."""
+    (None: every listed block) recomputed by the oracle (fp64) within tolerance.
+    a_e, cache, out: CPU NHWC; idx: the GPU's list; mask_full: [n, hm, wm] diff
+    mask.  Returns the relative error."""
     n, h, w, _ = a_e.shape
     act = oracle.block_activity(mask_full, h, w, L.k, L.stride, L.pad, L.block, L.dilate)
     ref_idx = oracle.index_list(act)
@@ -119,7 +138,8 @@ def check_layer_sampled(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed
     if ref_idx.numel() == 0:
         return 0.0
     rng = np.random.default_rng(seed)
-    pick = rng.choice(ref_idx.numpy(), size=min(sample, ref_idx.numel()), replace=False)
+    pick = ref_idx.numpy() if sample is None else \
+        rng.choice(ref_idx.numpy(), size=min(sample, ref_idx.numel()), replace=False)
     sub = torch.zeros_like(act)
     sub.view(-1)[torch.from_numpy(pick).long()] = 1
     ref = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, sub, out, out_f64=True)
@@ -127,6 +147,7 @@ def check_layer_sampled(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed
     g64, r64 = out.double()[sel], ref[sel]
     scale = r64.abs().max().item()
     err = (g64 - r64).abs().max().item()
+    note_error(out.dtype, err / max(scale, 1e-30), name)
     assert err <= TOL[out.dtype] * scale, f"{name}: max err {err:.3e} vs scale {scale:.3e}"
     return err / scale
 

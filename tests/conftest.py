@@ -20,3 +20,14 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The largest relative error each dtype reached against the oracle in this run."""
+    par = sys.modules.get("_parity")  # imported by the GPU parity tests only
+    if par is None:
+        return
+    TOL, WORST = par.TOL, par.WORST
+    for dt, (rel, what) in sorted(WORST.items(), key=lambda kv: str(kv[0])):
+        terminalreporter.write_line(f"parity margin {dt}: worst max|err|/max|ref| {rel:.3e} ({what}) "
+                                    f"vs tolerance {TOL[dt]:.0e}")

@@ -6,7 +6,7 @@ import torch
 import oracle
 import spatially_sparse_incremental_amd as ssi
 import synth
-from _parity import TOL, bits, rand
+from _parity import TOL, bits, note_error, rand
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,7 @@ def _check(got, ref64, cache, act, b, dt, what):
         err = (g64 - r64).abs().max().item()
         scale = r64.abs().max().item()
         print(f"[case] {what}: max relative error {err / scale:.2e}", flush=True)
+        note_error(dt, err / scale, what)
         assert err <= TOL[dt] * scale, f"{what}: max err {err:.3e} vs scale {scale:.3e}"
         return err / scale
     return 0.0

@@ -3,8 +3,10 @@
 For every layer of every workload: the change mask and the block list are
 compared with the oracle in full (bit-exact), every output pixel outside the
 listed blocks must equal the cache bit for bit, and the recomputed values are
-checked against the oracle's fp64 result on a seeded sample of listed blocks
-(the oracle computes just those blocks; the rest of its output is the GPU's).
+checked against the oracle's fp64 result on every listed block for the chain
+and the GauGAN layers up to the 1.2% edit, on a seeded sample of listed blocks
+for larger edits (the oracle computes just those blocks; the rest of its output
+is the GPU's).
 The chain is checked layer by layer, each layer's oracle taking the GPU's
 output of the layer before as its edited input.
 """
@@ -90,7 +92,8 @@ def test_unet_chain_12conv_layerwise():
         ho, wo, _, _, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
         cache = synth.make_activation(1, ho, wo, L.c_out, L.dtype, seed * 100 + li + 50)
         out, idx = run_layer_full(x, wt, bias, cache.cuda(), L, mask)
-        check_layer_sampled(f"chain {L.name}", x.cpu(), wt, bias, cache, out.cpu(), idx, L, mask.cpu(), seed + li)
+        check_layer_sampled(f"chain {L.name}", x.cpu(), wt, bias, cache, out.cpu(), idx, L, mask.cpu(), seed + li,
+                            sample=None)  # every listed block of the 1.2% edit
         x = out  # layer l+1 takes layer l's edited output
 
 
@@ -107,7 +110,8 @@ def test_gaugan_4conv_layers(area):
         cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
         mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
         out, idx = run_layer_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
-        check_layer_sampled(f"gaugan {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li)
+        check_layer_sampled(f"gaugan {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L, mask.cpu(), li,
+                            sample=None if area <= 0.012 else 10)  # every listed block up to the 1.2% edit
 
 
 @pytest.mark.parametrize("area", [0.012, 0.10])

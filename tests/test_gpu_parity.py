@@ -355,6 +355,58 @@ def test_outputs_have_no_stray_writes():
     assert (blk_buf[cnt * ib * ib * c:nb] == 5.0).all()  # unused block slots untouched
 
 
+def test_more_outputs_have_no_stray_writes():
+    # guard canaries after the outputs of the block conv, the scatter, the split
+    # layer (and its workspace), the restore and the attention
+    n, h, w, c, b = 1, 30, 30, 64, 6
+    dt = torch.bfloat16
+    G = 4096
+    mask = random_mask(n, h, w, 0.03, 141)
+    a_o, a_e, wt, bias = layer_inputs(n, h, w, c, c, 3, dt, 142, mask)
+    g = _geom(n, h, w, c, c, 3, 1, 1, b)
+    d = ssi.sige_geom_derive(g)
+    cap = d.cap
+    cache = gpu(rand((n, h, w, c), dt, 143))
+    ae, wk, bs = gpu(a_e), gpu(ssi.weight_to_krsc(wt)), gpu(bias)
+    idx, count = ssi.sige_reduce_mask(ssi.sige_diff_mask(gpu(a_o), ae), g, 1)
+    blocks = ssi.sige_gather(ae, g, idx, count)
+
+    def guarded(numel, fill, dtype=dt):
+        buf = torch.full((numel + G,), fill, dtype=dtype, device="cuda")
+        return buf, buf[:numel]
+
+    nob = cap * b * b * c
+    ob_buf, ob = guarded(nob, 5.0)
+    ssi.sige_conv_blocks(blocks, wk, bs, g, count, out_blocks=ob.view(cap, b, b, c))
+    nout = n * h * w * c
+    sc_buf, sc = guarded(nout, 3.0)
+    ssi.sige_scatter(ob.view(cap, b, b, c), idx, count, g, cache, out=sc.view(n, h, w, c))
+    sp_buf, sp = guarded(nout, 3.0)
+    nws = ssi.sige_sparse_conv_layer_split_workspace(g, dt)
+    ws_buf, ws = guarded(nws, 9, torch.uint8)
+    ssi.sige_sparse_conv_layer_split(ae, wk, bs, cache, idx, count, g, out=sp.view(n, h, w, c), workspace=ws)
+    rs_buf, rs = guarded(nout, 3.0)
+    rs.copy_(cache.view(-1))
+    ssi.sige_restore_blocks(idx, count, None, None, g, cache, rs.view(n, h, w, c))
+    heads = 1
+    q, k, v = (gpu(rand((n, h, w, 64), dt, 150 + i)) for i in range(3))
+    ga = _geom(n, h, w, 64, 64, 1, 1, 0, 5)
+    ia, ca = ssi.sige_reduce_mask(ssi.sige_diff_mask(gpu(a_o[..., :64].contiguous()), gpu(a_e[..., :64].contiguous())),
+                                  ga, 1)
+    at_buf, at = guarded(n * h * w * 64, 3.0)
+    nwa = ssi.sige_sparse_attention_workspace(n, h, w, heads, 64, 5)
+    wa_buf, wa = guarded(nwa, 9, torch.uint8)
+    ssi.sige_sparse_attention(q, k, v, ia, ca, heads, 5, cached=gpu(rand((n, h, w, 64), dt, 154)),
+                              out=at.view(n, h, w, 64), workspace=wa)
+    torch.cuda.synchronize()
+    cnt = int(count.item())
+    assert cnt > 0 and int(ca.item()) > 0
+    assert (ob_buf[nob:] == 5.0).all() and (ob_buf[cnt * b * b * c:nob] == 5.0).all()  # unused slots untouched
+    assert (sc_buf[nout:] == 3.0).all() and (sp_buf[nout:] == 3.0).all() and (rs_buf[nout:] == 3.0).all()
+    assert (ws_buf[nws:] == 9).all() and (wa_buf[nwa:] == 9).all()
+    assert (at_buf[n * h * w * 64:] == 3.0).all()
+
+
 def test_batch_of_two_images():
     n, h, w, c, b = 2, 24, 20, 32, 4
     dt = torch.float16

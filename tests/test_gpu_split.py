@@ -177,10 +177,12 @@ def test_split_graph_replays_match_eager():
         assert torch.equal(bits(got), bits(out)), rep
 
 
-@pytest.mark.parametrize("area", [0.005, 0.012, 0.05])
+@pytest.mark.parametrize("area", [0.005, 0.012, 0.05, 0.15, 0.30])
 def test_split_gaugan_layers(area):
     # the four GauGAN-shaped bf16 convs (18.9 MB of weights at 32x64x1024): list and
-    # untouched pixels bit for bit, sampled blocks against the oracle
+    # untouched pixels bit for bit, sampled blocks against the oracle, and every
+    # listed pixel against the single-range layer (an independently written kernel
+    # that the oracle checks on the same layers) within the bf16 tolerance
     wl = synth.workload("gaugan_4conv_bf16")
     seed = 6
     shape = synth.edit_shape(wl, seed, area)
@@ -194,7 +196,15 @@ def test_split_gaugan_layers(area):
         out, idx = _split_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask)
         print(f"\n[case] gaugan split {L.name} area {area}: {idx.numel()} blocks", flush=True)
         check_layer_sampled(f"gaugan split {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L,
-                            mask.cpu(), li)
+                            mask.cpu(), li, sample=None if area <= 0.012 else 10)
+        g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+        i2, c2 = ssi.sige_reduce_mask(mask, g, L.dilate)
+        single = ssi.sige_sparse_conv_layer(a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache.cuda(),
+                                            i2, c2, g).cpu()
+        act = torch.zeros(1, *oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)[2:4], dtype=torch.uint8)
+        act.view(-1)[idx.long()] = 1
+        sel = active_pixels(act, L.block, L.h, L.w).expand_as(out)
+        assert_close(out.cpu(), single.double(), out.dtype, sel, f"gaugan split vs single {L.name} area {area}")
 
 
 def test_split_unet_chain_12conv_layerwise():
