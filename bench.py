@@ -731,8 +731,9 @@ def _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
 
 def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     """The latent-diffusion 16x16x1280 fp16 3x3 layer (b = 2, dilation 1) with the
-    blob edit: the single-range fused layer, the layer split over input channels
-    and the dense conv (torch/MIOpen), each with the cache copy."""
+    blob edit: the library's choice (sige_sparse_conv_layer_auto), the
+    single-range fused layer, the layer split over input channels and the dense
+    conv (torch/MIOpen), each with the cache copy."""
     dev = torch.device("cuda:0")
     wl = synth.workload("ldm_64x64x320_f16")
     L = [x for x in wl.layers if x.name == "l16_3x3"][0]
@@ -749,13 +750,20 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     t_plain = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out))
     t_split = graph_time(lambda: ssi.sige_sparse_conv_layer_split(a_e, wk, bias, cache, idx, cnt, g, out=out,
                                                                   workspace=ws))
-    res = {"blocks": int(cnt.item()), "single_range_us": round(t_plain, 3), "split_us": round(t_split, 3)}
+    plan = ssi.sige_sparse_conv_layer_plan(g, a_e.dtype)
+    ws_auto = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    t_auto = graph_time(lambda: ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, cache, idx, cnt, g, out=out,
+                                                                workspace=ws_auto))
+    res = {"blocks": int(cnt.item()), "auto_us": round(t_auto, 3),
+           "auto_path": "split" if int(cnt.item()) <= plan.split_max else "single", "split_max": plan.split_max,
+           "single_range_us": round(t_plain, 3), "split_us": round(t_split, 3)}
     try:
         x_cl = a_e.permute(0, 3, 1, 2)
         w_cl = w_cpu.to(dev).contiguous(memory_format=torch.channels_last)
         with torch.no_grad():
             t_dense = timed_eager(lambda: F.conv2d(x_cl, w_cl, bias.to(a_e.dtype), padding=L.pad), 50)
         res["dense_miopen_us"] = round(t_dense, 3)
+        res["speedup_auto_vs_dense"] = round(t_dense / t_auto, 2)
         res["speedup_split_vs_dense"] = round(t_dense / t_split, 2)
     except Exception as exc:  # noqa: BLE001 - report, do not hide
         print(f"[bench] dense 16x16x1280 conv failed: {exc}", file=sys.stderr)
@@ -808,51 +816,65 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
     torch.cuda.synchronize()
     blocks = [int(ly["cnt"].item()) for ly in layers]
     t_single = graph_time(sparse_chain, 2, 25)
-    # per layer, the faster of the single-range layer and its split over input
-    # channels (each timed with its reduce, on the inputs and lists of the run above)
     xs = [a_e] + [ly["out"] for ly in layers[:-1]]
     for ly, x in zip(layers, xs):
-        ly["ws"] = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(ly["g"], a_e.dtype), dtype=torch.uint8,
-                               device=dev)
-        ly["split"] = False
+        plan = ssi.sige_sparse_conv_layer_plan(ly["g"], a_e.dtype)
+        ly["ws"] = torch.empty(max(ssi.sige_sparse_conv_layer_split_workspace(ly["g"], a_e.dtype),
+                                   plan.workspace_bytes), dtype=torch.uint8, device=dev)
+        ly["auto_path"] = "split" if int(ly["cnt"].item()) <= plan.split_max else "single"
+        # the bound: per layer, the faster of the two kernels timed on this very edit
+        ly["mode"] = "single"
         t1 = graph_time(lambda: _chain_layer(ssi, ly, x, first), 5, 20)
-        ly["split"] = True
+        ly["mode"] = "split"
         t2 = graph_time(lambda: _chain_layer(ssi, ly, x, first), 5, 20)
-        ly["split"] = t2 < t1
+        ly["best"] = "split" if t2 < t1 else "single"
 
-    def chosen_chain():
-        ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
-        x = a_e
+    def chain_with(mode):
         for ly in layers:
-            _chain_layer(ssi, ly, x, first)
-            x = ly["out"]
+            ly["mode"] = ly["best"] if mode == "best" else mode
 
-    t_per_layer = graph_time(chosen_chain, 2, 25)
+        def run():
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+            x = a_e
+            for ly in layers:
+                _chain_layer(ssi, ly, x, first)
+                x = ly["out"]
+        return run
+
+    t_per_layer = graph_time(chain_with("auto"), 2, 25)
     # every layer's list depends on the one mask only: all twelve lists and cache
     # copies in one launch, then the twelve layers
     geoms, dils = [ly["g"] for ly in layers], [ly["L"].dilate for ly in layers]
     idxs, cnts = [ly["idx"] for ly in layers], [ly["cnt"] for ly in layers]
     caches, outs = [ly["cache"] for ly in layers], [ly["out"] for ly in layers]
 
-    def batched_chain():
-        ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
-        ssi.sige_reduce_bits_layers(mbits, first.h, first.w, geoms, dils, idxs, cnts, caches, outs)
-        x = a_e
-        for ly in layers:
-            _chain_conv(ssi, ly, x)
-            x = ly["out"]
+    def batched_with(mode):
+        def run():
+            ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
+            ssi.sige_reduce_bits_layers(mbits, first.h, first.w, geoms, dils, idxs, cnts, caches, outs)
+            x = a_e
+            for ly in layers:
+                ly["mode"] = ly["best"] if mode == "best" else mode
+                _chain_conv(ssi, ly, x)
+                x = ly["out"]
+        return run
 
-    t_sparse = graph_time(batched_chain, 2, 25)
+    t_sparse = graph_time(batched_with("auto"), 2, 25)
+    t_best = graph_time(batched_with("best"), 2, 25)
     with torch.no_grad():
         t_dense = graph_time(dense_chain, 1, 10)
     return {"sparse_us": round(t_sparse, 3), "dense_miopen_us": round(t_dense, 3),
             "speedup": round(t_dense / t_sparse, 2), "blocks_per_layer": blocks,
-            "path_per_layer": ["split" if ly["split"] else "single" for ly in layers],
+            "path_per_layer": [ly["auto_path"] for ly in layers],
+            "best_of_two_bound_us": round(t_best, 3),
+            "best_of_two_path_per_layer": [ly["best"] for ly in layers],
             "sparse_per_layer_reduce_us": round(t_per_layer, 3),
             "sparse_single_range_only_us": round(t_single, 3),
-            "note": "one diff + one launch building all 12 lists with the 12 cache copies + 12 layers (the faster "
-                    "of the fused layer and its split, chosen per layer); per_layer_reduce: a reduce with its "
-                    "copy before each layer; dense: 12 x F.conv2d; HIP graphs"}
+            "note": "one diff + one launch building all 12 lists with the 12 cache copies + 12 layers through "
+                    "sige_sparse_conv_layer_auto (the kernel the library picks from the list length; "
+                    "path_per_layer is its choice); best_of_two_bound: the faster of the two kernels per layer, "
+                    "timed on this edit (not available to a caller); per_layer_reduce: a reduce with its copy "
+                    "before each layer; dense: 12 x F.conv2d; HIP graphs"}
 
 
 def _chain_layer(ssi, ly, x, first):
@@ -864,8 +886,12 @@ def _chain_layer(ssi, ly, x, first):
 
 
 def _chain_conv(ssi, ly, x):
-    """The layer of the chain on its list, into its output (which holds the cache copy)."""
-    if ly["split"]:
+    """The layer of the chain on its list, into its output (which holds the cache
+    copy), by ly["mode"]: the library's choice, or one kernel."""
+    if ly["mode"] == "auto":
+        ssi.sige_sparse_conv_layer_auto(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
+                                        out=ly["out"], copy_cached=False, workspace=ly["ws"])
+    elif ly["mode"] == "split":
         ssi.sige_sparse_conv_layer_split(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
                                          out=ly["out"], copy_cached=False, workspace=ly["ws"])
     else:
@@ -876,8 +902,10 @@ def _chain_conv(ssi, ly, x):
 def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     """The four GauGAN-shaped bf16 convs (32x64x1024 to 256x512x256) under the seeded star polygon at
     0.5 / 1.2 / 5 / 15 / 30% of the frame: the reduce (mask one bit per pixel,
-    the cache copy on its idle workgroups) + the faster of the fused layer and
-    its split per layer, against the dense conv through torch/MIOpen."""
+    the cache copy on its idle workgroups) + sige_sparse_conv_layer_auto (the
+    kernel the library picks; `path`), against the dense conv through
+    torch/MIOpen; best_of_two_bound: the faster of the two kernels timed on the
+    very edit, which a caller cannot do."""
     dev = torch.device("cuda:0")
     wl = synth.workload("gaugan_4conv_bf16")
     res, dense = {}, {}
@@ -903,6 +931,13 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
             out = torch.empty_like(cache)
             ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8,
                              device=dev)
+            plan = ssi.sige_sparse_conv_layer_plan(g, a_e.dtype)
+            ws_auto = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+
+            def auto():
+                ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)
+                ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False,
+                                                workspace=ws_auto)
 
             def one():
                 ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)
@@ -913,10 +948,13 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
                 ssi.sige_sparse_conv_layer_split(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False,
                                                  workspace=ws)
 
-            t1, t2 = graph_time(one, 5, 20), graph_time(split, 5, 20)
-            row[L.name] = {"blocks": int(cnt.item()), "sparse_us": round(min(t1, t2), 3),
-                           "path": "split" if t2 < t1 else "single", "dense_miopen_us": dense[L.name],
-                           "speedup": round(dense[L.name] / min(t1, t2), 2)}
+            t0, t1, t2 = graph_time(auto, 5, 20), graph_time(one, 5, 20), graph_time(split, 5, 20)
+            n = int(cnt.item())
+            row[L.name] = {"blocks": n, "sparse_us": round(t0, 3),
+                           "path": "split" if n <= plan.split_max else "single", "dense_miopen_us": dense[L.name],
+                           "speedup": round(dense[L.name] / t0, 2),
+                           "best_of_two_bound_us": round(min(t1, t2), 3),
+                           "best_of_two_path": "split" if t2 < t1 else "single"}
         res[f"area_{area:g}"] = row
     return res
 

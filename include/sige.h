@@ -241,6 +241,45 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
                                  const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                                  int copy_cached, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* The fused layer with the kernel chosen by the library: the single-range
+ * kernel of sige_sparse_conv_layer or the split of
+ * sige_sparse_conv_layer_split, whichever a cost model fixed in the library
+ * prices faster for the list length *count.  The mer.dev notes (5 "Conclusion
+ * & Discussion") name small blocks at low resolution as the method's weak
+ * spot: there the K range is long and the blocks few, and the split is the
+ * faster kernel.  The list length is read on the device, so the host derives
+ * one threshold per layer, sige_layer_plan.split_max: lists of at most that
+ * many blocks go to the split, longer ones to the single-range kernel.  When
+ * both can occur, both kernels are enqueued and the one not chosen exits as
+ * soon as it has read *count (about two microseconds); no host timing, no
+ * synchronisation, nothing allocated.
+ *   Same arguments, checks and result as sige_sparse_conv_layer (up to the
+ *   fp32 summation order of the kernel that runs), plus the split's
+ *   workspace: at least sige_layer_plan.workspace_bytes of caller-owned
+ *   device memory (16-byte aligned, no initialisation, contents afterwards
+ *   meaningless, not shared by calls that overlap in time); NULL and 0 when
+ *   workspace_bytes is 0 (the split is never chosen).  SIGE_ERANGE when the
+ *   workspace is smaller.
+ * sige_sparse_conv_layer_plan reports the choice for a geometry: split_max
+ * (-1: never the split; >= cap: always), the workspace size, and the cost
+ * model's inputs (the single-range kernel's K chunks per tile, K steps per
+ * chunk, 1 KiB staging groups per tile and chunk, resident workgroup slots,
+ * tiles of 32 output channels; the split's chunks, resident workgroup slots
+ * and KiB of staged windows per tile (0 when the split cannot run); the
+ * layer's weight megabytes and GFLOP per listed block). */
+typedef struct {
+    int32_t split_max;        /* the split takes lists of at most this many blocks (-1: none) */
+    int32_t cap;              /* blocks at full capacity (sige_max_blocks) */
+    int64_t workspace_bytes;  /* workspace sige_sparse_conv_layer_auto needs (0: none) */
+    int32_t chunks, steps, stage_groups, slots, n_tiles;
+    int32_t split_chunks, split_slots;
+    double split_stage_kb, weight_mb, gflop_per_block;
+} sige_layer_plan;
+int sige_sparse_conv_layer_plan(const sige_geom *g, int dtype, sige_layer_plan *out);
+int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
+                                int copy_cached, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* sige_sparse_conv_layer_split without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  The partial tiles go to a static

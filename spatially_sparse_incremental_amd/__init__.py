@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     Derived,
     Geom,
+    LayerPlan,
     SigeError,
     geom,
     lib,
@@ -27,6 +28,8 @@ from ._lib import (  # noqa: F401
     sige_sparse_attention,
     sige_sparse_attention_workspace,
     sige_sparse_conv_layer,
+    sige_sparse_conv_layer_auto,
+    sige_sparse_conv_layer_plan,
     sige_sparse_conv_layer_restore,
     sige_noalloc_scratch_bytes,
     sige_sparse_conv_layer_split,

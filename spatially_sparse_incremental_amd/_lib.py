@@ -22,6 +22,7 @@ EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce
            "sige_diff_mask_bits", "sige_reduce_bits", "sige_reduce_bits_copy", "sige_reduce_bits_layers",
            "sige_sparse_conv_layer_split", "sige_sparse_conv_layer_split_workspace",
            "sige_sparse_conv_layer_split_noalloc", "sige_noalloc_scratch_bytes",
+           "sige_sparse_conv_layer_plan", "sige_sparse_conv_layer_auto",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
            "sige_sparse_attention_workspace", "sige_sparse_attention", "sige_strerror",
@@ -37,6 +38,18 @@ class SigeError(RuntimeError):
 class Geom(ctypes.Structure):
     """sige_geom: input [n, h, w, c_in], k x k kernel, stride, pad, output block edge."""
     _fields_ = [(f, ctypes.c_int32) for f in ("n", "h", "w", "c_in", "c_out", "k", "stride", "pad", "block")]
+
+
+class LayerPlan(ctypes.Structure):
+    """sige_layer_plan: which kernel sige_sparse_conv_layer_auto runs for which list lengths."""
+    _fields_ = [("split_max", ctypes.c_int32), ("cap", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
+                ("chunks", ctypes.c_int32), ("steps", ctypes.c_int32), ("stage_groups", ctypes.c_int32),
+                ("slots", ctypes.c_int32), ("n_tiles", ctypes.c_int32), ("split_chunks", ctypes.c_int32),
+                ("split_slots", ctypes.c_int32), ("split_stage_kb", ctypes.c_double), ("weight_mb", ctypes.c_double),
+                ("gflop_per_block", ctypes.c_double)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 class Derived(ctypes.Structure):
@@ -74,6 +87,8 @@ def lib():
         L.sige_sparse_conv_layer_split_workspace.restype = ctypes.c_int64
         L.sige_sparse_conv_layer_split.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
         L.sige_sparse_conv_layer_split_noalloc.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
+        L.sige_sparse_conv_layer_plan.argtypes = [P, I, ctypes.POINTER(LayerPlan)]
+        L.sige_sparse_conv_layer_auto.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
         L.sige_noalloc_scratch_bytes.argtypes = []
         L.sige_noalloc_scratch_bytes.restype = ctypes.c_int64
         L.sige_restore_blocks.argtypes = [V, V, V, V, P, I, V, V, V]
@@ -415,6 +430,40 @@ def sige_sparse_conv_layer_split(a_edit, w_krsc, bias, cached, idx, count, g: Ge
                                             int(bool(copy_cached)), _p(workspace), workspace.numel(),
                                             _stream(stream))
     _check(rc, "sige_sparse_conv_layer_split")
+    return out
+
+
+def sige_sparse_conv_layer_plan(g: Geom, dtype) -> LayerPlan:
+    """The kernel choice of sige_sparse_conv_layer_auto for g and a torch dtype:
+    the split takes lists of at most .split_max blocks (-1: never), the
+    single-range kernel the longer ones; .workspace_bytes for the split."""
+    plan = LayerPlan()
+    _check(lib().sige_sparse_conv_layer_plan(ctypes.byref(g), DTYPE_CODE[dtype], ctypes.byref(plan)),
+           "sige_sparse_conv_layer_plan")
+    return plan
+
+
+def sige_sparse_conv_layer_auto(a_edit, w_krsc, bias, cached, idx, count, g: Geom, out=None, copy_cached=True,
+                                workspace=None, stream=None):
+    """The fused layer on the kernel the library picks for *count (see
+    sige_sparse_conv_layer_plan); the workspace is allocated here when the
+    plan needs one and none is given."""
+    _dev(a_edit, w_krsc, bias, cached, idx, count, out, workspace)
+    _need_list(g, idx, count)
+    d = _need_layer(g, a_edit, w_krsc, bias, cached if copy_cached else None, out)
+    if out is None:
+        if not copy_cached:
+            raise ValueError("copy_cached=False needs a persistent `out`")
+        out = torch.empty((g.n, d.ho, d.wo, g.c_out), dtype=a_edit.dtype, device=a_edit.device)
+    if workspace is None:
+        need = sige_sparse_conv_layer_plan(g, a_edit.dtype).workspace_bytes
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=a_edit.device)
+    rc = lib().sige_sparse_conv_layer_auto(_p(a_edit), _p(w_krsc), _p(bias), _p(cached if copy_cached else None),
+                                           _p(idx), _p(count), _dt(a_edit), ctypes.byref(g), _p(out),
+                                           int(bool(copy_cached)), _p(workspace),
+                                           workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(rc, "sige_sparse_conv_layer_auto")
     return out
 
 

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv_stream(ConvArgs a) {
     const bool dbuf = stream_dbuf(c, BM, BN, kConvWaves);  // two buffers of windows
     const int buf1 = dbuf ? (wbytes > pbytes ? wbytes : pbytes) : 0;  // byte offset of buffer 1
     const int cnt = clamp_count(a.count, g.cap);
+    if (cnt > c.gate_max) return;  // paired with the single-range layer, which takes longer lists
     const int mrows = cnt * b2;
     const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, gridDim.x, dbuf);
 
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
     const int b2 = g.b * g.b, ntn = (g.cout + BN - 1) / BN;
     const int nch = (g.cin + c.ck - 1) / c.ck;
     const int cnt = clamp_count(a.count, g.cap);
+    if (cnt > c.gate_max) return;  // the single-range layer does this list (and the copy)
     const StreamPlan pl = stream_plan(cnt, b2, BM, ntn, nch, slots, stream_dbuf(c, BM, BN, kConvWaves));
     const int mrows = cnt * b2;
     const long total = (long)pl.mtn * ntn * BM * VPR;

@@ -79,12 +79,13 @@ __device__ __forceinline__ int layer_tiles(const LayerCfg &c, int cnt, int b2) {
 // This wave's weight fragments of the K steps st0, st0 + 1, ... of the chunk
 // at input channel c0 (lane l: column l % 16 of each N subtile and the EPV
 // input channels at (l / 16) * EPV of the step's slice).  wcol[nt] is the
-// lane's column offset into the weights; the step's (tap, slice) offset is
-// uniform, so each load is a scalar base plus a 32-bit lane offset.  Channels
-// past c_in (a partial last chunk) read the last valid ones of the column:
-// their products meet zeros in the staged windows.  `dummy` points every
-// lane at the first fragment instead (one cache line), for a workgroup that
-// does not know yet whether it has a tile.
+// lane's column offset into the weights; the step's tap offset is uniform, so
+// each load is a scalar base plus a 32-bit lane offset (column, then channel
+// within the tap, both non-negative).  Channels past c_in (a partial last
+// chunk, whose later K slices may start past c_in) read the last valid vector
+// of the tap: their products meet zeros in the staged windows.  `dummy` points
+// every lane at the first fragment instead (one cache line), for a workgroup
+// that does not know yet whether it has a tile.
 template <int DT, int NT, int SMAX>
 __device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, const LayerCfg &c,
                                               u32x4 (&bfr)[SMAX][NT], const int (&wcol)[NT], int c0, int st0,
@@ -95,8 +96,8 @@ __device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, co
     for (int j = 0; j < SMAX; ++j) {
         const int stp = min(st0 + j, c.steps - 1);
         const int tap = stp >> c.lkpc, cb = c0 + (stp & (c.kpc - 1)) * KS;
-        const uint8_t *base = w + ((uint32_t)((tap * g.cin + cb) * ES) & keep);
-        const int lch = min(kl, g.cin - EPV - cb) * ES;
+        const uint8_t *base = w + ((uint32_t)(tap * g.cin * ES) & keep);
+        const int lch = min(cb + kl, g.cin - EPV) * ES;  // in [0, c_in * ES)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) bfr[j][nt] = ld16(base + ((uint32_t)(wcol[nt] + lch) & keep));
     }
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                  "s"(c.lkpc), "s"(c.steps), "s"(c.spw), "s"(c.vpc), "s"(c.ps), "s"(c.rs), "s"(c.gps), "s"(c.sb), "s"(c.ntn),
                  "s"(c.xcd));
     asm volatile("" ::"s"(c.tiles_cap), "s"(c.spec), "s"(c.m_ps), "s"(c.m_rs), "s"(c.m_b2),
-                 "s"(c.m_b));
+                 "s"(c.m_b), "s"(c.gate_min));
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
@@ -190,7 +191,9 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             layer_weights<DT, NT, SMAX>(a.w, g, c, bfr, wcol, 0, st0, kl, !early_w);
             __builtin_amdgcn_sched_barrier(0);
             cnt = min(max(cnt_raw, 0), g.cap);
-            ntiles = layer_tiles<BM>(c, cnt, b2);
+            // A launch paired with the split over input channels: a list below
+            // gate_min blocks is the split's (the whole layer and the copy).
+            ntiles = cnt < c.gate_min ? 0 : layer_tiles<BM>(c, cnt, b2);
             mrows = cnt * b2;
             if (t >= ntiles) return false;
         }
@@ -378,6 +381,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             cnt = min(max(cnt_raw, 0), g.cap);
             ntiles = layer_tiles<BM>(c, cnt, b2);
         }
+        if (cnt < c.gate_min) return;  // the split does this list and the copy
         long long lo, hi;
         if (a.prev_idx) {
             const int np = clamp_count(a.prev_count, g.cap);
@@ -428,7 +432,9 @@ static hipError_t launch_layer_k(const LayerArgs &args, hipStream_t st) {
     if (!TAIL && c.tiles_cap < grid) grid = c.tiles_cap;  // nothing past the tiles at capacity
     if (grid > 8) grid = grid / 8 * 8;                     // keep tile t on XCD t % 8 across passes
     LayerArgs a = args;
-    a.c.spec = (int)(grid < c.cus ? grid : c.cus);         // the first workgroup of each CU
+    // the first workgroup of each CU; none when the launch is gated (most of
+    // its lists may be the split's, and the weights would be fetched for nothing)
+    a.c.spec = c.gate_min > 0 ? 0 : (int)(grid < c.cus ? grid : c.cus);
     hipLaunchKernelGGL(k, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kLayerThreads), c.lds_bytes, st, a);
     return hipGetLastError();
 }

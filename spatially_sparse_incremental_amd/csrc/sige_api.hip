@@ -1,6 +1,7 @@
 // sige_api.hip -- the C ABI of libsige.so: argument checks, status codes,
 // launch configuration.  Every check runs on the host before anything is
 // enqueued; the kernels live in kernels_mask.hip and kernels_conv.hip.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -236,6 +237,7 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
     c.m_vpc1 = sige::fast_div_magic(best * es / 16 + 1);
     c.m_b2 = sige::fast_div_magic(b2);
     c.m_b = sige::fast_div_magic(g.b);
+    c.gate_max = 0x7FFFFFFF;
     long grid = 1L << 30;  // the launch trims this to the CUs' resident capacity
     if (!(fused && copy))  // tiles at capacity, M tiles padded to a multiple of 8 (see the kernel's tile order)
         grid = (((long)g.cap * b2 + BM - 1) / BM + 7) / 8 * 8 * ((g.cout + BN - 1) / BN);
@@ -248,9 +250,11 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
 // Launch configuration of k_layer (kernels_layer.hip).  A wave holds the
 // weight fragments of at most kLayerFrags/NT K steps of a chunk, so a chunk
 // has at most 4*kLayerFrags/NT steps: kpc <= floor(4*kLayerFrags/(NT*k*k))
-// K slices per tap, a power of 2.  Among those, the fewest K slices in all
-// (then the fewest chunks) whose staged windows fit in half of the CU's LDS
-// (two workgroups per CU), else in all of it.  A block slot's staged window
+// K slices per tap, a power of 2.  Among those, the fewest chunks (then the
+// fewest K slices in all) whose staged windows fit in half of the CU's LDS
+// (two workgroups per CU), else in all of it: a chunk costs a round trip of
+// window staging and a barrier, several microseconds, while a K slice of zero
+// padding costs a few MFMAs.  A block slot's staged window
 // takes gps groups of 64 16-byte units plus 16 units for its bank rotation
 // (see kernels_layer.hip); the LDS also holds the
 // epilogue's 4 partial tiles and the rounded tile.
@@ -292,7 +296,7 @@ int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
             const long need_w = (long)ns * (64 * gps + 16) * 16;
             const long need = need_w > epi ? need_w : epi;
             if (need > limit) break;
-            const long cost = (long)nch * kpc * 1024 + nch;  // K slices in all, then chunks
+            const long cost = (long)nch * 4096 + nch * kpc;  // chunks, then K slices in all
             if (!best_kpc || cost < best_cost) {
                 best_kpc = kpc;
                 best_gps = gps;
@@ -323,6 +327,7 @@ int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
     c.tiles_cap = (int)tiles;
     c.cus = dv.cus;
     c.spec = 0;
+    c.gate_min = 0;
     c.m_ps = sige::fast_div_magic(c.ps);
     c.m_rs = sige::fast_div_magic(c.rs);
     c.m_b2 = sige::fast_div_magic(b2);
@@ -490,6 +495,182 @@ int split_common(const void *a_edit, const void *w_krsc, const float *bias, cons
     return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
                                     nullptr, nullptr, g, cfg, cc, (hipStream_t)stream, (float *)workspace),
                   what, (hipStream_t)stream);
+}
+
+
+// ---- The kernel choice of sige_sparse_conv_layer_auto ----
+//
+// Two kernels compute the fused layer.  k_layer gives each tile of output rows
+// its whole K range, chunk after chunk, and every row tile reads its own copy
+// of the weights; the split spreads (row group, input-channel chunk, channel
+// tile) work items over all CUs, reads each weight once per row group and adds
+// the chunks in a second launch.  A long K range over few blocks -- the deep,
+// low-resolution layers, where the mer.dev notes (5 "Conclusion &
+// Discussion") find the block-sparse method least effective -- favours the
+// split; many blocks favour k_layer.  The list length is on the device, so
+// the host prices both kernels for every list length with the cost model
+// below and derives one threshold: the split does lists of at most split_max
+// blocks, k_layer the longer ones.  When both sides of the threshold can
+// occur, both kernels are launched and each checks *count on the device
+// (LayerCfg::gate_min, ConvCfg::gate_max): the one not chosen exits at once.
+//
+// The model, in microseconds for a list of `cnt` blocks (M tiles of 64 rows
+// and N tiles of 32 channels, `tiles` of them):
+//   k_layer: s0 + chunks * (s1 + s2 * stage_groups) * max(1, s3 * tiles * steps / slots)
+//     (a chunk's round trip grows with the 1 KiB staging loads of its windows,
+//      stage_groups per tile; once the tiles' MFMA steps exceed what the
+//      resident slots overlap, time grows with the tiles)
+//   split:   p0 + p1 * weight MB + p2 * GFLOP + p3 * tiles
+//            + p4 * ceil(tiles * split_chunks / split_slots) * split_stage_kb
+//     (the weights stream once; the work items' rounds each stage a tile's
+//      windows of split_stage_kb KiB)
+// Constants fitted (least squares on log time) to both kernels timed on MI355X
+// on edits of seeds other than the benchmark's, five edit areas, the U-Net,
+// GauGAN and latent-diffusion layers (calibrate_layer_choice.py in the package).
+struct ChoiceModel {
+    double s[4], p[5];
+};
+constexpr ChoiceModel kChoice = {{3.425, 3.042, 0.05165, 0.04214}, {10.91, 0.1544, 2.363, 0.003549, 0.04061}};
+
+struct LayerFeat {
+    int cap, b2, ntn;
+    int chunks, steps, groups, slots;  // k_layer
+    int split_chunks, split_slots;     // the split
+    double split_kb;                   // KiB of one tile's staged windows in the split
+    double wmb, gflop_per_block;       // both
+};
+
+LayerFeat layer_features(const Geo &g, int dt, const sige::LayerCfg &lc) {
+    LayerFeat f{};
+    const int es = sige::elem_bytes(dt);
+    const int b2 = g.b * g.b, BM = 16 * lc.mt;
+    int ns = (BM - 1) / b2 + 2;
+    if (ns > BM) ns = BM;
+    if (ns > g.cap) ns = g.cap;
+    const DevInfo dv = dev_info();
+    f.cap = g.cap;
+    f.b2 = b2;
+    f.ntn = (g.cout + 31) / 32;
+    f.chunks = lc.nch;
+    f.steps = lc.steps;
+    f.groups = ns * lc.gps;
+    f.slots = dv.cus * (lc.lds_bytes <= dv.lds / 2 - 1024 ? 2 : 1);
+    f.wmb = (double)g.cout * g.k * g.k * g.cin * es * 1e-6;
+    f.gflop_per_block = 2.0 * b2 * g.cout * g.k * g.k * (double)g.cin * 1e-9;
+    ConvCfg cc;
+    if (choose_conv(g, dt, 1, 1, &cc, 1) == SIGE_OK) {
+        f.split_chunks = (g.cin + cc.ck - 1) / cc.ck;
+        f.split_slots = dv.cus * (cc.lds_bytes <= dv.lds / 2 ? 2 : 1);
+        f.split_kb = cc.a_bytes / 1024.0;
+    }
+    return f;
+}
+
+double cost_single(const LayerFeat &f, int cnt) {
+    const double tiles = (double)(((long)cnt * f.b2 + 63) / 64) * f.ntn;
+    const double per = kChoice.s[1] + kChoice.s[2] * f.groups;
+    const double fill = kChoice.s[3] * tiles * f.steps / f.slots;
+    return kChoice.s[0] + f.chunks * per * (fill > 1.0 ? fill : 1.0);
+}
+
+double cost_split(const LayerFeat &f, int cnt) {
+    const long tiles = (((long)cnt * f.b2 + 63) / 64) * f.ntn;
+    const long rounds = (tiles * f.split_chunks + f.split_slots - 1) / f.split_slots;
+    return kChoice.p[0] + kChoice.p[1] * f.wmb + kChoice.p[2] * f.gflop_per_block * cnt + kChoice.p[3] * tiles +
+           kChoice.p[4] * rounds * f.split_kb;
+}
+
+// Microseconds a launch adds when its kernel exits at once (measured on
+// MI355X against the kernel alone): k_layer (a persistent grid, one round
+// trip for *count and the indices), the split (two launches).
+constexpr double kGateOffSingle = 3.0, kGateOffSplit = 3.2;
+
+// The plan: the split for lists of at most the returned length, k_layer for
+// longer ones (-1: k_layer only; cap: the split only).  T is the largest list
+// length the split is priced faster at; gating at T costs every list the other
+// kernel's empty launch, so the plan is, of k_layer only, the split only and
+// the gate at T, the one whose worst relative loss against the cheaper kernel
+// over list lengths 1..cap is smallest.
+int split_threshold(const LayerFeat &f) {
+    int t = -1;
+    for (int cnt = 1; cnt <= f.cap; ++cnt)
+        if (cost_split(f, cnt) < cost_single(f, cnt)) t = cnt;
+    if (t < 0 || t >= f.cap) return t;
+    double loss_single = 0, loss_split = 0, loss_gate = 0;
+    for (int cnt = 1; cnt <= f.cap; ++cnt) {
+        const double a = cost_single(f, cnt), b = cost_split(f, cnt), best = a < b ? a : b;
+        const double gate = cnt <= t ? b + kGateOffSingle : a + kGateOffSplit;
+        loss_single = fmax(loss_single, a / best);
+        loss_split = fmax(loss_split, b / best);
+        loss_gate = fmax(loss_gate, gate / best);
+    }
+    if (loss_gate <= loss_single && loss_gate <= loss_split) return t;
+    return loss_split < loss_single ? f.cap : -1;
+}
+
+struct AutoPlan {
+    sige::LayerCfg lc;
+    ConvCfg cc;
+    LayerFeat f;
+    int split_max;  // -1: k_layer only; >= cap: the split only; else both, gated on *count
+    long ws_bytes;  // workspace for lists of at most split_max blocks
+};
+
+// The plan of a layer, remembered per (geometry, dtype, device): the
+// threshold scan prices every list length once.
+int plan_auto(const Geo &g, int dt, AutoPlan *out) {
+    struct Entry {
+        Geo g;
+        int dt, dev;
+        AutoPlan p;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int used = 0, next = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        dev = -1;
+    }
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].dt == dt && cache[i].dev == dev && !memcmp(&cache[i].g, &g, sizeof(Geo))) {
+                *out = cache[i].p;
+                return SIGE_OK;
+            }
+    }
+    AutoPlan p{};
+    int rc;
+    if ((rc = choose_layer(g, dt, &p.lc))) return rc;
+    p.f = layer_features(g, dt, p.lc);
+    // the split's limits (LDS, register-resident weights) may exclude it
+    p.split_max = p.f.split_chunks > 0 ? split_threshold(p.f) : -1;
+    p.ws_bytes = 0;
+    if (p.split_max >= 0) {
+        if (choose_conv(g, dt, 1, 1, &p.cc, 1) != SIGE_OK) {
+            p.split_max = -1;
+        } else {
+            Geo gt = g;
+            gt.cap = p.split_max < g.cap ? p.split_max : g.cap;
+            p.ws_bytes = sige::split_workspace_bytes(dt, gt, p.cc);
+            if (p.ws_bytes < 0) return fail(SIGE_EINVAL, "unknown tile shape");
+        }
+    }
+    if (p.split_max >= g.cap) {
+        p.cc.gate_max = 0x7FFFFFFF;
+    } else if (p.split_max >= 0) {
+        p.cc.gate_max = p.split_max;
+        p.lc.gate_min = p.split_max + 1;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    Entry &e = cache[used < 64 ? used++ : (next++ & 63)];
+    e.g = g;
+    e.dt = dt;
+    e.dev = dev;
+    e.p = p;
+    *out = p;
+    return SIGE_OK;
 }
 
 }  // namespace
@@ -768,6 +949,82 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
     return finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
                                      nullptr, nullptr, g, cfg, cc, (hipStream_t)stream),
                   "sige_sparse_conv_layer", (hipStream_t)stream);
+}
+
+int sige_sparse_conv_layer_plan(const sige_geom *gp, int dtype, sige_layer_plan *out) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!out) return fail(SIGE_EINVAL, "output pointer is NULL");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    AutoPlan p;
+    if ((rc = plan_auto(g, dtype, &p))) return rc;
+    out->split_max = p.split_max;
+    out->cap = g.cap;
+    out->workspace_bytes = p.ws_bytes;
+    out->chunks = p.f.chunks;
+    out->steps = p.f.steps;
+    out->stage_groups = p.f.groups;
+    out->slots = p.f.slots;
+    out->n_tiles = p.f.ntn;
+    out->weight_mb = p.f.wmb;
+    out->gflop_per_block = p.f.gflop_per_block;
+    out->split_chunks = p.f.split_chunks;
+    out->split_slots = p.f.split_slots;
+    out->split_stage_kb = p.f.split_kb;
+    g_msg[0] = 0;
+    return SIGE_OK;
+}
+
+int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                                int copy_cached, void *workspace, int64_t workspace_bytes, void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!a_edit || !w_krsc || !idx || !count || !out || (copy_cached && !cached))
+        return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(a_edit, 16) || !aligned(w_krsc, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+        (copy_cached && !aligned(cached, 16)))
+        return fail(SIGE_EALIGN, "tensors and workspace must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SIGE_EALIGN, "bias must be 4-byte aligned");
+    if (workspace_bytes < 0) return fail(SIGE_EINVAL, "negative workspace size");
+    const int es = sige::elem_bytes(dtype);
+    const size_t obytes = (size_t)g.n * g.ho * g.wo * g.cout * es;
+    const Region rd[] = {{a_edit, (size_t)g.n * g.h * g.w * g.cin * es}, {copy_cached ? cached : nullptr, obytes},
+                         {w_krsc, (size_t)g.cout * g.k * g.k * g.cin * es}, {bias, (size_t)g.cout * 4},
+                         {idx, (size_t)g.cap * 4}, {count, 4}};
+    {
+        const Region wr[] = {{out, obytes}};
+        if (regions_overlap(wr, 1, rd, 6))
+            return fail(SIGE_EINVAL, "out overlaps a_edit, cached, the weights, bias, idx or count");
+    }
+    AutoPlan p;
+    if ((rc = plan_auto(g, dtype, &p))) return rc;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes)
+            return fail(SIGE_ERANGE, "workspace of %lld bytes, %ld needed", (long long)workspace_bytes, p.ws_bytes);
+        const Region wr[] = {{out, obytes}, {workspace, (size_t)p.ws_bytes}};
+        if (regions_overlap(wr, 2, rd, 6)) return fail(SIGE_EINVAL, "the workspace overlaps another argument");
+    }
+    if ((rc = device_ready())) return rc;
+    const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
+    const hipStream_t st = (hipStream_t)stream;
+    if (p.split_max < g.cap) {  // k_layer: every list when the split never wins, else those above split_max
+        if ((rc = finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out,
+                                            copy_cached ? cached : nullptr, nullptr, nullptr, g, p.lc, cc, st),
+                         "sige_sparse_conv_layer_auto", st)))
+            return rc;
+    }
+    if (p.split_max >= 0)  // the split: lists of at most split_max blocks
+        return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out,
+                                        copy_cached ? cached : nullptr, nullptr, nullptr, g, p.cc, cc, st,
+                                        (float *)workspace),
+                      "sige_sparse_conv_layer_auto", st);
+    return SIGE_OK;
 }
 
 int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *gp, int dtype) {

@@ -38,6 +38,7 @@ struct ConvCfg {
     uint32_t m_ib2, m_ib;  // fast_div_magic(ib*ib), fast_div_magic(ib)
     uint32_t m_vpc1;       // fast_div_magic(ck*es/16 + 1): 16-byte LDS slots per staged pixel
     uint32_t m_b2, m_b;    // fast_div_magic(b*b), fast_div_magic(b): output rows -> block slot, pixel
+    int gate_max;          // the split runs only for lists of at most this many blocks (else it exits at once)
 };
 
 // Launch configuration of the fused layer / block convolution (kernels_layer.hip).
@@ -57,6 +58,7 @@ struct LayerCfg {
     int tiles_cap;       // tiles (padding included) at full capacity
     int cus;             // compute units of the device
     int spec;            // workgroups below this fetch their first weights before the list length (set at launch)
+    int gate_min;        // runs only for lists of at least this many blocks (else every workgroup exits at once)
     uint32_t m_ps, m_rs, m_b2, m_b;  // fast_div_magic of ps, rs, b*b, b
 };
 

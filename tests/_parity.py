@@ -152,10 +152,12 @@ def check_layer_sampled(name, a_e, wt, bias, cache, out, idx, L, mask_full, seed
     return err / scale
 
 
-def run_layer_full(a_e_gpu, wt, bias, cache_gpu, L, mask_gpu):
-    """reduce + fused layer (copy_cached = 1) on the GPU for layer spec L; returns (out, CPU list)."""
+def run_layer_full(a_e_gpu, wt, bias, cache_gpu, L, mask_gpu, layer=None):
+    """reduce + fused layer (copy_cached = 1) on the GPU for layer spec L; returns (out, CPU list).
+    layer: the entry point (default sige_sparse_conv_layer)."""
     g = ssi.geom(a_e_gpu.shape[0], L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
     idx, count = ssi.sige_reduce_mask(mask_gpu, g, L.dilate)
-    out = ssi.sige_sparse_conv_layer(a_e_gpu, ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache_gpu, idx, count, g)
+    layer = layer or ssi.sige_sparse_conv_layer
+    out = layer(a_e_gpu, ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache_gpu, idx, count, g)
     torch.cuda.synchronize()
     return out, idx[:int(count.item())].cpu()

@@ -377,3 +377,39 @@ def test_reduce_layers_validation(lib):
     assert call(cached=cached, out=out, dt=7) == EDTYPE
     assert call(cached=[cached[0] + 8, cached[1], cached[2]], out=out) == EALIGN
     assert call(geoms=[gs[0], _g(h=256, w=256, b=1), gs[2]]) == ERANGE  # 65536 blocks: beyond one workgroup
+
+
+
+def test_layer_plan_without_a_gpu(lib):
+    """sige_sparse_conv_layer_plan needs no device: the threshold lies in [-1, cap],
+    a workspace is asked for exactly when the split can run, and a deep
+    low-resolution layer goes to the split for its smallest lists."""
+    for g, dt in ((_g(), torch.bfloat16), (_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2), torch.float16),
+                  (_g(1, 64, 128, 1024, 512), torch.bfloat16), (_g(1, 16, 16, 1280, 1280, 1, 1, 0, 2), torch.float16),
+                  (_g(1, 64, 64, 64, 64, 3, 1, 1, 8), torch.float32)):
+        p = ssi.sige_sparse_conv_layer_plan(g, dt)
+        assert -1 <= p.split_max <= p.cap == ssi.sige_max_blocks(g)
+        assert (p.workspace_bytes > 0) == (p.split_max >= 0)
+        assert p.chunks >= 1 and p.steps >= 1 and p.slots >= 1 and p.n_tiles >= 1
+    assert ssi.sige_sparse_conv_layer_plan(_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2), torch.float16).split_max >= 1
+    plan = L.LayerPlan()
+    assert lib.sige_sparse_conv_layer_plan(ctypes.byref(_g()), 7, ctypes.byref(plan)) == EDTYPE
+    assert lib.sige_sparse_conv_layer_plan(ctypes.byref(_g()), 1, None) == EINVAL
+
+
+def test_auto_layer_validation(lib):
+    """Checks before any device work: a workspace smaller than the plan's is
+    SIGE_ERANGE, overlaps and NULL pointers SIGE_EINVAL."""
+    f = lib.sige_sparse_conv_layer_auto
+    g = _g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)
+    need = ssi.sige_sparse_conv_layer_plan(g, torch.float16).workspace_bytes
+    assert need > 0
+    s = _v(0)
+    args = (_v(A), _v(B), None, None, _v(C), _v(C + 4096), 2, ctypes.byref(g), _v(D), 0)
+    assert f(*args, _v(E), need - 16, s) == ERANGE
+    assert f(*args, None, 0, s) == ERANGE
+    assert f(_v(A), _v(B), None, None, _v(C), _v(C + 4096), 2, ctypes.byref(g), _v(A + 64), 0, _v(E), need,
+             s) == EINVAL  # out overlaps a_edit
+    assert f(*args, _v(D + 4096), need, s) == EINVAL  # the workspace overlaps out
+    assert f(None, _v(B), None, None, _v(C), _v(C + 4096), 2, ctypes.byref(g), _v(D), 0, _v(E), need, s) == EINVAL
+    assert f(*args[:6], 7, *args[7:], _v(E), need, s) == EDTYPE

@@ -1,0 +1,128 @@
+"""The layer entry point that picks its kernel (sige_sparse_conv_layer_auto):
+every chain, GauGAN and latent-diffusion layer against the oracle, and bit for
+bit against the kernel the plan names for the list length (the other kernel
+must leave `out` alone, cache copy included)."""
+import pytest
+import torch
+
+import oracle
+import spatially_sparse_incremental_amd as ssi
+import synth
+from synth.gen import DTYPES
+from _parity import check_layer_sampled, run_layer_full
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_choice(name, a_e_gpu, wt, bias, cache_gpu, L, mask_gpu, out):
+    """`out` (auto) equals, bit for bit, the kernel the plan picks for this list."""
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    plan = ssi.sige_sparse_conv_layer_plan(g, DTYPES[L.dtype])
+    assert -1 <= plan.split_max <= plan.cap == ssi.sige_max_blocks(g)
+    idx, count = ssi.sige_reduce_mask(mask_gpu, g, L.dilate)
+    n = int(count.item())
+    wk = ssi.weight_to_krsc(wt).cuda()
+    if n <= plan.split_max:
+        ref = ssi.sige_sparse_conv_layer_split(a_e_gpu, wk, bias.cuda(), cache_gpu, idx, count, g)
+    else:
+        ref = ssi.sige_sparse_conv_layer(a_e_gpu, wk, bias.cuda(), cache_gpu, idx, count, g)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), \
+        f"{name}: auto differs from the {'split' if n <= plan.split_max else 'single-range'} kernel"
+    return "split" if n <= plan.split_max else "single"
+
+
+@pytest.mark.parametrize("area", [0.005, 0.012, 0.15])
+def test_auto_unet_chain_every_layer(area):
+    wl = synth.workload("unet_chain_12conv_bf16")
+    seed = 3
+    first = wl.layers[0]
+    m = synth.edit_shape(wl, seed, area).raster(first.h, first.w)
+    a_o = synth.make_activation(1, first.h, first.w, first.c_in, first.dtype, seed)
+    a_e = synth.make_edit(a_o, m, wl.edit_kind, seed)
+    mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+    x = a_e.cuda()
+    paths = []
+    for li, L in enumerate(wl.layers):
+        wt, bias = synth.make_layer_tensors(L, seed * 100 + li)
+        ho, wo, _, _, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
+        cache = synth.make_activation(1, ho, wo, L.c_out, L.dtype, seed * 100 + li + 50)
+        out, idx = run_layer_full(x, wt, bias, cache.cuda(), L, mask, layer=ssi.sige_sparse_conv_layer_auto)
+        check_layer_sampled(f"auto chain {L.name} area {area}", x.cpu(), wt, bias, cache, out.cpu(), idx, L,
+                            mask.cpu(), seed + li, sample=None if area <= 0.012 else 8)
+        paths.append(_check_choice(f"auto chain {L.name}", x, wt, bias, cache.cuda(), L, mask, out))
+        x = out
+    print(f"chain area {area}: {paths}")
+
+
+@pytest.mark.parametrize("area", [0.005, 0.05, 0.30])
+def test_auto_gaugan_layers(area):
+    wl = synth.workload("gaugan_4conv_bf16")
+    seed = 4
+    shape = synth.edit_shape(wl, seed, area)
+    for li, L in enumerate(wl.layers):
+        m = shape.raster(L.h, L.w)
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li)
+        a_e = synth.make_edit(a_o, m, wl.edit_kind, seed + li)
+        wt, bias = synth.make_layer_tensors(L, seed + li)
+        cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
+        mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+        out, idx = run_layer_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask, layer=ssi.sige_sparse_conv_layer_auto)
+        check_layer_sampled(f"auto gaugan {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L,
+                            mask.cpu(), li, sample=None if area <= 0.012 else 8)
+        _check_choice(f"auto gaugan {L.name}", a_e.cuda(), wt, bias, cache.cuda(), L, mask, out)
+
+
+@pytest.mark.parametrize("area", [0.012, 0.30])
+def test_auto_latent_diffusion_layers(area):
+    wname = "ldm_64x64x320_f16"
+    wl = synth.workload(wname)
+    seed = 5
+    shape = synth.edit_shape(wl, seed, area)
+    for li, L in enumerate(wl.layers):
+        m = shape.raster(L.h, L.w)
+        a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li)
+        a_e = synth.make_edit(a_o, m, wl.edit_kind, seed + li)
+        wt, bias = synth.make_layer_tensors(L, seed + li)
+        cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50)
+        mask = ssi.sige_diff_mask(a_o.cuda(), a_e.cuda(), wl.tau)
+        out, idx = run_layer_full(a_e.cuda(), wt, bias, cache.cuda(), L, mask, layer=ssi.sige_sparse_conv_layer_auto)
+        check_layer_sampled(f"auto {wname} {L.name} area {area}", a_e, wt, bias, cache, out.cpu(), idx, L,
+                            mask.cpu(), li)
+        _check_choice(f"auto {wname} {L.name}", a_e.cuda(), wt, bias, cache.cuda(), L, mask, out)
+
+
+def test_auto_persistent_buffer_and_empty_list():
+    """copy_cached = 0 writes only the listed blocks; an empty list writes nothing
+    (copy_cached = 0) or the cache (copy_cached = 1), on both sides of the plan."""
+    L = synth.workload("gaugan_4conv_bf16").layers[1]  # 64x128x1024 -> 512: the plan uses both kernels
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    plan = ssi.sige_sparse_conv_layer_plan(g, DTYPES[L.dtype])
+    assert 0 <= plan.split_max < plan.cap, "this layer should exercise both gated kernels"
+    wt, bias = synth.make_layer_tensors(L, 9)
+    wk = ssi.weight_to_krsc(wt).cuda()
+    a = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 9).cuda()
+    cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, 10).cuda()
+    cap = plan.cap
+    for n in (0, 1, plan.split_max, plan.split_max + 1, cap):
+        idx = torch.arange(cap, dtype=torch.int32, device="cuda")  # ascending, the first n listed
+        count = torch.tensor([n], dtype=torch.int32, device="cuda")
+        sentinel = torch.full_like(cache, 7.0)
+        got = ssi.sige_sparse_conv_layer_auto(a, wk, bias.cuda(), None, idx, count, g, out=sentinel.clone(),
+                                              copy_cached=False)
+        ref_fn = ssi.sige_sparse_conv_layer_split if n <= plan.split_max else ssi.sige_sparse_conv_layer
+        ref = ref_fn(a, wk, bias.cuda(), None, idx, count, g, out=sentinel.clone(), copy_cached=False)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"copy_cached=0, {n} blocks"
+        got = ssi.sige_sparse_conv_layer_auto(a, wk, bias.cuda(), cache, idx, count, g)
+        ref = ref_fn(a, wk, bias.cuda(), cache, idx, count, g)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"copy_cached=1, {n} blocks"
+        if n == 0:
+            assert torch.equal(got.view(torch.uint8), cache.view(torch.uint8))
