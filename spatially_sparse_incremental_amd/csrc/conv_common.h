@@ -36,6 +36,26 @@ struct MfmaStep<0> {  // fp32: four 16x16x4 MFMAs; lane group g holds k = 4g..4g
     }
 };
 
+// One 32x32x16 MFMA (bf16, fp16): lane l holds A row l % 32 and B column
+// l % 32, each at k = 8 * (l / 32) .. +7; accumulator register v of lane l
+// is D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
+template <int DT>
+struct Mfma32;
+template <>
+struct Mfma32<1> {
+    __device__ static __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma32<2> {
+    __device__ static __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+};
+
 // Store 8 consecutive channels (fp32: the second 16-byte half only when
 // `full`; c_out is a multiple of 4 there, of 8 for 16-bit types).
 template <int DT>

@@ -14,7 +14,11 @@
 // walked as (tap, slice of KS input channels) steps.  A workgroup of 4 waves
 // owns a tile of 16*MT rows x 16*NT output channels; the waves split the K
 // steps in contiguous runs and each accumulates the whole tile, so every
-// staged window element is read from LDS by one wave only.  Two workgroups
+// staged window element is read from LDS by one wave only.  16-bit types run
+// 32x32x16 MFMAs (a 64 x 32 tile is two 32 x 32 fragments, a 32-channel K
+// slice two 16-channel halves): at one or two waves per SIMD they issue about
+// 1.3-1.7 times the flops of 16x16x32 ones.  fp32 (and tiles of 16 channels)
+// run 16x16 MFMAs.  Two workgroups
 // share a CU, so one's memory round trips overlap the other's MFMAs.
 //
 // The critical path of a tile, at small edits the whole launch:
@@ -77,8 +81,9 @@ __device__ __forceinline__ int layer_tiles(const LayerCfg &c, int cnt, int b2) {
 }
 
 // This wave's weight fragments of the K steps st0, st0 + 1, ... of the chunk
-// at input channel c0 (lane l: column l % 16 of each N subtile and the EPV
-// input channels at (l / 16) * EPV of the step's slice).  wcol[nt] is the
+// at input channel c0 (16x16: lane l takes column l % 16 of each N subtile
+// and the EPV input channels at (l / 16) * EPV of the step's slice; W32:
+// column l % 32, fragment h the channels at 16 h + (l / 32) * EPV).  wcol[nt] is the
 // lane's column offset into the weights; the step's tap offset is uniform, so
 // each load is a scalar base plus a 32-bit lane offset (column, then channel
 // within the tap, both non-negative).  Channels past c_in (a partial last
@@ -86,7 +91,7 @@ __device__ __forceinline__ int layer_tiles(const LayerCfg &c, int cnt, int b2) {
 // of the tap: their products meet zeros in the staged windows.  `dummy` points
 // every lane at the first fragment instead (one cache line), for a workgroup
 // that does not know yet whether it has a tile.
-template <int DT, int NT, int SMAX>
+template <int DT, int NT, int SMAX, bool W32>
 __device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, const LayerCfg &c,
                                               u32x4 (&bfr)[SMAX][NT], const int (&wcol)[NT], int c0, int st0,
                                               int kl, bool dummy) {
@@ -97,9 +102,11 @@ __device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, co
         const int stp = min(st0 + j, c.steps - 1);
         const int tap = stp >> c.lkpc, cb = c0 + (stp & (c.kpc - 1)) * KS;
         const uint8_t *base = w + ((uint32_t)(tap * g.cin * ES) & keep);
-        const int lch = min(cb + kl, g.cin - EPV) * ES;  // in [0, c_in * ES)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bfr[j][nt] = ld16(base + ((uint32_t)(wcol[nt] + lch) & keep));
+        for (int nt = 0; nt < NT; ++nt) {
+            const int lch = min(cb + kl + (W32 ? nt * 16 : 0), g.cin - EPV) * ES;  // in [0, c_in * ES)
+            bfr[j][nt] = ld16(base + ((uint32_t)(wcol[nt] + lch) & keep));
+        }
     }
 }
 
@@ -110,7 +117,11 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     constexpr int BM = 16 * MT, BN = 16 * NT, NF = MT * NT;
     constexpr int SMAX = kLayerFrags / NT;  // K steps per wave and chunk (weights in registers)
     constexpr int VPR = BN * ES / 16;       // 16-byte output vectors per tile row
+    constexpr bool W32 = DT != 0 && NT == 2;  // 32x32x16 MFMAs: one 32-channel N fragment
+    constexpr int MF = W32 ? MT / 2 : MT;     // M fragments (32 or 16 rows)
+    constexpr int NH = W32 ? 2 : 1;           // A fragments per M fragment and K step
     static_assert(BM <= 64, "a tile touches at most 64 block slots: one per lane");
+    static_assert(!W32 || MT % 2 == 0, "32-row M fragments");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const Geo &g = a.g;
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     const int grid = gridDim.x;
     const int st0 = wave * c.spw;                                                     // this wave's K steps
     const int nst = __builtin_amdgcn_readfirstlane(max(0, min(c.steps - st0, c.spw)));  // [st0, st0 + nst)
-    const int kl = (lane >> 4) * EPV;  // this lane's channels within a K slice
+    const int kl = (W32 ? lane >> 5 : lane >> 4) * EPV;  // this lane's channels within a K slice (half)
 
     // The list length, as a vector load issued before anything else (cap >> 31
     // is 0: the per-lane address keeps the value in a vector register, so the
@@ -182,13 +193,13 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
         const float *bsrc = a.bias ? a.bias : (const float *)a.w;  // any readable floats without a bias
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int col = min(n0 + nt * 16 + (lane & 15), g.cout - 1);
+            const int col = min(n0 + (W32 ? lane & 31 : nt * 16 + (lane & 15)), g.cout - 1);
             bcol[nt] = bsrc[col];
             wcol[nt] = col * k2 * g.cin * ES;
         }
         const bool early_w = (int)blockIdx.x < c.spec;
         if constexpr (FIRST) {
-            layer_weights<DT, NT, SMAX>(a.w, g, c, bfr, wcol, 0, st0, kl, !early_w);
+            layer_weights<DT, NT, SMAX, W32>(a.w, g, c, bfr, wcol, 0, st0, kl, !early_w);
             __builtin_amdgcn_sched_barrier(0);
             cnt = min(max(cnt_raw, 0), g.cap);
             // A launch paired with the split over input channels: a list below
@@ -213,11 +224,11 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                 sox = bx * g.b;
             }
         }
-        // LDS byte offset of this lane's row in each M subtile (tap 0, this lane's channels)
-        int rb[MT];
+        // LDS byte offset of this lane's row in each M fragment (tap 0, this lane's channels)
+        int rb[MF];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = m0 + mt * 16 + (lane & 15);
+        for (int mt = 0; mt < MF; ++mt) {
+            const int r = m0 + (W32 ? mt * 32 + (lane & 31) : mt * 16 + (lane & 15));
             int off = 0;
             if (r < mrows) {
                 const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
@@ -227,11 +238,16 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             }
             rb[mt] = off + kl * ES;
         }
-        f32x4 acc[MT][NT];
+        f32x4 acc[W32 ? 1 : MT][NT];  // 16x16 fragments
+        f32x16 acc32[MF];             // 32x32 fragments (W32)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < (W32 ? 1 : MT); ++mt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < MF; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc32[mt][v] = 0.f;
 
         for (int ch = 0; ch < c.nch; ++ch) {
             const int c0 = ch * c.ck;
@@ -268,7 +284,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                 }
             }
             // the weights, when the registers do not hold this chunk's yet
-            if (ch > 0 || need_w) layer_weights<DT, NT, SMAX>(a.w, g, c, bfr, wcol, c0, st0, kl, false);
+            if (ch > 0 || need_w) layer_weights<DT, NT, SMAX, W32>(a.w, g, c, bfr, wcol, c0, st0, kl, false);
             __builtin_amdgcn_s_waitcnt(0);  // this wave's windows and weights have landed
             __syncthreads();
             // This wave's K steps: A fragments from LDS, B from registers.  Step
@@ -277,10 +293,12 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             // LDS wait is exact.
             {
                 int kk = kk0, kx = kx0, toff = toff0;
-                u32x4 av[2][MT];
-                int ua = (toff + kk * 4) * 16;  // a K slice is 4 units (KS * ES = 64 bytes)
+                u32x4 av[2][MF][NH];
+                int ua = (toff + kk * 4) * 16;  // a K slice is 4 units (KS * ES = 64 bytes), a half 2
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) av[0][mt] = *(const u32x4 *)(smem + rb[mt] + ua);
+                for (int mt = 0; mt < MF; ++mt)
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) av[0][mt][h] = *(const u32x4 *)(smem + rb[mt] + ua + h * 32);
 #pragma unroll
                 for (int j = 0; j < SMAX; ++j) {
                     if (j + 1 < SMAX) {
@@ -296,14 +314,25 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                             ua = (toff + kk * 4) * 16;
                         }
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) av[(j + 1) & 1][mt] = *(const u32x4 *)(smem + rb[mt] + ua);
+                        for (int mt = 0; mt < MF; ++mt)
+#pragma unroll
+                            for (int h = 0; h < NH; ++h)
+                                av[(j + 1) & 1][mt][h] = *(const u32x4 *)(smem + rb[mt] + ua + h * 32);
                     }
                     if (j < nst) {
+                        if constexpr (W32) {
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
+                            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                            for (int nt = 0; nt < NT; ++nt)
-                                acc[mt][nt] = MfmaStep<DT>::run(av[j & 1][mt], bfr[j][nt], acc[mt][nt]);
+                                for (int mt = 0; mt < MF; ++mt)
+                                    acc32[mt] = Mfma32<DT>::run(av[j & 1][mt][h], bfr[j][h], acc32[mt]);
+                        } else {
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                                for (int nt = 0; nt < NT; ++nt)
+                                    acc[mt][nt] = MfmaStep<DT>::run(av[j & 1][mt][0], bfr[j][nt], acc[mt][nt]);
+                        }
                     }
                 }
             }
@@ -312,11 +341,20 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
         // Epilogue: park the 4 partial tiles in accumulator layout, sum them per
         // (fragment, lane), add the bias, round, transpose through LDS, store rows.
         __syncthreads();  // every wave is done reading the windows (the partials take their LDS)
+        if constexpr (W32) {  // fragment (mt, q) = registers 4q..4q+3 of acc32[mt]
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MF; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                *(f32x4 *)(smem + (((wave * NF + mt * NT + nt) << 6) + lane) * 16) = acc[mt][nt];
+                for (int q = 0; q < 4; ++q)
+                    *(f32x4 *)(smem + (((wave * NF + mt * 4 + q) << 6) + lane) * 16) =
+                        f32x4{acc32[mt][4 * q], acc32[mt][4 * q + 1], acc32[mt][4 * q + 2], acc32[mt][4 * q + 3]};
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    *(f32x4 *)(smem + (((wave * NF + mt * NT + nt) << 6) + lane) * 16) = acc[mt][nt];
+        }
         __syncthreads();
         uint8_t *otile = smem + NW * NF * 64 * 16;  // the rounded tile, [BM][BN] in the storage type
 #pragma unroll
@@ -328,15 +366,22 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                 const f32x4 v = *(const f32x4 *)(smem + (((w * NF + f) << 6) + lane) * 16);
                 s += v;
             }
-            const int mt = f / NT, nt = f - mt * NT;
+            int row0, col;  // this lane's first row and its column in the tile
             float bv = bcol[0];
+            if constexpr (W32) {
+                row0 = (f >> 2) * 32 + (f & 3) * 8 + (lane >> 5) * 4;
+                col = lane & 31;
+            } else {
+                const int mt = f / NT, nt = f - mt * NT;
 #pragma unroll
-            for (int q = 1; q < NT; ++q) bv = nt == q ? bcol[q] : bv;
+                for (int q = 1; q < NT; ++q) bv = nt == q ? bcol[q] : bv;
+                row0 = mt * 16 + (lane >> 4) * 4;
+                col = nt * 16 + (lane & 15);
+            }
             if (!a.bias) bv = 0.f;
-            const int col = nt * 16 + (lane & 15);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = mt * 16 + (lane >> 4) * 4 + i;
+                const int row = row0 + i;
                 const float v = s[i] + bv;
                 if constexpr (DT == 0) {
                     *(float *)(otile + (row * BN + col) * 4) = v;
