@@ -150,6 +150,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     const int cnt_raw = a.count[lane & (g.cap >> 31)];
     int cnt = -1, ntiles = -1, mrows = 0;
     int tn_w = -1;  // N tile whose (single-chunk) weights are in the registers
+    int lin_next = 0;  // the next tile's block indices, loaded during this tile
     u32x4 bfr[SMAX][NT];
 
     // LDS layout of a staged window, in 16-byte units: pixel (yy, xx) holds its
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
         // fragments (the first workgroup of a CU fetches them before the list
         // length is known; the others load one line instead, then the weights
         // once the tile is known to exist)
-        const int lin = FUSED ? a.idx[s_lo + min(lane, ns - 1)] : 0;
+        const int lin = FUSED ? (FIRST ? a.idx[s_lo + min(lane, ns - 1)] : lin_next) : 0;
         float bcol[NT];
         int wcol[NT];
         const float *bsrc = a.bias ? a.bias : (const float *)a.w;  // any readable floats without a bias
@@ -207,6 +208,13 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             ntiles = cnt < c.gate_min ? 0 : layer_tiles<BM>(c, cnt, b2);
             mrows = cnt * b2;
             if (t >= ntiles) return false;
+        }
+        if (FUSED && t + grid < ntiles) {  // this workgroup's next tile: its block indices, one tile early
+            int tm2, tn2;
+            layer_tile(c, t + grid, tm2, tn2);
+            const int s2 = fdiv(min(tm2 * BM, mcap - 1), c.m_b2);
+            const int ns2 = min(g.cap - 1, fdiv(min(tm2 * BM + BM - 1, mcap - 1), c.m_b2)) - s2 + 1;
+            lin_next = a.idx[s2 + min(lane, ns2 - 1)];
         }
         if (m0 >= mrows) return true;  // a padding tile
         const bool need_w = FIRST ? !early_w : (c.nch > 1 || tn != tn_w);
