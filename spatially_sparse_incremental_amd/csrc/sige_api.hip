@@ -530,7 +530,7 @@ int split_common(const void *a_edit, const void *w_krsc, const float *bias, cons
 struct ChoiceModel {
     double s[4], p[5];
 };
-constexpr ChoiceModel kChoice = {{3.425, 3.042, 0.05165, 0.04214}, {10.91, 0.1544, 2.363, 0.003549, 0.04061}};
+constexpr ChoiceModel kChoice = {{3.572, 2.761, 0.0528, 0.04297}, {10.96, 0.16, 2.381, 0.003331, 0.04085}};
 
 struct LayerFeat {
     int cap, b2, ntn;
