@@ -614,7 +614,8 @@ def run_sweep(args):
     """Block size and dilation sweep (one JSON line per point, then a markdown
     table): blocks listed, MAC reduction, reduce and fused-layer times with and
     without the cache copy, the same for the layer split over input channels,
-    and the dense conv (torch/MIOpen) of the layer."""
+    the library's choice between the two (sige_sparse_conv_layer_auto), and the
+    dense conv (torch/MIOpen) of the layer."""
     import torch
     import torch.nn.functional as F
 
@@ -652,6 +653,11 @@ def run_sweep(args):
         t_split_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer_split(a_e, wk, bias, None, idx, cnt, g,
                                                                              out=persist, copy_cached=False,
                                                                              workspace=ws))
+        plan = ssi.sige_sparse_conv_layer_plan(g, a_e.dtype)
+        ws_auto = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+        t_auto_nocopy = graph_time(lambda: ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, None, idx, cnt, g,
+                                                                           out=persist, copy_cached=False,
+                                                                           workspace=ws_auto))
         key = (wname, L.h, L.c_in)
         if key not in dense_t:
             x_cl = a_e.permute(0, 3, 1, 2)
@@ -674,12 +680,15 @@ def run_sweep(args):
                "mac_reduction": round(d.ho * d.wo / act_pix, 2) if act_pix else None,
                "reduce_us": round(t_red, 3), "fused_copy_us": round(t_copy, 3),
                "fused_nocopy_us": round(t_nocopy, 3), "split_copy_us": round(t_split_copy, 3),
-               "split_nocopy_us": round(t_split_nocopy, 3), "dense_miopen_us": round(dense_t[key], 3),
-               "speedup_nocopy_vs_dense": round(dense_t[key] / min(t_nocopy, t_split_nocopy), 2)}
+               "split_nocopy_us": round(t_split_nocopy, 3), "auto_nocopy_us": round(t_auto_nocopy, 3),
+               "auto_path": "split" if blocks <= plan.split_max else "single",
+               "dense_miopen_us": round(dense_t[key], 3),
+               "speedup_auto_nocopy_vs_dense": round(dense_t[key] / t_auto_nocopy, 2)}
         rows.append(row)
         print(json.dumps(row), flush=True)
     cols = ["layer", "block", "dilate", "blocks", "capacity", "mac_reduction", "reduce_us", "fused_copy_us",
-            "fused_nocopy_us", "split_copy_us", "split_nocopy_us", "dense_miopen_us", "speedup_nocopy_vs_dense"]
+            "fused_nocopy_us", "split_copy_us", "split_nocopy_us", "auto_nocopy_us", "auto_path", "dense_miopen_us",
+            "speedup_auto_nocopy_vs_dense"]
     print("| " + " | ".join(cols) + " |")
     print("|" + "---|" * len(cols))
     for r in rows:
