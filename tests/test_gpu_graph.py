@@ -73,3 +73,51 @@ def test_graph_replays_match_eager(copy):
         assert torch.equal(got_idx, idx[:int(cnt.item())]), rep
         assert torch.equal(bits(got), bits(out)), rep
         assert int(cnt.item()) > 0
+
+
+def test_graph_replays_of_the_auto_layer_follow_the_list_length():
+    """sige_sparse_conv_layer_auto captured once on a layer whose plan enqueues both
+    kernels: replays with list lengths on either side of the threshold (written in
+    place) match an eager call bit for bit, and the kernel the plan names."""
+    L = synth.workload("gaugan_4conv_bf16").layers[1]  # 64x128x1024 -> 512: gated plan
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    plan = ssi.sige_sparse_conv_layer_plan(g, torch.bfloat16)
+    assert 0 <= plan.split_max < plan.cap
+    wt, bias = synth.make_layer_tensors(L, 31)
+    wk, bias = ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    a = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 32).cuda()
+    cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, 33).cuda()
+    idx = torch.zeros((plan.cap,), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(cache)
+
+    def layer():
+        ssi.sige_sparse_conv_layer_auto(a, wk, bias, cache, idx, cnt, g, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    rng = np.random.default_rng(34)
+    for n in (7, plan.split_max, plan.split_max + 1, 300, 0, plan.split_max // 2):
+        pick = np.sort(rng.choice(plan.cap, size=n, replace=False)).astype(np.int32)
+        idx.zero_()
+        idx[:n] = torch.from_numpy(pick).cuda()
+        cnt.fill_(n)
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        out.zero_()
+        layer()  # eager, same inputs
+        ref_fn = ssi.sige_sparse_conv_layer_split if n <= plan.split_max else ssi.sige_sparse_conv_layer
+        ref = ref_fn(a, wk, bias, cache, idx, cnt, g)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(got), bits(out)), n
+        assert torch.equal(bits(got), bits(ref)), n
