@@ -251,8 +251,10 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
  * one threshold per layer, sige_layer_plan.split_max: lists of at most that
  * many blocks go to the split, longer ones to the single-range kernel.  When
  * both can occur, both kernels are enqueued and the one not chosen exits as
- * soon as it has read *count (about two microseconds); no host timing, no
- * synchronisation, nothing allocated.
+ * soon as it has read *count (about three microseconds on MI355X); no host
+ * timing, no synchronisation, nothing allocated.  The first call for a
+ * geometry, dtype and device prices every list length up to the capacity
+ * (host work proportional to sige_max_blocks); later calls reuse the plan.
  *   Same arguments, checks and result as sige_sparse_conv_layer (up to the
  *   fp32 summation order of the kernel that runs), plus the split's
  *   workspace: at least sige_layer_plan.workspace_bytes of caller-owned
