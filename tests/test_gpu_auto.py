@@ -126,3 +126,43 @@ def test_auto_persistent_buffer_and_empty_list():
         assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"copy_cached=1, {n} blocks"
         if n == 0:
             assert torch.equal(got.view(torch.uint8), cache.view(torch.uint8))
+
+
+# (name, n, h, w, cin, cout, k, s, p, b, dtype, dilate, edit fraction): small shapes with
+# ragged tiles, two images, stride 2, 1x1 and 5x5 kernels, fp32
+SMALL = [
+    ("f32_nhwc", 1, 64, 64, 64, 64, 3, 1, 1, 8, "f32", 0, 0.01),
+    ("two_images_bf16", 2, 13, 17, 40, 24, 3, 1, 1, 4, "bf16", 1, 0.02),
+    ("stride2_f16", 1, 30, 26, 32, 48, 3, 2, 1, 3, "f16", 1, 0.02),
+    ("pointwise_f16", 1, 20, 20, 320, 64, 1, 1, 0, 4, "f16", 1, 0.02),
+    ("k5_f32", 1, 19, 23, 16, 16, 5, 1, 2, 3, "f32", 0, 0.02),
+    ("deep_small_f16", 1, 16, 16, 640, 640, 3, 1, 1, 2, "f16", 1, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_auto_small_shapes_against_the_oracle(case):
+    from _parity import DT, active_pixels, assert_close, bits, layer_inputs, rand, random_mask, run_layer_oracle
+    name, n, h, w, cin, cout, k, s, p, b, dts, d, frac = case
+    dt = DT[dts]
+    mask = random_mask(n, h, w, frac, 17)
+    a_o, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 18, mask)
+    ho, wo, _, _, _ = oracle.geometry(h, w, k, s, p, b)
+    cache = rand((n, ho, wo, cout), dt, 19)
+    g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
+    ref = run_layer_oracle(a_o, a_e, wt, bias, cache, k, s, p, b, d)
+    plan = ssi.sige_sparse_conv_layer_plan(g, dt)
+    ae, wk, bs, cg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache.cuda()
+    idx, count = ssi.sige_reduce_mask(ssi.sige_diff_mask(a_o.cuda(), ae, 1e-6), g, d)
+    out = ssi.sige_sparse_conv_layer_auto(ae, wk, bs, cg, idx, count, g)
+    torch.cuda.synchronize()
+    cnt = int(count.item())
+    assert torch.equal(idx[:cnt].cpu(), ref["idx"]) and cnt > 0
+    sel = active_pixels(ref["act"], b, ho, wo)
+    keep = ~sel.expand_as(cache)
+    assert torch.equal(out.cpu()[keep].view(torch.uint8), cache[keep].view(torch.uint8))
+    assert_close(out.cpu(), ref["out64"], dt, sel, f"auto {name}")
+    fn = ssi.sige_sparse_conv_layer_split if cnt <= plan.split_max else ssi.sige_sparse_conv_layer
+    chosen = fn(ae, wk, bs, cg, idx, count, g)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out.cpu()), bits(chosen.cpu())), f"{name}: auto differs from the planned kernel"
