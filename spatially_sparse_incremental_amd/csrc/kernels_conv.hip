@@ -161,7 +161,6 @@ __device__ __forceinline__ StreamPlan stream_plan(int cnt, int b2, int bm, int n
 }
 
 constexpr int kConvWaves = 8;  // waves per workgroup of the implicit GEMM
-constexpr int kCopyBitmapWords = 1024;  // static LDS bitmap of listed blocks for the copy (32768 blocks)
 constexpr int kConvThreads = 64 * kConvWaves;
 
 // This wave's weight fragments for the chunk at input channel c0: K steps

@@ -113,7 +113,7 @@ __device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, co
 template <int DT, int MT, int NT, bool FUSED, bool TAIL>
 __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     constexpr int NW = kLayerWaves, NTHR = kLayerThreads;
-    constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
+    constexpr int ES = elem_bytes(DT), EPV = 16 / ES;
     constexpr int BM = 16 * MT, BN = 16 * NT, NF = MT * NT;
     constexpr int SMAX = kLayerFrags / NT;  // K steps per wave and chunk (weights in registers)
     constexpr int VPR = BN * ES / 16;       // 16-byte output vectors per tile row

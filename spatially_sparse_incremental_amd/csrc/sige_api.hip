@@ -264,7 +264,7 @@ int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
     c.nt = 2;
     const int es = sige::elem_bytes(dt);
     const int ks = dt == SIGE_F32 ? 16 : 32;
-    const int b2 = g.b * g.b, ib2 = g.ib * g.ib, k2 = g.k * g.k;
+    const int b2 = g.b * g.b, k2 = g.k * g.k;
     const int nw = sige::kLayerWaves;
     if ((nw * (sige::kLayerFrags / c.nt)) / k2 < 1) c.nt = 1;  // large kernels: 16 channels per tile
     const int max_kpc = (nw * (sige::kLayerFrags / c.nt)) / k2;  // K slices per tap and chunk
