@@ -681,7 +681,7 @@ def run_sweep(args):
                "reduce_us": round(t_red, 3), "fused_copy_us": round(t_copy, 3),
                "fused_nocopy_us": round(t_nocopy, 3), "split_copy_us": round(t_split_copy, 3),
                "split_nocopy_us": round(t_split_nocopy, 3), "auto_nocopy_us": round(t_auto_nocopy, 3),
-               "auto_path": "split" if blocks <= plan.split_max else "single",
+               "auto_path": _auto_path(plan, blocks),
                "dense_miopen_us": round(dense_t[key], 3),
                "speedup_auto_nocopy_vs_dense": round(dense_t[key] / t_auto_nocopy, 2)}
         rows.append(row)
@@ -764,7 +764,7 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     t_auto = graph_time(lambda: ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, cache, idx, cnt, g, out=out,
                                                                 workspace=ws_auto))
     res = {"blocks": int(cnt.item()), "auto_us": round(t_auto, 3),
-           "auto_path": "split" if int(cnt.item()) <= plan.split_max else "single", "split_max": plan.split_max,
+           "auto_path": _auto_path(plan, int(cnt.item())), "split_max": plan.split_max,
            "single_range_us": round(t_plain, 3), "split_us": round(t_split, 3)}
     try:
         x_cl = a_e.permute(0, 3, 1, 2)
@@ -830,7 +830,7 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
         plan = ssi.sige_sparse_conv_layer_plan(ly["g"], a_e.dtype)
         ly["ws"] = torch.empty(max(ssi.sige_sparse_conv_layer_split_workspace(ly["g"], a_e.dtype),
                                    plan.workspace_bytes), dtype=torch.uint8, device=dev)
-        ly["auto_path"] = "split" if int(ly["cnt"].item()) <= plan.split_max else "single"
+        ly["auto_path"] = _auto_path(plan, int(ly["cnt"].item()))
         # the bound: per layer, the faster of the two kernels timed on this very edit
         ly["mode"] = "single"
         t1 = graph_time(lambda: _chain_layer(ssi, ly, x, first), 5, 20)
@@ -881,9 +881,18 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
             "sparse_single_range_only_us": round(t_single, 3),
             "note": "one diff + one launch building all 12 lists with the 12 cache copies + 12 layers through "
                     "sige_sparse_conv_layer_auto (the kernel the library picks from the list length; "
-                    "path_per_layer is its choice); best_of_two_bound: the faster of the two kernels per layer, "
-                    "timed on this edit (not available to a caller); per_layer_reduce: a reduce with its copy "
+                    "path_per_layer is its choice: split, single (64 x 32 tiles) or wide (256 x 128 tiles)); "
+                    "best_of_two_bound: the faster of the single-range and split kernels per layer (the two with "
+                    "entry points of their own), timed on this edit (not available to a caller); "
+                    "per_layer_reduce: a reduce with its copy "
                     "before each layer; dense: 12 x F.conv2d; HIP graphs"}
+
+
+def _auto_path(plan, n):
+    """The kernel sige_sparse_conv_layer_auto runs for a list of n blocks."""
+    if n <= plan.split_max:
+        return "split"
+    return "wide" if plan.wide_min <= n <= plan.wide_max else "single"
 
 
 def _chain_layer(ssi, ly, x, first):
@@ -912,9 +921,11 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     """The four GauGAN-shaped bf16 convs (32x64x1024 to 256x512x256) under the seeded star polygon at
     0.5 / 1.2 / 5 / 15 / 30% of the frame: the reduce (mask one bit per pixel,
     the cache copy on its idle workgroups) + sige_sparse_conv_layer_auto (the
-    kernel the library picks; `path`), against the dense conv through
-    torch/MIOpen; best_of_two_bound: the faster of the two kernels timed on the
-    very edit, which a caller cannot do."""
+    kernel the library picks; `path`: split, single (64 x 32 tiles) or wide
+    (256 x 128 tiles)), against the dense conv through torch/MIOpen;
+    best_of_two_bound: the faster of the single-range and split kernels (the
+    two with entry points of their own) timed on the very edit, which a caller
+    cannot do."""
     dev = torch.device("cuda:0")
     wl = synth.workload("gaugan_4conv_bf16")
     res, dense = {}, {}
@@ -960,7 +971,7 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
             t0, t1, t2 = graph_time(auto, 5, 20), graph_time(one, 5, 20), graph_time(split, 5, 20)
             n = int(cnt.item())
             row[L.name] = {"blocks": n, "sparse_us": round(t0, 3),
-                           "path": "split" if n <= plan.split_max else "single", "dense_miopen_us": dense[L.name],
+                           "path": _auto_path(plan, n), "dense_miopen_us": dense[L.name],
                            "speedup": round(dense[L.name] / t0, 2),
                            "best_of_two_bound_us": round(min(t1, t2), 3),
                            "best_of_two_path": "split" if t2 < t1 else "single"}

@@ -242,19 +242,26 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
                                  int copy_cached, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* The fused layer with the kernel chosen by the library: the single-range
- * kernel of sige_sparse_conv_layer or the split of
- * sige_sparse_conv_layer_split, whichever a cost model fixed in the library
- * prices faster for the list length *count.  The mer.dev notes (5 "Conclusion
- * & Discussion") name small blocks at low resolution as the method's weak
- * spot: there the K range is long and the blocks few, and the split is the
- * faster kernel.  The list length is read on the device, so the host derives
- * one threshold per layer, sige_layer_plan.split_max: lists of at most that
- * many blocks go to the split, longer ones to the single-range kernel.  When
- * both can occur, both kernels are enqueued and the one not chosen exits as
- * soon as it has read *count (about three microseconds on MI355X); no host
+ * kernel of sige_sparse_conv_layer (64 x 32 tiles), the split of
+ * sige_sparse_conv_layer_split, or wide tiles of 256 rows x 128 output
+ * channels (16-bit types, k <= 3; no entry point of their own), whichever a
+ * cost model fixed in the library prices fastest for the list length *count.
+ * The mer.dev notes (5 "Conclusion & Discussion") name small blocks at low
+ * resolution as the method's weak spot: there the K range is long and the
+ * blocks few, and the split is the faster kernel; long lists of large edits
+ * (nubint.ai review, "ABSTRACT") go to the wide tiles, which stage each
+ * window once for 128 output channels.  The list length is read on the
+ * device, so the host derives thresholds per layer: lists of at most
+ * sige_layer_plan.split_max blocks go to the split, lists of wide_min ..
+ * wide_max blocks to the wide tiles, the rest to the single-range kernel.
+ * Every kernel whose range can occur is enqueued and the ones not chosen exit
+ * as soon as they have read *count (about three microseconds on MI355X for
+ * the single-range kernel and the split, 1.4 for the wide tiles); no host
  * timing, no synchronisation, nothing allocated.  The first call for a
  * geometry, dtype and device prices every list length up to the capacity
- * (host work proportional to sige_max_blocks); later calls reuse the plan.
+ * (host work proportional to sige_max_blocks); later calls reuse the plan
+ * (SIGE_WIDE_MIN, read when a plan is made, sends lists of at least that many
+ * blocks to the wide tiles where they can run: a tuning knob).
  *   Same arguments, checks and result as sige_sparse_conv_layer (up to the
  *   fp32 summation order of the kernel that runs), plus the split's
  *   workspace: at least sige_layer_plan.workspace_bytes of caller-owned
@@ -263,12 +270,16 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
  *   workspace_bytes is 0 (the split is never chosen).  SIGE_ERANGE when the
  *   workspace is smaller.
  * sige_sparse_conv_layer_plan reports the choice for a geometry: split_max
- * (-1: never the split; >= cap: always), the workspace size, and the cost
+ * (-1: never the split; >= cap: always), wide_min and wide_max (the wide
+ * tiles for lists of that many blocks; 0x7FFFFFFF: never, or no upper bound),
+ * the workspace size, and the cost
  * model's inputs (the single-range kernel's K chunks per tile, K steps per
  * chunk, 1 KiB staging groups per tile and chunk, resident workgroup slots,
  * tiles of 32 output channels; the split's chunks, resident workgroup slots
  * and KiB of staged windows per tile (0 when the split cannot run); the
- * layer's weight megabytes and GFLOP per listed block). */
+ * layer's weight megabytes and GFLOP per listed block; the wide tiles' K
+ * stages of 16 channels, 1 KiB staging loads per stage and tiles of 128
+ * output channels (0 when they cannot run)). */
 typedef struct {
     int32_t split_max;        /* the split takes lists of at most this many blocks (-1: none) */
     int32_t cap;              /* blocks at full capacity (sige_max_blocks) */
@@ -276,6 +287,9 @@ typedef struct {
     int32_t chunks, steps, stage_groups, slots, n_tiles;
     int32_t split_chunks, split_slots;
     double split_stage_kb, weight_mb, gflop_per_block;
+    int32_t wide_min;         /* the wide tiles take lists of wide_min..wide_max blocks (wide_min > cap: none) */
+    int32_t wide_stages, wide_loads, wide_n_tiles;
+    int32_t wide_max;
 } sige_layer_plan;
 int sige_sparse_conv_layer_plan(const sige_geom *g, int dtype, sige_layer_plan *out);
 int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,

@@ -1,28 +1,33 @@
 """Calibration of the layer-kernel choice of sige_sparse_conv_layer_auto.
 
-The library prices its two fused-layer kernels with a small cost model
+The library prices its three fused-layer kernels with a small cost model
 (sige_api.hip, "The kernel choice of sige_sparse_conv_layer_auto") and sends
-each list length to the cheaper one.  This script measures both kernels and
-fits that model's nine constants:
+each list length to the cheapest one.  This script measures the kernels and
+fits that model's eleven constants:
 
-    python -m spatially_sparse_incremental_amd.calibrate_layer_choice measure out.jsonl   # on the GPU
-    python -m spatially_sparse_incremental_amd.calibrate_layer_choice fit out.jsonl       # anywhere
+    python -m spatially_sparse_incremental_amd.calibrate_layer_choice measure out.jsonl        # on the GPU
+    python -m spatially_sparse_incremental_amd.calibrate_layer_choice measure-wide wide.jsonl  # on the GPU
+    python -m spatially_sparse_incremental_amd.calibrate_layer_choice fit out.jsonl wide.jsonl # anywhere
 
 `measure` times the single-range kernel (sige_sparse_conv_layer) and the split
 (sige_sparse_conv_layer_split), without the cache copy, on every layer of the
-U-Net chain, the GauGAN convolutions and the latent-diffusion levels, at five
+U-Net chain, the GauGAN convolutions and the latent-diffusion levels, at seven
 edit areas, on edits of seeds 2 and 3 -- the benchmark reports seed 1, so the
-rule is fixed before the input it is judged on.  Each row carries the plan's
+rule is fixed before the input it is judged on.  `measure-wide` times the
+wide tiles on the same cases (sige_sparse_conv_layer_auto with SIGE_WIDE_MIN=0,
+which sends every list of a layer that can run them there; a process of its
+own, since the plan is made once per geometry).  Each row carries the plan's
 model inputs (sige_sparse_conv_layer_plan).  `fit` takes those inputs from the
 library as built (measure again after a kernel change), minimises the squared
 log error of each kernel's model, prints the constants in the library's order,
-and the time a caller would lose, per case, against the faster of the two.
+and the time a caller would lose, per case, against the fastest kernel.
 """
 import json
 import math
+import os
 import sys
 
-AREAS = (0.005, 0.012, 0.05, 0.15, 0.30)
+AREAS = (0.005, 0.012, 0.05, 0.15, 0.30, 0.5, 0.8)
 SEEDS = (2, 3)
 WORKLOADS = ("unet_chain_12conv_bf16", "gaugan_4conv_bf16", "ldm_64x64x320_f16")
 
@@ -50,7 +55,9 @@ def _graph_us(torch, fn, n_in=10, replays=10):
     return e0.elapsed_time(e1) / (n_in * replays) * 1e3
 
 
-def measure(path):
+def measure(path, wide=False):
+    if wide:
+        os.environ["SIGE_WIDE_MIN"] = "0"
     import torch
 
     import spatially_sparse_incremental_amd as ssi
@@ -75,6 +82,18 @@ def measure(path):
                         wk, bias = ssi.weight_to_krsc(w_cpu).to(dev), b_cpu.to(dev)
                         idx, cnt = ssi.sige_reduce_mask(ssi.sige_diff_mask(a_o, a_e, wl.tau), g, L.dilate)
                         out = torch.empty((1, d.ho, d.wo, L.c_out), dtype=a_e.dtype, device=dev)
+                        if wide:
+                            if plan["wide_stages"] == 0:
+                                continue
+                            wsa = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
+                            tw = _graph_us(torch, lambda: ssi.sige_sparse_conv_layer_auto(
+                                a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False, workspace=wsa))
+                            row = dict(wl=wname, layer=L.name, seed=seed, area=area, b=L.block,
+                                       blocks=int(cnt.item()), wide_us=round(tw, 2), plan=plan)
+                            fo.write(json.dumps(row) + "\n")
+                            fo.flush()
+                            print(json.dumps(row), flush=True)
+                            continue
                         ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8,
                                          device=dev)
                         t1 = _graph_us(torch, lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, None, idx, cnt, g,
@@ -107,7 +126,15 @@ def cost_split(q, p, b, cnt):
             + q[4] * rounds * p["split_stage_kb"])
 
 
-def fit(path):
+def cost_wide(w, p, b, cnt, cus=256):
+    """The library's model of the wide tiles, in microseconds."""
+    mtn = -(-cnt * b * b // 256)
+    ntn = p["wide_n_tiles"]
+    tiles = (-(-mtn // 8) * 8 if ntn > 1 else mtn) * ntn
+    return w[0] + -(-tiles // cus) * p["wide_stages"] * w[1] * p["wide_loads"]
+
+
+def fit(*paths):
     import numpy as np
     from scipy.optimize import least_squares
 
@@ -115,39 +142,59 @@ def fit(path):
     import synth
     from synth.gen import DTYPES
 
-    rows = [json.loads(line) for line in open(path) if line.startswith("{")]
+    merged = {}
+    for path in paths:
+        for line in open(path):
+            if line.startswith("{"):
+                r = json.loads(line)
+                merged.setdefault((r["wl"], r["layer"], r["seed"], r["area"]), {}).update(r)
+    rows = list(merged.values())
     # the model's inputs as the library computes them now (no GPU needed)
     for r in rows:
         L = next(x for x in synth.workload(r["wl"]).layers if x.name == r["layer"])
         g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
         r["plan"] = ssi.sige_sparse_conv_layer_plan(g, DTYPES[L.dtype]).as_dict()
 
+    rs = [r for r in rows if "single_us" in r]
+    rw = [r for r in rows if "wide_us" in r]
+
     def res_single(s):
-        return [math.log(cost_single(s, r["plan"], r["b"], r["blocks"]) / r["single_us"]) for r in rows]
+        return [math.log(cost_single(s, r["plan"], r["b"], r["blocks"]) / r["single_us"]) for r in rs]
 
     def res_split(q):
-        return [math.log(max(cost_split(q, r["plan"], r["b"], r["blocks"]), 1e-3) / r["split_us"]) for r in rows]
+        return [math.log(max(cost_split(q, r["plan"], r["b"], r["blocks"]), 1e-3) / r["split_us"]) for r in rs]
+
+    def res_wide(w):
+        return [math.log(cost_wide(w, r["plan"], r["b"], r["blocks"]) / r["wide_us"]) for r in rw]
 
     s = least_squares(res_single, [4.0, 3.0, 0.05, 0.04], bounds=(0, np.inf)).x
     q = least_squares(res_split, [12.0, 0.3, 3.0, 0.006, 0.01], bounds=(0, np.inf)).x
-    print("rms log error: single %.3f, split %.3f" % (np.sqrt(np.mean(np.square(res_single(s)))),
-                                                      np.sqrt(np.mean(np.square(res_split(q))))))
-    print("constexpr ChoiceModel kChoice = {{%s}, {%s}};" % (", ".join("%.4g" % v for v in s),
-                                                             ", ".join("%.4g" % v for v in q)))
+    w = least_squares(res_wide, [7.0, 0.05], bounds=(0, np.inf)).x if rw else [0.0, 0.0]
+    print("rms log error: single %.3f, split %.3f, wide %.3f" % (
+        np.sqrt(np.mean(np.square(res_single(s)))), np.sqrt(np.mean(np.square(res_split(q)))),
+        np.sqrt(np.mean(np.square(res_wide(w)))) if rw else 0.0))
+    print("constexpr ChoiceModel kChoice = {{%s}, {%s}, {%s}};" % (
+        ", ".join("%.4g" % v for v in s), ", ".join("%.4g" % v for v in q), ", ".join("%.4g" % v for v in w)))
     lost = best = 0.0
-    for r in rows:
+    for r in rs:
         p, b, n = r["plan"], r["b"], r["blocks"]
-        pick = r["split_us"] if cost_split(q, p, b, n) < cost_single(s, p, b, n) else r["single_us"]
-        fast = min(r["single_us"], r["split_us"])
+        cand = {"single": (cost_single(s, p, b, n), r["single_us"]), "split": (cost_split(q, p, b, n), r["split_us"])}
+        if "wide_us" in r:
+            cand["wide"] = (cost_wide(w, p, b, n), r["wide_us"])
+        pick = min(cand.values())[1]
+        fast = min(v[1] for v in cand.values())
         lost += pick - fast
         best += fast
         if pick > 1.1 * fast:
-            print("  %-10s area %.3f seed %d blocks %4d: single %.1f split %.1f us, model picks %.1f" %
-                  (r["layer"], r["area"], r["seed"], n, r["single_us"], r["split_us"], pick))
-    print("time lost against the faster kernel: %.1f of %.1f us (%.1f%%)" % (lost, best, 100 * lost / best))
+            print("  %-10s area %.3f seed %d blocks %4d: %s, model picks %.1f" % (
+                r["layer"], r["area"], r["seed"], n, ", ".join("%s %.1f" % (k, v[1]) for k, v in cand.items()), pick))
+    print("time lost against the fastest kernel: %.1f of %.1f us (%.1f%%)" % (lost, best, 100 * lost / best))
 
 
 if __name__ == "__main__":
-    if len(sys.argv) != 3 or sys.argv[1] not in ("measure", "fit"):
+    if len(sys.argv) < 3 or sys.argv[1] not in ("measure", "measure-wide", "fit"):
         sys.exit(__doc__)
-    (measure if sys.argv[1] == "measure" else fit)(sys.argv[2])
+    if sys.argv[1] == "fit":
+        fit(*sys.argv[2:])
+    else:
+        measure(sys.argv[2], wide=sys.argv[1] == "measure-wide")

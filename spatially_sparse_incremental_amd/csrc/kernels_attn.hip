@@ -382,10 +382,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(AttnArgs a) {
 
 // Combine the key splits of every query and head and write the outputs; the
 // workgroups past the ones with combine work copy the cache elsewhere
-// (copy_cached).  Every split's partial of a thread is requested at once.
+// (copy_cached).  Four neighbouring lanes share one (query, 8 channels): lane
+// r takes the splits r, r + 4, ..., all of its partials requested at once, and
+// the four merge by lane exchanges, so the partials' bytes are spread over 4x
+// the workgroups of one lane per output.
 template <int DT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
-    constexpr int D = kAttnD, SMAX = 16;
+    constexpr int D = kAttnD, SL = 4, SMAX = 16 / SL;  // lanes per output; splits per lane
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ AttnTiles tiles;
     __shared__ int cnt_img[kAttnMaxImages];
@@ -398,12 +401,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
     const int items = ntiles * a.heads;
     int S, ktp;
     attn_split(items, nkt, a.grid1, S, ktp);
-    // work unit: (item, query, 8-channel chunk)
-    const long total = (long)items * kAttnQT * (D / 8);
+    // work unit: (item, query, 8-channel chunk, split lane); the SL lanes of a
+    // unit are consecutive, so every condition below is uniform over them
+    const long total = (long)items * kAttnQT * (D / 8) * SL;
     for (long u = (long)blockIdx.x * kAttnThreads + threadIdx.x; u < total; u += (long)gridDim.x * kAttnThreads) {
-        const int dc = (int)(u % (D / 8));
-        const int qi = (int)((u / (D / 8)) % kAttnQT);
-        const int item = (int)(u / ((long)(D / 8) * kAttnQT));
+        const int r = (int)(u % SL);
+        const long v = u / SL;
+        const int dc = (int)(v % (D / 8));
+        const int qi = (int)((v / (D / 8)) % kAttnQT);
+        const int item = (int)(v / ((long)(D / 8) * kAttnQT));
         const int head = item % a.heads, tile = item / a.heads;
         int n = 0;
         while (n + 1 < g.n && tiles.first_tile[n + 1] <= tile) ++n;
@@ -412,38 +418,48 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
         float2 ml[SMAX];
         f32x4 x0[SMAX], x1[SMAX];
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) {
+        for (int j = 0; j < SMAX; ++j) {
+            const int s = r + SL * j;
             if (s < S) {
                 const float *wp = a.ws + ((size_t)(item * S + s) * kAttnQT + qi) * kAttnWsRow;
-                ml[s] = *(const float2 *)(wp + D);
-                x0[s] = *(const f32x4 *)(wp + dc * 8);
-                x1[s] = *(const f32x4 *)(wp + dc * 8 + 4);
+                ml[j] = *(const float2 *)(wp + D);
+                x0[j] = *(const f32x4 *)(wp + dc * 8);
+                x1[j] = *(const f32x4 *)(wp + dc * 8 + 4);
+            } else {
+                ml[j] = float2{-INFINITY, 0.f};
+                x0[j] = x1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
         const int tok = attn_token_of(g, tiles, n, row, ent);
         if (tok < 0) continue;
         float mx = -INFINITY;
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-            if (s < S) mx = fmaxf(mx, ml[s].x);
+        for (int j = 0; j < SMAX; ++j) mx = fmaxf(mx, ml[j].x);
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
         float sum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) {
-            if (s < S) {
-                const float f = ml[s].x == -INFINITY ? 0.f : exp2f(ml[s].x - mx);
-                sum += f * ml[s].y;
+        for (int j = 0; j < SMAX; ++j) {
+            const float f = ml[j].x == -INFINITY ? 0.f : exp2f(ml[j].x - mx);
+            sum += f * ml[j].y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o[e] += f * x0[s][e];
-                    o[4 + e] += f * x1[s][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                o[e] += f * x0[j][e];
+                o[4 + e] += f * x1[j][e];
             }
         }
-        const float inv = 1.f / sum;
-        u32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pack2<DT>(o[2 * e] * inv, o[2 * e + 1] * inv);
-        st16(a.out + (((size_t)n * L + tok) * C + head * D + dc * 8) * 2, r);
+        for (int sh = 1; sh < SL; sh *= 2) {
+            sum += __shfl_xor(sum, sh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], sh);
+        }
+        if (r != 0) continue;
+        const float inv = 1.f / sum;
+        u32x4 res;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = pack2<DT>(o[2 * e] * inv, o[2 * e + 1] * inv);
+        st16(a.out + (((size_t)n * L + tok) * C + head * D + dc * 8) * 2, res);
     }
     if (a.cc.nvec > 0) {
         const int busy = (int)((total + kAttnThreads - 1) / kAttnThreads);

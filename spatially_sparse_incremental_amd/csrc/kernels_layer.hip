@@ -204,8 +204,9 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             cnt = min(max(cnt_raw, 0), g.cap);
             // A launch paired with the split over input channels: a list below
-            // gate_min blocks is the split's (the whole layer and the copy).
-            ntiles = cnt < c.gate_min ? 0 : layer_tiles<BM>(c, cnt, b2);
+            // gate_min blocks is the split's (the whole layer and the copy); one
+            // of gate_wide..wide_max blocks is the wide tiles'.
+            ntiles = cnt < c.gate_min || (cnt >= c.gate_wide && cnt <= c.wide_max) ? 0 : layer_tiles<BM>(c, cnt, b2);
             mrows = cnt * b2;
             if (t >= ntiles) return false;
         }
@@ -434,7 +435,8 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
             cnt = min(max(cnt_raw, 0), g.cap);
             ntiles = layer_tiles<BM>(c, cnt, b2);
         }
-        if (cnt < c.gate_min) return;  // the split does this list and the copy
+        if (cnt < c.gate_min || (cnt >= c.gate_wide && cnt <= c.wide_max))
+            return;  // the split or the wide tiles do this list and the copy
         long long lo, hi;
         if (a.prev_idx) {
             const int np = clamp_count(a.prev_count, g.cap);
@@ -454,6 +456,262 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                 copy_span<4, NTHR>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, lo, hi);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Wide tiles, for long lists (k_layer_wide).  A workgroup owns 256 output
+// rows x 128 output channels and walks K in stages of 16 input channels (one
+// 32x32x16 MFMA K step per tap), with both operands in LDS: the windows of the
+// tile's block slots and the stage's weights for every tap and the 128
+// columns, double-buffered (one workgroup per CU holds both buffers).  Of the
+// 8 waves, 4 compute and 4 stage: a wave stalls while the CU's memory path
+// accepts its loads (about as long as a stage's MFMAs), so the loading waves
+// stage s + 1 while the computing ones run stage s.  Computing wave w takes
+// rows 64w .. 64w+63 against all 128 columns (2 x 4 fragments of 32 x 32: 128
+// accumulator registers), so each staged weight serves the 4 of them and each
+// staged window element one.  Against the 64 x 32 tiles, a window is staged once for 128
+// output channels instead of once per 32, and the weights once per 256 rows
+// instead of once per 64.
+// LDS of one stage, in 16-byte units: pixel (yy, xx) of slot l's window holds
+// channels 0-7 and 8-15 of the stage at base_l + yy*w_rs + 3*xx (+0, +1), the
+// third unit and each row's tail being padding; with w_rs = 3b mod 16 and
+// base_l = l*w_sb + (3*l*b*b mod 16), output row r of the tile reads 3r mod
+// 16 plus an offset common to all rows at every tap, so the 16 rows that one
+// ds_read_b128 serves together fall on 16 different bank groups (stride 1; 8
+// at stride 2).  Weight (tap t, column n, half h) sits at unit
+// (128t + n)*2 + (h ^ (n/8 mod 2)), likewise conflict-free for 16 columns.
+// Tile t runs on XCD t % 8, the N tiles of one M tile on one XCD.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 8, kWideThreads = 64 * kWideWaves;  // 4 computing + 4 staging waves
+
+template <int DT, bool TAIL>
+__global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
+    constexpr int ES = 2, WR = kLayerWideRows, WC = kLayerWideCols, TP = kLayerWidePitch;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const Geo &g = a.g;
+    const LayerCfg &c = a.c;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= 4;  // a staging wave (else a computing one)
+    const int cw = wave & 3;         // index among the computing or among the staging waves
+    const int b2 = g.b * g.b, k2 = g.k * g.k;
+    const int cnt = clamp_count(a.count, g.cap);
+    if (cnt < c.wide_min || cnt > c.wide_max) return;  // another kernel's list (with the copy)
+    const int mrows = cnt * b2;
+    const int mtn = (mrows + WR - 1) / WR;
+    const int ntiles = (c.w_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * c.w_ntn;
+    const int nst = (g.cin + 15) / 16;
+    const int nld = (g.ib + c.w_rpi - 1) / c.w_rpi;  // staging loads per slot window
+    const int h = lane >> 5;                           // K half: channels 8h .. 8h+7 of the stage
+    const int buf_bytes = c.w_wofs + k2 * WC * 32;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        int tm, tn;
+        if (c.w_ntn > 1) {
+            const int r8 = t >> 3;
+            tn = r8 % c.w_ntn;
+            tm = (r8 / c.w_ntn) * 8 + (t & 7);
+        } else {
+            tm = t;
+            tn = 0;
+        }
+        if (tm >= mtn) continue;  // padding of the tile order
+        const int m0 = tm * WR, n0 = tn * WC;
+        const int s_lo = fdiv(m0, c.m_b2);
+        const int ns = fdiv(min(m0 + WR, mrows) - 1, c.m_b2) - s_lo + 1;  // at most 64 (checked on the host)
+        const int lin = a.idx[s_lo + min(lane, ns - 1)];
+        int sn = -1, siy = 0, six = 0, soy = 0, sox = 0;  // slot `lane`: image, window and block origins
+        {
+            int n, by, bx;
+            if (lane < ns && decode_block(g, lin, n, by, bx)) {
+                sn = n;
+                siy = by * g.b * g.s - g.p;
+                six = bx * g.b * g.s - g.p;
+                soy = by * g.b;
+                sox = bx * g.b;
+            }
+        }
+        int ua[2];  // LDS unit of this lane's row (and K half) in each M fragment, tap 0
+#pragma unroll
+        for (int mf = 0; mf < 2; ++mf) {
+            const int r = m0 + cw * 64 + mf * 32 + (lane & 31);
+            ua[mf] = h;
+            if (r < mrows) {
+                const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
+                const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+                const int l = slot - s_lo;
+                ua[mf] = l * c.w_sb + ((3 * l * b2) & 15) + py * g.s * c.w_rs + px * g.s * 3 + h;
+            }
+        }
+        int ub[4];  // LDS unit of this lane's column (and K half) in each N fragment, tap 0
+        float bcol[4];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+            const int n = nf * 32 + (lane & 31);
+            ub[nf] = n * 2 + (h ^ ((n >> 3) & 1));
+            bcol[nf] = a.bias ? a.bias[min(n0 + n, g.cout - 1)] : 0.f;
+        }
+        f32x16 acc[2][4];
+#pragma unroll
+        for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mf][nf][v] = 0.f;
+
+        // Stage st's windows and weights into buffer `buf`.
+        auto stage = [&](int st, int buf) __attribute__((always_inline)) {
+            const int c0 = st * 16;
+            uint8_t *const wb = smem + buf * buf_bytes;
+            // windows: load (l, j) covers rows j*rpi .. of slot l's window; lane i
+            // takes unit i from the load's first row (the second row's units start
+            // at lane w_rs); lanes on padding are masked off
+#pragma unroll 1
+            for (int it = cw; it < ns * nld; it += 4) {
+                const int l = it / nld, j = it - l * nld;
+                const int n = __builtin_amdgcn_readlane(sn, l);
+                const int iy0 = __builtin_amdgcn_readlane(siy, l), ix0 = __builtin_amdgcn_readlane(six, l);
+                const int second = (c.w_rpi == 2 && lane >= c.w_rs) ? 1 : 0;
+                const int yy = j * c.w_rpi + second, rem = lane - second * c.w_rs;
+                const int xx = (rem * 43) >> 7, hh = rem - 3 * xx;  // rem / 3, rem % 3 (rem < 64)
+                const bool act = hh < 2 && xx < g.ib && yy < g.ib;
+                const int iy = iy0 + yy, ix = ix0 + xx, ch = c0 + 8 * hh;
+                const bool ok = act && n >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w && ch < g.cin;
+                const void *src = ok ? (const void *)(a.src + ((((long)n * g.h + iy) * g.w + ix) * g.cin + ch) * ES)
+                                     : (const void *)&k_zero16;
+                uint8_t *dst = wb + (l * c.w_sb + ((3 * l * b2) & 15) + j * c.w_rpi * c.w_rs) * 16;
+                if (act)
+                    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+            }
+            // weights: 4 k^2 groups of 64 units
+#pragma unroll 1
+            for (int gi = cw; gi < 4 * k2; gi += 4) {
+                const int u = gi * 64 + lane;
+                const int tap = u >> 8, nn = (u >> 1) & 127, hh = (u & 1) ^ ((nn >> 3) & 1);
+                const int col = n0 + nn, ch = c0 + 8 * hh;
+                const void *src = col < g.cout && ch < g.cin
+                                      ? (const void *)(a.w + (((long)col * k2 + tap) * g.cin + ch) * ES)
+                                      : (const void *)&k_zero16;
+                __builtin_amdgcn_global_load_lds(
+                    src, (__attribute__((address_space(3))) void *)(wb + c.w_wofs + gi * 1024), 16, 0, 0);
+            }
+        };
+
+        __syncthreads();  // the previous tile's epilogue is done with the LDS
+        if (loader) {  // stage st + 1 while stage st is computed; one barrier per stage, as below
+            stage(0, 0);
+            for (int st = 0; st < nst; ++st) {
+                __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage st have landed
+                __syncthreads();                // everyone's; and stage st - 1's reads are done
+                if (st + 1 < nst) stage(st + 1, (st + 1) & 1);
+            }
+        } else {
+            for (int st = 0; st < nst; ++st) {
+                __syncthreads();  // stage st is in LDS
+                const uint8_t *const wb = smem + (st & 1) * buf_bytes;
+                const uint8_t *const wl = wb + c.w_wofs;
+                // tap by tap (k <= 3): the next tap's fragments are read while this one's MFMAs run
+                u32x4 av[2][2], bv[2][4];
+                int ky = 0, kx = 0;
+#pragma unroll
+                for (int mf = 0; mf < 2; ++mf) av[0][mf] = *(const u32x4 *)(wb + ua[mf] * 16);
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) bv[0][nf] = *(const u32x4 *)(wl + ub[nf] * 16);
+#pragma unroll
+                for (int tp = 0; tp < 9; ++tp) {
+                    if (tp >= k2) continue;
+                    if (tp + 1 < k2) {
+                        if (++kx == g.k) {
+                            kx = 0;
+                            ++ky;
+                        }
+                        const int toff = ky * c.w_rs + kx * 3;
+#pragma unroll
+                        for (int mf = 0; mf < 2; ++mf)
+                            av[(tp + 1) & 1][mf] = *(const u32x4 *)(wb + (ua[mf] + toff) * 16);
+#pragma unroll
+                        for (int nf = 0; nf < 4; ++nf)
+                            bv[(tp + 1) & 1][nf] = *(const u32x4 *)(wl + (ub[nf] + (tp + 1) * 256) * 16);
+                    }
+#pragma unroll
+                    for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+                        for (int nf = 0; nf < 4; ++nf)
+                            acc[mf][nf] = Mfma32<DT>::run(av[tp & 1][mf], bv[tp & 1][nf], acc[mf][nf]);
+                }
+            }
+        }
+
+        // Epilogue: bias, one rounding, the tile transposed through LDS, 16-byte row stores.
+        __syncthreads();  // every wave is done reading the last stage
+        if (!loader) {
+#pragma unroll
+            for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int row = cw * 64 + mf * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+                        const int col = nf * 32 + (lane & 31);
+                        const float v = acc[mf][nf][i] + bcol[nf];
+                        if constexpr (DT == 1)
+                            *(__bf16 *)(smem + row * TP + col * 2) = (__bf16)v;
+                        else
+                            *(_Float16 *)(smem + row * TP + col * 2) = (_Float16)v;
+                    }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e0 = 0; e0 < WR * (WC / 8); e0 += kWideThreads) {
+            const int e = e0 + tid;
+            const int row = e >> 4, v = e & 15;
+            const int r = m0 + row, co = n0 + v * 8;
+            const int slot = fdiv(min(r, mrows - 1), c.m_b2), pix = min(r, mrows - 1) - slot * b2;
+            const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+            const int l = min(max(slot - s_lo, 0), 63);
+            const int pn = __builtin_amdgcn_ds_bpermute(l << 2, sn);
+            const int y = __builtin_amdgcn_ds_bpermute(l << 2, soy) + py;
+            const int x = __builtin_amdgcn_ds_bpermute(l << 2, sox) + px;
+            const u32x4 val = *(const u32x4 *)(smem + row * TP + v * 16);
+            if (r >= mrows || co >= g.cout || pn < 0 || y >= g.ho || x >= g.wo) continue;
+            __builtin_nontemporal_store(val,
+                                        (u32x4 *)(a.dst + ((((size_t)pn * g.ho + y) * g.wo + x) * g.cout + co) * ES));
+        }
+    }
+
+    if (TAIL) {  // the cache outside the listed blocks (copy_cached)
+        __syncthreads();
+        long long lo, hi;
+        copy_split(a.cc, ntiles, gridDim.x, blockIdx.x, lo, hi);
+        if (lo < hi) {
+            uint32_t *bm = nullptr;
+            if (((g.cap + 31) >> 5) * 4 <= c.w_lds) {
+                bm = (uint32_t *)smem;
+                build_bitmap<kWideThreads>(a.idx, cnt, g.cap, bm);
+            }
+            copy_span<4, kWideThreads>(g, a.cc, bm, a.idx, cnt, a.cache, a.dst, lo, hi);
+        }
+    }
+}
+
+template <int DT, bool TAIL>
+static hipError_t launch_wide_k(const LayerArgs &args, hipStream_t st) {
+    auto k = k_layer_wide<DT, TAIL>;
+    const LayerCfg &c = args.c;
+    long grid = c.cus;  // one workgroup per CU (both LDS buffers)
+    if (!TAIL && c.w_tiles_cap < grid) grid = c.w_tiles_cap;
+    if (grid > 8) grid = grid / 8 * 8;
+    hipLaunchKernelGGL(k, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kWideThreads), c.w_lds, st, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_wide(int dt, const void *src, const void *w, const float *bias, const int32_t *idx,
+                             const int32_t *count, void *dst, const void *cache, const Geo &g, const LayerCfg &cfg,
+                             const CopyCfg &cc, hipStream_t st) {
+    const LayerArgs a{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
+                      (const uint8_t *)cache, nullptr, nullptr, g, cfg, cc};
+    const bool tail = cc.nvec > 0;
+    if (dt == 1) return tail ? launch_wide_k<1, true>(a, st) : launch_wide_k<1, false>(a, st);
+    return tail ? launch_wide_k<2, true>(a, st) : launch_wide_k<2, false>(a, st);
 }
 
 // Workgroups of `kernel` resident on one CU with `lds` bytes of dynamic LDS

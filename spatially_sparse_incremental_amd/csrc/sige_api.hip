@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "sige.h"
 #include "sige_internal.h"
@@ -247,6 +248,51 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
     return SIGE_OK;
 }
 
+// Wide tiles (k_layer_wide in kernels_layer.hip): 256 rows x 128 output
+// channels, K in stages of 16 input channels, two LDS buffers, for 16-bit
+// types and k <= 3.  A slot's staged window (one stage) takes rows of w_rs
+// units (w_rs >= 3*ib, w_rs = 3b mod 16: see the kernel's bank layout); a
+// staging load covers one or two window rows (64 lanes, those on padding
+// masked off), and a slot's LDS holds its window rows plus the bank rotation.
+// No wide tiles when both buffers (or the epilogue's tile) exceed the CU's
+// LDS.  wide_min: the list length from which the wide kernel runs
+// (SIGE_WIDE_MIN overrides it for tuning).
+void wide_layer(const Geo &g, int dt, const DevInfo &dv, sige::LayerCfg *c) {
+    c->wide_min = c->wide_max = c->gate_wide = 0x7FFFFFFF;
+    if (dt == SIGE_F32 || g.k > 3 || 3 * g.ib > 64) return;
+    const int b2 = g.b * g.b, k2 = g.k * g.k;
+    int rs = 3 * g.ib;
+    while (rs % 16 != (3 * g.b) % 16) ++rs;
+    const int rpi = rs + 3 * g.ib <= 64 ? 2 : 1;
+    const int foot = (g.ib - 1) * rs + 3 * g.ib;  // the last window row's last data unit + 1
+    const int adj = (3 * b2) % 16 ? 15 : 0;
+    const int sb = (foot + adj + 15) / 16 * 16;
+    const int WR = sige::kLayerWideRows;
+    long nsw = WR % b2 == 0 ? WR / b2 : (WR - 1) / b2 + 2;
+    if (nsw > g.cap) nsw = g.cap;
+    if (nsw > 64) return;
+    const long win = nsw * sb * 16, buf = win + (long)k2 * sige::kLayerWideCols * 32;
+    const long need_e = (long)WR * sige::kLayerWidePitch;
+    const long need = 2 * buf > need_e ? 2 * buf : need_e;
+    if (need > (long)dv.lds - 1024) return;
+    if (((long)g.cap * b2 + WR) > 0x7FFFFFFFL) return;
+    c->w_rs = rs;
+    c->w_sb = sb;
+    c->w_rpi = rpi;
+    c->w_ntn = (g.cout + sige::kLayerWideCols - 1) / sige::kLayerWideCols;
+    c->w_wofs = (int)win;
+    c->w_lds = (int)need;
+    const long mtn = ((long)g.cap * b2 + WR - 1) / WR;
+    c->w_tiles_cap = (int)((c->w_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * c->w_ntn);
+    long wmin = 0x7FFFFFFF;
+    const char *e = getenv("SIGE_WIDE_MIN");
+    if (e) {
+        const long x = strtol(e, nullptr, 10);
+        if (x >= 0) wmin = x;
+    }
+    c->wide_min = (int)(wmin < 0x7FFFFFFF ? wmin : 0x7FFFFFFF);
+}
+
 // Launch configuration of k_layer (kernels_layer.hip).  A wave holds the
 // weight fragments of at most kLayerFrags/NT K steps of a chunk, so a chunk
 // has at most 4*kLayerFrags/NT steps: kpc <= floor(4*kLayerFrags/(NT*k*k))
@@ -332,6 +378,7 @@ int choose_layer(const Geo &g, int dt, sige::LayerCfg *out) {
     c.m_rs = sige::fast_div_magic(c.rs);
     c.m_b2 = sige::fast_div_magic(b2);
     c.m_b = sige::fast_div_magic(g.b);
+    wide_layer(g, dt, dv, &c);
     *out = c;
     return SIGE_OK;
 }
@@ -500,19 +547,23 @@ int split_common(const void *a_edit, const void *w_krsc, const float *bias, cons
 
 // ---- The kernel choice of sige_sparse_conv_layer_auto ----
 //
-// Two kernels compute the fused layer.  k_layer gives each tile of output rows
-// its whole K range, chunk after chunk, and every row tile reads its own copy
-// of the weights; the split spreads (row group, input-channel chunk, channel
-// tile) work items over all CUs, reads each weight once per row group and adds
-// the chunks in a second launch.  A long K range over few blocks -- the deep,
-// low-resolution layers, where the mer.dev notes (5 "Conclusion &
-// Discussion") find the block-sparse method least effective -- favours the
-// split; many blocks favour k_layer.  The list length is on the device, so
-// the host prices both kernels for every list length with the cost model
-// below and derives one threshold: the split does lists of at most split_max
-// blocks, k_layer the longer ones.  When both sides of the threshold can
-// occur, both kernels are launched and each checks *count on the device
-// (LayerCfg::gate_min, ConvCfg::gate_max): the one not chosen exits at once.
+// Three kernels compute the fused layer.  k_layer gives each 64 x 32 tile of
+// output rows and channels its whole K range, chunk after chunk, and every
+// row tile reads its own copy of the weights; the split spreads (row group,
+// input-channel chunk, channel tile) work items over all CUs, reads each
+// weight once per row group and adds the chunks in a second launch;
+// k_layer_wide runs 256 x 128 tiles, one per CU, staging windows and weights
+// once per tile.  A long K range over few blocks -- the deep, low-resolution
+// layers, where the mer.dev notes (5 "Conclusion & Discussion") find the
+// block-sparse method least effective -- favours the split; many blocks favour
+// k_layer, and long lists of large edits (nubint.ai review, "ABSTRACT": large
+// edits) the wide tiles.  The list length is on the device, so the host
+// prices the kernels for every list length with the cost model below and
+// derives two thresholds: the split does lists of at most split_max blocks,
+// the wide tiles those of at least wide_min, k_layer the ones between.  Every
+// kernel whose range can occur is launched and checks *count on the device
+// (ConvCfg::gate_max, LayerCfg::gate_min and gate_wide, LayerCfg::wide_min):
+// the ones not chosen exit at once.
 //
 // The model, in microseconds for a list of `cnt` blocks (M tiles of 64 rows
 // and N tiles of 32 channels, `tiles` of them):
@@ -524,20 +575,30 @@ int split_common(const void *a_edit, const void *w_krsc, const float *bias, cons
 //            + p4 * ceil(tiles * split_chunks / split_slots) * split_stage_kb
 //     (the weights stream once; the work items' rounds each stage a tile's
 //      windows of split_stage_kb KiB)
-// Constants fitted (least squares on log time) to both kernels timed on MI355X
-// on edits of seeds other than the benchmark's, five edit areas, the U-Net,
-// GauGAN and latent-diffusion layers (calibrate_layer_choice.py in the package).
+//   wide:    w0 + ceil(wide tiles / CUs) * stages * w1 * loads
+//     (a stage of 16 input channels takes as long as the CU's memory path
+//      needs to accept its `loads` 1 KiB staging loads)
+// Constants fitted (least squares on log time) to the kernels timed on MI355X
+// on edits of seeds other than the benchmark's, seven edit areas from 0.5% to
+// 80% of the frame, the U-Net, GauGAN and latent-diffusion layers
+// (calibrate_layer_choice.py in the package).  The k_layer model is the
+// loosest (rms error of log time 0.17, the others 0.07 and 0.17 for the wide
+// tiles), so a list goes from k_layer to the wide tiles only where the model
+// puts them ahead by more than that: kWideMargin.
 struct ChoiceModel {
-    double s[4], p[5];
+    double s[4], p[5], w[2];
 };
-constexpr ChoiceModel kChoice = {{3.572, 2.761, 0.0528, 0.04297}, {10.96, 0.16, 2.381, 0.003331, 0.04085}};
+constexpr ChoiceModel kChoice = {
+    {4.395, 1.916, 0.06717, 0.04092}, {10.76, 0.2046, 2.133, 0.003156, 0.0456}, {10.15, 0.04456}};
 
 struct LayerFeat {
     int cap, b2, ntn;
     int chunks, steps, groups, slots;  // k_layer
     int split_chunks, split_slots;     // the split
     double split_kb;                   // KiB of one tile's staged windows in the split
-    double wmb, gflop_per_block;       // both
+    double wmb, gflop_per_block;       // all
+    int wide_stages, wide_loads;       // the wide tiles: K stages, staging loads per stage (0: no wide tiles)
+    int wide_ntn, cus;
 };
 
 LayerFeat layer_features(const Geo &g, int dt, const sige::LayerCfg &lc) {
@@ -557,6 +618,15 @@ LayerFeat layer_features(const Geo &g, int dt, const sige::LayerCfg &lc) {
     f.slots = dv.cus * (lc.lds_bytes <= dv.lds / 2 - 1024 ? 2 : 1);
     f.wmb = (double)g.cout * g.k * g.k * g.cin * es * 1e-6;
     f.gflop_per_block = 2.0 * b2 * g.cout * g.k * g.k * (double)g.cin * 1e-9;
+    f.cus = dv.cus;
+    if (lc.w_lds > 0) {
+        const int WR = sige::kLayerWideRows;
+        long nsw = WR % b2 == 0 ? WR / b2 : (WR - 1) / b2 + 2;
+        if (nsw > g.cap) nsw = g.cap;
+        f.wide_stages = (g.cin + 15) / 16;
+        f.wide_loads = (int)(nsw * ((g.ib + lc.w_rpi - 1) / lc.w_rpi) + 4 * g.k * g.k);
+        f.wide_ntn = lc.w_ntn;
+    }
     ConvCfg cc;
     if (choose_conv(g, dt, 1, 1, &cc, 1) == SIGE_OK) {
         f.split_chunks = (g.cin + cc.ck - 1) / cc.ck;
@@ -580,32 +650,95 @@ double cost_split(const LayerFeat &f, int cnt) {
            kChoice.p[4] * rounds * f.split_kb;
 }
 
+double cost_wide(const LayerFeat &f, int cnt) {
+    const long mtn = ((long)cnt * f.b2 + sige::kLayerWideRows - 1) / sige::kLayerWideRows;
+    const long tiles = (f.wide_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * f.wide_ntn;
+    const long rounds = (tiles + f.cus - 1) / f.cus;
+    return kChoice.w[0] + (double)rounds * f.wide_stages * kChoice.w[1] * f.wide_loads;
+}
+
 // Microseconds a launch adds when its kernel exits at once (measured on
 // MI355X against the kernel alone): k_layer (a persistent grid, one round
-// trip for *count and the indices), the split (two launches).
-constexpr double kGateOffSingle = 3.0, kGateOffSplit = 3.2;
+// trip for *count and the indices), the split (two launches), the wide tiles
+// (one workgroup per CU).
+constexpr double kGateOffSingle = 3.0, kGateOffSplit = 3.2, kGateOffWide = 1.4;
+constexpr double kWideMargin = 1.2;
 
-// The plan: the split for lists of at most the returned length, k_layer for
-// longer ones (-1: k_layer only; cap: the split only).  T is the largest list
-// length the split is priced faster at; gating at T costs every list the other
-// kernel's empty launch, so the plan is, of k_layer only, the split only and
-// the gate at T, the one whose worst relative loss against the cheaper kernel
-// over list lengths 1..cap is smallest.
-int split_threshold(const LayerFeat &f) {
-    int t = -1;
-    for (int cnt = 1; cnt <= f.cap; ++cnt)
-        if (cost_split(f, cnt) < cost_single(f, cnt)) t = cnt;
-    if (t < 0 || t >= f.cap) return t;
-    double loss_single = 0, loss_split = 0, loss_gate = 0;
+// The plan: the split for lists of at most split_max blocks, the wide tiles
+// for lists of at least wide_min, k_layer for the ones between (split_max -1:
+// no split; wide_min > cap: no wide tiles).  Each nonempty subset of the
+// available kernels, in that order by list length, is priced: a list goes to
+// the cheapest kernel of the subset (the split for lengths up to the last one
+// where it is, the wide tiles from the first one after that where they are,
+// ahead of k_layer by kWideMargin),
+// plus the empty launches of the subset's other kernels.  The plan is the
+// subset whose worst relative loss against the cheapest kernel over list
+// lengths 1..cap is smallest (fewer kernels on a tie).
+void plan_thresholds(const LayerFeat &f, int *split_max, int *wide_min, int *wide_max) {
+    const bool have[3] = {f.split_chunks > 0, true, f.wide_stages > 0};  // split, k_layer, wide
+    const double off[3] = {kGateOffSplit, kGateOffSingle, kGateOffWide};
+    std::vector<double> c[3];
+    for (int k = 0; k < 3; ++k) c[k].assign(f.cap + 1, 1e30);
+    std::vector<double> best(f.cap + 1, 1e30);
     for (int cnt = 1; cnt <= f.cap; ++cnt) {
-        const double a = cost_single(f, cnt), b = cost_split(f, cnt), best = a < b ? a : b;
-        const double gate = cnt <= t ? b + kGateOffSingle : a + kGateOffSplit;
-        loss_single = fmax(loss_single, a / best);
-        loss_split = fmax(loss_split, b / best);
-        loss_gate = fmax(loss_gate, gate / best);
+        if (have[0]) c[0][cnt] = cost_split(f, cnt);
+        c[1][cnt] = cost_single(f, cnt);
+        if (have[2]) c[2][cnt] = cost_wide(f, cnt);
+        for (int k = 0; k < 3; ++k) best[cnt] = fmin(best[cnt], c[k][cnt]);
     }
-    if (loss_gate <= loss_single && loss_gate <= loss_split) return t;
-    return loss_split < loss_single ? f.cap : -1;
+    double best_loss = 1e30;
+    int best_n = 4;
+    *split_max = -1;
+    *wide_min = *wide_max = 0x7FFFFFFF;
+    for (int mask = 1; mask < 8; ++mask) {
+        bool ok = true;
+        int n = 0;
+        for (int k = 0; k < 3; ++k)
+            if (mask >> k & 1) {
+                ok = ok && have[k];
+                ++n;
+            }
+        if (!ok) continue;
+        // thresholds within the subset
+        const bool S = mask & 1, L = mask & 2, W = mask & 4;
+        int t1 = S ? 0 : -1, t2 = f.cap + 1, t3 = f.cap;
+        if (S && !L && !W) t1 = f.cap;
+        if (S && (L || W))
+            for (int cnt = 1; cnt <= f.cap; ++cnt) {
+                const double other = fmin(L ? c[1][cnt] : 1e30, W ? c[2][cnt] : 1e30);
+                if (c[0][cnt] < other) t1 = cnt;
+            }
+        if (W && !L && !S) t2 = 1;
+        if (W && (L || S)) {
+            t2 = f.cap + 1;
+            for (int cnt = t1 + 1; cnt <= f.cap; ++cnt)
+                if (c[2][cnt] * (L ? kWideMargin : 1.0) < (L ? c[1][cnt] : c[0][cnt])) {
+                    if (t2 > f.cap) t2 = cnt;
+                    t3 = cnt;  // with k_layer, the last length where the wide tiles lead
+                }
+            if (!L) t3 = f.cap;
+        }
+        // kernels that actually get a range of lengths
+        const bool runS = S && t1 >= 1, runW = W && t2 <= f.cap, runL = L && (t2 > t1 + 1 || t3 < f.cap);
+        if (S && !runS) continue;  // priced as the smaller subset
+        if (W && !runW) continue;
+        if (L && !runL) continue;
+        double loss = 0;
+        for (int cnt = 1; cnt <= f.cap; ++cnt) {
+            const int k = cnt <= t1 ? 0 : (cnt >= t2 && cnt <= t3 ? 2 : 1);
+            double t = c[k][cnt];
+            for (int j = 0; j < 3; ++j)
+                if (j != k && (mask >> j & 1)) t += off[j];
+            loss = fmax(loss, t / best[cnt]);
+        }
+        if (loss < best_loss - 1e-9 || (loss < best_loss + 1e-9 && n < best_n)) {
+            best_loss = loss;
+            best_n = n;
+            *split_max = runS ? (runL || runW ? t1 : f.cap) : -1;
+            *wide_min = runW ? (runL || runS ? t2 : 0) : 0x7FFFFFFF;
+            *wide_max = runW ? (t3 < f.cap ? t3 : 0x7FFFFFFF) : 0x7FFFFFFF;
+        }
+    }
 }
 
 struct AutoPlan {
@@ -613,6 +746,8 @@ struct AutoPlan {
     ConvCfg cc;
     LayerFeat f;
     int split_max;  // -1: k_layer only; >= cap: the split only; else both, gated on *count
+    int wide_min;   // lists of wide_min..wide_max blocks go to the wide tiles (min > cap: never)
+    int wide_max;
     long ws_bytes;  // workspace for lists of at most split_max blocks
 };
 
@@ -644,8 +779,14 @@ int plan_auto(const Geo &g, int dt, AutoPlan *out) {
     int rc;
     if ((rc = choose_layer(g, dt, &p.lc))) return rc;
     p.f = layer_features(g, dt, p.lc);
-    // the split's limits (LDS, register-resident weights) may exclude it
-    p.split_max = p.f.split_chunks > 0 ? split_threshold(p.f) : -1;
+    // the split's limits (LDS, register-resident weights) may exclude it, and
+    // the wide tiles' (16-bit types, k <= 3, LDS) them
+    plan_thresholds(p.f, &p.split_max, &p.wide_min, &p.wide_max);
+    if (p.lc.wide_min < 0x7FFFFFFF && p.f.wide_stages > 0) {  // SIGE_WIDE_MIN (tuning): from there on, wide tiles
+        p.wide_min = p.lc.wide_min;
+        p.wide_max = 0x7FFFFFFF;
+        if (p.split_max >= p.wide_min) p.split_max = p.wide_min - 1;
+    }
     p.ws_bytes = 0;
     if (p.split_max >= 0) {
         if (choose_conv(g, dt, 1, 1, &p.cc, 1) != SIGE_OK) {
@@ -662,6 +803,12 @@ int plan_auto(const Geo &g, int dt, AutoPlan *out) {
     } else if (p.split_max >= 0) {
         p.cc.gate_max = p.split_max;
         p.lc.gate_min = p.split_max + 1;
+    }
+    if (p.f.wide_stages == 0) p.wide_min = p.wide_max = 0x7FFFFFFF;
+    if (p.wide_min <= g.cap) {
+        p.lc.gate_wide = p.wide_min;
+        p.lc.wide_min = p.wide_min;
+        p.lc.wide_max = p.wide_max;
     }
     std::lock_guard<std::mutex> lk(mu);
     Entry &e = cache[used < 64 ? used++ : (next++ & 63)];
@@ -973,6 +1120,11 @@ int sige_sparse_conv_layer_plan(const sige_geom *gp, int dtype, sige_layer_plan 
     out->split_chunks = p.f.split_chunks;
     out->split_slots = p.f.split_slots;
     out->split_stage_kb = p.f.split_kb;
+    out->wide_min = p.wide_min;
+    out->wide_max = p.wide_max;
+    out->wide_stages = p.f.wide_stages;
+    out->wide_loads = p.f.wide_loads;
+    out->wide_n_tiles = p.f.wide_ntn;
     g_msg[0] = 0;
     return SIGE_OK;
 }
@@ -1013,9 +1165,17 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
     const hipStream_t st = (hipStream_t)stream;
-    if (p.split_max < g.cap) {  // k_layer: every list when the split never wins, else those above split_max
+    // k_layer: every list when the split never wins, else those above split_max
+    // (and below wide_min)
+    if (p.split_max < g.cap && (p.wide_min > p.split_max + 1 || p.wide_max < g.cap)) {
         if ((rc = finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out,
                                             copy_cached ? cached : nullptr, nullptr, nullptr, g, p.lc, cc, st),
+                         "sige_sparse_conv_layer_auto", st)))
+            return rc;
+    }
+    if (p.wide_min <= g.cap) {  // the wide tiles: lists of at least wide_min blocks
+        if ((rc = finish(sige::launch_layer_wide(dtype, a_edit, w_krsc, bias, idx, count, out,
+                                                 copy_cached ? cached : nullptr, g, p.lc, cc, st),
                          "sige_sparse_conv_layer_auto", st)))
             return rc;
     }

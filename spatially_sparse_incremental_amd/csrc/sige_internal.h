@@ -61,7 +61,19 @@ struct LayerCfg {
     int spec;            // workgroups below this fetch their first weights before the list length (set at launch)
     int gate_min;        // runs only for lists of at least this many blocks (else every workgroup exits at once)
     uint32_t m_ps, m_rs, m_b2, m_b;  // fast_div_magic of ps, rs, b*b, b
+    // Wide tiles (kLayerWideRows x kLayerWideCols, 16-channel stages) for long lists
+    int wide_min, wide_max;  // the wide kernel runs for lists of wide_min..wide_max blocks (min 0x7FFFFFFF: never)
+    int w_rs, w_sb;      // LDS units (16 B) per staged window row and per block slot
+    int w_rpi;           // window rows per staging load (1 or 2)
+    int w_ntn;           // N tiles of kLayerWideCols channels
+    int w_wofs;          // LDS byte offset of the staged weights within one of the two buffers
+    int w_lds;           // dynamic LDS of the wide kernel (two buffers, or the epilogue's tile)
+    int w_tiles_cap;     // wide tiles (padding included) at full capacity
+    int gate_wide;       // k_layer: lists of gate_wide..wide_max blocks are the wide kernel's (it exits)
 };
+constexpr int kLayerWideRows = 256;  // output rows (block pixels) of a wide tile
+constexpr int kLayerWideCols = 128;  // output channels of a wide tile
+constexpr int kLayerWidePitch = kLayerWideCols * 2 + 16;  // LDS bytes per row of the rounded wide tile
 
 // Copy of the cache outside the listed blocks, in 16-byte vectors of the
 // output flattened over (n, y, x, vector of the channel row).
@@ -118,6 +130,11 @@ hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const
                         const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                         const int32_t *prev_count, const Geo &g, const LayerCfg &cfg, const CopyCfg &cc,
                         hipStream_t st);
+// The wide tiles of the fused layer (16-bit types), run for lists of at least
+// cfg.wide_min blocks (the launch exits at once for shorter ones).
+hipError_t launch_layer_wide(int dt, const void *src, const void *w, const float *bias, const int32_t *idx,
+                             const int32_t *count, void *dst, const void *cache, const Geo &g, const LayerCfg &cfg,
+                             const CopyCfg &cc, hipStream_t st);
 // Bytes of that workspace for g and the launch configuration c (< 0: unknown tile shape).
 long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c);
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,

@@ -397,6 +397,28 @@ def test_layer_plan_without_a_gpu(lib):
     assert lib.sige_sparse_conv_layer_plan(ctypes.byref(_g()), 1, None) == EINVAL
 
 
+def test_layer_plan_wide_tiles_without_a_gpu():
+    """The wide tiles' range in the plan: after the split's, within the capacity,
+    for 16-bit types with k <= 3 only (not fp32, not 5x5, not where two staging
+    buffers exceed the LDS: stride 2, 2x2 blocks); 16-channel stages and their
+    1 KiB staging loads as the kernel issues them (windows of the <= 9 slots a
+    256-row tile of 6x6 blocks touches, two 8x8 window rows per load, plus 4
+    loads per tap for 128 columns of weights)."""
+    p = ssi.sige_sparse_conv_layer_plan(_g(1, 256, 256, 128, 128, 3, 1, 1, 6), torch.bfloat16)
+    assert p.wide_stages == 8 and p.wide_loads == 9 * 4 + 4 * 9 and p.wide_n_tiles == 1
+    assert p.split_max < p.wide_min <= p.wide_max <= p.cap
+    # the wide range ends at the longest list of one round (256 tiles of 256 rows on 256 CUs)
+    assert p.wide_max == 256 * 256 // 36
+    p = ssi.sige_sparse_conv_layer_plan(_g(1, 256, 512, 256, 128, 3, 1, 1, 6), torch.bfloat16)
+    assert p.wide_stages == 16 and p.split_max < p.wide_min <= p.cap
+    for g, dt in ((_g(1, 256, 256, 128, 128, 3, 1, 1, 6), torch.float32),
+                  (_g(1, 64, 64, 64, 64, 5, 1, 2, 6), torch.bfloat16),
+                  (_g(1, 64, 64, 64, 128, 3, 2, 1, 4), torch.float16),
+                  (_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2), torch.float16)):
+        p = ssi.sige_sparse_conv_layer_plan(g, dt)
+        assert p.wide_stages == 0 and p.wide_min == p.wide_max == 0x7FFFFFFF, (g.k, g.s, g.b)
+
+
 def test_auto_layer_validation(lib):
     """Checks before any device work: a workspace smaller than the plan's is
     SIGE_ERANGE, overlaps and NULL pointers SIGE_EINVAL."""

@@ -9,7 +9,7 @@ import oracle
 import spatially_sparse_incremental_amd as ssi
 import synth
 from synth.gen import DTYPES
-from _parity import check_layer_sampled, run_layer_full
+from _parity import active_pixels, assert_close, check_layer_sampled, run_layer_full
 
 pytestmark = pytest.mark.gpu
 
@@ -21,21 +21,33 @@ def _need_gpu():
 
 
 def _check_choice(name, a_e_gpu, wt, bias, cache_gpu, L, mask_gpu, out):
-    """`out` (auto) equals, bit for bit, the kernel the plan picks for this list."""
+    """`out` (auto) equals, bit for bit, the kernel the plan picks for this list;
+    the wide tiles (no entry point of their own) equal the single-range kernel
+    within the dtype's tolerance, and bit for bit outside the listed blocks."""
     g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
     plan = ssi.sige_sparse_conv_layer_plan(g, DTYPES[L.dtype])
     assert -1 <= plan.split_max <= plan.cap == ssi.sige_max_blocks(g)
+    assert plan.split_max < plan.wide_min <= plan.wide_max
     idx, count = ssi.sige_reduce_mask(mask_gpu, g, L.dilate)
     n = int(count.item())
     wk = ssi.weight_to_krsc(wt).cuda()
-    if n <= plan.split_max:
+    path = "split" if n <= plan.split_max else ("wide" if plan.wide_min <= n <= plan.wide_max else "single")
+    if path == "split":
         ref = ssi.sige_sparse_conv_layer_split(a_e_gpu, wk, bias.cuda(), cache_gpu, idx, count, g)
     else:
         ref = ssi.sige_sparse_conv_layer(a_e_gpu, wk, bias.cuda(), cache_gpu, idx, count, g)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), \
-        f"{name}: auto differs from the {'split' if n <= plan.split_max else 'single-range'} kernel"
-    return "split" if n <= plan.split_max else "single"
+    if path != "wide":
+        assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), f"{name}: auto differs from the {path} kernel"
+    else:
+        d = ssi.sige_geom_derive(g)
+        act = torch.zeros(d.nby * d.nbx, dtype=torch.uint8)
+        act[idx[:n].long().cpu()] = 1
+        sel = active_pixels(act.view(1, d.nby, d.nbx), L.block, d.ho, d.wo).expand_as(out.cpu())
+        o, r = out.cpu(), ref.cpu()
+        assert torch.equal(o[~sel].view(torch.uint8), r[~sel].view(torch.uint8)), f"{name}: untouched pixels"
+        assert_close(o, r.double(), o.dtype, sel, f"{name}: wide tiles against the single-range kernel")
+    return path
 
 
 @pytest.mark.parametrize("area", [0.005, 0.012, 0.15])

@@ -1,0 +1,160 @@
+"""The wide tiles of the fused layer (k_layer_wide, run by
+sige_sparse_conv_layer_auto for long lists) against the oracle.
+
+SIGE_WIDE_MIN=0 makes the plan send every list of these geometries to the wide
+tiles (the plan is made once per geometry, so the geometries here are used by
+no other test).  Edge cases: a partial last 16-channel stage (c_in = 24),
+output channels past one or two 128-channel tiles (c_out = 136, 64), two
+images, 1x1 and 3x3 kernels, blocks of 4, 5, 6 and 8 (one or two window rows
+per staging load), windows over the image border, several 256-row tiles, the
+empty list, one block, every block, with and without the cache copy."""
+import os
+
+import pytest
+import torch
+
+import oracle
+import spatially_sparse_incremental_amd as ssi
+from _parity import DT, active_pixels, assert_close, layer_inputs, rand, random_mask
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# (name, n, h, w, cin, cout, k, s, p, b, dtype)
+CASES = [
+    ("cin24_cout136_b6_bf16", 1, 40, 44, 24, 136, 3, 1, 1, 6, "bf16"),
+    ("two_images_b4_f16", 2, 30, 30, 32, 64, 3, 1, 1, 4, "f16"),
+    ("pointwise_b5_bf16", 1, 33, 35, 48, 128, 1, 1, 0, 5, "bf16"),
+    ("b8_one_row_per_load_f16", 1, 48, 52, 40, 96, 3, 1, 1, 8, "f16"),
+]
+
+
+def _forced_plan(g, dt, monkeypatch):
+    monkeypatch.setenv("SIGE_WIDE_MIN", "0")
+    plan = ssi.sige_sparse_conv_layer_plan(g, dt)
+    assert plan.wide_stages > 0 and plan.wide_min <= plan.split_max + 1, plan.as_dict()
+    return plan
+
+
+def _lists(cap, seed):
+    gen = torch.Generator().manual_seed(seed)
+    sizes = sorted({0, 1, max(1, cap // 7), max(1, cap // 2), cap})
+    for n in sizes:
+        yield torch.randperm(cap, generator=gen)[:n].sort().values.to(torch.int32)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_wide_tiles_against_the_oracle(case, monkeypatch):
+    name, n, h, w, cin, cout, k, s, p, b, dts = case
+    dt = DT[dts]
+    g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
+    plan = _forced_plan(g, dt, monkeypatch)
+    ho, wo, nby, nbx, _ = oracle.geometry(h, w, k, s, p, b)
+    cap = n * nby * nbx
+    mask = random_mask(n, h, w, 0.5, 3)
+    _, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 5, mask)
+    cache = rand((n, ho, wo, cout), dt, 7)
+    wk, bg, ag, cg = ssi.weight_to_krsc(wt).cuda(), bias.cuda(), a_e.cuda(), cache.cuda()
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    for lst in _lists(cap, 11):
+        cnt = lst.numel()
+        idx = torch.zeros(cap, dtype=torch.int32)
+        idx[:cnt] = lst
+        idx_g, count = idx.cuda(), torch.tensor([cnt], dtype=torch.int32, device="cuda")
+        act = torch.zeros(cap, dtype=torch.uint8)
+        act[lst.long()] = 1
+        act = act.view(n, nby, nbx)
+        print(f"[case] {name}: {cnt} of {cap} blocks", flush=True)
+        ref = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, act, cache, out_f64=True)
+        sel = active_pixels(act, b, ho, wo)
+        keep = ~sel.expand_as(cache)
+        out = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg, idx_g, count, g, workspace=ws).cpu()
+        assert torch.equal(out[keep].view(torch.uint8), cache[keep].view(torch.uint8)), f"{name}: copy"
+        assert_close(out, ref, dt, sel, f"{name} {cnt} blocks")
+        pers = cg.clone()
+        ssi.sige_sparse_conv_layer_auto(ag, wk, bg, None, idx_g, count, g, out=pers, copy_cached=False,
+                                        workspace=ws)
+        assert torch.equal(pers.cpu().view(torch.uint8), out.view(torch.uint8)), f"{name}: persistent buffer"
+
+
+def test_wide_tiles_in_a_graph_replay(monkeypatch):
+    """Replays of a captured wide-tile layer equal the eager result (each replay's
+    output cleared in between)."""
+    n, h, w, cin, cout, k, s, p, b = 1, 36, 60, 32, 128, 3, 1, 1, 6
+    dt = torch.bfloat16
+    g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
+    plan = _forced_plan(g, dt, monkeypatch)
+    mask = random_mask(n, h, w, 0.3, 41)
+    a_o, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 43, mask)
+    cache = rand((n, h, w, cout), dt, 45).cuda()
+    ag, ao, wk, bg = a_e.cuda(), a_o.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    mk = ssi.sige_diff_mask(ao, ag, 1e-6)
+    idx, count = ssi.sige_reduce_mask(mk, g, 1)
+    out = torch.empty_like(cache)
+
+    def step():
+        ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cache, idx, count, g, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert int(count.item()) > 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), eager.view(torch.uint8))
+
+
+def test_wide_tiles_at_full_size():
+    """The 256x256x128 bf16 layer with 1500 of its 1849 blocks listed: the
+    library's own plan sends the list to the wide tiles; equal to the 64 x 32
+    tiles within tolerance (untouched pixels bit for bit), and to the oracle on
+    sampled blocks."""
+    assert "SIGE_WIDE_MIN" not in os.environ
+    n, h, w, cin, cout, k, s, p, b = 1, 256, 256, 128, 128, 3, 1, 1, 6
+    dt = torch.bfloat16
+    g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
+    plan = ssi.sige_sparse_conv_layer_plan(g, dt)
+    cap, cnt = plan.cap, 1500
+    assert plan.wide_min <= cnt <= plan.wide_max, plan.as_dict()
+    mask = random_mask(n, h, w, 1.0, 51)
+    _, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 53, mask)
+    cache = rand((n, h, w, cout), dt, 55)
+    ag, wk, bg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    gen = torch.Generator().manual_seed(57)
+    lst = torch.randperm(cap, generator=gen)[:cnt].sort().values.to(torch.int32)
+    idx = torch.zeros(cap, dtype=torch.int32)
+    idx[:cnt] = lst
+    idx, count = idx.cuda(), torch.tensor([cnt], dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    out = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cache.cuda(), idx, count, g, workspace=ws).cpu()
+    ref = ssi.sige_sparse_conv_layer(ag, wk, bg, cache.cuda(), idx, count, g).cpu()
+    ho, wo, nby, nbx, _ = oracle.geometry(h, w, k, s, p, b)
+    act = torch.zeros(cap, dtype=torch.uint8)
+    act[lst.long()] = 1
+    sel = active_pixels(act.view(1, nby, nbx), b, ho, wo).expand_as(out)
+    assert torch.equal(out[~sel].view(torch.uint8), ref[~sel].view(torch.uint8)), "untouched pixels"
+    assert_close(out, ref.double(), dt, sel, "wide vs 64x32 tiles, 1500 blocks")
+    sub = torch.zeros(cap, dtype=torch.uint8)
+    sub[lst[torch.randperm(cnt, generator=gen)[:6]].long()] = 1
+    sub = sub.view(1, nby, nbx)
+    r64 = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, sub, out, out_f64=True)
+    assert_close(out, r64, dt, active_pixels(sub, b, ho, wo), "wide tiles, sampled blocks against the oracle")
