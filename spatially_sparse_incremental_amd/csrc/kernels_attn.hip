@@ -28,6 +28,8 @@
 // Query tiles never straddle two images: each image's listed blocks are
 // padded to whole 128-row tiles (per-image block counts come from one pass
 // over the list in every workgroup).
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace sige {
@@ -207,44 +209,48 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(AttnArgs a) {
         const int row0 = (tile - tiles.first_tile[n]) * kAttnQT + wave * kAttnQW + ql;  // group q: row0 + 16 q
         const int kt0 = split * ktp, kt1 = min(nkt, kt0 + ktp);
         __syncthreads();  // every wave is done with the staged tiles of the previous item
-        // One round trip per chunk: the list entries of this lane's queries
-        // first, then every K and V load of the chunk (keys past the end are
-        // clamped and their values never used).
+        // The list entries of this lane's queries first, then the first two key
+        // tiles (K and V rows into registers), then the Q fragments; each tile is
+        // written to LDS once its registers arrive, and the tile two ahead is
+        // requested into them while this one is computed (keys past the end are
+        // clamped and their values never used).  Plain loads, not LDS DMA: the
+        // compiler's waits for registers are exact, while any LDS access after
+        // a DMA load waits for all of them.
         int ent[G];
 #pragma unroll
         for (int q = 0; q < G; ++q) ent[q] = a.idx[attn_slot(g, tiles, n, row0 + 16 * q)];
         __builtin_amdgcn_sched_barrier(0);
-        u32x4 vv[kAttnChunk][2];
-        auto issue = [&](int c0, int nt) {
-            // K: up to kAttnChunk tiles x 64 keys x 9 slots (8 of 16 bytes, then
-            // a pad slot that takes a duplicate) = 9 wave loads per wave and 4 tiles
+        u32x4 kv[2][2], vv[2][2];  // the two tiles in flight: 16 bytes of a K and a V row, twice per thread
+        auto issue_tile = [&](int c0, int t) __attribute__((always_inline)) {
+            // thread cx takes key cx % 64, channels 8 (cx / 64) .. of it, cx = tid, tid + 256
 #pragma unroll
-            for (int i = 0; i < kAttnChunk * KT * 9 / 64 / 4; ++i) {
-                const int qg = wave + 4 * i;
-                const int s = qg * 64 + lane;
-                const int t = s / (KT * 9), r = s - t * (KT * 9), key = r / 9, c = (r - key * 9) & 7;
-                if (qg * 64 < nt * KT * 9) {  // wave-uniform
-                    const int j = min(min(c0 + t, nkt - 1) * KT + key, L - 1);
-                    __builtin_amdgcn_global_load_lds(
-                        (const void *)(a.k + ((img + j) * C + head * D + c * 8) * 2),
-                        (__attribute__((address_space(3))) void *)((uint8_t *)Ks + qg * 1024), 16, 0, 0);
+            for (int i = 0; i < 2; ++i) {
+                const int cx = tid + i * kAttnThreads, key = cx & 63, dc = cx >> 6;
+                const size_t off = ((img + min((c0 + t) * KT + key, L - 1)) * C + head * D + dc * 8) * 2;
+                kv[t & 1][i] = ld16(a.k + off);
+                vv[t & 1][i] = ld16(a.v + off);
+            }
+        };
+        // tile t's registers into LDS slot t: K rows as they are, V transposed
+        // (a wave takes one 8-channel slice of 64 keys: its 16-bit writes go to 64
+        // consecutive halves of each row of V^T)
+        auto stage_tile = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int cx = tid + i * kAttnThreads, key = cx & 63, dc = cx >> 6;
+                *(u32x4 *)(Ks + t * kAttnKTile + key * kAttnKPitch + dc * 8) = kv[t & 1][i];
+                uint16_t *vt = Vt + t * kAttnVTile + key;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vt[(dc * 8 + 2 * e) * kAttnVPitch] = (uint16_t)(vv[t & 1][i][e] & 0xFFFFu);
+                    vt[(dc * 8 + 2 * e + 1) * kAttnVPitch] = (uint16_t)(vv[t & 1][i][e] >> 16);
                 }
             }
-            // V: 16 bytes of one key row per thread, two per tile (into registers);
-            // a wave takes one 8-channel slice of 64 keys, so that the transposed
-            // writes below go to 64 consecutive halves
-#pragma unroll
-            for (int t = 0; t < kAttnChunk; ++t)
-                if (t < nt) {
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const int cx = tid + i * kAttnThreads, key = cx & 63, dc = cx >> 6;
-                        const int j = min((c0 + t) * KT + key, L - 1);
-                        vv[t][i] = ld16(a.v + ((img + j) * C + head * D + dc * 8) * 2);
-                    }
-                }
         };
-        issue(kt0, min(kAttnChunk, kt1 - kt0));
+        // the first chunk's first two tiles (unconditionally: keys past the end
+        // are clamped), then the Q fragments
+        issue_tile(kt0, 0);
+        issue_tile(kt0, 1);
         __builtin_amdgcn_sched_barrier(0);
         // this wave's Q^T fragments: query ql of group q, d = 32 * ks + 8 * kg + (0..7)
         u32x4 qf[G][2];
@@ -264,109 +270,112 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(AttnArgs a) {
             m_run[q] = -INFINITY;
             l_run[q] = 0.f;
         }
-        for (int c0 = kt0; c0 < kt1; c0 += kAttnChunk) {
-            const int nt = min(kAttnChunk, kt1 - c0);
-            if (c0 > kt0) {
-                __syncthreads();  // every wave is done with the previous chunk
-                issue(c0, nt);
-            }
-            __builtin_amdgcn_s_waitcnt(0);  // the chunk (LDS and registers) has landed
-            // V tiles, transposed: 8 values of one key row per thread and load
+        // tile t of the chunk at key tile c0, from LDS slot t
+        auto compute_tile = [&](int c0, int t) __attribute__((always_inline)) {
+            const int j0 = (c0 + t) * KT;
+            const uint16_t *kb = Ks + t * kAttnKTile, *vb = Vt + t * kAttnVTile;
+            // every fragment of the tile requested at once: K rows for S^T,
+            // rows of V^T for O^T (keys 32*pr + 4*kg + (0..3) and 32*pr + 16 + 4*kg + (0..3));
+            // both query groups share them
+            u32x4 kf[4][2], vf[2][4];
 #pragma unroll
-            for (int t = 0; t < kAttnChunk; ++t)
-                if (t < nt) {
+            for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const int cx = tid + i * kAttnThreads, key = cx & 63, dc = cx >> 6;
-                        uint16_t *vt = Vt + t * kAttnVTile + key;
+                for (int ks = 0; ks < 2; ++ks)
+                    kf[sub][ks] = *(const u32x4 *)(kb + (sub * 16 + ql) * kAttnKPitch + ks * 32 + kg * 8);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            vt[(dc * 8 + 2 * e) * kAttnVPitch] = (uint16_t)(vv[t][i][e] & 0xFFFFu);
-                            vt[(dc * 8 + 2 * e + 1) * kAttnVPitch] = (uint16_t)(vv[t][i][e] >> 16);
-                        }
-                    }
+            for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint16_t *vr = vb + (m * 16 + ql) * kAttnVPitch + pr * 32 + kg * 4;
+                    const uint2 lo = *(const uint2 *)vr, hi = *(const uint2 *)(vr + 16);
+                    vf[pr][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
                 }
-            __syncthreads();
-            for (int t = 0; t < nt; ++t) {
-                const int j0 = (c0 + t) * KT;
-                const uint16_t *kb = Ks + t * kAttnKTile, *vb = Vt + t * kAttnVTile;
-                // every fragment of the tile requested at once: K rows for S^T,
-                // rows of V^T for O^T (keys 32*pr + 4*kg + (0..3) and 32*pr + 16 + 4*kg + (0..3));
-                // both query groups share them
-                u32x4 kf[4][2], vf[2][4];
+            // S^T = K Q^T for the 4 subtiles of 16 keys
+            f32x4 sT[G][4];
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub) {
+                    sT[q][sub] = AttnMfma<DT>::run(kf[sub][0], qf[q][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                    sT[q][sub] = AttnMfma<DT>::run(kf[sub][1], qf[q][1], sT[q][sub]);
+                }
+            // online softmax for query ql of each group: keys 16 * sub + 4 * kg + i
+            // of this tile.  Scores stay unscaled (the scale is positive, so the
+            // max commutes with it); only a tile past the last key masks.
+            if (j0 + KT > L) {
+#pragma unroll
+                for (int q = 0; q < G; ++q)
+#pragma unroll
+                    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (j0 + sub * 16 + kg * 4 + i >= L) sT[q][sub][i] = -INFINITY;
+            }
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                float mt = -INFINITY;
 #pragma unroll
                 for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        kf[sub][ks] = *(const u32x4 *)(kb + (sub * 16 + ql) * kAttnKPitch + ks * 32 + kg * 8);
+                    for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sT[q][sub][i]);
+                const float m_new = fmaxf(m_run[q], a.scale_log2 * qmax(mt));
+                if (__ballot(m_new != m_run[q])) {  // some query's max moved: rescale the wave's sums
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
+                    l_run[q] *= alpha;
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const uint16_t *vr = vb + (m * 16 + ql) * kAttnVPitch + pr * 32 + kg * 4;
-                        const uint2 lo = *(const uint2 *)vr, hi = *(const uint2 *)(vr + 16);
-                        vf[pr][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                    }
-                // S^T = K Q^T for the 4 subtiles of 16 keys
-                f32x4 sT[G][4];
-#pragma unroll
-                for (int q = 0; q < G; ++q)
-#pragma unroll
-                    for (int sub = 0; sub < 4; ++sub) {
-                        sT[q][sub] = AttnMfma<DT>::run(kf[sub][0], qf[q][0], f32x4{0.f, 0.f, 0.f, 0.f});
-                        sT[q][sub] = AttnMfma<DT>::run(kf[sub][1], qf[q][1], sT[q][sub]);
-                    }
-                // online softmax for query ql of each group: keys 16 * sub + 4 * kg + i
-                // of this tile.  Scores stay unscaled (the scale is positive, so the
-                // max commutes with it); only a tile past the last key masks.
-                if (j0 + KT > L) {
-#pragma unroll
-                    for (int q = 0; q < G; ++q)
-#pragma unroll
-                        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (j0 + sub * 16 + kg * 4 + i >= L) sT[q][sub][i] = -INFINITY;
+                    for (int m = 0; m < 4; ++m) oT[q][m] *= alpha;
+                    m_run[q] = m_new;
                 }
+                float ps = 0.f;
 #pragma unroll
-                for (int q = 0; q < G; ++q) {
-                    float mt = -INFINITY;
+                for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sT[q][sub][i]);
-                    const float m_new = fmaxf(m_run[q], a.scale_log2 * qmax(mt));
-                    if (__ballot(m_new != m_run[q])) {  // some query's max moved: rescale the wave's sums
-                        const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
-                        l_run[q] *= alpha;
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) oT[q][m] *= alpha;
-                        m_run[q] = m_new;
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = __builtin_amdgcn_exp2f(fmaf(sT[q][sub][i], a.scale_log2, -m_new));
+                        sT[q][sub][i] = e;
+                        ps += e;
                     }
-                    float ps = 0.f;
-#pragma unroll
-                    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float e = __builtin_amdgcn_exp2f(fmaf(sT[q][sub][i], a.scale_log2, -m_new));
-                            sT[q][sub][i] = e;
-                            ps += e;
-                        }
-                    l_run[q] += qsum(ps);
-                }
-                // O^T += V^T P^T, 32 keys per MFMA; P^T straight from S^T's accumulators
-#pragma unroll
-                for (int q = 0; q < G; ++q)
-#pragma unroll
-                    for (int pr = 0; pr < 2; ++pr) {
-                        const u32x4 pb = u32x4{pack2<DT>(sT[q][2 * pr][0], sT[q][2 * pr][1]),
-                                               pack2<DT>(sT[q][2 * pr][2], sT[q][2 * pr][3]),
-                                               pack2<DT>(sT[q][2 * pr + 1][0], sT[q][2 * pr + 1][1]),
-                                               pack2<DT>(sT[q][2 * pr + 1][2], sT[q][2 * pr + 1][3])};
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) oT[q][m] = AttnMfma<DT>::run(vf[pr][m], pb, oT[q][m]);
-                    }
+                l_run[q] += qsum(ps);
             }
+            // O^T += V^T P^T, 32 keys per MFMA; P^T straight from S^T's accumulators
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const u32x4 pb = u32x4{pack2<DT>(sT[q][2 * pr][0], sT[q][2 * pr][1]),
+                                           pack2<DT>(sT[q][2 * pr][2], sT[q][2 * pr][3]),
+                                           pack2<DT>(sT[q][2 * pr + 1][0], sT[q][2 * pr + 1][1]),
+                                           pack2<DT>(sT[q][2 * pr + 1][2], sT[q][2 * pr + 1][3])};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) oT[q][m] = AttnMfma<DT>::run(vf[pr][m], pb, oT[q][m]);
+                }
+        };
+        // A chunk of nt key tiles whose first two are requested: each tile is
+        // written to LDS, then the tile two ahead is requested into its registers
+        // (the next chunk's first two from the third and fourth on) while it is
+        // computed.  Full chunks are straight-line code, so the compiler's waits
+        // for the registers are exact.
+        auto run_chunk = [&](int c0, int nt, auto full_tag) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+            for (int t = 0; t < kAttnChunk; ++t) {
+                if (!FULL && t >= nt) continue;
+                stage_tile(t);
+                __syncthreads();  // tile t is in LDS for every wave
+                if (FULL ? t + 2 < kAttnChunk : t + 2 < nt)
+                    issue_tile(c0, t + 2);
+                else if (c0 + kAttnChunk < kt1 && t + 2 - kAttnChunk >= 0 && (FULL || nt == kAttnChunk))
+                    issue_tile(c0 + kAttnChunk, t + 2 - kAttnChunk);
+                compute_tile(c0, t);
+            }
+        };
+        for (int c0 = kt0; c0 < kt1; c0 += kAttnChunk) {
+            const int nt = min(kAttnChunk, kt1 - c0);
+            if (nt == kAttnChunk)
+                run_chunk(c0, nt, std::true_type{});
+            else
+                run_chunk(c0, nt, std::false_type{});
         }
         // this item's partial: unnormalised O^T column of each query, then max and sum
 #pragma unroll
