@@ -158,3 +158,39 @@ def test_wide_tiles_at_full_size():
     sub = sub.view(1, nby, nbx)
     r64 = oracle.sparse_layer(a_e, wt, bias, k, s, p, b, sub, out, out_f64=True)
     assert_close(out, r64, dt, active_pixels(sub, b, ho, wo), "wide tiles, sampled blocks against the oracle")
+
+
+def test_wide_tiles_write_nothing_outside_out(monkeypatch):
+    """Guard canaries before and after `out`: the wide tiles (every list of this
+    geometry forced to them) write only inside the output, with and without the
+    cache copy, and leave the unlisted blocks alone without it."""
+    n, h, w, cin, cout, k, s, p, b = 1, 26, 34, 40, 72, 3, 1, 1, 6
+    dt = torch.bfloat16
+    g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
+    plan = _forced_plan(g, dt, monkeypatch)
+    ho, wo, nby, nbx, _ = oracle.geometry(h, w, k, s, p, b)
+    cap = n * nby * nbx
+    mask = random_mask(n, h, w, 0.5, 61)
+    _, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 63, mask)
+    cache = rand((n, ho, wo, cout), dt, 65).cuda()
+    ag, wk, bg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    G, nout = 4096, n * ho * wo * cout
+    gen = torch.Generator().manual_seed(67)
+    for cnt, copy in ((cap, True), (cap // 2, False), (1, True)):
+        lst = torch.randperm(cap, generator=gen)[:cnt].sort().values.to(torch.int32)
+        idx = torch.zeros(cap, dtype=torch.int32)
+        idx[:cnt] = lst
+        idx, count = idx.cuda(), torch.tensor([cnt], dtype=torch.int32, device="cuda")
+        buf = torch.full((G + nout + G,), 3.0, dtype=dt, device="cuda")
+        out = buf[G:G + nout].view(n, ho, wo, cout)
+        if not copy:
+            out.copy_(cache)
+        ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cache if copy else None, idx, count, g, out=out,
+                                        copy_cached=copy, workspace=ws)
+        torch.cuda.synchronize()
+        assert (buf[:G] == 3.0).all() and (buf[G + nout:] == 3.0).all(), f"{cnt} blocks: stray writes"
+        act = torch.zeros(cap, dtype=torch.uint8)
+        act[lst.long()] = 1
+        sel = active_pixels(act.view(n, nby, nbx), b, ho, wo).expand_as(out).cuda()
+        assert torch.equal(out[~sel].view(torch.uint8), cache[~sel].view(torch.uint8)), f"{cnt} blocks: unlisted"
