@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import numpy as np
 import torch
 
 import oracle
@@ -417,6 +418,34 @@ def test_layer_plan_wide_tiles_without_a_gpu():
                   (_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2), torch.float16)):
         p = ssi.sige_sparse_conv_layer_plan(g, dt)
         assert p.wide_stages == 0 and p.wide_min == p.wide_max == 0x7FFFFFFF, (g.k, g.s, g.b)
+
+
+def test_layer_plan_ranges_over_random_geometries():
+    """For any valid geometry and 16-bit or fp32 type the plan's ranges are
+    ordered and disjoint (split up to split_max, wide tiles wide_min..wide_max
+    after it, never past the capacity when present), the workspace is asked
+    for exactly when the split can run, and the wide tiles appear only where
+    their kernel can run (16-bit, k <= 3, stride 1 here)."""
+    rng = np.random.default_rng(5)
+    for _ in range(60):
+        k = int(rng.choice([1, 3, 5]))
+        s = int(rng.choice([1, 1, 2]))
+        b = int(rng.integers(2, 9))
+        h, w = int(rng.integers(8, 257)), int(rng.integers(8, 257))
+        cin, cout = 8 * int(rng.integers(1, 41)), 8 * int(rng.integers(1, 41))
+        dt = [torch.bfloat16, torch.float16, torch.float32][int(rng.integers(0, 3))]
+        g = _g(1, h, w, cin, cout, k, s, k // 2, b)
+        try:
+            p = ssi.sige_sparse_conv_layer_plan(g, dt)
+        except ssi.SigeError:
+            continue  # a geometry some kernel's limits exclude (the call says which)
+        assert -1 <= p.split_max <= p.cap
+        assert (p.workspace_bytes > 0) == (p.split_max >= 0)
+        if p.wide_min <= p.cap:
+            assert dt != torch.float32 and k <= 3 and p.wide_stages == (cin + 15) // 16
+            assert p.split_max < p.wide_min <= p.wide_max
+        else:
+            assert p.wide_min == 0x7FFFFFFF
 
 
 def test_auto_layer_validation(lib):
