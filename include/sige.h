@@ -263,11 +263,14 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
  * (SIGE_WIDE_MIN, read when a plan is made, sends lists of at least that many
  * blocks to the wide tiles where they can run: a tuning knob).
  *   Same arguments, checks and result as sige_sparse_conv_layer (up to the
- *   fp32 summation order of the kernel that runs), plus the split's
- *   workspace: at least sige_layer_plan.workspace_bytes of caller-owned
+ *   fp32 summation order of the kernel that runs), plus a workspace for the
+ *   split's partial tiles and for the wide tiles' K parts (lists too short
+ *   to give every compute unit a wide tile split their 16-channel stages
+ *   into up to wide_parts_max parts, whose fp32 partials a second launch
+ *   adds up): at least sige_layer_plan.workspace_bytes of caller-owned
  *   device memory (16-byte aligned, no initialisation, contents afterwards
  *   meaningless, not shared by calls that overlap in time); NULL and 0 when
- *   workspace_bytes is 0 (the split is never chosen).  SIGE_ERANGE when the
+ *   workspace_bytes is 0 (neither is ever chosen).  SIGE_ERANGE when the
  *   workspace is smaller.
  * sige_sparse_conv_layer_plan reports the choice for a geometry: split_max
  * (-1: never the split; >= cap: always), wide_min and wide_max (the wide
@@ -278,8 +281,9 @@ int sige_sparse_conv_layer_split(const void *a_edit, const void *w_krsc, const f
  * tiles of 32 output channels; the split's chunks, resident workgroup slots
  * and KiB of staged windows per tile (0 when the split cannot run); the
  * layer's weight megabytes and GFLOP per listed block; the wide tiles' K
- * stages of 16 channels, 1 KiB staging loads per stage and tiles of 128
- * output channels (0 when they cannot run)). */
+ * stages of 16 channels, staging loads per stage and tiles of 128 output
+ * channels (0 when they cannot run), and the most K parts a wide tile is
+ * split into (1: none)). */
 typedef struct {
     int32_t split_max;        /* the split takes lists of at most this many blocks (-1: none) */
     int32_t cap;              /* blocks at full capacity (sige_max_blocks) */
@@ -290,6 +294,7 @@ typedef struct {
     int32_t wide_min;         /* the wide tiles take lists of wide_min..wide_max blocks (wide_min > cap: none) */
     int32_t wide_stages, wide_loads, wide_n_tiles;
     int32_t wide_max;
+    int32_t wide_parts_max;   /* most K parts of a wide tile (1: never split; 0: no wide tiles) */
 } sige_layer_plan;
 int sige_sparse_conv_layer_plan(const sige_geom *g, int dtype, sige_layer_plan *out);
 int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,

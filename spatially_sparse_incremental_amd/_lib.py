@@ -47,7 +47,8 @@ class LayerPlan(ctypes.Structure):
                 ("slots", ctypes.c_int32), ("n_tiles", ctypes.c_int32), ("split_chunks", ctypes.c_int32),
                 ("split_slots", ctypes.c_int32), ("split_stage_kb", ctypes.c_double), ("weight_mb", ctypes.c_double),
                 ("gflop_per_block", ctypes.c_double), ("wide_min", ctypes.c_int32), ("wide_stages", ctypes.c_int32),
-                ("wide_loads", ctypes.c_int32), ("wide_n_tiles", ctypes.c_int32), ("wide_max", ctypes.c_int32)]
+                ("wide_loads", ctypes.c_int32), ("wide_n_tiles", ctypes.c_int32), ("wide_max", ctypes.c_int32),
+                ("wide_parts_max", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -3,7 +3,7 @@
 The library prices its three fused-layer kernels with a small cost model
 (sige_api.hip, "The kernel choice of sige_sparse_conv_layer_auto") and sends
 each list length to the cheapest one.  This script measures the kernels and
-fits that model's eleven constants:
+fits that model's thirteen constants:
 
     python -m spatially_sparse_incremental_amd.calibrate_layer_choice measure out.jsonl        # on the GPU
     python -m spatially_sparse_incremental_amd.calibrate_layer_choice measure-wide wide.jsonl  # on the GPU
@@ -126,12 +126,31 @@ def cost_split(q, p, b, cnt):
             + q[4] * rounds * p["split_stage_kb"])
 
 
+GATE_OFF_COMBINE = 1.5  # the library's kGateOffCombine
+
+
+def wide_parts(cus, pmax, ntr):
+    """K parts of the wide tiles for a list making ntr tiles (the library's wide_parts)."""
+    return max(1, min(pmax, cus // ntr if ntr > 0 else 1))
+
+
 def cost_wide(w, p, b, cnt, cus=256):
     """The library's model of the wide tiles, in microseconds."""
     mtn = -(-cnt * b * b // 256)
     ntn = p["wide_n_tiles"]
-    tiles = (-(-mtn // 8) * 8 if ntn > 1 else mtn) * ntn
-    return w[0] + -(-tiles // cus) * p["wide_stages"] * w[1] * p["wide_loads"]
+    pmax = max(1, p["wide_parts_max"])
+    np_ = wide_parts(cus, pmax, mtn * ntn)
+    items = mtn * ntn * np_ if np_ > 1 else (-(-mtn // 8) * 8 if ntn > 1 else mtn) * ntn
+    stages = -(-p["wide_stages"] // np_)
+    mb = items * (256 * 128 * 4e-6) if np_ > 1 else 0.0
+    return (w[0] + -(-items // cus) * (w[1] * stages * p["wide_loads"] + w[2]) + w[3] * mb
+            + (GATE_OFF_COMBINE if pmax > 1 and np_ == 1 else 0.0))
+
+
+def _wide_slots(b, cap):
+    """Block slots of one wide tile (256 rows), as the library sizes them."""
+    b2 = b * b
+    return min(256 // b2 if 256 % b2 == 0 else 255 // b2 + 2, cap)
 
 
 def fit(*paths):
@@ -156,7 +175,9 @@ def fit(*paths):
         r["plan"] = ssi.sige_sparse_conv_layer_plan(g, DTYPES[L.dtype]).as_dict()
 
     rs = [r for r in rows if "single_us" in r]
-    rw = [r for r in rows if "wide_us" in r]
+    # the wide model describes lists that fill a tile's block slots (a shorter
+    # list stages fewer windows per stage than the plan's wide_loads counts)
+    rw = [r for r in rows if "wide_us" in r and r["blocks"] >= _wide_slots(r["b"], r["plan"]["cap"])]
 
     def res_single(s):
         return [math.log(cost_single(s, r["plan"], r["b"], r["blocks"]) / r["single_us"]) for r in rs]
@@ -169,7 +190,7 @@ def fit(*paths):
 
     s = least_squares(res_single, [4.0, 3.0, 0.05, 0.04], bounds=(0, np.inf)).x
     q = least_squares(res_split, [12.0, 0.3, 3.0, 0.006, 0.01], bounds=(0, np.inf)).x
-    w = least_squares(res_wide, [7.0, 0.05], bounds=(0, np.inf)).x if rw else [0.0, 0.0]
+    w = least_squares(res_wide, [1.0, 0.03, 10.0, 0.4], bounds=(0, np.inf)).x if rw else [0.0, 0.0, 0.0, 0.0]
     print("rms log error: single %.3f, split %.3f, wide %.3f" % (
         np.sqrt(np.mean(np.square(res_single(s)))), np.sqrt(np.mean(np.square(res_split(q)))),
         np.sqrt(np.mean(np.square(res_wide(w)))) if rw else 0.0))

@@ -60,6 +60,7 @@ struct LayerArgs {
     Geo g;
     LayerCfg c;
     CopyCfg cc;
+    float *ws;                     // wide tiles split over K: the fp32 partial tiles
 };
 
 __device__ __forceinline__ void layer_tile(const LayerCfg &c, int t, int &tm, int &tn) {
@@ -501,20 +502,31 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
     const int mtn = (mrows + WR - 1) / WR;
     const int ntiles = (c.w_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * c.w_ntn;
     const int nst = (g.cin + 15) / 16;
+    // K parts, for lists whose tiles leave CUs idle: work item (tm*np + part)*w_ntn + tn
+    // takes stages st0..st1-1 of tile (tm, tn) and writes its fp32 partial tile
+    // to workspace slot `item`; k_wide_combine adds the parts up
+    const int np = a.ws ? wide_parts(c.cus, c.w_pmax, mtn * c.w_ntn) : 1;
+    const int nitems = np > 1 ? mtn * c.w_ntn * np : ntiles;
     const int nld = (g.ib + c.w_rpi - 1) / c.w_rpi;  // staging loads per slot window
     const int h = lane >> 5;                           // K half: channels 8h .. 8h+7 of the stage
     const int buf_bytes = c.w_wofs + k2 * WC * 32;
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        int tm, tn;
-        if (c.w_ntn > 1) {
-            const int r8 = t >> 3;
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        int tm, tn, part = 0;
+        if (np > 1) {
+            tn = item % c.w_ntn;
+            const int q = item / c.w_ntn;
+            part = q % np;
+            tm = q / np;
+        } else if (c.w_ntn > 1) {
+            const int r8 = item >> 3;
             tn = r8 % c.w_ntn;
-            tm = (r8 / c.w_ntn) * 8 + (t & 7);
+            tm = (r8 / c.w_ntn) * 8 + (item & 7);
         } else {
-            tm = t;
+            tm = item;
             tn = 0;
         }
         if (tm >= mtn) continue;  // padding of the tile order
+        const int st0 = part * nst / np, st1 = (part + 1) * nst / np;
         const int m0 = tm * WR, n0 = tn * WC;
         const int s_lo = fdiv(m0, c.m_b2);
         const int ns = fdiv(min(m0 + WR, mrows) - 1, c.m_b2) - s_lo + 1;  // at most 64 (checked on the host)
@@ -530,84 +542,121 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
                 sox = bx * g.b;
             }
         }
-        int ua[2];  // LDS unit of this lane's row (and K half) in each M fragment, tap 0
-#pragma unroll
-        for (int mf = 0; mf < 2; ++mf) {
-            const int r = m0 + cw * 64 + mf * 32 + (lane & 31);
-            ua[mf] = h;
-            if (r < mrows) {
-                const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
-                const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
-                const int l = slot - s_lo;
-                ua[mf] = l * c.w_sb + ((3 * l * b2) & 15) + py * g.s * c.w_rs + px * g.s * 3 + h;
-            }
-        }
-        int ub[4];  // LDS unit of this lane's column (and K half) in each N fragment, tap 0
-        float bcol[4];
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-            const int n = nf * 32 + (lane & 31);
-            ub[nf] = n * 2 + (h ^ ((n >> 3) & 1));
-            bcol[nf] = a.bias ? a.bias[min(n0 + n, g.cout - 1)] : 0.f;
-        }
-        f32x16 acc[2][4];
-#pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-            for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[mf][nf][v] = 0.f;
-
-        // Stage st's windows and weights into buffer `buf`.
-        auto stage = [&](int st, int buf) __attribute__((always_inline)) {
-            const int c0 = st * 16;
-            uint8_t *const wb = smem + buf * buf_bytes;
-            // windows: load (l, j) covers rows j*rpi .. of slot l's window; lane i
-            // takes unit i from the load's first row (the second row's units start
-            // at lane w_rs); lanes on padding are masked off
-#pragma unroll 1
-            for (int it = cw; it < ns * nld; it += 4) {
-                const int l = it / nld, j = it - l * nld;
-                const int n = __builtin_amdgcn_readlane(sn, l);
-                const int iy0 = __builtin_amdgcn_readlane(siy, l), ix0 = __builtin_amdgcn_readlane(six, l);
-                const int second = (c.w_rpi == 2 && lane >= c.w_rs) ? 1 : 0;
-                const int yy = j * c.w_rpi + second, rem = lane - second * c.w_rs;
-                const int xx = (rem * 43) >> 7, hh = rem - 3 * xx;  // rem / 3, rem % 3 (rem < 64)
-                const bool act = hh < 2 && xx < g.ib && yy < g.ib;
-                const int iy = iy0 + yy, ix = ix0 + xx, ch = c0 + 8 * hh;
-                const bool ok = act && n >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w && ch < g.cin;
-                const void *src = ok ? (const void *)(a.src + ((((long)n * g.h + iy) * g.w + ix) * g.cin + ch) * ES)
-                                     : (const void *)&k_zero16;
-                uint8_t *dst = wb + (l * c.w_sb + ((3 * l * b2) & 15) + j * c.w_rpi * c.w_rs) * 16;
-                if (act)
-                    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-            }
-            // weights: 4 k^2 groups of 64 units
-#pragma unroll 1
-            for (int gi = cw; gi < 4 * k2; gi += 4) {
-                const int u = gi * 64 + lane;
-                const int tap = u >> 8, nn = (u >> 1) & 127, hh = (u & 1) ^ ((nn >> 3) & 1);
-                const int col = n0 + nn, ch = c0 + 8 * hh;
-                const void *src = col < g.cout && ch < g.cin
-                                      ? (const void *)(a.w + (((long)col * k2 + tap) * g.cin + ch) * ES)
-                                      : (const void *)&k_zero16;
-                __builtin_amdgcn_global_load_lds(
-                    src, (__attribute__((address_space(3))) void *)(wb + c.w_wofs + gi * 1024), 16, 0, 0);
-            }
-        };
-
         __syncthreads();  // the previous tile's epilogue is done with the LDS
-        if (loader) {  // stage st + 1 while stage st is computed; one barrier per stage, as below
-            stage(0, 0);
-            for (int st = 0; st < nst; ++st) {
+        if (loader) {
+            // Stage st + 1 while stage st is computed; one barrier per stage, as in
+            // the computing waves.  The sources of this wave's loads are worked out
+            // once per tile: a stage adds 16 channels (32 bytes) to each, so issuing
+            // a load costs a select and an add.  Window load q of this wave is
+            // it = cw + 4q: rows j*rpi .. of slot l's window (it = l*nld + j); lane
+            // i takes unit i from the load's first row (the second row's units
+            // start at lane w_rs); lanes on padding are masked off.
+            const int second = (c.w_rpi == 2 && lane >= c.w_rs) ? 1 : 0;
+            const int rem = lane - second * c.w_rs;
+            const int xx = (rem * 43) >> 7, hh = rem - 3 * xx;  // rem / 3, rem % 3 (rem < 64)
+            const int nqw = (ns * nld - cw + 3) >> 2;            // <= kLayerWideWinLoads (checked on the host)
+            const uint8_t *wsrc[kLayerWideWinLoads];
+            int wdst[kLayerWideWinLoads];
+            uint32_t wact = 0, wok = 0;  // bit q: the lane holds data / its source lies in the image
+#pragma unroll
+            for (int q = 0; q < kLayerWideWinLoads; ++q) {
+                wsrc[q] = a.src;
+                wdst[q] = 0;
+                if (q < nqw) {
+                    const int it = cw + 4 * q, l = it / nld, j = it - l * nld;
+                    const int n = __builtin_amdgcn_readlane(sn, l);
+                    const int iy0 = __builtin_amdgcn_readlane(siy, l), ix0 = __builtin_amdgcn_readlane(six, l);
+                    const int yy = j * c.w_rpi + second;
+                    const bool act = hh < 2 && xx < g.ib && yy < g.ib;
+                    const int iy = iy0 + yy, ix = ix0 + xx;
+                    const bool ok = act && n >= 0 && iy >= 0 && iy < g.h && ix >= 0 && ix < g.w;
+                    if (ok) wsrc[q] = a.src + ((((long)n * g.h + iy) * g.w + ix) * g.cin + 8 * hh) * ES;
+                    wdst[q] = (l * c.w_sb + ((3 * l * b2) & 15) + j * c.w_rpi * c.w_rs) * 16;
+                    wact |= (uint32_t)act << q;
+                    wok |= (uint32_t)ok << q;
+                }
+            }
+            // Weight load q is group gi = cw + 4q of 64 units: unit u = gi*64 + lane
+            // holds (tap u/256, column (u/2) mod 128, channel half th), th being the
+            // same for every group of a lane.
+            const int th = (lane & 1) ^ ((lane >> 4) & 1);
+            const uint8_t *tsrc[9];
+            uint32_t tok = 0;
+#pragma unroll
+            for (int q = 0; q < 9; ++q) {
+                tsrc[q] = a.w;
+                if (q < k2) {
+                    const int u = (cw + 4 * q) * 64 + lane;
+                    const int tap = u >> 8, col = n0 + ((u >> 1) & 127);
+                    if (col < g.cout) {
+                        tsrc[q] = a.w + (((long)col * k2 + tap) * g.cin + 8 * th) * ES;
+                        tok |= 1u << q;
+                    }
+                }
+            }
+            const uint8_t *const zero = (const uint8_t *)&k_zero16;
+            auto stage = [&](int st, int buf) __attribute__((always_inline)) {
+                const long dl = (long)st * 32;
+                const bool hi_out = st * 16 + 8 >= g.cin;  // channels 8..15 of the stage past c_in
+                uint8_t *const wb = smem + buf * buf_bytes;
+#pragma unroll
+                for (int q = 0; q < kLayerWideWinLoads; ++q) {
+                    if (q < nqw && ((wact >> q) & 1)) {
+                        const bool ok = ((wok >> q) & 1) && !(hi_out && hh == 1);
+                        __builtin_amdgcn_global_load_lds(ok ? wsrc[q] + dl : zero,
+                                                         (__attribute__((address_space(3))) void *)(wb + wdst[q]),
+                                                         16, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 9; ++q) {
+                    if (q < k2) {
+                        const bool ok = ((tok >> q) & 1) && !(hi_out && th == 1);
+                        __builtin_amdgcn_global_load_lds(
+                            ok ? tsrc[q] + dl : zero,
+                            (__attribute__((address_space(3))) void *)(wb + c.w_wofs + (cw + 4 * q) * 1024), 16, 0,
+                            0);
+                    }
+                }
+            };
+            stage(st0, 0);
+            for (int st = st0; st < st1; ++st) {
                 __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage st have landed
                 __syncthreads();                // everyone's; and stage st - 1's reads are done
-                if (st + 1 < nst) stage(st + 1, (st + 1) & 1);
+                if (st + 1 < st1) stage(st + 1, (st + 1 - st0) & 1);
             }
+            __syncthreads();  // the computing waves are done reading the last stage
         } else {
-            for (int st = 0; st < nst; ++st) {
+            int ua[2];  // LDS unit of this lane's row (and K half) in each M fragment, tap 0
+#pragma unroll
+            for (int mf = 0; mf < 2; ++mf) {
+                const int r = m0 + cw * 64 + mf * 32 + (lane & 31);
+                ua[mf] = h;
+                if (r < mrows) {
+                    const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
+                    const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+                    const int l = slot - s_lo;
+                    ua[mf] = l * c.w_sb + ((3 * l * b2) & 15) + py * g.s * c.w_rs + px * g.s * 3 + h;
+                }
+            }
+            int ub[4];  // LDS unit of this lane's column (and K half) in each N fragment, tap 0
+            float bcol[4];
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) {
+                const int n = nf * 32 + (lane & 31);
+                ub[nf] = n * 2 + (h ^ ((n >> 3) & 1));
+                bcol[nf] = a.bias ? a.bias[min(n0 + n, g.cout - 1)] : 0.f;
+            }
+            f32x16 acc[2][4];
+#pragma unroll
+            for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mf][nf][v] = 0.f;
+            for (int st = st0; st < st1; ++st) {
                 __syncthreads();  // stage st is in LDS
-                const uint8_t *const wb = smem + (st & 1) * buf_bytes;
+                const uint8_t *const wb = smem + ((st - st0) & 1) * buf_bytes;
                 const uint8_t *const wl = wb + c.w_wofs;
                 // tap by tap (k <= 3): the next tap's fragments are read while this one's MFMAs run
                 u32x4 av[2][2], bv[2][4];
@@ -639,27 +688,37 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
                             acc[mf][nf] = Mfma32<DT>::run(av[tp & 1][mf], bv[tp & 1][nf], acc[mf][nf]);
                 }
             }
-        }
-
-        // Epilogue: bias, one rounding, the tile transposed through LDS, 16-byte row stores.
-        __syncthreads();  // every wave is done reading the last stage
-        if (!loader) {
+            // Epilogue: bias, one rounding, the tile transposed through LDS, 16-byte row stores;
+            // a K part: its fp32 partial tile, row-major, to the workspace
+            __syncthreads();  // every wave is done reading the last stage
+            if (np > 1) {
+                float *const wp = a.ws + (size_t)item * (WR * WC) + (cw * 64 + h * 4) * WC + (lane & 31);
 #pragma unroll
-            for (int mf = 0; mf < 2; ++mf)
+                for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-                for (int nf = 0; nf < 4; ++nf)
+                    for (int i = 0; i < 16; ++i)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int row = cw * 64 + mf * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-                        const int col = nf * 32 + (lane & 31);
-                        const float v = acc[mf][nf][i] + bcol[nf];
-                        if constexpr (DT == 1)
-                            *(__bf16 *)(smem + row * TP + col * 2) = (__bf16)v;
-                        else
-                            *(_Float16 *)(smem + row * TP + col * 2) = (_Float16)v;
-                    }
+                        for (int nf = 0; nf < 4; ++nf)
+                            wp[(mf * 32 + (i >> 2) * 8 + (i & 3)) * WC + nf * 32] = acc[mf][nf][i];
+            } else {
+#pragma unroll
+                for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int row = cw * 64 + mf * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+                            const int col = nf * 32 + (lane & 31);
+                            const float v = acc[mf][nf][i] + bcol[nf];
+                            if constexpr (DT == 1)
+                                *(__bf16 *)(smem + row * TP + col * 2) = (__bf16)v;
+                            else
+                                *(_Float16 *)(smem + row * TP + col * 2) = (_Float16)v;
+                        }
+            }
         }
         __syncthreads();
+        if (np > 1) continue;  // k_wide_combine stores the tile
 #pragma unroll
         for (int e0 = 0; e0 < WR * (WC / 8); e0 += kWideThreads) {
             const int e = e0 + tid;
@@ -681,7 +740,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
     if (TAIL) {  // the cache outside the listed blocks (copy_cached)
         __syncthreads();
         long long lo, hi;
-        copy_split(a.cc, ntiles, gridDim.x, blockIdx.x, lo, hi);
+        copy_split(a.cc, nitems, gridDim.x, blockIdx.x, lo, hi);
         if (lo < hi) {
             uint32_t *bm = nullptr;
             if (((g.cap + 31) >> 5) * 4 <= c.w_lds) {
@@ -693,22 +752,73 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
     }
 }
 
+// The K parts of the wide tiles added up: per listed output pixel and 8
+// channels, the bias plus the parts' fp32 partials in part order, rounded once.
+// Exits at once when the list is not the wide tiles' or makes no K parts.
+template <int DT>
+__global__ __launch_bounds__(256) void k_wide_combine(LayerArgs a) {
+    constexpr int WR = kLayerWideRows, WC = kLayerWideCols, VPR = WC / 8;
+    const Geo &g = a.g;
+    const LayerCfg &c = a.c;
+    const int cnt = clamp_count(a.count, g.cap);
+    if (cnt < c.wide_min || cnt > c.wide_max) return;
+    const int b2 = g.b * g.b, mrows = cnt * b2;
+    const int mtn = (mrows + WR - 1) / WR;
+    const int np = wide_parts(c.cus, c.w_pmax, mtn * c.w_ntn);
+    if (np < 2) return;
+    const long total = (long)mrows * c.w_ntn * VPR;  // (row, N tile, 8 channels)
+    for (long u = (long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long)gridDim.x * 256) {
+        const int v = (int)(u % VPR);
+        const long q = u / VPR;
+        const int tn = (int)(q % c.w_ntn), r = (int)(q / c.w_ntn);
+        const int co = tn * WC + v * 8;
+        if (co >= g.cout) continue;
+        const int tm = r / WR, row = r - tm * WR;
+        const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
+        const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
+        int n, by, bx;
+        if (!decode_block(g, a.idx[slot], n, by, bx)) continue;
+        const int y = by * g.b + py, x = bx * g.b + px;
+        if (y >= g.ho || x >= g.wo) continue;
+        float sum[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] = a.bias ? a.bias[co + j] : 0.f;
+#pragma unroll 4
+        for (int p = 0; p < np; ++p) {  // the parts' slots (tm*np + p)*w_ntn + tn, in part order
+            const float *wp = a.ws + ((size_t)((tm * np + p) * c.w_ntn + tn) * WR + row) * WC + v * 8;
+            const f32x4 lo = *(const f32x4 *)wp, hi = *(const f32x4 *)(wp + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sum[j] += lo[j];
+                sum[4 + j] += hi[j];
+            }
+        }
+        store_row8<DT>(a.dst + ((((size_t)n * g.ho + y) * g.wo + x) * g.cout + co) * 2, sum, true);
+    }
+}
+
 template <int DT, bool TAIL>
 static hipError_t launch_wide_k(const LayerArgs &args, hipStream_t st) {
     auto k = k_layer_wide<DT, TAIL>;
     const LayerCfg &c = args.c;
     long grid = c.cus;  // one workgroup per CU (both LDS buffers)
-    if (!TAIL && c.w_tiles_cap < grid) grid = c.w_tiles_cap;
+    if (!TAIL && c.w_pmax < 2 && c.w_tiles_cap < grid) grid = c.w_tiles_cap;
     if (grid > 8) grid = grid / 8 * 8;
     hipLaunchKernelGGL(k, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kWideThreads), c.w_lds, st, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !args.ws) return e;
+    const long rows = (long)c.w_ws_items * kLayerWideRows * (kLayerWideCols / 8);  // (row, 8 channels) at most
+    long cgrid = (rows + 255) / 256;
+    if (cgrid > 4L * c.cus) cgrid = 4L * c.cus;
+    hipLaunchKernelGGL(k_wide_combine<DT>, dim3((unsigned)(cgrid > 0 ? cgrid : 1)), dim3(256), 0, st, args);
     return hipGetLastError();
 }
 
 hipError_t launch_layer_wide(int dt, const void *src, const void *w, const float *bias, const int32_t *idx,
                              const int32_t *count, void *dst, const void *cache, const Geo &g, const LayerCfg &cfg,
-                             const CopyCfg &cc, hipStream_t st) {
+                             const CopyCfg &cc, hipStream_t st, float *ws) {
     const LayerArgs a{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
-                      (const uint8_t *)cache, nullptr, nullptr, g, cfg, cc};
+                      (const uint8_t *)cache, nullptr, nullptr, g, cfg, cc, cfg.w_pmax > 1 ? ws : nullptr};
     const bool tail = cc.nvec > 0;
     if (dt == 1) return tail ? launch_wide_k<1, true>(a, st) : launch_wide_k<1, false>(a, st);
     return tail ? launch_wide_k<2, true>(a, st) : launch_wide_k<2, false>(a, st);

@@ -255,10 +255,13 @@ int choose_conv(const Geo &g, int dt, int fused, int copy, ConvCfg *out, int str
 // staging load covers one or two window rows (64 lanes, those on padding
 // masked off), and a slot's LDS holds its window rows plus the bank rotation.
 // No wide tiles when both buffers (or the epilogue's tile) exceed the CU's
-// LDS.  wide_min: the list length from which the wide kernel runs
+// LDS, or when a staging wave would have more than kLayerWideWinLoads window
+// loads per stage (their sources are kept in registers).  wide_min: the list length from which the wide kernel runs
 // (SIGE_WIDE_MIN overrides it for tuning).
 void wide_layer(const Geo &g, int dt, const DevInfo &dv, sige::LayerCfg *c) {
     c->wide_min = c->wide_max = c->gate_wide = 0x7FFFFFFF;
+    c->w_pmax = 1;
+    c->w_ws_items = 0;
     if (dt == SIGE_F32 || g.k > 3 || 3 * g.ib > 64) return;
     const int b2 = g.b * g.b, k2 = g.k * g.k;
     int rs = 3 * g.ib;
@@ -271,6 +274,8 @@ void wide_layer(const Geo &g, int dt, const DevInfo &dv, sige::LayerCfg *c) {
     long nsw = WR % b2 == 0 ? WR / b2 : (WR - 1) / b2 + 2;
     if (nsw > g.cap) nsw = g.cap;
     if (nsw > 64) return;
+    const int nld = (g.ib + rpi - 1) / rpi;  // staging loads per slot window
+    if ((nsw * nld + 3) / 4 > sige::kLayerWideWinLoads) return;  // sources held in registers
     const long win = nsw * sb * 16, buf = win + (long)k2 * sige::kLayerWideCols * 32;
     const long need_e = (long)WR * sige::kLayerWidePitch;
     const long need = 2 * buf > need_e ? 2 * buf : need_e;
@@ -284,6 +289,19 @@ void wide_layer(const Geo &g, int dt, const DevInfo &dv, sige::LayerCfg *c) {
     c->w_lds = (int)need;
     const long mtn = ((long)g.cap * b2 + WR - 1) / WR;
     c->w_tiles_cap = (int)((c->w_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * c->w_ntn);
+    // K parts for lists too short to give every CU a tile: at least
+    // kLayerWideMinStages stages each; the workspace holds the most partial
+    // tiles any list length makes
+    const int nst = (g.cin + 15) / 16;
+    int pmax = nst / sige::kLayerWideMinStages;
+    c->w_pmax = pmax < 1 ? 1 : (pmax > 16 ? 16 : pmax);
+    c->w_ws_items = 0;
+    for (long m = 1; m <= mtn && m * c->w_ntn <= dv.cus / 2; ++m) {
+        const int np = sige::wide_parts(dv.cus, c->w_pmax, (int)(m * c->w_ntn));
+        const long items = m * c->w_ntn * np;
+        if (np > 1 && items > c->w_ws_items) c->w_ws_items = (int)items;
+    }
+    if (c->w_ws_items == 0) c->w_pmax = 1;
     long wmin = 0x7FFFFFFF;
     const char *e = getenv("SIGE_WIDE_MIN");
     if (e) {
@@ -575,21 +593,25 @@ int split_common(const void *a_edit, const void *w_krsc, const float *bias, cons
 //            + p4 * ceil(tiles * split_chunks / split_slots) * split_stage_kb
 //     (the weights stream once; the work items' rounds each stage a tile's
 //      windows of split_stage_kb KiB)
-//   wide:    w0 + ceil(wide tiles / CUs) * stages * w1 * loads
+//   wide:    w0 + ceil(wide tiles * parts / CUs) * (w1 * stages * loads + w2)
+//            + w3 * MB of fp32 partial tiles (parts > 1)
 //     (a stage of 16 input channels takes as long as the CU's memory path
-//      needs to accept its `loads` 1 KiB staging loads)
+//      needs to accept its `loads` staging loads; a round of work items adds
+//      its set-up, first stage and epilogue; `stages` are those of the longest
+//      of a tile's K parts, and the parts' partials are written and read back
+//      once)
 // Constants fitted (least squares on log time) to the kernels timed on MI355X
 // on edits of seeds other than the benchmark's, seven edit areas from 0.5% to
 // 80% of the frame, the U-Net, GauGAN and latent-diffusion layers
 // (calibrate_layer_choice.py in the package).  The k_layer model is the
-// loosest (rms error of log time 0.17, the others 0.07 and 0.17 for the wide
-// tiles), so a list goes from k_layer to the wide tiles only where the model
+// loosest (rms error of log time 0.17, the others 0.07 and 0.06 for the wide
+// tiles, fitted on lists that fill a wide tile's block slots), so a list goes from k_layer to the wide tiles only where the model
 // puts them ahead by more than that: kWideMargin.
 struct ChoiceModel {
-    double s[4], p[5], w[2];
+    double s[4], p[5], w[4];
 };
 constexpr ChoiceModel kChoice = {
-    {4.395, 1.916, 0.06717, 0.04092}, {10.76, 0.2046, 2.133, 0.003156, 0.0456}, {10.15, 0.04456}};
+    {4.395, 1.916, 0.06717, 0.04092}, {10.76, 0.2046, 2.133, 0.003156, 0.0456}, {0.9554, 0.03757, 10.8, 0.4737}};
 
 struct LayerFeat {
     int cap, b2, ntn;
@@ -599,6 +621,7 @@ struct LayerFeat {
     double wmb, gflop_per_block;       // all
     int wide_stages, wide_loads;       // the wide tiles: K stages, staging loads per stage (0: no wide tiles)
     int wide_ntn, cus;
+    int wide_pmax;                     // most K parts of a wide tile (1: no split)
 };
 
 LayerFeat layer_features(const Geo &g, int dt, const sige::LayerCfg &lc) {
@@ -626,6 +649,7 @@ LayerFeat layer_features(const Geo &g, int dt, const sige::LayerCfg &lc) {
         f.wide_stages = (g.cin + 15) / 16;
         f.wide_loads = (int)(nsw * ((g.ib + lc.w_rpi - 1) / lc.w_rpi) + 4 * g.k * g.k);
         f.wide_ntn = lc.w_ntn;
+        f.wide_pmax = lc.w_pmax;
     }
     ConvCfg cc;
     if (choose_conv(g, dt, 1, 1, &cc, 1) == SIGE_OK) {
@@ -635,6 +659,15 @@ LayerFeat layer_features(const Geo &g, int dt, const sige::LayerCfg &lc) {
     }
     return f;
 }
+
+// Microseconds a launch adds when its kernel exits at once (measured on
+// MI355X against the kernel alone): k_layer (a persistent grid, one round
+// trip for *count and the indices), the split (two launches), the wide tiles
+// (one workgroup per CU) and, when their tiles are split over K, its second
+// launch that adds the parts up.
+constexpr double kGateOffSingle = 3.0, kGateOffSplit = 3.2, kGateOffWide = 1.4;
+constexpr double kGateOffCombine = 1.5;
+constexpr double kWideMargin = 1.2;
 
 double cost_single(const LayerFeat &f, int cnt) {
     const double tiles = (double)(((long)cnt * f.b2 + 63) / 64) * f.ntn;
@@ -652,17 +685,14 @@ double cost_split(const LayerFeat &f, int cnt) {
 
 double cost_wide(const LayerFeat &f, int cnt) {
     const long mtn = ((long)cnt * f.b2 + sige::kLayerWideRows - 1) / sige::kLayerWideRows;
-    const long tiles = (f.wide_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * f.wide_ntn;
-    const long rounds = (tiles + f.cus - 1) / f.cus;
-    return kChoice.w[0] + (double)rounds * f.wide_stages * kChoice.w[1] * f.wide_loads;
+    const int np = sige::wide_parts(f.cus, f.wide_pmax, (int)(mtn * f.wide_ntn));
+    const long items = np > 1 ? mtn * f.wide_ntn * np : (f.wide_ntn > 1 ? (mtn + 7) / 8 * 8 : mtn) * f.wide_ntn;
+    const long rounds = (items + f.cus - 1) / f.cus;
+    const int stages = (f.wide_stages + np - 1) / np;  // the longest part
+    const double mb = np > 1 ? items * (sige::kLayerWideRows * sige::kLayerWideCols * 4e-6) : 0.0;
+    return kChoice.w[0] + (double)rounds * (kChoice.w[1] * stages * f.wide_loads + kChoice.w[2]) +
+           kChoice.w[3] * mb + (f.wide_pmax > 1 && np == 1 ? kGateOffCombine : 0.0);
 }
-
-// Microseconds a launch adds when its kernel exits at once (measured on
-// MI355X against the kernel alone): k_layer (a persistent grid, one round
-// trip for *count and the indices), the split (two launches), the wide tiles
-// (one workgroup per CU).
-constexpr double kGateOffSingle = 3.0, kGateOffSplit = 3.2, kGateOffWide = 1.4;
-constexpr double kWideMargin = 1.2;
 
 // The plan: the split for lists of at most split_max blocks, the wide tiles
 // for lists of at least wide_min, k_layer for the ones between (split_max -1:
@@ -676,7 +706,7 @@ constexpr double kWideMargin = 1.2;
 // lengths 1..cap is smallest (fewer kernels on a tie).
 void plan_thresholds(const LayerFeat &f, int *split_max, int *wide_min, int *wide_max) {
     const bool have[3] = {f.split_chunks > 0, true, f.wide_stages > 0};  // split, k_layer, wide
-    const double off[3] = {kGateOffSplit, kGateOffSingle, kGateOffWide};
+    const double off[3] = {kGateOffSplit, kGateOffSingle, kGateOffWide + (f.wide_pmax > 1 ? kGateOffCombine : 0.0)};
     std::vector<double> c[3];
     for (int k = 0; k < 3; ++k) c[k].assign(f.cap + 1, 1e30);
     std::vector<double> best(f.cap + 1, 1e30);
@@ -748,7 +778,7 @@ struct AutoPlan {
     int split_max;  // -1: k_layer only; >= cap: the split only; else both, gated on *count
     int wide_min;   // lists of wide_min..wide_max blocks go to the wide tiles (min > cap: never)
     int wide_max;
-    long ws_bytes;  // workspace for lists of at most split_max blocks
+    long ws_bytes;  // workspace: the split's partials (lists of at most split_max blocks), the wide tiles' K parts
 };
 
 // The plan of a layer, remembered per (geometry, dtype, device): the
@@ -809,6 +839,21 @@ int plan_auto(const Geo &g, int dt, AutoPlan *out) {
         p.lc.gate_wide = p.wide_min;
         p.lc.wide_min = p.wide_min;
         p.lc.wide_max = p.wide_max;
+    }
+    // K parts of the wide tiles only when a list of their range makes any (the
+    // shortest makes the fewest tiles); their partials share the workspace with
+    // the split's, which never runs on the same list
+    if (p.wide_min <= g.cap && p.lc.w_pmax > 1) {
+        const long WR = sige::kLayerWideRows;
+        const long mtn0 = ((long)(p.wide_min > 1 ? p.wide_min : 1) * g.b * g.b + WR - 1) / WR;
+        if (sige::wide_parts(p.lc.cus, p.lc.w_pmax, (int)(mtn0 * p.lc.w_ntn)) < 2) {
+            p.lc.w_pmax = 1;
+        } else {
+            const long wb = (long)p.lc.w_ws_items * WR * sige::kLayerWideCols * 4;
+            if (wb > p.ws_bytes) p.ws_bytes = wb;
+        }
+    } else {
+        p.lc.w_pmax = 1;
     }
     std::lock_guard<std::mutex> lk(mu);
     Entry &e = cache[used < 64 ? used++ : (next++ & 63)];
@@ -1122,6 +1167,7 @@ int sige_sparse_conv_layer_plan(const sige_geom *gp, int dtype, sige_layer_plan 
     out->split_stage_kb = p.f.split_kb;
     out->wide_min = p.wide_min;
     out->wide_max = p.wide_max;
+    out->wide_parts_max = p.f.wide_stages > 0 ? p.f.wide_pmax : 0;
     out->wide_stages = p.f.wide_stages;
     out->wide_loads = p.f.wide_loads;
     out->wide_n_tiles = p.f.wide_ntn;
@@ -1175,7 +1221,7 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
     }
     if (p.wide_min <= g.cap) {  // the wide tiles: lists of at least wide_min blocks
         if ((rc = finish(sige::launch_layer_wide(dtype, a_edit, w_krsc, bias, idx, count, out,
-                                                 copy_cached ? cached : nullptr, g, p.lc, cc, st),
+                                                 copy_cached ? cached : nullptr, g, p.lc, cc, st, (float *)workspace),
                          "sige_sparse_conv_layer_auto", st)))
             return rc;
     }

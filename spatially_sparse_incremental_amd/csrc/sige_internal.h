@@ -70,10 +70,22 @@ struct LayerCfg {
     int w_lds;           // dynamic LDS of the wide kernel (two buffers, or the epilogue's tile)
     int w_tiles_cap;     // wide tiles (padding included) at full capacity
     int gate_wide;       // k_layer: lists of gate_wide..wide_max blocks are the wide kernel's (it exits)
+    int w_pmax;          // most K parts a wide tile's stages are split into (1: none); parts > 1 leave
+                         // fp32 partial tiles in the workspace for k_wide_combine
+    int w_ws_items;      // partial tiles (kLayerWideRows x kLayerWideCols fp32) the workspace holds
 };
 constexpr int kLayerWideRows = 256;  // output rows (block pixels) of a wide tile
 constexpr int kLayerWideCols = 128;  // output channels of a wide tile
 constexpr int kLayerWidePitch = kLayerWideCols * 2 + 16;  // LDS bytes per row of the rounded wide tile
+constexpr int kLayerWideWinLoads = 16;  // window loads per staging wave and stage of a wide tile, at most
+constexpr int kLayerWideMinStages = 4;   // 16-channel stages per K part of a wide tile, at least
+
+// K parts of the wide tiles for a list that makes `ntr` of them (padding not
+// counted): as many as give every CU a work item, at most pmax.
+__host__ __device__ inline int wide_parts(int cus, int pmax, int ntr) {
+    const int p = ntr > 0 ? cus / ntr : 1;
+    return p < 1 ? 1 : (p > pmax ? pmax : p);
+}
 
 // Copy of the cache outside the listed blocks, in 16-byte vectors of the
 // output flattened over (n, y, x, vector of the channel row).
@@ -130,11 +142,14 @@ hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const
                         const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                         const int32_t *prev_count, const Geo &g, const LayerCfg &cfg, const CopyCfg &cc,
                         hipStream_t st);
-// The wide tiles of the fused layer (16-bit types), run for lists of at least
-// cfg.wide_min blocks (the launch exits at once for shorter ones).
+// The wide tiles of the fused layer (16-bit types), run for lists of
+// cfg.wide_min..cfg.wide_max blocks (the launches exit at once for others).
+// With cfg.w_pmax > 1 a short list's tiles are split over K into parts whose
+// fp32 partials go to ws (cfg.w_ws_items tiles), and a second launch adds
+// them up into dst.
 hipError_t launch_layer_wide(int dt, const void *src, const void *w, const float *bias, const int32_t *idx,
                              const int32_t *count, void *dst, const void *cache, const Geo &g, const LayerCfg &cfg,
-                             const CopyCfg &cc, hipStream_t st);
+                             const CopyCfg &cc, hipStream_t st, float *ws);
 // Bytes of that workspace for g and the launch configuration c (< 0: unknown tile shape).
 long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c);
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,

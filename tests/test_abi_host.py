@@ -407,17 +407,21 @@ def test_layer_plan_wide_tiles_without_a_gpu():
     loads per tap for 128 columns of weights)."""
     p = ssi.sige_sparse_conv_layer_plan(_g(1, 256, 256, 128, 128, 3, 1, 1, 6), torch.bfloat16)
     assert p.wide_stages == 8 and p.wide_loads == 9 * 4 + 4 * 9 and p.wide_n_tiles == 1
-    assert p.split_max < p.wide_min <= p.wide_max <= p.cap
-    # the wide range ends at the longest list of one round (256 tiles of 256 rows on 256 CUs)
-    assert p.wide_max == 256 * 256 // 36
+    # from a few hundred blocks on, up to every block (wide_max past the capacity: no end)
+    assert p.split_max < p.wide_min <= p.cap // 2 and p.wide_max >= p.cap
+    # 8 stages: at most 2 K parts of 4 stages
+    assert p.wide_parts_max == 2
     p = ssi.sige_sparse_conv_layer_plan(_g(1, 256, 512, 256, 128, 3, 1, 1, 6), torch.bfloat16)
-    assert p.wide_stages == 16 and p.split_max < p.wide_min <= p.cap
+    assert p.wide_stages == 16 and p.split_max < p.wide_min <= p.cap and p.wide_parts_max == 4
+    p = ssi.sige_sparse_conv_layer_plan(_g(1, 32, 64, 1024, 1024, 3, 1, 1, 4), torch.bfloat16)
+    assert p.wide_stages == 64 and p.wide_parts_max == 16
     for g, dt in ((_g(1, 256, 256, 128, 128, 3, 1, 1, 6), torch.float32),
                   (_g(1, 64, 64, 64, 64, 5, 1, 2, 6), torch.bfloat16),
                   (_g(1, 64, 64, 64, 128, 3, 2, 1, 4), torch.float16),
                   (_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2), torch.float16)):
         p = ssi.sige_sparse_conv_layer_plan(g, dt)
         assert p.wide_stages == 0 and p.wide_min == p.wide_max == 0x7FFFFFFF, (g.k, g.s, g.b)
+        assert p.wide_parts_max == 0
 
 
 def test_layer_plan_ranges_over_random_geometries():

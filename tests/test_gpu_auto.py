@@ -112,7 +112,10 @@ def test_auto_latent_diffusion_layers(area):
 
 def test_auto_persistent_buffer_and_empty_list():
     """copy_cached = 0 writes only the listed blocks; an empty list writes nothing
-    (copy_cached = 0) or the cache (copy_cached = 1), on both sides of the plan."""
+    (copy_cached = 0) or the cache (copy_cached = 1), on every side of the plan
+    (bit for bit against the kernel the plan names; the wide tiles against the
+    single-range kernel within tolerance on the listed blocks, bit for bit
+    elsewhere)."""
     L = synth.workload("gaugan_4conv_bf16").layers[1]  # 64x128x1024 -> 512: the plan uses both kernels
     g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
     plan = ssi.sige_sparse_conv_layer_plan(g, DTYPES[L.dtype])
@@ -122,20 +125,36 @@ def test_auto_persistent_buffer_and_empty_list():
     a = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 9).cuda()
     cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, 10).cuda()
     cap = plan.cap
-    for n in (0, 1, plan.split_max, plan.split_max + 1, cap):
+    d = ssi.sige_geom_derive(g)
+    lengths = sorted({0, 1, plan.split_max, plan.split_max + 1, min(plan.wide_min - 1, cap), min(plan.wide_min, cap),
+                      cap})
+    for n in lengths:
         idx = torch.arange(cap, dtype=torch.int32, device="cuda")  # ascending, the first n listed
         count = torch.tensor([n], dtype=torch.int32, device="cuda")
+        wide = plan.wide_min <= n <= plan.wide_max
+        act = torch.zeros(cap, dtype=torch.uint8)
+        act[:n] = 1
+        sel = active_pixels(act.view(1, d.nby, d.nbx), L.block, d.ho, d.wo).expand_as(cache.cpu())
+
+        def same(got, ref, what):
+            o, r = got.cpu(), ref.cpu()
+            if not wide:
+                assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), what
+                return
+            assert torch.equal(o[~sel].view(torch.uint8), r[~sel].view(torch.uint8)), what + ": untouched pixels"
+            assert_close(o, r.double(), o.dtype, sel, what + ": wide tiles against the single-range kernel")
+
         sentinel = torch.full_like(cache, 7.0)
         got = ssi.sige_sparse_conv_layer_auto(a, wk, bias.cuda(), None, idx, count, g, out=sentinel.clone(),
                                               copy_cached=False)
         ref_fn = ssi.sige_sparse_conv_layer_split if n <= plan.split_max else ssi.sige_sparse_conv_layer
         ref = ref_fn(a, wk, bias.cuda(), None, idx, count, g, out=sentinel.clone(), copy_cached=False)
         torch.cuda.synchronize()
-        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"copy_cached=0, {n} blocks"
+        same(got, ref, f"copy_cached=0, {n} blocks")
         got = ssi.sige_sparse_conv_layer_auto(a, wk, bias.cuda(), cache, idx, count, g)
         ref = ref_fn(a, wk, bias.cuda(), cache, idx, count, g)
         torch.cuda.synchronize()
-        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"copy_cached=1, {n} blocks"
+        same(got, ref, f"copy_cached=1, {n} blocks")
         if n == 0:
             assert torch.equal(got.view(torch.uint8), cache.view(torch.uint8))
 

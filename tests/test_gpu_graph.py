@@ -9,7 +9,7 @@ import torch
 
 import spatially_sparse_incremental_amd as ssi
 import synth
-from _parity import bits, layer_inputs, rand
+from _parity import active_pixels, assert_close, bits, layer_inputs, rand
 
 pytestmark = pytest.mark.gpu
 
@@ -76,13 +76,15 @@ def test_graph_replays_match_eager(copy):
 
 
 def test_graph_replays_of_the_auto_layer_follow_the_list_length():
-    """sige_sparse_conv_layer_auto captured once on a layer whose plan enqueues both
-    kernels: replays with list lengths on either side of the threshold (written in
-    place) match an eager call bit for bit, and the kernel the plan names."""
+    """sige_sparse_conv_layer_auto captured once on a layer whose plan enqueues all
+    three kernels: replays with list lengths on every side of the thresholds
+    (written in place) match an eager call bit for bit, and the kernel the plan
+    names (the wide tiles: the single-range kernel within tolerance on the listed
+    blocks, bit for bit elsewhere)."""
     L = synth.workload("gaugan_4conv_bf16").layers[1]  # 64x128x1024 -> 512: gated plan
     g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
     plan = ssi.sige_sparse_conv_layer_plan(g, torch.bfloat16)
-    assert 0 <= plan.split_max < plan.cap
+    assert 0 <= plan.split_max < plan.wide_min <= plan.cap
     wt, bias = synth.make_layer_tensors(L, 31)
     wk, bias = ssi.weight_to_krsc(wt).cuda(), bias.cuda()
     a = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 32).cuda()
@@ -105,7 +107,9 @@ def test_graph_replays_of_the_auto_layer_follow_the_list_length():
     with torch.cuda.graph(graph):
         layer()
     rng = np.random.default_rng(34)
-    for n in (7, plan.split_max, plan.split_max + 1, 300, 0, plan.split_max // 2):
+    d = ssi.sige_geom_derive(g)
+    for n in (7, plan.split_max, plan.split_max + 1, plan.wide_min - 1, plan.wide_min, plan.cap, 0,
+              plan.split_max // 2):
         pick = np.sort(rng.choice(plan.cap, size=n, replace=False)).astype(np.int32)
         idx.zero_()
         idx[:n] = torch.from_numpy(pick).cuda()
@@ -120,4 +124,12 @@ def test_graph_replays_of_the_auto_layer_follow_the_list_length():
         ref = ref_fn(a, wk, bias, cache, idx, cnt, g)
         torch.cuda.synchronize()
         assert torch.equal(bits(got), bits(out)), n
-        assert torch.equal(bits(got), bits(ref)), n
+        if n < plan.wide_min:
+            assert torch.equal(bits(got), bits(ref)), n
+        else:
+            act = torch.zeros(plan.cap, dtype=torch.uint8)
+            act[torch.from_numpy(pick).long()] = 1
+            sel = active_pixels(act.view(1, d.nby, d.nbx), L.block, d.ho, d.wo).expand_as(cache.cpu())
+            o, r = got.cpu(), ref.cpu()
+            assert torch.equal(o[~sel].view(torch.uint8), r[~sel].view(torch.uint8)), n
+            assert_close(o, r.double(), o.dtype, sel, f"wide tiles in a graph replay, {n} blocks")

@@ -3,11 +3,14 @@ sige_sparse_conv_layer_auto for long lists) against the oracle.
 
 SIGE_WIDE_MIN=0 makes the plan send every list of these geometries to the wide
 tiles (the plan is made once per geometry, so the geometries here are used by
-no other test).  Edge cases: a partial last 16-channel stage (c_in = 24),
+no other test).  Edge cases: a partial last 16-channel stage (c_in = 24, 200),
 output channels past one or two 128-channel tiles (c_out = 136, 64), two
 images, 1x1 and 3x3 kernels, blocks of 4, 5, 6 and 8 (one or two window rows
 per staging load), windows over the image border, several 256-row tiles, the
-empty list, one block, every block, with and without the cache copy."""
+empty list, one block, every block, with and without the cache copy; and
+tiles split over K (c_in >= 128: these lists make fewer tiles than there are
+compute units, so each tile's stages are split into 2-4 parts, of unequal
+length for c_in = 200, whose fp32 partials a second launch adds up)."""
 import os
 
 import pytest
@@ -32,13 +35,24 @@ CASES = [
     ("two_images_b4_f16", 2, 30, 30, 32, 64, 3, 1, 1, 4, "f16"),
     ("pointwise_b5_bf16", 1, 33, 35, 48, 128, 1, 1, 0, 5, "bf16"),
     ("b8_one_row_per_load_f16", 1, 48, 52, 40, 96, 3, 1, 1, 8, "f16"),
+    ("parts3_cin200_cout136_b6_bf16", 1, 40, 44, 200, 136, 3, 1, 1, 6, "bf16"),
+    ("parts4_cin256_two_images_b4_f16", 2, 30, 30, 256, 64, 3, 1, 1, 4, "f16"),
+    ("parts2_pointwise_cin128_b5_bf16", 1, 33, 35, 128, 128, 1, 1, 0, 5, "bf16"),
 ]
+
+
+def _parts_max(cin):
+    """The most K parts of a wide tile: at least 4 stages of 16 channels each, at most 16 parts."""
+    return max(1, min(16, ((cin + 15) // 16) // 4))
 
 
 def _forced_plan(g, dt, monkeypatch):
     monkeypatch.setenv("SIGE_WIDE_MIN", "0")
     plan = ssi.sige_sparse_conv_layer_plan(g, dt)
     assert plan.wide_stages > 0 and plan.wide_min <= plan.split_max + 1, plan.as_dict()
+    assert plan.wide_parts_max == _parts_max(g.c_in), plan.as_dict()
+    if plan.wide_parts_max > 1:  # the partial tiles' workspace
+        assert plan.workspace_bytes >= 2 * 256 * 128 * 4, plan.as_dict()
     return plan
 
 
@@ -83,10 +97,11 @@ def test_wide_tiles_against_the_oracle(case, monkeypatch):
         assert torch.equal(pers.cpu().view(torch.uint8), out.view(torch.uint8)), f"{name}: persistent buffer"
 
 
-def test_wide_tiles_in_a_graph_replay(monkeypatch):
+@pytest.mark.parametrize("cin", [32, 256], ids=["one_part", "four_parts"])
+def test_wide_tiles_in_a_graph_replay(cin, monkeypatch):
     """Replays of a captured wide-tile layer equal the eager result (each replay's
-    output cleared in between)."""
-    n, h, w, cin, cout, k, s, p, b = 1, 36, 60, 32, 128, 3, 1, 1, 6
+    output cleared in between), with and without the K split."""
+    n, h, w, cout, k, s, p, b = 1, 36, 60, 128, 3, 1, 1, 6
     dt = torch.bfloat16
     g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
     plan = _forced_plan(g, dt, monkeypatch)
@@ -160,11 +175,13 @@ def test_wide_tiles_at_full_size():
     assert_close(out, r64, dt, active_pixels(sub, b, ho, wo), "wide tiles, sampled blocks against the oracle")
 
 
-def test_wide_tiles_write_nothing_outside_out(monkeypatch):
-    """Guard canaries before and after `out`: the wide tiles (every list of this
-    geometry forced to them) write only inside the output, with and without the
-    cache copy, and leave the unlisted blocks alone without it."""
-    n, h, w, cin, cout, k, s, p, b = 1, 26, 34, 40, 72, 3, 1, 1, 6
+@pytest.mark.parametrize("cin", [40, 128], ids=["one_part", "two_parts"])
+def test_wide_tiles_write_nothing_outside_out(cin, monkeypatch):
+    """Guard canaries before and after `out` (and after the workspace): the wide
+    tiles (every list of this geometry forced to them) write only inside the
+    output and the workspace, with and without the cache copy and the K split,
+    and leave the unlisted blocks alone without the copy."""
+    n, h, w, cout, k, s, p, b = 1, 26, 34, 72, 3, 1, 1, 6
     dt = torch.bfloat16
     g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
     plan = _forced_plan(g, dt, monkeypatch)
@@ -174,7 +191,9 @@ def test_wide_tiles_write_nothing_outside_out(monkeypatch):
     _, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 63, mask)
     cache = rand((n, ho, wo, cout), dt, 65).cuda()
     ag, wk, bg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda()
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    nws = max(plan.workspace_bytes, 16)
+    wbuf = torch.full((nws + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = wbuf[:nws]
     G, nout = 4096, n * ho * wo * cout
     gen = torch.Generator().manual_seed(67)
     for cnt, copy in ((cap, True), (cap // 2, False), (1, True)):
@@ -190,6 +209,7 @@ def test_wide_tiles_write_nothing_outside_out(monkeypatch):
                                         copy_cached=copy, workspace=ws)
         torch.cuda.synchronize()
         assert (buf[:G] == 3.0).all() and (buf[G + nout:] == 3.0).all(), f"{cnt} blocks: stray writes"
+        assert (wbuf[nws:] == 0x5A).all(), f"{cnt} blocks: writes past the workspace"
         act = torch.zeros(cap, dtype=torch.uint8)
         act[lst.long()] = 1
         sel = active_pixels(act.view(n, nby, nbx), b, ho, wo).expand_as(out).cuda()
