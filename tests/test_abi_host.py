@@ -407,8 +407,9 @@ def test_layer_plan_wide_tiles_without_a_gpu():
     loads per tap for 128 columns of weights)."""
     p = ssi.sige_sparse_conv_layer_plan(_g(1, 256, 256, 128, 128, 3, 1, 1, 6), torch.bfloat16)
     assert p.wide_stages == 8 and p.wide_loads == 9 * 4 + 4 * 9 and p.wide_n_tiles == 1
-    # from a few hundred blocks on, up to every block (wide_max past the capacity: no end)
-    assert p.split_max < p.wide_min <= p.cap // 2 and p.wide_max >= p.cap
+    # from several hundred blocks on, to the longest list of one round (256 tiles of
+    # 256 rows on 256 CUs): a list one tile longer takes two rounds and k_layer leads
+    assert p.split_max < p.wide_min <= p.wide_max == 256 * 256 // 36 < p.cap
     # 8 stages: at most 2 K parts of 4 stages
     assert p.wide_parts_max == 2
     p = ssi.sige_sparse_conv_layer_plan(_g(1, 256, 512, 256, 128, 3, 1, 1, 6), torch.bfloat16)
