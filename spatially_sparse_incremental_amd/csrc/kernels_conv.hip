@@ -532,22 +532,37 @@ __global__ __launch_bounds__(256) void k_split_combine(ConvArgs a, int slots) {
         if (r >= mrows || co >= g.cout) continue;
         const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
         const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
-        int n, by, bx;
-        if (!decode_block(g, a.idx[slot], n, by, bx)) continue;
-        const int y = by * g.b + py, x = bx * g.b + px;
-        if (y >= g.ho || x >= g.wo) continue;
+        // the block index and the first partials are requested together (the
+        // partials' addresses do not depend on the index), then the sum
+        const int lin = a.idx[slot];
         float sum[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) sum[j] = a.bias ? a.bias[min(co + j, g.cout - 1)] : 0.f;
-        for (int ks = 0; ks < nch; ks += pl.acc_range ? pl.cpk : 1) {
-            const float *wp = a.ws + (((size_t)tile * nch + ks) * BM + row) * BN + col;
-            const f32x4 lo = *(const f32x4 *)wp, hi = *(const f32x4 *)(wp + 4);
+        const int kstep = pl.acc_range ? pl.cpk : 1;
+        constexpr int PB = 4;  // partial tiles requested at once
+        for (int ks0 = 0; ks0 < nch; ks0 += PB * kstep) {
+            f32x4 lo[PB], hi[PB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sum[j] += lo[j];
-                sum[4 + j] += hi[j];
+            for (int q = 0; q < PB; ++q) {
+                const int ks = min(ks0 + q * kstep, nch - 1);
+                const float *wp = a.ws + (((size_t)tile * nch + ks) * BM + row) * BN + col;
+                lo[q] = *(const f32x4 *)wp;
+                hi[q] = *(const f32x4 *)(wp + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                if (ks0 + q * kstep >= nch) break;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sum[j] += lo[q][j];
+                    sum[4 + j] += hi[q][j];
+                }
             }
         }
+        int n, by, bx;
+        if (!decode_block(g, lin, n, by, bx)) continue;
+        const int y = by * g.b + py, x = bx * g.b + px;
+        if (y >= g.ho || x >= g.wo) continue;
         store_row8<DT>(a.dst + ((((size_t)n * g.ho + y) * g.wo + x) * g.cout + co) * ES, sum, g.cout - co >= 8);
     }
     if (a.cc.nvec > 0) {

@@ -776,23 +776,36 @@ __global__ __launch_bounds__(256) void k_wide_combine(LayerArgs a) {
         const int tm = r / WR, row = r - tm * WR;
         const int slot = fdiv(r, c.m_b2), pix = r - slot * b2;
         const int py = fdiv(pix, c.m_b), px = pix - py * g.b;
-        int n, by, bx;
-        if (!decode_block(g, a.idx[slot], n, by, bx)) continue;
-        const int y = by * g.b + py, x = bx * g.b + px;
-        if (y >= g.ho || x >= g.wo) continue;
+        // the block index and the first parts are requested together (the
+        // parts' addresses do not depend on the index), then the sum
+        const int lin = a.idx[slot];
         float sum[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) sum[j] = a.bias ? a.bias[co + j] : 0.f;
-#pragma unroll 4
-        for (int p = 0; p < np; ++p) {  // the parts' slots (tm*np + p)*w_ntn + tn, in part order
-            const float *wp = a.ws + ((size_t)((tm * np + p) * c.w_ntn + tn) * WR + row) * WC + v * 8;
-            const f32x4 lo = *(const f32x4 *)wp, hi = *(const f32x4 *)(wp + 4);
+        constexpr int PB = 4;  // parts requested at once
+        for (int p0 = 0; p0 < np; p0 += PB) {  // the parts' slots (tm*np + p)*w_ntn + tn, in part order
+            f32x4 lo[PB], hi[PB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sum[j] += lo[j];
-                sum[4 + j] += hi[j];
+            for (int q = 0; q < PB; ++q) {
+                const int p = min(p0 + q, np - 1);
+                const float *wp = a.ws + ((size_t)((tm * np + p) * c.w_ntn + tn) * WR + row) * WC + v * 8;
+                lo[q] = *(const f32x4 *)wp;
+                hi[q] = *(const f32x4 *)(wp + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                if (p0 + q >= np) break;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sum[j] += lo[q][j];
+                    sum[4 + j] += hi[q][j];
+                }
             }
         }
+        int n, by, bx;
+        if (!decode_block(g, lin, n, by, bx)) continue;
+        const int y = by * g.b + py, x = bx * g.b + px;
+        if (y >= g.ho || x >= g.wo) continue;
         store_row8<DT>(a.dst + ((((size_t)n * g.ho + y) * g.wo + x) * g.cout + co) * 2, sum, true);
     }
 }
