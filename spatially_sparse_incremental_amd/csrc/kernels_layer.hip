@@ -508,9 +508,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
     const int np = a.ws ? wide_parts(c.cus, c.w_pmax, mtn * c.w_ntn) : 1;
     const int nitems = np > 1 ? mtn * c.w_ntn * np : ntiles;
     const int nld = (g.ib + c.w_rpi - 1) / c.w_rpi;  // staging loads per slot window
-    const int h = lane >> 5;                           // K half: channels 8h .. 8h+7 of the stage
     const int buf_bytes = c.w_wofs + k2 * WC * 32;
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        // the lane index made opaque per tile: values derived from it are
+        // recomputed here instead of being hoisted out of the loop and kept live
+        // beside the accumulators (which made the kernel spill registers)
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int h = lane >> 5;  // K half: channels 8h .. 8h+7 of the stage
         int tm, tn, part = 0;
         if (np > 1) {
             tn = item % c.w_ntn;
