@@ -804,6 +804,8 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
                            cnt=torch.empty((1,), dtype=torch.int32, device=dev),
                            w_cl=w_cpu.to(dev).contiguous(memory_format=torch.channels_last),
                            b16=b_cpu.to(dev).to(a_e.dtype), mbits=mbits))
+        ly = layers[-1]
+        ly["ww"] = ssi.sige_wide_weights_pack(ly["wk"], g) if ssi.sige_wide_weights_bytes(g, a_e.dtype) > 0 else None
     blocks = []
 
     def sparse_chain():
@@ -908,7 +910,7 @@ def _chain_conv(ssi, ly, x):
     copy), by ly["mode"]: the library's choice, or one kernel."""
     if ly["mode"] == "auto":
         ssi.sige_sparse_conv_layer_auto(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
-                                        out=ly["out"], copy_cached=False, workspace=ly["ws"])
+                                        out=ly["out"], copy_cached=False, workspace=ly["ws"], w_wide=ly["ww"])
     elif ly["mode"] == "split":
         ssi.sige_sparse_conv_layer_split(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
                                          out=ly["out"], copy_cached=False, workspace=ly["ws"])
@@ -922,7 +924,9 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     0.5 / 1.2 / 5 / 15 / 30% of the frame: the reduce (mask one bit per pixel,
     the cache copy on its idle workgroups) + sige_sparse_conv_layer_auto (the
     kernel the library picks; `path`: split, single (64 x 32 tiles) or wide
-    (256 x 128 tiles)), against the dense conv through torch/MIOpen;
+    (256 x 128 tiles, staging their weights from the stage-major copy that
+    sige_wide_weights_pack makes once per layer, outside the timing)), against
+    the dense conv through torch/MIOpen;
     best_of_two_bound: the faster of the single-range and split kernels (the
     two with entry points of their own) timed on the very edit, which a caller
     cannot do."""
@@ -935,8 +939,10 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
         a_o = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, seed + li).to(dev)
         g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
         cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50).to(dev)
-        prep.append((L, g, a_o, ssi.weight_to_krsc(w_cpu).to(dev), b_cpu.to(dev), cache,
-                     w_cpu.to(dev).contiguous(memory_format=torch.channels_last)))
+        wk = ssi.weight_to_krsc(w_cpu).to(dev)
+        ww = ssi.sige_wide_weights_pack(wk, g) if ssi.sige_wide_weights_bytes(g, a_o.dtype) > 0 else None
+        prep.append((L, g, a_o, wk, b_cpu.to(dev), cache,
+                     w_cpu.to(dev).contiguous(memory_format=torch.channels_last), ww))
         with torch.no_grad():
             x = a_o.permute(0, 3, 1, 2)
             dense[L.name] = round(timed_eager(lambda: F.conv2d(x, prep[-1][6], prep[-1][4].to(a_o.dtype),
@@ -944,7 +950,7 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     for area in (0.005, 0.012, 0.05, 0.15, 0.30):
         shape = synth.edit_shape(wl, seed, area)
         row = {}
-        for li, (L, g, a_o, wk, bias, cache, _) in enumerate(prep):
+        for li, (L, g, a_o, wk, bias, cache, _, ww) in enumerate(prep):
             a_e = synth.make_edit(a_o.cpu(), shape.raster(L.h, L.w), wl.edit_kind, seed + li).to(dev)
             mbits = ssi.sige_diff_mask_bits(a_o, a_e, wl.tau)
             idx, cnt = ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate)
@@ -957,7 +963,7 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
             def auto():
                 ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)
                 ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False,
-                                                workspace=ws_auto)
+                                                workspace=ws_auto, w_wide=ww)
 
             def one():
                 ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)

@@ -61,6 +61,7 @@ struct LayerArgs {
     LayerCfg c;
     CopyCfg cc;
     float *ws;                     // wide tiles split over K: the fp32 partial tiles
+    const uint8_t *ww;             // wide tiles: the weights in stage-major order (NULL: from w, KRSC)
 };
 
 __device__ __forceinline__ void layer_tile(const LayerCfg &c, int t, int &tm, int &tn) {
@@ -583,17 +584,25 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
             }
             // Weight load q is group gi = cw + 4q of 64 units: unit u = gi*64 + lane
             // holds (tap u/256, column (u/2) mod 128, channel half th), th being the
-            // same for every group of a lane.
+            // same for every group of a lane.  From KRSC weights a load gathers 32
+            // bytes of each of 32 columns and a stage adds 32 bytes to its source;
+            // from the stage-major copy (ww: the units of one N tile and stage in
+            // this LDS order, padding zero) a load reads 1 KiB in a row and a
+            // stage adds k*k KiB x 4.
             const int th = (lane & 1) ^ ((lane >> 4) & 1);
             const uint8_t *tsrc[9];
             uint32_t tok = 0;
+            const long wstep = a.ww ? (long)k2 * 4096 : 32;  // bytes a stage adds to a weight source
 #pragma unroll
             for (int q = 0; q < 9; ++q) {
                 tsrc[q] = a.w;
                 if (q < k2) {
                     const int u = (cw + 4 * q) * 64 + lane;
                     const int tap = u >> 8, col = n0 + ((u >> 1) & 127);
-                    if (col < g.cout) {
+                    if (a.ww) {
+                        tsrc[q] = a.ww + ((long)tn * nst * k2 * 256 + u) * 16;
+                        tok |= 1u << q;
+                    } else if (col < g.cout) {
                         tsrc[q] = a.w + (((long)col * k2 + tap) * g.cin + 8 * th) * ES;
                         tok |= 1u << q;
                     }
@@ -601,7 +610,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
             }
             const uint8_t *const zero = (const uint8_t *)&k_zero16;
             auto stage = [&](int st, int buf) __attribute__((always_inline)) {
-                const long dl = (long)st * 32;
+                const long dl = (long)st * 32, dw = (long)st * wstep;
                 const bool hi_out = st * 16 + 8 >= g.cin;  // channels 8..15 of the stage past c_in
                 uint8_t *const wb = smem + buf * buf_bytes;
 #pragma unroll
@@ -618,7 +627,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_layer_wide(LayerArgs a) {
                     if (q < k2) {
                         const bool ok = ((tok >> q) & 1) && !(hi_out && th == 1);
                         __builtin_amdgcn_global_load_lds(
-                            ok ? tsrc[q] + dl : zero,
+                            ok ? tsrc[q] + dw : zero,
                             (__attribute__((address_space(3))) void *)(wb + c.w_wofs + (cw + 4 * q) * 1024), 16, 0,
                             0);
                     }
@@ -834,12 +843,48 @@ static hipError_t launch_wide_k(const LayerArgs &args, hipStream_t st) {
 
 hipError_t launch_layer_wide(int dt, const void *src, const void *w, const float *bias, const int32_t *idx,
                              const int32_t *count, void *dst, const void *cache, const Geo &g, const LayerCfg &cfg,
-                             const CopyCfg &cc, hipStream_t st, float *ws) {
+                             const CopyCfg &cc, hipStream_t st, float *ws, const void *ww) {
     const LayerArgs a{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
-                      (const uint8_t *)cache, nullptr, nullptr, g, cfg, cc, cfg.w_pmax > 1 ? ws : nullptr};
+                      (const uint8_t *)cache, nullptr, nullptr, g, cfg, cc, cfg.w_pmax > 1 ? ws : nullptr,
+                      (const uint8_t *)ww};
     const bool tail = cc.nvec > 0;
     if (dt == 1) return tail ? launch_wide_k<1, true>(a, st) : launch_wide_k<1, false>(a, st);
     return tail ? launch_wide_k<2, true>(a, st) : launch_wide_k<2, false>(a, st);
+}
+
+// The stage-major copy of KRSC weights that the wide tiles stage from: for N
+// tile tn (128 output channels), stage s (16 input channels), tap t, column n
+// and channel half h, the 8 channels 16s + 8h .. of output channel 128 tn + n
+// at tap t sit at 16-byte unit ((tn * nst + s) * k*k + t) * 256 + 2n +
+// (h ^ (n/8 mod 2)) -- the order of the stage's weights in LDS -- and zeros
+// stand for output channels past c_out and input channels past c_in.  One
+// thread per unit; c_in is a multiple of 8, so a unit is all valid or all zero.
+__global__ __launch_bounds__(256) void k_wide_weights_pack(const uint8_t *__restrict__ w, Geo g, uint8_t *ww,
+                                                           long units) {
+    const int k2 = g.k * g.k, nst = (g.cin + 15) / 16;
+    for (long v = (long)blockIdx.x * 256 + threadIdx.x; v < units; v += (long)gridDim.x * 256) {
+        const int u = (int)(v % (k2 * 256));
+        const long ts = v / (k2 * 256);
+        const int s = (int)(ts % nst), tn = (int)(ts / nst);
+        const int tap = u >> 8, n = (u >> 1) & 127, h = (u & 1) ^ ((n >> 3) & 1);
+        const int col = tn * kLayerWideCols + n, ch = s * 16 + h * 8;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (col < g.cout && ch < g.cin) x = ld16(w + (((size_t)col * k2 + tap) * g.cin + ch) * 2);
+        *(u32x4 *)(ww + v * 16) = x;
+    }
+}
+
+long wide_weights_units(const Geo &g) {
+    return (long)((g.cout + kLayerWideCols - 1) / kLayerWideCols) * ((g.cin + 15) / 16) * g.k * g.k * 256;
+}
+
+hipError_t launch_wide_weights_pack(const void *w, const Geo &g, void *ww, int cus, hipStream_t st) {
+    const long units = wide_weights_units(g);
+    long grid = (units + 255) / 256;
+    if (grid > 4L * cus) grid = 4L * cus;
+    hipLaunchKernelGGL(k_wide_weights_pack, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, st,
+                       (const uint8_t *)w, g, (uint8_t *)ww, units);
+    return hipGetLastError();
 }
 
 // Workgroups of `kernel` resident on one CU with `lds` bytes of dynamic LDS

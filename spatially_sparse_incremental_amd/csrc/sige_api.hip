@@ -1175,9 +1175,19 @@ int sige_sparse_conv_layer_plan(const sige_geom *gp, int dtype, sige_layer_plan 
     return SIGE_OK;
 }
 
-int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
-                                const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
-                                int copy_cached, void *workspace, int64_t workspace_bytes, void *stream) {
+// The stage-major weights of the wide tiles: bytes for geometry g (0 when the
+// wide tiles cannot run on it).
+static int64_t wide_weights_bytes(const Geo &g, int dtype) {
+    if (dtype == SIGE_F32) return 0;
+    sige::LayerCfg lc;
+    if (choose_layer(g, dtype, &lc) != SIGE_OK) return 0;  // no layer kernel, so no wide tiles
+    return lc.w_lds > 0 ? (int64_t)sige::wide_weights_units(g) * 16 : 0;
+}
+
+static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                      const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                      int copy_cached, void *workspace, int64_t workspace_bytes, const void *w_wide,
+                      int64_t w_wide_bytes, void *stream) {
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
     Geo g;
     int rc = derive(gp, &g);
@@ -1208,6 +1218,15 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
         const Region wr[] = {{out, obytes}, {workspace, (size_t)p.ws_bytes}};
         if (regions_overlap(wr, 2, rd, 6)) return fail(SIGE_EINVAL, "the workspace overlaps another argument");
     }
+    const int64_t wwb = w_wide ? wide_weights_bytes(g, dtype) : 0;
+    if (w_wide && wwb > 0) {  // the wide tiles stage their weights from the stage-major copy
+        if (!aligned(w_wide, 16)) return fail(SIGE_EALIGN, "w_wide must be 16-byte aligned");
+        if (w_wide_bytes < wwb)
+            return fail(SIGE_ERANGE, "w_wide of %lld bytes, %lld needed", (long long)w_wide_bytes, (long long)wwb);
+        const Region wr[] = {{out, obytes}, {workspace, (size_t)(p.ws_bytes > 0 ? p.ws_bytes : 0)}};
+        const Region ww[] = {{w_wide, (size_t)wwb}};
+        if (regions_overlap(wr, 2, ww, 1)) return fail(SIGE_EINVAL, "w_wide overlaps out or the workspace");
+    }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
     const hipStream_t st = (hipStream_t)stream;
@@ -1221,7 +1240,8 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
     }
     if (p.wide_min <= g.cap) {  // the wide tiles: lists of at least wide_min blocks
         if ((rc = finish(sige::launch_layer_wide(dtype, a_edit, w_krsc, bias, idx, count, out,
-                                                 copy_cached ? cached : nullptr, g, p.lc, cc, st, (float *)workspace),
+                                                 copy_cached ? cached : nullptr, g, p.lc, cc, st, (float *)workspace,
+                                                 wwb > 0 ? w_wide : nullptr),
                          "sige_sparse_conv_layer_auto", st)))
             return rc;
     }
@@ -1231,6 +1251,54 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
                                         (float *)workspace),
                       "sige_sparse_conv_layer_auto", st);
     return SIGE_OK;
+}
+
+int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                                int copy_cached, void *workspace, int64_t workspace_bytes, void *stream) {
+    return layer_auto(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, workspace,
+                      workspace_bytes, nullptr, 0, stream);
+}
+
+int sige_sparse_conv_layer_auto_packed(const void *a_edit, const void *w_krsc, const float *bias,
+                                       const void *cached, const int32_t *idx, const int32_t *count, int dtype,
+                                       const sige_geom *gp, void *out, int copy_cached, void *workspace,
+                                       int64_t workspace_bytes, const void *w_wide, int64_t w_wide_bytes,
+                                       void *stream) {
+    if (!w_wide) return fail(SIGE_EINVAL, "NULL pointer");
+    return layer_auto(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, workspace,
+                      workspace_bytes, w_wide, w_wide_bytes, stream);
+}
+
+int64_t sige_wide_weights_bytes(const sige_geom *gp, int dtype) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    const int rc = derive(gp, &g);
+    if (rc) return rc;
+    return wide_weights_bytes(g, dtype);
+}
+
+int sige_wide_weights_pack(const void *w_krsc, int dtype, const sige_geom *gp, void *w_wide, int64_t w_wide_bytes,
+                           void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    if (dtype == SIGE_F32) return fail(SIGE_EDTYPE, "the wide tiles run on 16-bit types only");
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!w_krsc || !w_wide) return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(w_krsc, 16) || !aligned(w_wide, 16)) return fail(SIGE_EALIGN, "weights must be 16-byte aligned");
+    const int64_t need = wide_weights_bytes(g, dtype);
+    if (need == 0) return fail(SIGE_ERANGE, "no wide tiles for this geometry");
+    if (w_wide_bytes < need)
+        return fail(SIGE_ERANGE, "w_wide of %lld bytes, %lld needed", (long long)w_wide_bytes, (long long)need);
+    const Region rd[] = {{w_krsc, (size_t)g.cout * g.k * g.k * g.cin * 2}};
+    const Region wr[] = {{w_wide, (size_t)need}};
+    if (regions_overlap(wr, 1, rd, 1)) return fail(SIGE_EINVAL, "w_wide overlaps w_krsc");
+    if ((rc = device_ready())) return rc;
+    const hipStream_t st = (hipStream_t)stream;
+    return finish(sige::launch_wide_weights_pack(w_krsc, g, w_wide, dev_info().cus, st), "sige_wide_weights_pack",
+                  st);
 }
 
 int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *gp, int dtype) {

@@ -147,9 +147,15 @@ hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const
 // With cfg.w_pmax > 1 a short list's tiles are split over K into parts whose
 // fp32 partials go to ws (cfg.w_ws_items tiles), and a second launch adds
 // them up into dst.
+// ww: the weights in the wide tiles' stage-major order (launch_wide_weights_pack), or
+// NULL to stage them from the KRSC weights w.
 hipError_t launch_layer_wide(int dt, const void *src, const void *w, const float *bias, const int32_t *idx,
                              const int32_t *count, void *dst, const void *cache, const Geo &g, const LayerCfg &cfg,
-                             const CopyCfg &cc, hipStream_t st, float *ws);
+                             const CopyCfg &cc, hipStream_t st, float *ws, const void *ww);
+// The stage-major copy of KRSC weights (16-bit types) for the wide tiles: 16-byte units
+// of it, and the launch that writes it.
+long wide_weights_units(const Geo &g);
+hipError_t launch_wide_weights_pack(const void *w, const Geo &g, void *ww, int cus, hipStream_t st);
 // Bytes of that workspace for g and the launch configuration c (< 0: unknown tile shape).
 long split_workspace_bytes(int dt, const Geo &g, const ConvCfg &c);
 hipError_t launch_restore(const int32_t *prev_idx, const int32_t *prev_count, const int32_t *idx,

@@ -469,3 +469,41 @@ def test_auto_layer_validation(lib):
     assert f(*args, _v(D + 4096), need, s) == EINVAL  # the workspace overlaps out
     assert f(None, _v(B), None, None, _v(C), _v(C + 4096), 2, ctypes.byref(g), _v(D), 0, _v(E), need, s) == EINVAL
     assert f(*args[:6], 7, *args[7:], _v(E), need, s) == EDTYPE
+
+
+def test_wide_weights_pack_and_packed_auto_validation(lib):
+    """The stage-major weight copy: its size (the KRSC size when c_out is a
+    multiple of 128 and c_in of 16, padded otherwise; 0 without wide tiles),
+    and the checks of the pack call and of the packed auto layer before any
+    device work (fp32 SIGE_EDTYPE, short buffers and layers without wide tiles
+    SIGE_ERANGE, NULL and overlapping pointers SIGE_EINVAL, misalignment
+    SIGE_EALIGN; a valid call without a GPU SIGE_ENODEV)."""
+    g = _g(1, 32, 64, 1024, 1024, 3, 1, 1, 4)
+    need = lib.sige_wide_weights_bytes(ctypes.byref(g), 1)
+    assert need == 1024 * 9 * 1024 * 2
+    assert lib.sige_wide_weights_bytes(ctypes.byref(_g(1, 64, 64, 24, 136, 3, 1, 1, 6)), 2) == \
+        2 * 2 * 9 * 256 * 16  # c_out 136 -> two N tiles, c_in 24 -> two stages
+    assert lib.sige_wide_weights_bytes(ctypes.byref(_g(1, 64, 64, 64, 64, 1, 1, 0, 4)), 1) == 1 * 4 * 1 * 256 * 16
+    assert lib.sige_wide_weights_bytes(ctypes.byref(g), 0) == 0  # fp32: no wide tiles
+    assert lib.sige_wide_weights_bytes(ctypes.byref(_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)), 2) == 0
+    assert lib.sige_wide_weights_bytes(ctypes.byref(g), 7) == EDTYPE
+    s = _v(0)
+    pack = lib.sige_wide_weights_pack
+    assert pack(_v(A), 1, ctypes.byref(g), _v(B), need, s) == ENODEV
+    assert pack(_v(A), 0, ctypes.byref(g), _v(B), need, s) == EDTYPE
+    assert pack(_v(A), 1, ctypes.byref(g), _v(B), need - 16, s) == ERANGE
+    assert pack(None, 1, ctypes.byref(g), _v(B), need, s) == EINVAL
+    assert pack(_v(A), 1, ctypes.byref(g), None, need, s) == EINVAL
+    assert pack(_v(A), 1, ctypes.byref(g), _v(A + 4096), need, s) == EINVAL  # overlaps the KRSC weights
+    assert pack(_v(A + 8), 1, ctypes.byref(g), _v(B), need, s) == EALIGN
+    assert pack(_v(A), 2, ctypes.byref(_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)), _v(B), need, s) == ERANGE
+
+    f = lib.sige_sparse_conv_layer_auto_packed
+    ws = ssi.sige_sparse_conv_layer_plan(g, torch.bfloat16).workspace_bytes
+    args = (_v(A), _v(B), None, None, _v(C), _v(C + 4096), 1, ctypes.byref(g), _v(D), 0, _v(E), ws)
+    assert f(*args, _v(A + (5 << 36)), need, s) == ENODEV
+    assert f(*args, None, need, s) == EINVAL
+    assert f(*args, _v(A + (5 << 36)), need - 16, s) == ERANGE
+    assert f(*args, _v(A + (5 << 36) + 8), need, s) == EALIGN
+    assert f(*args, _v(D + 64), need, s) == EINVAL  # overlaps out
+    assert f(*args, _v(E + 64), need, s) == EINVAL  # overlaps the workspace

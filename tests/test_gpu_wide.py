@@ -214,3 +214,118 @@ def test_wide_tiles_write_nothing_outside_out(cin, monkeypatch):
         act[lst.long()] = 1
         sel = active_pixels(act.view(n, nby, nbx), b, ho, wo).expand_as(out).cuda()
         assert torch.equal(out[~sel].view(torch.uint8), cache[~sel].view(torch.uint8)), f"{cnt} blocks: unlisted"
+
+
+def _packed_reference(wk, cin, cout, k):
+    """The stage-major layout written out from its definition, on the CPU: unit
+    ((tn * nst + s) * k*k + t) * 256 + 2n + (h xor (n/8 mod 2)) holds the 8
+    channels 16s + 8h .. of output channel 128 tn + n at tap t, zeros outside
+    the weights."""
+    ntn, nst, k2 = (cout + 127) // 128, (cin + 15) // 16, k * k
+    w = wk.view(cout, k2, cin)
+    ref = torch.zeros(ntn, nst, k2, 256, 8, dtype=wk.dtype)
+    for u in range(256):
+        n = (u >> 1) & 127
+        h = (u & 1) ^ ((n >> 3) & 1)
+        for tn in range(ntn):
+            col = tn * 128 + n
+            if col >= cout:
+                continue
+            for s in range(nst):
+                ch = s * 16 + h * 8
+                if ch < cin:
+                    ref[tn, s, :, u, :] = w[col, :, ch:ch + 8]
+    return ref.reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [(24, 136, 3), (48, 128, 1), (200, 136, 3), (256, 64, 3)],
+                         ids=["cin24_cout136", "pointwise", "cin200", "cin256_cout64"])
+def test_wide_weights_pack_layout(shape):
+    """sige_wide_weights_pack against the layout written out on the CPU, bit for
+    bit, with a guard canary after the packed buffer."""
+    cin, cout, k = shape
+    g = ssi.geom(1, 40, 44, cin, cout, k, 1, k // 2, 6)
+    dt = torch.bfloat16
+    wt = rand((cout, cin, k, k), dt, 71)
+    wk = ssi.weight_to_krsc(wt)
+    need = ssi.sige_wide_weights_bytes(g, dt)
+    assert need == ((cout + 127) // 128) * ((cin + 15) // 16) * k * k * 4096
+    buf = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    ssi.sige_wide_weights_pack(wk.cuda(), g, out=buf[:need])
+    torch.cuda.synchronize()
+    assert (buf[need:] == 0x5A).all(), "writes past the packed buffer"
+    got = buf[:need].cpu().view(torch.int16)
+    ref = _packed_reference(wk, cin, cout, k).view(torch.int16)
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_packed_weights_give_the_same_layer(case, monkeypatch):
+    """sige_sparse_conv_layer_auto_packed equals sige_sparse_conv_layer_auto bit
+    for bit (the same weights reach the same LDS slots), on every forced-wide
+    geometry (K splits included) and list length, with and without the copy."""
+    name, n, h, w, cin, cout, k, s, p, b, dts = case
+    dt = DT[dts]
+    g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
+    plan = _forced_plan(g, dt, monkeypatch)
+    ho, wo, nby, nbx, _ = oracle.geometry(h, w, k, s, p, b)
+    cap = n * nby * nbx
+    mask = random_mask(n, h, w, 0.5, 3)
+    _, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 5, mask)
+    cache = rand((n, ho, wo, cout), dt, 7)
+    wk, bg, ag, cg = ssi.weight_to_krsc(wt).cuda(), bias.cuda(), a_e.cuda(), cache.cuda()
+    ww = ssi.sige_wide_weights_pack(wk, g)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    for lst in _lists(cap, 13):
+        cnt = lst.numel()
+        idx = torch.zeros(cap, dtype=torch.int32)
+        idx[:cnt] = lst
+        idx_g, count = idx.cuda(), torch.tensor([cnt], dtype=torch.int32, device="cuda")
+        print(f"[case] {name} packed: {cnt} of {cap} blocks", flush=True)
+        for copy in (True, False):
+            o1 = cg.clone()
+            o2 = cg.clone()
+            ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg if copy else None, idx_g, count, g, out=o1,
+                                            copy_cached=copy, workspace=ws)
+            ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg if copy else None, idx_g, count, g, out=o2,
+                                            copy_cached=copy, workspace=ws, w_wide=ww)
+            assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), f"{name} {cnt} blocks copy={copy}"
+
+
+@pytest.mark.parametrize("layer,cnt", [("g32x64", 64), ("g64x128", 252), ("g256x512", 1400)])
+def test_packed_weights_on_gaugan_layers(layer, cnt):
+    """The GauGAN-shaped layers at the list lengths of the 15-30% edits, on the
+    library's own plan (the wide tiles, split over K for the deep layers): the
+    packed entry point equals the KRSC one bit for bit, and the oracle on
+    sampled blocks."""
+    import synth
+
+    assert "SIGE_WIDE_MIN" not in os.environ
+    L = [x for x in synth.workload("gaugan_4conv_bf16").layers if x.name == layer][0]
+    dt = torch.bfloat16
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    plan = ssi.sige_sparse_conv_layer_plan(g, dt)
+    assert plan.wide_min <= cnt <= plan.wide_max, plan.as_dict()
+    ho, wo, nby, nbx, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
+    a_e = synth.make_activation(1, L.h, L.w, L.c_in, "bf16", 81)
+    wt, bias = synth.make_layer_tensors(L, 83)
+    cache = synth.make_activation(1, ho, wo, L.c_out, "bf16", 85)
+    ag, wk, bg, cg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache.cuda()
+    ww = ssi.sige_wide_weights_pack(wk, g)
+    gen = torch.Generator().manual_seed(87)
+    lst = torch.randperm(plan.cap, generator=gen)[:cnt].sort().values.to(torch.int32)
+    idx = torch.zeros(plan.cap, dtype=torch.int32)
+    idx[:cnt] = lst
+    idx, count = idx.cuda(), torch.tensor([cnt], dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    print(f"[case] {layer} packed: {cnt} of {plan.cap} blocks", flush=True)
+    o1 = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg, idx, count, g, workspace=ws)
+    o2 = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg, idx, count, g, workspace=ws, w_wide=ww)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8))
+    sub = torch.zeros(plan.cap, dtype=torch.uint8)
+    sub[lst[torch.randperm(cnt, generator=gen)[:4]].long()] = 1
+    sub = sub.view(1, nby, nbx)
+    out = o2.cpu()
+    r64 = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, sub, out, out_f64=True)
+    assert_close(out, r64, dt, active_pixels(sub, L.block, ho, wo), f"{layer} packed, sampled blocks")
