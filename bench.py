@@ -106,12 +106,17 @@ def main():
     g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
     d = ssi.sige_geom_derive(g)
     cap = d.cap
+    # the layer's weights packed once in the fused kernel's load order (a per-layer
+    # preparation like the OIHW -> KRSC permute, outside every timing); the fused
+    # layer calls below read them (sige_sparse_conv_layer_packed)
+    w_packed = ssi.sige_pack_weights(w_krsc, g)
 
     # cache = conv(A_o), computed once (untimed) by the library with every block active
     idx_all = torch.arange(cap, dtype=torch.int32, device=dev)
     cnt_all = torch.tensor([cap], dtype=torch.int32, device=dev)
     cache = torch.empty((1, d.ho, d.wo, L.c_out), dtype=dt, device=dev)
-    ssi.sige_sparse_conv_layer(a_o, w_krsc, bias, None, idx_all, cnt_all, g, out=cache, copy_cached=False)
+    ssi.sige_sparse_conv_layer(a_o, w_krsc, bias, None, idx_all, cnt_all, g, out=cache, copy_cached=False,
+                               w_packed=w_packed)
 
     mask = torch.empty((1, L.h, L.w), dtype=torch.uint8, device=dev)
     mbits = torch.empty((L.h * L.w // 32,), dtype=torch.int32, device=dev)  # the mask, one bit per pixel
@@ -124,7 +129,8 @@ def main():
         # runs on the idle workgroups of the single-workgroup reduce
         ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits, stream=st)
         ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=count, stream=st)
-        ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False, stream=st)
+        ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False, stream=st,
+                                   w_packed=w_packed)
 
     K, W = args.steps, args.warmup
     for _ in range(W):
@@ -215,7 +221,7 @@ def main():
         "reduce_copy": graph_time(lambda: ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out,
                                                                     idx=idx, count=count)),
         "fused_layer": graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g,
-                                                                     out=out, copy_cached=False)),
+                                                                     out=out, copy_cached=False, w_packed=w_packed)),
     }
     # the three-call path's kernels on the same list (separate launches, block tensors in HBM)
     blocks = torch.empty((cap, d.ib, d.ib, L.c_in), dtype=dt, device=dev)
@@ -232,7 +238,7 @@ def main():
                  lambda: ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx,
                                                    count=count),
                  lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out,
-                                                    copy_cached=False),
+                                                    copy_cached=False, w_packed=w_packed),
                  lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks),
                  lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks),
                  lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)]
@@ -263,13 +269,15 @@ def main():
         def step_conv_copy():
             ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
             ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count)
-            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g, out=out_c, copy_cached=True)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g, out=out_c, copy_cached=True,
+                                       w_packed=w_packed)
 
         t_step_conv_copy = graph_time(step_conv_copy, 5, 40)
 
         def layer_only():  # the per-layer part of the step: reduce (with the copy) and the fused layer
             ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=count)
-            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False,
+                                       w_packed=w_packed)
 
         t_layer = graph_time(layer_only, 5, 40)
         t_reduce = graph_time(lambda: ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count))
@@ -277,12 +285,13 @@ def main():
         def step_bytes():  # the step with the change mask as bytes
             ssi.sige_diff_mask(a_o, a_e, wl.tau, mask=mask)
             ssi.sige_reduce_mask_copy(mask, g, L.dilate, cache, out=out, idx=idx, count=count)
-            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out, copy_cached=False,
+                                       w_packed=w_packed)
 
         t_step_bytes = graph_time(step_bytes, 5, 40)
         t_reduce_bytes = graph_time(lambda: ssi.sige_reduce_mask(mask, g, L.dilate, idx=idx, count=count))
         t_fused_copy = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, idx, count, g,
-                                                                     out=out_c, copy_cached=True))
+                                                                     out=out_c, copy_cached=True, w_packed=w_packed))
 
         # the step without the cache copy (persistent output buffer)
         out_persist = cache.clone()
@@ -290,7 +299,8 @@ def main():
         def step_nocopy():
             ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
             ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count)
-            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False)
+            ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out_persist, copy_cached=False,
+                                       w_packed=w_packed)
 
         # the three-call path
         def step_three():
@@ -305,7 +315,8 @@ def main():
         # dense comparators on the same GPU
         dense_all = torch.empty_like(cache)
         t_dense_ours = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx_all, cnt_all, g,
-                                                                     out=dense_all, copy_cached=False), 5, 10)
+                                                                     out=dense_all, copy_cached=False,
+                                                                     w_packed=w_packed), 5, 10)
 
         def timed_eager(fn, reps):
             for _ in range(min(10, reps)):
@@ -349,7 +360,7 @@ def main():
             else:
                 ssi.sige_restore_blocks(seq_idx[prv], seq_cnt[prv], seq_idx[cur], seq_cnt[cur], g, cache, seq_out)
                 ssi.sige_sparse_conv_layer(seq_edits[cur], w_krsc, bias, None, seq_idx[cur], seq_cnt[cur], g,
-                                           out=seq_out, copy_cached=False)
+                                           out=seq_out, copy_cached=False)  # KRSC, as the one-launch restore
 
         # both edits per call, so that graph replays keep the alternation
         t_seq = graph_time(lambda: (seq_step(0, True), seq_step(1, True)), 5, 40) / 2
@@ -383,7 +394,7 @@ def main():
         def step_bbox_tiles():
             ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
             ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, cache, bbox_idx, bbox_cnt, g, out=bbox_out,
-                                       copy_cached=True)
+                                       copy_cached=True, w_packed=w_packed)
 
         t_bbox_tiles = graph_time(step_bbox_tiles, 5, 40)
 
@@ -494,7 +505,8 @@ def main():
         "unit": "us per incremental layer update (diff + reduce with the cache copy + fused sparse conv)",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(step_ms, 6),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": L.dtype,
-        "data": "synthetic: seeded 3-ellipse blob edit, N(0,1) activations, He-normal weights",
+        "data": "synthetic: seeded 3-ellipse blob edit, N(0,1) activations, He-normal weights (packed once per "
+                "layer in the fused kernel's load order by sige_pack_weights, outside the timed region)",
         "config": {"workload": "unet_256x256x128_bf16_3x3s1_b6_d1_blob1.2pct", "n": 1, "h": L.h, "w": L.w,
                    "c_in": L.c_in, "c_out": L.c_out, "k": L.k, "stride": L.stride, "block": L.block,
                    "dilate": L.dilate, "seed": seed, "edit_fraction": round(edit_frac, 5),
@@ -805,7 +817,7 @@ def _chain_comparator(torch, F, ssi, synth, graph_time, seed):
                            w_cl=w_cpu.to(dev).contiguous(memory_format=torch.channels_last),
                            b16=b_cpu.to(dev).to(a_e.dtype), mbits=mbits))
         ly = layers[-1]
-        ly["ww"] = ssi.sige_wide_weights_pack(ly["wk"], g) if ssi.sige_wide_weights_bytes(g, a_e.dtype) > 0 else None
+        ly["wp"] = ssi.sige_pack_weights(ly["wk"], g)
     blocks = []
 
     def sparse_chain():
@@ -910,7 +922,7 @@ def _chain_conv(ssi, ly, x):
     copy), by ly["mode"]: the library's choice, or one kernel."""
     if ly["mode"] == "auto":
         ssi.sige_sparse_conv_layer_auto(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
-                                        out=ly["out"], copy_cached=False, workspace=ly["ws"], w_wide=ly["ww"])
+                                        out=ly["out"], copy_cached=False, workspace=ly["ws"], w_packed=ly["wp"])
     elif ly["mode"] == "split":
         ssi.sige_sparse_conv_layer_split(x, ly["wk"], ly["bias"], None, ly["idx"], ly["cnt"], ly["g"],
                                          out=ly["out"], copy_cached=False, workspace=ly["ws"])
@@ -924,9 +936,9 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     0.5 / 1.2 / 5 / 15 / 30% of the frame: the reduce (mask one bit per pixel,
     the cache copy on its idle workgroups) + sige_sparse_conv_layer_auto (the
     kernel the library picks; `path`: split, single (64 x 32 tiles) or wide
-    (256 x 128 tiles, staging their weights from the stage-major copy that
-    sige_wide_weights_pack makes once per layer, outside the timing)), against
-    the dense conv through torch/MIOpen;
+    (256 x 128 tiles); the weights packed once per layer by
+    sige_pack_weights, outside the timing), against the dense conv through
+    torch/MIOpen;
     best_of_two_bound: the faster of the single-range and split kernels (the
     two with entry points of their own) timed on the very edit, which a caller
     cannot do."""
@@ -940,7 +952,7 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
         g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
         cache = synth.make_activation(1, L.h, L.w, L.c_out, L.dtype, seed + li + 50).to(dev)
         wk = ssi.weight_to_krsc(w_cpu).to(dev)
-        ww = ssi.sige_wide_weights_pack(wk, g) if ssi.sige_wide_weights_bytes(g, a_o.dtype) > 0 else None
+        ww = ssi.sige_pack_weights(wk, g)
         prep.append((L, g, a_o, wk, b_cpu.to(dev), cache,
                      w_cpu.to(dev).contiguous(memory_format=torch.channels_last), ww))
         with torch.no_grad():
@@ -963,7 +975,7 @@ def _gaugan_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
             def auto():
                 ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)
                 ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, None, idx, cnt, g, out=out, copy_cached=False,
-                                                workspace=ws_auto, w_wide=ww)
+                                                workspace=ws_auto, w_packed=ww)
 
             def one():
                 ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cache, out=out, idx=idx, count=cnt)

@@ -301,47 +301,56 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
                                 const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                                 int copy_cached, void *workspace, int64_t workspace_bytes, void *stream);
 
-/* The wide tiles' weights in stage-major order.  A wide tile stages, for each
- * 16 input channels, the weights of its 128 output channels at every tap
- * (nubint.ai review, "ABSTRACT": large edits; the tiles of
- * sige_sparse_conv_layer_auto).  From KRSC weights each 1 KiB staging load
- * gathers 32 bytes of each of 32 output channels; from this copy it reads
- * 1 KiB in a row (measured on MI355X: about 9% off the wide tiles' time on
- * the GauGAN-shaped layers).  Layout (bf16 or fp16): for N tile tn (output
- * channels 128 tn .. 128 tn + 127), stage s (input channels 16 s .. 16 s +
- * 15), tap t = ky * k + kx, column n < 128 and half h < 2, the 8 values
- * W[128 tn + n][ky][kx][16 s + 8 h .. 16 s + 8 h + 7] fill the 16-byte unit
- * ((tn * ceil(c_in / 16) + s) * k * k + t) * 256 + 2 n + (h XOR ((n / 8) mod 2))
- * -- the order in which a stage sits in LDS -- and units of output channels
- * >= c_out or input channels >= c_in hold zeros.
- *   sige_wide_weights_bytes: the size of that copy for the geometry and dtype
- *   (0 when the wide tiles cannot run on it: fp32, k > 3, or windows and
- *   weights that do not fit in LDS; a negative status code for invalid
- *   arguments).
- *   sige_wide_weights_pack: writes it from w_krsc (the KRSC weights of
- *   sige_sparse_conv_layer) into w_wide, caller-owned device memory of
- *   w_wide_bytes >= sige_wide_weights_bytes, 16-byte aligned and not
+/* A layer's weights packed once in the order the layer kernels load them.
+ * From KRSC weights a 1 KiB load of the single-range kernel gathers 32 bytes
+ * of each of 32 output channels (two lanes per channel: a K slice's weight
+ * fragment of the 32x32 MFMA), and a staging load of the wide tiles
+ * (nubint.ai review, "ABSTRACT": large edits) 32 bytes of each of 32 output
+ * channels of a 16-channel stage; from the packed copy every such load reads
+ * 1 KiB in a row.  Measured on MI355X: the 1.2% single-range layer of the
+ * 256x256x128 U-Net conv about 9% faster, the wide tiles 6-10%.
+ * The copy has two sections, both in the library's own load order for the
+ * geometry and dtype (they follow the kernel configuration the library picks,
+ * so a copy is valid for that geometry, dtype and library build only):
+ *   - the single-range kernel's: for chunk ch of the K range, N tile tn of
+ *     the layer's output-channel tiles, K step s of the chunk (tap, K slice),
+ *     N subtile q and lane l, the 16 bytes that lane loads from w_krsc
+ *     (output channels past c_out and input channels past c_in clamped as the
+ *     kernel clamps them), at unit (((ch * tiles + tn) * steps + s) *
+ *     subtiles + q) * 64 + l;
+ *   - from the next 256-byte boundary, for 16-bit types where the wide tiles
+ *     can run (k <= 3, the stage buffers within the LDS): for N tile tn of
+ *     128 output channels, stage s of 16 input channels, tap t = ky * k + kx,
+ *     column n < 128 and half h < 2, the 8 values W[128 tn + n][ky][kx][16 s
+ *     + 8 h .. + 7] at unit ((tn * ceil(c_in / 16) + s) * k * k + t) * 256 +
+ *     2 n + (h XOR ((n / 8) mod 2)), zeros past c_out and c_in.
+ *   sige_packed_weights_bytes: the size of the copy (a negative status code
+ *   for invalid arguments).
+ *   sige_pack_weights: writes it from w_krsc (the KRSC weights of
+ *   sige_sparse_conv_layer) into w_packed, caller-owned device memory of
+ *   w_packed_bytes >= sige_packed_weights_bytes, 256-byte aligned, not
  *   overlapping w_krsc; enqueued on `stream`, nothing synchronised or
- *   allocated.  SIGE_EDTYPE for fp32, SIGE_ERANGE when the geometry has no
- *   wide tiles or w_wide_bytes is too small, SIGE_EINVAL / SIGE_EALIGN for
- *   NULL, overlapping or misaligned pointers.  A layer's weights are packed
- *   once and reused by every call. */
-int64_t sige_wide_weights_bytes(const sige_geom *g, int dtype);
-int sige_wide_weights_pack(const void *w_krsc, int dtype, const sige_geom *g, void *w_wide, int64_t w_wide_bytes,
-                           void *stream);
+ *   allocated.  SIGE_ERANGE when w_packed_bytes is too small, SIGE_EINVAL /
+ *   SIGE_EALIGN for NULL, overlapping or misaligned pointers. */
+int64_t sige_packed_weights_bytes(const sige_geom *g, int dtype);
+int sige_pack_weights(const void *w_krsc, int dtype, const sige_geom *g, void *w_packed, int64_t w_packed_bytes,
+                      void *stream);
 
-/* sige_sparse_conv_layer_auto with the wide tiles staging their weights from
- * w_wide (sige_wide_weights_pack of the same w_krsc) instead of w_krsc; the
- * single-range kernel and the split still read w_krsc.  Same arguments,
- * checks and result as sige_sparse_conv_layer_auto, bit for bit (the same
- * values reach the same LDS slots in the same order).  w_wide: non-NULL
- * (SIGE_EINVAL), 16-byte aligned (SIGE_EALIGN), w_wide_bytes at least
- * sige_wide_weights_bytes (SIGE_ERANGE), not overlapping out or the workspace
- * (SIGE_EINVAL); not read when the geometry has no wide tiles. */
+/* sige_sparse_conv_layer and sige_sparse_conv_layer_auto with the
+ * single-range kernel and the wide tiles loading their weights from w_packed
+ * (sige_pack_weights of the same w_krsc) instead of w_krsc; the split still
+ * reads w_krsc.  Same arguments, checks and result as the unpacked calls, bit
+ * for bit (the same values reach the same registers and LDS slots in the same
+ * order).  w_packed: non-NULL (SIGE_EINVAL), 256-byte aligned (SIGE_EALIGN),
+ * w_packed_bytes at least sige_packed_weights_bytes (SIGE_ERANGE), not
+ * overlapping out or the workspace (SIGE_EINVAL). */
+int sige_sparse_conv_layer_packed(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                  const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
+                                  int copy_cached, const void *w_packed, int64_t w_packed_bytes, void *stream);
 int sige_sparse_conv_layer_auto_packed(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                                        const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g,
                                        void *out, int copy_cached, void *workspace, int64_t workspace_bytes,
-                                       const void *w_wide, int64_t w_wide_bytes, void *stream);
+                                       const void *w_packed, int64_t w_packed_bytes, void *stream);
 
 /* sige_sparse_conv_layer_split without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving

@@ -23,7 +23,8 @@ EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce
            "sige_sparse_conv_layer_split", "sige_sparse_conv_layer_split_workspace",
            "sige_sparse_conv_layer_split_noalloc", "sige_noalloc_scratch_bytes",
            "sige_sparse_conv_layer_plan", "sige_sparse_conv_layer_auto",
-           "sige_wide_weights_bytes", "sige_wide_weights_pack", "sige_sparse_conv_layer_auto_packed",
+           "sige_packed_weights_bytes", "sige_pack_weights", "sige_sparse_conv_layer_packed",
+           "sige_sparse_conv_layer_auto_packed",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
            "sige_sparse_attention_workspace", "sige_sparse_attention", "sige_strerror",
@@ -92,9 +93,10 @@ def lib():
         L.sige_sparse_conv_layer_split_noalloc.argtypes = [V, V, V, V, V, V, I, P, V, I, V]
         L.sige_sparse_conv_layer_plan.argtypes = [P, I, ctypes.POINTER(LayerPlan)]
         L.sige_sparse_conv_layer_auto.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
-        L.sige_wide_weights_bytes.argtypes = [P, I]
-        L.sige_wide_weights_bytes.restype = ctypes.c_int64
-        L.sige_wide_weights_pack.argtypes = [V, I, P, V, ctypes.c_int64, V]
+        L.sige_packed_weights_bytes.argtypes = [P, I]
+        L.sige_packed_weights_bytes.restype = ctypes.c_int64
+        L.sige_pack_weights.argtypes = [V, I, P, V, ctypes.c_int64, V]
+        L.sige_sparse_conv_layer_packed.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
         L.sige_sparse_conv_layer_auto_packed.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V,
                                                          ctypes.c_int64, V]
         L.sige_noalloc_scratch_bytes.argtypes = []
@@ -111,7 +113,7 @@ def lib():
         for f in EXPORTS:
             if f not in ("sige_strerror", "sige_last_error", "sige_max_blocks", "sige_sparse_attention_workspace",
                          "sige_sparse_conv_layer_split_workspace", "sige_noalloc_scratch_bytes",
-                         "sige_wide_weights_bytes"):
+                         "sige_packed_weights_bytes"):
                 getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -396,19 +398,26 @@ def sige_scatter(out_blocks, idx, count, g: Geom, cached, out=None, copy_cached=
 
 
 def sige_sparse_conv_layer(a_edit, w_krsc, bias, cached, idx, count, g: Geom, out=None, copy_cached=True,
-                           stream=None):
-    """Fused gather + conv + scatter into `out` (NHWC [n, ho, wo, c_out])."""
-    _dev(a_edit, w_krsc, bias, cached, idx, count, out)
+                           stream=None, w_packed=None):
+    """Fused gather + conv + scatter into `out` (NHWC [n, ho, wo, c_out]); with w_packed
+    (sige_pack_weights of w_krsc) the kernel loads its weights from the packed copy
+    (sige_sparse_conv_layer_packed)."""
+    _dev(a_edit, w_krsc, bias, cached, idx, count, out, w_packed)
     _need_list(g, idx, count)
     d = _need_layer(g, a_edit, w_krsc, bias, cached if copy_cached else None, out)
     if out is None:
         if not copy_cached:
             raise ValueError("copy_cached=False needs a persistent `out`")
         out = torch.empty((g.n, d.ho, d.wo, g.c_out), dtype=a_edit.dtype, device=a_edit.device)
-    rc = lib().sige_sparse_conv_layer(_p(a_edit), _p(w_krsc), _p(bias), _p(cached if copy_cached else None),
-                                      _p(idx), _p(count), _dt(a_edit), ctypes.byref(g), _p(out),
-                                      int(bool(copy_cached)), _stream(stream))
-    _check(rc, "sige_sparse_conv_layer")
+    args = (_p(a_edit), _p(w_krsc), _p(bias), _p(cached if copy_cached else None), _p(idx), _p(count), _dt(a_edit),
+            ctypes.byref(g), _p(out), int(bool(copy_cached)))
+    if w_packed is None:
+        rc = lib().sige_sparse_conv_layer(*args, _stream(stream))
+        _check(rc, "sige_sparse_conv_layer")
+    else:
+        rc = lib().sige_sparse_conv_layer_packed(*args, _p(w_packed), w_packed.numel() * w_packed.element_size(),
+                                                 _stream(stream))
+        _check(rc, "sige_sparse_conv_layer_packed")
     return out
 
 
@@ -452,35 +461,36 @@ def sige_sparse_conv_layer_plan(g: Geom, dtype) -> LayerPlan:
     return plan
 
 
-def sige_wide_weights_bytes(g: Geom, dtype) -> int:
-    """Bytes of the wide tiles' stage-major weight copy for g and a torch dtype (0: no wide tiles)."""
-    n = int(lib().sige_wide_weights_bytes(ctypes.byref(g), DTYPE_CODE[dtype]))
+def sige_packed_weights_bytes(g: Geom, dtype) -> int:
+    """Bytes of the packed copy of a layer's weights for g and a torch dtype (sige_pack_weights)."""
+    n = int(lib().sige_packed_weights_bytes(ctypes.byref(g), DTYPE_CODE[dtype]))
     if n < 0:
-        _check(n, "sige_wide_weights_bytes")
+        _check(n, "sige_packed_weights_bytes")
     return n
 
 
-def sige_wide_weights_pack(w_krsc, g: Geom, out=None, stream=None):
-    """The stage-major copy of KRSC weights that sige_sparse_conv_layer_auto(w_wide=...) stages
-    the wide tiles from (made once per layer); allocated here when `out` is not given."""
+def sige_pack_weights(w_krsc, g: Geom, out=None, stream=None):
+    """The packed copy of KRSC weights in the layer kernels' load order (made once per layer),
+    for sige_sparse_conv_layer(..., w_packed=) and sige_sparse_conv_layer_auto(..., w_packed=);
+    allocated here when `out` is not given (256-byte aligned)."""
     _dev(w_krsc, out)
-    need = sige_wide_weights_bytes(g, w_krsc.dtype)
+    need = sige_packed_weights_bytes(g, w_krsc.dtype)
     if out is None:
-        out = torch.empty(max(need, 16), dtype=torch.uint8, device=w_krsc.device)
-    rc = lib().sige_wide_weights_pack(_p(w_krsc), _dt(w_krsc), ctypes.byref(g), _p(out),
-                                      out.numel() * out.element_size(), _stream(stream))
-    _check(rc, "sige_wide_weights_pack")
+        out = torch.empty(need, dtype=torch.uint8, device=w_krsc.device)
+    rc = lib().sige_pack_weights(_p(w_krsc), _dt(w_krsc), ctypes.byref(g), _p(out),
+                                 out.numel() * out.element_size(), _stream(stream))
+    _check(rc, "sige_pack_weights")
     return out
 
 
 def sige_sparse_conv_layer_auto(a_edit, w_krsc, bias, cached, idx, count, g: Geom, out=None, copy_cached=True,
-                                workspace=None, stream=None, w_wide=None):
+                                workspace=None, stream=None, w_packed=None):
     """The fused layer on the kernel the library picks for *count (see
     sige_sparse_conv_layer_plan); the workspace is allocated here when the
-    plan needs one and none is given.  With w_wide (sige_wide_weights_pack of
-    w_krsc) the wide tiles stage their weights from it
-    (sige_sparse_conv_layer_auto_packed)."""
-    _dev(a_edit, w_krsc, bias, cached, idx, count, out, workspace, w_wide)
+    plan needs one and none is given.  With w_packed (sige_pack_weights of
+    w_krsc) the single-range kernel and the wide tiles load their weights
+    from it (sige_sparse_conv_layer_auto_packed)."""
+    _dev(a_edit, w_krsc, bias, cached, idx, count, out, workspace, w_packed)
     _need_list(g, idx, count)
     d = _need_layer(g, a_edit, w_krsc, bias, cached if copy_cached else None, out)
     if out is None:
@@ -494,11 +504,11 @@ def sige_sparse_conv_layer_auto(a_edit, w_krsc, bias, cached, idx, count, g: Geo
     args = (_p(a_edit), _p(w_krsc), _p(bias), _p(cached if copy_cached else None), _p(idx), _p(count), _dt(a_edit),
             ctypes.byref(g), _p(out), int(bool(copy_cached)), _p(workspace),
             workspace.numel() if workspace is not None else 0)
-    if w_wide is None:
+    if w_packed is None:
         rc = lib().sige_sparse_conv_layer_auto(*args, _stream(stream))
         _check(rc, "sige_sparse_conv_layer_auto")
     else:
-        rc = lib().sige_sparse_conv_layer_auto_packed(*args, _p(w_wide), w_wide.numel() * w_wide.element_size(),
+        rc = lib().sige_sparse_conv_layer_auto_packed(*args, _p(w_packed), w_packed.numel() * w_packed.element_size(),
                                                       _stream(stream))
         _check(rc, "sige_sparse_conv_layer_auto_packed")
     return out

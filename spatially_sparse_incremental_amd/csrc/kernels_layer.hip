@@ -62,6 +62,7 @@ struct LayerArgs {
     CopyCfg cc;
     float *ws;                     // wide tiles split over K: the fp32 partial tiles
     const uint8_t *ww;             // wide tiles: the weights in stage-major order (NULL: from w, KRSC)
+    const uint8_t *wp;             // k_layer: the weights in fragment order (NULL: from w, KRSC)
 };
 
 __device__ __forceinline__ void layer_tile(const LayerCfg &c, int t, int &tm, int &tn) {
@@ -93,12 +94,26 @@ __device__ __forceinline__ int layer_tiles(const LayerCfg &c, int cnt, int b2) {
 // of the tap: their products meet zeros in the staged windows.  `dummy` points
 // every lane at the first fragment instead (one cache line), for a workgroup
 // that does not know yet whether it has a tile.
+// From the fragment-order copy (wp, see k_layer_weights_pack) the same
+// fragments are 1 KiB in a row per load: (chunk, N tile, K step, N subtile),
+// 64 lanes of 16 bytes.
 template <int DT, int NT, int SMAX, bool W32>
-__device__ __forceinline__ void layer_weights(const uint8_t *w, const Geo &g, const LayerCfg &c,
+__device__ __forceinline__ void layer_weights(const uint8_t *w, const uint8_t *wp, const Geo &g, const LayerCfg &c,
                                               u32x4 (&bfr)[SMAX][NT], const int (&wcol)[NT], int c0, int st0,
-                                              int kl, bool dummy) {
+                                              int kl, bool dummy, int ch, int tn, int lane) {
     constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
     const uint32_t keep = dummy ? 0u : ~0u;  // masks instead of selects: no branches between the loads
+    if (wp) {
+        const uint8_t *pb = wp + (size_t)(ch * c.ntn + tn) * c.steps * NT * 1024;
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+            const int stp = min(st0 + j, c.steps - 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                bfr[j][nt] = ld16(pb + ((uint32_t)(((stp * NT + nt) * 64 + lane) * 16) & keep));
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < SMAX; ++j) {
         const int stp = min(st0 + j, c.steps - 1);
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
         }
         const bool early_w = (int)blockIdx.x < c.spec;
         if constexpr (FIRST) {
-            layer_weights<DT, NT, SMAX, W32>(a.w, g, c, bfr, wcol, 0, st0, kl, !early_w);
+            layer_weights<DT, NT, SMAX, W32>(a.w, a.wp, g, c, bfr, wcol, 0, st0, kl, !early_w, 0, tn, lane);
             __builtin_amdgcn_sched_barrier(0);
             cnt = min(max(cnt_raw, 0), g.cap);
             // A launch paired with the split over input channels: a list below
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                 }
             }
             // the weights, when the registers do not hold this chunk's yet
-            if (ch > 0 || need_w) layer_weights<DT, NT, SMAX, W32>(a.w, g, c, bfr, wcol, c0, st0, kl, false);
+            if (ch > 0 || need_w) layer_weights<DT, NT, SMAX, W32>(a.w, a.wp, g, c, bfr, wcol, c0, st0, kl, false, ch, tn, lane);
             __builtin_amdgcn_s_waitcnt(0);  // this wave's windows and weights have landed
             __syncthreads();
             // This wave's K steps: A fragments from LDS, B from registers.  Step
@@ -874,6 +889,45 @@ __global__ __launch_bounds__(256) void k_wide_weights_pack(const uint8_t *__rest
     }
 }
 
+// The fragment-order copy of KRSC weights that k_layer loads from: for chunk
+// ch, N tile tn (16*nt output channels), K step s of the chunk, N subtile q
+// and lane l, the 16 bytes layer_weights would load from the KRSC weights
+// (clamped columns and channels included, so the MFMAs see the same values)
+// at unit (((ch * ntn + tn) * steps + s) * nt + q) * 64 + l.  One thread per unit.
+__global__ __launch_bounds__(256) void k_layer_weights_pack(const uint8_t *__restrict__ w, Geo g, LayerCfg c, int dt,
+                                                            uint8_t *wp, long units) {
+    const int es = elem_bytes(dt), epv = 16 / es, ks = dt == 0 ? 16 : 32;
+    const bool w32 = dt != 0 && c.nt == 2;
+    const int k2 = g.k * g.k;
+    for (long v = (long)blockIdx.x * 256 + threadIdx.x; v < units; v += (long)gridDim.x * 256) {
+        const int l = (int)(v & 63);
+        long q = v >> 6;
+        const int nt = (int)(q % c.nt);
+        q /= c.nt;
+        const int s = (int)(q % c.steps);
+        q /= c.steps;
+        const int tn = (int)(q % c.ntn), ch = (int)(q / c.ntn);
+        const int n0 = tn * 16 * c.nt;
+        const int tap = s >> c.lkpc, cb = ch * c.ck + (s & (c.kpc - 1)) * ks;
+        const int kl = (w32 ? l >> 5 : l >> 4) * epv;
+        const int col = min(n0 + (w32 ? l & 31 : nt * 16 + (l & 15)), g.cout - 1);
+        const int lch = min(cb + kl + (w32 ? nt * 16 : 0), g.cin - epv);
+        *(u32x4 *)(wp + v * 16) = ld16(w + (((size_t)col * k2 + tap) * g.cin + lch) * es);
+    }
+}
+
+long layer_weights_units(const Geo &g, const LayerCfg &c) { return (long)c.nch * c.ntn * c.steps * c.nt * 64; }
+
+hipError_t launch_layer_weights_pack(int dt, const void *w, const Geo &g, const LayerCfg &c, void *wp, int cus,
+                                     hipStream_t st) {
+    const long units = layer_weights_units(g, c);
+    long grid = (units + 255) / 256;
+    if (grid > 4L * cus) grid = 4L * cus;
+    hipLaunchKernelGGL(k_layer_weights_pack, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, st,
+                       (const uint8_t *)w, g, c, dt, (uint8_t *)wp, units);
+    return hipGetLastError();
+}
+
 long wide_weights_units(const Geo &g) {
     return (long)((g.cout + kLayerWideCols - 1) / kLayerWideCols) * ((g.cin + 15) / 16) * g.k * g.k * 256;
 }
@@ -941,9 +995,10 @@ static hipError_t launch_layer_dt(int fused, bool tail, const LayerArgs &a, hipS
 hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                         const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                         const int32_t *prev_count, const Geo &g, const LayerCfg &cfg, const CopyCfg &cc,
-                        hipStream_t st) {
+                        hipStream_t st, const void *wp) {
     const LayerArgs a{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
-                      (const uint8_t *)cache, prev_idx, prev_count, g, cfg, cc};
+                      (const uint8_t *)cache, prev_idx, prev_count, g, cfg, cc, nullptr, nullptr,
+                      (const uint8_t *)wp};
     const bool tail = fused && (cc.nvec > 0 || prev_idx);
     switch (dt) {
     case 0: return launch_layer_dt<0>(fused, tail, a, st);

@@ -1111,9 +1111,33 @@ int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *coun
                   "sige_scatter", (hipStream_t)stream);
 }
 
-int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
-                           const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
-                           int copy_cached, void *stream) {
+// The packed copy of a layer's weights (sige_pack_weights): the single-range
+// kernel's fragment-order section, then (16-bit types, where the wide tiles
+// can run) the wide tiles' stage-major section at a 256-byte aligned offset.
+struct PackedLayout {
+    sige::LayerCfg lc;
+    int64_t layer_bytes, wide_off, wide_bytes, total;
+};
+
+static int packed_layout(const Geo &g, int dtype, PackedLayout *pl) {
+    int rc = choose_layer(g, dtype, &pl->lc);
+    if (rc) return rc;
+    pl->layer_bytes = (int64_t)sige::layer_weights_units(g, pl->lc) * 16;
+    pl->wide_off = (pl->layer_bytes + 255) / 256 * 256;
+    pl->wide_bytes = dtype != SIGE_F32 && pl->lc.w_lds > 0 ? (int64_t)sige::wide_weights_units(g) * 16 : 0;
+    pl->total = pl->wide_off + pl->wide_bytes;
+    return SIGE_OK;
+}
+
+// Checks of a caller's packed weights against the layout: non-NULL, aligned,
+// large enough, not overlapping the written regions wr[0, nwr).
+static int check_packed(const void *w_packed, int64_t w_packed_bytes, const PackedLayout &pl, const Region *wr,
+                        int nwr);
+
+static int layer_single(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                        const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                        int copy_cached, const void *w_packed, int64_t w_packed_bytes, void *stream,
+                        const char *name) {
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
     Geo g;
     int rc = derive(gp, &g);
@@ -1136,11 +1160,33 @@ int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *
     }
     sige::LayerCfg cfg;
     if ((rc = choose_layer(g, dtype, &cfg))) return rc;
+    if (w_packed) {
+        PackedLayout pl;
+        if ((rc = packed_layout(g, dtype, &pl))) return rc;
+        const Region wr[] = {{out, obytes}};
+        if ((rc = check_packed(w_packed, w_packed_bytes, pl, wr, 1))) return rc;
+    }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
     return finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out, copy_cached ? cached : nullptr,
-                                     nullptr, nullptr, g, cfg, cc, (hipStream_t)stream),
-                  "sige_sparse_conv_layer", (hipStream_t)stream);
+                                     nullptr, nullptr, g, cfg, cc, (hipStream_t)stream, w_packed),
+                  name, (hipStream_t)stream);
+}
+
+int sige_sparse_conv_layer(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                           const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
+                           int copy_cached, void *stream) {
+    return layer_single(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, nullptr, 0, stream,
+                        "sige_sparse_conv_layer");
+}
+
+int sige_sparse_conv_layer_packed(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
+                                  const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp,
+                                  void *out, int copy_cached, const void *w_packed, int64_t w_packed_bytes,
+                                  void *stream) {
+    if (!w_packed) return fail(SIGE_EINVAL, "NULL pointer");
+    return layer_single(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, w_packed,
+                        w_packed_bytes, stream, "sige_sparse_conv_layer_packed");
 }
 
 int sige_sparse_conv_layer_plan(const sige_geom *gp, int dtype, sige_layer_plan *out) {
@@ -1175,19 +1221,11 @@ int sige_sparse_conv_layer_plan(const sige_geom *gp, int dtype, sige_layer_plan 
     return SIGE_OK;
 }
 
-// The stage-major weights of the wide tiles: bytes for geometry g (0 when the
-// wide tiles cannot run on it).
-static int64_t wide_weights_bytes(const Geo &g, int dtype) {
-    if (dtype == SIGE_F32) return 0;
-    sige::LayerCfg lc;
-    if (choose_layer(g, dtype, &lc) != SIGE_OK) return 0;  // no layer kernel, so no wide tiles
-    return lc.w_lds > 0 ? (int64_t)sige::wide_weights_units(g) * 16 : 0;
-}
 
 static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                       const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,
-                      int copy_cached, void *workspace, int64_t workspace_bytes, const void *w_wide,
-                      int64_t w_wide_bytes, void *stream) {
+                      int copy_cached, void *workspace, int64_t workspace_bytes, const void *w_packed,
+                      int64_t w_packed_bytes, void *stream) {
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
     Geo g;
     int rc = derive(gp, &g);
@@ -1218,14 +1256,14 @@ static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias,
         const Region wr[] = {{out, obytes}, {workspace, (size_t)p.ws_bytes}};
         if (regions_overlap(wr, 2, rd, 6)) return fail(SIGE_EINVAL, "the workspace overlaps another argument");
     }
-    const int64_t wwb = w_wide ? wide_weights_bytes(g, dtype) : 0;
-    if (w_wide && wwb > 0) {  // the wide tiles stage their weights from the stage-major copy
-        if (!aligned(w_wide, 16)) return fail(SIGE_EALIGN, "w_wide must be 16-byte aligned");
-        if (w_wide_bytes < wwb)
-            return fail(SIGE_ERANGE, "w_wide of %lld bytes, %lld needed", (long long)w_wide_bytes, (long long)wwb);
+    const uint8_t *wp = nullptr, *ww = nullptr;  // the packed sections, when given
+    if (w_packed) {
+        PackedLayout pl;
+        if ((rc = packed_layout(g, dtype, &pl))) return rc;
         const Region wr[] = {{out, obytes}, {workspace, (size_t)(p.ws_bytes > 0 ? p.ws_bytes : 0)}};
-        const Region ww[] = {{w_wide, (size_t)wwb}};
-        if (regions_overlap(wr, 2, ww, 1)) return fail(SIGE_EINVAL, "w_wide overlaps out or the workspace");
+        if ((rc = check_packed(w_packed, w_packed_bytes, pl, wr, 2))) return rc;
+        wp = (const uint8_t *)w_packed;
+        ww = pl.wide_bytes > 0 ? wp + pl.wide_off : nullptr;
     }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
@@ -1234,14 +1272,14 @@ static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias,
     // (and below wide_min)
     if (p.split_max < g.cap && (p.wide_min > p.split_max + 1 || p.wide_max < g.cap)) {
         if ((rc = finish(sige::launch_layer(dtype, 1, a_edit, w_krsc, bias, idx, count, out,
-                                            copy_cached ? cached : nullptr, nullptr, nullptr, g, p.lc, cc, st),
+                                            copy_cached ? cached : nullptr, nullptr, nullptr, g, p.lc, cc, st, wp),
                          "sige_sparse_conv_layer_auto", st)))
             return rc;
     }
     if (p.wide_min <= g.cap) {  // the wide tiles: lists of at least wide_min blocks
         if ((rc = finish(sige::launch_layer_wide(dtype, a_edit, w_krsc, bias, idx, count, out,
                                                  copy_cached ? cached : nullptr, g, p.lc, cc, st, (float *)workspace,
-                                                 wwb > 0 ? w_wide : nullptr),
+                                                 ww),
                          "sige_sparse_conv_layer_auto", st)))
             return rc;
     }
@@ -1263,42 +1301,59 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
 int sige_sparse_conv_layer_auto_packed(const void *a_edit, const void *w_krsc, const float *bias,
                                        const void *cached, const int32_t *idx, const int32_t *count, int dtype,
                                        const sige_geom *gp, void *out, int copy_cached, void *workspace,
-                                       int64_t workspace_bytes, const void *w_wide, int64_t w_wide_bytes,
+                                       int64_t workspace_bytes, const void *w_packed, int64_t w_packed_bytes,
                                        void *stream) {
-    if (!w_wide) return fail(SIGE_EINVAL, "NULL pointer");
+    if (!w_packed) return fail(SIGE_EINVAL, "NULL pointer");
     return layer_auto(a_edit, w_krsc, bias, cached, idx, count, dtype, gp, out, copy_cached, workspace,
-                      workspace_bytes, w_wide, w_wide_bytes, stream);
+                      workspace_bytes, w_packed, w_packed_bytes, stream);
 }
 
-int64_t sige_wide_weights_bytes(const sige_geom *gp, int dtype) {
-    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
-    Geo g;
-    const int rc = derive(gp, &g);
-    if (rc) return rc;
-    return wide_weights_bytes(g, dtype);
+static int check_packed(const void *w_packed, int64_t w_packed_bytes, const PackedLayout &pl, const Region *wr,
+                        int nwr) {
+    if (!w_packed) return fail(SIGE_EINVAL, "NULL pointer");
+    if (!aligned(w_packed, 256)) return fail(SIGE_EALIGN, "packed weights must be 256-byte aligned");
+    if (w_packed_bytes < pl.total)
+        return fail(SIGE_ERANGE, "packed weights of %lld bytes, %lld needed", (long long)w_packed_bytes,
+                    (long long)pl.total);
+    const Region rd[] = {{w_packed, (size_t)pl.total}};
+    if (regions_overlap(wr, nwr, rd, 1)) return fail(SIGE_EINVAL, "the packed weights overlap an output");
+    return SIGE_OK;
 }
 
-int sige_wide_weights_pack(const void *w_krsc, int dtype, const sige_geom *gp, void *w_wide, int64_t w_wide_bytes,
-                           void *stream) {
+int64_t sige_packed_weights_bytes(const sige_geom *gp, int dtype) {
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
-    if (dtype == SIGE_F32) return fail(SIGE_EDTYPE, "the wide tiles run on 16-bit types only");
     Geo g;
     int rc = derive(gp, &g);
     if (rc) return rc;
-    if (!w_krsc || !w_wide) return fail(SIGE_EINVAL, "NULL pointer");
     if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
-    if (!aligned(w_krsc, 16) || !aligned(w_wide, 16)) return fail(SIGE_EALIGN, "weights must be 16-byte aligned");
-    const int64_t need = wide_weights_bytes(g, dtype);
-    if (need == 0) return fail(SIGE_ERANGE, "no wide tiles for this geometry");
-    if (w_wide_bytes < need)
-        return fail(SIGE_ERANGE, "w_wide of %lld bytes, %lld needed", (long long)w_wide_bytes, (long long)need);
-    const Region rd[] = {{w_krsc, (size_t)g.cout * g.k * g.k * g.cin * 2}};
-    const Region wr[] = {{w_wide, (size_t)need}};
-    if (regions_overlap(wr, 1, rd, 1)) return fail(SIGE_EINVAL, "w_wide overlaps w_krsc");
+    PackedLayout pl;
+    if ((rc = packed_layout(g, dtype, &pl))) return rc;
+    return pl.total;
+}
+
+int sige_pack_weights(const void *w_krsc, int dtype, const sige_geom *gp, void *w_packed, int64_t w_packed_bytes,
+                      void *stream) {
+    if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
+    Geo g;
+    int rc = derive(gp, &g);
+    if (rc) return rc;
+    if (!w_krsc || !w_packed) return fail(SIGE_EINVAL, "NULL pointer");
+    if ((rc = channel_rows_ok(dtype, g.cin, "c_in")) || (rc = channel_rows_ok(dtype, g.cout, "c_out"))) return rc;
+    if (!aligned(w_krsc, 16)) return fail(SIGE_EALIGN, "weights must be 16-byte aligned");
+    PackedLayout pl;
+    if ((rc = packed_layout(g, dtype, &pl))) return rc;
+    const Region wr[] = {{w_krsc, (size_t)g.cout * g.k * g.k * g.cin * sige::elem_bytes(dtype)}};
+    if ((rc = check_packed(w_packed, w_packed_bytes, pl, wr, 1))) return rc;
     if ((rc = device_ready())) return rc;
     const hipStream_t st = (hipStream_t)stream;
-    return finish(sige::launch_wide_weights_pack(w_krsc, g, w_wide, dev_info().cus, st), "sige_wide_weights_pack",
-                  st);
+    const int cus = dev_info().cus;
+    if ((rc = finish(sige::launch_layer_weights_pack(dtype, w_krsc, g, pl.lc, w_packed, cus, st), "sige_pack_weights",
+                     st)))
+        return rc;
+    if (pl.wide_bytes > 0)
+        return finish(sige::launch_wide_weights_pack(w_krsc, g, (uint8_t *)w_packed + pl.wide_off, cus, st),
+                      "sige_pack_weights", st);
+    return SIGE_OK;
 }
 
 int64_t sige_sparse_conv_layer_split_workspace(const sige_geom *gp, int dtype) {

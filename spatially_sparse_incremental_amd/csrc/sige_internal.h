@@ -138,10 +138,17 @@ hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const 
 // cache is copied outside the listed blocks, with prev_idx the previous
 // list's blocks are restored) or the block convolution (fused = 0: src =
 // stacked blocks, dst = output blocks), on kernels_layer.hip's k_layer.
+// wp: the weights in k_layer's fragment order (launch_layer_weights_pack), or NULL
+// to load them from the KRSC weights w.
 hipError_t launch_layer(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                         const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                         const int32_t *prev_count, const Geo &g, const LayerCfg &cfg, const CopyCfg &cc,
-                        hipStream_t st);
+                        hipStream_t st, const void *wp = nullptr);
+// The fragment-order copy of KRSC weights for k_layer with configuration cfg: 16-byte
+// units of it, and the launch that writes it.
+long layer_weights_units(const Geo &g, const LayerCfg &cfg);
+hipError_t launch_layer_weights_pack(int dt, const void *w, const Geo &g, const LayerCfg &cfg, void *wp, int cus,
+                                     hipStream_t st);
 // The wide tiles of the fused layer (16-bit types), run for lists of
 // cfg.wide_min..cfg.wide_max blocks (the launches exit at once for others).
 // With cfg.w_pmax > 1 a short list's tiles are split over K into parts whose

@@ -471,39 +471,60 @@ def test_auto_layer_validation(lib):
     assert f(*args[:6], 7, *args[7:], _v(E), need, s) == EDTYPE
 
 
-def test_wide_weights_pack_and_packed_auto_validation(lib):
-    """The stage-major weight copy: its size (the KRSC size when c_out is a
-    multiple of 128 and c_in of 16, padded otherwise; 0 without wide tiles),
-    and the checks of the pack call and of the packed auto layer before any
-    device work (fp32 SIGE_EDTYPE, short buffers and layers without wide tiles
+def test_packed_weights_validation(lib):
+    """The packed weight copy: its size (the single-range kernel's section, one
+    1 KiB load per chunk, N tile, K step and N subtile -- the KRSC size when
+    nothing is padded -- then, from a 256-byte boundary, the wide tiles'
+    section for 16-bit types where they run), and the checks of the pack call
+    and of the packed layer entry points before any device work (short buffers
     SIGE_ERANGE, NULL and overlapping pointers SIGE_EINVAL, misalignment
     SIGE_EALIGN; a valid call without a GPU SIGE_ENODEV)."""
-    g = _g(1, 32, 64, 1024, 1024, 3, 1, 1, 4)
-    need = lib.sige_wide_weights_bytes(ctypes.byref(g), 1)
-    assert need == 1024 * 9 * 1024 * 2
-    assert lib.sige_wide_weights_bytes(ctypes.byref(_g(1, 64, 64, 24, 136, 3, 1, 1, 6)), 2) == \
-        2 * 2 * 9 * 256 * 16  # c_out 136 -> two N tiles, c_in 24 -> two stages
-    assert lib.sige_wide_weights_bytes(ctypes.byref(_g(1, 64, 64, 64, 64, 1, 1, 0, 4)), 1) == 1 * 4 * 1 * 256 * 16
-    assert lib.sige_wide_weights_bytes(ctypes.byref(g), 0) == 0  # fp32: no wide tiles
-    assert lib.sige_wide_weights_bytes(ctypes.byref(_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)), 2) == 0
-    assert lib.sige_wide_weights_bytes(ctypes.byref(g), 7) == EDTYPE
+    def size(g, dt):
+        return lib.sige_packed_weights_bytes(ctypes.byref(g), dt)
+
+    def layer_part(g, dt):
+        p = ssi.sige_sparse_conv_layer_plan(g, {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dt])
+        nsub = 2 if p.n_tiles * 32 >= g.c_out else 1  # 16 x NT output channels per N tile
+        return p.chunks * p.n_tiles * p.steps * nsub * 1024
+    g = _g(1, 256, 256, 128, 128, 3, 1, 1, 6)
+    krsc = 128 * 9 * 128 * 2
+    assert layer_part(g, 1) == krsc
+    assert size(g, 1) == krsc + krsc  # both sections, nothing padded
+    assert size(g, 0) == layer_part(g, 0) == 2 * krsc  # fp32: the single-range section only
+    g2 = _g(1, 64, 64, 24, 136, 3, 1, 1, 6)  # c_out 136: 5 N tiles of 32; c_in 24: one 32-channel slice
+    lp = layer_part(g2, 2)
+    assert size(g2, 2) == (lp + 255) // 256 * 256 + 2 * 2 * 9 * 256 * 16
+    gs = _g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)  # no wide tiles (2x2 blocks)
+    assert size(gs, 2) == layer_part(gs, 2)
+    assert size(g, 7) == EDTYPE
+    need = size(g, 1)
     s = _v(0)
-    pack = lib.sige_wide_weights_pack
+    pack = lib.sige_pack_weights
     assert pack(_v(A), 1, ctypes.byref(g), _v(B), need, s) == ENODEV
-    assert pack(_v(A), 0, ctypes.byref(g), _v(B), need, s) == EDTYPE
     assert pack(_v(A), 1, ctypes.byref(g), _v(B), need - 16, s) == ERANGE
     assert pack(None, 1, ctypes.byref(g), _v(B), need, s) == EINVAL
     assert pack(_v(A), 1, ctypes.byref(g), None, need, s) == EINVAL
     assert pack(_v(A), 1, ctypes.byref(g), _v(A + 4096), need, s) == EINVAL  # overlaps the KRSC weights
     assert pack(_v(A + 8), 1, ctypes.byref(g), _v(B), need, s) == EALIGN
-    assert pack(_v(A), 2, ctypes.byref(_g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)), _v(B), need, s) == ERANGE
+    assert pack(_v(A), 1, ctypes.byref(g), _v(B + 16), need, s) == EALIGN  # 256-byte alignment
+
+    W = A + (5 << 36)
+    f = lib.sige_sparse_conv_layer_packed
+    args = (_v(A), _v(B), None, None, _v(C), _v(C + 4096), 1, ctypes.byref(g), _v(D), 0)
+    assert f(*args, _v(W), need, s) == ENODEV
+    assert f(*args, None, need, s) == EINVAL
+    assert f(*args, _v(W), need - 16, s) == ERANGE
+    assert f(*args, _v(W + 16), need, s) == EALIGN
+    assert f(*args, _v(D + 256), need, s) == EINVAL  # overlaps out
 
     f = lib.sige_sparse_conv_layer_auto_packed
-    ws = ssi.sige_sparse_conv_layer_plan(g, torch.bfloat16).workspace_bytes
-    args = (_v(A), _v(B), None, None, _v(C), _v(C + 4096), 1, ctypes.byref(g), _v(D), 0, _v(E), ws)
-    assert f(*args, _v(A + (5 << 36)), need, s) == ENODEV
-    assert f(*args, None, need, s) == EINVAL
-    assert f(*args, _v(A + (5 << 36)), need - 16, s) == ERANGE
-    assert f(*args, _v(A + (5 << 36) + 8), need, s) == EALIGN
-    assert f(*args, _v(D + 64), need, s) == EINVAL  # overlaps out
-    assert f(*args, _v(E + 64), need, s) == EINVAL  # overlaps the workspace
+    g3 = _g(1, 32, 64, 1024, 1024, 3, 1, 1, 4)
+    need3 = size(g3, 1)
+    ws = ssi.sige_sparse_conv_layer_plan(g3, torch.bfloat16).workspace_bytes
+    args = (_v(A), _v(B), None, None, _v(C), _v(C + 4096), 1, ctypes.byref(g3), _v(D), 0, _v(E), ws)
+    assert f(*args, _v(W), need3, s) == ENODEV
+    assert f(*args, None, need3, s) == EINVAL
+    assert f(*args, _v(W), need3 - 16, s) == ERANGE
+    assert f(*args, _v(W + 16), need3, s) == EALIGN
+    assert f(*args, _v(D + 256), need3, s) == EINVAL  # overlaps out
+    assert f(*args, _v(E + 256), need3, s) == EINVAL  # overlaps the workspace

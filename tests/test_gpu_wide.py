@@ -240,21 +240,24 @@ def _packed_reference(wk, cin, cout, k):
 
 @pytest.mark.parametrize("shape", [(24, 136, 3), (48, 128, 1), (200, 136, 3), (256, 64, 3)],
                          ids=["cin24_cout136", "pointwise", "cin200", "cin256_cout64"])
-def test_wide_weights_pack_layout(shape):
-    """sige_wide_weights_pack against the layout written out on the CPU, bit for
-    bit, with a guard canary after the packed buffer."""
+def test_packed_weights_wide_section_layout(shape):
+    """The wide tiles' section of sige_pack_weights (from the 256-byte boundary
+    after the single-range kernel's section) against the stage-major layout
+    written out on the CPU, bit for bit, with a guard canary after the copy."""
     cin, cout, k = shape
     g = ssi.geom(1, 40, 44, cin, cout, k, 1, k // 2, 6)
     dt = torch.bfloat16
     wt = rand((cout, cin, k, k), dt, 71)
     wk = ssi.weight_to_krsc(wt)
-    need = ssi.sige_wide_weights_bytes(g, dt)
-    assert need == ((cout + 127) // 128) * ((cin + 15) // 16) * k * k * 4096
+    need = ssi.sige_packed_weights_bytes(g, dt)
+    wide = ((cout + 127) // 128) * ((cin + 15) // 16) * k * k * 4096
+    off = need - wide
+    assert off % 256 == 0 and off >= cout * k * k * cin * 2
     buf = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
-    ssi.sige_wide_weights_pack(wk.cuda(), g, out=buf[:need])
+    ssi.sige_pack_weights(wk.cuda(), g, out=buf[:need])
     torch.cuda.synchronize()
-    assert (buf[need:] == 0x5A).all(), "writes past the packed buffer"
-    got = buf[:need].cpu().view(torch.int16)
+    assert (buf[need:] == 0x5A).all(), "writes past the packed copy"
+    got = buf[off:need].cpu().view(torch.int16)
     ref = _packed_reference(wk, cin, cout, k).view(torch.int16)
     assert torch.equal(got, ref)
 
@@ -262,8 +265,9 @@ def test_wide_weights_pack_layout(shape):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_packed_weights_give_the_same_layer(case, monkeypatch):
     """sige_sparse_conv_layer_auto_packed equals sige_sparse_conv_layer_auto bit
-    for bit (the same weights reach the same LDS slots), on every forced-wide
-    geometry (K splits included) and list length, with and without the copy."""
+    for bit (the same weights reach the same registers and LDS slots), on every
+    forced-wide geometry (K splits included) and list length, with and without
+    the copy."""
     name, n, h, w, cin, cout, k, s, p, b, dts = case
     dt = DT[dts]
     g = ssi.geom(n, h, w, cin, cout, k, s, p, b)
@@ -274,7 +278,7 @@ def test_packed_weights_give_the_same_layer(case, monkeypatch):
     _, a_e, wt, bias = layer_inputs(n, h, w, cin, cout, k, dt, 5, mask)
     cache = rand((n, ho, wo, cout), dt, 7)
     wk, bg, ag, cg = ssi.weight_to_krsc(wt).cuda(), bias.cuda(), a_e.cuda(), cache.cuda()
-    ww = ssi.sige_wide_weights_pack(wk, g)
+    ww = ssi.sige_pack_weights(wk, g)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
     for lst in _lists(cap, 13):
         cnt = lst.numel()
@@ -288,7 +292,7 @@ def test_packed_weights_give_the_same_layer(case, monkeypatch):
             ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg if copy else None, idx_g, count, g, out=o1,
                                             copy_cached=copy, workspace=ws)
             ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg if copy else None, idx_g, count, g, out=o2,
-                                            copy_cached=copy, workspace=ws, w_wide=ww)
+                                            copy_cached=copy, workspace=ws, w_packed=ww)
             assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), f"{name} {cnt} blocks copy={copy}"
 
 
@@ -311,7 +315,7 @@ def test_packed_weights_on_gaugan_layers(layer, cnt):
     wt, bias = synth.make_layer_tensors(L, 83)
     cache = synth.make_activation(1, ho, wo, L.c_out, "bf16", 85)
     ag, wk, bg, cg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda(), cache.cuda()
-    ww = ssi.sige_wide_weights_pack(wk, g)
+    ww = ssi.sige_pack_weights(wk, g)
     gen = torch.Generator().manual_seed(87)
     lst = torch.randperm(plan.cap, generator=gen)[:cnt].sort().values.to(torch.int32)
     idx = torch.zeros(plan.cap, dtype=torch.int32)
@@ -320,7 +324,7 @@ def test_packed_weights_on_gaugan_layers(layer, cnt):
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
     print(f"[case] {layer} packed: {cnt} of {plan.cap} blocks", flush=True)
     o1 = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg, idx, count, g, workspace=ws)
-    o2 = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg, idx, count, g, workspace=ws, w_wide=ww)
+    o2 = ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cg, idx, count, g, workspace=ws, w_packed=ww)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8))
     sub = torch.zeros(plan.cap, dtype=torch.uint8)
