@@ -97,13 +97,13 @@ __device__ __forceinline__ int layer_tiles(const LayerCfg &c, int cnt, int b2) {
 // From the fragment-order copy (wp, see k_layer_weights_pack) the same
 // fragments are 1 KiB in a row per load: (chunk, N tile, K step, N subtile),
 // 64 lanes of 16 bytes.
-template <int DT, int NT, int SMAX, bool W32>
+template <int DT, int NT, int SMAX, bool W32, bool PK>
 __device__ __forceinline__ void layer_weights(const uint8_t *w, const uint8_t *wp, const Geo &g, const LayerCfg &c,
                                               u32x4 (&bfr)[SMAX][NT], const int (&wcol)[NT], int c0, int st0,
                                               int kl, bool dummy, int ch, int tn, int lane) {
     constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
     const uint32_t keep = dummy ? 0u : ~0u;  // masks instead of selects: no branches between the loads
-    if (wp) {
+    if constexpr (PK) {
         const uint8_t *pb = wp + (size_t)(ch * c.ntn + tn) * c.steps * NT * 1024;
 #pragma unroll
         for (int j = 0; j < SMAX; ++j) {
@@ -127,7 +127,7 @@ __device__ __forceinline__ void layer_weights(const uint8_t *w, const uint8_t *w
     }
 }
 
-template <int DT, int MT, int NT, bool FUSED, bool TAIL>
+template <int DT, int MT, int NT, bool FUSED, bool TAIL, bool PK>
 __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
     constexpr int NW = kLayerWaves, NTHR = kLayerThreads;
     constexpr int ES = elem_bytes(DT), EPV = 16 / ES;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
         }
         const bool early_w = (int)blockIdx.x < c.spec;
         if constexpr (FIRST) {
-            layer_weights<DT, NT, SMAX, W32>(a.w, a.wp, g, c, bfr, wcol, 0, st0, kl, !early_w, 0, tn, lane);
+            layer_weights<DT, NT, SMAX, W32, PK>(a.w, a.wp, g, c, bfr, wcol, 0, st0, kl, !early_w, 0, tn, lane);
             __builtin_amdgcn_sched_barrier(0);
             cnt = min(max(cnt_raw, 0), g.cap);
             // A launch paired with the split over input channels: a list below
@@ -310,7 +310,8 @@ __global__ __launch_bounds__(kLayerThreads, 2) void k_layer(LayerArgs a) {
                 }
             }
             // the weights, when the registers do not hold this chunk's yet
-            if (ch > 0 || need_w) layer_weights<DT, NT, SMAX, W32>(a.w, a.wp, g, c, bfr, wcol, c0, st0, kl, false, ch, tn, lane);
+            if (ch > 0 || need_w)
+                layer_weights<DT, NT, SMAX, W32, PK>(a.w, a.wp, g, c, bfr, wcol, c0, st0, kl, false, ch, tn, lane);
             __builtin_amdgcn_s_waitcnt(0);  // this wave's windows and weights have landed
             __syncthreads();
             // This wave's K steps: A fragments from LDS, B from registers.  Step
@@ -962,9 +963,9 @@ static int layer_resident(K kernel, int lds) {
     return n;
 }
 
-template <int DT, int MT, int NT, bool FUSED, bool TAIL>
+template <int DT, int MT, int NT, bool FUSED, bool TAIL, bool PK = false>
 static hipError_t launch_layer_k(const LayerArgs &args, hipStream_t st) {
-    auto k = k_layer<DT, MT, NT, FUSED, TAIL>;
+    auto k = k_layer<DT, MT, NT, FUSED, TAIL, PK>;
     const LayerCfg &c = args.c;
     long grid = (long)c.cus * layer_resident(k, c.lds_bytes);
     if (!TAIL && c.tiles_cap < grid) grid = c.tiles_cap;  // nothing past the tiles at capacity
@@ -980,6 +981,9 @@ static hipError_t launch_layer_k(const LayerArgs &args, hipStream_t st) {
 template <int DT, int MT, int NT>
 static hipError_t launch_layer_t(int fused, bool tail, const LayerArgs &a, hipStream_t st) {
     if (!fused) return launch_layer_k<DT, MT, NT, false, false>(a, st);
+    if (a.wp)  // the weights from the fragment-order copy
+        return tail ? launch_layer_k<DT, MT, NT, true, true, true>(a, st)
+                    : launch_layer_k<DT, MT, NT, true, false, true>(a, st);
     return tail ? launch_layer_k<DT, MT, NT, true, true>(a, st) : launch_layer_k<DT, MT, NT, true, false>(a, st);
 }
 

@@ -1,6 +1,7 @@
 """The bench's measured step at its full size, against the oracle on every
 listed block: sige_diff_mask_bits -> sige_reduce_bits_copy ->
-sige_sparse_conv_layer(copy_cached = 0) on the 256x256x128 -> 128 bf16 U-Net
+sige_sparse_conv_layer_packed(copy_cached = 0) (the weights packed once by
+sige_pack_weights, as the bench does) on the 256x256x128 -> 128 bf16 U-Net
 layer with the bench's own seeded 1.2% blob edit, run as replays of a captured
 HIP graph (the launch configuration the bench times).
 
@@ -39,6 +40,7 @@ def test_bench_step_at_full_size_against_the_oracle():
     cap = ssi.sige_max_blocks(g)
     ao, ae, cg = a_o.cuda(), a_e.cuda(), cache.cuda()
     wk, bs = ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    wp = ssi.sige_pack_weights(wk, g)
     mbits = torch.empty((L.h * L.w // 32,), dtype=torch.int32, device="cuda")
     idx = torch.empty((cap,), dtype=torch.int32, device="cuda")
     count = torch.empty((1,), dtype=torch.int32, device="cuda")
@@ -47,7 +49,7 @@ def test_bench_step_at_full_size_against_the_oracle():
     def step():
         ssi.sige_diff_mask_bits(ao, ae, wl.tau, bits=mbits)
         ssi.sige_reduce_bits_copy(mbits, L.h, L.w, g, L.dilate, cg, out=out, idx=idx, count=count)
-        ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx, count, g, out=out, copy_cached=False)
+        ssi.sige_sparse_conv_layer(ae, wk, bs, None, idx, count, g, out=out, copy_cached=False, w_packed=wp)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
