@@ -752,9 +752,10 @@ def _attention_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
 
 def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     """The latent-diffusion 16x16x1280 fp16 3x3 layer (b = 2, dilation 1) with the
-    blob edit: the library's choice (sige_sparse_conv_layer_auto), the
-    single-range fused layer, the layer split over input channels and the dense
-    conv (torch/MIOpen), each with the cache copy."""
+    blob edit: the library's choice (sige_sparse_conv_layer_auto) and the
+    single-range fused layer on the packed weights, the layer split over input
+    channels (KRSC weights, its own entry point) and the dense conv
+    (torch/MIOpen), each with the cache copy."""
     dev = torch.device("cuda:0")
     wl = synth.workload("ldm_64x64x320_f16")
     L = [x for x in wl.layers if x.name == "l16_3x3"][0]
@@ -768,13 +769,14 @@ def _ldm_split_comparator(torch, F, ssi, synth, graph_time, timed_eager, seed):
     idx, cnt = ssi.sige_reduce_mask(ssi.sige_diff_mask(a_o, a_e, wl.tau), g, L.dilate)
     out = torch.empty_like(cache)
     ws = torch.empty(ssi.sige_sparse_conv_layer_split_workspace(g, a_e.dtype), dtype=torch.uint8, device=dev)
-    t_plain = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out))
+    wpk = ssi.sige_pack_weights(wk, g)  # packed once, outside the timing
+    t_plain = graph_time(lambda: ssi.sige_sparse_conv_layer(a_e, wk, bias, cache, idx, cnt, g, out=out, w_packed=wpk))
     t_split = graph_time(lambda: ssi.sige_sparse_conv_layer_split(a_e, wk, bias, cache, idx, cnt, g, out=out,
                                                                   workspace=ws))
     plan = ssi.sige_sparse_conv_layer_plan(g, a_e.dtype)
     ws_auto = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     t_auto = graph_time(lambda: ssi.sige_sparse_conv_layer_auto(a_e, wk, bias, cache, idx, cnt, g, out=out,
-                                                                workspace=ws_auto))
+                                                                workspace=ws_auto, w_packed=wpk))
     res = {"blocks": int(cnt.item()), "auto_us": round(t_auto, 3),
            "auto_path": _auto_path(plan, int(cnt.item())), "split_max": plan.split_max,
            "single_range_us": round(t_plain, 3), "split_us": round(t_split, 3)}

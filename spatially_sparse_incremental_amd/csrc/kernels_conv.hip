@@ -96,6 +96,7 @@ struct ConvArgs {
     Geo g;
     ConvCfg c;
     CopyCfg cc;
+    const uint8_t *wp;          // split mode: the weights in fragment order (NULL: from w, KRSC)
 };
 
 // Split over input channels (the fused layer with a workspace): a work item
@@ -167,11 +168,22 @@ constexpr int kConvThreads = 64 * kConvWaves;
 // wave, wave + 8, ... (tap, KS-channel slice), 16 output channels per N
 // subtile.  Unconditional loads at clamped addresses (the convolution zeroes
 // fragments outside the weight tensor where it uses them).
-template <int DT, int NT, int SMAX>
+template <int DT, int NT, int SMAX, bool PK>
 __device__ __forceinline__ void load_weights(const ConvArgs &a, u32x4 (&bfr)[SMAX][NT], int c0, int n0, int wave,
                                              int lane, int steps, int kpc) {
     constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
     const Geo &g = a.g;
+    if constexpr (PK) {  // from the fragment-order copy: (chunk, N tile, K step, N subtile) x 64 lanes
+        const int ntn = (g.cout + 16 * NT - 1) / (16 * NT);
+        const uint8_t *pb = a.wp + (size_t)((c0 / a.c.ck) * ntn + n0 / (16 * NT)) * steps * NT * 1024;
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+            const int stp = min(wave + kConvWaves * j, steps - 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bfr[j][nt] = ld16(pb + ((stp * NT + nt) * 64 + lane) * 16);
+        }
+        return;
+    }
     const int k2 = g.k * g.k, kl = (lane >> 4) * EPV;
 #pragma unroll
     for (int j = 0; j < SMAX; ++j) {
@@ -356,7 +368,7 @@ __device__ __forceinline__ void lds_barrier() {
 // for the group's first tile, kept for every chunk of the range, and one for
 // the others (written for tile i + 1 after every wave has passed the barriers
 // that follow its last read, the staging of tile i).
-template <int DT, int MT, int NT>
+template <int DT, int MT, int NT, bool PK>
 __global__ __launch_bounds__(kConvThreads, 2) void k_conv_stream(ConvArgs a) {
     constexpr int NTHR = kConvThreads;
     constexpr int ES = elem_bytes(DT), EPV = 16 / ES, KS = MfmaStep<DT>::KS;
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(kConvThreads, 2) void k_conv_stream(ConvArgs a) {
             // every M tile of the group), the first tile's windows and wave 0's
             // block indices of the second tile
             u32x4 bfr[SMAX][NT];
-            load_weights<DT, NT, SMAX>(a, bfr, c0, n0, wave, lane, steps, kpc);
+            load_weights<DT, NT, SMAX, PK>(a, bfr, c0, n0, wave, lane, steps, kpc);
             int lin = 0;
             if (wave == 0 && tm0 + 1 < tm1) lin = read_lin(tm0 + 1);
             stage(tm0, 0, smem, c0);
@@ -606,7 +618,7 @@ static int resident_per_cu(K kernel, int lds) {
 template <int DT, int MT, int NT>
 static hipError_t launch_conv_t(int fused, const ConvArgs &args, hipStream_t st) {
     if (fused && args.ws) {  // the split over input channels, then the combine (and the copy)
-        auto k = k_conv_stream<DT, MT, NT>;
+        auto k = args.wp ? k_conv_stream<DT, MT, NT, true> : k_conv_stream<DT, MT, NT, false>;
         int slots = args.c.cus * resident_per_cu(k, args.c.lds_bytes);
         if (slots > 8) slots = slots / 8 * 8;  // keep position p on XCD p % 8 across passes
         ConvArgs conv = args;
@@ -672,14 +684,55 @@ static hipError_t launch_conv_dt(int fused, const ConvArgs &args, hipStream_t st
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                        const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
-                       hipStream_t st, float *ws) {
+                       hipStream_t st, float *ws, const void *wp) {
     ConvArgs args{(const uint8_t *)src, (const uint8_t *)w, bias, idx, count, (uint8_t *)dst,
-                  (const uint8_t *)cache, prev_idx, prev_count, ws, g, cfg, cc};
+                  (const uint8_t *)cache, prev_idx, prev_count, ws, g, cfg, cc, (const uint8_t *)wp};
     switch (dt) {
     case 0: return launch_conv_dt<0>(fused, args, st);
     case 1: return launch_conv_dt<1>(fused, args, st);
     default: return launch_conv_dt<2>(fused, args, st);
     }
+}
+
+// The fragment-order copy of KRSC weights for the split's load_weights: for
+// chunk ch (c.ck input channels), N tile tn (16 NT output channels), K step s
+// of the chunk, N subtile q and lane l, the 16 bytes that lane loads from the
+// KRSC weights (clamped columns and channels included) at unit (((ch * ntn +
+// tn) * steps + s) * NT + q) * 64 + l.  One thread per unit.
+__global__ __launch_bounds__(256) void k_split_weights_pack(const uint8_t *__restrict__ w, Geo g, ConvCfg c, int dt,
+                                                            uint8_t *wp, long units) {
+    const int es = elem_bytes(dt), epv = 16 / es, ks = dt == 0 ? 16 : 32;
+    const int k2 = g.k * g.k, kpc = c.ck / ks, steps = k2 * kpc;
+    const int ntn = (g.cout + 16 * c.nt - 1) / (16 * c.nt);
+    for (long v = (long)blockIdx.x * 256 + threadIdx.x; v < units; v += (long)gridDim.x * 256) {
+        const int l = (int)(v & 63);
+        long q = v >> 6;
+        const int nt = (int)(q % c.nt);
+        q /= c.nt;
+        const int s = (int)(q % steps);
+        q /= steps;
+        const int tn = (int)(q % ntn), ch = (int)(q / ntn);
+        const int tap = s / kpc, kk = s - tap * kpc;
+        const int cb = min(ch * c.ck + kk * ks + (l >> 4) * epv, g.cin - epv);
+        const int col = min(tn * 16 * c.nt + nt * 16 + (l & 15), g.cout - 1);
+        *(u32x4 *)(wp + v * 16) = ld16(w + (((size_t)col * k2 + tap) * g.cin + cb) * es);
+    }
+}
+
+long split_weights_units(int dt, const Geo &g, const ConvCfg &c) {
+    const int ks = dt == 0 ? 16 : 32;
+    const long nch = (g.cin + c.ck - 1) / c.ck, ntn = (g.cout + 16 * c.nt - 1) / (16 * c.nt);
+    return nch * ntn * (long)g.k * g.k * (c.ck / ks) * c.nt * 64;
+}
+
+hipError_t launch_split_weights_pack(int dt, const void *w, const Geo &g, const ConvCfg &c, void *wp, int cus,
+                                     hipStream_t st) {
+    const long units = split_weights_units(dt, g, c);
+    long grid = (units + 255) / 256;
+    if (grid > 4L * cus) grid = 4L * cus;
+    hipLaunchKernelGGL(k_split_weights_pack, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, st,
+                       (const uint8_t *)w, g, c, dt, (uint8_t *)wp, units);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -1116,7 +1116,8 @@ int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *coun
 // can run) the wide tiles' stage-major section at a 256-byte aligned offset.
 struct PackedLayout {
     sige::LayerCfg lc;
-    int64_t layer_bytes, wide_off, wide_bytes, total;
+    ConvCfg cc;  // the split's configuration (split_bytes 0: the split cannot run)
+    int64_t layer_bytes, wide_off, wide_bytes, split_off, split_bytes, total;
 };
 
 static int packed_layout(const Geo &g, int dtype, PackedLayout *pl) {
@@ -1125,7 +1126,11 @@ static int packed_layout(const Geo &g, int dtype, PackedLayout *pl) {
     pl->layer_bytes = (int64_t)sige::layer_weights_units(g, pl->lc) * 16;
     pl->wide_off = (pl->layer_bytes + 255) / 256 * 256;
     pl->wide_bytes = dtype != SIGE_F32 && pl->lc.w_lds > 0 ? (int64_t)sige::wide_weights_units(g) * 16 : 0;
-    pl->total = pl->wide_off + pl->wide_bytes;
+    pl->split_off = (pl->wide_off + pl->wide_bytes + 255) / 256 * 256;
+    pl->split_bytes = choose_conv(g, dtype, 1, 1, &pl->cc, 1) == SIGE_OK
+                          ? (int64_t)sige::split_weights_units(dtype, g, pl->cc) * 16
+                          : 0;
+    pl->total = pl->split_off + pl->split_bytes;
     return SIGE_OK;
 }
 
@@ -1256,7 +1261,7 @@ static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias,
         const Region wr[] = {{out, obytes}, {workspace, (size_t)p.ws_bytes}};
         if (regions_overlap(wr, 2, rd, 6)) return fail(SIGE_EINVAL, "the workspace overlaps another argument");
     }
-    const uint8_t *wp = nullptr, *ww = nullptr;  // the packed sections, when given
+    const uint8_t *wp = nullptr, *ww = nullptr, *wsp = nullptr;  // the packed sections, when given
     if (w_packed) {
         PackedLayout pl;
         if ((rc = packed_layout(g, dtype, &pl))) return rc;
@@ -1264,6 +1269,8 @@ static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias,
         if ((rc = check_packed(w_packed, w_packed_bytes, pl, wr, 2))) return rc;
         wp = (const uint8_t *)w_packed;
         ww = pl.wide_bytes > 0 ? wp + pl.wide_off : nullptr;
+        // the split's section follows the split's configuration of the plan
+        wsp = pl.split_bytes > 0 && pl.cc.ck == p.cc.ck && pl.cc.nt == p.cc.nt ? wp + pl.split_off : nullptr;
     }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, copy_cached != 0);
@@ -1286,7 +1293,7 @@ static int layer_auto(const void *a_edit, const void *w_krsc, const float *bias,
     if (p.split_max >= 0)  // the split: lists of at most split_max blocks
         return finish(sige::launch_conv(dtype, 1, a_edit, w_krsc, bias, idx, count, out,
                                         copy_cached ? cached : nullptr, nullptr, nullptr, g, p.cc, cc, st,
-                                        (float *)workspace),
+                                        (float *)workspace, wsp),
                       "sige_sparse_conv_layer_auto", st);
     return SIGE_OK;
 }
@@ -1350,8 +1357,13 @@ int sige_pack_weights(const void *w_krsc, int dtype, const sige_geom *gp, void *
     if ((rc = finish(sige::launch_layer_weights_pack(dtype, w_krsc, g, pl.lc, w_packed, cus, st), "sige_pack_weights",
                      st)))
         return rc;
-    if (pl.wide_bytes > 0)
-        return finish(sige::launch_wide_weights_pack(w_krsc, g, (uint8_t *)w_packed + pl.wide_off, cus, st),
+    if (pl.wide_bytes > 0 &&
+        (rc = finish(sige::launch_wide_weights_pack(w_krsc, g, (uint8_t *)w_packed + pl.wide_off, cus, st),
+                     "sige_pack_weights", st)))
+        return rc;
+    if (pl.split_bytes > 0)
+        return finish(sige::launch_split_weights_pack(dtype, w_krsc, g, pl.cc, (uint8_t *)w_packed + pl.split_off,
+                                                      cus, st),
                       "sige_pack_weights", st);
     return SIGE_OK;
 }

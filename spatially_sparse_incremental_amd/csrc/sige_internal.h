@@ -133,7 +133,12 @@ hipError_t launch_gather(const void *a_edit, int dt, const Geo &g, const int32_t
 hipError_t launch_conv(int dt, int fused, const void *src, const void *w, const float *bias, const int32_t *idx,
                        const int32_t *count, void *dst, const void *cache, const int32_t *prev_idx,
                        const int32_t *prev_count, const Geo &g, const ConvCfg &cfg, const CopyCfg &cc,
-                       hipStream_t st, float *ws = nullptr);
+                       hipStream_t st, float *ws = nullptr, const void *wp = nullptr);
+// The split's fragment-order copy of KRSC weights (wp above) for configuration c:
+// 16-byte units of it, and the launch that writes it.
+long split_weights_units(int dt, const Geo &g, const ConvCfg &c);
+hipError_t launch_split_weights_pack(int dt, const void *w, const Geo &g, const ConvCfg &c, void *wp, int cus,
+                                     hipStream_t st);
 // The fused layer (fused = 1: src = a_edit, dst = out; with cc.nvec > 0 the
 // cache is copied outside the listed blocks, with prev_idx the previous
 // list's blocks are restored) or the block convolution (fused = 0: src =

@@ -489,13 +489,16 @@ def test_packed_weights_validation(lib):
     g = _g(1, 256, 256, 128, 128, 3, 1, 1, 6)
     krsc = 128 * 9 * 128 * 2
     assert layer_part(g, 1) == krsc
-    assert size(g, 1) == krsc + krsc  # both sections, nothing padded
-    assert size(g, 0) == layer_part(g, 0) == 2 * krsc  # fp32: the single-range section only
+    assert size(g, 1) == 3 * krsc  # the three sections, nothing padded
+    assert layer_part(g, 0) == 2 * krsc and size(g, 0) == 4 * krsc  # fp32: no wide tiles; split chunks of 64
     g2 = _g(1, 64, 64, 24, 136, 3, 1, 1, 6)  # c_out 136: 5 N tiles of 32; c_in 24: one 32-channel slice
-    lp = layer_part(g2, 2)
-    assert size(g2, 2) == (lp + 255) // 256 * 256 + 2 * 2 * 9 * 256 * 16
+    lp = (layer_part(g2, 2) + 255) // 256 * 256
+    wide = 2 * 2 * 9 * 256 * 16
+    split = 1 * 5 * 9 * 1 * 2 * 1024  # one chunk, 5 N tiles, 9 taps x 1 slice, 2 subtiles
+    assert size(g2, 2) == lp + wide + split
     gs = _g(1, 16, 16, 1280, 1280, 3, 1, 1, 2)  # no wide tiles (2x2 blocks)
-    assert size(gs, 2) == layer_part(gs, 2)
+    k2 = 1280 * 9 * 1280 * 2
+    assert layer_part(gs, 2) == k2 and size(gs, 2) == 2 * k2
     assert size(g, 7) == EDTYPE
     need = size(g, 1)
     s = _v(0)

@@ -110,3 +110,47 @@ def test_packed_bench_layer_at_full_size():
     o2 = ssi.sige_sparse_conv_layer(ag, wk, bg, cg, idx_all, c_all, g, w_packed=wp)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), "every block"
+
+
+@pytest.mark.parametrize("workload,layer", [("ldm_64x64x320_f16", "l16_3x3"), ("ldm_64x64x320_f16", "l32_1x1"),
+                                            ("gaugan_4conv_bf16", "g32x64"), ("unet_chain_12conv_bf16", "L32_down"),
+                                            ("unet_chain_12conv_bf16", "L128_down")])
+def test_packed_split_equals_krsc(workload, layer):
+    """Lists the library's plan gives to the split (the low-resolution,
+    weight-bound layers; stride 2; 1x1): sige_sparse_conv_layer_auto_packed
+    (the split's weight fragments from the packed copy) equals the KRSC call
+    bit for bit, with and without the copy, and the oracle on sampled blocks."""
+    import synth
+
+    L = [x for x in synth.workload(workload).layers if x.name == layer][0]
+    dt = DT[L.dtype]
+    g = ssi.geom(1, L.h, L.w, L.c_in, L.c_out, L.k, L.stride, L.pad, L.block)
+    plan = ssi.sige_sparse_conv_layer_plan(g, dt)
+    assert plan.split_max >= 1, plan.as_dict()
+    ho, wo, nby, nbx, _ = oracle.geometry(L.h, L.w, L.k, L.stride, L.pad, L.block)
+    a_e = synth.make_activation(1, L.h, L.w, L.c_in, L.dtype, 101)
+    wt, bias = synth.make_layer_tensors(L, 103)
+    cache = synth.make_activation(1, ho, wo, L.c_out, L.dtype, 105).cuda()
+    ag, wk, bg = a_e.cuda(), ssi.weight_to_krsc(wt).cuda(), bias.cuda()
+    wp = _pack_guarded(wk, g)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator().manual_seed(107)
+    for cnt in sorted({1, max(1, plan.split_max // 2), min(plan.split_max, plan.cap)}):
+        lst = torch.randperm(plan.cap, generator=gen)[:cnt].sort().values.to(torch.int32)
+        idx = torch.zeros(plan.cap, dtype=torch.int32)
+        idx[:cnt] = lst
+        idx, count = idx.cuda(), torch.tensor([cnt], dtype=torch.int32, device="cuda")
+        print(f"[case] {layer} split packed: {cnt} of {plan.cap} blocks", flush=True)
+        for copy in (True, False):
+            o1, o2 = cache.clone(), cache.clone()
+            ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cache if copy else None, idx, count, g, out=o1,
+                                            copy_cached=copy, workspace=ws)
+            ssi.sige_sparse_conv_layer_auto(ag, wk, bg, cache if copy else None, idx, count, g, out=o2,
+                                            copy_cached=copy, workspace=ws, w_packed=wp)
+            assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), f"{layer} {cnt} blocks copy={copy}"
+        sub = torch.zeros(plan.cap, dtype=torch.uint8)
+        sub[lst[torch.randperm(cnt, generator=gen)[:2]].long()] = 1
+        sub = sub.view(1, nby, nbx)
+        out = o2.cpu()
+        r64 = oracle.sparse_layer(a_e, wt, bias, L.k, L.stride, L.pad, L.block, sub, out, out_f64=True)
+        assert_close(out, r64, dt, active_pixels(sub, L.block, ho, wo), f"{layer} split packed, sampled blocks")
