@@ -308,7 +308,8 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
  * (nubint.ai review, "ABSTRACT": large edits) 32 bytes of each of 32 output
  * channels of a 16-channel stage; from the packed copy every such load reads
  * 1 KiB in a row.  Measured on MI355X: the 1.2% single-range layer of the
- * 256x256x128 U-Net conv about 9% faster, the wide tiles 6-10%.
+ * 256x256x128 U-Net conv about 9% faster, the wide tiles 6-10%, the split
+ * about 4%.
  * The copy has two sections, both in the library's own load order for the
  * geometry and dtype (they follow the kernel configuration the library picks,
  * so a copy is valid for that geometry, dtype and library build only):
@@ -323,7 +324,11 @@ int sige_sparse_conv_layer_auto(const void *a_edit, const void *w_krsc, const fl
  *     128 output channels, stage s of 16 input channels, tap t = ky * k + kx,
  *     column n < 128 and half h < 2, the 8 values W[128 tn + n][ky][kx][16 s
  *     + 8 h .. + 7] at unit ((tn * ceil(c_in / 16) + s) * k * k + t) * 256 +
- *     2 n + (h XOR ((n / 8) mod 2)), zeros past c_out and c_in.
+ *     2 n + (h XOR ((n / 8) mod 2)), zeros past c_out and c_in;
+ *   - from the next 256-byte boundary, where the split over input channels
+ *     can run: its fragments, as the first section's but in the split's own
+ *     chunks and N tiles (16 lanes per output channel of a 16x16 MFMA
+ *     fragment).
  *   sige_packed_weights_bytes: the size of the copy (a negative status code
  *   for invalid arguments).
  *   sige_pack_weights: writes it from w_krsc (the KRSC weights of
@@ -337,9 +342,9 @@ int sige_pack_weights(const void *w_krsc, int dtype, const sige_geom *g, void *w
                       void *stream);
 
 /* sige_sparse_conv_layer and sige_sparse_conv_layer_auto with the
- * single-range kernel and the wide tiles loading their weights from w_packed
- * (sige_pack_weights of the same w_krsc) instead of w_krsc; the split still
- * reads w_krsc.  Same arguments, checks and result as the unpacked calls, bit
+ * single-range kernel, the wide tiles and (auto) the split loading their
+ * weights from w_packed (sige_pack_weights of the same w_krsc) instead of
+ * w_krsc.  Same arguments, checks and result as the unpacked calls, bit
  * for bit (the same values reach the same registers and LDS slots in the same
  * order).  w_packed: non-NULL (SIGE_EINVAL), 256-byte aligned (SIGE_EALIGN),
  * w_packed_bytes at least sige_packed_weights_bytes (SIGE_ERANGE), not
