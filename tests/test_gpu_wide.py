@@ -242,8 +242,9 @@ def _packed_reference(wk, cin, cout, k):
                          ids=["cin24_cout136", "pointwise", "cin200", "cin256_cout64"])
 def test_packed_weights_wide_section_layout(shape):
     """The wide tiles' section of sige_pack_weights (from the 256-byte boundary
-    after the single-range kernel's section) against the stage-major layout
-    written out on the CPU, bit for bit, with a guard canary after the copy."""
+    after the single-range kernel's section; the split's section follows it)
+    against the stage-major layout written out on the CPU, bit for bit, with a
+    guard canary after the copy."""
     cin, cout, k = shape
     g = ssi.geom(1, 40, 44, cin, cout, k, 1, k // 2, 6)
     dt = torch.bfloat16
@@ -251,13 +252,15 @@ def test_packed_weights_wide_section_layout(shape):
     wk = ssi.weight_to_krsc(wt)
     need = ssi.sige_packed_weights_bytes(g, dt)
     wide = ((cout + 127) // 128) * ((cin + 15) // 16) * k * k * 4096
-    off = need - wide
-    assert off % 256 == 0 and off >= cout * k * k * cin * 2
+    plan = ssi.sige_sparse_conv_layer_plan(g, dt)
+    nsub = 2 if plan.n_tiles * 32 >= cout else 1  # the single-range kernel's N subtiles per tile
+    off = (plan.chunks * plan.n_tiles * plan.steps * nsub * 1024 + 255) // 256 * 256  # after its section
+    assert off + wide <= need
     buf = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
     ssi.sige_pack_weights(wk.cuda(), g, out=buf[:need])
     torch.cuda.synchronize()
     assert (buf[need:] == 0x5A).all(), "writes past the packed copy"
-    got = buf[off:need].cpu().view(torch.int16)
+    got = buf[off:off + wide].cpu().view(torch.int16)
     ref = _packed_reference(wk, cin, cout, k).view(torch.int16)
     assert torch.equal(got, ref)
 
