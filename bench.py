@@ -228,7 +228,8 @@ def main():
     oblocks = torch.empty((cap, L.block, L.block, L.c_out), dtype=dt, device=dev)
     out3 = torch.empty_like(cache)
     t_gather = graph_time(lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks))
-    t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks))
+    t_convb = graph_time(lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks,
+                                                      w_packed=w_packed))
     t_scatter = graph_time(lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True))
     print(f"[bench] kernels {kt} gather {t_gather:.2f} conv_blocks {t_convb:.2f} scatter {t_scatter:.2f}",
           file=sys.stderr, flush=True)
@@ -240,7 +241,8 @@ def main():
                  lambda: ssi.sige_sparse_conv_layer(a_e, w_krsc, bias, None, idx, count, g, out=out,
                                                     copy_cached=False, w_packed=w_packed),
                  lambda: ssi.sige_gather(a_e, g, idx, count, blocks=blocks),
-                 lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks),
+                 lambda: ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks,
+                                              w_packed=w_packed),
                  lambda: ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)]
         evict = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
         for r in range(args.cold_kernels):  # evicted by writes: the MALL is left full of dirty lines
@@ -307,7 +309,7 @@ def main():
             ssi.sige_diff_mask_bits(a_o, a_e, wl.tau, bits=mbits)
             ssi.sige_reduce_bits(mbits, L.h, L.w, g, L.dilate, idx=idx, count=count)
             ssi.sige_gather(a_e, g, idx, count, blocks=blocks)
-            ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks)
+            ssi.sige_conv_blocks(blocks, w_krsc, bias, g, count, out_blocks=oblocks, w_packed=w_packed)
             ssi.sige_scatter(oblocks, idx, count, g, cache, out=out3, copy_cached=True)
 
         t_nocopy = graph_time(step_nocopy, 5, 40)

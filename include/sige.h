@@ -341,14 +341,17 @@ int64_t sige_packed_weights_bytes(const sige_geom *g, int dtype);
 int sige_pack_weights(const void *w_krsc, int dtype, const sige_geom *g, void *w_packed, int64_t w_packed_bytes,
                       void *stream);
 
-/* sige_sparse_conv_layer and sige_sparse_conv_layer_auto with the
- * single-range kernel, the wide tiles and (auto) the split loading their
- * weights from w_packed (sige_pack_weights of the same w_krsc) instead of
- * w_krsc.  Same arguments, checks and result as the unpacked calls, bit
+/* sige_conv_blocks, sige_sparse_conv_layer and sige_sparse_conv_layer_auto
+ * with the single-range kernel (the block convolution's too), the wide tiles
+ * and (auto) the split loading their weights from w_packed
+ * (sige_pack_weights of the same w_krsc) instead of w_krsc.  Same arguments, checks and result as the unpacked calls, bit
  * for bit (the same values reach the same registers and LDS slots in the same
  * order).  w_packed: non-NULL (SIGE_EINVAL), 256-byte aligned (SIGE_EALIGN),
  * w_packed_bytes at least sige_packed_weights_bytes (SIGE_ERANGE), not
- * overlapping out or the workspace (SIGE_EINVAL). */
+ * overlapping out, out_blocks or the workspace (SIGE_EINVAL). */
+int sige_conv_blocks_packed(const void *blocks, const void *w_krsc, const float *bias, int dtype, const sige_geom *g,
+                            const int32_t *count, void *out_blocks, const void *w_packed, int64_t w_packed_bytes,
+                            void *stream);
 int sige_sparse_conv_layer_packed(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                                   const int32_t *idx, const int32_t *count, int dtype, const sige_geom *g, void *out,
                                   int copy_cached, const void *w_packed, int64_t w_packed_bytes, void *stream);

@@ -24,6 +24,7 @@ EXPORTS = ("sige_geom_derive", "sige_max_blocks", "sige_diff_mask", "sige_reduce
            "sige_sparse_conv_layer_split_noalloc", "sige_noalloc_scratch_bytes",
            "sige_sparse_conv_layer_plan", "sige_sparse_conv_layer_auto",
            "sige_packed_weights_bytes", "sige_pack_weights", "sige_sparse_conv_layer_packed",
+           "sige_conv_blocks_packed",
            "sige_sparse_conv_layer_auto_packed",
            "sige_gather",
            "sige_conv_blocks", "sige_scatter", "sige_sparse_conv_layer", "sige_restore_blocks", "sige_sparse_conv_layer_restore",
@@ -97,6 +98,7 @@ def lib():
         L.sige_packed_weights_bytes.restype = ctypes.c_int64
         L.sige_pack_weights.argtypes = [V, I, P, V, ctypes.c_int64, V]
         L.sige_sparse_conv_layer_packed.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V]
+        L.sige_conv_blocks_packed.argtypes = [V, V, V, I, P, V, V, V, ctypes.c_int64, V]
         L.sige_sparse_conv_layer_auto_packed.argtypes = [V, V, V, V, V, V, I, P, V, I, V, ctypes.c_int64, V,
                                                          ctypes.c_int64, V]
         L.sige_noalloc_scratch_bytes.argtypes = []
@@ -359,9 +361,11 @@ def sige_gather(a_edit, g: Geom, idx, count, blocks=None, stream=None):
     return blocks
 
 
-def sige_conv_blocks(blocks, w_krsc, bias, g: Geom, count, out_blocks=None, stream=None):
-    """[cap, b, b, c_out]: conv of each stacked block (slots < count)."""
-    _dev(blocks, w_krsc, bias, count, out_blocks)
+def sige_conv_blocks(blocks, w_krsc, bias, g: Geom, count, out_blocks=None, stream=None, w_packed=None):
+    """[cap, b, b, c_out]: conv of each stacked block (slots < count); with w_packed
+    (sige_pack_weights of w_krsc) the weights come from the packed copy
+    (sige_conv_blocks_packed)."""
+    _dev(blocks, w_krsc, bias, count, out_blocks, w_packed)
     if w_krsc.dtype != blocks.dtype or (bias is not None and bias.dtype != torch.float32):
         raise ValueError("weights must match the activation dtype; bias must be fp32")
     d = sige_geom_derive(g)
@@ -373,9 +377,14 @@ def sige_conv_blocks(blocks, w_krsc, bias, g: Geom, count, out_blocks=None, stre
     if out_blocks is None:
         out_blocks = torch.empty((max(d.cap, 1), g.block, g.block, g.c_out), dtype=blocks.dtype,
                                  device=blocks.device)
-    rc = lib().sige_conv_blocks(_p(blocks), _p(w_krsc), _p(bias), _dt(blocks), ctypes.byref(g), _p(count),
-                                _p(out_blocks), _stream(stream))
-    _check(rc, "sige_conv_blocks")
+    args = (_p(blocks), _p(w_krsc), _p(bias), _dt(blocks), ctypes.byref(g), _p(count), _p(out_blocks))
+    if w_packed is None:
+        rc = lib().sige_conv_blocks(*args, _stream(stream))
+        _check(rc, "sige_conv_blocks")
+    else:
+        rc = lib().sige_conv_blocks_packed(*args, _p(w_packed), w_packed.numel() * w_packed.element_size(),
+                                           _stream(stream))
+        _check(rc, "sige_conv_blocks_packed")
     return out_blocks
 
 

@@ -980,7 +980,8 @@ static hipError_t launch_layer_k(const LayerArgs &args, hipStream_t st) {
 
 template <int DT, int MT, int NT>
 static hipError_t launch_layer_t(int fused, bool tail, const LayerArgs &a, hipStream_t st) {
-    if (!fused) return launch_layer_k<DT, MT, NT, false, false>(a, st);
+    if (!fused)
+        return a.wp ? launch_layer_k<DT, MT, NT, false, false, true>(a, st) : launch_layer_k<DT, MT, NT, false, false>(a, st);
     if (a.wp)  // the weights from the fragment-order copy
         return tail ? launch_layer_k<DT, MT, NT, true, true, true>(a, st)
                     : launch_layer_k<DT, MT, NT, true, false, true>(a, st);

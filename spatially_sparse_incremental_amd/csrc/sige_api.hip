@@ -1057,8 +1057,37 @@ int sige_gather(const void *a_edit, int dtype, const sige_geom *gp, const int32_
                   (hipStream_t)stream);
 }
 
-int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, int dtype, const sige_geom *gp,
-                     const int32_t *count, void *out_blocks, void *stream) {
+// The packed copy of a layer's weights (sige_pack_weights): the single-range
+// kernel's fragment-order section, then (16-bit types, where the wide tiles
+// can run) the wide tiles' stage-major section at a 256-byte aligned offset.
+struct PackedLayout {
+    sige::LayerCfg lc;
+    ConvCfg cc;  // the split's configuration (split_bytes 0: the split cannot run)
+    int64_t layer_bytes, wide_off, wide_bytes, split_off, split_bytes, total;
+};
+
+static int packed_layout(const Geo &g, int dtype, PackedLayout *pl) {
+    int rc = choose_layer(g, dtype, &pl->lc);
+    if (rc) return rc;
+    pl->layer_bytes = (int64_t)sige::layer_weights_units(g, pl->lc) * 16;
+    pl->wide_off = (pl->layer_bytes + 255) / 256 * 256;
+    pl->wide_bytes = dtype != SIGE_F32 && pl->lc.w_lds > 0 ? (int64_t)sige::wide_weights_units(g) * 16 : 0;
+    pl->split_off = (pl->wide_off + pl->wide_bytes + 255) / 256 * 256;
+    pl->split_bytes = choose_conv(g, dtype, 1, 1, &pl->cc, 1) == SIGE_OK
+                          ? (int64_t)sige::split_weights_units(dtype, g, pl->cc) * 16
+                          : 0;
+    pl->total = pl->split_off + pl->split_bytes;
+    return SIGE_OK;
+}
+
+// Checks of a caller's packed weights against the layout: non-NULL, aligned,
+// large enough, not overlapping the written regions wr[0, nwr).
+static int check_packed(const void *w_packed, int64_t w_packed_bytes, const PackedLayout &pl, const Region *wr,
+                        int nwr);
+
+static int conv_blocks(const void *blocks, const void *w_krsc, const float *bias, int dtype, const sige_geom *gp,
+                       const int32_t *count, void *out_blocks, const void *w_packed, int64_t w_packed_bytes,
+                       void *stream, const char *name) {
     if (!dtype_ok(dtype)) return fail(SIGE_EDTYPE, "dtype %d", dtype);
     Geo g;
     int rc = derive(gp, &g);
@@ -1077,11 +1106,30 @@ int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, 
     }
     sige::LayerCfg cfg;
     if ((rc = choose_layer(g, dtype, &cfg))) return rc;
+    if (w_packed) {
+        PackedLayout pl;
+        if ((rc = packed_layout(g, dtype, &pl))) return rc;
+        const Region wr[] = {{out_blocks, (size_t)g.cap * g.b * g.b * g.cout * es}};
+        if ((rc = check_packed(w_packed, w_packed_bytes, pl, wr, 1))) return rc;
+    }
     if ((rc = device_ready())) return rc;
     const sige::CopyCfg cc = copy_plan(g, es, false);
     return finish(sige::launch_layer(dtype, 0, blocks, w_krsc, bias, nullptr, count, out_blocks, nullptr, nullptr,
-                                     nullptr, g, cfg, cc, (hipStream_t)stream),
-                  "sige_conv_blocks", (hipStream_t)stream);
+                                     nullptr, g, cfg, cc, (hipStream_t)stream, w_packed),
+                  name, (hipStream_t)stream);
+}
+
+int sige_conv_blocks(const void *blocks, const void *w_krsc, const float *bias, int dtype, const sige_geom *gp,
+                     const int32_t *count, void *out_blocks, void *stream) {
+    return conv_blocks(blocks, w_krsc, bias, dtype, gp, count, out_blocks, nullptr, 0, stream, "sige_conv_blocks");
+}
+
+int sige_conv_blocks_packed(const void *blocks, const void *w_krsc, const float *bias, int dtype,
+                            const sige_geom *gp, const int32_t *count, void *out_blocks, const void *w_packed,
+                            int64_t w_packed_bytes, void *stream) {
+    if (!w_packed) return fail(SIGE_EINVAL, "NULL pointer");
+    return conv_blocks(blocks, w_krsc, bias, dtype, gp, count, out_blocks, w_packed, w_packed_bytes, stream,
+                       "sige_conv_blocks_packed");
 }
 
 int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *count, const sige_geom *gp, int dtype,
@@ -1111,33 +1159,6 @@ int sige_scatter(const void *out_blocks, const int32_t *idx, const int32_t *coun
                   "sige_scatter", (hipStream_t)stream);
 }
 
-// The packed copy of a layer's weights (sige_pack_weights): the single-range
-// kernel's fragment-order section, then (16-bit types, where the wide tiles
-// can run) the wide tiles' stage-major section at a 256-byte aligned offset.
-struct PackedLayout {
-    sige::LayerCfg lc;
-    ConvCfg cc;  // the split's configuration (split_bytes 0: the split cannot run)
-    int64_t layer_bytes, wide_off, wide_bytes, split_off, split_bytes, total;
-};
-
-static int packed_layout(const Geo &g, int dtype, PackedLayout *pl) {
-    int rc = choose_layer(g, dtype, &pl->lc);
-    if (rc) return rc;
-    pl->layer_bytes = (int64_t)sige::layer_weights_units(g, pl->lc) * 16;
-    pl->wide_off = (pl->layer_bytes + 255) / 256 * 256;
-    pl->wide_bytes = dtype != SIGE_F32 && pl->lc.w_lds > 0 ? (int64_t)sige::wide_weights_units(g) * 16 : 0;
-    pl->split_off = (pl->wide_off + pl->wide_bytes + 255) / 256 * 256;
-    pl->split_bytes = choose_conv(g, dtype, 1, 1, &pl->cc, 1) == SIGE_OK
-                          ? (int64_t)sige::split_weights_units(dtype, g, pl->cc) * 16
-                          : 0;
-    pl->total = pl->split_off + pl->split_bytes;
-    return SIGE_OK;
-}
-
-// Checks of a caller's packed weights against the layout: non-NULL, aligned,
-// large enough, not overlapping the written regions wr[0, nwr).
-static int check_packed(const void *w_packed, int64_t w_packed_bytes, const PackedLayout &pl, const Region *wr,
-                        int nwr);
 
 static int layer_single(const void *a_edit, const void *w_krsc, const float *bias, const void *cached,
                         const int32_t *idx, const int32_t *count, int dtype, const sige_geom *gp, void *out,

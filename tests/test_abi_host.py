@@ -520,6 +520,13 @@ def test_packed_weights_validation(lib):
     assert f(*args, _v(W + 16), need, s) == EALIGN
     assert f(*args, _v(D + 256), need, s) == EINVAL  # overlaps out
 
+    f = lib.sige_conv_blocks_packed
+    args = (_v(A), _v(B), None, 1, ctypes.byref(g), _v(C), _v(D))
+    assert f(*args, _v(W), need, s) == ENODEV
+    assert f(*args, None, need, s) == EINVAL
+    assert f(*args, _v(W), need - 16, s) == ERANGE
+    assert f(*args, _v(D + 256), need, s) == EINVAL  # overlaps out_blocks
+
     f = lib.sige_sparse_conv_layer_auto_packed
     g3 = _g(1, 32, 64, 1024, 1024, 3, 1, 1, 4)
     need3 = size(g3, 1)

@@ -1,5 +1,6 @@
 """The single-range layer kernel with its weights packed in load order
-(sige_pack_weights, sige_sparse_conv_layer_packed) against the same kernel on
+(sige_pack_weights, sige_sparse_conv_layer_packed, sige_conv_blocks_packed)
+against the same kernel on
 the KRSC weights, bit for bit: the packed copy holds exactly the 16 bytes each
 lane would load from the KRSC weights (clamped columns and channels included),
 so every MFMA sees the same operands in the same order.  Geometries: 16-bit
@@ -71,6 +72,12 @@ def test_packed_single_range_layer_equals_krsc(case):
             ssi.sige_sparse_conv_layer(ag, wk, bg, cache if copy else None, idx, count, g, out=o2, copy_cached=copy,
                                        w_packed=wp)
             assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), f"{name} {cnt} blocks copy={copy}"
+        # the three-call path's block convolution on the same list
+        blocks = ssi.sige_gather(ag, g, idx, count)
+        b1 = ssi.sige_conv_blocks(blocks, wk, bg, g, count)
+        b2 = ssi.sige_conv_blocks(blocks, wk, bg, g, count, w_packed=wp)
+        torch.cuda.synchronize()
+        assert torch.equal(b1[:cnt].view(torch.uint8), b2[:cnt].view(torch.uint8)), f"{name} {cnt} blocks: conv_blocks"
 
 
 def test_packed_bench_layer_at_full_size():
